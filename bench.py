@@ -1,0 +1,252 @@
+#!/usr/bin/env python3
+"""Decode throughput of one CSA attention layer at 1M context on one MI355X.
+
+One step is the whole CSA decode hot path for a batch of 4 sequences of 1,048,576 raw
+tokens (262,144 compressed entries each), 64 query heads, top-1024, window 128:
+  compress_kv (newest complete chunk) -> indexer_scores -> topk_select -> sparse_attn_decode.
+Inputs are synthetic (seeded N(0,1) bf16, indexer N(0,1/64)), resident in HBM before the
+timed region. The compressed cache and the indexer keys are kept in several independent
+copies that consecutive steps rotate through, so every step streams from HBM rather than
+from the last-level cache.
+
+Prints one JSON line: queries/s, ms per step, the indexer kernel's achieved HBM bandwidth
+against the 8 TB/s peak (measured with HIP events around each launch inside the timed
+region), and the fp64 CPU oracle's rate on a bounded sample of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--copies R] [--no-cpu-baseline]
+  python bench.py --copy-calibration     # plain device copy of known size (for counters)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "CSA/HCA decode queries/s at 1M ctx; achieved HBM GB/s vs MI355X peak"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published peak
+WORKLOAD = "csa_decode_1m"
+COUNTER_FILE = os.path.join(ROOT, "profiles", "indexer_csa_decode_1m_counters.txt")
+INDEXER_SOURCES = ["compressed_sparse_long_amd/csrc/indexer.hip", "compressed_sparse_long_amd/csrc/device_common.h"]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--copies", type=int, default=4, help="rotated input copies (>= 4 defeats the 256 MB MALL)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="wall budget of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stages", action="store_true", help="skip the per-stage breakdown pass")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (reference for HBM counters)")
+    return ap.parse_args()
+
+
+def sources_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def read_traffic(launch_bytes_alg):
+    """HBM bytes per indexer launch from committed counter runs, or None if the kernel
+    source changed since they were taken."""
+    if not os.path.exists(COUNTER_FILE):
+        return None
+    vals = {}
+    with open(COUNTER_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != sources_hash(INDEXER_SOURCES):
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "copies": 5}))
+
+
+def cpu_baseline(inp, seconds: float):
+    """The fp64 oracle on whole decode queries of the same workload, on the host cores."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import csa
+
+    li = inp.lanes[0]
+    lane = li.lane
+    B, m, k, W = lane.B, lane.m, lane.k, lane.W
+    kv, z, q = inp.kv, inp.z, inp.q
+    keys = [li.kI[lane.ent_off()[b]:lane.ent_off()[b + 1]].double().numpy() for b in range(B)]
+    scale = 1.0 / np.sqrt(lane.D)
+    t0 = time.perf_counter()
+    n = 0
+    while n == 0 or time.perf_counter() - t0 < seconds:
+        b = n % B
+        row0 = lane.kv_off()[b]
+        N = lane.lengths[b]
+        p = lane.q_pos[b]
+        # newest complete chunk, then the query-side steps
+        csa.compress(kv[row0 + N - m: row0 + N].double().numpy(), z[row0 + N - m: row0 + N].double().numpy(), m)
+        s = csa.indexer(li.qI[b, 0].double().numpy(), li.w[b, 0].double().numpy(), keys[b][:csa.n_visible(p, m, N // m)])
+        sel = csa.topk(s, k)
+        sel = sel[sel >= 0]
+        rows = (row0 + sel[:, None] * m + np.arange(m)[None, :]).reshape(-1)
+        import torch
+        rt = torch.from_numpy(rows)
+        comp = csa.to_bf16_f64(csa.compress(kv.index_select(0, rt).double().numpy(),
+                                            z.index_select(0, rt).double().numpy(), m))
+        win = csa.window_rows(p, N, W)
+        X = np.concatenate([comp, kv[row0 + win.start: row0 + win.stop].double().numpy()])
+        csa.attend(q[b, 0].double().numpy(), X, scale)
+        n += 1
+    el = time.perf_counter() - t0
+    threads = 1
+    for info in threadpool_info():
+        if info.get("user_api") == "blas":
+            threads = max(threads, int(info.get("num_threads", 1)))
+    return {"value": n / el, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} whole decode queries of {WORKLOAD} (fp64 numpy: newest-chunk compression, "
+                      f"indexer over 262144 keys, top-1024, attention over 1152 rows) in {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this path runs on a "
+              f"single MI355X and has no multi-GPU mode)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import synth
+    from compressed_sparse_long_amd import lanes
+
+    t_gen = time.perf_counter()
+    inp = synth.generate(WORKLOAD)
+    (cl,) = lanes.build_lanes(inp)
+    cl.rotate(args.copies)
+    cl.compress_all()
+    torch.cuda.synchronize()
+    print(f"# inputs ready in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+    lane = inp.lanes[0].lane
+    B, T, E, HI, CI, H, D, k, W = lane.B, lane.T, lane.entries[0], lane.HI, lane.CI, lane.H, lane.D, lane.k, lane.W
+
+    for i in range(args.warmup):
+        cl.step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(K):
+        cl.compress_new(i)
+        ev[i][0].record()
+        cl.index(i)
+        ev[i][1].record()
+        cl.select()
+        cl.attend(i)
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / K
+    idx_us = sum(a.elapsed_time(b) for a, b in ev) / K * 1e3
+    queries = B * T * K
+    value = queries / (total_ms / 1e3)
+
+    # algorithmic bytes (per step, and per indexer launch)
+    idx_bytes = B * (E * CI * 2 + E * 4 + HI * CI * 2 + HI * 4)                # keys + scores + q + w
+    step_bytes = (B * (E * CI * 2 + HI * CI * 2 + HI * 4)                       # indexer inputs
+                  + B * (k * D * 2 + W * D * 2 + H * D * 2 + H * D * 4 + H * 4)  # gathers, q, out, lse
+                  + B * (2 * lane.m * D * 2 + D * 2))                            # newest-chunk compress
+    achieved = idx_bytes / (idx_us * 1e-6) / 1e9
+    traffic = read_traffic(idx_bytes)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "batch": B, "context_tokens": lane.lengths[0], "entries": E,
+                   "heads": H, "head_dim": D, "m": lane.m, "top_k": k, "window": W, "indexer_heads": HI,
+                   "indexer_dim": CI, "rotated_copies": args.copies},
+        "roofline": {"kernel": "indexer_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "launch_us": round(idx_us, 3), "bytes_per_launch": idx_bytes},
+        "step_hbm": {"bytes": step_bytes, "GB_s": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+                     "frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+    }
+
+    if not args.no_stages:
+        # per-stage breakdown in a separate pass (not part of the timed region)
+        S = 50
+        names = ["compress_new", "indexer", "topk", "attention"]
+        evs = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(S)]
+               for n in names}
+        fns = {"compress_new": cl.compress_new, "indexer": cl.index, "topk": lambda i: cl.select(),
+               "attention": cl.attend}
+        torch.cuda.synchronize()
+        for i in range(S):
+            for n in names:
+                evs[n][i][0].record()
+                fns[n](i)
+                evs[n][i][1].record()
+        torch.cuda.synchronize()
+        result["stages_us"] = {n: round(sum(a.elapsed_time(b) for a, b in evs[n]) / S * 1e3, 2) for n in names}
+        # bulk compression of one whole 4 x 1M-token context (2 GiB read)
+        ce = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(3)]
+        for i in range(3):
+            ce[i][0].record()
+            lanes.compress_kv(cl.kv, cl.z, cl.kv_off, cl.ent_off, cl.m, cl.ckv_copies[i % len(cl.ckv_copies)],
+                              max_new_entries=cl.max_entries)
+            ce[i][1].record()
+        torch.cuda.synchronize()
+        cus = sum(a.elapsed_time(b) for a, b in ce) / 3 * 1e3
+        cbytes = sum(lane.lengths) * D * 2 * 2 + sum(lane.entries) * D * 2
+        result["compress_bulk"] = {"us": round(cus, 1), "bytes": cbytes, "GB_s": round(cbytes / (cus * 1e-6) / 1e9, 1),
+                                   "frac": round(cbytes / (cus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,194 @@
+"""Python binding of libcsl.so, the gfx950 hybrid compressed-attention library.
+
+Argument marshalling only: every function takes torch tensors that already live on the
+GPU, passes their device pointers, sizes and torch's current HIP stream to the C ABI
+(include/csl.h), and raises on a non-zero status. All computation happens in the HIP
+kernels; there is no fallback path. Importing fails if the shared library is not built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "compress_kv", "indexer_scores", "topk_select", "sparse_attn_decode", "hca_attn_decode",
+    "topk_workspace_bytes", "attn_workspace_bytes", "version", "LIB_PATH", "EXPORTS",
+    "CslError",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsl.so")
+
+BF16, F32, FP8_E4M3 = 0, 1, 2
+EXPORTS = [
+    "csl_last_error", "csl_version", "csl_compress_kv", "csl_indexer_scores",
+    "csl_topk_workspace_bytes", "csl_topk_select", "csl_attn_workspace_bytes",
+    "csl_sparse_attn_decode", "csl_hca_attn_decode",
+]
+
+
+class CslError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"csl status {status}: {msg}")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m compressed_sparse_long_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, L, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    sig = {
+        "csl_last_error": (ctypes.c_char_p, []),
+        "csl_version": (I, []),
+        "csl_compress_kv": (I, [P, P, P, P, P, I, I, I, L, P, I, P]),
+        "csl_indexer_scores": (I, [P, P, P, I, P, P, I, P, P, I, I, I, I, I, L, P, L, P]),
+        "csl_topk_workspace_bytes": (S, [I, I, L, I]),
+        "csl_topk_select": (I, [P, L, P, P, I, I, I, I, L, P, P, S, P]),
+        "csl_attn_workspace_bytes": (S, [I, I, I, I, L]),
+        "csl_sparse_attn_decode": (I, [P, P, P, I, P, P, P, P, I, I, I, I, I, F, P, P, P, S, P]),
+        "csl_hca_attn_decode": (I, [P, P, P, P, P, P, I, I, I, I, I, I, F, L, P, P, P, S, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def version() -> int:
+    return int(_lib.csl_version())
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise CslError(status, _lib.csl_last_error().decode())
+
+
+def _ptr(t: torch.Tensor | None, name: str, dtypes=None) -> int | None:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+_I64 = (torch.int64,)
+_BF16 = (torch.bfloat16,)
+_F32 = (torch.float32,)
+
+
+def compress_kv(kv, z, kv_off, ent_off, m: int, out, first_entry=None, max_new_entries: int | None = None,
+                stream=None):
+    """Softmax-weighted pooling of every m raw rows into out (fp32 or bf16 [*, D]); see csl.h."""
+    B = kv_off.numel() - 1
+    D = kv.shape[-1]
+    dt = {torch.float32: F32, torch.bfloat16: BF16}.get(out.dtype)
+    if dt is None:
+        raise ValueError("out must be float32 or bfloat16")
+    if max_new_entries is None:
+        max_new_entries = out.shape[0]
+    _check(_lib.csl_compress_kv(
+        _ptr(kv, "kv", _BF16), _ptr(z, "z", _BF16), _ptr(kv_off, "kv_off", _I64), _ptr(ent_off, "ent_off", _I64),
+        _ptr(first_entry, "first_entry", _I64), B, D, int(m), int(max_new_entries), _ptr(out, "out"), dt,
+        _stream(stream)))
+    return out
+
+
+def indexer_scores(qI, w, kI, ent_off, q_pos, m: int, scores, max_entries: int | None = None, k_scale=None,
+                   scale_off=None, scale_group: int = 64, stream=None):
+    """Lightning-indexer scores into scores fp32 [B, T, ld]; see csl.h."""
+    B, T, HI, CI = qI.shape
+    if kI.dtype == torch.bfloat16:
+        kd = BF16
+    elif kI.dtype in (torch.uint8, torch.float8_e4m3fn):
+        kd = FP8_E4M3
+    else:
+        raise ValueError("kI must be bfloat16 or fp8 e4m3 (uint8 codes)")
+    ld = scores.shape[-1]
+    if max_entries is None:
+        max_entries = ld
+    _check(_lib.csl_indexer_scores(
+        _ptr(qI, "qI", _BF16), _ptr(w, "w", _F32), _ptr(kI, "kI"), kd, _ptr(k_scale, "k_scale", _F32),
+        _ptr(scale_off, "scale_off", _I64), int(scale_group), _ptr(ent_off, "ent_off", _I64),
+        _ptr(q_pos, "q_pos", _I64), int(m), B, T, HI, CI, int(max_entries), _ptr(scores, "scores", _F32), ld,
+        _stream(stream)))
+    return scores
+
+
+def topk_workspace_bytes(B: int, T: int, max_entries: int, k: int) -> int:
+    return int(_lib.csl_topk_workspace_bytes(B, T, max_entries, k))
+
+
+def topk_select(scores, ent_off, q_pos, m: int, k: int, idx, ws=None, max_entries: int | None = None, stream=None):
+    """Top-k ids per row into idx int32 [B, T, k] (ascending, -1 padded). ``ws`` must be a
+    zero-initialised uint8 device tensor reused across calls; a fresh one is made if None."""
+    B, T, ld = scores.shape
+    if max_entries is None:
+        max_entries = ld
+    need = topk_workspace_bytes(B, T, max_entries, k)
+    if ws is None and need > 0:
+        ws = torch.zeros(need, dtype=torch.uint8, device=scores.device)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.csl_topk_select(
+        _ptr(scores, "scores", _F32), ld, _ptr(ent_off, "ent_off", _I64), _ptr(q_pos, "q_pos", _I64), int(m), B, T,
+        int(k), int(max_entries), _ptr(idx, "idx", (torch.int32,)), _ptr(ws, "ws"), ws_bytes, _stream(stream)))
+    return idx
+
+
+def attn_workspace_bytes(B: int, T: int, H: int, D: int, max_keys: int) -> int:
+    return int(_lib.csl_attn_workspace_bytes(B, T, H, D, max_keys))
+
+
+def _attn_ws(ws, B, T, H, D, max_keys, device):
+    need = attn_workspace_bytes(B, T, H, D, max_keys)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    return ws, (0 if ws is None else ws.numel() * ws.element_size())
+
+
+def sparse_attn_decode(q, ckv, idx, kv, kv_off, ent_off, q_pos, n_win: int, out, lse=None, scale: float | None = None,
+                       ws=None, stream=None):
+    """CSA attention over the selected entries plus the raw window; see csl.h."""
+    B, T, H, D = q.shape
+    k = idx.shape[-1]
+    if scale is None:
+        scale = D ** -0.5
+    ws, wb = _attn_ws(ws, B, T, H, D, k + n_win, q.device)
+    _check(_lib.csl_sparse_attn_decode(
+        _ptr(q, "q", _BF16), _ptr(ckv, "ckv", _BF16), _ptr(idx, "idx", (torch.int32,)), k, _ptr(kv, "kv", _BF16),
+        _ptr(kv_off, "kv_off", _I64), _ptr(ent_off, "ent_off", _I64), _ptr(q_pos, "q_pos", _I64), int(n_win), B, T, H,
+        D, float(scale), _ptr(out, "out", _F32), _ptr(lse, "lse", _F32), _ptr(ws, "ws"), wb, _stream(stream)))
+    return out
+
+
+def hca_attn_decode(q, ckv, kv, kv_off, ent_off, q_pos, m: int, n_win: int, out, lse=None, scale: float | None = None,
+                    max_entries: int | None = None, ws=None, stream=None):
+    """HCA dense attention over every visible entry plus the raw window; see csl.h."""
+    B, T, H, D = q.shape
+    if scale is None:
+        scale = D ** -0.5
+    if max_entries is None:
+        max_entries = ckv.shape[0]
+    ws, wb = _attn_ws(ws, B, T, H, D, max_entries + n_win, q.device)
+    _check(_lib.csl_hca_attn_decode(
+        _ptr(q, "q", _BF16), _ptr(ckv, "ckv", _BF16), _ptr(kv, "kv", _BF16), _ptr(kv_off, "kv_off", _I64),
+        _ptr(ent_off, "ent_off", _I64), _ptr(q_pos, "q_pos", _I64), int(m), int(n_win), B, T, H, D, float(scale),
+        int(max_entries), _ptr(out, "out", _F32), _ptr(lse, "lse", _F32), _ptr(ws, "ws"), wb, _stream(stream)))
+    return out

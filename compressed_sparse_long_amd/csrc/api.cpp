@@ -1,0 +1,179 @@
+// C ABI of the library: host-side argument validation, thread-local error text, and the
+// hand-off to the kernel launchers. Nothing here allocates device memory or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/csl.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return CSL_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(CSL_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+constexpr int kMaxGridY = 65535;
+
+}  // namespace
+
+extern "C" {
+
+const char* csl_last_error(void) { return g_last_error.c_str(); }
+
+int csl_version(void) { return 100; }
+
+int csl_compress_kv(const void* kv, const void* z, const int64_t* kv_off, const int64_t* ent_off,
+                    const int64_t* first_entry, int B, int D, int m, int64_t max_new_entries, void* out,
+                    int out_dtype, void* stream) {
+  if (B < 0 || max_new_entries < 0) return fail(CSL_ERR_INVALID, "compress_kv: negative B or max_new_entries");
+  if (!kv || !kv_off || !ent_off || !out) return fail(CSL_ERR_INVALID, "compress_kv: null pointer argument");
+  if (m < 1 || m > 65536) return fail(CSL_ERR_INVALID, "compress_kv: m must be in [1, 65536], got %d", m);
+  if (D != 64 && D != 128 && D != 256 && D != 512)
+    return fail(CSL_ERR_UNSUPPORTED, "compress_kv: D must be 64, 128, 256 or 512, got %d", D);
+  if (out_dtype != CSL_DTYPE_F32 && out_dtype != CSL_DTYPE_BF16)
+    return fail(CSL_ERR_UNSUPPORTED, "compress_kv: out_dtype must be F32 or BF16");
+  if (B > kMaxGridY) return fail(CSL_ERR_UNSUPPORTED, "compress_kv: B must be <= %d", kMaxGridY);
+  if (!aligned(kv, 16) || (z && !aligned(z, 16)) || !aligned(out, 16))
+    return fail(CSL_ERR_INVALID, "compress_kv: kv, z and out must be 16-byte aligned");
+  if (B == 0 || max_new_entries == 0) return ok();
+  return hip_status(csl::launch_compress(kv, z, kv_off, ent_off, first_entry, B, D, m, max_new_entries, out,
+                                         out_dtype == CSL_DTYPE_BF16, as_stream(stream)),
+                    "compress_kv launch");
+}
+
+int csl_indexer_scores(const void* q_idx, const float* w, const void* k_idx, int k_dtype, const float* k_scale,
+                       const int64_t* scale_off, int scale_group, const int64_t* ent_off, const int64_t* q_pos, int m,
+                       int B, int T, int HI, int CI, int64_t max_entries, float* scores, int64_t ld, void* stream) {
+  if (B < 0 || T < 0 || max_entries < 0) return fail(CSL_ERR_INVALID, "indexer_scores: negative size");
+  if (!q_idx || !w || !k_idx || !ent_off || !q_pos || !scores)
+    return fail(CSL_ERR_INVALID, "indexer_scores: null pointer argument");
+  if (m < 1) return fail(CSL_ERR_INVALID, "indexer_scores: m must be >= 1");
+  if (k_dtype != CSL_DTYPE_BF16 && k_dtype != CSL_DTYPE_FP8_E4M3)
+    return fail(CSL_ERR_UNSUPPORTED, "indexer_scores: k_dtype must be BF16 or FP8_E4M3");
+  const bool fp8 = k_dtype == CSL_DTYPE_FP8_E4M3;
+  if (fp8 && (!k_scale || !scale_off || scale_group < 1))
+    return fail(CSL_ERR_INVALID, "indexer_scores: fp8 keys need k_scale, scale_off and scale_group >= 1");
+  if (HI != 1 && HI != 2 && HI != 4 && HI != 8 && HI != 16)
+    return fail(CSL_ERR_UNSUPPORTED, "indexer_scores: HI must be 1, 2, 4, 8 or 16, got %d", HI);
+  if (CI != 64) return fail(CSL_ERR_UNSUPPORTED, "indexer_scores: CI must be 64, got %d", CI);
+  if (ld < max_entries) return fail(CSL_ERR_INVALID, "indexer_scores: ld (%lld) < max_entries (%lld)",
+                                    (long long)ld, (long long)max_entries);
+  if (B > kMaxGridY) return fail(CSL_ERR_UNSUPPORTED, "indexer_scores: B must be <= %d", kMaxGridY);
+  if (!aligned(q_idx, 16) || !aligned(k_idx, fp8 ? 8 : 16))
+    return fail(CSL_ERR_INVALID, "indexer_scores: q_idx must be 16-byte and k_idx %d-byte aligned", fp8 ? 8 : 16);
+  if (B == 0 || T == 0 || max_entries == 0) return ok();
+  return hip_status(csl::launch_indexer(q_idx, w, k_idx, fp8, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T,
+                                        HI, max_entries, scores, ld, as_stream(stream)),
+                    "indexer_scores launch");
+}
+
+size_t csl_topk_workspace_bytes(int B, int T, int64_t max_entries, int k) {
+  if (B <= 0 || T <= 0 || max_entries <= 0 || k <= 0) return 0;
+  return csl::topk_workspace_bytes(B, T, max_entries, k);
+}
+
+int csl_topk_select(const float* scores, int64_t ld, const int64_t* ent_off, const int64_t* q_pos, int m, int B,
+                    int T, int k, int64_t max_entries, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  if (B < 0 || T < 0 || max_entries < 0) return fail(CSL_ERR_INVALID, "topk_select: negative size");
+  if (!scores || !ent_off || !q_pos || !idx) return fail(CSL_ERR_INVALID, "topk_select: null pointer argument");
+  if (m < 1) return fail(CSL_ERR_INVALID, "topk_select: m must be >= 1");
+  if (k < 1 || k > csl::topk_max_k())
+    return fail(CSL_ERR_UNSUPPORTED, "topk_select: k must be in [1, %d], got %d", csl::topk_max_k(), k);
+  if (max_entries >= (int64_t)1 << 31) return fail(CSL_ERR_UNSUPPORTED, "topk_select: max_entries must be < 2^31");
+  if (ld < max_entries) return fail(CSL_ERR_INVALID, "topk_select: ld < max_entries");
+  if ((int64_t)B * T > 0x7fffffff) return fail(CSL_ERR_UNSUPPORTED, "topk_select: too many rows");
+  if (B == 0 || T == 0) return ok();
+  const size_t need = csl_topk_workspace_bytes(B, T, max_entries, k);
+  if (need > 0) {
+    if ((int64_t)B * T > kMaxGridY) return fail(CSL_ERR_UNSUPPORTED, "topk_select: long rows need B*T <= %d", kMaxGridY);
+    if (!ws || ws_bytes < need)
+      return fail(CSL_ERR_WORKSPACE, "topk_select: workspace of %zu bytes required, got %zu", need, ws ? ws_bytes : 0);
+    if (!aligned(ws, 16)) return fail(CSL_ERR_INVALID, "topk_select: workspace must be 16-byte aligned");
+  }
+  return hip_status(csl::launch_topk(scores, ld, ent_off, q_pos, m, B, T, k, max_entries, idx, ws, as_stream(stream)),
+                    "topk_select launch");
+}
+
+size_t csl_attn_workspace_bytes(int B, int T, int H, int D, int64_t max_keys) {
+  if (B <= 0 || T <= 0 || H <= 0 || D != 128 || max_keys < 0) return 0;
+  return csl::attn_workspace_bytes(B, T, H, max_keys);
+}
+
+static int check_attn(const char* who, const void* q, const void* ckv, const void* kv, const int64_t* kv_off,
+                      const int64_t* ent_off, const int64_t* q_pos, int n_win, int B, int T, int H, int D, float scale,
+                      const float* out, void* ws, size_t ws_bytes, int64_t max_keys) {
+  if (B < 0 || T < 0 || n_win < 0) return fail(CSL_ERR_INVALID, "%s: negative size", who);
+  if (!q || !ckv || !kv || !kv_off || !ent_off || !q_pos || !out)
+    return fail(CSL_ERR_INVALID, "%s: null pointer argument", who);
+  if (D != 128) return fail(CSL_ERR_UNSUPPORTED, "%s: D must be 128, got %d", who, D);
+  if (H < 16 || H > 128 || H % 16 != 0)
+    return fail(CSL_ERR_UNSUPPORTED, "%s: H must be a multiple of 16 in [16, 128], got %d", who, H);
+  if (!std::isfinite(scale)) return fail(CSL_ERR_INVALID, "%s: scale must be finite", who);
+  if ((int64_t)B * T > kMaxGridY) return fail(CSL_ERR_UNSUPPORTED, "%s: B*T must be <= %d", who, kMaxGridY);
+  if (!aligned(q, 16) || !aligned(ckv, 16) || !aligned(kv, 16) || !aligned(out, 16))
+    return fail(CSL_ERR_INVALID, "%s: q, ckv, kv and out must be 16-byte aligned", who);
+  if (B == 0 || T == 0) return -1;
+  const size_t need = csl_attn_workspace_bytes(B, T, H, D, max_keys);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(CSL_ERR_WORKSPACE, "%s: workspace of %zu bytes required, got %zu", who, need, ws ? ws_bytes : 0);
+  if (need > 0 && !aligned(ws, 16)) return fail(CSL_ERR_INVALID, "%s: workspace must be 16-byte aligned", who);
+  return CSL_OK;
+}
+
+int csl_sparse_attn_decode(const void* q, const void* ckv, const int32_t* idx, int k, const void* kv,
+                           const int64_t* kv_off, const int64_t* ent_off, const int64_t* q_pos, int n_win, int B, int T,
+                           int H, int D, float scale, float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (k < 0) return fail(CSL_ERR_INVALID, "sparse_attn_decode: k must be >= 0");
+  if (k > 0 && !idx) return fail(CSL_ERR_INVALID, "sparse_attn_decode: idx is NULL");
+  const int64_t max_keys = (int64_t)k + n_win;
+  const int st = check_attn("sparse_attn_decode", q, ckv, kv, kv_off, ent_off, q_pos, n_win, B, T, H, D, scale, out, ws,
+                            ws_bytes, max_keys);
+  if (st == -1) return ok();
+  if (st != CSL_OK) return st;
+  return hip_status(csl::launch_attention(true, q, ckv, idx, k, kv, kv_off, ent_off, q_pos, 1, n_win, B, T, H, scale,
+                                          (int64_t)1 << 62, max_keys, out, lse, ws, as_stream(stream)),
+                    "sparse_attn_decode launch");
+}
+
+int csl_hca_attn_decode(const void* q, const void* ckv, const void* kv, const int64_t* kv_off, const int64_t* ent_off,
+                        const int64_t* q_pos, int m, int n_win, int B, int T, int H, int D, float scale,
+                        int64_t max_entries, float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (m < 1) return fail(CSL_ERR_INVALID, "hca_attn_decode: m must be >= 1");
+  if (max_entries < 0) return fail(CSL_ERR_INVALID, "hca_attn_decode: max_entries must be >= 0");
+  const int64_t max_keys = max_entries + n_win;
+  const int st = check_attn("hca_attn_decode", q, ckv, kv, kv_off, ent_off, q_pos, n_win, B, T, H, D, scale, out, ws,
+                            ws_bytes, max_keys);
+  if (st == -1) return ok();
+  if (st != CSL_OK) return st;
+  return hip_status(csl::launch_attention(false, q, ckv, nullptr, 0, kv, kv_off, ent_off, q_pos, m, n_win, B, T, H,
+                                          scale, max_entries, max_keys, out, lse, ws, as_stream(stream)),
+                    "hca_attn_decode launch");
+}
+
+}  // extern "C"

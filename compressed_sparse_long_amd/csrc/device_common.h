@@ -1,0 +1,81 @@
+// Device helpers shared by the gfx950 kernels: bf16 / fp8 widening, rounding, MFMA
+// operand types and wave-level shuffles. CDNA4 wavefronts are 64 lanes wide.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csl {
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;   // MFMA A/B operand, 8 x bf16
+typedef __attribute__((ext_vector_type(4))) float f32x4;      // 16x16 MFMA accumulator
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+// bf16 bit patterns held in 32-bit words: low half = element 2i, high half = element 2i+1.
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN, overflow goes to inf.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// One OCP E4M3FN code -> bf16 bits. Every finite e4m3 value is exact in bf16:
+// normal codes keep their 3 mantissa bits and rebias the exponent (7 -> 127);
+// subnormal codes f * 2^-9 are normalised; S.1111.111 becomes a quiet NaN.
+__device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t b) {
+  uint32_t s = (b & 0x80u) << 8;
+  uint32_t e = (b >> 3) & 0xfu;
+  uint32_t f = b & 0x7u;
+  uint32_t mag;
+  if (e == 0) {
+    // f * 2^-9 for f in 1..7 (0 stays 0): convert through fp32, exact
+    mag = __float_as_uint((float)f * 0.001953125f) >> 16;
+  } else if (e == 15 && f == 7) {
+    mag = 0x7fc0u;
+  } else {
+    mag = ((e + 120u) << 7) | (f << 4);
+  }
+  return s | mag;
+}
+
+// Four e4m3 codes packed in a 32-bit word -> two words of bf16 pairs.
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
+  u32x2 r;
+  r.x = e4m3_to_bf16_bits(w & 0xffu) | (e4m3_to_bf16_bits((w >> 8) & 0xffu) << 16);
+  r.y = e4m3_to_bf16_bits((w >> 16) & 0xffu) | (e4m3_to_bf16_bits(w >> 24) << 16);
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// D = A * B + C for a 16x16 tile with K = 32 (gfx950). Per lane l (g = l / 16):
+//   A: row l % 16, 8 consecutive k-slots 8g..8g+7; B: column l % 16, same k-slots;
+//   C/D: column l % 16, rows 4g..4g+3 (element i of the f32x4 is row 4g+i).
+// The k-slot order only has to agree between A and B.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, kWave); }
+
+// Order-preserving map of an fp32 score to an unsigned key (larger score -> larger key);
+// -0.0 is folded onto +0.0 first so that the two compare equal.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace csl

@@ -1,0 +1,37 @@
+// Internal launchers: one per kernel family. Host-side validation lives in api.cpp; these
+// only pick template instances and grid shapes and enqueue work on the given stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csl {
+
+hipError_t launch_compress(const void* kv, const void* z, const int64_t* kv_off, const int64_t* ent_off,
+                           const int64_t* first_entry, int B, int D, int m, int64_t max_new_entries,
+                           void* out, bool out_bf16, hipStream_t stream);
+
+hipError_t launch_indexer(const void* qI, const float* w, const void* kI, bool fp8, const float* k_scale,
+                          const int64_t* scale_off, int scale_group, const int64_t* ent_off,
+                          const int64_t* q_pos, int m, int B, int T, int HI, int64_t max_entries,
+                          float* scores, int64_t ld, hipStream_t stream);
+
+bool topk_uses_row_kernel(int64_t max_entries);
+size_t topk_workspace_bytes(int B, int T, int64_t max_entries, int k);
+int topk_max_k();
+hipError_t launch_topk(const float* scores, int64_t ld, const int64_t* ent_off, const int64_t* q_pos, int m,
+                       int B, int T, int k, int64_t max_entries, int32_t* idx, void* ws, hipStream_t stream);
+
+struct AttnPlan {
+  int nsplit;
+  int keys_per_split;
+};
+AttnPlan attn_plan(int B, int T, int64_t max_keys);
+size_t attn_workspace_bytes(int B, int T, int H, int64_t max_keys);
+hipError_t launch_attention(bool sparse, const void* q, const void* ckv, const int32_t* idx, int k, const void* kv,
+                            const int64_t* kv_off, const int64_t* ent_off, const int64_t* q_pos, int m, int n_win,
+                            int B, int T, int H, float scale, int64_t max_entries, int64_t max_keys, float* out,
+                            float* lse, void* ws, hipStream_t stream);
+
+}  // namespace csl

@@ -1,0 +1,180 @@
+/*
+ * csl.h -- C ABI of the MI355X (gfx950) hybrid compressed-attention library.
+ *
+ * One attention layer of the method described on these pages:
+ *   [P1] "1M Context != Lossless Long Memory: What DeepSeek-V4 Reveals About the
+ *        Engineering Tradeoffs" (wiki.gxlh.xyz/doc/1210)
+ *   [P2] "DeepSeek-V4: Million-Token Context via Hybrid Compressed Attention"
+ *        (zhongzhoutan-coder.github.io, DeepSeek-V4 training notes)
+ *   [P3] "DeepSeek-V4 的暗线之一：分层记忆比输入框更关键" (blog.xieydd.top)
+ *   [P5] "DeepSeek-V4 technical report" breakdown (deconstructedpapers.com)
+ *
+ * CSA (compressed sparse attention): compress_kv (m = 4) -> indexer_scores -> topk_select
+ *   -> sparse_attn_decode.  HCA (heavily compressed attention): compress_kv (m = 128) ->
+ *   hca_attn_decode.
+ *
+ * Conventions shared by every call
+ *   - Every tensor argument is a caller-owned DEVICE pointer to contiguous row-major data.
+ *     bf16 tensors are passed as raw 16-bit words. The library never allocates, frees,
+ *     synchronises, or keeps a pointer after the call returns; work is enqueued on
+ *     `stream` (a hipStream_t; NULL is the default stream). Buffers must stay alive until
+ *     the stream has passed the work.
+ *   - Ragged batches are packed: sequence b owns raw rows [kv_off[b], kv_off[b+1]) of the
+ *     raw K=V array and compressed entries [ent_off[b], ent_off[b+1]) of the compressed
+ *     array. kv_off / ent_off are DEVICE int64 arrays of B+1 non-decreasing values.
+ *     Query row t of sequence b sits at absolute position p = q_pos[b] + t (q_pos is a
+ *     DEVICE int64 array of B values).
+ *   - Visibility: a query at position p sees compressed entries s < floor(p / m) of its
+ *     sequence (never the block it falls in, [P1] section 6.1) and the raw window of the
+ *     n_win newest rows j with j <= p and j < N_b ([P1] section 6; [P2] "KV Cache
+ *     Management"). Decode uses p = N_b: all floor(N_b/m) entries plus rows
+ *     [N_b - n_win, N_b).
+ *   - Host scalars are validated before anything is enqueued; a bad value returns
+ *     CSL_ERR_INVALID or CSL_ERR_UNSUPPORTED and enqueues nothing. Device-resident data
+ *     (offsets, positions, selected ids, scales) are preconditions and are not checked,
+ *     except that selected ids outside [0, E_b) are treated as padding.
+ *   - Every call returns a csl_status. csl_last_error() returns a thread-local message
+ *     describing the last failure on the calling thread.
+ *   - The library holds no global state; calls on different streams may run concurrently
+ *     as long as they do not share output or workspace buffers.
+ */
+#ifndef CSL_H
+#define CSL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CSL_OK = 0,
+  CSL_ERR_INVALID = 1,     /* null pointer, negative size, inconsistent arguments       */
+  CSL_ERR_UNSUPPORTED = 2, /* a shape or dtype outside what the kernels implement        */
+  CSL_ERR_WORKSPACE = 3,   /* workspace pointer missing or smaller than required         */
+  CSL_ERR_HIP = 4          /* the HIP runtime reported an error at launch                */
+} csl_status;
+
+typedef enum {
+  CSL_DTYPE_BF16 = 0,
+  CSL_DTYPE_F32 = 1,
+  CSL_DTYPE_FP8_E4M3 = 2 /* OCP E4M3FN: bias 7, no infinities, max 448, S.1111.111 = NaN */
+} csl_dtype;
+
+/* Message for the last failed call on this thread ("" if none). Never NULL. */
+const char* csl_last_error(void);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int csl_version(void);
+
+/*
+ * compress_kv -- softmax-weighted chunk pooling ([P3] section 3, the compressed KV entry;
+ * [P2] "Deep Dive", CSA step 2 and HCA "How it works"; [P1] section 4.1).
+ *
+ *   out[ent_off[b] + i, d] = sum_{r<m} w_r[d] * kv[kv_off[b] + m*i + r, d],
+ *   w[:, d] = softmax over the m rows of z[kv_off[b] + m*i + r, d]   (uniform 1/m if z NULL)
+ *
+ * for every sequence b and entry i with first_entry[b] <= i < E_b, E_b = floor(N_b / m),
+ * N_b = kv_off[b+1] - kv_off[b], and at most max_new_entries entries per sequence
+ * (i < first_entry[b] + max_new_entries). first_entry NULL means 0 (bulk compression of a
+ * whole prefix); first_entry[b] = E_b - 1 recompresses only the newest complete chunk, as
+ * a decode step does. The trailing N_b mod m rows are not pooled.
+ *
+ *   kv, z   bf16 [rows, D] (z nullable)        D in {64, 128, 256, 512}; m in [1, 65536]
+ *   out     [*, D] of out_dtype (CSL_DTYPE_F32 or CSL_DTYPE_BF16, bf16 rounded to nearest
+ *           even); out rows other than the ones listed above are not written.
+ * Arithmetic: fp32, exponentials in base 2 with a log2(e) prescale.
+ */
+int csl_compress_kv(const void* kv, const void* z, const int64_t* kv_off, const int64_t* ent_off,
+                    const int64_t* first_entry, int B, int D, int m, int64_t max_new_entries,
+                    void* out, int out_dtype, void* stream);
+
+/*
+ * indexer_scores -- Lightning-indexer scores ([P5], the indexer score formula;
+ * [P2] "Deep Dive", CSA Lightning Indexer; [P1] section 4.2):
+ *
+ *   scores[b, t, s] = sum_{j<HI} w[b, t, j] * max(0, sum_{c<CI} q_idx[b, t, j, c] * key(s, c))
+ *
+ * for s < n(b, t) = min(floor(p / m), E_b, max_entries), E_b = ent_off[b+1] - ent_off[b].
+ * key(s, c) = k_idx[ent_off[b] + s, c] for bf16 keys; for fp8 keys it is
+ * decode(k_idx[ent_off[b] + s, c]) * k_scale[scale_off[b] + s / scale_group].
+ * No 1/sqrt(CI) factor is applied. scores[b, t, s] for s >= n(b, t) is not written.
+ *
+ *   q_idx   bf16 [B, T, HI, CI]     HI in {1, 2, 4, 8, 16}; CI == 64
+ *   w       fp32 [B, T, HI]
+ *   k_idx   [E_tot, CI] of k_dtype (CSL_DTYPE_BF16 or CSL_DTYPE_FP8_E4M3)
+ *   k_scale fp32, scale_off int64 [B+1]: required for fp8 keys, ignored (may be NULL) else;
+ *           scales must be positive. scale_group >= 1.
+ *   scores  fp32 [B, T, ld], ld >= max_entries
+ * Arithmetic: bf16 MFMA products with fp32 accumulation; fp8 codes are widened to bf16
+ * exactly before the product and the group scale multiplies the fp32 dot.
+ */
+int csl_indexer_scores(const void* q_idx, const float* w, const void* k_idx, int k_dtype,
+                       const float* k_scale, const int64_t* scale_off, int scale_group,
+                       const int64_t* ent_off, const int64_t* q_pos, int m, int B, int T, int HI,
+                       int CI, int64_t max_entries, float* scores, int64_t ld, void* stream);
+
+/*
+ * topk_select -- top-k compressed entries per query row ([P2] "Deep Dive", CSA top-k
+ * selection; [P2] "Putting It Together"; [P1] section 4.1).
+ *
+ * For each row (b, t) with n = min(floor(p / m), E_b, max_entries) scores:
+ *   idx[b, t, :] = the ids of the min(k, n) largest scores[b, t, 0:n], ordered by
+ *   (score descending, id ascending) for the choice -- so the lower id wins a tie --
+ *   then written in ASCENDING id order, padded with -1 up to k.
+ * -0.0 and +0.0 compare equal. NaN scores are outside the contract.
+ *
+ *   scores fp32 [B, T, ld]; idx int32 [B, T, k]; 1 <= k <= 4096; max_entries < 2^31.
+ *   ws: device workspace of at least csl_topk_workspace_bytes(B, T, max_entries, k)
+ *   bytes (may be NULL when that is 0). Its contents must be ZERO before the first call
+ *   that uses it (for example a zero-filled allocation); every completed call leaves it
+ *   zero again, so it can be reused by the next call on the same stream.
+ * Integer work only: scores are compared through an order-preserving 32-bit key.
+ */
+size_t csl_topk_workspace_bytes(int B, int T, int64_t max_entries, int k);
+int csl_topk_select(const float* scores, int64_t ld, const int64_t* ent_off, const int64_t* q_pos,
+                    int m, int B, int T, int k, int64_t max_entries, int32_t* idx, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/*
+ * sparse_attn_decode -- CSA core attention ([P2] "Deep Dive", CSA core attention with
+ * shared-KV MQA and the sliding-window branch; [P2] "Putting It Together"; [P5] the
+ * attention formula):
+ *
+ *   X(b, t) = { ckv[ent_off[b] + idx[b,t,v]] : 0 <= idx[b,t,v] < E_b } followed by the raw
+ *             window rows kv[kv_off[b] + j], j in [max(0, hi - n_win + 1), hi],
+ *             hi = min(p, N_b - 1)
+ *   out[b, t, h] = sum_{x in X} softmax_x(scale * q[b,t,h] . x) x   (K = V, one softmax)
+ *   lse[b, t, h] = log sum_{x in X} exp(scale * q[b,t,h] . x)        (natural log)
+ * An empty X gives out = 0 and lse = -inf. No de-duplication between the two lanes.
+ *
+ *   q bf16 [B, T, H, D]; ckv bf16 [E_tot, D]; idx int32 [B, T, k]; kv bf16 [N_tot, D]
+ *   out fp32 [B, T, H, D]; lse fp32 [B, T, H] (nullable)
+ *   D == 128; H a multiple of 16, <= 128; k >= 0; n_win >= 0.
+ *   ws: at least csl_attn_workspace_bytes(B, T, H, D, k + n_win) bytes (contents free).
+ * Arithmetic: bf16 MFMA operands (probabilities rounded to bf16 for the value product),
+ * fp32 accumulation, fp32 online softmax in base 2, log-sum-exp merge of split partials.
+ */
+size_t csl_attn_workspace_bytes(int B, int T, int H, int D, int64_t max_keys);
+int csl_sparse_attn_decode(const void* q, const void* ckv, const int32_t* idx, int k,
+                           const void* kv, const int64_t* kv_off, const int64_t* ent_off,
+                           const int64_t* q_pos, int n_win, int B, int T, int H, int D, float scale,
+                           float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * hca_attn_decode -- HCA dense attention ([P1] section 5.1; [P2] "Heavily Compressed
+ * Attention"): as sparse_attn_decode, with the compressed part of X being every visible
+ * entry s < min(floor(p / m), E_b, max_entries) instead of a selected list.
+ *   ws: at least csl_attn_workspace_bytes(B, T, H, D, max_entries + n_win) bytes.
+ */
+int csl_hca_attn_decode(const void* q, const void* ckv, const void* kv, const int64_t* kv_off,
+                        const int64_t* ent_off, const int64_t* q_pos, int m, int n_win, int B,
+                        int T, int H, int D, float scale, int64_t max_entries, float* out,
+                        float* lse, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSL_H */

@@ -43,8 +43,9 @@ def index_keys_f64(kI, k_scale=None, scale_off=None, ent_off=None, group: int = 
     ent_off = [int(x) for x in ent_off]
     scale_off = [int(x) for x in scale_off]
     for b in range(len(ent_off) - 1):
-        for s in range(ent_off[b + 1] - ent_off[b]):
-            out[ent_off[b] + s] = vals[ent_off[b] + s] * sc[scale_off[b] + s // group]
+        e0, e1 = ent_off[b], ent_off[b + 1]
+        grp = scale_off[b] + np.arange(e1 - e0) // group     # key s of sequence b uses scale s // group
+        out[e0:e1] = vals[e0:e1] * sc[grp][:, None]
     return out
 
 

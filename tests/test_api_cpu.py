@@ -1,0 +1,130 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol, and rejects bad
+host arguments before enqueuing anything (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csl.h")
+LIB = os.path.join(ROOT, "compressed_sparse_long_amd", "libcsl.so")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from compressed_sparse_long_amd import build as b
+        b.build()
+    return ctypes.CDLL(LIB)
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(csl_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_five_stages():
+    syms = declared_symbols()
+    for s in ("csl_compress_kv", "csl_indexer_scores", "csl_topk_select", "csl_sparse_attn_decode",
+              "csl_hca_attn_decode"):
+        assert s in syms
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for s in declared_symbols():
+        assert hasattr(lib, s), s
+    import compressed_sparse_long_amd as csl
+    assert sorted(csl.EXPORTS) == declared_symbols()
+    assert csl.version() == 100
+
+
+P = ctypes.c_void_p
+FAKE = P(1 << 20)  # never dereferenced: every call below fails host validation first
+
+
+def _err(lib):
+    lib.csl_last_error.restype = ctypes.c_char_p
+    return lib.csl_last_error().decode()
+
+
+def test_compress_validation(lib):
+    f = lib.csl_compress_kv
+    f.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64, P, ctypes.c_int, P]
+    assert f(None, None, FAKE, FAKE, None, 1, 128, 4, 10, FAKE, 1, None) == 1
+    assert "null" in _err(lib)
+    assert f(FAKE, None, FAKE, FAKE, None, 1, 96, 4, 10, FAKE, 1, None) == 2
+    assert f(FAKE, None, FAKE, FAKE, None, 1, 128, 0, 10, FAKE, 1, None) == 1
+    assert f(FAKE, None, FAKE, FAKE, None, 1, 128, 4, 10, FAKE, 2, None) == 2
+    assert f(FAKE, None, FAKE, FAKE, None, -1, 128, 4, 10, FAKE, 1, None) == 1
+    assert f(P((1 << 20) + 2), None, FAKE, FAKE, None, 1, 128, 4, 10, FAKE, 1, None) == 1
+    assert "aligned" in _err(lib)
+    # nothing to do is a success without touching the device
+    assert f(FAKE, None, FAKE, FAKE, None, 0, 128, 4, 10, FAKE, 1, None) == 0
+    assert _err(lib) == ""
+
+
+def test_indexer_validation(lib):
+    f = lib.csl_indexer_scores
+    I, L = ctypes.c_int, ctypes.c_int64
+    f.argtypes = [P, P, P, I, P, P, I, P, P, I, I, I, I, I, L, P, L, P]
+    args = [FAKE, FAKE, FAKE, 0, None, None, 64, FAKE, FAKE, 4, 1, 1, 8, 64, 1000, FAKE, 1000, None]
+    bad = list(args); bad[12] = 3
+    assert f(*bad) == 2                       # HI
+    bad = list(args); bad[13] = 128
+    assert f(*bad) == 2                       # CI
+    bad = list(args); bad[3] = 2
+    assert f(*bad) == 1                       # fp8 without scales
+    bad = list(args); bad[16] = 999
+    assert f(*bad) == 1                       # ld < max_entries
+    bad = list(args); bad[1] = None
+    assert f(*bad) == 1
+    ok0 = list(args); ok0[11] = 0
+    assert f(*ok0) == 0                       # T = 0: nothing to do
+
+
+def test_topk_validation_and_workspace(lib):
+    ws = lib.csl_topk_workspace_bytes
+    ws.restype = ctypes.c_size_t
+    ws.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int]
+    assert ws(1, 1, 1024, 64) == 0            # short rows: one workgroup per row, no workspace
+    assert ws(1, 8192, 34816, 512) == 0
+    big = ws(4, 1, 262144, 1024)
+    assert big > 4 * (2048 * 4 + 1024 * 4)
+    f = lib.csl_topk_select
+    I, L = ctypes.c_int, ctypes.c_int64
+    f.argtypes = [P, L, P, P, I, I, I, I, L, P, P, ctypes.c_size_t, P]
+    assert f(FAKE, 262144, FAKE, FAKE, 4, 4, 1, 1024, 262144, FAKE, FAKE, big - 1, None) == 3
+    assert "workspace" in _err(lib)
+    assert f(FAKE, 262144, FAKE, FAKE, 4, 4, 1, 1024, 262144, FAKE, None, 0, None) == 3
+    assert f(FAKE, 1024, FAKE, FAKE, 4, 1, 1, 0, 1024, FAKE, None, 0, None) == 2      # k = 0
+    assert f(FAKE, 1024, FAKE, FAKE, 4, 1, 1, 5000, 1024, FAKE, None, 0, None) == 2   # k too large
+    assert f(FAKE, 100, FAKE, FAKE, 4, 1, 1, 64, 1024, FAKE, None, 0, None) == 1      # ld < max_entries
+
+
+def test_attention_validation_and_workspace(lib):
+    ws = lib.csl_attn_workspace_bytes
+    ws.restype = ctypes.c_size_t
+    ws.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64]
+    assert ws(1, 8192, 64, 128, 640) == 0     # many rows: one split per row
+    w3 = ws(4, 1, 64, 128, 1024 + 128)
+    assert w3 > 0 and w3 % (4 * 64 * 129 * 4) == 0
+    f = lib.csl_sparse_attn_decode
+    I = ctypes.c_int
+    f.argtypes = [P, P, P, I, P, P, P, P, I, I, I, I, I, ctypes.c_float, P, P, P, ctypes.c_size_t, P]
+    base = [FAKE, FAKE, FAKE, 1024, FAKE, FAKE, FAKE, FAKE, 128, 4, 1, 64, 128, 0.088, FAKE, None, FAKE, w3, None]
+    bad = list(base); bad[12] = 64
+    assert f(*bad) == 2                       # D
+    bad = list(base); bad[11] = 24
+    assert f(*bad) == 2                       # H not a multiple of 16
+    bad = list(base); bad[17] = w3 - 4
+    assert f(*bad) == 3
+    bad = list(base); bad[2] = None
+    assert f(*bad) == 1
+    bad = list(base); bad[13] = float("nan")
+    assert f(*bad) == 1
+    g = lib.csl_hca_attn_decode
+    L = ctypes.c_int64
+    g.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, ctypes.c_float, L, P, P, P, ctypes.c_size_t, P]
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 128, 8, 1, 64, 128, 0.088, 1024, FAKE, None, FAKE, 0, None) == 1
