@@ -9,9 +9,11 @@ timed region. The compressed cache and the indexer keys are kept in several inde
 copies that consecutive steps rotate through, so every step streams from HBM rather than
 from the last-level cache.
 
-Prints one JSON line: queries/s, ms per step, the indexer kernel's achieved HBM bandwidth
-against the 8 TB/s peak (measured with HIP events around each launch inside the timed
-region), and the fp64 CPU oracle's rate on a bounded sample of the same workload.
+Each step is captured once per rotated copy as a HIP graph (the four launches back to back)
+and the timed region replays K steps. Prints one JSON line: queries/s, ms per step, the
+indexer kernel's achieved HBM bandwidth against the 8 TB/s peak (HIP events around 100
+back-to-back launches), and the fp64 CPU oracle's rate on a bounded sample of the same
+workload.
 
   python bench.py [--steps K] [--warmup W] [--copies R] [--no-cpu-baseline]
   python bench.py --copy-calibration     # plain device copy of known size (for counters)
@@ -159,29 +161,53 @@ def main():
     lane = inp.lanes[0].lane
     B, T, E, HI, CI, H, D, k, W = lane.B, lane.T, lane.entries[0], lane.HI, lane.CI, lane.H, lane.D, lane.k, lane.W
 
+    R = len(cl.ckv_copies)
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        return g
+
+    def time_graphs(graphs, reps, per_replay=1):
+        """Average device time per unit of `reps` back-to-back replays (round-robin)."""
+        for i in range(min(reps, 2 * len(graphs))):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(reps):
+            graphs[i % len(graphs)].replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / (reps * per_replay) * 1e3  # microseconds
+
+    # one captured graph per rotated input copy: the whole decode step
+    steps = [capture(lambda r=r: cl.step(r)) for r in range(R)]
     for i in range(args.warmup):
-        cl.step(i)
+        steps[i % R].replay()
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for i in range(K):
-        cl.compress_new(i)
-        ev[i][0].record()
-        cl.index(i)
-        ev[i][1].record()
-        cl.select()
-        cl.attend(i)
+        steps[i % R].replay()
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_step = total_ms / K
-    idx_us = sum(a.elapsed_time(b) for a, b in ev) / K * 1e3
     queries = B * T * K
     value = queries / (total_ms / 1e3)
+
+    # the dominant kernel (indexer): 100 back-to-back launches over the rotated copies per
+    # replay, timed with events on the stream the kernels run on
+    n_idx = 25 * R
+    idx_graph = capture(lambda: [cl.index(i % R) for i in range(n_idx)])
+    idx_us = time_graphs([idx_graph], 4, per_replay=n_idx)
+    cl.select()  # consume the candidate lists the timing loop left behind
+    torch.cuda.synchronize()
 
     # algorithmic bytes (per step, and per indexer launch)
     idx_bytes = B * (E * CI * 2 + E * 4 + HI * CI * 2 + HI * 4)                # keys + scores + q + w
@@ -215,30 +241,21 @@ def main():
     }
 
     if not args.no_stages:
-        # per-stage breakdown in a separate pass (not part of the timed region)
-        S = 50
-        names = ["compress_new", "indexer", "topk", "attention"]
-        evs = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(S)]
-               for n in names}
-        fns = {"compress_new": cl.compress_new, "indexer": cl.index, "topk": lambda i: cl.select(),
-               "attention": cl.attend}
+        # per-stage device time from graphs of single stages (top-k is timed with its indexer)
+        g_comp = [capture(lambda r=r: cl.compress_new(r)) for r in range(R)]
+        g_idx = [capture(lambda r=r: cl.index(r)) for r in range(R)]
+        g_idx_topk = [capture(lambda r=r: (cl.index(r), cl.select())) for r in range(R)]
+        g_attn = [capture(lambda r=r: cl.attend(r)) for r in range(R)]
+        t_idx = time_graphs(g_idx, 200)
+        cl.select()
         torch.cuda.synchronize()
-        for i in range(S):
-            for n in names:
-                evs[n][i][0].record()
-                fns[n](i)
-                evs[n][i][1].record()
-        torch.cuda.synchronize()
-        result["stages_us"] = {n: round(sum(a.elapsed_time(b) for a, b in evs[n]) / S * 1e3, 2) for n in names}
+        t_it = time_graphs(g_idx_topk, 200)
+        result["stages_us"] = {"compress_new": round(time_graphs(g_comp, 200), 2), "indexer": round(t_idx, 2),
+                               "topk": round(t_it - t_idx, 2), "attention": round(time_graphs(g_attn, 200), 2)}
         # bulk compression of one whole 4 x 1M-token context (2 GiB read)
-        ce = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(3)]
-        for i in range(3):
-            ce[i][0].record()
-            lanes.compress_kv(cl.kv, cl.z, cl.kv_off, cl.ent_off, cl.m, cl.ckv_copies[i % len(cl.ckv_copies)],
-                              max_new_entries=cl.max_entries)
-            ce[i][1].record()
-        torch.cuda.synchronize()
-        cus = sum(a.elapsed_time(b) for a, b in ce) / 3 * 1e3
+        g_bulk = [capture(lambda r=r: lanes.compress_kv(cl.kv, cl.z, cl.kv_off, cl.ent_off, cl.m, cl.ckv_copies[r],
+                                                        max_new_entries=cl.max_entries)) for r in range(R)]
+        cus = time_graphs(g_bulk, 8)
         cbytes = sum(lane.lengths) * D * 2 * 2 + sum(lane.entries) * D * 2
         result["compress_bulk"] = {"us": round(cus, 1), "bytes": cbytes, "GB_s": round(cbytes / (cus * 1e-6) / 1e9, 1),
                                    "frac": round(cbytes / (cus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}

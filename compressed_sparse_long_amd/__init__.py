@@ -43,9 +43,9 @@ def _load() -> ctypes.CDLL:
         "csl_last_error": (ctypes.c_char_p, []),
         "csl_version": (I, []),
         "csl_compress_kv": (I, [P, P, P, P, P, I, I, I, L, P, I, P]),
-        "csl_indexer_scores": (I, [P, P, P, I, P, P, I, P, P, I, I, I, I, I, L, P, L, P]),
+        "csl_indexer_scores": (I, [P, P, P, I, P, P, I, P, P, I, I, I, I, I, L, P, L, P, S, I, P]),
         "csl_topk_workspace_bytes": (S, [I, I, L, I]),
-        "csl_topk_select": (I, [P, L, P, P, I, I, I, I, L, P, P, S, P]),
+        "csl_topk_select": (I, [P, L, P, P, I, I, I, I, L, P, P, S, I, P]),
         "csl_attn_workspace_bytes": (S, [I, I, I, I, L]),
         "csl_sparse_attn_decode": (I, [P, P, P, I, P, P, P, P, I, I, I, I, I, F, P, P, P, S, P]),
         "csl_hca_attn_decode": (I, [P, P, P, P, P, P, I, I, I, I, I, I, F, L, P, P, P, S, P]),
@@ -112,8 +112,9 @@ def compress_kv(kv, z, kv_off, ent_off, m: int, out, first_entry=None, max_new_e
 
 
 def indexer_scores(qI, w, kI, ent_off, q_pos, m: int, scores, max_entries: int | None = None, k_scale=None,
-                   scale_off=None, scale_group: int = 64, stream=None):
-    """Lightning-indexer scores into scores fp32 [B, T, ld]; see csl.h."""
+                   scale_off=None, scale_group: int = 64, topk_ws=None, topk_k: int = 0, stream=None):
+    """Lightning-indexer scores into scores fp32 [B, T, ld]; with ``topk_ws``/``topk_k`` it also
+    leaves top-k candidate lists for ``topk_select(..., prepared=True)``; see csl.h."""
     B, T, HI, CI = qI.shape
     if kI.dtype == torch.bfloat16:
         kd = BF16
@@ -128,6 +129,7 @@ def indexer_scores(qI, w, kI, ent_off, q_pos, m: int, scores, max_entries: int |
         _ptr(qI, "qI", _BF16), _ptr(w, "w", _F32), _ptr(kI, "kI"), kd, _ptr(k_scale, "k_scale", _F32),
         _ptr(scale_off, "scale_off", _I64), int(scale_group), _ptr(ent_off, "ent_off", _I64),
         _ptr(q_pos, "q_pos", _I64), int(m), B, T, HI, CI, int(max_entries), _ptr(scores, "scores", _F32), ld,
+        _ptr(topk_ws, "topk_ws"), 0 if topk_ws is None else topk_ws.numel() * topk_ws.element_size(), int(topk_k),
         _stream(stream)))
     return scores
 
@@ -136,7 +138,8 @@ def topk_workspace_bytes(B: int, T: int, max_entries: int, k: int) -> int:
     return int(_lib.csl_topk_workspace_bytes(B, T, max_entries, k))
 
 
-def topk_select(scores, ent_off, q_pos, m: int, k: int, idx, ws=None, max_entries: int | None = None, stream=None):
+def topk_select(scores, ent_off, q_pos, m: int, k: int, idx, ws=None, max_entries: int | None = None,
+                prepared: bool = False, stream=None):
     """Top-k ids per row into idx int32 [B, T, k] (ascending, -1 padded). ``ws`` must be a
     zero-initialised uint8 device tensor reused across calls; a fresh one is made if None."""
     B, T, ld = scores.shape
@@ -148,7 +151,8 @@ def topk_select(scores, ent_off, q_pos, m: int, k: int, idx, ws=None, max_entrie
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(_lib.csl_topk_select(
         _ptr(scores, "scores", _F32), ld, _ptr(ent_off, "ent_off", _I64), _ptr(q_pos, "q_pos", _I64), int(m), B, T,
-        int(k), int(max_entries), _ptr(idx, "idx", (torch.int32,)), _ptr(ws, "ws"), ws_bytes, _stream(stream)))
+        int(k), int(max_entries), _ptr(idx, "idx", (torch.int32,)), _ptr(ws, "ws"), ws_bytes, int(bool(prepared)),
+        _stream(stream)))
     return idx
 
 

@@ -69,7 +69,8 @@ int csl_compress_kv(const void* kv, const void* z, const int64_t* kv_off, const 
 
 int csl_indexer_scores(const void* q_idx, const float* w, const void* k_idx, int k_dtype, const float* k_scale,
                        const int64_t* scale_off, int scale_group, const int64_t* ent_off, const int64_t* q_pos, int m,
-                       int B, int T, int HI, int CI, int64_t max_entries, float* scores, int64_t ld, void* stream) {
+                       int B, int T, int HI, int CI, int64_t max_entries, float* scores, int64_t ld, void* topk_ws,
+                       size_t topk_ws_bytes, int topk_k, void* stream) {
   if (B < 0 || T < 0 || max_entries < 0) return fail(CSL_ERR_INVALID, "indexer_scores: negative size");
   if (!q_idx || !w || !k_idx || !ent_off || !q_pos || !scores)
     return fail(CSL_ERR_INVALID, "indexer_scores: null pointer argument");
@@ -87,9 +88,19 @@ int csl_indexer_scores(const void* q_idx, const float* w, const void* k_idx, int
   if (B > kMaxGridY) return fail(CSL_ERR_UNSUPPORTED, "indexer_scores: B must be <= %d", kMaxGridY);
   if (!aligned(q_idx, 16) || !aligned(k_idx, fp8 ? 8 : 16))
     return fail(CSL_ERR_INVALID, "indexer_scores: q_idx must be 16-byte and k_idx %d-byte aligned", fp8 ? 8 : 16);
+  if (topk_ws) {
+    if (topk_k < 1 || topk_k > csl::topk_max_k())
+      return fail(CSL_ERR_UNSUPPORTED, "indexer_scores: topk_k must be in [1, %d], got %d", csl::topk_max_k(), topk_k);
+    const size_t need = csl_topk_workspace_bytes(B, T, max_entries, topk_k);
+    if (topk_ws_bytes < need)
+      return fail(CSL_ERR_WORKSPACE, "indexer_scores: top-k workspace of %zu bytes required, got %zu", need,
+                  topk_ws_bytes);
+    if (!aligned(topk_ws, 16)) return fail(CSL_ERR_INVALID, "indexer_scores: topk_ws must be 16-byte aligned");
+    if (need == 0) topk_ws = nullptr;  // short rows: the selection needs no candidate lists
+  }
   if (B == 0 || T == 0 || max_entries == 0) return ok();
   return hip_status(csl::launch_indexer(q_idx, w, k_idx, fp8, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T,
-                                        HI, max_entries, scores, ld, as_stream(stream)),
+                                        HI, max_entries, scores, ld, topk_ws, topk_k, as_stream(stream)),
                     "indexer_scores launch");
 }
 
@@ -99,13 +110,15 @@ size_t csl_topk_workspace_bytes(int B, int T, int64_t max_entries, int k) {
 }
 
 int csl_topk_select(const float* scores, int64_t ld, const int64_t* ent_off, const int64_t* q_pos, int m, int B,
-                    int T, int k, int64_t max_entries, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+                    int T, int k, int64_t max_entries, int32_t* idx, void* ws, size_t ws_bytes, int prepared,
+                    void* stream) {
   if (B < 0 || T < 0 || max_entries < 0) return fail(CSL_ERR_INVALID, "topk_select: negative size");
   if (!scores || !ent_off || !q_pos || !idx) return fail(CSL_ERR_INVALID, "topk_select: null pointer argument");
   if (m < 1) return fail(CSL_ERR_INVALID, "topk_select: m must be >= 1");
   if (k < 1 || k > csl::topk_max_k())
     return fail(CSL_ERR_UNSUPPORTED, "topk_select: k must be in [1, %d], got %d", csl::topk_max_k(), k);
-  if (max_entries >= (int64_t)1 << 31) return fail(CSL_ERR_UNSUPPORTED, "topk_select: max_entries must be < 2^31");
+  if (max_entries > csl::topk_max_entries())
+    return fail(CSL_ERR_UNSUPPORTED, "topk_select: max_entries must be <= %lld", (long long)csl::topk_max_entries());
   if (ld < max_entries) return fail(CSL_ERR_INVALID, "topk_select: ld < max_entries");
   if ((int64_t)B * T > 0x7fffffff) return fail(CSL_ERR_UNSUPPORTED, "topk_select: too many rows");
   if (B == 0 || T == 0) return ok();
@@ -116,7 +129,9 @@ int csl_topk_select(const float* scores, int64_t ld, const int64_t* ent_off, con
       return fail(CSL_ERR_WORKSPACE, "topk_select: workspace of %zu bytes required, got %zu", need, ws ? ws_bytes : 0);
     if (!aligned(ws, 16)) return fail(CSL_ERR_INVALID, "topk_select: workspace must be 16-byte aligned");
   }
-  return hip_status(csl::launch_topk(scores, ld, ent_off, q_pos, m, B, T, k, max_entries, idx, ws, as_stream(stream)),
+  const bool use_lists = prepared != 0 && csl::indexer_prepares_topk(ws, T, max_entries);
+  return hip_status(csl::launch_topk(scores, ld, ent_off, q_pos, m, B, T, k, max_entries, idx, ws, use_lists,
+                                     as_stream(stream)),
                     "topk_select launch");
 }
 

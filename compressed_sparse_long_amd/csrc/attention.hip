@@ -67,6 +67,7 @@ __global__ __launch_bounds__(NHG * 64) void attn_kernel(
   __shared__ __align__(16) uint16_t Ks[kKT * kKsStride];
   __shared__ __align__(16) uint16_t Vt[kD * kVtStride];
   __shared__ const uint16_t* rowp[kKT];
+  __shared__ uint64_t tile_valid;  // bit v: slot v of the current tile holds a key
 
   const int split = blockIdx.x;
   const int row = blockIdx.y;
@@ -78,10 +79,13 @@ __global__ __launch_bounds__(NHG * 64) void attn_kernel(
   const int g = lane / 16;
   const int c = lane % 16;
 
+  const int64_t k_lo = (int64_t)split * keys_per_split;
+  // the first tile's selected ids do not depend on the row geometry: load them right away
+  int32_t first_id = -1;
+  if (SPARSE && tid < kKT && k_lo + tid < k) first_id = idx[(int64_t)row * k + k_lo + tid];
   const RowGeom geo = row_geom(kv_off, ent_off, q_pos, b, t, m, n_win, max_entries);
   const int64_t n_comp = SPARSE ? (int64_t)k : geo.nvis;  // compressed slots in the list
   const int64_t L = n_comp + geo.win_cnt;
-  const int64_t k_lo = (int64_t)split * keys_per_split;
   const int64_t k_hi = (k_lo + keys_per_split < L) ? k_lo + keys_per_split : L;
 
   // queries of this wave's 16 heads as MFMA B operands (d-slots 8g..8g+7 of each 32-chunk)
@@ -99,12 +103,14 @@ __global__ __launch_bounds__(NHG * 64) void attn_kernel(
 
   for (int64_t t0 = k_lo; t0 < k_hi; t0 += kKT) {
     // ---- resolve the 64 slots of this tile to row pointers (nullptr = masked) ----
-    for (int v = tid; v < kKT; v += NT) {
+    if (tid < kKT) {  // kKT slots, one per thread of the first wave
+      const int v = tid;
       const int64_t slot = t0 + v;
       const uint16_t* p = nullptr;
       if (slot < k_hi) {
         if (slot < n_comp) {
-          int64_t id = SPARSE ? (int64_t)idx[(int64_t)row * k + slot] : slot;
+          int64_t id = slot;
+          if (SPARSE) id = (t0 == k_lo) ? (int64_t)first_id : (int64_t)idx[(int64_t)row * k + slot];
           if (id >= 0 && id < geo.n_ent) p = ckv + (geo.ent_base + id) * kD;
         } else {
           const int64_t w = slot - n_comp;
@@ -112,18 +118,24 @@ __global__ __launch_bounds__(NHG * 64) void attn_kernel(
         }
       }
       rowp[v] = p;
+      const uint64_t vb = __ballot(p != nullptr);
+      if (v == 0) tile_valid = vb;
     }
     __syncthreads();
     // ---- gather: each thread moves a 4-key x 8-dim block into both LDS layouts ----
     for (int blk = tid; blk < 16 * 16; blk += NT) {
       const int kg = blk / 16;  // keys 4kg..4kg+3
       const int dg = blk % 16;  // dims 8dg..8dg+7
+      const uint16_t* pp[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) pp[u] = rowp[4 * kg + u];
       u32x4 r[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint16_t* p = rowp[4 * kg + u];
-        r[u] = p ? *reinterpret_cast<const u32x4*>(p + dg * 8) : u32x4{0, 0, 0, 0};
-      }
+      for (int u = 0; u < 4; ++u)  // unconditional loads (a masked slot reads row 0) keep all four in flight
+        r[u] = *reinterpret_cast<const u32x4*>((pp[u] ? pp[u] : ckv) + dg * 8);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (!pp[u]) r[u] = u32x4{0, 0, 0, 0};
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         *reinterpret_cast<u32x4*>(&Ks[(4 * kg + u) * kKsStride + dg * 8]) = r[u];
@@ -143,24 +155,29 @@ __global__ __launch_bounds__(NHG * 64) void attn_kernel(
     __syncthreads();
 
     // ---- S^T = K Q^T: 4 key blocks x 4 d-chunks ----
+    // all 16 key fragments are read before the first product so LDS latency overlaps
+    bf16x8 ka[4][4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+        ka[kk][mb] = as_bf16x8(*reinterpret_cast<const u32x4*>(&Ks[(16 * mb + c) * kKsStride + kk * 32 + g * 8]));
     f32x4 sacc[4];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      sacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mb = 0; mb < 4; ++mb) sacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(&Ks[(16 * mb + c) * kKsStride + kk * 32 + g * 8]));
-        sacc[mb] = mfma16x16x32(ka, qb[kk], sacc[mb]);
-      }
-    }
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) sacc[mb] = mfma16x16x32(ka[kk][mb], qb[kk], sacc[mb]);
     // ---- online softmax (base 2) for head c over keys 16mb + 4g + i ----
+    const uint64_t valid = tile_valid;
     float x[4][4];
     float mx = -INFINITY;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool ok = rowp[16 * mb + 4 * g + i] != nullptr;
+        const bool ok = (valid >> (16 * mb + 4 * g + i)) & 1ull;
         x[mb][i] = ok ? sacc[mb][i] * scale_log2 : -INFINITY;
         mx = fmaxf(mx, x[mb][i]);
       }
@@ -238,39 +255,49 @@ __global__ __launch_bounds__(NHG * 64) void attn_kernel(
   }
 }
 
-// Log-sum-exp merge of the split partials: one workgroup per query row.
+// Log-sum-exp merge of the split partials: one thread per (query row, head, dim). Splits are
+// consumed 16 at a time with all their loads issued together and an online rescale, so a
+// row with up to 16 splits costs a single round trip to memory.
 __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
                                                          int nsplit, int nrows, int H, float* __restrict__ out,
                                                          float* __restrict__ lse_out) {
+  constexpr int CH = 16;
   const int row = blockIdx.x;
-  for (int it = threadIdx.x; it < H * (kD / 4); it += blockDim.x) {
-    const int h = it / (kD / 4);
-    const int d4 = it % (kD / 4);
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ws_lse[((int64_t)s * nrows + row) * H + h]);
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    float wsum = 0.f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < nsplit; ++s) {
-        const float ls = ws_lse[((int64_t)s * nrows + row) * H + h];
-        if (ls == -INFINITY) continue;
-        const float wgt = __expf(ls - M);
-        const float4 o = *reinterpret_cast<const float4*>(ws_o + (((int64_t)s * nrows + row) * H + h) * kD + 4 * d4);
-        acc.x += wgt * o.x;
-        acc.y += wgt * o.y;
-        acc.z += wgt * o.z;
-        acc.w += wgt * o.w;
-        wsum += wgt;
-      }
-      const float inv = 1.f / wsum;
-      acc.x *= inv;
-      acc.y *= inv;
-      acc.z *= inv;
-      acc.w *= inv;
+  const int e = blockIdx.y * 256 + threadIdx.x;  // (head, dim) index inside the row
+  if (e >= H * kD) return;
+  const int h = e / kD;
+  const int d = e % kD;
+  const float* lse_p = ws_lse + (int64_t)row * H + h;
+  const float* o_p = ws_o + ((int64_t)row * H + h) * kD + d;
+  const int64_t lse_stride = (int64_t)nrows * H;
+  const int64_t o_stride = lse_stride * kD;
+  float M = -INFINITY, acc = 0.f, wsum = 0.f;
+  for (int c0 = 0; c0 < nsplit; c0 += CH) {
+    float ls[CH], o[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int s = c0 + j;
+      ls[j] = (s < nsplit) ? lse_p[s * lse_stride] : -INFINITY;
+      o[j] = (s < nsplit) ? o_p[s * o_stride] : 0.f;
     }
-    *reinterpret_cast<float4*>(out + ((int64_t)row * H + h) * kD + 4 * d4) = acc;
-    if (d4 == 0 && lse_out) lse_out[(int64_t)row * H + h] = (M == -INFINITY) ? -INFINITY : M + __logf(wsum);
+    float cm = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) cm = fmaxf(cm, ls[j]);
+    const float Mn = fmaxf(M, cm);
+    if (Mn == -INFINITY) continue;  // no split so far saw a key
+    const float r = __expf(M - Mn);  // 0 while M is still -inf
+    acc *= r;
+    wsum *= r;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const float wgt = (ls[j] == -INFINITY) ? 0.f : __expf(ls[j] - Mn);
+      acc = fmaf(wgt, o[j], acc);
+      wsum += wgt;
+    }
+    M = Mn;
   }
+  out[((int64_t)row * H + h) * kD + d] = (M == -INFINITY) ? 0.f : acc / wsum;
+  if (d == 0 && lse_out) lse_out[(int64_t)row * H + h] = (M == -INFINITY) ? -INFINITY : M + __logf(wsum);
 }
 
 template <bool SPARSE>
@@ -337,7 +364,8 @@ hipError_t launch_attention(bool sparse, const void* q, const void* ckv, const i
                         : launch_nhg<false>(H, grid, st, q16, c16, idx, k, k16, kv_off, ent_off, q_pos, m, n_win, T,
                                             sl2, max_entries, p.keys_per_split, out, lse, ws_o, ws_lse);
   if (e != hipSuccess || p.nsplit <= 1) return e;
-  attn_merge_kernel<<<dim3((unsigned)rows), 256, 0, st>>>(ws_o, ws_lse, p.nsplit, rows, H, out, lse);
+  attn_merge_kernel<<<dim3((unsigned)rows, (unsigned)((H * kD + 255) / 256)), 256, 0, st>>>(ws_o, ws_lse, p.nsplit,
+                                                                                             rows, H, out, lse);
   return hipGetLastError();
 }
 

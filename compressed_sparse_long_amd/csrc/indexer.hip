@@ -12,13 +12,18 @@
 // of score write per query row.
 //
 // Two tilings share the kernel:
-//   decode  (NB=1, WQ=1): one A tile per wave; the 4 waves of a block split a contiguous
-//           key range, each wave keeping U key tiles (U*2 KiB) of loads in flight.
+//   decode  (NB=1, WQ=1): one A tile per wave; the 8 waves of a block split a contiguous
+//           range of 512 keys, each wave issuing all its U=4 key tiles (8 KiB) in one pass
+//           (a single pass per wave keeps the memory pipeline full; looping waves do not).
 //   prefill (NB=8, WQ=4): each wave holds 8 A tiles (16/HI * 8 query rows) and the 4
 //           waves walk the same key range, so a key tile fetched once is reused for
 //           64/HI * 8 query rows through L1/L2.
+// With a top-k workspace (single query row per sequence, long rows), each decode
+// workgroup also keeps its 512 scores' keys in LDS and leaves that slice's top-k
+// candidates in the workspace (topk_common.h), so the selection never re-reads the scores.
 #include "device_common.h"
 #include "launch.h"
+#include "topk_common.h"
 
 namespace csl {
 
@@ -54,15 +59,16 @@ __device__ __forceinline__ bf16x8 key_operand(const u32x4& k) {
   return as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
 }
 
-template <int HI, int NB, int WQ, int U, bool FP8>
-__global__ __launch_bounds__(256) void indexer_kernel(
+template <int HI, int NB, int NWAVES, int WQ, int U, bool FP8, bool PREP>
+__global__ __launch_bounds__(NWAVES * 64) void indexer_kernel(
     const uint16_t* __restrict__ qI, const float* __restrict__ w, const void* __restrict__ kI,
     const float* __restrict__ k_scale, const int64_t* __restrict__ scale_off, int scale_group,
     const int64_t* __restrict__ ent_off, const int64_t* __restrict__ q_pos, int m, int T,
-    int64_t max_entries, float* __restrict__ scores, int64_t ld, int epw) {
+    int64_t max_entries, float* __restrict__ scores, int64_t ld, int epw, void* topk_ws, int topk_k) {
   constexpr int QPB = 16 / HI;       // query rows per A tile
   constexpr int QPW = NB * QPB;      // query rows per wave
-  constexpr int WE = 4 / WQ;         // key sub-ranges per block
+  constexpr int WE = NWAVES / WQ;    // key sub-ranges per block
+  constexpr int NT = NWAVES * 64;
   constexpr int ROWS_PER_GROUP = (HI >= 4) ? 1 : 4 / HI;  // query rows in one lane group's 4 C rows
 
   const int wave = threadIdx.x / kWave;
@@ -79,17 +85,23 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   const int64_t e_base = ent_off[b];
   const int64_t n_ent = ent_off[b + 1] - e_base;
   const int64_t p0 = q_pos[b];
+  // visible entries of query row t (masks the score writes only: the key loads below depend
+  // on nothing but the sequence's entry range, so they leave without waiting for this)
   auto n_vis = [&](int t) -> int64_t {
-    int64_t nv = (p0 + t) / m;
+    const int64_t p = p0 + t;
+    int64_t nv = (p >= 0 && p < ((int64_t)1 << 32)) ? (int64_t)((uint32_t)p / (uint32_t)m) : p / m;
     nv = nv < n_ent ? nv : n_ent;
     nv = nv < max_entries ? nv : max_entries;
     return nv < 0 ? 0 : nv;
   };
-  const int t_last = min(t0 + QPW - 1, T - 1);
-  const int64_t n_hi = n_vis(t_last);
-  const int64_t e0 = (int64_t)blockIdx.x * epw * WE + (int64_t)we * epw;
-  const int64_t e_end = min(e0 + epw, n_hi);
-  if (e0 >= e_end) return;
+  const int64_t wg_e0 = (int64_t)blockIdx.x * epw * WE;
+  const int64_t e0 = wg_e0 + (int64_t)we * epw;
+  const int64_t n_load = n_ent < max_entries ? n_ent : max_entries;
+  const int64_t e_end = min(e0 + epw, n_load);
+  if (!PREP && e0 >= e_end) return;  // with PREP every wave must reach the slice barrier
+  constexpr int S = PREP ? WE * 16 * U : 1;  // a block's keys form one top-k slice
+  static_assert(!PREP || S == kSliceMin, "a prepared slice is one decode block");
+  __shared__ uint32_t skeys[S];
 
   // A operands (queries) and the head weights this lane needs in the epilogue
   bf16x8 a[NB][2];
@@ -121,7 +133,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(
     }
   }
 
-  for (int64_t s0 = e0; s0 < e_end; s0 += 16 * U) {
+  for (int64_t s0 = e0; s0 < e_end; s0 += 16 * U) {  // empty when this wave has no keys
     u32x4 kb[U][2];
     float sc[U];
 #pragma unroll
@@ -166,10 +178,24 @@ __global__ __launch_bounds__(256) void indexer_kernel(
               float v = part[q];
               if (FP8) v *= sc[u];
               scores[((int64_t)b * T + tt) * ld + s] = v;
+              if (PREP) skeys[s - wg_e0] = score_key(v);
             }
           }
         }
       }
+    }
+  }
+  if (PREP) {
+    __shared__ uint32_t hist[2048];
+    __shared__ uint32_t wsum[NT / kWave];
+    __shared__ uint32_t res[4];
+    __syncthreads();
+    const int64_t n = n_vis(0);
+    if (n > topk_k && wg_e0 < n) {
+      const int nv = (int)((n - wg_e0) < S ? (n - wg_e0) : S);
+      const TopkRowWs rw = topk_row_ws(topk_ws, (int64_t)b * T, max_entries);
+      slice_cut_to_slots<NT, (S + NT - 1) / NT>(skeys, nv, wg_e0, slice_quota(n, topk_k, S), hist, wsum, res,
+                                                &rw.cuts[blockIdx.x], rw.slots + (int64_t)blockIdx.x * kSliceR);
     }
   }
 }
@@ -178,29 +204,36 @@ template <int HI, bool FP8>
 hipError_t launch_hi(const void* qI, const float* w, const void* kI, const float* k_scale,
                      const int64_t* scale_off, int scale_group, const int64_t* ent_off,
                      const int64_t* q_pos, int m, int B, int T, int64_t max_entries, float* scores,
-                     int64_t ld, hipStream_t st) {
+                     int64_t ld, void* topk_ws, int topk_k, hipStream_t st) {
   const uint16_t* q16 = static_cast<const uint16_t*>(qI);
   const int rows = B * T;
-  if (rows >= 64 && T >= 16) {
+  const bool prep = indexer_prepares_topk(topk_ws, T, max_entries);
+  if (!prep && rows >= 64 && T >= 16) {
     // prefill tiling: 8 A tiles per wave, 4 waves over the same keys
-    constexpr int NB = 8, WQ = 4, U = 2;
+    constexpr int NB = 8, NW = 4, WQ = 4, U = 2;
     constexpr int QPW = NB * (16 / HI);
     const int epw = 256;
     const int64_t gx = (max_entries + epw - 1) / epw;
     const int gy = (T + QPW * WQ - 1) / (QPW * WQ);
     dim3 grid((unsigned)(gx > 0 ? gx : 1), (unsigned)gy, (unsigned)B);
-    indexer_kernel<HI, NB, WQ, U, FP8><<<grid, 256, 0, st>>>(q16, w, kI, k_scale, scale_off, scale_group,
-                                                              ent_off, q_pos, m, T, max_entries, scores, ld, epw);
+    indexer_kernel<HI, NB, NW, WQ, U, FP8, false><<<grid, NW * 64, 0, st>>>(
+        q16, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, T, max_entries, scores, ld, epw, nullptr, 0);
   } else {
-    constexpr int NB = 1, WQ = 1, U = 8;
+    // decode tiling: every wave streams one pass of U key tiles (64 keys), 8 waves per block
+    constexpr int NB = 1, NW = 8, WQ = 1, U = 4;
     constexpr int QPW = 16 / HI;
-    const int epw = 512;  // keys per wave
-    const int64_t per_block = (int64_t)epw * 4;
+    const int epw = 16 * U;
+    const int64_t per_block = (int64_t)epw * NW;
     const int64_t gx = (max_entries + per_block - 1) / per_block;
     const int gy = (T + QPW - 1) / QPW;
     dim3 grid((unsigned)(gx > 0 ? gx : 1), (unsigned)gy, (unsigned)B);
-    indexer_kernel<HI, NB, WQ, U, FP8><<<grid, 256, 0, st>>>(q16, w, kI, k_scale, scale_off, scale_group,
-                                                              ent_off, q_pos, m, T, max_entries, scores, ld, epw);
+    if (prep)
+      indexer_kernel<HI, NB, NW, WQ, U, FP8, true><<<grid, NW * 64, 0, st>>>(
+          q16, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, T, max_entries, scores, ld, epw, topk_ws,
+          topk_k);
+    else
+      indexer_kernel<HI, NB, NW, WQ, U, FP8, false><<<grid, NW * 64, 0, st>>>(
+          q16, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, T, max_entries, scores, ld, epw, nullptr, 0);
   }
   return hipGetLastError();
 }
@@ -209,26 +242,38 @@ template <bool FP8>
 hipError_t launch_fp8(int HI, const void* qI, const float* w, const void* kI, const float* k_scale,
                       const int64_t* scale_off, int scale_group, const int64_t* ent_off,
                       const int64_t* q_pos, int m, int B, int T, int64_t max_entries, float* scores,
-                      int64_t ld, hipStream_t st) {
+                      int64_t ld, void* topk_ws, int topk_k, hipStream_t st) {
+#define CSL_IDX_CASE(H)                                                                                          \
+  case H:                                                                                                        \
+    return launch_hi<H, FP8>(qI, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T, max_entries, \
+                             scores, ld, topk_ws, topk_k, st);
   switch (HI) {
-    case 1: return launch_hi<1, FP8>(qI, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T, max_entries, scores, ld, st);
-    case 2: return launch_hi<2, FP8>(qI, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T, max_entries, scores, ld, st);
-    case 4: return launch_hi<4, FP8>(qI, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T, max_entries, scores, ld, st);
-    case 8: return launch_hi<8, FP8>(qI, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T, max_entries, scores, ld, st);
-    case 16: return launch_hi<16, FP8>(qI, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T, max_entries, scores, ld, st);
+    CSL_IDX_CASE(1)
+    CSL_IDX_CASE(2)
+    CSL_IDX_CASE(4)
+    CSL_IDX_CASE(8)
+    CSL_IDX_CASE(16)
     default: return hipErrorInvalidValue;
   }
+#undef CSL_IDX_CASE
 }
 
 }  // namespace
 
+bool indexer_prepares_topk(const void* topk_ws, int T, int64_t max_entries) {
+  return topk_ws != nullptr && T == 1 && !topk_uses_row_kernel(max_entries) &&
+         topk_slice_size(max_entries) == kSliceMin;
+}
+
 hipError_t launch_indexer(const void* qI, const float* w, const void* kI, bool fp8, const float* k_scale,
                           const int64_t* scale_off, int scale_group, const int64_t* ent_off,
                           const int64_t* q_pos, int m, int B, int T, int HI, int64_t max_entries,
-                          float* scores, int64_t ld, hipStream_t stream) {
+                          float* scores, int64_t ld, void* topk_ws, int topk_k, hipStream_t stream) {
   if (fp8)
-    return launch_fp8<true>(HI, qI, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T, max_entries, scores, ld, stream);
-  return launch_fp8<false>(HI, qI, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T, max_entries, scores, ld, stream);
+    return launch_fp8<true>(HI, qI, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T, max_entries,
+                            scores, ld, topk_ws, topk_k, stream);
+  return launch_fp8<false>(HI, qI, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T, max_entries,
+                           scores, ld, topk_ws, topk_k, stream);
 }
 
 }  // namespace csl

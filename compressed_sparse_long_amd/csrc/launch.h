@@ -15,13 +15,17 @@ hipError_t launch_compress(const void* kv, const void* z, const int64_t* kv_off,
 hipError_t launch_indexer(const void* qI, const float* w, const void* kI, bool fp8, const float* k_scale,
                           const int64_t* scale_off, int scale_group, const int64_t* ent_off,
                           const int64_t* q_pos, int m, int B, int T, int HI, int64_t max_entries,
-                          float* scores, int64_t ld, hipStream_t stream);
+                          float* scores, int64_t ld, void* topk_ws, int topk_k, hipStream_t stream);
+// whether launch_indexer leaves top-k candidate lists in topk_ws for these shapes
+bool indexer_prepares_topk(const void* topk_ws, int T, int64_t max_entries);
 
 bool topk_uses_row_kernel(int64_t max_entries);
+int64_t topk_max_entries();
 size_t topk_workspace_bytes(int B, int T, int64_t max_entries, int k);
 int topk_max_k();
 hipError_t launch_topk(const float* scores, int64_t ld, const int64_t* ent_off, const int64_t* q_pos, int m,
-                       int B, int T, int k, int64_t max_entries, int32_t* idx, void* ws, hipStream_t stream);
+                       int B, int T, int k, int64_t max_entries, int32_t* idx, void* ws, bool prepared,
+                       hipStream_t stream);
 
 struct AttnPlan {
   int nsplit;

@@ -65,9 +65,10 @@ class _Lane:
 
 
 class CsaLane(_Lane):
-    def __init__(self, lane, kv, z, q, li, device="cuda"):
+    def __init__(self, lane, kv, z, q, li, device="cuda", fused: bool = True):
         super().__init__(lane, kv, z, q, li.kv_off, li.ent_off, li.q_pos, device)
         self.k = lane.k
+        self.fused = fused  # the indexer leaves top-k candidate lists for the selection
         self.qI = li.qI.to(device)
         self.w = li.w.to(device)
         self.kI = li.kI.to(device)
@@ -89,11 +90,11 @@ class CsaLane(_Lane):
     def index(self, r: int = 0):
         indexer_scores(self.qI, self.w, self.kI_copies[r % len(self.kI_copies)], self.ent_off, self.q_pos, self.m,
                        self.scores, max_entries=self.max_entries, k_scale=self.k_scale, scale_off=self.scale_off,
-                       scale_group=self.scale_group)
+                       scale_group=self.scale_group, topk_ws=self.topk_ws if self.fused else None, topk_k=self.k)
 
     def select(self):
         topk_select(self.scores, self.ent_off, self.q_pos, self.m, self.k, self.idx, ws=self.topk_ws,
-                    max_entries=self.max_entries)
+                    max_entries=self.max_entries, prepared=self.fused)
 
     def attend(self, r: int = 0):
         sparse_attn_decode(self.q, self.ckv_copies[r % len(self.ckv_copies)], self.idx, self.kv, self.kv_off,

@@ -107,13 +107,19 @@ int csl_compress_kv(const void* kv, const void* z, const int64_t* kv_off, const 
  *   k_scale fp32, scale_off int64 [B+1]: required for fp8 keys, ignored (may be NULL) else;
  *           scales must be positive. scale_group >= 1.
  *   scores  fp32 [B, T, ld], ld >= max_entries
+ *   topk_ws (nullable) with topk_ws_bytes >= csl_topk_workspace_bytes(B, T, max_entries,
+ *           topk_k): when given with T == 1 and rows longer than 40960 entries, the kernel
+ *           also leaves per-row top-k candidate lists in it (each 2048-entry slice keeps the
+ *           entries above a slice-local cut), for the csl_topk_select call that follows with
+ *           prepared = 1 (rows of at most 2^18 entries); for other shapes it is not touched.
  * Arithmetic: bf16 MFMA products with fp32 accumulation; fp8 codes are widened to bf16
  * exactly before the product and the group scale multiplies the fp32 dot.
  */
 int csl_indexer_scores(const void* q_idx, const float* w, const void* k_idx, int k_dtype,
                        const float* k_scale, const int64_t* scale_off, int scale_group,
                        const int64_t* ent_off, const int64_t* q_pos, int m, int B, int T, int HI,
-                       int CI, int64_t max_entries, float* scores, int64_t ld, void* stream);
+                       int CI, int64_t max_entries, float* scores, int64_t ld, void* topk_ws,
+                       size_t topk_ws_bytes, int topk_k, void* stream);
 
 /*
  * topk_select -- top-k compressed entries per query row ([P2] "Deep Dive", CSA top-k
@@ -125,17 +131,20 @@ int csl_indexer_scores(const void* q_idx, const float* w, const void* k_idx, int
  *   then written in ASCENDING id order, padded with -1 up to k.
  * -0.0 and +0.0 compare equal. NaN scores are outside the contract.
  *
- *   scores fp32 [B, T, ld]; idx int32 [B, T, k]; 1 <= k <= 4096; max_entries < 2^31.
+ *   scores fp32 [B, T, ld]; idx int32 [B, T, k]; 1 <= k <= 4096; max_entries <= 2^20.
  *   ws: device workspace of at least csl_topk_workspace_bytes(B, T, max_entries, k)
- *   bytes (may be NULL when that is 0). Its contents must be ZERO before the first call
- *   that uses it (for example a zero-filled allocation); every completed call leaves it
- *   zero again, so it can be reused by the next call on the same stream.
+ *   bytes (may be NULL when that is 0); its contents on entry do not matter.
+ *   prepared: 1 when the csl_indexer_scores call that wrote these scores was given this
+ *   workspace and k (its candidate lists are then used instead of a pass over the scores);
+ *   0 otherwise. The result is the same either way; if the lists cannot prove the selection
+ *   exact (rows whose best entries crowd into a few 512-entry slices), the whole row is
+ *   searched.
  * Integer work only: scores are compared through an order-preserving 32-bit key.
  */
 size_t csl_topk_workspace_bytes(int B, int T, int64_t max_entries, int k);
 int csl_topk_select(const float* scores, int64_t ld, const int64_t* ent_off, const int64_t* q_pos,
                     int m, int B, int T, int k, int64_t max_entries, int32_t* idx, void* ws,
-                    size_t ws_bytes, void* stream);
+                    size_t ws_bytes, int prepared, void* stream);
 
 /*
  * sparse_attn_decode -- CSA core attention ([P2] "Deep Dive", CSA core attention with

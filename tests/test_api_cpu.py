@@ -68,8 +68,8 @@ def test_compress_validation(lib):
 def test_indexer_validation(lib):
     f = lib.csl_indexer_scores
     I, L = ctypes.c_int, ctypes.c_int64
-    f.argtypes = [P, P, P, I, P, P, I, P, P, I, I, I, I, I, L, P, L, P]
-    args = [FAKE, FAKE, FAKE, 0, None, None, 64, FAKE, FAKE, 4, 1, 1, 8, 64, 1000, FAKE, 1000, None]
+    f.argtypes = [P, P, P, I, P, P, I, P, P, I, I, I, I, I, L, P, L, P, ctypes.c_size_t, I, P]
+    args = [FAKE, FAKE, FAKE, 0, None, None, 64, FAKE, FAKE, 4, 1, 1, 8, 64, 1000, FAKE, 1000, None, 0, 0, None]
     bad = list(args); bad[12] = 3
     assert f(*bad) == 2                       # HI
     bad = list(args); bad[13] = 128
@@ -82,6 +82,11 @@ def test_indexer_validation(lib):
     assert f(*bad) == 1
     ok0 = list(args); ok0[11] = 0
     assert f(*ok0) == 0                       # T = 0: nothing to do
+    long_rows = list(args); long_rows[14] = 262144; long_rows[16] = 262144
+    bad = list(long_rows); bad[17] = FAKE; bad[18] = 100; bad[19] = 1024
+    assert f(*bad) == 3                       # top-k workspace too small
+    bad = list(long_rows); bad[17] = FAKE; bad[18] = 1 << 30; bad[19] = 0
+    assert f(*bad) == 2                       # topk_k out of range
 
 
 def test_topk_validation_and_workspace(lib):
@@ -94,13 +99,13 @@ def test_topk_validation_and_workspace(lib):
     assert big > 4 * (2048 * 4 + 1024 * 4)
     f = lib.csl_topk_select
     I, L = ctypes.c_int, ctypes.c_int64
-    f.argtypes = [P, L, P, P, I, I, I, I, L, P, P, ctypes.c_size_t, P]
-    assert f(FAKE, 262144, FAKE, FAKE, 4, 4, 1, 1024, 262144, FAKE, FAKE, big - 1, None) == 3
+    f.argtypes = [P, L, P, P, I, I, I, I, L, P, P, ctypes.c_size_t, I, P]
+    assert f(FAKE, 262144, FAKE, FAKE, 4, 4, 1, 1024, 262144, FAKE, FAKE, big - 1, 0, None) == 3
     assert "workspace" in _err(lib)
-    assert f(FAKE, 262144, FAKE, FAKE, 4, 4, 1, 1024, 262144, FAKE, None, 0, None) == 3
-    assert f(FAKE, 1024, FAKE, FAKE, 4, 1, 1, 0, 1024, FAKE, None, 0, None) == 2      # k = 0
-    assert f(FAKE, 1024, FAKE, FAKE, 4, 1, 1, 5000, 1024, FAKE, None, 0, None) == 2   # k too large
-    assert f(FAKE, 100, FAKE, FAKE, 4, 1, 1, 64, 1024, FAKE, None, 0, None) == 1      # ld < max_entries
+    assert f(FAKE, 262144, FAKE, FAKE, 4, 4, 1, 1024, 262144, FAKE, None, 0, 1, None) == 3
+    assert f(FAKE, 1024, FAKE, FAKE, 4, 1, 1, 0, 1024, FAKE, None, 0, 0, None) == 2      # k = 0
+    assert f(FAKE, 1024, FAKE, FAKE, 4, 1, 1, 5000, 1024, FAKE, None, 0, 0, None) == 2   # k too large
+    assert f(FAKE, 100, FAKE, FAKE, 4, 1, 1, 64, 1024, FAKE, None, 0, 0, None) == 1      # ld < max_entries
 
 
 def test_attention_validation_and_workspace(lib):
