@@ -256,12 +256,11 @@ __global__ __launch_bounds__(NHG * 64) void attn_kernel(
 }
 
 // Log-sum-exp merge of the split partials: one thread per (query row, head, dim). Splits are
-// consumed 16 at a time with all their loads issued together and an online rescale, so a
-// row with up to 16 splits costs a single round trip to memory.
+// consumed 8 at a time with all their loads issued together and an online rescale.
 __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
                                                          int nsplit, int nrows, int H, float* __restrict__ out,
                                                          float* __restrict__ lse_out) {
-  constexpr int CH = 16;
+  constexpr int CH = 8;
   const int row = blockIdx.x;
   const int e = blockIdx.y * 256 + threadIdx.x;  // (head, dim) index inside the row
   if (e >= H * kD) return;

@@ -20,7 +20,8 @@
 //           64/HI * 8 query rows through L1/L2.
 // With a top-k workspace (single query row per sequence, long rows), each decode
 // workgroup also keeps its 512 scores' keys in LDS and leaves that slice's top-k
-// candidates in the workspace (topk_common.h), so the selection never re-reads the scores.
+// candidate list in the workspace (topk_common.h), so the selection never re-reads the
+// scores.
 #include "device_common.h"
 #include "launch.h"
 #include "topk_common.h"
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_kernel(
   const int64_t e_end = min(e0 + epw, n_load);
   if (!PREP && e0 >= e_end) return;  // with PREP every wave must reach the slice barrier
   constexpr int S = PREP ? WE * 16 * U : 1;  // a block's keys form one top-k slice
-  static_assert(!PREP || S == kSliceMin, "a prepared slice is one decode block");
+  static_assert(!PREP || (S == kSlice && NT == kSlice), "a prepared slice is one decode block, one key per thread");
   __shared__ uint32_t skeys[S];
 
   // A operands (queries) and the head weights this lane needs in the epilogue
@@ -186,16 +187,14 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_kernel(
     }
   }
   if (PREP) {
-    __shared__ uint32_t hist[2048];
-    __shared__ uint32_t wsum[NT / kWave];
-    __shared__ uint32_t res[4];
-    __syncthreads();
+    __shared__ SliceScratch sc;
+    __syncthreads();  // every wave's keys are in skeys
     const int64_t n = n_vis(0);
     if (n > topk_k && wg_e0 < n) {
-      const int nv = (int)((n - wg_e0) < S ? (n - wg_e0) : S);
+      const uint32_t x = (wg_e0 + threadIdx.x < n) ? skeys[threadIdx.x] : 0u;
       const TopkRowWs rw = topk_row_ws(topk_ws, (int64_t)b * T, max_entries);
-      slice_cut_to_slots<NT, (S + NT - 1) / NT>(skeys, nv, wg_e0, slice_quota(n, topk_k, S), hist, wsum, res,
-                                                &rw.cuts[blockIdx.x], rw.slots + (int64_t)blockIdx.x * kSliceR);
+      slice_candidates(x, slice_quota(n, topk_k), sc, wg_e0, &rw.cuts[blockIdx.x],
+                       rw.slots + (int64_t)blockIdx.x * kSliceSlots);
     }
   }
 }
@@ -261,8 +260,7 @@ hipError_t launch_fp8(int HI, const void* qI, const float* w, const void* kI, co
 }  // namespace
 
 bool indexer_prepares_topk(const void* topk_ws, int T, int64_t max_entries) {
-  return topk_ws != nullptr && T == 1 && !topk_uses_row_kernel(max_entries) &&
-         topk_slice_size(max_entries) == kSliceMin;
+  return topk_ws != nullptr && T == 1 && !topk_uses_row_kernel(max_entries) && max_entries <= kMultiMaxEntries;
 }
 
 hipError_t launch_indexer(const void* qI, const float* w, const void* kI, bool fp8, const float* k_scale,

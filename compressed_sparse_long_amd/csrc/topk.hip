@@ -11,14 +11,14 @@
 //     C(i) = key << 16 | (0xffff - i), and writes the selection with a block-wide ordered
 //     compaction, so the output is ascending by construction;
 //
-//   * long rows (decode at 1M context: 262144 scores per row): every slice of the row lists
-//     its own candidates above an honest slice cut (topk_common.h) -- either inside
-//     indexer_scores, which already holds the scores, or in a prepare kernel here -- and one
-//     workgroup per row finishes: it keeps the listed entries whose key reaches the row's
-//     largest cut (exactly the row's entries at or above that cut), radix-selects the k
-//     best of them with the candidates held in registers, marks the winners in an LDS bitmap
-//     of the row and scans it to emit ascending ids. If fewer than k entries reach the cut
-//     it runs an exact pass over the whole row instead.
+//   * long rows (decode at 1M context: 262144 scores per row): every 512-entry slice of the
+//     row lists its own candidates above an honest slice cut (topk_common.h) -- either
+//     inside indexer_scores, which already holds the scores, or in a prepare kernel here --
+//     and one workgroup per row finishes: it radix-selects the k best listed entries on
+//     their 32-bit keys (lower id first within the last tied key), checks that the k-th
+//     best listed key reaches every slice's cut (then the selection is the row's), and
+//     writes the winners in ascending id order straight from the slot order with one
+//     block-wide scan. If the check fails it runs an exact pass over the whole row instead.
 #include "device_common.h"
 #include "launch.h"
 #include "topk_common.h"
@@ -132,226 +132,296 @@ __global__ __launch_bounds__(1024) void topk_row_kernel(const float* __restrict_
 // ---------------------------------------------------------------------------------------
 // Long rows: slice candidates, then one finishing workgroup per row.
 // ---------------------------------------------------------------------------------------
-template <int S>
-__global__ __launch_bounds__(256) void topk_prepare_kernel(const float* __restrict__ scores, int64_t ld,
-                                                           const int64_t* __restrict__ ent_off,
-                                                           const int64_t* __restrict__ q_pos, int m, int T, int k,
-                                                           int64_t max_entries, void* ws) {
-  __shared__ uint32_t keys[S];
-  __shared__ uint32_t hist[2048];
-  __shared__ uint32_t wsum[256 / kWave];
-  __shared__ uint32_t res[4];
+__global__ __launch_bounds__(kSlice) void topk_prepare_kernel(const float* __restrict__ scores, int64_t ld,
+                                                               const int64_t* __restrict__ ent_off,
+                                                               const int64_t* __restrict__ q_pos, int m, int T, int k,
+                                                               int64_t max_entries, void* ws) {
+  __shared__ SliceScratch sc;
   const int row = blockIdx.y;
   const int b = row / T, t = row % T;
   const int64_t n = row_count(ent_off, q_pos, b, t, m, max_entries);
   if (n <= k) return;  // the finishing kernel selects everything
-  const int64_t lo = (int64_t)blockIdx.x * S;
+  const int64_t lo = (int64_t)blockIdx.x * kSlice;
   if (lo >= n) return;
-  const float* srow = scores + (int64_t)row * ld;
-  const int nv = (int)((n - lo) < S ? (n - lo) : S);
-#pragma unroll
-  for (int j = 0; j < S / 256; ++j) {
-    const int s = j * 256 + threadIdx.x;
-    keys[s] = (s < nv) ? score_key(srow[lo + s]) : 0u;
-  }
-  __syncthreads();
+  const int64_t i = lo + threadIdx.x;
+  const uint32_t x = (i < n) ? score_key(scores[(int64_t)row * ld + i]) : 0u;
   const TopkRowWs rw = topk_row_ws(ws, row, max_entries);
-  slice_cut_to_slots<256, S / 256>(keys, nv, lo, slice_quota(n, k, S), hist, wsum, res, &rw.cuts[blockIdx.x],
-                                   rw.slots + (int64_t)blockIdx.x * kSliceR);
+  slice_candidates(x, slice_quota(n, k), sc, lo, &rw.cuts[blockIdx.x], rw.slots + (int64_t)blockIdx.x * kSliceSlots);
 }
 
 constexpr int kFinNT = 1024;
-constexpr int kFinPer = (kMaxRowSlots + kFinNT - 1) / kFinNT;  // candidate slots per thread
-constexpr int kBitmapIds = 1 << 18;  // rows up to this length are ordered through an LDS bitmap
+constexpr int kFinWaves = kFinNT / kWave;
 
+// One radix step of the finish: over BINS bins (hist in LDS), find the bin holding the
+// need-th largest key counting from the top bin down. res = {bin, count above it, count in
+// it, total}. Contains two workgroup barriers; the caller reads res after it returns.
+template <int BINS>
+__device__ __forceinline__ void fin_threshold(const uint32_t* hist, uint32_t need, uint32_t* wsum, uint32_t* res) {
+  constexpr int PER = BINS / kFinNT;
+  static_assert(PER * kFinNT == BINS, "bins per thread");
+  const int tid = threadIdx.x;
+  uint32_t v[PER];
+  uint32_t local = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    v[q] = hist[BINS - 1 - (tid * PER + q)];
+    local += v[q];
+  }
+  const uint32_t incl = wave_incl_scan(local);
+  if (lane_id() == kWave - 1) wsum[tid / kWave] = incl;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kFinWaves; ++w) {
+    const uint32_t x = wsum[w];
+    before += (w < tid / kWave) ? x : 0u;
+    all += x;
+  }
+  uint32_t excl = before + incl - local;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    if (excl < need && need <= excl + v[q]) {
+      res[0] = (uint32_t)(BINS - 1 - (tid * PER + q));
+      res[1] = excl;
+      res[2] = v[q];
+    }
+    excl += v[q];
+  }
+  if (tid == 0) res[3] = all;
+  __syncthreads();
+}
+
+// Exact selection over the whole row from the scores: radix select on key << 32 | ~id,
+// then an ordered compaction. Used when the candidate lists cannot prove the selection.
+__device__ void finish_full_row(const float* __restrict__ srow, int64_t n, uint32_t keep, int32_t* __restrict__ out,
+                                uint32_t* hist, uint32_t* wsum, uint32_t* res) {
+  const int tid = threadIdx.x;
+  uint64_t pre = 0;
+  int pb = 0;
+  uint32_t need = keep;
+  while (pb < 64) {
+    const int width = (64 - pb) < 11 ? (64 - pb) : 11;
+    const int shift = 64 - pb - width;
+    for (int q = tid; q < 2048; q += kFinNT) hist[q] = 0;
+    __syncthreads();
+    for (int64_t i = tid; i < n; i += kFinNT) {
+      const uint64_t C = ((uint64_t)score_key(srow[i]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)i);
+      if (pb == 0 || (C >> (64 - pb)) == pre) atomicAdd(&hist[(uint32_t)(C >> shift) & ((1u << width) - 1u)], 1u);
+    }
+    __syncthreads();
+    find_threshold_bin<kFinNT, 2048>(hist, need, wsum, res);
+    const uint32_t d = res[0], above = res[1], in_bin = res[2];
+    pre = (pre << width) | d;
+    pb += width;
+    need -= above;
+    __syncthreads();
+    if (in_bin == need) break;
+  }
+  uint32_t base = 0;
+  for (int64_t c0 = 0; c0 < n; c0 += kFinNT) {
+    const int64_t i = c0 + tid;
+    bool s = false;
+    if (i < n) {
+      const uint64_t C = ((uint64_t)score_key(srow[i]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)i);
+      s = (C >> (64 - pb)) >= pre;
+    }
+    uint32_t tot;
+    const uint32_t e = block_exclusive_scan<kFinNT>(s ? 1u : 0u, wsum, &tot);
+    if (s && base + e < keep) out[base + e] = (int32_t)i;
+    base += tot;
+  }
+}
+
+// One workgroup per row. Thread i owns CH consecutive chunks of 8 slots (half a slice each),
+// so thread order is slot order is id order.
+template <int CH>
 __global__ __launch_bounds__(kFinNT) void topk_finish_kernel(const float* __restrict__ scores, int64_t ld,
                                                              const int64_t* __restrict__ ent_off,
                                                              const int64_t* __restrict__ q_pos, int m, int T, int k,
                                                              int64_t max_entries, int32_t* __restrict__ idx, void* ws) {
-  __shared__ uint32_t hist[2048];
-  __shared__ uint32_t bitmap[kBitmapIds / 32];  // also the id buffer of very long rows
-  __shared__ uint32_t wsum[kFinNT / kWave];
+  constexpr int PER = 8;  // slots per chunk
+  static_assert(2 * PER == kSliceSlots, "a chunk is half a slice");
+  __shared__ uint32_t hist_a[2048];
+  __shared__ uint32_t hist_b[2048];
+  __shared__ uint32_t hist_c[1024];
+  __shared__ uint32_t wsum[3 * kFinWaves];
   __shared__ uint32_t res[4];
 
   const int row = blockIdx.x;
   const int b = row / T, t = row % T;
   const int tid = threadIdx.x;
   const TopkRowWs rw = topk_row_ws(ws, row, max_entries);
-  const int S = topk_slice_size(max_entries);
-  const int ns_max = (int)topk_num_slices(max_entries, S);
-  // every global read is issued up front: row geometry, all slice cuts and all slots (those
-  // of slices past this row's length are ignored below)
-  const uint32_t my_cut = (tid < ns_max) ? rw.cuts[tid] : 0u;
-  uint64_t cv[kFinPer];
+  const int ns_max = (int)topk_num_slices(max_entries);
+  // every global read is issued up front: the thread's slots and cuts, then the row geometry
+  uint64_t sl[CH][PER];
+  uint32_t cut[CH];
 #pragma unroll
-  for (int q = 0; q < kFinPer; ++q) {
-    const int j = q * kFinNT + tid;
-    cv[q] = (j < ns_max * kSliceR) ? rw.slots[j] : 0ull;
+  for (int c = 0; c < CH; ++c) {
+    const int j = tid * CH + c;
+    const bool in = (j >> 1) < ns_max;
+    const u32x4* src = reinterpret_cast<const u32x4*>(rw.slots + (int64_t)j * PER);
+#pragma unroll
+    for (int q = 0; q < PER / 2; ++q) {
+      const u32x4 v = in ? src[q] : u32x4{0, 0, 0, 0};
+      sl[c][2 * q] = ((uint64_t)v.y << 32) | v.x;
+      sl[c][2 * q + 1] = ((uint64_t)v.w << 32) | v.z;
+    }
+    cut[c] = in ? rw.cuts[j >> 1] : 0u;
   }
   const int64_t n = row_count(ent_off, q_pos, b, t, m, max_entries);
   const uint32_t keep = (uint32_t)(n < k ? n : k);
   int32_t* out = idx + (int64_t)row * k;
-  const float* srow = scores + (int64_t)row * ld;
-  const int words = (int)(n <= kBitmapIds ? (n + 31) / 32 : 0);
-  for (int w = tid; w < words; w += kFinNT) bitmap[w] = 0;
+  for (int q = tid; q < 2048; q += kFinNT) {
+    hist_a[q] = 0;
+    hist_b[q] = 0;
+  }
+  hist_c[tid] = 0;
 
   if ((int64_t)keep == n) {
     for (int p = tid; p < k; p += kFinNT) out[p] = p < n ? p : -1;
     return;
   }
-
-  // the listed entries whose key reaches the largest slice cut are exactly the row's entries
-  // at or above that cut
-  const int ns = (int)topk_num_slices(n, S);
-  const uint32_t max_cut = block_max_u32<kFinNT>(tid < ns ? my_cut : 0u, wsum);
-  uint32_t vmask = 0, kmax = 0;
+  const int ns = (int)topk_num_slices(n);
+  uint32_t key[CH][PER];
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
-  for (int q = 0; q < kFinPer; ++q) {
-    const int j = q * kFinNT + tid;
-    const uint32_t key = (uint32_t)(cv[q] >> 32);
-    if (j < ns * kSliceR && key != 0u && key >= max_cut) {
-      vmask |= 1u << q;
-      kmax = max(kmax, key);
+  for (int c = 0; c < CH; ++c) {
+    const bool in = ((tid * CH + c) >> 1) < ns;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const uint32_t x = in ? (uint32_t)(sl[c][q] >> 32) : 0u;
+      key[c][q] = x;
+      if (x) {
+        kmin = min(kmin, x);
+        kmax = max(kmax, x);
+      }
     }
   }
-  const uint32_t max_key = block_max_u32<kFinNT>(kmax, wsum);
-  const uint32_t range = max_key - max_cut;
-  const int start_bit = 32 + (range ? 32 - __clz(range) : 0);
-  uint64_t v[kFinPer];  // (max_key - key) << 32 | id: the k smallest are the k best
+  const int wave = tid / kWave;
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  if (lane_id() == 0) {
+    wsum[wave] = kmin;
+    wsum[kFinWaves + wave] = kmax;
+  }
+  __syncthreads();  // histograms cleared, wave extremes posted
 #pragma unroll
-  for (int q = 0; q < kFinPer; ++q) v[q] = ((uint64_t)(max_key - (uint32_t)(cv[q] >> 32)) << 32) | (uint32_t)cv[q];
+  for (int w = 0; w < kFinWaves; ++w) {
+    kmin = min(kmin, wsum[w]);
+    kmax = max(kmax, wsum[kFinWaves + w]);
+  }
+
+  // radix select of the keep-th largest listed key. The listed keys share their top
+  // L = clz(kmin ^ kmax) bits, so the first pass bins the 11 bits below those (spreading the
+  // keys over the bins instead of piling them into a few), the later passes the rest.
   bool ok = true;
-  uint64_t prefix = 0;
-  int pbits = 0;
-  {
-    uint32_t need = keep;
-    while (pbits < start_bit) {
-      const int width = (start_bit - pbits) < 11 ? (start_bit - pbits) : 11;
-      const int shift = start_bit - pbits - width;
-      for (int q = tid; q < 2048; q += kFinNT) hist[q] = 0;
-      __syncthreads();
+  bool all_in = false;
+  uint32_t need = keep;
+  const int common = __clz(kmin ^ kmax);  // 32 when all keys are equal
+  int shift = common >= 21 ? 0 : 21 - common;
+  uint32_t prefix;  // value of key >> shift shared by the keys still in play
 #pragma unroll
-      for (int q = 0; q < kFinPer; ++q)
-        if (((vmask >> q) & 1u) && (pbits == 0 || (v[q] >> (start_bit - pbits)) == prefix))
-          atomicAdd(&hist[2047u - ((uint32_t)(v[q] >> shift) & ((1u << width) - 1u))], 1u);
+  for (int c = 0; c < CH; ++c)
+#pragma unroll
+    for (int q = 0; q < PER; ++q)
+      if (key[c][q]) atomicAdd(&hist_a[(key[c][q] >> shift) & 2047u], 1u);
+  __syncthreads();
+  fin_threshold<2048>(hist_a, need, wsum, res);
+  if (res[3] < keep) {
+    ok = false;  // fewer listed entries than winners
+  } else {
+    prefix = ((shift < 21 ? (kmin >> shift) : 0u) & ~2047u) | res[0];
+    need -= res[1];
+    all_in = res[2] == need;
+    if (!all_in && shift > 0) {
+      const int wb = shift < 11 ? shift : 11;
+      const int sb = shift - wb;
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+#pragma unroll
+        for (int q = 0; q < PER; ++q)
+          if (key[c][q] && (key[c][q] >> shift) == prefix)
+            atomicAdd(&hist_b[(key[c][q] >> sb) & ((1u << wb) - 1u)], 1u);
       __syncthreads();
-      if (pbits == 0) {  // total of the first histogram = listed entries at or above max_cut
-        uint32_t tot;
-        block_exclusive_scan<kFinNT>(hist[2 * tid] + hist[2 * tid + 1], wsum, &tot);
-        if (tot < keep) {
-          ok = false;
-          break;
-        }
+      fin_threshold<2048>(hist_b, need, wsum, res);
+      prefix = (prefix << wb) | res[0];
+      shift = sb;
+      need -= res[1];
+      all_in = res[2] == need;
+      if (!all_in && shift > 0) {  // shift <= 10 here
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+#pragma unroll
+          for (int q = 0; q < PER; ++q)
+            if (key[c][q] && (key[c][q] >> shift) == prefix)
+              atomicAdd(&hist_c[key[c][q] & ((1u << shift) - 1u)], 1u);
+        __syncthreads();
+        fin_threshold<1024>(hist_c, need, wsum, res);
+        prefix = (prefix << shift) | res[0];
+        shift = 0;
+        need -= res[1];
+        all_in = res[2] == need;
       }
-      find_threshold_bin<kFinNT, 2048>(hist, need, wsum, res);  // top-down over reversed bins
-      const uint32_t d = 2047u - res[0], below = res[1], in_bin = res[2];
-      prefix = (prefix << width) | d;
-      pbits += width;
-      need -= below;
-      __syncthreads();
-      if (in_bin == need) break;
     }
   }
 
-  if (ok && n <= kBitmapIds) {
-    // mark the winners in a bitmap of the row and emit them in id order
-    constexpr int WPT = kBitmapIds / 32 / kFinNT;  // bitmap words per thread
+  if (ok) {
+    // winners: keys above the selected bin, plus (unless the whole bin is taken) the first
+    // `need` keys equal to the exact key value, in id order
+    const uint32_t lo = prefix << shift;  // lowest key a winner can have
+    uint32_t gmask = 0, emask = 0, viol = 0;
 #pragma unroll
-    for (int q = 0; q < kFinPer; ++q)
-      if (((vmask >> q) & 1u) && (v[q] >> (start_bit - pbits)) <= prefix) {
-        const uint32_t id = (uint32_t)v[q];
-        atomicOr(&bitmap[id >> 5], 1u << (id & 31));
-      }
-    __syncthreads();
-    uint32_t wv[WPT];
-    uint32_t c = 0;
+    for (int c = 0; c < CH; ++c) {
+      if (((tid * CH + c) >> 1) < ns && cut[c] > lo) viol = 1;
 #pragma unroll
-    for (int q = 0; q < WPT; ++q) {
-      const int w = tid * WPT + q;
-      wv[q] = (w < words) ? bitmap[w] : 0u;
-      c += __popc(wv[q]);
-    }
-    uint32_t pos = block_exclusive_scan<kFinNT>(c, wsum, nullptr);
-#pragma unroll
-    for (int q = 0; q < WPT; ++q) {
-      uint32_t bits = wv[q];
-      while (bits) {
-        const int bit = __ffs(bits) - 1;
-        bits &= bits - 1;
-        if (pos < keep) out[pos] = (tid * WPT + q) * 32 + bit;
-        ++pos;
+      for (int q = 0; q < PER; ++q) {
+        const uint32_t x = key[c][q];
+        const uint32_t h = x >> shift;
+        const bool g = x != 0u && (h > prefix || (all_in && h == prefix));
+        const bool e = x != 0u && !all_in && h == prefix;
+        gmask |= (uint32_t)g << (c * PER + q);
+        emask |= (uint32_t)e << (c * PER + q);
       }
     }
-  } else if (ok) {
-    // very long rows: gather the winners and sort their ids
-    uint32_t* ids = bitmap;
-    if (tid == 0) res[3] = 0;
+    // one block scan of (gt count | eq count << 16): a row lists at most 32768 keys
+    const uint32_t mine = (uint32_t)__popc(gmask) | ((uint32_t)__popc(emask) << 16);
+    const uint32_t incl = wave_incl_scan(mine);
+    const bool wviol = __ballot(viol != 0u) != 0ull;
+    if (lane_id() == kWave - 1) {
+      wsum[wave] = incl;
+      wsum[kFinWaves + wave] = wviol ? 1u : 0u;
+    }
     __syncthreads();
+    uint32_t before = 0, tv = 0;
 #pragma unroll
-    for (int q = 0; q < kFinPer; ++q)
-      if (((vmask >> q) & 1u) && (v[q] >> (start_bit - pbits)) <= prefix) {
-        const uint32_t p = atomicAdd(&res[3], 1u);
-        if (p < keep) ids[p] = (uint32_t)v[q];
-      }
-    __syncthreads();
-    uint32_t np2 = 1;
-    while (np2 < keep) np2 <<= 1;
-    for (uint32_t q = keep + tid; q < np2; q += kFinNT) ids[q] = 0xffffffffu;
-    __syncthreads();
-    for (uint32_t size = 2; size <= np2; size <<= 1) {
-      for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
-        for (uint32_t i = tid; i < np2 / 2; i += kFinNT) {
-          const uint32_t a = 2 * i - (i & (stride - 1));
-          const uint32_t c2 = a + stride;
-          const bool up = (a & size) == 0;
-          const uint32_t x = ids[a], y = ids[c2];
-          if ((x > y) == up) {
-            ids[a] = y;
-            ids[c2] = x;
+    for (int w = 0; w < kFinWaves; ++w) {
+      before += (w < wave) ? wsum[w] : 0u;
+      tv |= wsum[kFinWaves + w];
+    }
+    if (tv != 0u) {
+      ok = false;  // a slice may hide a winner below its cut
+      __syncthreads();
+    } else {
+      const uint32_t ex = before + incl - mine;
+      uint32_t gpos = ex & 0xffffu, epos = ex >> 16;
+      const uint32_t need_eq = all_in ? 0u : need;
+      const uint32_t wins = gmask | emask;
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+          const int bit = c * PER + q;
+          if ((wins >> bit) & 1u) {
+            const bool g = (gmask >> bit) & 1u;
+            const uint32_t e_before = min(epos, need_eq);
+            if (g || epos < need_eq) out[gpos + e_before] = (int32_t)(uint32_t)sl[c][q];
+            gpos += g ? 1u : 0u;
+            epos += g ? 0u : 1u;
           }
         }
-        __syncthreads();
-      }
-    }
-    for (uint32_t q = tid; q < keep; q += kFinNT) out[q] = (int32_t)ids[q];
-  } else {
-    // the lists cannot prove the selection: exact radix select on key << 32 | (~id) over
-    // the whole row
-    uint64_t pre = 0;
-    int pb = 0;
-    uint32_t need = keep;
-    while (pb < 64) {
-      const int width = (64 - pb) < 11 ? (64 - pb) : 11;
-      const int shift = 64 - pb - width;
-      for (int q = tid; q < 2048; q += kFinNT) hist[q] = 0;
-      __syncthreads();
-      for (int64_t i = tid; i < n; i += kFinNT) {
-        const uint64_t C = ((uint64_t)score_key(srow[i]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)i);
-        if (pb == 0 || (C >> (64 - pb)) == pre) atomicAdd(&hist[(uint32_t)(C >> shift) & ((1u << width) - 1u)], 1u);
-      }
-      __syncthreads();
-      find_threshold_bin<kFinNT, 2048>(hist, need, wsum, res);
-      const uint32_t d = res[0], above = res[1], in_bin = res[2];
-      pre = (pre << width) | d;
-      pb += width;
-      need -= above;
-      __syncthreads();
-      if (in_bin == need) break;
-    }
-    uint32_t base = 0;
-    for (int64_t c0 = 0; c0 < n; c0 += kFinNT) {
-      const int64_t i = c0 + tid;
-      bool s = false;
-      if (i < n) {
-        const uint64_t C = ((uint64_t)score_key(srow[i]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)i);
-        s = (C >> (64 - pb)) >= pre;
-      }
-      uint32_t tot;
-      const uint32_t e = block_exclusive_scan<kFinNT>(s ? 1u : 0u, wsum, &tot);
-      if (s && base + e < keep) out[base + e] = (int32_t)i;
-      base += tot;
     }
   }
+  if (!ok) finish_full_row(scores + (int64_t)row * ld, n, keep, out, hist_a, wsum, res);
   for (int p = (int)keep + tid; p < k; p += kFinNT) out[p] = -1;
 }
 
@@ -385,19 +455,18 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int64_t* ent_off, 
   }
   const int rows = B * T;
   if (!prepared) {
-    const int S = topk_slice_size(max_entries);
-    dim3 grid((unsigned)topk_num_slices(max_entries, S), (unsigned)rows);
-    if (S == 512)
-      topk_prepare_kernel<512><<<grid, 256, 0, st>>>(scores, ld, ent_off, q_pos, m, T, k, max_entries, ws);
-    else if (S == 1024)
-      topk_prepare_kernel<1024><<<grid, 256, 0, st>>>(scores, ld, ent_off, q_pos, m, T, k, max_entries, ws);
-    else
-      topk_prepare_kernel<2048><<<grid, 256, 0, st>>>(scores, ld, ent_off, q_pos, m, T, k, max_entries, ws);
+    dim3 grid((unsigned)topk_num_slices(max_entries), (unsigned)rows);
+    topk_prepare_kernel<<<grid, kSlice, 0, st>>>(scores, ld, ent_off, q_pos, m, T, k, max_entries, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  topk_finish_kernel<<<dim3((unsigned)rows), kFinNT, 0, st>>>(scores, ld, ent_off, q_pos, m, T, k, max_entries, idx,
-                                                               ws);
+  // chunks of 8 slots: 2 per slice, CH per thread
+  if (topk_num_slices(max_entries) * 2 <= kFinNT)
+    topk_finish_kernel<1><<<dim3((unsigned)rows), kFinNT, 0, st>>>(scores, ld, ent_off, q_pos, m, T, k, max_entries,
+                                                                    idx, ws);
+  else
+    topk_finish_kernel<4><<<dim3((unsigned)rows), kFinNT, 0, st>>>(scores, ld, ent_off, q_pos, m, T, k, max_entries,
+                                                                    idx, ws);
   return hipGetLastError();
 }
 

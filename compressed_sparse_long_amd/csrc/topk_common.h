@@ -1,45 +1,40 @@
 // Pieces of the top-k selection shared by the indexer (which can leave per-row candidate
-// lists behind) and the top-k kernels: block scans, radix threshold search, and the
-// per-slice candidate cut.
+// lists behind) and the top-k kernels: wave and block scans, radix threshold search, and the
+// per-slice candidate lists.
 //
-// Slice candidates. A row of n scores is cut into slices of S consecutive entries
-// (S = 512 for rows up to 2^18 entries, doubling beyond). Every slice writes, with plain
-// stores and no atomics, its cut -- a key value such that all of the slice's entries with
-// key >= cut are listed -- and up to R = 24 listed (key, id) pairs into its own slots. The
-// cut is chosen so that `quota` entries pass (16..20, about 8x the slice's expected share of
-// the k winners) but never more than R; it is honest either way. Every entry of the row whose
-// key reaches the largest cut of all slices is therefore listed, so whenever at least k listed
-// entries reach that largest cut, the k best of them are exactly the k best of the row.
-// Otherwise the finishing step searches the whole row. A slice holds 16 or more of the
-// k winners when it expects two with probability ~2e-9.
+// Slice candidates. A row of n scores is cut into slices of 512 consecutive entries. Every
+// slice writes, with plain stores and no atomics, its cut -- a key value such that every entry
+// of the slice whose key reaches the cut is listed -- and at most 16 listed (key << 32 | id)
+// pairs, in ascending id order, into its own slots (0 marks an empty slot). The cut comes from
+// two levels of exact order statistics taken with wave ballots: each wave of 64 entries keeps
+// its 8 largest keys, and one wave keeps the `quota` largest of those 64 (quota is 8..16, six
+// times the slice's expected share of the k winners). Both levels drop a value that ties
+// across the boundary, so the lists stay honest. When the k-th largest listed key is at least
+// every slice's cut, the k best listed entries are exactly the k best of the row: every entry
+// left out lies strictly below its slice's cut. The finishing step checks that and searches
+// the whole row otherwise; a slice holds 12 or more of the k winners when it expects two with
+// probability ~1.4e-6.
 #pragma once
 
 #include "device_common.h"
 
 namespace csl {
 
-constexpr int kSliceMin = 512;                 // slice of the indexer-prepared path (one block)
-constexpr int kSliceR = 24;                    // candidate slots per slice
-constexpr int kMaxRowSlots = (1 << 18) / kSliceMin * kSliceR;  // 12288 slots per row
-constexpr int kMultiMaxEntries = 1 << 20;      // longest row of the multi-workgroup path
+constexpr int kSlice = 512;        // entries per slice (one decode indexer workgroup)
+constexpr int kSliceSlots = 16;    // listed candidates per slice at most
+constexpr int kWaveList = 8;       // largest keys kept per wave of 64 entries
+constexpr int kMultiMaxEntries = 1 << 20;  // longest row of the multi-workgroup path
 constexpr int kTopkMaxK = 4096;
-constexpr int kRowKernelMax = 40 * 1024;       // rows up to this length use one workgroup
+constexpr int kRowKernelMax = 40 * 1024;   // rows up to this length use one workgroup
 
-__host__ __device__ inline int topk_slice_size(int64_t max_entries) {
-  int S = kSliceMin;
-  while ((max_entries + S - 1) / S * kSliceR > kMaxRowSlots) S *= 2;
-  return S;
-}
-__host__ __device__ inline int64_t topk_num_slices(int64_t entries, int S) { return (entries + S - 1) / S; }
+__host__ __device__ inline int64_t topk_num_slices(int64_t entries) { return (entries + kSlice - 1) / kSlice; }
 
-// per-row workspace: cut per slice (padded to 256 bytes), then kSliceR slots per slice
+// per-row workspace: the cut of every slice (padded to 256 bytes), then kSliceSlots slots per slice
 __host__ __device__ inline size_t topk_cuts_bytes(int64_t max_entries) {
-  const int64_t ns = topk_num_slices(max_entries, topk_slice_size(max_entries));
-  return ((size_t)ns * 4 + 255) & ~(size_t)255;
+  return ((size_t)topk_num_slices(max_entries) * 4 + 255) & ~(size_t)255;
 }
 __host__ __device__ inline size_t topk_row_stride(int64_t max_entries) {
-  const int64_t ns = topk_num_slices(max_entries, topk_slice_size(max_entries));
-  return topk_cuts_bytes(max_entries) + (size_t)ns * kSliceR * 8;
+  return topk_cuts_bytes(max_entries) + (size_t)topk_num_slices(max_entries) * kSliceSlots * 8;
 }
 
 struct TopkRowWs {
@@ -55,11 +50,11 @@ __device__ __forceinline__ TopkRowWs topk_row_ws(void* ws, int64_t row, int64_t 
   return r;
 }
 
-// entries a slice of S aims to list: ~8x its expected share of the k winners, within [16, 20]
-__device__ __forceinline__ int slice_quota(int64_t n, int k, int S) {
-  int64_t q = (8 * (int64_t)k * S + n - 1) / (n > 0 ? n : 1);
-  if (q < 16) q = 16;
-  if (q > 20) q = 20;
+// entries a slice aims to list: ~6x its expected share of the k winners, within [8, 16]
+__device__ __forceinline__ int slice_quota(int64_t n, int k) {
+  int64_t q = (6 * (int64_t)k * kSlice + n - 1) / (n > 0 ? n : 1);
+  if (q < kWaveList) q = kWaveList;
+  if (q > kSliceSlots) q = kSliceSlots;
   return (int)q;
 }
 
@@ -69,6 +64,43 @@ __device__ __forceinline__ uint32_t rank_in_wave(uint64_t mask) {
   const uint32_t l = lane_id();
   const uint64_t below = (l == 0) ? 0ull : (mask & ((~0ull) >> (64 - l)));
   return (uint32_t)__popcll(below);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: row shifts (DPP) inside each row of 16
+// lanes, then the totals of the lower rows read back with readlane.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true);  // row_shr:8
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 47);
+  const uint32_t row = lane_id() >> 4;
+  return v + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+}
+
+// Maximum and minimum over the 64 lanes of a wave (wave-uniform results).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false));
+  return max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 15), (uint32_t)__builtin_amdgcn_readlane((int)v, 31)),
+             max((uint32_t)__builtin_amdgcn_readlane((int)v, 47), (uint32_t)__builtin_amdgcn_readlane((int)v, 63)));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return ~wave_max_u32(~v); }
+
+// Largest t with at least r lanes holding x >= t (r >= 1): the r-th largest x of the wave,
+// found bit by bit from ballot counts. Wave-uniform.
+__device__ __forceinline__ uint32_t wave_rth_largest(uint32_t x, int r) {
+  uint32_t t = 0;
+#pragma unroll
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = t | (1u << bit);
+    if (__popcll(__ballot(x >= c)) >= r) t = c;
+  }
+  return t;
 }
 
 // Exclusive prefix sum over a workgroup of NT threads. `wsum` holds >= NT/64 words.
@@ -149,64 +181,56 @@ __device__ __forceinline__ void find_threshold_bin(const uint32_t* hist, uint32_
   __syncthreads();
 }
 
-// Choose a slice's honest cut (at most kSliceR entries at or above it, about `quota` when
-// the keys allow) and write the cut and the listed (key << 32 | id) pairs, empty slots as 0.
-// keys: LDS [S], slots [0, nv) valid, slot s is entry id id_base + s. hist: LDS [2048];
-// wsum: LDS [NT/64]; res: LDS [4]. Keys of real scores are never 0 (0 marks an empty slot).
-template <int NT, int PER>
-__device__ void slice_cut_to_slots(const uint32_t* keys, int nv, int64_t id_base, int quota, uint32_t* hist,
-                                   uint32_t* wsum, uint32_t* res, uint32_t* cut_out, uint64_t* slots_out) {
-  const int tid = threadIdx.x;
-  uint32_t cut = 0;
-  if (nv > quota) {
-    for (int q = tid; q < 2048; q += NT) hist[q] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      const int s = j * NT + tid;
-      if (s < nv) atomicAdd(&hist[keys[s] >> 21], 1u);
-    }
-    __syncthreads();
-    find_threshold_bin<NT, 2048>(hist, (uint32_t)quota, wsum, res);
-    const uint32_t b1 = res[0], above = res[1], inbin = res[2];
-    __syncthreads();
-    if (above + inbin <= (uint32_t)kSliceR) {
-      cut = b1 << 21;
-    } else {
-      // the coarse bin holds too many: refine inside it on the next 11 key bits
-      for (int q = tid; q < 2048; q += NT) hist[q] = 0;
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int s = j * NT + tid;
-        if (s < nv && (keys[s] >> 21) == b1) atomicAdd(&hist[(keys[s] >> 10) & 2047u], 1u);
-      }
-      __syncthreads();
-      find_threshold_bin<NT, 2048>(hist, (uint32_t)quota - above, wsum, res);
-      const uint32_t b2 = res[0], above2 = res[1], inbin2 = res[2];
-      __syncthreads();
-      cut = (b1 << 21) | (b2 << 10);
-      if (above + above2 + inbin2 > (uint32_t)kSliceR) cut += 1u << 10;  // drop the tied bin: fewer, still honest
-    }
+static_assert(kSlice / kWave * kWaveList == kWave, "the wave lists of a slice fill one wave");
+static_assert(kSliceSlots <= kWave, "one wave writes the slice's slots");
+
+// LDS scratch of slice_candidates: every wave's list and cut
+struct SliceScratch {
+  uint32_t key[kSlice / kWave][kWaveList];
+  uint32_t off[kSlice / kWave][kWaveList];
+  uint32_t cut[kSlice / kWave];
+};
+
+// Write one slice's honest cut and its listed (key << 32 | id) pairs in ascending id order,
+// empty slots as 0. Called by all kSlice threads of a workgroup; thread i holds the key x of
+// the slice's entry i (0 for no entry; keys of real scores are never 0), whose id is
+// id_base + i. Contains one workgroup barrier; only wave 0 writes.
+__device__ __forceinline__ void slice_candidates(uint32_t x, int quota, SliceScratch& sc, int64_t id_base,
+                                                 uint32_t* cut_out, uint64_t* slots_out) {
+  const int lane = (int)lane_id();
+  const int wave = threadIdx.x / kWave;
+  // level 1: the wave's kWaveList largest keys; all of the wave's entries at or above th are listed
+  uint32_t th = wave_rth_largest(x, kWaveList);
+  uint64_t mk = __ballot(x != 0u && x >= th);
+  if (__popcll(mk) > kWaveList) {  // a tie across the boundary: list only the keys above it
+    th += 1u;
+    mk = __ballot(x >= th);
   }
-  uint32_t mine = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int s = j * NT + tid;
-    if (s < nv && keys[s] >= cut) ++mine;
+  if ((mk >> lane) & 1ull) {
+    const uint32_t r = rank_in_wave(mk);
+    sc.key[wave][r] = x;
+    sc.off[wave][r] = (uint32_t)threadIdx.x;
   }
-  uint32_t total;
-  uint32_t pos = block_exclusive_scan<NT>(mine, wsum, &total);
+  const int cw = __popcll(mk);
+  if (lane >= cw && lane < kWaveList) sc.key[wave][lane] = 0u;
+  if (lane == 0) sc.cut[wave] = th;
+  __syncthreads();
+  if (wave != 0) return;
+  // level 2: the quota largest of the wave lists, and never below a wave's own cut
+  const uint32_t y = sc.key[lane / kWaveList][lane % kWaveList];
+  const uint32_t yo = sc.off[lane / kWaveList][lane % kWaveList];
+  uint32_t cut = wave_rth_largest(y, quota);
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int s = j * NT + tid;
-    if (s < nv && keys[s] >= cut) {
-      if (pos < (uint32_t)kSliceR) slots_out[pos] = ((uint64_t)keys[s] << 32) | (uint64_t)(uint32_t)(id_base + s);
-      ++pos;
-    }
+  for (int w = 0; w < kSlice / kWave; ++w) cut = max(cut, sc.cut[w]);
+  uint64_t ms = __ballot(y != 0u && y >= cut);
+  if (__popcll(ms) > kSliceSlots) {
+    cut += 1u;
+    ms = __ballot(y >= cut);
   }
-  for (int q = (int)total + tid; q < kSliceR; q += NT) slots_out[q] = 0ull;
-  if (tid == 0) *cut_out = cut;
+  const int cnt = __popcll(ms);
+  if ((ms >> lane) & 1ull) slots_out[rank_in_wave(ms)] = ((uint64_t)y << 32) | (uint32_t)(id_base + yo);
+  if (lane >= cnt && lane < kSliceSlots) slots_out[lane] = 0ull;
+  if (lane == 0) *cut_out = cut;
 }
 
 }  // namespace csl

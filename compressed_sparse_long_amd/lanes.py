@@ -78,7 +78,7 @@ class CsaLane(_Lane):
         self.scores = torch.empty((self.B, self.T, max(self.max_entries, 1)), dtype=torch.float32, device=device)
         self.idx = torch.empty((self.B, self.T, self.k), dtype=torch.int32, device=device)
         nb = topk_workspace_bytes(self.B, self.T, self.max_entries, self.k)
-        self.topk_ws = torch.zeros(max(nb, 16), dtype=torch.uint8, device=device)  # zero once; calls keep it zero
+        self.topk_ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=device)  # contents never matter on entry
         na = attn_workspace_bytes(self.B, self.T, self.H, lane.D, self.k + self.W)
         self.attn_ws = torch.empty(max(na, 16), dtype=torch.uint8, device=device)
         self.kI_copies = [self.kI]

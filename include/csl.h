@@ -109,9 +109,10 @@ int csl_compress_kv(const void* kv, const void* z, const int64_t* kv_off, const 
  *   scores  fp32 [B, T, ld], ld >= max_entries
  *   topk_ws (nullable) with topk_ws_bytes >= csl_topk_workspace_bytes(B, T, max_entries,
  *           topk_k): when given with T == 1 and rows longer than 40960 entries, the kernel
- *           also leaves per-row top-k candidate lists in it (each 2048-entry slice keeps the
- *           entries above a slice-local cut), for the csl_topk_select call that follows with
- *           prepared = 1 (rows of at most 2^18 entries); for other shapes it is not touched.
+ *           also leaves per-row top-k candidate lists in it (each 512-entry slice lists at
+ *           most 16 entries, all of its entries above a slice-local cut), for the
+ *           csl_topk_select call that follows with prepared = 1 and the same k (rows of at
+ *           most 2^20 entries); for other shapes it is not touched.
  * Arithmetic: bf16 MFMA products with fp32 accumulation; fp8 codes are widened to bf16
  * exactly before the product and the group scale multiplies the fp32 dot.
  */

@@ -134,6 +134,11 @@ def _run_indexer(csl, HI, T, lengths, q_pos, fp8):
     dict(E=[262144], q_pos=[1 << 20], T=2, k=1024, levels=200),
     dict(E=[60000, 50000], q_pos=[240000, 200000], T=1, k=1000, levels=1),
     dict(E=[70000, 500], q_pos=[280000, 2000], T=1, k=4096, levels=0, neg=True),
+    # rows up to 2^20 (four 8-slot chunks per finishing thread)
+    dict(E=[1 << 20, 300000], q_pos=[1 << 22, 1200000], T=1, k=1024, levels=0),
+    # ties at the k-th key that the candidate lists still prove: the lower ids must win
+    dict(E=[262144], q_pos=[1 << 20], T=1, k=1024, levels=100000),
+    dict(E=[262144, 90000], q_pos=[1 << 20, 360000], T=1, k=2048, levels=20000, neg=True),
 ])
 def test_topk_bit_exact(csl, case):
     print(f"topk {case}", flush=True)
