@@ -241,7 +241,7 @@ def main():
         "config": {"workload": WORKLOAD, "batch": B, "context_tokens": lane.lengths[0], "entries": E,
                    "heads": H, "head_dim": D, "m": lane.m, "top_k": k, "window": W, "indexer_heads": HI,
                    "indexer_dim": CI, "rotated_copies": args.copies},
-        "roofline": {"kernel": "indexer_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+        "roofline": {"kernel": "indexer_decode_kernel", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "launch_us": round(idx_us, 3), "bytes_per_launch": idx_bytes},
         "step_us_one_graph_per_step": round(single_us, 2),

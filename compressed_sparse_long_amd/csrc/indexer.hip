@@ -3,25 +3,23 @@
 // The score of every visible compressed indexer key is a dense contraction
 // ([P5] indexer score formula; [P2] "Deep Dive", CSA Lightning Indexer): per query row,
 // [HI heads x CI] x [CI x n keys], followed by ReLU, the head weights and a sum over heads.
-// It runs on the gfx950 matrix cores as 16x16x32 bf16 MFMA tiles:
-//   A (16 rows)   = 16/HI query rows x HI heads, held in registers for the whole kernel,
-//   B (16 cols)   = 16 consecutive keys of one sequence, streamed from HBM,
-//   D (16 x 16)   = per (query row, head) x key dot products in fp32.
+// It runs on the gfx950 matrix cores as 16x16x32 bf16 MFMA tiles of 16/HI query rows x HI
+// heads against 16 consecutive keys of one sequence (streamed from HBM), dot products in fp32.
 // ReLU, the head weights, the optional fp8 group scale and the head sum run on the
 // accumulator registers, so each key costs 128 bytes of reads (64 for fp8) and 4 bytes
 // of score write per query row.
 //
-// Two tilings share the kernel:
-//   decode  (NB=1, WQ=1): one A tile per wave; the 8 waves of a block split a contiguous
-//           range of 512 keys, each wave issuing all its U=4 key tiles (8 KiB) in one pass
-//           (a single pass per wave keeps the memory pipeline full; looping waves do not).
-//   prefill (NB=8, WQ=4): each wave holds 8 A tiles (16/HI * 8 query rows) and the 4
-//           waves walk the same key range, so a key tile fetched once is reused for
-//           64/HI * 8 query rows through L1/L2.
-// With a top-k workspace (single query row per sequence, long rows), each decode
-// workgroup also keeps its 512 scores' keys in LDS and leaves that slice's top-k
-// candidate list in the workspace (topk_common.h), so the selection never re-reads the
-// scores.
+// Two tilings:
+//   decode  (indexer_decode_kernel): 8 waves per workgroup, each with one pass over its own
+//           64 consecutive keys (a single pass per wave keeps the memory pipeline full). The
+//           keys are the MFMA A operand and the query rows x heads the B operand, so the head
+//           sum is a DPP reduction inside a row of 16 lanes and the scores leave through LDS as
+//           coalesced 256-byte stores. With a top-k workspace (single query row per sequence,
+//           long rows) each workgroup also leaves its 512-entry slice's top-k candidate list
+//           (topk_common.h), so the selection never re-reads the scores.
+//   prefill (indexer_kernel, many query rows): each wave holds 8 A tiles of queries
+//           (16/HI * 8 query rows) and the 4 waves walk the same key range, so a key tile
+//           fetched once is reused for 64/HI * 8 query rows through L1/L2.
 #include "device_common.h"
 #include "launch.h"
 #include "topk_common.h"
@@ -60,16 +58,15 @@ __device__ __forceinline__ bf16x8 key_operand(const u32x4& k) {
   return as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
 }
 
-template <int HI, int NB, int NWAVES, int WQ, int U, bool FP8, bool PREP>
+template <int HI, int NB, int NWAVES, int WQ, int U, bool FP8>
 __global__ __launch_bounds__(NWAVES * 64) void indexer_kernel(
     const uint16_t* __restrict__ qI, const float* __restrict__ w, const void* __restrict__ kI,
     const float* __restrict__ k_scale, const int64_t* __restrict__ scale_off, int scale_group,
     const int64_t* __restrict__ ent_off, const int64_t* __restrict__ q_pos, int m, int T,
-    int64_t max_entries, float* __restrict__ scores, int64_t ld, int epw, void* topk_ws, int topk_k) {
+    int64_t max_entries, float* __restrict__ scores, int64_t ld, int epw) {
   constexpr int QPB = 16 / HI;       // query rows per A tile
   constexpr int QPW = NB * QPB;      // query rows per wave
   constexpr int WE = NWAVES / WQ;    // key sub-ranges per block
-  constexpr int NT = NWAVES * 64;
   constexpr int ROWS_PER_GROUP = (HI >= 4) ? 1 : 4 / HI;  // query rows in one lane group's 4 C rows
 
   const int wave = threadIdx.x / kWave;
@@ -99,10 +96,7 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_kernel(
   const int64_t e0 = wg_e0 + (int64_t)we * epw;
   const int64_t n_load = n_ent < max_entries ? n_ent : max_entries;
   const int64_t e_end = min(e0 + epw, n_load);
-  if (!PREP && e0 >= e_end) return;  // with PREP every wave must reach the slice barrier
-  constexpr int S = PREP ? WE * 16 * U : 1;  // a block's keys form one top-k slice
-  static_assert(!PREP || (S == kSlice && NT == kSlice), "a prepared slice is one decode block, one key per thread");
-  __shared__ uint32_t skeys[S];
+  if (e0 >= e_end) return;
 
   // A operands (queries) and the head weights this lane needs in the epilogue
   bf16x8 a[NB][2];
@@ -179,19 +173,124 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_kernel(
               float v = part[q];
               if (FP8) v *= sc[u];
               scores[((int64_t)b * T + tt) * ld + s] = v;
-              if (PREP) skeys[s - wg_e0] = score_key(v);
             }
           }
         }
       }
     }
   }
+}
+
+// Sum over the HI consecutive lanes that hold one query row's heads (HI a power of two up to
+// 16, groups aligned inside a row of 16 lanes): xor-1 and xor-2 quad permutes, then the
+// half-row and row mirrors, all DPP, so every lane of the group ends with the group sum.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+template <int HI>
+__device__ __forceinline__ float head_sum(float v) {
+  if (HI >= 2) v += dpp_f<0xb1>(v);   // quad_perm [1,0,3,2]
+  if (HI >= 4) v += dpp_f<0x4e>(v);   // quad_perm [2,3,0,1]
+  if (HI >= 8) v += dpp_f<0x141>(v);  // row_half_mirror
+  if (HI >= 16) v += dpp_f<0x140>(v); // row_mirror
+  return v;
+}
+
+// Decode tiling: 8 waves, each with one pass over its own 64 consecutive keys (4 tiles of 16).
+// The keys are the MFMA A operand and the 16/HI query rows x HI heads the B operand, so the
+// accumulator holds 4 keys x 1 (row, head) per lane and the head sum stays inside a row of 16
+// lanes (DPP). The scores go through LDS and leave as one coalesced 256-byte store per wave
+// and query row; with a top-k workspace (T == 1) every thread then holds the key of one entry
+// of the block's 512-entry slice for the candidate lists.
+template <int HI, bool FP8, bool PREP>
+__global__ __launch_bounds__(512) void indexer_decode_kernel(
+    const uint16_t* __restrict__ qI, const float* __restrict__ w, const void* __restrict__ kI,
+    const float* __restrict__ k_scale, const int64_t* __restrict__ scale_off, int scale_group,
+    const int64_t* __restrict__ ent_off, const int64_t* __restrict__ q_pos, int m, int T,
+    int64_t max_entries, float* __restrict__ scores, int64_t ld, void* topk_ws, int topk_k) {
+  constexpr int NW = 8;
+  constexpr int U = 4;
+  constexpr int EPW = 16 * U;   // keys per wave: one per lane on the way out
+  constexpr int EPB = EPW * NW; // keys per block
+  constexpr int QPB = 16 / HI;  // query rows per tile
+  static_assert(EPW == kWave && EPB == kSlice, "one key per thread, one slice per block");
+  __shared__ __align__(16) float sval[QPB][EPB];
+  __shared__ SliceScratch sc;
+
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int g = lane / 16;
+  const int c = lane % 16;
+  const int b = blockIdx.z;
+  const int t0 = blockIdx.y * QPB;
+
+  const int64_t e_base = ent_off[b];
+  const int64_t n_ent = ent_off[b + 1] - e_base;
+  const int64_t n_load = n_ent < max_entries ? n_ent : max_entries;
+  const int64_t wg_e0 = (int64_t)blockIdx.x * EPB;
+  const int64_t e0 = wg_e0 + (int64_t)wave * EPW;
+  const int64_t e_end = min(e0 + EPW, n_load);
+
+  // key tiles first: they depend on nothing but the sequence's entry range
+  u32x4 kb[U][2];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t s = e0 + u * 16 + c;
+    load_key_tile<FP8>(kI, e_base + s, s < e_end, g, kb[u][0], kb[u][1]);
+  }
+  float my_scale = 1.f;  // fp8 group scale of this lane's entry on the way out
+  if (FP8 && e0 + lane < e_end) my_scale = k_scale[scale_off[b] + (e0 + lane) / scale_group];
+
+  // B operand: column c is head c % HI of query row t0 + c / HI
+  const int tq = t0 + c / HI;
+  bf16x8 qb[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    u32x4 v = u32x4{0, 0, 0, 0};
+    if (tq < T) v = *reinterpret_cast<const u32x4*>(qI + (((int64_t)b * T + tq) * HI + c % HI) * 64 + kk * 32 + g * 8);
+    qb[kk] = as_bf16x8(v);
+  }
+  const float wc = (tq < T) ? w[((int64_t)b * T + tq) * HI + c % HI] : 0.f;
+  const int64_t p0 = q_pos[b];
+  auto n_vis = [&](int t) -> int64_t {
+    const int64_t p = p0 + t;
+    int64_t nv = (p >= 0 && p < ((int64_t)1 << 32)) ? (int64_t)((uint32_t)p / (uint32_t)m) : p / m;
+    nv = nv < n_load ? nv : n_load;
+    return nv < 0 ? 0 : nv;
+  };
+
+  const bool writer = (c % HI) == 0 && tq < T;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = mfma16x16x32(key_operand<FP8>(kb[u][0]), qb[0], acc);
+    acc = mfma16x16x32(key_operand<FP8>(kb[u][1]), qb[1], acc);
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = head_sum<HI>(wc * fmaxf(acc[i], 0.f));
+    if (writer)
+      *reinterpret_cast<float4*>(&sval[c / HI][wave * EPW + u * 16 + 4 * g]) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+  // each wave reads back only what it wrote: LDS operations of one wave complete in order
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  const int64_t s = e0 + lane;
+  float mine = 0.f;
+#pragma unroll
+  for (int q = 0; q < QPB; ++q) {
+    const int tt = t0 + q;
+    if (tt >= T) break;
+    const float val = sval[q][wave * EPW + lane] * my_scale;
+    if (q == 0) mine = val;
+    if (s < n_vis(tt)) scores[((int64_t)b * T + tt) * ld + s] = val;
+  }
   if (PREP) {
-    __shared__ SliceScratch sc;
-    __syncthreads();  // every wave's keys are in skeys
     const int64_t n = n_vis(0);
     if (n > topk_k && wg_e0 < n) {
-      const uint32_t x = (wg_e0 + threadIdx.x < n) ? skeys[threadIdx.x] : 0u;
+      const uint32_t x = (s < n) ? score_key(mine) : 0u;
       const TopkRowWs rw = topk_row_ws(topk_ws, (int64_t)b * T, max_entries);
       slice_candidates(x, slice_quota(n, topk_k), sc, wg_e0, &rw.cuts[blockIdx.x],
                        rw.slots + (int64_t)blockIdx.x * kSliceSlots);
@@ -215,24 +314,21 @@ hipError_t launch_hi(const void* qI, const float* w, const void* kI, const float
     const int64_t gx = (max_entries + epw - 1) / epw;
     const int gy = (T + QPW * WQ - 1) / (QPW * WQ);
     dim3 grid((unsigned)(gx > 0 ? gx : 1), (unsigned)gy, (unsigned)B);
-    indexer_kernel<HI, NB, NW, WQ, U, FP8, false><<<grid, NW * 64, 0, st>>>(
-        q16, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, T, max_entries, scores, ld, epw, nullptr, 0);
+    indexer_kernel<HI, NB, NW, WQ, U, FP8><<<grid, NW * 64, 0, st>>>(q16, w, kI, k_scale, scale_off, scale_group,
+                                                                    ent_off, q_pos, m, T, max_entries, scores, ld, epw);
   } else {
-    // decode tiling: every wave streams one pass of U key tiles (64 keys), 8 waves per block
-    constexpr int NB = 1, NW = 8, WQ = 1, U = 4;
-    constexpr int QPW = 16 / HI;
-    const int epw = 16 * U;
-    const int64_t per_block = (int64_t)epw * NW;
-    const int64_t gx = (max_entries + per_block - 1) / per_block;
-    const int gy = (T + QPW - 1) / QPW;
+    // decode tiling: 8 waves per block, each with one pass over 64 keys
+    constexpr int QPB = 16 / HI;
+    const int64_t gx = (max_entries + kSlice - 1) / kSlice;
+    const int gy = (T + QPB - 1) / QPB;
     dim3 grid((unsigned)(gx > 0 ? gx : 1), (unsigned)gy, (unsigned)B);
     if (prep)
-      indexer_kernel<HI, NB, NW, WQ, U, FP8, true><<<grid, NW * 64, 0, st>>>(
-          q16, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, T, max_entries, scores, ld, epw, topk_ws,
-          topk_k);
+      indexer_decode_kernel<HI, FP8, true><<<grid, kSlice, 0, st>>>(q16, w, kI, k_scale, scale_off, scale_group, ent_off,
+                                                                    q_pos, m, T, max_entries, scores, ld, topk_ws, topk_k);
     else
-      indexer_kernel<HI, NB, NW, WQ, U, FP8, false><<<grid, NW * 64, 0, st>>>(
-          q16, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, T, max_entries, scores, ld, epw, nullptr, 0);
+      indexer_decode_kernel<HI, FP8, false><<<grid, kSlice, 0, st>>>(q16, w, kI, k_scale, scale_off, scale_group,
+                                                                     ent_off, q_pos, m, T, max_entries, scores, ld,
+                                                                     nullptr, 0);
   }
   return hipGetLastError();
 }

@@ -6,10 +6,11 @@
 // slice writes, with plain stores and no atomics, its cut -- a key value such that every entry
 // of the slice whose key reaches the cut is listed -- and at most 16 listed (key << 32 | id)
 // pairs, in ascending id order, into its own slots (0 marks an empty slot). The cut comes from
-// two levels of exact order statistics taken with wave ballots: each wave of 64 entries keeps
-// its 8 largest keys, and one wave keeps the `quota` largest of those 64 (quota is 8..16, six
-// times the slice's expected share of the k winners). Both levels drop a value that ties
-// across the boundary, so the lists stay honest. When the k-th largest listed key is at least
+// two levels of order statistics taken with wave ballots: each wave of 64 entries keeps its 8
+// largest keys, and one wave keeps the `quota` largest of those 64 (quota is 8..16, six times
+// the slice's expected share of the k winners). Each level's cut is the r-th largest key or a
+// bit prefix of it that already admits exactly r keys, and a value that ties across the
+// boundary is dropped, so the lists stay honest. When the k-th largest listed key is at least
 // every slice's cut, the k best listed entries are exactly the k best of the row: every entry
 // left out lies strictly below its slice's cut. The finishing step checks that and searches
 // the whole row otherwise; a slice holds 12 or more of the k winners when it expects two with
@@ -91,14 +92,18 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 }
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return ~wave_max_u32(~v); }
 
-// Largest t with at least r lanes holding x >= t (r >= 1): the r-th largest x of the wave,
-// found bit by bit from ballot counts. Wave-uniform.
-__device__ __forceinline__ uint32_t wave_rth_largest(uint32_t x, int r) {
+// A threshold t with at least r lanes holding x >= t (r >= 1), found bit by bit from ballot
+// counts: the r-th largest x of the wave, or -- as soon as a prefix of it already has exactly
+// r lanes at or above it -- that prefix (every x >= t is then among those r). Wave-uniform.
+__device__ __forceinline__ uint32_t wave_rth_threshold(uint32_t x, int r) {
   uint32_t t = 0;
-#pragma unroll
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t c = t | (1u << bit);
-    if (__popcll(__ballot(x >= c)) >= r) t = c;
+    const int n = (int)__popcll(__ballot(x >= c));
+    if (n >= r) {
+      t = c;
+      if (n == r) break;
+    }
   }
   return t;
 }
@@ -200,7 +205,7 @@ __device__ __forceinline__ void slice_candidates(uint32_t x, int quota, SliceScr
   const int lane = (int)lane_id();
   const int wave = threadIdx.x / kWave;
   // level 1: the wave's kWaveList largest keys; all of the wave's entries at or above th are listed
-  uint32_t th = wave_rth_largest(x, kWaveList);
+  uint32_t th = wave_rth_threshold(x, kWaveList);
   uint64_t mk = __ballot(x != 0u && x >= th);
   if (__popcll(mk) > kWaveList) {  // a tie across the boundary: list only the keys above it
     th += 1u;
@@ -219,7 +224,7 @@ __device__ __forceinline__ void slice_candidates(uint32_t x, int quota, SliceScr
   // level 2: the quota largest of the wave lists, and never below a wave's own cut
   const uint32_t y = sc.key[lane / kWaveList][lane % kWaveList];
   const uint32_t yo = sc.off[lane / kWaveList][lane % kWaveList];
-  uint32_t cut = wave_rth_largest(y, quota);
+  uint32_t cut = wave_rth_threshold(y, quota);
 #pragma unroll
   for (int w = 0; w < kSlice / kWave; ++w) cut = max(cut, sc.cut[w]);
   uint64_t ms = __ballot(y != 0u && y >= cut);
