@@ -3,7 +3,8 @@
 
 One step is the whole CSA decode hot path for a batch of 4 sequences of 1,048,576 raw
 tokens (262,144 compressed entries each), 64 query heads, top-1024, window 128:
-  compress_kv (newest complete chunk) -> indexer_scores -> topk_select -> sparse_attn_decode.
+  compress_kv (newest complete chunk) -> indexer_scores -> topk_select -> sparse_attn_decode,
+issued as one csl_csa_decode_step call (the compression rides in the indexer's launch).
 Inputs are synthetic (seeded N(0,1) bf16, indexer N(0,1/64)), resident in HBM before the
 timed region. The compressed cache and the indexer keys are kept in several independent
 copies that consecutive steps rotate through, so every step streams from HBM rather than

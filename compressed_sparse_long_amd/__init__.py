@@ -13,7 +13,7 @@ import os
 import torch
 
 __all__ = [
-    "compress_kv", "indexer_scores", "topk_select", "sparse_attn_decode", "hca_attn_decode",
+    "compress_kv", "indexer_scores", "topk_select", "sparse_attn_decode", "hca_attn_decode", "csa_decode_step",
     "topk_workspace_bytes", "attn_workspace_bytes", "version", "LIB_PATH", "EXPORTS",
     "CslError",
 ]
@@ -24,8 +24,25 @@ BF16, F32, FP8_E4M3 = 0, 1, 2
 EXPORTS = [
     "csl_last_error", "csl_version", "csl_compress_kv", "csl_indexer_scores",
     "csl_topk_workspace_bytes", "csl_topk_select", "csl_attn_workspace_bytes",
-    "csl_sparse_attn_decode", "csl_hca_attn_decode",
+    "csl_sparse_attn_decode", "csl_hca_attn_decode", "csl_csa_decode_step",
 ]
+
+_P, _I, _L, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+
+class _CsaStep(ctypes.Structure):
+    """csl_csa_step (include/csl.h), field for field."""
+    _fields_ = [
+        ("kv", _P), ("z", _P), ("kv_off", _P), ("ent_off", _P), ("first_entry", _P), ("max_new_entries", _L),
+        ("ckv", _P),
+        ("q_idx", _P), ("w", _P), ("k_idx", _P), ("k_dtype", _I), ("k_scale", _P), ("scale_off", _P),
+        ("scale_group", _I), ("HI", _I), ("CI", _I), ("scores", _P), ("ld", _L), ("topk_ws", _P),
+        ("topk_ws_bytes", _S),
+        ("k", _I), ("idx", _P),
+        ("q", _P), ("H", _I), ("D", _I), ("n_win", _I), ("scale", _F), ("out", _P), ("lse", _P), ("attn_ws", _P),
+        ("attn_ws_bytes", _S),
+        ("q_pos", _P), ("m", _I), ("B", _I), ("T", _I), ("max_entries", _L),
+    ]
 
 
 class CslError(RuntimeError):
@@ -49,6 +66,7 @@ def _load() -> ctypes.CDLL:
         "csl_attn_workspace_bytes": (S, [I, I, I, I, L]),
         "csl_sparse_attn_decode": (I, [P, P, P, I, P, P, P, P, I, I, I, I, I, F, P, P, P, S, P]),
         "csl_hca_attn_decode": (I, [P, P, P, P, P, P, I, I, I, I, I, I, F, L, P, P, P, S, P]),
+        "csl_csa_decode_step": (I, [ctypes.POINTER(_CsaStep), P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -140,14 +158,14 @@ def topk_workspace_bytes(B: int, T: int, max_entries: int, k: int) -> int:
 
 def topk_select(scores, ent_off, q_pos, m: int, k: int, idx, ws=None, max_entries: int | None = None,
                 prepared: bool = False, stream=None):
-    """Top-k ids per row into idx int32 [B, T, k] (ascending, -1 padded). ``ws`` must be a
-    zero-initialised uint8 device tensor reused across calls; a fresh one is made if None."""
+    """Top-k ids per row into idx int32 [B, T, k] (ascending, -1 padded). ``ws`` is a uint8
+    device workspace (its contents do not matter); one is allocated if None and needed."""
     B, T, ld = scores.shape
     if max_entries is None:
         max_entries = ld
     need = topk_workspace_bytes(B, T, max_entries, k)
     if ws is None and need > 0:
-        ws = torch.zeros(need, dtype=torch.uint8, device=scores.device)
+        ws = torch.empty(need, dtype=torch.uint8, device=scores.device)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(_lib.csl_topk_select(
         _ptr(scores, "scores", _F32), ld, _ptr(ent_off, "ent_off", _I64), _ptr(q_pos, "q_pos", _I64), int(m), B, T,
@@ -195,4 +213,44 @@ def hca_attn_decode(q, ckv, kv, kv_off, ent_off, q_pos, m: int, n_win: int, out,
         _ptr(q, "q", _BF16), _ptr(ckv, "ckv", _BF16), _ptr(kv, "kv", _BF16), _ptr(kv_off, "kv_off", _I64),
         _ptr(ent_off, "ent_off", _I64), _ptr(q_pos, "q_pos", _I64), int(m), int(n_win), B, T, H, D, float(scale),
         int(max_entries), _ptr(out, "out", _F32), _ptr(lse, "lse", _F32), _ptr(ws, "ws"), wb, _stream(stream)))
+    return out
+
+
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def csa_decode_step(kv, z, kv_off, ent_off, first_entry, max_new_entries: int, ckv, qI, w, kI, scores, topk_ws,
+                    k: int, idx, q, n_win: int, out, q_pos, m: int, lse=None, scale: float | None = None,
+                    k_scale=None, scale_off=None, scale_group: int = 64, max_entries: int | None = None,
+                    attn_ws=None, stream=None):
+    """One whole CSA step (compress_kv of the newest entries into ckv, indexer_scores with
+    candidate lists, topk_select, sparse_attn_decode) in one C call; see csl.h."""
+    B, T, HI, CI = qI.shape
+    H, D = q.shape[2], q.shape[3]
+    if kI.dtype == torch.bfloat16:
+        kd = BF16
+    elif kI.dtype in (torch.uint8, torch.float8_e4m3fn):
+        kd = FP8_E4M3
+    else:
+        raise ValueError("kI must be bfloat16 or fp8 e4m3 (uint8 codes)")
+    ld = scores.shape[-1]
+    if max_entries is None:
+        max_entries = ld
+    if scale is None:
+        scale = D ** -0.5
+    attn_ws, awb = _attn_ws(attn_ws, B, T, H, D, k + n_win, q.device)
+    s = _CsaStep(
+        kv=_ptr(kv, "kv", _BF16), z=_ptr(z, "z", _BF16), kv_off=_ptr(kv_off, "kv_off", _I64),
+        ent_off=_ptr(ent_off, "ent_off", _I64), first_entry=_ptr(first_entry, "first_entry", _I64),
+        max_new_entries=int(max_new_entries), ckv=_ptr(ckv, "ckv", _BF16),
+        q_idx=_ptr(qI, "qI", _BF16), w=_ptr(w, "w", _F32), k_idx=_ptr(kI, "kI"), k_dtype=kd,
+        k_scale=_ptr(k_scale, "k_scale", _F32), scale_off=_ptr(scale_off, "scale_off", _I64),
+        scale_group=int(scale_group), HI=HI, CI=CI, scores=_ptr(scores, "scores", _F32), ld=ld,
+        topk_ws=_ptr(topk_ws, "topk_ws"), topk_ws_bytes=_nbytes(topk_ws),
+        k=int(k), idx=_ptr(idx, "idx", (torch.int32,)),
+        q=_ptr(q, "q", _BF16), H=H, D=D, n_win=int(n_win), scale=float(scale), out=_ptr(out, "out", _F32),
+        lse=_ptr(lse, "lse", _F32), attn_ws=_ptr(attn_ws, "attn_ws"), attn_ws_bytes=awb,
+        q_pos=_ptr(q_pos, "q_pos", _I64), m=int(m), B=B, T=T, max_entries=int(max_entries))
+    _check(_lib.csl_csa_decode_step(ctypes.byref(s), _stream(stream)))
     return out

@@ -48,9 +48,14 @@ const char* csl_last_error(void) { return g_last_error.c_str(); }
 
 int csl_version(void) { return 100; }
 
-int csl_compress_kv(const void* kv, const void* z, const int64_t* kv_off, const int64_t* ent_off,
-                    const int64_t* first_entry, int B, int D, int m, int64_t max_new_entries, void* out,
-                    int out_dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation halves of the entry points: CSL_OK when the arguments are good (the launch may
+// still have nothing to do), an error status (with the message set) otherwise.
+int check_compress(const void* kv, const void* z, const int64_t* kv_off, const int64_t* ent_off, int B, int D, int m,
+                   int64_t max_new_entries, const void* out, int out_dtype) {
   if (B < 0 || max_new_entries < 0) return fail(CSL_ERR_INVALID, "compress_kv: negative B or max_new_entries");
   if (!kv || !kv_off || !ent_off || !out) return fail(CSL_ERR_INVALID, "compress_kv: null pointer argument");
   if (m < 1 || m > 65536) return fail(CSL_ERR_INVALID, "compress_kv: m must be in [1, 65536], got %d", m);
@@ -61,16 +66,14 @@ int csl_compress_kv(const void* kv, const void* z, const int64_t* kv_off, const 
   if (B > kMaxGridY) return fail(CSL_ERR_UNSUPPORTED, "compress_kv: B must be <= %d", kMaxGridY);
   if (!aligned(kv, 16) || (z && !aligned(z, 16)) || !aligned(out, 16))
     return fail(CSL_ERR_INVALID, "compress_kv: kv, z and out must be 16-byte aligned");
-  if (B == 0 || max_new_entries == 0) return ok();
-  return hip_status(csl::launch_compress(kv, z, kv_off, ent_off, first_entry, B, D, m, max_new_entries, out,
-                                         out_dtype == CSL_DTYPE_BF16, as_stream(stream)),
-                    "compress_kv launch");
+  return CSL_OK;
 }
 
-int csl_indexer_scores(const void* q_idx, const float* w, const void* k_idx, int k_dtype, const float* k_scale,
-                       const int64_t* scale_off, int scale_group, const int64_t* ent_off, const int64_t* q_pos, int m,
-                       int B, int T, int HI, int CI, int64_t max_entries, float* scores, int64_t ld, void* topk_ws,
-                       size_t topk_ws_bytes, int topk_k, void* stream) {
+// topk_ws is cleared when the shapes need no candidate lists
+int check_indexer(const void* q_idx, const float* w, const void* k_idx, int k_dtype, const float* k_scale,
+                  const int64_t* scale_off, int scale_group, const int64_t* ent_off, const int64_t* q_pos, int m, int B,
+                  int T, int HI, int CI, int64_t max_entries, const float* scores, int64_t ld, void*& topk_ws,
+                  size_t topk_ws_bytes, int topk_k) {
   if (B < 0 || T < 0 || max_entries < 0) return fail(CSL_ERR_INVALID, "indexer_scores: negative size");
   if (!q_idx || !w || !k_idx || !ent_off || !q_pos || !scores)
     return fail(CSL_ERR_INVALID, "indexer_scores: null pointer argument");
@@ -98,9 +101,57 @@ int csl_indexer_scores(const void* q_idx, const float* w, const void* k_idx, int
     if (!aligned(topk_ws, 16)) return fail(CSL_ERR_INVALID, "indexer_scores: topk_ws must be 16-byte aligned");
     if (need == 0) topk_ws = nullptr;  // short rows: the selection needs no candidate lists
   }
+  return CSL_OK;
+}
+
+int check_topk(const float* scores, int64_t ld, const int64_t* ent_off, const int64_t* q_pos, int m, int B, int T,
+               int k, int64_t max_entries, const int32_t* idx, const void* ws, size_t ws_bytes) {
+  if (B < 0 || T < 0 || max_entries < 0) return fail(CSL_ERR_INVALID, "topk_select: negative size");
+  if (!scores || !ent_off || !q_pos || !idx) return fail(CSL_ERR_INVALID, "topk_select: null pointer argument");
+  if (m < 1) return fail(CSL_ERR_INVALID, "topk_select: m must be >= 1");
+  if (k < 1 || k > csl::topk_max_k())
+    return fail(CSL_ERR_UNSUPPORTED, "topk_select: k must be in [1, %d], got %d", csl::topk_max_k(), k);
+  if (max_entries > csl::topk_max_entries())
+    return fail(CSL_ERR_UNSUPPORTED, "topk_select: max_entries must be <= %lld", (long long)csl::topk_max_entries());
+  if (ld < max_entries) return fail(CSL_ERR_INVALID, "topk_select: ld < max_entries");
+  if ((int64_t)B * T > 0x7fffffff) return fail(CSL_ERR_UNSUPPORTED, "topk_select: too many rows");
+  if (B == 0 || T == 0) return CSL_OK;
+  const size_t need = csl_topk_workspace_bytes(B, T, max_entries, k);
+  if (need > 0) {
+    if ((int64_t)B * T > kMaxGridY) return fail(CSL_ERR_UNSUPPORTED, "topk_select: long rows need B*T <= %d", kMaxGridY);
+    if (!ws || ws_bytes < need)
+      return fail(CSL_ERR_WORKSPACE, "topk_select: workspace of %zu bytes required, got %zu", need, ws ? ws_bytes : 0);
+    if (!aligned(ws, 16)) return fail(CSL_ERR_INVALID, "topk_select: workspace must be 16-byte aligned");
+  }
+  return CSL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int csl_compress_kv(const void* kv, const void* z, const int64_t* kv_off, const int64_t* ent_off,
+                    const int64_t* first_entry, int B, int D, int m, int64_t max_new_entries, void* out,
+                    int out_dtype, void* stream) {
+  const int st = check_compress(kv, z, kv_off, ent_off, B, D, m, max_new_entries, out, out_dtype);
+  if (st != CSL_OK) return st;
+  if (B == 0 || max_new_entries == 0) return ok();
+  return hip_status(csl::launch_compress(kv, z, kv_off, ent_off, first_entry, B, D, m, max_new_entries, out,
+                                         out_dtype == CSL_DTYPE_BF16, as_stream(stream)),
+                    "compress_kv launch");
+}
+
+int csl_indexer_scores(const void* q_idx, const float* w, const void* k_idx, int k_dtype, const float* k_scale,
+                       const int64_t* scale_off, int scale_group, const int64_t* ent_off, const int64_t* q_pos, int m,
+                       int B, int T, int HI, int CI, int64_t max_entries, float* scores, int64_t ld, void* topk_ws,
+                       size_t topk_ws_bytes, int topk_k, void* stream) {
+  const int st = check_indexer(q_idx, w, k_idx, k_dtype, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T, HI,
+                               CI, max_entries, scores, ld, topk_ws, topk_ws_bytes, topk_k);
+  if (st != CSL_OK) return st;
   if (B == 0 || T == 0 || max_entries == 0) return ok();
-  return hip_status(csl::launch_indexer(q_idx, w, k_idx, fp8, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T,
-                                        HI, max_entries, scores, ld, topk_ws, topk_k, as_stream(stream)),
+  return hip_status(csl::launch_indexer(q_idx, w, k_idx, k_dtype == CSL_DTYPE_FP8_E4M3, k_scale, scale_off, scale_group,
+                                        ent_off, q_pos, m, B, T, HI, max_entries, scores, ld, topk_ws, topk_k,
+                                        as_stream(stream)),
                     "indexer_scores launch");
 }
 
@@ -112,23 +163,9 @@ size_t csl_topk_workspace_bytes(int B, int T, int64_t max_entries, int k) {
 int csl_topk_select(const float* scores, int64_t ld, const int64_t* ent_off, const int64_t* q_pos, int m, int B,
                     int T, int k, int64_t max_entries, int32_t* idx, void* ws, size_t ws_bytes, int prepared,
                     void* stream) {
-  if (B < 0 || T < 0 || max_entries < 0) return fail(CSL_ERR_INVALID, "topk_select: negative size");
-  if (!scores || !ent_off || !q_pos || !idx) return fail(CSL_ERR_INVALID, "topk_select: null pointer argument");
-  if (m < 1) return fail(CSL_ERR_INVALID, "topk_select: m must be >= 1");
-  if (k < 1 || k > csl::topk_max_k())
-    return fail(CSL_ERR_UNSUPPORTED, "topk_select: k must be in [1, %d], got %d", csl::topk_max_k(), k);
-  if (max_entries > csl::topk_max_entries())
-    return fail(CSL_ERR_UNSUPPORTED, "topk_select: max_entries must be <= %lld", (long long)csl::topk_max_entries());
-  if (ld < max_entries) return fail(CSL_ERR_INVALID, "topk_select: ld < max_entries");
-  if ((int64_t)B * T > 0x7fffffff) return fail(CSL_ERR_UNSUPPORTED, "topk_select: too many rows");
+  const int st = check_topk(scores, ld, ent_off, q_pos, m, B, T, k, max_entries, idx, ws, ws_bytes);
+  if (st != CSL_OK) return st;
   if (B == 0 || T == 0) return ok();
-  const size_t need = csl_topk_workspace_bytes(B, T, max_entries, k);
-  if (need > 0) {
-    if ((int64_t)B * T > kMaxGridY) return fail(CSL_ERR_UNSUPPORTED, "topk_select: long rows need B*T <= %d", kMaxGridY);
-    if (!ws || ws_bytes < need)
-      return fail(CSL_ERR_WORKSPACE, "topk_select: workspace of %zu bytes required, got %zu", need, ws ? ws_bytes : 0);
-    if (!aligned(ws, 16)) return fail(CSL_ERR_INVALID, "topk_select: workspace must be 16-byte aligned");
-  }
   const bool use_lists = prepared != 0 && csl::indexer_prepares_topk(ws, T, max_entries);
   return hip_status(csl::launch_topk(scores, ld, ent_off, q_pos, m, B, T, k, max_entries, idx, ws, use_lists,
                                      as_stream(stream)),
@@ -189,6 +226,54 @@ int csl_hca_attn_decode(const void* q, const void* ckv, const void* kv, const in
   return hip_status(csl::launch_attention(false, q, ckv, nullptr, 0, kv, kv_off, ent_off, q_pos, m, n_win, B, T, H,
                                           scale, max_entries, max_keys, out, lse, ws, as_stream(stream)),
                     "hca_attn_decode launch");
+}
+
+int csl_csa_decode_step(const csl_csa_step* s, void* stream) {
+  if (!s) return fail(CSL_ERR_INVALID, "csa_decode_step: null argument");
+  // every part is validated before anything is enqueued
+  int st = check_compress(s->kv, s->z, s->kv_off, s->ent_off, s->B, s->D, s->m, s->max_new_entries, s->ckv,
+                          CSL_DTYPE_BF16);
+  if (st != CSL_OK) return st;
+  void* topk_ws = s->topk_ws;
+  st = check_indexer(s->q_idx, s->w, s->k_idx, s->k_dtype, s->k_scale, s->scale_off, s->scale_group, s->ent_off,
+                     s->q_pos, s->m, s->B, s->T, s->HI, s->CI, s->max_entries, s->scores, s->ld, topk_ws,
+                     s->topk_ws_bytes, s->k);
+  if (st != CSL_OK) return st;
+  st = check_topk(s->scores, s->ld, s->ent_off, s->q_pos, s->m, s->B, s->T, s->k, s->max_entries, s->idx, s->topk_ws,
+                  s->topk_ws_bytes);
+  if (st != CSL_OK) return st;
+  const int64_t max_keys = (int64_t)s->k + s->n_win;
+  st = check_attn("csa_decode_step", s->q, s->ckv, s->kv, s->kv_off, s->ent_off, s->q_pos, s->n_win, s->B, s->T, s->H,
+                  s->D, s->scale, s->out, s->attn_ws, s->attn_ws_bytes, max_keys);
+  if (st == -1) return ok();  // B or T is 0
+  if (st != CSL_OK) return st;
+
+  const hipStream_t hs = as_stream(stream);
+  const bool fp8 = s->k_dtype == CSL_DTYPE_FP8_E4M3;
+  const bool compress = s->max_new_entries > 0;
+  const bool index = s->max_entries > 0;
+  hipError_t e = hipSuccess;
+  if (compress && index && csl::indexer_carries_compress(topk_ws, s->B, s->T, s->max_entries, s->D, s->m)) {
+    // the newest-chunk compression rides in spare workgroups of the indexer launch
+    const csl::CompressJob job{s->kv, s->z, s->kv_off, s->first_entry, s->max_new_entries, s->ckv, s->m};
+    e = csl::launch_indexer(s->q_idx, s->w, s->k_idx, fp8, s->k_scale, s->scale_off, s->scale_group, s->ent_off,
+                            s->q_pos, s->m, s->B, s->T, s->HI, s->max_entries, s->scores, s->ld, topk_ws, s->k, hs, &job);
+  } else {
+    if (compress)
+      e = csl::launch_compress(s->kv, s->z, s->kv_off, s->ent_off, s->first_entry, s->B, s->D, s->m,
+                               s->max_new_entries, s->ckv, true, hs);
+    if (e == hipSuccess && index)
+      e = csl::launch_indexer(s->q_idx, s->w, s->k_idx, fp8, s->k_scale, s->scale_off, s->scale_group, s->ent_off,
+                              s->q_pos, s->m, s->B, s->T, s->HI, s->max_entries, s->scores, s->ld, topk_ws, s->k, hs);
+  }
+  if (e != hipSuccess) return hip_status(e, "csa_decode_step launch");
+  e = csl::launch_topk(s->scores, s->ld, s->ent_off, s->q_pos, s->m, s->B, s->T, s->k, s->max_entries, s->idx,
+                       s->topk_ws, csl::indexer_prepares_topk(topk_ws, s->T, s->max_entries), hs);
+  if (e != hipSuccess) return hip_status(e, "csa_decode_step launch");
+  return hip_status(csl::launch_attention(true, s->q, s->ckv, s->idx, s->k, s->kv, s->kv_off, s->ent_off, s->q_pos, 1,
+                                          s->n_win, s->B, s->T, s->H, s->scale, (int64_t)1 << 62, max_keys, s->out,
+                                          s->lse, s->attn_ws, hs),
+                    "csa_decode_step launch");
 }
 
 }  // extern "C"

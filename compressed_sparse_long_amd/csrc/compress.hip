@@ -1,15 +1,7 @@
-// compress_kv: softmax-weighted pooling of m consecutive raw K=V rows into one entry.
-//
-// Each compressed entry is, per dimension d, a softmax over the m chunk rows of the
-// logits z[:, d] applied to kv[:, d] ([P3] section 3: per-dimension weights of the chunk
-// tokens; [P2] "Deep Dive", CSA step 2 and HCA "How it works").
-//
-// Layout: a thread owns 8 consecutive dimensions (16 bytes of bf16) of one entry and a
-// strided subset of its rows; TPE = D/8 threads cover one row, RS row-splits of the same
-// entry sit TPE lanes apart inside a wave and merge their partial softmax states with
-// xor-shuffles. Loads are 16-byte, row-contiguous across the TPE lanes, so a wave reads
-// whole 256-byte rows. The whole kernel is an HBM stream: it reads 2*m*D*2 bytes and
-// writes D*4 (fp32) or D*2 (bf16) bytes per entry.
+// compress_kv: softmax-weighted pooling of m consecutive raw K=V rows into one entry
+// (compress_common.h holds the arithmetic and the thread layout). The whole kernel is an HBM
+// stream over the raw rows.
+#include "compress_common.h"
 #include "device_common.h"
 #include "launch.h"
 
@@ -17,148 +9,13 @@ namespace csl {
 
 namespace {
 
-constexpr int kRowsPerStep = 4;
-
 template <int TPE, int RS, bool HAS_Z, bool OUT_BF16>
 __global__ __launch_bounds__(256) void compress_kernel(
     const uint16_t* __restrict__ kv, const uint16_t* __restrict__ z,
     const int64_t* __restrict__ kv_off, const int64_t* __restrict__ ent_off,
     const int64_t* __restrict__ first_entry, int D, int m, int64_t max_new, void* __restrict__ out) {
-  constexpr int EPB = 256 / (TPE * RS);  // entries per block
-  const int t = threadIdx.x;
-  const int dg = t % TPE;
-  const int rs = (t / TPE) % RS;
-  const int el = t / (TPE * RS);
-  const int b = blockIdx.y;
-
-  const int64_t row0 = kv_off[b];
-  const int64_t n_rows = kv_off[b + 1] - row0;
-  const int64_t n_ent = n_rows / m;
-  int64_t first = first_entry ? first_entry[b] : 0;
-  if (first < 0) first = 0;
-  const int64_t rel = (int64_t)blockIdx.x * EPB + el;
-  const int64_t i = first + rel;
-  const bool valid = (rel < max_new) && (i < n_ent);
-
-  float mu[8], s[8], acc[8];
-#pragma unroll
-  for (int d = 0; d < 8; ++d) {
-    mu[d] = -INFINITY;
-    s[d] = 0.f;
-    acc[d] = 0.f;
-  }
-
-  if (valid) {
-    const int64_t base_row = row0 + i * (int64_t)m;
-    const uint16_t* kvp = kv + base_row * D + dg * 8;
-    const uint16_t* zp = HAS_Z ? (z + base_row * D + dg * 8) : nullptr;
-    // rows handled by this lane: r = rs + RS * j
-    const int my_rows = (m > rs) ? (m - rs + RS - 1) / RS : 0;
-    for (int j0 = 0; j0 < my_rows; j0 += kRowsPerStep) {
-      u32x4 kr[kRowsPerStep], zr[kRowsPerStep];
-      const int cnt = min(kRowsPerStep, my_rows - j0);
-#pragma unroll
-      for (int u = 0; u < kRowsPerStep; ++u) {
-        if (u < cnt) {
-          const int64_t r = rs + (int64_t)RS * (j0 + u);
-          kr[u] = *reinterpret_cast<const u32x4*>(kvp + r * D);
-          if (HAS_Z) zr[u] = *reinterpret_cast<const u32x4*>(zp + r * D);
-        }
-      }
-      if (HAS_Z) {
-        float zl[kRowsPerStep][8];
-#pragma unroll
-        for (int u = 0; u < kRowsPerStep; ++u) {
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            zl[u][2 * w] = bf16lo(zr[u][w]) * kLog2e;
-            zl[u][2 * w + 1] = bf16hi(zr[u][w]) * kLog2e;
-          }
-        }
-#pragma unroll
-        for (int d = 0; d < 8; ++d) {
-          float cmax = zl[0][d];
-#pragma unroll
-          for (int u = 1; u < kRowsPerStep; ++u)
-            if (u < cnt) cmax = fmaxf(cmax, zl[u][d]);
-          const float nmu = fmaxf(mu[d], cmax);
-          const float alpha = __builtin_amdgcn_exp2f(mu[d] - nmu);  // 0 on the first step
-          s[d] *= alpha;
-          acc[d] *= alpha;
-          mu[d] = nmu;
-        }
-#pragma unroll
-        for (int u = 0; u < kRowsPerStep; ++u) {
-          if (u < cnt) {
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              const float e0 = __builtin_amdgcn_exp2f(zl[u][2 * w] - mu[2 * w]);
-              const float e1 = __builtin_amdgcn_exp2f(zl[u][2 * w + 1] - mu[2 * w + 1]);
-              s[2 * w] += e0;
-              s[2 * w + 1] += e1;
-              acc[2 * w] = fmaf(e0, bf16lo(kr[u][w]), acc[2 * w]);
-              acc[2 * w + 1] = fmaf(e1, bf16hi(kr[u][w]), acc[2 * w + 1]);
-            }
-          }
-        }
-      } else {
-#pragma unroll
-        for (int u = 0; u < kRowsPerStep; ++u) {
-          if (u < cnt) {
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              acc[2 * w] += bf16lo(kr[u][w]);
-              acc[2 * w + 1] += bf16hi(kr[u][w]);
-              s[2 * w] += 1.f;
-              s[2 * w + 1] += 1.f;
-            }
-          }
-        }
-        if (cnt > 0) {
-#pragma unroll
-          for (int d = 0; d < 8; ++d) mu[d] = 0.f;
-        }
-      }
-    }
-  }
-
-  // merge the RS partial states of one entry (lanes TPE*2^j apart in the same wave)
-#pragma unroll
-  for (int step = 1; step < RS; step <<= 1) {
-    const int mask = TPE * step;
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      const float mu2 = shfl_xor_f(mu[d], mask);
-      const float s2 = shfl_xor_f(s[d], mask);
-      const float a2 = shfl_xor_f(acc[d], mask);
-      const float M = fmaxf(mu[d], mu2);
-      if (M == -INFINITY) continue;  // neither side saw a row
-      const float f1 = __builtin_amdgcn_exp2f(mu[d] - M);
-      const float f2 = __builtin_amdgcn_exp2f(mu2 - M);
-      s[d] = s[d] * f1 + s2 * f2;
-      acc[d] = acc[d] * f1 + a2 * f2;
-      mu[d] = M;
-    }
-  }
-
-  if (valid && rs == 0) {
-    const int64_t orow = ent_off[b] + i;
-    float o[8];
-#pragma unroll
-    for (int d = 0; d < 8; ++d) o[d] = acc[d] / s[d];
-    if (OUT_BF16) {
-      u32x4 v;
-      v.x = pack_bf16x2(o[0], o[1]);
-      v.y = pack_bf16x2(o[2], o[3]);
-      v.z = pack_bf16x2(o[4], o[5]);
-      v.w = pack_bf16x2(o[6], o[7]);
-      *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + orow * D + dg * 8) = v;
-    } else {
-      float* op = reinterpret_cast<float*>(out) + orow * D + dg * 8;
-      *reinterpret_cast<float4*>(op) = make_float4(o[0], o[1], o[2], o[3]);
-      *reinterpret_cast<float4*>(op + 4) = make_float4(o[4], o[5], o[6], o[7]);
-    }
-  }
+  compress_block<256, TPE, RS, HAS_Z, OUT_BF16>(kv, z, kv_off, ent_off, first_entry, D, m, max_new, out, blockIdx.y,
+                                                blockIdx.x);
 }
 
 template <int TPE, int RS>

@@ -20,6 +20,7 @@
 //   prefill (indexer_kernel, many query rows): each wave holds 8 A tiles of queries
 //           (16/HI * 8 query rows) and the 4 waves walk the same key range, so a key tile
 //           fetched once is reused for 64/HI * 8 query rows through L1/L2.
+#include "compress_common.h"
 #include "device_common.h"
 #include "launch.h"
 #include "topk_common.h"
@@ -202,13 +203,19 @@ __device__ __forceinline__ float head_sum(float v) {
 // accumulator holds 4 keys x 1 (row, head) per lane and the head sum stays inside a row of 16
 // lanes (DPP). The scores go through LDS and leave as one coalesced 256-byte store per wave
 // and query row; with a top-k workspace (T == 1) every thread then holds the key of one entry
-// of the block's 512-entry slice for the candidate lists.
+// of the block's 512-entry slice for the candidate lists. Workgroups past the key range
+// (blockIdx.x >= key_blocks, first query tile) run a CompressJob instead: 4 row-splits x 16
+// lanes per entry, one row per thread, so the job adds no registers to the streaming path.
+constexpr int kJobRS = 4;
+constexpr int kJobEntriesPerBlock = 512 / (16 * kJobRS);
+
 template <int HI, bool FP8, bool PREP>
 __global__ __launch_bounds__(512) void indexer_decode_kernel(
     const uint16_t* __restrict__ qI, const float* __restrict__ w, const void* __restrict__ kI,
     const float* __restrict__ k_scale, const int64_t* __restrict__ scale_off, int scale_group,
     const int64_t* __restrict__ ent_off, const int64_t* __restrict__ q_pos, int m, int T,
-    int64_t max_entries, float* __restrict__ scores, int64_t ld, void* topk_ws, int topk_k) {
+    int64_t max_entries, float* __restrict__ scores, int64_t ld, void* topk_ws, int topk_k, int key_blocks,
+    CompressJob job) {
   constexpr int NW = 8;
   constexpr int U = 4;
   constexpr int EPW = 16 * U;   // keys per wave: one per lane on the way out
@@ -218,6 +225,20 @@ __global__ __launch_bounds__(512) void indexer_decode_kernel(
   __shared__ __align__(16) float sval[QPB][EPB];
   __shared__ SliceScratch sc;
 
+  if ((int)blockIdx.x >= key_blocks) {
+    if (blockIdx.y == 0) {
+      const uint16_t* k16 = static_cast<const uint16_t*>(job.kv);
+      const uint16_t* z16 = static_cast<const uint16_t*>(job.z);
+      const int64_t blk = (int64_t)blockIdx.x - key_blocks;
+      if (z16)
+        compress_block<512, 16, kJobRS, true, true, 1>(k16, z16, job.kv_off, ent_off, job.first_entry, 128, job.m,
+                                                       job.max_new, job.out, blockIdx.z, blk);
+      else
+        compress_block<512, 16, kJobRS, false, true, 1>(k16, z16, job.kv_off, ent_off, job.first_entry, 128, job.m,
+                                                        job.max_new, job.out, blockIdx.z, blk);
+    }
+    return;
+  }
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   const int g = lane / 16;
@@ -302,11 +323,11 @@ template <int HI, bool FP8>
 hipError_t launch_hi(const void* qI, const float* w, const void* kI, const float* k_scale,
                      const int64_t* scale_off, int scale_group, const int64_t* ent_off,
                      const int64_t* q_pos, int m, int B, int T, int64_t max_entries, float* scores,
-                     int64_t ld, void* topk_ws, int topk_k, hipStream_t st) {
+                     int64_t ld, void* topk_ws, int topk_k, hipStream_t st, const CompressJob* job) {
   const uint16_t* q16 = static_cast<const uint16_t*>(qI);
   const int rows = B * T;
   const bool prep = indexer_prepares_topk(topk_ws, T, max_entries);
-  if (!prep && rows >= 64 && T >= 16) {
+  if (!prep && rows >= 64 && T >= 16) {  // prefill tiling (never carries a compress job)
     // prefill tiling: 8 A tiles per wave, 4 waves over the same keys
     constexpr int NB = 8, NW = 4, WQ = 4, U = 2;
     constexpr int QPW = NB * (16 / HI);
@@ -317,18 +338,22 @@ hipError_t launch_hi(const void* qI, const float* w, const void* kI, const float
     indexer_kernel<HI, NB, NW, WQ, U, FP8><<<grid, NW * 64, 0, st>>>(q16, w, kI, k_scale, scale_off, scale_group,
                                                                     ent_off, q_pos, m, T, max_entries, scores, ld, epw);
   } else {
-    // decode tiling: 8 waves per block, each with one pass over 64 keys
+    // decode tiling: 8 waves per block, each with one pass over 64 keys (plus the job's blocks)
     constexpr int QPB = 16 / HI;
-    const int64_t gx = (max_entries + kSlice - 1) / kSlice;
+    const int64_t kb = (max_entries + kSlice - 1) / kSlice;
+    const int64_t jb = job ? (job->max_new + kJobEntriesPerBlock - 1) / kJobEntriesPerBlock : 0;
     const int gy = (T + QPB - 1) / QPB;
-    dim3 grid((unsigned)(gx > 0 ? gx : 1), (unsigned)gy, (unsigned)B);
+    dim3 grid((unsigned)(kb + jb), (unsigned)gy, (unsigned)B);
+    const CompressJob none{};
+    const CompressJob& cj = job ? *job : none;
     if (prep)
       indexer_decode_kernel<HI, FP8, true><<<grid, kSlice, 0, st>>>(q16, w, kI, k_scale, scale_off, scale_group, ent_off,
-                                                                    q_pos, m, T, max_entries, scores, ld, topk_ws, topk_k);
+                                                                    q_pos, m, T, max_entries, scores, ld, topk_ws, topk_k,
+                                                                    (int)kb, cj);
     else
       indexer_decode_kernel<HI, FP8, false><<<grid, kSlice, 0, st>>>(q16, w, kI, k_scale, scale_off, scale_group,
                                                                      ent_off, q_pos, m, T, max_entries, scores, ld,
-                                                                     nullptr, 0);
+                                                                     nullptr, 0, (int)kb, cj);
   }
   return hipGetLastError();
 }
@@ -337,11 +362,11 @@ template <bool FP8>
 hipError_t launch_fp8(int HI, const void* qI, const float* w, const void* kI, const float* k_scale,
                       const int64_t* scale_off, int scale_group, const int64_t* ent_off,
                       const int64_t* q_pos, int m, int B, int T, int64_t max_entries, float* scores,
-                      int64_t ld, void* topk_ws, int topk_k, hipStream_t st) {
+                      int64_t ld, void* topk_ws, int topk_k, hipStream_t st, const CompressJob* job) {
 #define CSL_IDX_CASE(H)                                                                                          \
   case H:                                                                                                        \
     return launch_hi<H, FP8>(qI, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T, max_entries, \
-                             scores, ld, topk_ws, topk_k, st);
+                             scores, ld, topk_ws, topk_k, st, job);
   switch (HI) {
     CSL_IDX_CASE(1)
     CSL_IDX_CASE(2)
@@ -359,15 +384,24 @@ bool indexer_prepares_topk(const void* topk_ws, int T, int64_t max_entries) {
   return topk_ws != nullptr && T == 1 && !topk_uses_row_kernel(max_entries) && max_entries <= kMultiMaxEntries;
 }
 
+static bool uses_prefill_tiling(const void* topk_ws, int B, int T, int64_t max_entries) {
+  return !indexer_prepares_topk(topk_ws, T, max_entries) && (int64_t)B * T >= 64 && T >= 16;
+}
+
+bool indexer_carries_compress(const void* topk_ws, int B, int T, int64_t max_entries, int D, int m) {
+  return D == 128 && m >= 1 && m <= 8 && max_entries > 0 && !uses_prefill_tiling(topk_ws, B, T, max_entries);
+}
+
 hipError_t launch_indexer(const void* qI, const float* w, const void* kI, bool fp8, const float* k_scale,
                           const int64_t* scale_off, int scale_group, const int64_t* ent_off,
                           const int64_t* q_pos, int m, int B, int T, int HI, int64_t max_entries,
-                          float* scores, int64_t ld, void* topk_ws, int topk_k, hipStream_t stream) {
+                          float* scores, int64_t ld, void* topk_ws, int topk_k, hipStream_t stream,
+                          const CompressJob* job) {
   if (fp8)
     return launch_fp8<true>(HI, qI, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T, max_entries,
-                            scores, ld, topk_ws, topk_k, stream);
+                            scores, ld, topk_ws, topk_k, stream, job);
   return launch_fp8<false>(HI, qI, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T, max_entries,
-                           scores, ld, topk_ws, topk_k, stream);
+                           scores, ld, topk_ws, topk_k, stream, job);
 }
 
 }  // namespace csl

@@ -12,12 +12,27 @@ hipError_t launch_compress(const void* kv, const void* z, const int64_t* kv_off,
                            const int64_t* first_entry, int B, int D, int m, int64_t max_new_entries,
                            void* out, bool out_bf16, hipStream_t stream);
 
+// Newest-chunk compression (bf16 out, D = 128, m <= 8) that the decode indexer can run in
+// spare workgroups of its own launch.
+struct CompressJob {
+  const void* kv;
+  const void* z;
+  const int64_t* kv_off;
+  const int64_t* first_entry;
+  int64_t max_new;
+  void* out;
+  int m;
+};
+
 hipError_t launch_indexer(const void* qI, const float* w, const void* kI, bool fp8, const float* k_scale,
                           const int64_t* scale_off, int scale_group, const int64_t* ent_off,
                           const int64_t* q_pos, int m, int B, int T, int HI, int64_t max_entries,
-                          float* scores, int64_t ld, void* topk_ws, int topk_k, hipStream_t stream);
+                          float* scores, int64_t ld, void* topk_ws, int topk_k, hipStream_t stream,
+                          const CompressJob* job = nullptr);
 // whether launch_indexer leaves top-k candidate lists in topk_ws for these shapes
 bool indexer_prepares_topk(const void* topk_ws, int T, int64_t max_entries);
+// whether launch_indexer can carry a CompressJob for these shapes (decode tiling, D = 128, m <= 8)
+bool indexer_carries_compress(const void* topk_ws, int B, int T, int64_t max_entries, int D, int m);
 
 bool topk_uses_row_kernel(int64_t max_entries);
 int64_t topk_max_entries();

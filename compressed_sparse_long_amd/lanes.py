@@ -15,7 +15,7 @@ import math
 
 import torch
 
-from . import (attn_workspace_bytes, compress_kv, hca_attn_decode, indexer_scores, sparse_attn_decode,
+from . import (attn_workspace_bytes, compress_kv, csa_decode_step, hca_attn_decode, indexer_scores, sparse_attn_decode,
                topk_select, topk_workspace_bytes)
 
 
@@ -101,11 +101,21 @@ class CsaLane(_Lane):
                            self.ent_off, self.q_pos, self.W, self.out, lse=self.lse, scale=self.scale,
                            ws=self.attn_ws)
 
-    def step(self, r: int = 0):
-        self.compress_new(r)
-        self.index(r)
-        self.select()
-        self.attend(r)
+    def step(self, r: int = 0, fused: bool = True):
+        """One decode step on rotated copy r: one csa_decode_step call, or (fused=False) the
+        four entry points one after the other; both give the same result."""
+        if not fused:
+            self.compress_new(r)
+            self.index(r)
+            self.select()
+            self.attend(r)
+            return
+        csa_decode_step(self.kv, self.z, self.kv_off, self.ent_off, self.first_new, self.n_new,
+                        self.ckv_copies[r % len(self.ckv_copies)], self.qI, self.w,
+                        self.kI_copies[r % len(self.kI_copies)], self.scores,
+                        self.topk_ws, self.k, self.idx, self.q, self.W, self.out, self.q_pos,
+                        self.m, lse=self.lse, scale=self.scale, k_scale=self.k_scale, scale_off=self.scale_off,
+                        scale_group=self.scale_group, max_entries=self.max_entries, attn_ws=self.attn_ws)
 
 
 class HcaLane(_Lane):

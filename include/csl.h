@@ -183,6 +183,66 @@ int csl_hca_attn_decode(const void* q, const void* ckv, const void* kv, const in
                         int T, int H, int D, float scale, int64_t max_entries, float* out,
                         float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * csa_decode_step -- one whole CSA step of one layer ([P2] "Putting It Together"; [P1]
+ * section 4.1): exactly
+ *     csl_compress_kv(kv, z, kv_off, ent_off, first_entry, B, D, m, max_new_entries, ckv, BF16)
+ *     csl_indexer_scores(q_idx, w, k_idx, ..., scores, ld, topk_ws, topk_ws_bytes, k)
+ *     csl_topk_select(scores, ..., k, idx, topk_ws, topk_ws_bytes, prepared = 1)
+ *     csl_sparse_attn_decode(q, ckv, idx, k, kv, ..., n_win, ..., out, lse, attn_ws)
+ * in that order on one stream, with the same outputs (ckv rows, scores, idx, out, lse). The
+ * calls' own argument rules apply to the fields below, and everything is validated before
+ * anything is enqueued. Where the shapes allow (D == 128, m <= 8, the decode tiling of the
+ * indexer), the compression runs in spare workgroups of the indexer launch instead of a
+ * launch of its own; it never reads what the indexer writes, and the attention runs after
+ * both.
+ */
+typedef struct csl_csa_step {
+  /* raw K = V cache and the compression this step adds to ckv */
+  const void* kv;             /* bf16 [N_tot, D] */
+  const void* z;              /* bf16 [N_tot, D] compression logits, or NULL (uniform) */
+  const int64_t* kv_off;      /* device [B+1] */
+  const int64_t* ent_off;     /* device [B+1] */
+  const int64_t* first_entry; /* device [B] or NULL (0): first entry compressed */
+  int64_t max_new_entries;    /* entries compressed per sequence, >= 0 */
+  void* ckv;                  /* bf16 [E_tot, D] compressed cache: written, then attended */
+  /* indexer */
+  const void* q_idx;          /* bf16 [B, T, HI, CI] */
+  const float* w;             /* fp32 [B, T, HI] */
+  const void* k_idx;          /* [E_tot, CI] of k_dtype */
+  int k_dtype;
+  const float* k_scale;
+  const int64_t* scale_off;
+  int scale_group;
+  int HI;
+  int CI;
+  float* scores;              /* fp32 [B, T, ld] */
+  int64_t ld;
+  void* topk_ws;              /* csl_topk_workspace_bytes(B, T, max_entries, k) bytes */
+  size_t topk_ws_bytes;
+  /* selection */
+  int k;
+  int32_t* idx;               /* int32 [B, T, k] */
+  /* attention */
+  const void* q;              /* bf16 [B, T, H, D] */
+  int H;
+  int D;
+  int n_win;
+  float scale;
+  float* out;                 /* fp32 [B, T, H, D] */
+  float* lse;                 /* fp32 [B, T, H] or NULL */
+  void* attn_ws;              /* csl_attn_workspace_bytes(B, T, H, D, k + n_win) bytes */
+  size_t attn_ws_bytes;
+  /* geometry */
+  const int64_t* q_pos;       /* device [B] */
+  int m;
+  int B;
+  int T;
+  int64_t max_entries;
+} csl_csa_step;
+
+int csl_csa_decode_step(const csl_csa_step* s, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -133,3 +133,27 @@ def test_attention_validation_and_workspace(lib):
     L = ctypes.c_int64
     g.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, ctypes.c_float, L, P, P, P, ctypes.c_size_t, P]
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 128, 8, 1, 64, 128, 0.088, 1024, FAKE, None, FAKE, 0, None) == 1
+
+
+def test_step_validation(lib):
+    import compressed_sparse_long_amd as csl
+    f = lib.csl_csa_decode_step
+    f.argtypes = [ctypes.POINTER(csl._CsaStep), P]
+    f.restype = ctypes.c_int
+    assert f(None, None) == 1
+    base = dict(kv=FAKE, kv_off=FAKE, ent_off=FAKE, max_new_entries=1, ckv=FAKE, q_idx=FAKE, w=FAKE, k_idx=FAKE,
+                k_dtype=0, scale_group=64, HI=8, CI=64, scores=FAKE, ld=1000, k=64, idx=FAKE, q=FAKE, H=64, D=128,
+                n_win=128, scale=0.088, out=FAKE, q_pos=FAKE, m=4, B=1, T=1, max_entries=1000)
+
+    def call(**over):
+        s = csl._CsaStep(**{**base, **over})
+        return f(ctypes.byref(s), None)
+    assert call(HI=3) == 2                      # indexer heads
+    assert call(D=64) == 2                      # attention needs D = 128
+    assert call(idx=None) == 1
+    assert call(ld=999) == 1                    # ld < max_entries
+    assert call(k=0) == 2
+    assert call(kv=P((1 << 20) + 2)) == 1       # misaligned raw cache
+    assert call(m=0) == 1
+    assert call(B=0) == 0                       # nothing to do: nothing enqueued
+    assert _err(lib) == ""
