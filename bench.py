@@ -38,7 +38,7 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published peak
 WORKLOAD = "csa_decode_1m"
 COUNTER_FILE = os.path.join(ROOT, "profiles", "indexer_csa_decode_1m_counters.txt")
 INDEXER_SOURCES = ["compressed_sparse_long_amd/csrc/indexer.hip", "compressed_sparse_long_amd/csrc/device_common.h",
-                   "compressed_sparse_long_amd/csrc/topk_common.h"]
+                   "compressed_sparse_long_amd/csrc/topk_common.h", "compressed_sparse_long_amd/csrc/compress_common.h"]
 
 
 def parse():
