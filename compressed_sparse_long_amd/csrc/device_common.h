@@ -31,30 +31,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
-// One OCP E4M3FN code -> bf16 bits. Every finite e4m3 value is exact in bf16:
-// normal codes keep their 3 mantissa bits and rebias the exponent (7 -> 127);
-// subnormal codes f * 2^-9 are normalised; S.1111.111 becomes a quiet NaN.
-__device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t b) {
-  uint32_t s = (b & 0x80u) << 8;
-  uint32_t e = (b >> 3) & 0xfu;
-  uint32_t f = b & 0x7u;
-  uint32_t mag;
-  if (e == 0) {
-    // f * 2^-9 for f in 1..7 (0 stays 0): convert through fp32, exact
-    mag = __float_as_uint((float)f * 0.001953125f) >> 16;
-  } else if (e == 15 && f == 7) {
-    mag = 0x7fc0u;
-  } else {
-    mag = ((e + 120u) << 7) | (f << 4);
-  }
-  return s | mag;
-}
-
-// Four e4m3 codes packed in a 32-bit word -> two words of bf16 pairs.
+// Four OCP E4M3FN codes packed in a 32-bit word -> two words of bf16 pairs. gfx950's packed
+// conversion decodes OCP E4M3FN (bias 7, no infinities, S.1111.111 = NaN) to fp32 exactly;
+// every e4m3 value has at most 4 significant bits and an exponent inside bf16's range, so
+// keeping the upper half of each fp32 is the exact bf16.
 __device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t w) {
+  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);  // bytes 0 and 1
+  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);   // bytes 2 and 3
   u32x2 r;
-  r.x = e4m3_to_bf16_bits(w & 0xffu) | (e4m3_to_bf16_bits((w >> 8) & 0xffu) << 16);
-  r.y = e4m3_to_bf16_bits((w >> 16) & 0xffu) | (e4m3_to_bf16_bits(w >> 24) << 16);
+  r.x = (__float_as_uint(lo[0]) >> 16) | (__float_as_uint(lo[1]) & 0xffff0000u);
+  r.y = (__float_as_uint(hi[0]) >> 16) | (__float_as_uint(hi[1]) & 0xffff0000u);
   return r;
 }
 

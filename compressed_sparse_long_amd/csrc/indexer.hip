@@ -250,6 +250,7 @@ __global__ __launch_bounds__(512) void indexer_decode_kernel(
   const int64_t n_ent = ent_off[b + 1] - e_base;
   const int64_t n_load = n_ent < max_entries ? n_ent : max_entries;
   const int64_t wg_e0 = (int64_t)blockIdx.x * EPB;
+  if (wg_e0 >= n_load) return;  // the whole slice lies past this sequence: nothing to score or list
   const int64_t e0 = wg_e0 + (int64_t)wave * EPW;
   const int64_t e_end = min(e0 + EPW, n_load);
 
@@ -310,11 +311,12 @@ __global__ __launch_bounds__(512) void indexer_decode_kernel(
   }
   if (PREP) {
     const int64_t n = n_vis(0);
-    if (n > topk_k && wg_e0 < n) {
+    if (n > topk_k && wg_e0 < n && !topk_row_dense(n, topk_k)) {
       const uint32_t x = (s < n) ? score_key(mine) : 0u;
-      const TopkRowWs rw = topk_row_ws(topk_ws, (int64_t)b * T, max_entries);
-      slice_candidates(x, slice_quota(n, topk_k), sc, wg_e0, &rw.cuts[blockIdx.x],
-                       rw.slots + (int64_t)blockIdx.x * kSliceSlots);
+      const TopkRowWs rw = topk_row_ws(topk_ws, (int64_t)b * T, max_entries, topk_k);
+      const int R = topk_row_slots(n, max_entries, topk_k);
+      slice_candidates(x, slice_quota(n, topk_k, R), topk_wave_list(n, topk_k), R, sc, wg_e0, &rw.cuts[blockIdx.x],
+                       rw.slots + (int64_t)blockIdx.x * R);
     }
   }
 }

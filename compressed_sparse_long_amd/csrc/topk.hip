@@ -140,13 +140,15 @@ __global__ __launch_bounds__(kSlice) void topk_prepare_kernel(const float* __res
   const int row = blockIdx.y;
   const int b = row / T, t = row % T;
   const int64_t n = row_count(ent_off, q_pos, b, t, m, max_entries);
-  if (n <= k) return;  // the finishing kernel selects everything
+  if (n <= k || topk_row_dense(n, k)) return;  // the finishing kernel selects everything / searches the row
   const int64_t lo = (int64_t)blockIdx.x * kSlice;
   if (lo >= n) return;
   const int64_t i = lo + threadIdx.x;
   const uint32_t x = (i < n) ? score_key(scores[(int64_t)row * ld + i]) : 0u;
-  const TopkRowWs rw = topk_row_ws(ws, row, max_entries);
-  slice_candidates(x, slice_quota(n, k), sc, lo, &rw.cuts[blockIdx.x], rw.slots + (int64_t)blockIdx.x * kSliceSlots);
+  const TopkRowWs rw = topk_row_ws(ws, row, max_entries, k);
+  const int R = topk_row_slots(n, max_entries, k);
+  slice_candidates(x, slice_quota(n, k, R), topk_wave_list(n, k), R, sc, lo, &rw.cuts[blockIdx.x],
+                   rw.slots + (int64_t)blockIdx.x * R);
 }
 
 constexpr int kFinNT = 1024;
@@ -191,56 +193,139 @@ __device__ __forceinline__ void fin_threshold(const uint32_t* hist, uint32_t nee
   __syncthreads();
 }
 
-// Exact selection over the whole row from the scores: radix select on key << 32 | ~id,
-// then an ordered compaction. Used when the candidate lists cannot prove the selection.
+// Exact selection over the whole row from its scores, for rows whose candidate lists cannot
+// prove the selection and rows too dense for them. Passes over the row (from L2):
+//   1. block min and max of the keys;
+//   2. radix select of the keep-th largest key: 11 bits just below the keys' common prefix,
+//      then the rest (usually one more pass);
+//   3. ordered compaction in chunks of 8 * kFinNT ids with one packed block scan of the
+//      (above, tied) counts per chunk, lower ids first among keys tied at the threshold.
+// hist_a / hist_b: LDS [2048]; wsum: LDS [2 * kFinWaves]; res: LDS [4].
 __device__ void finish_full_row(const float* __restrict__ srow, int64_t n, uint32_t keep, int32_t* __restrict__ out,
-                                uint32_t* hist, uint32_t* wsum, uint32_t* res) {
+                                uint32_t* hist_a, uint32_t* hist_b, uint32_t* wsum, uint32_t* res) {
   const int tid = threadIdx.x;
-  uint64_t pre = 0;
-  int pb = 0;
-  uint32_t need = keep;
-  while (pb < 64) {
-    const int width = (64 - pb) < 11 ? (64 - pb) : 11;
-    const int shift = 64 - pb - width;
-    for (int q = tid; q < 2048; q += kFinNT) hist[q] = 0;
-    __syncthreads();
-    for (int64_t i = tid; i < n; i += kFinNT) {
-      const uint64_t C = ((uint64_t)score_key(srow[i]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)i);
-      if (pb == 0 || (C >> (64 - pb)) == pre) atomicAdd(&hist[(uint32_t)(C >> shift) & ((1u << width) - 1u)], 1u);
+  const int wave = tid / kWave;
+  // visit every key of the row: 16 coalesced loads in flight per thread
+  constexpr int U = 16;
+  auto for_keys = [&](auto&& fn) {
+    for (int64_t c0 = 0; c0 < n; c0 += (int64_t)U * kFinNT) {
+      float v[U];
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        const int64_t i = c0 + (int64_t)j * kFinNT + tid;
+        v[j] = (i < n) ? srow[i] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < U; ++j)
+        if (c0 + (int64_t)j * kFinNT + tid < n) fn(score_key(v[j]));
     }
-    __syncthreads();
-    find_threshold_bin<kFinNT, 2048>(hist, need, wsum, res);
-    const uint32_t d = res[0], above = res[1], in_bin = res[2];
-    pre = (pre << width) | d;
-    pb += width;
-    need -= above;
-    __syncthreads();
-    if (in_bin == need) break;
+  };
+  for (int q = tid; q < 2048; q += kFinNT) {
+    hist_a[q] = 0;
+    hist_b[q] = 0;
   }
-  uint32_t base = 0;
-  for (int64_t c0 = 0; c0 < n; c0 += kFinNT) {
-    const int64_t i = c0 + tid;
-    bool s = false;
-    if (i < n) {
-      const uint64_t C = ((uint64_t)score_key(srow[i]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)i);
-      s = (C >> (64 - pb)) >= pre;
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  for_keys([&](uint32_t x) {
+    kmin = min(kmin, x);
+    kmax = max(kmax, x);
+  });
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  if (lane_id() == 0) {
+    wsum[wave] = kmin;
+    wsum[kFinWaves + wave] = kmax;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kFinWaves; ++w) {
+    kmin = min(kmin, wsum[w]);
+    kmax = max(kmax, wsum[kFinWaves + w]);
+  }
+  // keys share their top `common` bits: bin the 11 below them first
+  const int common = __clz(kmin ^ kmax);
+  int shift = common >= 21 ? 0 : 21 - common;
+  uint32_t need = keep;
+  for_keys([&](uint32_t x) { atomicAdd(&hist_a[(x >> shift) & 2047u], 1u); });
+  __syncthreads();
+  fin_threshold<2048>(hist_a, need, wsum, res);
+  uint32_t prefix = ((shift < 21 ? (kmin >> shift) : 0u) & ~2047u) | res[0];
+  need -= res[1];
+  bool all_in = res[2] == need;
+  uint32_t* hist = hist_b;
+  while (!all_in && shift > 0) {
+    const int wb = shift < 11 ? shift : 11;
+    const int sb = shift - wb;
+    for_keys([&](uint32_t x) {
+      if ((x >> shift) == prefix) atomicAdd(&hist[(x >> sb) & ((1u << wb) - 1u)], 1u);
+    });
+    __syncthreads();
+    fin_threshold<2048>(hist, need, wsum, res);
+    prefix = (prefix << wb) | res[0];
+    shift = sb;
+    need -= res[1];
+    all_in = res[2] == need;
+    // the other histogram is free again (its last reads ended before fin_threshold's barriers)
+    uint32_t* other = (hist == hist_b) ? hist_a : hist_b;
+    for (int q = tid; q < 2048; q += kFinNT) other[q] = 0;
+    hist = other;
+    __syncthreads();
+  }
+  const uint32_t need_eq = all_in ? 0u : need;
+
+  constexpr int J = 16;
+  uint32_t gbase = 0, ebase = 0;
+  for (int64_t c0 = 0; c0 < n; c0 += (int64_t)J * kFinNT) {
+    const int64_t i0 = c0 + (int64_t)J * tid;
+    uint32_t gm = 0, em = 0;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int64_t i = i0 + j;
+      if (i < n) {
+        const uint32_t h = score_key(srow[i]) >> shift;
+        if (h > prefix || (all_in && h == prefix)) gm |= 1u << j;
+        else if (h == prefix) em |= 1u << j;
+      }
     }
-    uint32_t tot;
-    const uint32_t e = block_exclusive_scan<kFinNT>(s ? 1u : 0u, wsum, &tot);
-    if (s && base + e < keep) out[base + e] = (int32_t)i;
-    base += tot;
+    const uint32_t mine = (uint32_t)__popc(gm) | ((uint32_t)__popc(em) << 16);
+    const uint32_t incl = wave_incl_scan(mine);
+    if (lane_id() == kWave - 1) wsum[wave] = incl;
+    __syncthreads();
+    uint32_t before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kFinWaves; ++w) {
+      const uint32_t x = wsum[w];
+      before += (w < wave) ? x : 0u;
+      total += x;
+    }
+    __syncthreads();  // wsum is rewritten by the next chunk
+    const uint32_t ex = before + incl - mine;
+    uint32_t gpos = gbase + (ex & 0xffffu), epos = ebase + (ex >> 16);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const bool g = (gm >> j) & 1u, e = (em >> j) & 1u;
+      if (g) {
+        out[gpos + min(epos, need_eq)] = (int32_t)(i0 + j);
+        ++gpos;
+      } else if (e) {
+        if (epos < need_eq) out[gpos + epos] = (int32_t)(i0 + j);
+        ++epos;
+      }
+    }
+    gbase += total & 0xffffu;
+    ebase += total >> 16;
+    if (gbase + min(ebase, need_eq) >= keep) break;  // every winner placed
   }
 }
 
-// One workgroup per row. Thread i owns CH consecutive chunks of 8 slots (half a slice each),
-// so thread order is slot order is id order.
+// One workgroup per row. Thread i owns CH consecutive chunks of 8 slots (a slice of the row's
+// layout spans R / 8 chunks), so thread order is slot order is id order.
 template <int CH>
 __global__ __launch_bounds__(kFinNT) void topk_finish_kernel(const float* __restrict__ scores, int64_t ld,
                                                              const int64_t* __restrict__ ent_off,
                                                              const int64_t* __restrict__ q_pos, int m, int T, int k,
                                                              int64_t max_entries, int32_t* __restrict__ idx, void* ws) {
   constexpr int PER = 8;  // slots per chunk
-  static_assert(2 * PER == kSliceSlots, "a chunk is half a slice");
+  static_assert(kMinSliceSlots % PER == 0, "a slice spans whole chunks");
   __shared__ uint32_t hist_a[2048];
   __shared__ uint32_t hist_b[2048];
   __shared__ uint32_t hist_c[1024];
@@ -250,15 +335,14 @@ __global__ __launch_bounds__(kFinNT) void topk_finish_kernel(const float* __rest
   const int row = blockIdx.x;
   const int b = row / T, t = row % T;
   const int tid = threadIdx.x;
-  const TopkRowWs rw = topk_row_ws(ws, row, max_entries);
-  const int ns_max = (int)topk_num_slices(max_entries);
+  const TopkRowWs rw = topk_row_ws(ws, row, max_entries, k);
+  const int n_chunks = (int)(topk_num_slices(max_entries) * topk_slot_budget(max_entries, k) / PER);
   // every global read is issued up front: the thread's slots and cuts, then the row geometry
   uint64_t sl[CH][PER];
-  uint32_t cut[CH];
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int j = tid * CH + c;
-    const bool in = (j >> 1) < ns_max;
+    const bool in = j < n_chunks;
     const u32x4* src = reinterpret_cast<const u32x4*>(rw.slots + (int64_t)j * PER);
 #pragma unroll
     for (int q = 0; q < PER / 2; ++q) {
@@ -266,7 +350,6 @@ __global__ __launch_bounds__(kFinNT) void topk_finish_kernel(const float* __rest
       sl[c][2 * q] = ((uint64_t)v.y << 32) | v.x;
       sl[c][2 * q + 1] = ((uint64_t)v.w << 32) | v.z;
     }
-    cut[c] = in ? rw.cuts[j >> 1] : 0u;
   }
   const int64_t n = row_count(ent_off, q_pos, b, t, m, max_entries);
   const uint32_t keep = (uint32_t)(n < k ? n : k);
@@ -281,12 +364,26 @@ __global__ __launch_bounds__(kFinNT) void topk_finish_kernel(const float* __rest
     for (int p = tid; p < k; p += kFinNT) out[p] = p < n ? p : -1;
     return;
   }
+  if (topk_row_dense(n, k)) {
+    // winners too dense for candidate lists (more than 5 expected per wave of 64 entries):
+    // the lists were not written, search the row directly
+    finish_full_row(scores + (int64_t)row * ld, n, keep, out, hist_a, hist_b, wsum, res);
+    for (int p = (int)keep + tid; p < k; p += kFinNT) out[p] = -1;
+    return;
+  }
   const int ns = (int)topk_num_slices(n);
+  const int cps = topk_row_slots(n, max_entries, k) / PER;  // chunks per slice in this row's layout
+  uint32_t cut[CH];  // the cut of each chunk's slice (needed only at the final check)
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int sj = (tid * CH + c) / cps;
+    cut[c] = sj < ns ? rw.cuts[sj] : 0u;
+  }
   uint32_t key[CH][PER];
   uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
-    const bool in = ((tid * CH + c) >> 1) < ns;
+    const bool in = (tid * CH + c) / cps < ns;
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
       const uint32_t x = in ? (uint32_t)(sl[c][q] >> 32) : 0u;
@@ -372,7 +469,7 @@ __global__ __launch_bounds__(kFinNT) void topk_finish_kernel(const float* __rest
     uint32_t gmask = 0, emask = 0, viol = 0;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      if (((tid * CH + c) >> 1) < ns && cut[c] > lo) viol = 1;
+      if ((tid * CH + c) / cps < ns && cut[c] > lo) viol = 1;
 #pragma unroll
       for (int q = 0; q < PER; ++q) {
         const uint32_t x = key[c][q];
@@ -421,7 +518,10 @@ __global__ __launch_bounds__(kFinNT) void topk_finish_kernel(const float* __rest
         }
     }
   }
-  if (!ok) finish_full_row(scores + (int64_t)row * ld, n, keep, out, hist_a, wsum, res);
+  if (!ok) {
+    __syncthreads();  // every thread is done with the histograms and wsum
+    finish_full_row(scores + (int64_t)row * ld, n, keep, out, hist_a, hist_b, wsum, res);
+  }
   for (int p = (int)keep + tid; p < k; p += kFinNT) out[p] = -1;
 }
 
@@ -440,7 +540,7 @@ int64_t topk_max_entries() { return kMultiMaxEntries; }
 
 size_t topk_workspace_bytes(int B, int T, int64_t max_entries, int k) {
   if (topk_uses_row_kernel(max_entries) || max_entries <= k || max_entries > kMultiMaxEntries) return 0;
-  return (size_t)B * T * topk_row_stride(max_entries);
+  return (size_t)B * T * topk_row_stride(max_entries, k);
 }
 
 int topk_max_k() { return kTopkMaxK; }
@@ -460,13 +560,15 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int64_t* ent_off, 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  // chunks of 8 slots: 2 per slice, CH per thread
-  if (topk_num_slices(max_entries) * 2 <= kFinNT)
-    topk_finish_kernel<1><<<dim3((unsigned)rows), kFinNT, 0, st>>>(scores, ld, ent_off, q_pos, m, T, k, max_entries,
-                                                                    idx, ws);
-  else
-    topk_finish_kernel<4><<<dim3((unsigned)rows), kFinNT, 0, st>>>(scores, ld, ent_off, q_pos, m, T, k, max_entries,
-                                                                    idx, ws);
+  // chunks of 8 slots, CH per thread
+  const int64_t chunks = topk_num_slices(max_entries) * topk_slot_budget(max_entries, k) / 8;
+  const dim3 fg((unsigned)rows);
+  if (chunks <= kFinNT)
+    topk_finish_kernel<1><<<fg, kFinNT, 0, st>>>(scores, ld, ent_off, q_pos, m, T, k, max_entries, idx, ws);
+  else if (chunks <= 2 * kFinNT)
+    topk_finish_kernel<2><<<fg, kFinNT, 0, st>>>(scores, ld, ent_off, q_pos, m, T, k, max_entries, idx, ws);
+  else  // at most kMaxRowSlots / 8 = 4 * kFinNT chunks
+    topk_finish_kernel<4><<<fg, kFinNT, 0, st>>>(scores, ld, ent_off, q_pos, m, T, k, max_entries, idx, ws);
   return hipGetLastError();
 }
 

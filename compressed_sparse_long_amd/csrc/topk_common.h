@@ -4,17 +4,20 @@
 //
 // Slice candidates. A row of n scores is cut into slices of 512 consecutive entries. Every
 // slice writes, with plain stores and no atomics, its cut -- a key value such that every entry
-// of the slice whose key reaches the cut is listed -- and at most 16 listed (key << 32 | id)
-// pairs, in ascending id order, into its own slots (0 marks an empty slot). The cut comes from
-// two levels of order statistics taken with wave ballots: each wave of 64 entries keeps its 8
-// largest keys, and one wave keeps the `quota` largest of those 64 (quota is 8..16, six times
-// the slice's expected share of the k winners). Each level's cut is the r-th largest key or a
-// bit prefix of it that already admits exactly r keys, and a value that ties across the
-// boundary is dropped, so the lists stay honest. When the k-th largest listed key is at least
-// every slice's cut, the k best listed entries are exactly the k best of the row: every entry
-// left out lies strictly below its slice's cut. The finishing step checks that and searches
-// the whole row otherwise; a slice holds 12 or more of the k winners when it expects two with
-// probability ~1.4e-6.
+// of the slice whose key reaches the cut is listed -- and at most R listed (key << 32 | id)
+// pairs, in ascending id order, into its own R slots (0 marks an empty slot). A row's slot
+// budget is 16..64 per slice of the longest row of the call (about six times such a slice's
+// expected share of the winners), and a shorter row gives each of its slices up to 64. The cut comes from two levels of order statistics taken
+// with wave ballots: each wave of 64 entries keeps its 8 (or, where a wave expects more than
+// 3/4 of a winner, 16) largest keys, and one wave keeps the `quota` largest of those (quota is
+// 8..R, six times the slice's expected share of the k winners). Each level's cut is the r-th
+// largest key or a bit prefix of it that already admits exactly r keys, and a value that ties
+// across the boundary is dropped, so the lists stay honest. When the k-th largest listed key
+// is at least every slice's cut, the k best listed entries are exactly the k best of the row:
+// every entry left out lies strictly below its slice's cut. The finishing step checks that and
+// searches the whole row otherwise; at 1M context a slice holds 12 or more of the k winners
+// when it expects two with probability ~1.4e-6. Rows with more than 5 expected winners per
+// wave of 64 skip the lists.
 #pragma once
 
 #include "device_common.h"
@@ -22,20 +25,34 @@
 namespace csl {
 
 constexpr int kSlice = 512;        // entries per slice (one decode indexer workgroup)
-constexpr int kSliceSlots = 16;    // listed candidates per slice at most
-constexpr int kWaveList = 8;       // largest keys kept per wave of 64 entries
+constexpr int kMinSliceSlots = 16; // slots per slice of the longest row, at least
+constexpr int kMaxSliceSlots = 64; // slots one slice may take
+constexpr int kWaveListMax = 16;   // largest keys kept per wave of 64 entries, at most
 constexpr int kMultiMaxEntries = 1 << 20;  // longest row of the multi-workgroup path
 constexpr int kTopkMaxK = 4096;
 constexpr int kRowKernelMax = 40 * 1024;   // rows up to this length use one workgroup
 
 __host__ __device__ inline int64_t topk_num_slices(int64_t entries) { return (entries + kSlice - 1) / kSlice; }
 
-// per-row workspace: the cut of every slice (padded to 256 bytes), then kSliceSlots slots per slice
+constexpr int64_t kMaxRowSlots = 32768;    // slots per row at most (4 x 8 per finishing thread)
+
+// slots per slice of the longest row of a call: the power of two in [16, 64] at or above six
+// times a slice's expected share of the k winners, within kMaxRowSlots per row
+__host__ __device__ inline int topk_slot_budget(int64_t max_entries, int k) {
+  const int64_t want = (6 * (int64_t)k * kSlice + max_entries - 1) / (max_entries > 0 ? max_entries : 1);
+  const int64_t ns = topk_num_slices(max_entries);
+  int R = kMinSliceSlots;
+  while (R < kMaxSliceSlots && R < want && ns * 2 * R <= kMaxRowSlots) R *= 2;
+  return R;
+}
+
+// per-row workspace: the cut of every slice (padded to 256 bytes), then the slots of the
+// longest row's layout
 __host__ __device__ inline size_t topk_cuts_bytes(int64_t max_entries) {
   return ((size_t)topk_num_slices(max_entries) * 4 + 255) & ~(size_t)255;
 }
-__host__ __device__ inline size_t topk_row_stride(int64_t max_entries) {
-  return topk_cuts_bytes(max_entries) + (size_t)topk_num_slices(max_entries) * kSliceSlots * 8;
+__host__ __device__ inline size_t topk_row_stride(int64_t max_entries, int k) {
+  return topk_cuts_bytes(max_entries) + (size_t)topk_num_slices(max_entries) * topk_slot_budget(max_entries, k) * 8;
 }
 
 struct TopkRowWs {
@@ -43,19 +60,35 @@ struct TopkRowWs {
   uint64_t* slots;
 };
 
-__device__ __forceinline__ TopkRowWs topk_row_ws(void* ws, int64_t row, int64_t max_entries) {
-  char* base = static_cast<char*>(ws) + (size_t)row * topk_row_stride(max_entries);
+__device__ __forceinline__ TopkRowWs topk_row_ws(void* ws, int64_t row, int64_t max_entries, int k) {
+  char* base = static_cast<char*>(ws) + (size_t)row * topk_row_stride(max_entries, k);
   TopkRowWs r;
   r.cuts = reinterpret_cast<uint32_t*>(base);
   r.slots = reinterpret_cast<uint64_t*>(base + topk_cuts_bytes(max_entries));
   return r;
 }
 
-// entries a slice aims to list: ~6x its expected share of the k winners, within [8, 16]
-__device__ __forceinline__ int slice_quota(int64_t n, int k) {
+// slots per slice of a row of n entries: the largest of 16, 32, 64 inside the row's budget
+// (a shorter row has fewer slices to share it)
+__host__ __device__ inline int topk_row_slots(int64_t n, int64_t max_entries, int k) {
+  const int64_t ns = topk_num_slices(n);
+  const int64_t budget = topk_num_slices(max_entries) * topk_slot_budget(max_entries, k);
+  int R = kMinSliceSlots;
+  while (R < kMaxSliceSlots && ns * (2 * R) <= budget) R *= 2;
+  return R;
+}
+
+// keys listed per wave of 64 entries: 16 where a wave expects more than 3/4 of a winner
+__host__ __device__ inline int topk_wave_list(int64_t n, int k) { return 4 * 64 * (int64_t)k > 3 * n ? 16 : 8; }
+
+// rows with more than 5 expected winners per wave of 64 are searched whole
+__host__ __device__ inline bool topk_row_dense(int64_t n, int k) { return 64 * (int64_t)k > 5 * n; }
+
+// entries a slice aims to list: ~6x its expected share of the k winners, within [8, R]
+__device__ __forceinline__ int slice_quota(int64_t n, int k, int R) {
   int64_t q = (6 * (int64_t)k * kSlice + n - 1) / (n > 0 ? n : 1);
-  if (q < kWaveList) q = kWaveList;
-  if (q > kSliceSlots) q = kSliceSlots;
+  if (q < 8) q = 8;
+  if (q > R) q = R;
   return (int)q;
 }
 
@@ -92,14 +125,17 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 }
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return ~wave_max_u32(~v); }
 
-// A threshold t with at least r lanes holding x >= t (r >= 1), found bit by bit from ballot
-// counts: the r-th largest x of the wave, or -- as soon as a prefix of it already has exactly
-// r lanes at or above it -- that prefix (every x >= t is then among those r). Wave-uniform.
-__device__ __forceinline__ uint32_t wave_rth_threshold(uint32_t x, int r) {
+// A threshold t with at least r of the wave's values x0, x1 (two per lane; pass 0 for an
+// unused one) at or above it (r >= 1), found bit by bit from ballot counts: the r-th largest
+// value, or -- as soon as a prefix of it already has exactly r values at or above it -- that
+// prefix (every value >= t is then among those r). Wave-uniform.
+template <bool TWO>
+__device__ __forceinline__ uint32_t wave_rth_threshold(uint32_t x0, uint32_t x1, int r) {
   uint32_t t = 0;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t c = t | (1u << bit);
-    const int n = (int)__popcll(__ballot(x >= c));
+    int n = (int)__popcll(__ballot(x0 >= c));
+    if (TWO) n += (int)__popcll(__ballot(x1 >= c));
     if (n >= r) {
       t = c;
       if (n == r) break;
@@ -186,28 +222,29 @@ __device__ __forceinline__ void find_threshold_bin(const uint32_t* hist, uint32_
   __syncthreads();
 }
 
-static_assert(kSlice / kWave * kWaveList == kWave, "the wave lists of a slice fill one wave");
-static_assert(kSliceSlots <= kWave, "one wave writes the slice's slots");
+static_assert(kSlice / kWave * kWaveListMax == 2 * kWave, "the wave lists of a slice fill two values per lane");
+static_assert(kMaxSliceSlots <= kWave, "one wave writes the slice's slots");
 
 // LDS scratch of slice_candidates: every wave's list and cut
 struct SliceScratch {
-  uint32_t key[kSlice / kWave][kWaveList];
-  uint32_t off[kSlice / kWave][kWaveList];
+  uint32_t key[kSlice / kWave][kWaveListMax];
+  uint32_t off[kSlice / kWave][kWaveListMax];
   uint32_t cut[kSlice / kWave];
 };
 
-// Write one slice's honest cut and its listed (key << 32 | id) pairs in ascending id order,
-// empty slots as 0. Called by all kSlice threads of a workgroup; thread i holds the key x of
-// the slice's entry i (0 for no entry; keys of real scores are never 0), whose id is
-// id_base + i. Contains one workgroup barrier; only wave 0 writes.
-__device__ __forceinline__ void slice_candidates(uint32_t x, int quota, SliceScratch& sc, int64_t id_base,
-                                                 uint32_t* cut_out, uint64_t* slots_out) {
+// Write one slice's honest cut and its (at most R) listed (key << 32 | id) pairs in ascending
+// id order, empty slots as 0. Called by all kSlice threads of a workgroup; thread i holds the
+// key x of the slice's entry i (0 for no entry; keys of real scores are never 0), whose id is
+// id_base + i. wl (8 or 16) keys are kept per wave, quota <= R <= 64 per slice. Contains one
+// workgroup barrier; only wave 0 writes.
+__device__ __forceinline__ void slice_candidates(uint32_t x, int quota, int wl, int R, SliceScratch& sc,
+                                                 int64_t id_base, uint32_t* cut_out, uint64_t* slots_out) {
   const int lane = (int)lane_id();
   const int wave = threadIdx.x / kWave;
-  // level 1: the wave's kWaveList largest keys; all of the wave's entries at or above th are listed
-  uint32_t th = wave_rth_threshold(x, kWaveList);
+  // level 1: the wave's wl largest keys; all of the wave's entries at or above th are listed
+  uint32_t th = wave_rth_threshold<false>(x, 0u, wl);
   uint64_t mk = __ballot(x != 0u && x >= th);
-  if (__popcll(mk) > kWaveList) {  // a tie across the boundary: list only the keys above it
+  if (__popcll(mk) > wl) {  // a tie across the boundary: list only the keys above it
     th += 1u;
     mk = __ballot(x >= th);
   }
@@ -217,24 +254,29 @@ __device__ __forceinline__ void slice_candidates(uint32_t x, int quota, SliceScr
     sc.off[wave][r] = (uint32_t)threadIdx.x;
   }
   const int cw = __popcll(mk);
-  if (lane >= cw && lane < kWaveList) sc.key[wave][lane] = 0u;
+  if (lane >= cw && lane < wl) sc.key[wave][lane] = 0u;
   if (lane == 0) sc.cut[wave] = th;
   __syncthreads();
   if (wave != 0) return;
-  // level 2: the quota largest of the wave lists, and never below a wave's own cut
-  const uint32_t y = sc.key[lane / kWaveList][lane % kWaveList];
-  const uint32_t yo = sc.off[lane / kWaveList][lane % kWaveList];
-  uint32_t cut = wave_rth_threshold(y, quota);
+  // level 2: the quota largest of the wave lists (entry e = w * wl + j; lane holds e = lane
+  // and, with 16 per wave, e = 64 + lane), and never below a wave's own cut
+  const bool two = wl * (kSlice / kWave) > kWave;
+  const int e0 = lane, e1 = lane + kWave;
+  const uint32_t y0 = sc.key[e0 / wl][e0 % wl], o0 = sc.off[e0 / wl][e0 % wl];
+  const uint32_t y1 = two ? sc.key[e1 / wl][e1 % wl] : 0u, o1 = two ? sc.off[e1 / wl][e1 % wl] : 0u;
+  uint32_t cut = two ? wave_rth_threshold<true>(y0, y1, quota) : wave_rth_threshold<false>(y0, 0u, quota);
 #pragma unroll
   for (int w = 0; w < kSlice / kWave; ++w) cut = max(cut, sc.cut[w]);
-  uint64_t ms = __ballot(y != 0u && y >= cut);
-  if (__popcll(ms) > kSliceSlots) {
+  uint64_t m0 = __ballot(y0 != 0u && y0 >= cut), m1 = __ballot(y1 != 0u && y1 >= cut);
+  if (__popcll(m0) + __popcll(m1) > R) {
     cut += 1u;
-    ms = __ballot(y >= cut);
+    m0 = __ballot(y0 >= cut);
+    m1 = __ballot(y1 >= cut);
   }
-  const int cnt = __popcll(ms);
-  if ((ms >> lane) & 1ull) slots_out[rank_in_wave(ms)] = ((uint64_t)y << 32) | (uint32_t)(id_base + yo);
-  if (lane >= cnt && lane < kSliceSlots) slots_out[lane] = 0ull;
+  const int c0 = __popcll(m0), cnt = c0 + __popcll(m1);
+  if ((m0 >> lane) & 1ull) slots_out[rank_in_wave(m0)] = ((uint64_t)y0 << 32) | (uint32_t)(id_base + o0);
+  if ((m1 >> lane) & 1ull) slots_out[c0 + rank_in_wave(m1)] = ((uint64_t)y1 << 32) | (uint32_t)(id_base + o1);
+  if (lane >= cnt && lane < R) slots_out[lane] = 0ull;
   if (lane == 0) *cut_out = cut;
 }
 

@@ -110,9 +110,9 @@ int csl_compress_kv(const void* kv, const void* z, const int64_t* kv_off, const 
  *   topk_ws (nullable) with topk_ws_bytes >= csl_topk_workspace_bytes(B, T, max_entries,
  *           topk_k): when given with T == 1 and rows longer than 40960 entries, the kernel
  *           also leaves per-row top-k candidate lists in it (each 512-entry slice lists at
- *           most 16 entries, all of its entries above a slice-local cut), for the
- *           csl_topk_select call that follows with prepared = 1 and the same k (rows of at
- *           most 2^20 entries); for other shapes it is not touched.
+ *           most 16..64 entries, all of its entries above a slice-local cut), for the
+ *           csl_topk_select call that follows with prepared = 1 and the same k and
+ *           max_entries (rows of at most 2^20 entries); for other shapes it is not touched.
  * Arithmetic: bf16 MFMA products with fp32 accumulation; fp8 codes are widened to bf16
  * exactly before the product and the group scale multiplies the fp32 dot.
  */
@@ -136,10 +136,10 @@ int csl_indexer_scores(const void* q_idx, const float* w, const void* k_idx, int
  *   ws: device workspace of at least csl_topk_workspace_bytes(B, T, max_entries, k)
  *   bytes (may be NULL when that is 0); its contents on entry do not matter.
  *   prepared: 1 when the csl_indexer_scores call that wrote these scores was given this
- *   workspace and k (its candidate lists are then used instead of a pass over the scores);
- *   0 otherwise. The result is the same either way; if the lists cannot prove the selection
- *   exact (rows whose best entries crowd into a few 512-entry slices), the whole row is
- *   searched.
+ *   workspace, k and max_entries (its candidate lists are then used instead of a pass over
+ *   the scores); 0 otherwise. The result is the same either way; if the lists cannot prove
+ *   the selection exact (rows whose best entries crowd into a few 512-entry slices, or rows
+ *   with more than 5 expected winners per 64 entries), the whole row is searched.
  * Integer work only: scores are compared through an order-preserving 32-bit key.
  */
 size_t csl_topk_workspace_bytes(int B, int T, int64_t max_entries, int k);
