@@ -214,8 +214,8 @@ __global__ __launch_bounds__(512) void indexer_decode_kernel(
     const uint16_t* __restrict__ qI, const float* __restrict__ w, const void* __restrict__ kI,
     const float* __restrict__ k_scale, const int64_t* __restrict__ scale_off, int scale_group,
     const int64_t* __restrict__ ent_off, const int64_t* __restrict__ q_pos, int m, int T,
-    int64_t max_entries, float* __restrict__ scores, int64_t ld, void* topk_ws, int topk_k, int key_blocks,
-    CompressJob job) {
+    int64_t max_entries, float* __restrict__ scores, int64_t ld, void* topk_ws, int topk_k, int slot_budget,
+    int key_blocks, CompressJob job) {
   constexpr int NW = 8;
   constexpr int U = 4;
   constexpr int EPW = 16 * U;   // keys per wave: one per lane on the way out
@@ -313,8 +313,8 @@ __global__ __launch_bounds__(512) void indexer_decode_kernel(
     const int64_t n = n_vis(0);
     if (n > topk_k && wg_e0 < n && !topk_row_dense(n, topk_k)) {
       const uint32_t x = (s < n) ? score_key(mine) : 0u;
-      const TopkRowWs rw = topk_row_ws(topk_ws, (int64_t)b * T, max_entries, topk_k);
-      const int R = topk_row_slots(n, max_entries, topk_k);
+      const TopkRowWs rw = topk_row_ws(topk_ws, (int64_t)b * T, max_entries, slot_budget);
+      const int R = topk_row_slots(n, max_entries, slot_budget);
       slice_candidates(x, slice_quota(n, topk_k, R), topk_wave_list(n, topk_k), R, sc, wg_e0, &rw.cuts[blockIdx.x],
                        rw.slots + (int64_t)blockIdx.x * R);
     }
@@ -351,11 +351,11 @@ hipError_t launch_hi(const void* qI, const float* w, const void* kI, const float
     if (prep)
       indexer_decode_kernel<HI, FP8, true><<<grid, kSlice, 0, st>>>(q16, w, kI, k_scale, scale_off, scale_group, ent_off,
                                                                     q_pos, m, T, max_entries, scores, ld, topk_ws, topk_k,
-                                                                    (int)kb, cj);
+                                                                    topk_slot_budget(max_entries, topk_k), (int)kb, cj);
     else
       indexer_decode_kernel<HI, FP8, false><<<grid, kSlice, 0, st>>>(q16, w, kI, k_scale, scale_off, scale_group,
                                                                      ent_off, q_pos, m, T, max_entries, scores, ld,
-                                                                     nullptr, 0, (int)kb, cj);
+                                                                     nullptr, 0, 0, (int)kb, cj);
   }
   return hipGetLastError();
 }

@@ -135,7 +135,7 @@ __global__ __launch_bounds__(1024) void topk_row_kernel(const float* __restrict_
 __global__ __launch_bounds__(kSlice) void topk_prepare_kernel(const float* __restrict__ scores, int64_t ld,
                                                                const int64_t* __restrict__ ent_off,
                                                                const int64_t* __restrict__ q_pos, int m, int T, int k,
-                                                               int64_t max_entries, void* ws) {
+                                                               int64_t max_entries, void* ws, int budget) {
   __shared__ SliceScratch sc;
   const int row = blockIdx.y;
   const int b = row / T, t = row % T;
@@ -145,8 +145,8 @@ __global__ __launch_bounds__(kSlice) void topk_prepare_kernel(const float* __res
   if (lo >= n) return;
   const int64_t i = lo + threadIdx.x;
   const uint32_t x = (i < n) ? score_key(scores[(int64_t)row * ld + i]) : 0u;
-  const TopkRowWs rw = topk_row_ws(ws, row, max_entries, k);
-  const int R = topk_row_slots(n, max_entries, k);
+  const TopkRowWs rw = topk_row_ws(ws, row, max_entries, budget);
+  const int R = topk_row_slots(n, max_entries, budget);
   slice_candidates(x, slice_quota(n, k, R), topk_wave_list(n, k), R, sc, lo, &rw.cuts[blockIdx.x],
                    rw.slots + (int64_t)blockIdx.x * R);
 }
@@ -323,7 +323,8 @@ template <int CH>
 __global__ __launch_bounds__(kFinNT) void topk_finish_kernel(const float* __restrict__ scores, int64_t ld,
                                                              const int64_t* __restrict__ ent_off,
                                                              const int64_t* __restrict__ q_pos, int m, int T, int k,
-                                                             int64_t max_entries, int32_t* __restrict__ idx, void* ws) {
+                                                             int64_t max_entries, int32_t* __restrict__ idx, void* ws,
+                                                             int budget) {
   constexpr int PER = 8;  // slots per chunk
   static_assert(kMinSliceSlots % PER == 0, "a slice spans whole chunks");
   __shared__ uint32_t hist_a[2048];
@@ -335,22 +336,27 @@ __global__ __launch_bounds__(kFinNT) void topk_finish_kernel(const float* __rest
   const int row = blockIdx.x;
   const int b = row / T, t = row % T;
   const int tid = threadIdx.x;
-  const TopkRowWs rw = topk_row_ws(ws, row, max_entries, k);
-  const int n_chunks = (int)(topk_num_slices(max_entries) * topk_slot_budget(max_entries, k) / PER);
-  // every global read is issued up front: the thread's slots and cuts, then the row geometry
-  uint64_t sl[CH][PER];
+  const TopkRowWs rw = topk_row_ws(ws, row, max_entries, budget);
+  const int n_chunks = (int)(topk_num_slices(max_entries) * budget / PER);
+  // every slot load is issued up front, raw (unpacked only once all of them are out)
+  // (a chunk past the row's slots reads the row's first chunk instead, so the loads carry no
+  // branches; such a chunk also lies past the row's last slice and is masked below)
+  u32x4 raw[CH][PER / 2];
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int j = tid * CH + c;
-    const bool in = j < n_chunks;
-    const u32x4* src = reinterpret_cast<const u32x4*>(rw.slots + (int64_t)j * PER);
+    const u32x4* src = reinterpret_cast<const u32x4*>(rw.slots + (j < n_chunks ? (int64_t)j * PER : 0));
 #pragma unroll
-    for (int q = 0; q < PER / 2; ++q) {
-      const u32x4 v = in ? src[q] : u32x4{0, 0, 0, 0};
-      sl[c][2 * q] = ((uint64_t)v.y << 32) | v.x;
-      sl[c][2 * q + 1] = ((uint64_t)v.w << 32) | v.z;
-    }
+    for (int q = 0; q < PER / 2; ++q) raw[c][q] = src[q];
   }
+  // the cut of each chunk's slice for each possible layout (2, 4 or 8 chunks per slice; the
+  // row's own layout is known only with n), also issued now and needed only at the end
+  const int ns_max = (int)topk_num_slices(max_entries);
+  uint32_t cut3[CH][3];
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+#pragma unroll
+    for (int l = 0; l < 3; ++l) cut3[c][l] = rw.cuts[min((tid * CH + c) >> (l + 1), ns_max - 1)];
   const int64_t n = row_count(ent_off, q_pos, b, t, m, max_entries);
   const uint32_t keep = (uint32_t)(n < k ? n : k);
   int32_t* out = idx + (int64_t)row * k;
@@ -372,18 +378,21 @@ __global__ __launch_bounds__(kFinNT) void topk_finish_kernel(const float* __rest
     return;
   }
   const int ns = (int)topk_num_slices(n);
-  const int cps = topk_row_slots(n, max_entries, k) / PER;  // chunks per slice in this row's layout
-  uint32_t cut[CH];  // the cut of each chunk's slice (needed only at the final check)
+  // chunks per slice in this row's layout: 2, 4 or 8
+  const int cps_log2 = __ffs(topk_row_slots(n, max_entries, budget) / PER) - 1;
+  uint64_t sl[CH][PER];
 #pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const int sj = (tid * CH + c) / cps;
-    cut[c] = sj < ns ? rw.cuts[sj] : 0u;
-  }
+  for (int c = 0; c < CH; ++c)
+#pragma unroll
+    for (int q = 0; q < PER / 2; ++q) {
+      sl[c][2 * q] = ((uint64_t)raw[c][q].y << 32) | raw[c][q].x;
+      sl[c][2 * q + 1] = ((uint64_t)raw[c][q].w << 32) | raw[c][q].z;
+    }
   uint32_t key[CH][PER];
   uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
-    const bool in = (tid * CH + c) / cps < ns;
+    const bool in = ((tid * CH + c) >> cps_log2) < ns;
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
       const uint32_t x = in ? (uint32_t)(sl[c][q] >> 32) : 0u;
@@ -394,6 +403,10 @@ __global__ __launch_bounds__(kFinNT) void topk_finish_kernel(const float* __rest
       }
     }
   }
+  uint32_t cut[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+    cut[c] = cps_log2 == 1 ? cut3[c][0] : (cps_log2 == 2 ? cut3[c][1] : cut3[c][2]);
   const int wave = tid / kWave;
   kmin = wave_min_u32(kmin);
   kmax = wave_max_u32(kmax);
@@ -469,7 +482,7 @@ __global__ __launch_bounds__(kFinNT) void topk_finish_kernel(const float* __rest
     uint32_t gmask = 0, emask = 0, viol = 0;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      if ((tid * CH + c) / cps < ns && cut[c] > lo) viol = 1;
+      if (((tid * CH + c) >> cps_log2) < ns && cut[c] > lo) viol = 1;
 #pragma unroll
       for (int q = 0; q < PER; ++q) {
         const uint32_t x = key[c][q];
@@ -540,7 +553,7 @@ int64_t topk_max_entries() { return kMultiMaxEntries; }
 
 size_t topk_workspace_bytes(int B, int T, int64_t max_entries, int k) {
   if (topk_uses_row_kernel(max_entries) || max_entries <= k || max_entries > kMultiMaxEntries) return 0;
-  return (size_t)B * T * topk_row_stride(max_entries, k);
+  return (size_t)B * T * topk_row_stride(max_entries, topk_slot_budget(max_entries, k));
 }
 
 int topk_max_k() { return kTopkMaxK; }
@@ -554,21 +567,22 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int64_t* ent_off, 
     return launch_row<40>(scores, ld, ent_off, q_pos, m, B, T, k, max_entries, idx, st);
   }
   const int rows = B * T;
+  const int budget = topk_slot_budget(max_entries, k);
   if (!prepared) {
     dim3 grid((unsigned)topk_num_slices(max_entries), (unsigned)rows);
-    topk_prepare_kernel<<<grid, kSlice, 0, st>>>(scores, ld, ent_off, q_pos, m, T, k, max_entries, ws);
+    topk_prepare_kernel<<<grid, kSlice, 0, st>>>(scores, ld, ent_off, q_pos, m, T, k, max_entries, ws, budget);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   // chunks of 8 slots, CH per thread
-  const int64_t chunks = topk_num_slices(max_entries) * topk_slot_budget(max_entries, k) / 8;
+  const int64_t chunks = topk_num_slices(max_entries) * budget / 8;
   const dim3 fg((unsigned)rows);
   if (chunks <= kFinNT)
-    topk_finish_kernel<1><<<fg, kFinNT, 0, st>>>(scores, ld, ent_off, q_pos, m, T, k, max_entries, idx, ws);
+    topk_finish_kernel<1><<<fg, kFinNT, 0, st>>>(scores, ld, ent_off, q_pos, m, T, k, max_entries, idx, ws, budget);
   else if (chunks <= 2 * kFinNT)
-    topk_finish_kernel<2><<<fg, kFinNT, 0, st>>>(scores, ld, ent_off, q_pos, m, T, k, max_entries, idx, ws);
+    topk_finish_kernel<2><<<fg, kFinNT, 0, st>>>(scores, ld, ent_off, q_pos, m, T, k, max_entries, idx, ws, budget);
   else  // at most kMaxRowSlots / 8 = 4 * kFinNT chunks
-    topk_finish_kernel<4><<<fg, kFinNT, 0, st>>>(scores, ld, ent_off, q_pos, m, T, k, max_entries, idx, ws);
+    topk_finish_kernel<4><<<fg, kFinNT, 0, st>>>(scores, ld, ent_off, q_pos, m, T, k, max_entries, idx, ws, budget);
   return hipGetLastError();
 }
 

@@ -47,12 +47,13 @@ __host__ __device__ inline int topk_slot_budget(int64_t max_entries, int k) {
 }
 
 // per-row workspace: the cut of every slice (padded to 256 bytes), then the slots of the
-// longest row's layout
+// longest row's layout (budget = topk_slot_budget(max_entries, k), computed on the host and
+// handed to the kernels)
 __host__ __device__ inline size_t topk_cuts_bytes(int64_t max_entries) {
   return ((size_t)topk_num_slices(max_entries) * 4 + 255) & ~(size_t)255;
 }
-__host__ __device__ inline size_t topk_row_stride(int64_t max_entries, int k) {
-  return topk_cuts_bytes(max_entries) + (size_t)topk_num_slices(max_entries) * topk_slot_budget(max_entries, k) * 8;
+__host__ __device__ inline size_t topk_row_stride(int64_t max_entries, int budget) {
+  return topk_cuts_bytes(max_entries) + (size_t)topk_num_slices(max_entries) * budget * 8;
 }
 
 struct TopkRowWs {
@@ -60,8 +61,8 @@ struct TopkRowWs {
   uint64_t* slots;
 };
 
-__device__ __forceinline__ TopkRowWs topk_row_ws(void* ws, int64_t row, int64_t max_entries, int k) {
-  char* base = static_cast<char*>(ws) + (size_t)row * topk_row_stride(max_entries, k);
+__device__ __forceinline__ TopkRowWs topk_row_ws(void* ws, int64_t row, int64_t max_entries, int budget) {
+  char* base = static_cast<char*>(ws) + (size_t)row * topk_row_stride(max_entries, budget);
   TopkRowWs r;
   r.cuts = reinterpret_cast<uint32_t*>(base);
   r.slots = reinterpret_cast<uint64_t*>(base + topk_cuts_bytes(max_entries));
@@ -70,11 +71,10 @@ __device__ __forceinline__ TopkRowWs topk_row_ws(void* ws, int64_t row, int64_t 
 
 // slots per slice of a row of n entries: the largest of 16, 32, 64 inside the row's budget
 // (a shorter row has fewer slices to share it)
-__host__ __device__ inline int topk_row_slots(int64_t n, int64_t max_entries, int k) {
-  const int64_t ns = topk_num_slices(n);
-  const int64_t budget = topk_num_slices(max_entries) * topk_slot_budget(max_entries, k);
+__host__ __device__ inline int topk_row_slots(int64_t n, int64_t max_entries, int budget) {
+  const int64_t ns = topk_num_slices(n), total = topk_num_slices(max_entries) * budget;
   int R = kMinSliceSlots;
-  while (R < kMaxSliceSlots && ns * (2 * R) <= budget) R *= 2;
+  while (R < kMaxSliceSlots && ns * (2 * R) <= total) R *= 2;
   return R;
 }
 
