@@ -55,6 +55,12 @@ __device__ __forceinline__ RowGeom row_geom(const int64_t* kv_off, const int64_t
   return g;
 }
 
+// 16-byte load through a pointer known to address global memory (a pointer that passed
+// through LDS as an integer would otherwise become a flat access)
+__device__ __forceinline__ u32x4 load_global16(const uint16_t* p) {
+  return *(const __attribute__((address_space(1))) u32x4*)(p);
+}
+
 template <int NHG, bool SPARSE>
 __global__ __launch_bounds__(NHG * 64) void attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ ckv, const int32_t* __restrict__ idx, int k,
@@ -66,7 +72,7 @@ __global__ __launch_bounds__(NHG * 64) void attn_kernel(
   constexpr int H = NHG * 16;
   __shared__ __align__(16) uint16_t Ks[kKT * kKsStride];
   __shared__ __align__(16) uint16_t Vt[kD * kVtStride];
-  __shared__ const uint16_t* rowp[kKT];
+  __shared__ uint64_t rowp[kKT];  // row addresses as integers (0 = masked)
   __shared__ uint64_t tile_valid;  // bit v: slot v of the current tile holds a key
 
   const int split = blockIdx.x;
@@ -80,9 +86,13 @@ __global__ __launch_bounds__(NHG * 64) void attn_kernel(
   const int c = lane % 16;
 
   const int64_t k_lo = (int64_t)split * keys_per_split;
-  // the first tile's selected ids do not depend on the row geometry: load them right away
-  int32_t first_id = -1;
-  if (SPARSE && tid < kKT && k_lo + tid < k) first_id = idx[(int64_t)row * k + k_lo + tid];
+  // the first tile's selected ids do not depend on the row geometry: load them right away.
+  // Every thread loads, from a clamped slot (or from q when there is no list), so the load
+  // carries no branch and is only awaited where the ids are used.
+  const bool has_ids = SPARSE && k > 0;
+  const int32_t* id_src = has_ids ? idx + (int64_t)row * k + (k_lo + tid < k ? k_lo + tid : k - 1)
+                                  : reinterpret_cast<const int32_t*>(q);
+  const int32_t first_raw = *id_src;
   const RowGeom geo = row_geom(kv_off, ent_off, q_pos, b, t, m, n_win, max_entries);
   const int64_t n_comp = SPARSE ? (int64_t)k : geo.nvis;  // compressed slots in the list
   const int64_t L = n_comp + geo.win_cnt;
@@ -110,14 +120,14 @@ __global__ __launch_bounds__(NHG * 64) void attn_kernel(
       if (slot < k_hi) {
         if (slot < n_comp) {
           int64_t id = slot;
-          if (SPARSE) id = (t0 == k_lo) ? (int64_t)first_id : (int64_t)idx[(int64_t)row * k + slot];
+          if (SPARSE) id = (t0 == k_lo) ? (int64_t)(has_ids ? first_raw : -1) : (int64_t)idx[(int64_t)row * k + slot];
           if (id >= 0 && id < geo.n_ent) p = ckv + (geo.ent_base + id) * kD;
         } else {
           const int64_t w = slot - n_comp;
           p = kv + (geo.kv_base + geo.win_lo + w) * kD;
         }
       }
-      rowp[v] = p;
+      rowp[v] = reinterpret_cast<uint64_t>(p);
       const uint64_t vb = __ballot(p != nullptr);
       if (v == 0) tile_valid = vb;
     }
@@ -128,11 +138,11 @@ __global__ __launch_bounds__(NHG * 64) void attn_kernel(
       const int dg = blk % 16;  // dims 8dg..8dg+7
       const uint16_t* pp[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) pp[u] = rowp[4 * kg + u];
+      for (int u = 0; u < 4; ++u) pp[u] = reinterpret_cast<const uint16_t*>(rowp[4 * kg + u]);
       u32x4 r[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u)  // unconditional loads (a masked slot reads row 0) keep all four in flight
-        r[u] = *reinterpret_cast<const u32x4*>((pp[u] ? pp[u] : ckv) + dg * 8);
+        r[u] = load_global16((pp[u] ? pp[u] : ckv) + dg * 8);
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         if (!pp[u]) r[u] = u32x4{0, 0, 0, 0};
