@@ -6,13 +6,16 @@
 // Split-K flash decoding:
 //   * a workgroup takes one query row (b, t) and a contiguous range of the row's key list;
 //     it has one wave per 16 query heads, all waves sharing one gathered tile;
-//   * each 64-key tile is gathered from HBM into LDS twice: row-major K[key][d] for the
-//     logits and transposed V^T[d][key] for the value product (K = V), so both MFMA
-//     operands are read as contiguous 16- and 8-byte LDS words;
+//   * each 64-key tile is gathered from HBM into one row-major LDS tile K[key][d] (K = V),
+//     XOR-swizzled by 16-byte units so that its writes and both kinds of reads are free of
+//     bank conflicts;
 //   * S^T = K Q^T runs as 16x16x32 bf16 MFMAs with keys on M and heads on N, so each
 //     lane holds 16 keys of one head and the softmax statistics stay per lane;
-//   * an fp32 online softmax in base 2 rescales the O^T accumulators, and the
-//     probabilities, rounded to bf16, feed O^T += V^T P^T without leaving registers;
+//   * an fp32 online softmax in base 2 (rescaling only when the maximum grows by more than
+//     2^8) feeds the probabilities, rounded to bf16, to O^T += V^T P^T; the V^T operand
+//     comes from the same tile through gfx950's transposing LDS reads;
+//   * workgroups that walk several tiles load the next tile's rows while the current one
+//     is multiplied;
 //   * with several splits per row each workgroup writes a normalised partial (o, lse) and
 //     a merge kernel combines them with log-sum-exp weights.
 #include "device_common.h"
@@ -24,8 +27,6 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kKT = 64;               // keys per tile
-constexpr int kKsStride = kD + 8;     // bf16 elements per LDS key row (pad breaks bank aliasing)
-constexpr int kVtStride = kKT + 8;    // bf16 elements per LDS transposed row
 
 struct RowGeom {
   int64_t ent_base, n_ent, kv_base, win_lo, win_cnt, nvis;
@@ -61,196 +62,132 @@ __device__ __forceinline__ u32x4 load_global16(const uint16_t* p) {
   return *(const __attribute__((address_space(1))) u32x4*)(p);
 }
 
-template <int NHG, bool SPARSE>
-__global__ __launch_bounds__(NHG * 64) void attn_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ ckv, const int32_t* __restrict__ idx, int k,
-    const uint16_t* __restrict__ kv, const int64_t* __restrict__ kv_off, const int64_t* __restrict__ ent_off,
-    const int64_t* __restrict__ q_pos, int m, int n_win, int T, float scale_log2, int64_t max_entries,
-    int keys_per_split, float* __restrict__ out, float* __restrict__ lse_out, float* __restrict__ ws_o,
-    float* __restrict__ ws_lse) {
-  constexpr int NT = NHG * 64;
-  constexpr int H = NHG * 16;
-  __shared__ __align__(16) uint16_t Ks[kKT * kKsStride];
-  __shared__ __align__(16) uint16_t Vt[kD * kVtStride];
-  __shared__ uint64_t rowp[kKT];  // row addresses as integers (0 = masked)
-  __shared__ uint64_t tile_valid;  // bit v: slot v of the current tile holds a key
+// The K tile in LDS: 64 rows of 256 bytes (16 units of 16 bytes, no padding); unit U of row r
+// sits at position U ^ ks_swz(r). The swizzle keeps every LDS access of the kernel free of
+// bank conflicts: the gather's writes (4 rows x 64 contiguous bytes per 16 lanes), the 16-byte
+// K-operand reads (16 rows of one unit) and the transposing 8-byte V-operand reads (4 rows x
+// 2 units per 16 lanes). It is linear over the row's low 4 bits.
+__device__ __forceinline__ int ks_swz(int r) {
+  return ((r & 1) ? 4 : 0) ^ ((r & 2) ? 10 : 0) ^ ((r & 4) ? 1 : 0) ^ ((r & 8) ? 2 : 0);
+}
 
-  const int split = blockIdx.x;
-  const int row = blockIdx.y;
-  const int nrows = gridDim.y;
-  const int b = row / T, t = row % T;
-  const int tid = threadIdx.x;
-  const int wave = tid / kWave;
-  const int lane = tid % kWave;
-  const int g = lane / 16;
-  const int c = lane % 16;
+// gfx950 transposing LDS read: within each 16-lane group, lanes 4j..4j+3 name 4 consecutive
+// 16-bit values each (row j, 16 values), and lane i receives value i of rows 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* lds_base, int byte_off) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s lds_v4s;
+  lds_v4s* p = (lds_v4s*)((__attribute__((address_space(3))) uint8_t*)(lds_base) + byte_off);
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(p));
+}
 
-  const int64_t k_lo = (int64_t)split * keys_per_split;
-  // the first tile's selected ids do not depend on the row geometry: load them right away.
-  // Every thread loads, from a clamped slot (or from q when there is no list), so the load
-  // carries no branch and is only awaited where the ids are used.
-  const bool has_ids = SPARSE && k > 0;
-  const int32_t* id_src = has_ids ? idx + (int64_t)row * k + (k_lo + tid < k ? k_lo + tid : k - 1)
-                                  : reinterpret_cast<const int32_t*>(q);
-  const int32_t first_raw = *id_src;
-  const RowGeom geo = row_geom(kv_off, ent_off, q_pos, b, t, m, n_win, max_entries);
-  const int64_t n_comp = SPARSE ? (int64_t)k : geo.nvis;  // compressed slots in the list
-  const int64_t L = n_comp + geo.win_cnt;
-  const int64_t k_hi = (k_lo + keys_per_split < L) ? k_lo + keys_per_split : L;
+// A score must exceed the running maximum (base-2 logits) by more than this before the
+// accumulators are rescaled; in between, probabilities are taken relative to the stale
+// maximum and stay below 2^8, which fp32 sums and bf16 probabilities hold without loss.
+constexpr float kRescaleSlack = 8.f;
 
-  // queries of this wave's 16 heads as MFMA B operands (d-slots 8g..8g+7 of each 32-chunk)
-  const int head = wave * 16 + c;
-  bf16x8 qb[4];
+// One 64-key tile from LDS for this wave's 16 heads: S^T = K Q^T (keys on M, heads on N), the
+// online softmax in base 2 (vld[v] != 0: slot v holds a key), and O^T += V^T P^T with the
+// probabilities rounded to bf16. V^T comes from the same row-major tile through transposing reads.
+__device__ __forceinline__ void tile_compute(const uint8_t* Ks, const uint8_t* vld, const bf16x8 (&qb)[4],
+                                             float scale_log2, f32x4 (&oacc)[8], float& m_run, float& l_run,
+                                             int c, int g) {
+  // K operand: lane (c, g) takes key 16mb + c, dims 32kk + 8g.. (unit 4kk + g); every row
+  // 16mb + c shares the swizzle of row c
+  const int swc = ks_swz(c);
+  f32x4 sacc[4];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-    qb[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(q + ((int64_t)row * H + head) * kD + kk * 32 + g * 8));
-
-  f32x4 oacc[8];
+  for (int mb = 0; mb < 4; ++mb) sacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int db = 0; db < 8; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-
-  for (int64_t t0 = k_lo; t0 < k_hi; t0 += kKT) {
-    // ---- resolve the 64 slots of this tile to row pointers (nullptr = masked) ----
-    if (tid < kKT) {  // kKT slots, one per thread of the first wave
-      const int v = tid;
-      const int64_t slot = t0 + v;
-      const uint16_t* p = nullptr;
-      if (slot < k_hi) {
-        if (slot < n_comp) {
-          int64_t id = slot;
-          if (SPARSE) id = (t0 == k_lo) ? (int64_t)(has_ids ? first_raw : -1) : (int64_t)idx[(int64_t)row * k + slot];
-          if (id >= 0 && id < geo.n_ent) p = ckv + (geo.ent_base + id) * kD;
-        } else {
-          const int64_t w = slot - n_comp;
-          p = kv + (geo.kv_base + geo.win_lo + w) * kD;
-        }
-      }
-      rowp[v] = reinterpret_cast<uint64_t>(p);
-      const uint64_t vb = __ballot(p != nullptr);
-      if (v == 0) tile_valid = vb;
-    }
-    __syncthreads();
-    // ---- gather: each thread moves a 4-key x 8-dim block into both LDS layouts ----
-    for (int blk = tid; blk < 16 * 16; blk += NT) {
-      const int kg = blk / 16;  // keys 4kg..4kg+3
-      const int dg = blk % 16;  // dims 8dg..8dg+7
-      const uint16_t* pp[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) pp[u] = reinterpret_cast<const uint16_t*>(rowp[4 * kg + u]);
-      u32x4 r[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)  // unconditional loads (a masked slot reads row 0) keep all four in flight
-        r[u] = load_global16((pp[u] ? pp[u] : ckv) + dg * 8);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (!pp[u]) r[u] = u32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        *reinterpret_cast<u32x4*>(&Ks[(4 * kg + u) * kKsStride + dg * 8]) = r[u];
-      // transpose: dim 8dg+2w (low halves) and 8dg+2w+1 (high halves) across the 4 keys
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t a0 = r[0][w], a1 = r[1][w], a2 = r[2][w], a3 = r[3][w];
-        u32x2 lo, hi;
-        lo.x = (a0 & 0xffffu) | (a1 << 16);
-        lo.y = (a2 & 0xffffu) | (a3 << 16);
-        hi.x = (a0 >> 16) | (a1 & 0xffff0000u);
-        hi.y = (a2 >> 16) | (a3 & 0xffff0000u);
-        *reinterpret_cast<u32x2*>(&Vt[(dg * 8 + 2 * w) * kVtStride + 4 * kg]) = lo;
-        *reinterpret_cast<u32x2*>(&Vt[(dg * 8 + 2 * w + 1) * kVtStride + 4 * kg]) = hi;
-      }
-    }
-    __syncthreads();
-
-    // ---- S^T = K Q^T: 4 key blocks x 4 d-chunks ----
-    // all 16 key fragments are read before the first product so LDS latency overlaps
-    bf16x8 ka[4][4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        ka[kk][mb] = as_bf16x8(*reinterpret_cast<const u32x4*>(&Ks[(16 * mb + c) * kKsStride + kk * 32 + g * 8]));
-    f32x4 sacc[4];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) sacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) sacc[mb] = mfma16x16x32(ka[kk][mb], qb[kk], sacc[mb]);
-    // ---- online softmax (base 2) for head c over keys 16mb + 4g + i ----
-    const uint64_t valid = tile_valid;
-    float x[4][4];
-    float mx = -INFINITY;
+  for (int kk = 0; kk < 4; ++kk) {
+    const int koff = c * 256 + 16 * ((4 * kk + g) ^ swc);
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool ok = (valid >> (16 * mb + 4 * g + i)) & 1ull;
-        x[mb][i] = ok ? sacc[mb][i] * scale_log2 : -INFINITY;
-        mx = fmaxf(mx, x[mb][i]);
-      }
+      const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(Ks + koff + mb * 16 * 256));
+      sacc[mb] = mfma16x16x32(ka, qb[kk], sacc[mb]);
     }
-    mx = fmaxf(mx, shfl_xor_f(mx, 16));
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    float alpha = 1.f;
-    float p[4][4];
-    if (m_new == -INFINITY) {
+  }
+  // this lane's 16 keys are 16mb + 4g + i; a tile with every slot filled skips the masking
+  uint32_t okw[4];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[mb][i] = 0.f;
-    } else {
-      alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[mb][i] = __builtin_amdgcn_exp2f(x[mb][i] - m_new);
-    }
-    m_run = m_new;
-    float psum = 0.f;
+  for (int mb = 0; mb < 4; ++mb) okw[mb] = *reinterpret_cast<const uint32_t*>(&vld[16 * mb + 4 * g]);
+  const bool full = __builtin_amdgcn_ballot_w64((okw[0] & okw[1] & okw[2] & okw[3]) != 0x01010101u) == 0;
+  float mx = -INFINITY;
+  if (full) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) psum += p[mb][i];
-    l_run = l_run * alpha + psum;
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[mb][i]);
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool ok = (okw[mb] >> (8 * i)) & 0xffu;
+        sacc[mb][i] = ok ? sacc[mb][i] : -INFINITY;
+        mx = fmaxf(mx, sacc[mb][i]);
+      }
+  }
+  mx = fmaxf(mx, shfl_xor_f(mx, 16));
+  mx = fmaxf(mx, shfl_xor_f(mx, 32));
+  mx *= scale_log2;  // scale > 0, so the maximum commutes with the scaling
+  if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0) {
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 while nothing was seen
+    l_run *= alpha;
 #pragma unroll
     for (int db = 0; db < 8; ++db) oacc[db] *= alpha;
-
-    // ---- O^T += V^T P^T: 8 d-blocks x 2 key chunks of 32 ----
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      u32x4 pw;
-      pw.x = pack_bf16x2(p[2 * s][0], p[2 * s][1]);
-      pw.y = pack_bf16x2(p[2 * s][2], p[2 * s][3]);
-      pw.z = pack_bf16x2(p[2 * s + 1][0], p[2 * s + 1][1]);
-      pw.w = pack_bf16x2(p[2 * s + 1][2], p[2 * s + 1][3]);
-      const bf16x8 pb = as_bf16x8(pw);
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const uint16_t* vr = &Vt[(16 * db + c) * kVtStride + 32 * s + 4 * g];
-        const u32x2 v0 = *reinterpret_cast<const u32x2*>(vr);
-        const u32x2 v1 = *reinterpret_cast<const u32x2*>(vr + 16);
-        const bf16x8 va = as_bf16x8(u32x4{v0.x, v0.y, v1.x, v1.y});
-        oacc[db] = mfma16x16x32(va, pb, oacc[db]);
-      }
-    }
-    __syncthreads();  // the next tile overwrites Ks / Vt / rowp
+    m_run = m_new;
   }
+  // p = 2^(s * scale - m); before the first key m is -inf and every p of the tile is masked
+  const float nm = m_run == -INFINITY ? 0.f : -m_run;
+  float p[4][4];
+  float psum = 0.f;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[mb][i] = __builtin_amdgcn_exp2f(fmaf(sacc[mb][i], scale_log2, nm));
+      psum += p[mb][i];
+    }
+  l_run += psum;
+  // O^T += V^T P^T: 8 d-blocks x 2 key chunks of 32. The A operand of lane (c, g) holds dim
+  // 16db + c of keys 32s + 4g + 0..3 and 32s + 16 + 4g + 0..3 (the key order of P's k-slots);
+  // in the transposing read the lane names row 32s (+16) + 4g + c/4 and dims 16db + 4(c%4)..
+  const int rv = 4 * g + (c >> 2);
+  const int swv = ks_swz(rv);
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    u32x4 pw;
+    pw.x = pack_bf16x2(p[2 * s][0], p[2 * s][1]);
+    pw.y = pack_bf16x2(p[2 * s][2], p[2 * s][3]);
+    pw.z = pack_bf16x2(p[2 * s + 1][0], p[2 * s + 1][1]);
+    pw.w = pack_bf16x2(p[2 * s + 1][2], p[2 * s + 1][3]);
+    const bf16x8 pb = as_bf16x8(pw);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const int voff = rv * 256 + 8 * (c & 1) + 16 * ((2 * db + ((c >> 1) & 1)) ^ swv) + 32 * s * 256;
+      const u32x2 v0 = lds_read_tr16(Ks, voff);
+      const u32x2 v1 = lds_read_tr16(Ks, voff + 16 * 256);
+      const bf16x8 va = as_bf16x8(u32x4{v0.x, v0.y, v1.x, v1.y});
+      oacc[db] = mfma16x16x32(va, pb, oacc[db]);
+    }
+  }
+}
 
-  // ---- finish: reduce the lane-partial denominators across the 4 lane groups ----
+// Common epilogue: normalise and write the output (one split) or the partial (o, lse).
+__device__ __forceinline__ void attn_write(const f32x4 (&oacc)[8], float m_run, float l_run, int row, int nrows,
+                                           int split, int H, int head, int g, float* __restrict__ out,
+                                           float* __restrict__ lse_out, float* __restrict__ ws_o,
+                                           float* __restrict__ ws_lse) {
+  // reduce the lane-partial denominators across the 4 lane groups
   float l = l_run;
   l += shfl_xor_f(l, 16);
   l += shfl_xor_f(l, 32);
   const bool empty = !(l > 0.f);
   const float inv = empty ? 0.f : 1.f / l;
   const float lse = empty ? -INFINITY : (m_run + __log2f(l)) * kLn2;
-
   const bool single = (gridDim.x == 1);
-  float* o_dst = single ? out + ((int64_t)row * H + head) * kD
-                        : ws_o + (((int64_t)split * nrows + row) * H + head) * kD;
+  float* o_dst = single ? out + ((int64_t)row * H + head) * kD : ws_o + (((int64_t)split * nrows + row) * H + head) * kD;
 #pragma unroll
   for (int db = 0; db < 8; ++db) {
     const f32x4 v = oacc[db] * inv;
@@ -263,6 +200,131 @@ __global__ __launch_bounds__(NHG * 64) void attn_kernel(
       ws_lse[((int64_t)split * nrows + row) * H + head] = lse;
     }
   }
+}
+
+// Attention over one query row's key range. Each thread gathers whole 64-byte pieces of rows:
+// pair p = j * NT + tid takes row p / 4, units 4q + p % 4 (q = 0..3), so 4 lanes read 64
+// contiguous bytes per load and a thread resolves one row address per tile. With MULTI the
+// workgroup walks several tiles and loads the next tile's rows (and the selected ids of the
+// one after) into registers while the current tile is multiplied; without it the range is
+// one tile (decode) and the kernel keeps fewer registers live.
+template <int NHG, bool SPARSE, bool MULTI>
+__global__ __launch_bounds__(NHG * 64) void attn_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ ckv, const int32_t* __restrict__ idx, int k,
+    const uint16_t* __restrict__ kv, const int64_t* __restrict__ kv_off, const int64_t* __restrict__ ent_off,
+    const int64_t* __restrict__ q_pos, int m, int n_win, int T, float scale_log2, int64_t max_entries,
+    int keys_per_split, float* __restrict__ out, float* __restrict__ lse_out, float* __restrict__ ws_o,
+    float* __restrict__ ws_lse) {
+  constexpr int NT = NHG * 64;
+  constexpr int H = NHG * 16;
+  constexpr int NP = 4 * kKT;              // gather pairs per tile
+  constexpr int RPT = (NP + NT - 1) / NT;  // pairs (rows) per thread
+  __shared__ __align__(16) uint8_t Ks[kKT * kD * 2];
+  __shared__ __align__(16) uint8_t vld[kKT];  // slot v of the current tile holds a key
+
+  const int split = blockIdx.x;
+  const int row = blockIdx.y;
+  const int nrows = gridDim.y;
+  const int b = row / T, t = row % T;
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+  const int g = lane / 16;
+  const int c = lane % 16;
+
+  const int64_t k_lo = (int64_t)split * keys_per_split;
+  // selected ids do not depend on the row geometry: the first ones load right away, from
+  // clamped slots (or from q when there is no list), so the loads carry no branch
+  const bool has_ids = SPARSE && k > 0;
+  const int32_t* idx_row = has_ids ? idx + (int64_t)row * k : reinterpret_cast<const int32_t*>(q);
+  auto load_ids = [&](int64_t t0, int32_t (&ids)[RPT]) {
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      const int64_t slot = t0 + (j * NT + tid) / 4;
+      ids[j] = idx_row[has_ids ? (slot < k ? slot : k - 1) : 0];
+    }
+  };
+  int32_t ids_cur[RPT], ids_nxt[RPT];
+  load_ids(k_lo, ids_cur);
+  if (MULTI) load_ids(k_lo + kKT, ids_nxt);
+  const RowGeom geo = row_geom(kv_off, ent_off, q_pos, b, t, m, n_win, max_entries);
+  const int64_t n_comp = SPARSE ? (int64_t)k : geo.nvis;  // compressed slots in the list
+  const int64_t L = n_comp + geo.win_cnt;
+  const int64_t k_hi = (k_lo + keys_per_split < L) ? k_lo + keys_per_split : L;
+
+  // Row addresses as integers, computed without branches. Slot t0 + v of a tile (v < 64) is
+  // a compressed entry while v < n_comp - t0 and holds a key while v < k_hi - t0; both limits
+  // are clamped to [0, 64] so the per-slot tests are 32-bit.
+  const uint64_t ckv_a = reinterpret_cast<uint64_t>(ckv);
+  const uint64_t ent_a = ckv_a + (uint64_t)geo.ent_base * (kD * 2);
+  const uint64_t win_a = reinterpret_cast<uint64_t>(kv) + (uint64_t)(geo.kv_base + geo.win_lo - n_comp) * (kD * 2);
+  const uint32_t n_ent32 = (uint32_t)(geo.n_ent < 0x7fffffff ? geo.n_ent : 0x7fffffff);
+  auto clamp_tile = [](int64_t x) { return (int)(x < 0 ? 0 : (x > kKT ? kKT : x)); };
+  u32x4 r[RPT][4];
+  uint32_t okm = 0;  // bit j: pair j's row holds a key
+  auto issue = [&](int64_t t0, const int32_t (&ids)[RPT]) {
+    const int lim_c = clamp_tile(n_comp - t0), lim_h = clamp_tile(k_hi - t0);
+    const uint64_t win_t = win_a + (uint64_t)t0 * (kD * 2);
+    okm = 0;
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      const int pr = j * NT + tid;
+      const bool in = (j + 1) * NT <= NP || pr < NP;
+      const int v = pr / 4;
+      const uint32_t e = SPARSE ? (uint32_t)ids[j] : (uint32_t)(t0 + v);  // negative ids wrap to huge
+      const bool comp = v < lim_c;
+      const bool ok = in && v < lim_h && (!comp || e < n_ent32);
+      const uint64_t a = comp ? ent_a + (uint64_t)e * (kD * 2) : win_t + (uint64_t)v * (kD * 2);
+      okm |= (ok ? 1u : 0u) << j;
+      const uint16_t* src = reinterpret_cast<const uint16_t*>(ok ? a : ckv_a) + 8 * (pr % 4);
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) r[j][qq] = load_global16(src + 32 * qq);  // unconditional: masked rows read row 0
+    }
+  };
+
+  // queries of this wave's 16 heads as MFMA B operands (d-slots 8g..8g+7 of each 32-chunk)
+  const int head = wave * 16 + c;
+  bf16x8 qb[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    qb[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(q + ((int64_t)row * H + head) * kD + kk * 32 + g * 8));
+  // with prefetching, the query and id loads complete before the first row loads: inside the
+  // tile loop the compiler then knows the query operands have arrived and the products do not
+  // wait for the prefetch (vmcnt(0); expcnt and lgkmcnt left at their maximum, gfx9 encoding)
+  if (MULTI) __builtin_amdgcn_s_waitcnt(0x0f70);
+
+  f32x4 oacc[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  if (k_lo < k_hi) issue(k_lo, ids_cur);
+  for (int64_t t0 = k_lo; t0 < k_hi; t0 += kKT) {
+    // this tile's rows (in flight since the previous tile) into the swizzled K tile
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      const int pr = j * NT + tid;
+      if ((j + 1) * NT > NP && pr >= NP) break;
+      const int v = pr / 4, u = pr % 4;
+      const bool ok = (okm >> j) & 1u;
+      const int sw = ks_swz(v);
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq)
+        *reinterpret_cast<u32x4*>(Ks + v * 256 + 16 * ((4 * qq + u) ^ sw)) = ok ? r[j][qq] : u32x4{0, 0, 0, 0};
+      if (u == 0) vld[v] = ok ? 1 : 0;
+    }
+    __syncthreads();
+    // the next tile's rows and the ids two tiles ahead go out while this one computes
+    if (MULTI && t0 + kKT < k_hi) {
+      issue(t0 + kKT, ids_nxt);
+      if (SPARSE && t0 + 2 * kKT < k_hi) load_ids(t0 + 2 * kKT, ids_nxt);
+    }
+    tile_compute(Ks, vld, qb, scale_log2, oacc, m_run, l_run, c, g);
+    if (!MULTI) break;  // the launch gives single-tile kernels at most one tile
+    __syncthreads();    // the next tile overwrites Ks / vld
+  }
+  attn_write(oacc, m_run, l_run, row, nrows, split, H, head, g, out, lse_out, ws_o, ws_lse);
 }
 
 // Log-sum-exp merge of the split partials: one thread per (query row, head, dim). Splits are
@@ -314,10 +376,17 @@ hipError_t launch_nhg(int H, dim3 grid, hipStream_t st, const uint16_t* q, const
                       int k, const uint16_t* kv, const int64_t* kv_off, const int64_t* ent_off, const int64_t* q_pos,
                       int m, int n_win, int T, float scale_log2, int64_t max_entries, int kps, float* out,
                       float* lse, float* ws_o, float* ws_lse) {
-#define CSL_ATTN_CASE(NHG)                                                                                   \
-  case NHG:                                                                                                  \
-    attn_kernel<NHG, SPARSE><<<grid, NHG * 64, 0, st>>>(q, ckv, idx, k, kv, kv_off, ent_off, q_pos, m, n_win, \
-                                                        T, scale_log2, max_entries, kps, out, lse, ws_o, ws_lse); \
+  const bool multi = kps > kKT;  // several tiles per workgroup: the prefetching kernel
+#define CSL_ATTN_CASE(NHG)                                                                                     \
+  case NHG:                                                                                                    \
+    if (multi)                                                                                                 \
+      attn_kernel<NHG, SPARSE, true><<<grid, NHG * 64, 0, st>>>(q, ckv, idx, k, kv, kv_off, ent_off, q_pos, m,  \
+                                                                n_win, T, scale_log2, max_entries, kps, out, lse, \
+                                                                ws_o, ws_lse);                                  \
+    else                                                                                                       \
+      attn_kernel<NHG, SPARSE, false><<<grid, NHG * 64, 0, st>>>(q, ckv, idx, k, kv, kv_off, ent_off, q_pos, m, \
+                                                                 n_win, T, scale_log2, max_entries, kps, out,   \
+                                                                 lse, ws_o, ws_lse);                            \
     break;
   switch (H / 16) {
     CSL_ATTN_CASE(1)

@@ -5,11 +5,11 @@
 // by the lower id, so (key descending, id ascending) is a strict total order and the top-k
 // set is unique. Two paths:
 //
-//   * short rows (n <= 40960, e.g. a 4K-context decode or a prefill chunk over a 131K
+//   * short rows (n <= 34816, e.g. a 4K-context decode or a prefill chunk over a 131K
 //     prefix): one 1024-thread workgroup per row holds the row's keys in registers
-//     (element i = j*1024 + tid), radix-selects the k-th best on a 48-bit composite
-//     C(i) = key << 16 | (0xffff - i), and writes the selection with a block-wide ordered
-//     compaction, so the output is ascending by construction;
+//     (element i = j*1024 + tid), radix-selects the k-th best key on the bits below the keys'
+//     common prefix, and writes the selection with a block-wide ordered compaction (lower
+//     ids first among keys tied at the threshold), so the output is ascending by construction;
 //
 //   * long rows (decode at 1M context: 262144 scores per row): every 512-entry slice of the
 //     row lists its own candidates above an honest slice cut (topk_common.h) -- either
@@ -34,99 +34,6 @@ __device__ __forceinline__ int64_t row_count(const int64_t* ent_off, const int64
   n = n < n_ent ? n : n_ent;
   n = n < max_entries ? n : max_entries;
   return n < 0 ? 0 : n;
-}
-
-// ---------------------------------------------------------------------------------------
-// Short rows: one workgroup per row, keys in registers.
-// ---------------------------------------------------------------------------------------
-template <int ITEMS>
-__global__ __launch_bounds__(1024) void topk_row_kernel(const float* __restrict__ scores, int64_t ld,
-                                                        const int64_t* __restrict__ ent_off,
-                                                        const int64_t* __restrict__ q_pos, int m, int T, int k,
-                                                        int64_t max_entries, int32_t* __restrict__ idx) {
-  constexpr int NT = 1024;
-  constexpr int NW = NT / kWave;
-  __shared__ uint32_t hist[2048];
-  __shared__ uint32_t wsum[NW];
-  __shared__ uint32_t res[4];
-  __shared__ uint32_t cnt[ITEMS * NW];
-
-  const int row = blockIdx.x;
-  const int b = row / T, t = row % T;
-  const int tid = threadIdx.x;
-  const int64_t n = row_count(ent_off, q_pos, b, t, m, max_entries);
-  const int keep = (int)(n < k ? n : k);
-  int32_t* out = idx + (int64_t)row * k;
-  const float* srow = scores + (int64_t)row * ld;
-
-  if (keep == n) {  // everything visible is selected
-    for (int p = tid; p < k; p += NT) out[p] = p < n ? p : -1;
-    return;
-  }
-
-  uint32_t key[ITEMS];
-#pragma unroll
-  for (int j = 0; j < ITEMS; ++j) {
-    const int i = j * NT + tid;
-    key[j] = (i < n) ? score_key(srow[i]) : 0u;
-  }
-  auto comp = [&](int j) -> uint64_t {
-    const int i = j * NT + tid;
-    return ((uint64_t)key[j] << 16) | (uint64_t)(0xffffu - (uint32_t)i);
-  };
-
-  uint64_t prefix = 0;
-  int pbits = 0;
-  uint32_t need = (uint32_t)keep;
-  for (int pass = 0; pass < 5; ++pass) {
-    const int width = pass < 2 ? 11 : (pass == 2 ? 10 : 8);
-    const int shift = 48 - pbits - width;
-    for (int q = tid; q < 2048; q += NT) hist[q] = 0;
-    __syncthreads();
-    for (int j = 0; j < ITEMS; ++j) {
-      const int i = j * NT + tid;
-      if (i < n) {
-        const uint64_t C = comp(j);
-        if (pbits == 0 || (C >> (48 - pbits)) == prefix)
-          atomicAdd(&hist[(uint32_t)(C >> shift) & ((1u << width) - 1u)], 1u);
-      }
-    }
-    __syncthreads();
-    find_threshold_bin<NT, 2048>(hist, need, wsum, res);
-    const uint32_t d = res[0], above = res[1], in_bin = res[2];
-    prefix = (prefix << width) | d;
-    pbits += width;
-    need -= above;
-    __syncthreads();
-    if (in_bin == need) break;  // the whole bin is taken
-  }
-
-  // ordered compaction of sel(i) = (C(i) >> (48 - pbits)) >= prefix
-  const int wave = tid / kWave;
-  for (int j = 0; j < ITEMS; ++j) {
-    const int i = j * NT + tid;
-    const bool s = (i < n) && ((comp(j) >> (48 - pbits)) >= prefix);
-    const uint64_t mask = __ballot(s);
-    if (lane_id() == 0) cnt[j * NW + wave] = (uint32_t)__popcll(mask);
-  }
-  __syncthreads();
-  {
-    const uint32_t v = (tid < ITEMS * NW) ? cnt[tid] : 0u;
-    __syncthreads();
-    const uint32_t e = block_exclusive_scan<NT>(v, wsum, nullptr);
-    if (tid < ITEMS * NW) cnt[tid] = e;
-    __syncthreads();
-  }
-  for (int j = 0; j < ITEMS; ++j) {
-    const int i = j * NT + tid;
-    const bool s = (i < n) && ((comp(j) >> (48 - pbits)) >= prefix);
-    const uint64_t mask = __ballot(s);
-    if (s) {
-      const uint32_t pos = cnt[j * NW + wave] + rank_in_wave(mask);
-      if (pos < (uint32_t)keep) out[pos] = i;
-    }
-  }
-  for (int p = keep + tid; p < k; p += NT) out[p] = -1;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -193,6 +100,193 @@ __device__ __forceinline__ void fin_threshold(const uint32_t* hist, uint32_t nee
   __syncthreads();
 }
 
+// ---------------------------------------------------------------------------------------
+// Short rows: one workgroup per row, keys in registers (element i = j * kFinNT + tid).
+// Radix select of the keep-th largest 32-bit key, first on the 11 bits just below the keys'
+// common prefix, then on the rest; winners are the keys above the threshold bin plus, when
+// the bin is not taken whole, the first `need` keys equal to the threshold in id order. The
+// winners are written in id order through one packed block scan of per-(item, wave) counts.
+// ---------------------------------------------------------------------------------------
+// fin_threshold over COPIES interleaved copies of a 2048-bin histogram (hist[bin * COPIES +
+// copy]), summed per bin: lanes spread their atomics over the copies, so keys that pile into a
+// few bins do not serialise a whole wave on one LDS address.
+template <int COPIES>
+__device__ __forceinline__ void fin_threshold_copies(const uint32_t* hist, uint32_t need, uint32_t* wsum,
+                                                     uint32_t* res) {
+  constexpr int BINS = 2048;
+  constexpr int PER = BINS / kFinNT;
+  const int tid = threadIdx.x;
+  uint32_t v[PER];
+  uint32_t local = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int bin = BINS - 1 - (tid * PER + q);
+    uint32_t x = 0;
+#pragma unroll
+    for (int c = 0; c < COPIES; ++c) x += hist[bin * COPIES + c];
+    v[q] = x;
+    local += x;
+  }
+  const uint32_t incl = wave_incl_scan(local);
+  if (lane_id() == kWave - 1) wsum[tid / kWave] = incl;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kFinWaves; ++w) {
+    const uint32_t x = wsum[w];
+    before += (w < tid / kWave) ? x : 0u;
+    all += x;
+  }
+  uint32_t excl = before + incl - local;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    if (excl < need && need <= excl + v[q]) {
+      res[0] = (uint32_t)(BINS - 1 - (tid * PER + q));
+      res[1] = excl;
+      res[2] = v[q];
+    }
+    excl += v[q];
+  }
+  if (tid == 0) res[3] = all;
+  __syncthreads();
+}
+
+template <int ITEMS>
+__global__ __launch_bounds__(kFinNT) void topk_row_kernel(const float* __restrict__ scores, int64_t ld,
+                                                          const int64_t* __restrict__ ent_off,
+                                                          const int64_t* __restrict__ q_pos, int m, int T, int k,
+                                                          int64_t max_entries, int32_t* __restrict__ idx) {
+  constexpr int COPIES = 8;  // first-pass histogram copies (lane % COPIES)
+  __shared__ uint32_t hist_a[2048 * COPIES];
+  __shared__ uint32_t hist_b[2048];
+  __shared__ uint32_t hist_c[1024];
+  __shared__ uint32_t wsum[2 * kFinWaves];
+  __shared__ uint32_t res[4];
+  __shared__ uint32_t cnt[ITEMS * kFinWaves];
+
+  const int row = blockIdx.x;
+  const int b = row / T, t = row % T;
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int64_t n = row_count(ent_off, q_pos, b, t, m, max_entries);
+  const uint32_t keep = (uint32_t)(n < k ? n : k);
+  int32_t* out = idx + (int64_t)row * k;
+  const float* srow = scores + (int64_t)row * ld;
+  if ((int64_t)keep == n) {  // everything visible is selected
+    for (int p = tid; p < k; p += kFinNT) out[p] = p < n ? p : -1;
+    return;
+  }
+
+  // loads from a clamped index (no branch per load, so all of them are in flight together),
+  // then the entries past the row are masked to 0 (keys of real scores are never 0)
+  uint32_t key[ITEMS];
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) {
+    const int i = j * kFinNT + tid;
+    key[j] = score_key(srow[i < n ? i : n - 1]);
+  }
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j)
+    if (j * kFinNT + tid >= n) key[j] = 0u;
+  for (int q = tid; q < 2048 * COPIES; q += kFinNT) hist_a[q] = 0;
+  for (int q = tid; q < 2048; q += kFinNT) hist_b[q] = 0;
+  hist_c[tid] = 0;
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j)
+    if (key[j]) {
+      kmin = min(kmin, key[j]);
+      kmax = max(kmax, key[j]);
+    }
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  if (lane_id() == 0) {
+    wsum[wave] = kmin;
+    wsum[kFinWaves + wave] = kmax;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kFinWaves; ++w) {
+    kmin = min(kmin, wsum[w]);
+    kmax = max(kmax, wsum[kFinWaves + w]);
+  }
+  const int common = __clz(kmin ^ kmax);
+  int shift = common >= 21 ? 0 : 21 - common;
+  uint32_t need = keep;
+  const uint32_t copy = lane_id() % COPIES;
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j)
+    if (key[j]) atomicAdd(&hist_a[((key[j] >> shift) & 2047u) * COPIES + copy], 1u);
+  __syncthreads();
+  fin_threshold_copies<COPIES>(hist_a, need, wsum, res);
+  uint32_t prefix = ((shift < 21 ? (kmin >> shift) : 0u) & ~2047u) | res[0];
+  need -= res[1];
+  bool all_in = res[2] == need;
+  if (!all_in && shift > 0) {
+    const int wb = shift < 11 ? shift : 11;
+    const int sb = shift - wb;
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j)
+      if (key[j] && (key[j] >> shift) == prefix) atomicAdd(&hist_b[(key[j] >> sb) & ((1u << wb) - 1u)], 1u);
+    __syncthreads();
+    fin_threshold<2048>(hist_b, need, wsum, res);
+    prefix = (prefix << wb) | res[0];
+    shift = sb;
+    need -= res[1];
+    all_in = res[2] == need;
+    if (!all_in && shift > 0) {  // shift <= 10 here
+#pragma unroll
+      for (int j = 0; j < ITEMS; ++j)
+        if (key[j] && (key[j] >> shift) == prefix) atomicAdd(&hist_c[key[j] & ((1u << shift) - 1u)], 1u);
+      __syncthreads();
+      fin_threshold<1024>(hist_c, need, wsum, res);
+      prefix = (prefix << shift) | res[0];
+      shift = 0;
+      need -= res[1];
+      all_in = res[2] == need;
+    }
+  }
+  const uint32_t need_eq = all_in ? 0u : need;
+
+  // ordered output: per (item, wave) counts of keys above the threshold and tied with it
+  auto above = [&](uint32_t x) {
+    const uint32_t h = x >> shift;
+    return x != 0u && (h > prefix || (all_in && h == prefix));
+  };
+  auto tied = [&](uint32_t x) { return x != 0u && !all_in && (x >> shift) == prefix; };
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) {
+    const uint64_t gm = __ballot(above(key[j])), em = __ballot(tied(key[j]));
+    if (lane_id() == 0) cnt[j * kFinWaves + wave] = (uint32_t)__popcll(gm) | ((uint32_t)__popcll(em) << 16);
+  }
+  __syncthreads();
+  {
+    constexpr int NC = ITEMS * kFinWaves;
+    static_assert(NC <= kFinNT, "one count per thread");
+    const uint32_t v = (tid < NC) ? cnt[tid] : 0u;
+    const uint32_t incl = wave_incl_scan(v);
+    if (lane_id() == kWave - 1) wsum[wave] = incl;
+    __syncthreads();
+    uint32_t before = 0;
+#pragma unroll
+    for (int w = 0; w < kFinWaves; ++w) before += (w < wave) ? wsum[w] : 0u;
+    if (tid < NC) cnt[tid] = before + incl - v;  // exclusive prefix of (gt | eq << 16)
+    __syncthreads();
+  }
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) {
+    const bool g = above(key[j]), e = tied(key[j]);
+    const uint64_t gm = __ballot(g), em = __ballot(e);
+    const uint32_t base = cnt[j * kFinWaves + wave];
+    const uint32_t gb = (base & 0xffffu) + rank_in_wave(gm);
+    const uint32_t eb = (base >> 16) + rank_in_wave(em);
+    const int i = j * kFinNT + tid;
+    if (g) out[gb + min(eb, need_eq)] = i;
+    else if (e && eb < need_eq) out[gb + eb] = i;
+  }
+  for (int p = (int)keep + tid; p < k; p += kFinNT) out[p] = -1;
+}
+
 // Exact selection over the whole row from its scores, for rows whose candidate lists cannot
 // prove the selection and rows too dense for them. Passes over the row (from L2):
 //   1. block min and max of the keys;
@@ -213,7 +307,7 @@ __device__ void finish_full_row(const float* __restrict__ srow, int64_t n, uint3
 #pragma unroll
       for (int j = 0; j < U; ++j) {
         const int64_t i = c0 + (int64_t)j * kFinNT + tid;
-        v[j] = (i < n) ? srow[i] : 0.f;
+        v[j] = srow[i < n ? i : n - 1];  // clamped: no branch per load
       }
 #pragma unroll
       for (int j = 0; j < U; ++j)
@@ -277,11 +371,13 @@ __device__ void finish_full_row(const float* __restrict__ srow, int64_t n, uint3
   for (int64_t c0 = 0; c0 < n; c0 += (int64_t)J * kFinNT) {
     const int64_t i0 = c0 + (int64_t)J * tid;
     uint32_t gm = 0, em = 0;
+    float v[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) v[j] = srow[i0 + j < n ? i0 + j : n - 1];  // clamped: no branch per load
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int64_t i = i0 + j;
-      if (i < n) {
-        const uint32_t h = score_key(srow[i]) >> shift;
+      if (i0 + j < n) {
+        const uint32_t h = score_key(v[j]) >> shift;
         if (h > prefix || (all_in && h == prefix)) gm |= 1u << j;
         else if (h == prefix) em |= 1u << j;
       }
@@ -564,7 +660,7 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int64_t* ent_off, 
     if (max_entries <= 1024) return launch_row<1>(scores, ld, ent_off, q_pos, m, B, T, k, max_entries, idx, st);
     if (max_entries <= 4096) return launch_row<4>(scores, ld, ent_off, q_pos, m, B, T, k, max_entries, idx, st);
     if (max_entries <= 16384) return launch_row<16>(scores, ld, ent_off, q_pos, m, B, T, k, max_entries, idx, st);
-    return launch_row<40>(scores, ld, ent_off, q_pos, m, B, T, k, max_entries, idx, st);
+    return launch_row<34>(scores, ld, ent_off, q_pos, m, B, T, k, max_entries, idx, st);
   }
   const int rows = B * T;
   const int budget = topk_slot_budget(max_entries, k);

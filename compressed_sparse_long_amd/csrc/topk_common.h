@@ -30,7 +30,7 @@ constexpr int kMaxSliceSlots = 64; // slots one slice may take
 constexpr int kWaveListMax = 16;   // largest keys kept per wave of 64 entries, at most
 constexpr int kMultiMaxEntries = 1 << 20;  // longest row of the multi-workgroup path
 constexpr int kTopkMaxK = 4096;
-constexpr int kRowKernelMax = 40 * 1024;   // rows up to this length use one workgroup
+constexpr int kRowKernelMax = 34 * 1024;   // rows up to this length use one workgroup (34 keys per thread)
 
 __host__ __device__ inline int64_t topk_num_slices(int64_t entries) { return (entries + kSlice - 1) / kSlice; }
 

@@ -108,7 +108,7 @@ int csl_compress_kv(const void* kv, const void* z, const int64_t* kv_off, const 
  *           scales must be positive. scale_group >= 1.
  *   scores  fp32 [B, T, ld], ld >= max_entries
  *   topk_ws (nullable) with topk_ws_bytes >= csl_topk_workspace_bytes(B, T, max_entries,
- *           topk_k): when given with T == 1 and rows longer than 40960 entries, the kernel
+ *           topk_k): when given with T == 1 and rows longer than 34816 entries, the kernel
  *           also leaves per-row top-k candidate lists in it (each 512-entry slice lists at
  *           most 16..64 entries, all of its entries above a slice-local cut), for the
  *           csl_topk_select call that follows with prepared = 1 and the same k and
