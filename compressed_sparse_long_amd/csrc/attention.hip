@@ -12,8 +12,9 @@
 //   * S^T = K Q^T runs as 16x16x32 bf16 MFMAs with keys on M and heads on N, so each
 //     lane holds 16 keys of one head and the softmax statistics stay per lane;
 //   * an fp32 online softmax in base 2 (rescaling only when the maximum grows by more than
-//     2^8) feeds the probabilities, rounded to bf16, to O^T += V^T P^T; the V^T operand
-//     comes from the same tile through gfx950's transposing LDS reads;
+//     2^8) feeds the probabilities, each split into a bf16 high part and a bf16 residual, to
+//     O^T += V^T P^T; the V^T operand comes from the same tile through gfx950's
+//     transposing LDS reads;
 //   * workgroups that walk several tiles load the next tile's rows while the current one
 //     is multiplied;
 //   * with several splits per row each workgroup writes a normalised partial (o, lse) and
@@ -86,8 +87,9 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* lds_base, int byte
 constexpr float kRescaleSlack = 8.f;
 
 // One 64-key tile from LDS for this wave's 16 heads: S^T = K Q^T (keys on M, heads on N), the
-// online softmax in base 2 (vld[v] != 0: slot v holds a key), and O^T += V^T P^T with the
-// probabilities rounded to bf16. V^T comes from the same row-major tile through transposing reads.
+// online softmax in base 2 (vld[v] != 0: slot v holds a key), and O^T += V^T P^T with each
+// probability split into two bf16 terms. V^T comes from the same row-major tile through
+// transposing reads.
 __device__ __forceinline__ void tile_compute(const uint8_t* Ks, const uint8_t* vld, const bf16x8 (&qb)[4],
                                              float scale_log2, f32x4 (&oacc)[8], float& m_run, float& l_run,
                                              int c, int g) {
@@ -155,21 +157,34 @@ __device__ __forceinline__ void tile_compute(const uint8_t* Ks, const uint8_t* v
   // in the transposing read the lane names row 32s (+16) + 4g + c/4 and dims 16db + 4(c%4)..
   const int rv = 4 * g + (c >> 2);
   const int swv = ks_swz(rv);
+  // Each probability enters as a bf16 pair p = hi + lo (lo = bf16(p - hi)), two products per
+  // block: the pair carries p to about 2^-16 relative, so the value product is as exact as
+  // its fp32 accumulation, where one bf16 would round every weight by up to 2^-9.
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    u32x4 pw;
-    pw.x = pack_bf16x2(p[2 * s][0], p[2 * s][1]);
-    pw.y = pack_bf16x2(p[2 * s][2], p[2 * s][3]);
-    pw.z = pack_bf16x2(p[2 * s + 1][0], p[2 * s + 1][1]);
-    pw.w = pack_bf16x2(p[2 * s + 1][2], p[2 * s + 1][3]);
-    const bf16x8 pb = as_bf16x8(pw);
+    const float* pp0 = p[2 * s];
+    const float* pp1 = p[2 * s + 1];
+    u32x4 hw, lw;
+    hw.x = pack_bf16x2(pp0[0], pp0[1]);
+    hw.y = pack_bf16x2(pp0[2], pp0[3]);
+    hw.z = pack_bf16x2(pp1[0], pp1[1]);
+    hw.w = pack_bf16x2(pp1[2], pp1[3]);
+    auto lo_pair = [](uint32_t h, float a, float b) {
+      return pack_bf16x2(a - __uint_as_float(h << 16), b - __uint_as_float(h & 0xffff0000u));
+    };
+    lw.x = lo_pair(hw.x, pp0[0], pp0[1]);
+    lw.y = lo_pair(hw.y, pp0[2], pp0[3]);
+    lw.z = lo_pair(hw.z, pp1[0], pp1[1]);
+    lw.w = lo_pair(hw.w, pp1[2], pp1[3]);
+    const bf16x8 ph = as_bf16x8(hw), pl = as_bf16x8(lw);
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       const int voff = rv * 256 + 8 * (c & 1) + 16 * ((2 * db + ((c >> 1) & 1)) ^ swv) + 32 * s * 256;
       const u32x2 v0 = lds_read_tr16(Ks, voff);
       const u32x2 v1 = lds_read_tr16(Ks, voff + 16 * 256);
       const bf16x8 va = as_bf16x8(u32x4{v0.x, v0.y, v1.x, v1.y});
-      oacc[db] = mfma16x16x32(va, pb, oacc[db]);
+      oacc[db] = mfma16x16x32(va, ph, oacc[db]);
+      oacc[db] = mfma16x16x32(va, pl, oacc[db]);
     }
   }
 }
@@ -328,11 +343,12 @@ __global__ __launch_bounds__(NHG * 64) void attn_kernel(
 }
 
 // Log-sum-exp merge of the split partials: one thread per (query row, head, dim). Splits are
-// consumed 8 at a time with all their loads issued together and an online rescale.
+// consumed CH at a time with all their loads issued together and an online rescale; the
+// launch picks CH >= nsplit when it can, so the merge waits on memory once.
+template <int CH>
 __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
                                                          int nsplit, int nrows, int H, float* __restrict__ out,
                                                          float* __restrict__ lse_out) {
-  constexpr int CH = 8;
   const int row = blockIdx.x;
   const int e = blockIdx.y * 256 + threadIdx.x;  // (head, dim) index inside the row
   if (e >= H * kD) return;
@@ -346,11 +362,14 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
   for (int c0 = 0; c0 < nsplit; c0 += CH) {
     float ls[CH], o[CH];
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const int s = c0 + j;
-      ls[j] = (s < nsplit) ? lse_p[s * lse_stride] : -INFINITY;
-      o[j] = (s < nsplit) ? o_p[s * o_stride] : 0.f;
+    for (int j = 0; j < CH; ++j) {  // clamped split index: every load is issued, none branches
+      const int s = c0 + j < nsplit ? c0 + j : nsplit - 1;
+      ls[j] = lse_p[s * lse_stride];
+      o[j] = o_p[s * o_stride];
     }
+#pragma unroll
+    for (int j = 0; j < CH; ++j)
+      if (c0 + j >= nsplit) ls[j] = -INFINITY;
     float cm = -INFINITY;
 #pragma unroll
     for (int j = 0; j < CH; ++j) cm = fmaxf(cm, ls[j]);
@@ -409,8 +428,11 @@ AttnPlan attn_plan(int B, int T, int64_t max_keys) {
   AttnPlan p;
   const int64_t rows = (int64_t)B * T;
   const int64_t tiles = max_keys > 0 ? (max_keys + kKT - 1) / kKT : 1;
-  int64_t want = rows >= 512 ? 1 : (1024 + rows - 1) / rows;  // aim for ~1024 workgroups
-  if (want > tiles) want = tiles;
+  // aim for about one workgroup per CU, with at least two tiles per split when the list has
+  // them: a workgroup walking several tiles prefetches them, while every extra split adds a
+  // partial (o, lse) to write and merge
+  int64_t want = rows >= 256 ? 1 : (256 + rows - 1) / rows;
+  if (want > (tiles + 1) / 2) want = (tiles + 1) / 2;
   if (want < 1) want = 1;
   const int64_t tps = (tiles + want - 1) / want;
   p.keys_per_split = (int)(tps * kKT);
@@ -442,8 +464,13 @@ hipError_t launch_attention(bool sparse, const void* q, const void* ckv, const i
                         : launch_nhg<false>(H, grid, st, q16, c16, idx, k, k16, kv_off, ent_off, q_pos, m, n_win, T,
                                             sl2, max_entries, p.keys_per_split, out, lse, ws_o, ws_lse);
   if (e != hipSuccess || p.nsplit <= 1) return e;
-  attn_merge_kernel<<<dim3((unsigned)rows, (unsigned)((H * kD + 255) / 256)), 256, 0, st>>>(ws_o, ws_lse, p.nsplit,
-                                                                                             rows, H, out, lse);
+  const dim3 mgrid((unsigned)rows, (unsigned)((H * kD + 255) / 256));
+  if (p.nsplit <= 8)
+    attn_merge_kernel<8><<<mgrid, 256, 0, st>>>(ws_o, ws_lse, p.nsplit, rows, H, out, lse);
+  else if (p.nsplit <= 16)
+    attn_merge_kernel<16><<<mgrid, 256, 0, st>>>(ws_o, ws_lse, p.nsplit, rows, H, out, lse);
+  else
+    attn_merge_kernel<32><<<mgrid, 256, 0, st>>>(ws_o, ws_lse, p.nsplit, rows, H, out, lse);
   return hipGetLastError();
 }
 

@@ -49,6 +49,7 @@ def assert_attn_close(g, r, what="", atol=ATTN_ABS):
     diff = np.where(both_inf, 0.0, np.abs(g - r))
     assert not np.isnan(diff).any(), f"{what}: NaN in comparison"
     m = diff.max() if diff.size else 0.0
+    print(f"  {what}: max abs err {m:.3e} (bound {atol})", flush=True)
     assert m <= atol, f"{what}: max abs err {m:.3e} > {atol}"
 
 

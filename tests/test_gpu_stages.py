@@ -218,6 +218,9 @@ def _attn_inputs(lengths, m, H, T, q_pos, seed):
     (16, 1, [800, 800], [800, 800], 256, 0, 0.3),
     (128, 1, [9000], [9000], 200, 50, 1.0),
     (64, 40, [3000], [2500], 96, 128, 0.9),
+    (16, 1, [4096], [4096], 32, 16, 1.0),         # one tile per row: the single-tile kernel
+    (48, 2, [300, 50], [300, 50], 40, 24, 0.8),   # 3 head groups, at most one tile
+    (80, 300, [5000], [4000], 64, 64, 1.0),       # 300 rows: one split per row, no merge
 ])
 def test_sparse_attention_matches_oracle(csl, H, T, lengths, q_pos, k, n_win, fill):
     print(f"sparse attn H={H} T={T} lengths={lengths} k={k} n_win={n_win} fill={fill}", flush=True)
@@ -266,6 +269,7 @@ def test_sparse_attention_ignores_out_of_range_ids_and_empty_sets(csl):
     (16, 4, [9000], [7000], 4, 128),
     (64, 1, [127, 128, 129], [127, 128, 129], 128, 128),
     (32, 2, [5000], [5000], 4, 0),
+    (96, 1, [2000, 700], [2000, 700], 128, 32),   # at most 47 keys: the single-tile kernel, 6 head groups
 ])
 def test_hca_attention_matches_oracle(csl, H, T, lengths, q_pos, m, n_win):
     print(f"hca attn H={H} T={T} lengths={lengths} m={m} n_win={n_win}", flush=True)
