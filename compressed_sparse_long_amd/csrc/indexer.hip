@@ -207,16 +207,16 @@ __device__ __forceinline__ float head_sum(float v) {
 // (blockIdx.x >= key_blocks, first query tile) run a CompressJob instead: 4 row-splits x 16
 // lanes per entry, one row per thread, so the job adds no registers to the streaming path.
 constexpr int kJobRS = 4;
-constexpr int kJobEntriesPerBlock = 512 / (16 * kJobRS);
+constexpr int kJobEntriesPerBlock = kSlice / (16 * kJobRS);
 
 template <int HI, bool FP8, bool PREP>
-__global__ __launch_bounds__(512) void indexer_decode_kernel(
+__global__ __launch_bounds__(kSlice) void indexer_decode_kernel(
     const uint16_t* __restrict__ qI, const float* __restrict__ w, const void* __restrict__ kI,
     const float* __restrict__ k_scale, const int64_t* __restrict__ scale_off, int scale_group,
     const int64_t* __restrict__ ent_off, const int64_t* __restrict__ q_pos, int m, int T,
     int64_t max_entries, float* __restrict__ scores, int64_t ld, void* topk_ws, int topk_k, int slot_budget,
     int key_blocks, CompressJob job) {
-  constexpr int NW = 8;
+  constexpr int NW = kSlice / kWave;
   constexpr int U = 4;
   constexpr int EPW = 16 * U;   // keys per wave: one per lane on the way out
   constexpr int EPB = EPW * NW; // keys per block
@@ -231,10 +231,10 @@ __global__ __launch_bounds__(512) void indexer_decode_kernel(
       const uint16_t* z16 = static_cast<const uint16_t*>(job.z);
       const int64_t blk = (int64_t)blockIdx.x - key_blocks;
       if (z16)
-        compress_block<512, 16, kJobRS, true, true, 1>(k16, z16, job.kv_off, ent_off, job.first_entry, 128, job.m,
+        compress_block<kSlice, 16, kJobRS, true, true, 1>(k16, z16, job.kv_off, ent_off, job.first_entry, 128, job.m,
                                                        job.max_new, job.out, blockIdx.z, blk);
       else
-        compress_block<512, 16, kJobRS, false, true, 1>(k16, z16, job.kv_off, ent_off, job.first_entry, 128, job.m,
+        compress_block<kSlice, 16, kJobRS, false, true, 1>(k16, z16, job.kv_off, ent_off, job.first_entry, 128, job.m,
                                                         job.max_new, job.out, blockIdx.z, blk);
     }
     return;

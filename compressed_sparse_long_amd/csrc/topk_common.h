@@ -7,7 +7,8 @@
 // of the slice whose key reaches the cut is listed -- and at most R listed (key << 32 | id)
 // pairs, in ascending id order, into its own R slots (0 marks an empty slot). A row's slot
 // budget is 16..64 per slice of the longest row of the call (about six times such a slice's
-// expected share of the winners), and a shorter row gives each of its slices up to 64. The cut comes from two levels of order statistics taken
+// expected share of the winners), and a shorter row gives each of its slices up to 64. The
+// cut comes from two levels of order statistics taken
 // with wave ballots: each wave of 64 entries keeps its 8 (or, where a wave expects more than
 // 3/4 of a winner, 16) largest keys, and one wave keeps the `quota` largest of those (quota is
 // 8..R, six times the slice's expected share of the k winners). Each level's cut is the r-th
@@ -16,8 +17,9 @@
 // is at least every slice's cut, the k best listed entries are exactly the k best of the row:
 // every entry left out lies strictly below its slice's cut. The finishing step checks that and
 // searches the whole row otherwise; at 1M context a slice holds 12 or more of the k winners
-// when it expects two with probability ~1.4e-6. Rows with more than 5 expected winners per
-// wave of 64 skip the lists.
+// when it expects two with probability ~1.4e-6 (smaller slices would need a larger multiple
+// of their expected share: the tail of a small count is fatter). Rows with more than 5
+// expected winners per wave of 64 skip the lists.
 #pragma once
 
 #include "device_common.h"
@@ -222,7 +224,7 @@ __device__ __forceinline__ void find_threshold_bin(const uint32_t* hist, uint32_
   __syncthreads();
 }
 
-static_assert(kSlice / kWave * kWaveListMax == 2 * kWave, "the wave lists of a slice fill two values per lane");
+static_assert(kSlice / kWave * kWaveListMax <= 2 * kWave, "the wave lists of a slice fit two values per lane");
 static_assert(kMaxSliceSlots <= kWave, "one wave writes the slice's slots");
 
 // LDS scratch of slice_candidates: every wave's list and cut
@@ -258,12 +260,14 @@ __device__ __forceinline__ void slice_candidates(uint32_t x, int quota, int wl, 
   if (lane == 0) sc.cut[wave] = th;
   __syncthreads();
   if (wave != 0) return;
-  // level 2: the quota largest of the wave lists (entry e = w * wl + j; lane holds e = lane
-  // and, with 16 per wave, e = 64 + lane), and never below a wave's own cut
-  const bool two = wl * (kSlice / kWave) > kWave;
-  const int e0 = lane, e1 = lane + kWave;
-  const uint32_t y0 = sc.key[e0 / wl][e0 % wl], o0 = sc.off[e0 / wl][e0 % wl];
-  const uint32_t y1 = two ? sc.key[e1 / wl][e1 % wl] : 0u, o1 = two ? sc.off[e1 / wl][e1 % wl] : 0u;
+  // level 2: the quota largest of the wave lists (entry e = w * wl + j, ne of them; lane holds
+  // e = lane and, when ne > 64, e = 64 + lane; lanes past ne hold no entry), and never below a
+  // wave's own cut
+  const int ne = wl * (kSlice / kWave);
+  const bool two = ne > kWave;
+  const int e0 = lane < ne ? lane : ne - 1, e1 = lane + kWave < ne ? lane + kWave : ne - 1;
+  const uint32_t y0 = lane < ne ? sc.key[e0 / wl][e0 % wl] : 0u, o0 = sc.off[e0 / wl][e0 % wl];
+  const uint32_t y1 = two && lane + kWave < ne ? sc.key[e1 / wl][e1 % wl] : 0u, o1 = sc.off[e1 / wl][e1 % wl];
   uint32_t cut = two ? wave_rth_threshold<true>(y0, y1, quota) : wave_rth_threshold<false>(y0, 0u, quota);
 #pragma unroll
   for (int w = 0; w < kSlice / kWave; ++w) cut = max(cut, sc.cut[w]);
