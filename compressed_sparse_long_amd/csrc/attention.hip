@@ -219,23 +219,29 @@ __device__ __forceinline__ void attn_write(const f32x4 (&oacc)[8], float m_run, 
 
 // Attention over one query row's key range. Each thread gathers whole 64-byte pieces of rows:
 // pair p = j * NT + tid takes row p / 4, units 4q + p % 4 (q = 0..3), so 4 lanes read 64
-// contiguous bytes per load and a thread resolves one row address per tile. With MULTI the
-// workgroup walks several tiles and loads the next tile's rows (and the selected ids of the
-// one after) into registers while the current tile is multiplied; without it the range is
-// one tile (decode) and the kernel keeps fewer registers live.
-template <int NHG, bool SPARSE, bool MULTI>
+// contiguous bytes per load and a thread resolves one row address per row it gathers.
+// MODE 1 or 2: the range is at most that many tiles, all gathered at once (one round trip)
+// and then multiplied; this is the decode shape, where a lone workgroup would otherwise wait
+// for each tile's rows in turn. MODE 0: the workgroup walks many tiles and loads the next
+// tile's rows (and the selected ids of the one after) into registers while the current tile
+// is multiplied.
+template <int NHG, bool SPARSE, int MODE>
 __global__ __launch_bounds__(NHG * 64) void attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ ckv, const int32_t* __restrict__ idx, int k,
     const uint16_t* __restrict__ kv, const int64_t* __restrict__ kv_off, const int64_t* __restrict__ ent_off,
     const int64_t* __restrict__ q_pos, int m, int n_win, int T, float scale_log2, int64_t max_entries,
     int keys_per_split, float* __restrict__ out, float* __restrict__ lse_out, float* __restrict__ ws_o,
     float* __restrict__ ws_lse) {
+  constexpr bool MULTI = MODE == 0;
+  constexpr int NTL = MULTI ? 1 : MODE;    // tiles held in LDS at once
   constexpr int NT = NHG * 64;
   constexpr int H = NHG * 16;
-  constexpr int NP = 4 * kKT;              // gather pairs per tile
+  constexpr int NV = kKT * NTL;            // rows gathered per round
+  constexpr int NP = 4 * NV;               // gather pairs per round
   constexpr int RPT = (NP + NT - 1) / NT;  // pairs (rows) per thread
-  __shared__ __align__(16) uint8_t Ks[kKT * kD * 2];
-  __shared__ __align__(16) uint8_t vld[kKT];  // slot v of the current tile holds a key
+  static_assert(RPT <= 32, "one mask bit per gathered row");
+  __shared__ __align__(16) uint8_t Ks[NTL][kKT * kD * 2];
+  __shared__ __align__(16) uint8_t vld[NTL][kKT];  // slot v of a tile holds a key
 
   const int split = blockIdx.x;
   const int row = blockIdx.y;
@@ -267,18 +273,18 @@ __global__ __launch_bounds__(NHG * 64) void attn_kernel(
   const int64_t L = n_comp + geo.win_cnt;
   const int64_t k_hi = (k_lo + keys_per_split < L) ? k_lo + keys_per_split : L;
 
-  // Row addresses as integers, computed without branches. Slot t0 + v of a tile (v < 64) is
+  // Row addresses as integers, computed without branches. Slot t0 + v of a round (v < NV) is
   // a compressed entry while v < n_comp - t0 and holds a key while v < k_hi - t0; both limits
-  // are clamped to [0, 64] so the per-slot tests are 32-bit.
+  // are clamped to [0, NV] so the per-slot tests are 32-bit.
   const uint64_t ckv_a = reinterpret_cast<uint64_t>(ckv);
   const uint64_t ent_a = ckv_a + (uint64_t)geo.ent_base * (kD * 2);
   const uint64_t win_a = reinterpret_cast<uint64_t>(kv) + (uint64_t)(geo.kv_base + geo.win_lo - n_comp) * (kD * 2);
   const uint32_t n_ent32 = (uint32_t)(geo.n_ent < 0x7fffffff ? geo.n_ent : 0x7fffffff);
-  auto clamp_tile = [](int64_t x) { return (int)(x < 0 ? 0 : (x > kKT ? kKT : x)); };
+  auto clamp_round = [](int64_t x) { return (int)(x < 0 ? 0 : (x > NV ? NV : x)); };
   u32x4 r[RPT][4];
   uint32_t okm = 0;  // bit j: pair j's row holds a key
   auto issue = [&](int64_t t0, const int32_t (&ids)[RPT]) {
-    const int lim_c = clamp_tile(n_comp - t0), lim_h = clamp_tile(k_hi - t0);
+    const int lim_c = clamp_round(n_comp - t0), lim_h = clamp_round(k_hi - t0);
     const uint64_t win_t = win_a + (uint64_t)t0 * (kD * 2);
     okm = 0;
 #pragma unroll
@@ -315,19 +321,20 @@ __global__ __launch_bounds__(NHG * 64) void attn_kernel(
   float l_run = 0.f;
 
   if (k_lo < k_hi) issue(k_lo, ids_cur);
-  for (int64_t t0 = k_lo; t0 < k_hi; t0 += kKT) {
-    // this tile's rows (in flight since the previous tile) into the swizzled K tile
+  for (int64_t t0 = k_lo; t0 < k_hi; t0 += NV) {
+    // this round's rows (in flight since the previous round) into the swizzled K tiles
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
       const int pr = j * NT + tid;
       if ((j + 1) * NT > NP && pr >= NP) break;
       const int v = pr / 4, u = pr % 4;
+      const int tl = v / kKT, vr = v % kKT;
       const bool ok = (okm >> j) & 1u;
-      const int sw = ks_swz(v);
+      const int sw = ks_swz(vr);
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq)
-        *reinterpret_cast<u32x4*>(Ks + v * 256 + 16 * ((4 * qq + u) ^ sw)) = ok ? r[j][qq] : u32x4{0, 0, 0, 0};
-      if (u == 0) vld[v] = ok ? 1 : 0;
+        *reinterpret_cast<u32x4*>(Ks[tl] + vr * 256 + 16 * ((4 * qq + u) ^ sw)) = ok ? r[j][qq] : u32x4{0, 0, 0, 0};
+      if (u == 0) vld[tl][vr] = ok ? 1 : 0;
     }
     __syncthreads();
     // the next tile's rows and the ids two tiles ahead go out while this one computes
@@ -335,8 +342,10 @@ __global__ __launch_bounds__(NHG * 64) void attn_kernel(
       issue(t0 + kKT, ids_nxt);
       if (SPARSE && t0 + 2 * kKT < k_hi) load_ids(t0 + 2 * kKT, ids_nxt);
     }
-    tile_compute(Ks, vld, qb, scale_log2, oacc, m_run, l_run, c, g);
-    if (!MULTI) break;  // the launch gives single-tile kernels at most one tile
+#pragma unroll
+    for (int tl = 0; tl < NTL; ++tl)
+      if (tl == 0 || t0 + tl * kKT < k_hi) tile_compute(Ks[tl], vld[tl], qb, scale_log2, oacc, m_run, l_run, c, g);
+    if (!MULTI) break;  // the launch gives single-round kernels at most NTL tiles
     __syncthreads();    // the next tile overwrites Ks / vld
   }
   attn_write(oacc, m_run, l_run, row, nrows, split, H, head, g, out, lse_out, ws_o, ws_lse);
@@ -395,17 +404,21 @@ hipError_t launch_nhg(int H, dim3 grid, hipStream_t st, const uint16_t* q, const
                       int k, const uint16_t* kv, const int64_t* kv_off, const int64_t* ent_off, const int64_t* q_pos,
                       int m, int n_win, int T, float scale_log2, int64_t max_entries, int kps, float* out,
                       float* lse, float* ws_o, float* ws_lse) {
-  const bool multi = kps > kKT;  // several tiles per workgroup: the prefetching kernel
+  const int tiles = kps / kKT;  // 1 or 2: gathered in one round; more: the prefetching loop
 #define CSL_ATTN_CASE(NHG)                                                                                     \
   case NHG:                                                                                                    \
-    if (multi)                                                                                                 \
-      attn_kernel<NHG, SPARSE, true><<<grid, NHG * 64, 0, st>>>(q, ckv, idx, k, kv, kv_off, ent_off, q_pos, m,  \
-                                                                n_win, T, scale_log2, max_entries, kps, out, lse, \
-                                                                ws_o, ws_lse);                                  \
+    if (tiles == 1)                                                                                            \
+      attn_kernel<NHG, SPARSE, 1><<<grid, NHG * 64, 0, st>>>(q, ckv, idx, k, kv, kv_off, ent_off, q_pos, m, n_win, \
+                                                             T, scale_log2, max_entries, kps, out, lse, ws_o,      \
+                                                             ws_lse);                                              \
+    else if (tiles == 2)                                                                                       \
+      attn_kernel<NHG, SPARSE, 2><<<grid, NHG * 64, 0, st>>>(q, ckv, idx, k, kv, kv_off, ent_off, q_pos, m, n_win, \
+                                                             T, scale_log2, max_entries, kps, out, lse, ws_o,      \
+                                                             ws_lse);                                              \
     else                                                                                                       \
-      attn_kernel<NHG, SPARSE, false><<<grid, NHG * 64, 0, st>>>(q, ckv, idx, k, kv, kv_off, ent_off, q_pos, m, \
-                                                                 n_win, T, scale_log2, max_entries, kps, out,   \
-                                                                 lse, ws_o, ws_lse);                            \
+      attn_kernel<NHG, SPARSE, 0><<<grid, NHG * 64, 0, st>>>(q, ckv, idx, k, kv, kv_off, ent_off, q_pos, m, n_win, \
+                                                             T, scale_log2, max_entries, kps, out, lse, ws_o,      \
+                                                             ws_lse);                                              \
     break;
   switch (H / 16) {
     CSL_ATTN_CASE(1)
