@@ -9,29 +9,36 @@
 // Layout: a thread owns 8 consecutive dimensions (16 bytes of bf16) of one entry and a
 // strided subset of its rows; TPE = D/8 threads cover one row, RS row-splits of the same
 // entry sit TPE lanes apart inside a wave and merge their partial softmax states with
-// xor-shuffles. Loads are 16-byte, row-contiguous across the TPE lanes, so a wave reads
-// whole 256-byte rows. It reads 2*m*D*2 bytes and writes D*4 (fp32) or D*2 (bf16) bytes
-// per entry.
+// xor-shuffles, and for long chunks RSX waves split the rows further and merge through LDS
+// (an m = 128 entry then loads in one round trip). Loads are 16-byte, row-contiguous across
+// the TPE lanes, so a wave reads whole 256-byte rows. It reads 2*m*D*2 bytes and writes D*4
+// (fp32) or D*2 (bf16) bytes per entry.
 #pragma once
 
 #include "device_common.h"
 
 namespace csl {
 
-// One workgroup of NT threads compresses the NT / (TPE * RS) entries first_entry[b] +
+// One workgroup of NT threads compresses the NT / (TPE * RS * RSX) entries first_entry[b] +
 // blk * that .. of sequence b (entries past max_new or past the sequence end are skipped).
-// Each thread loads ROWS of its rows at a time.
-template <int NT, int TPE, int RS, bool HAS_Z, bool OUT_BF16, int ROWS = 4>
+// Each thread loads ROWS of its rows at a time. With RSX > 1 every thread of the workgroup
+// must call this (it holds a workgroup barrier).
+template <int NT, int TPE, int RS, bool HAS_Z, bool OUT_BF16, int ROWS = 4, int RSX = 1>
 __device__ __forceinline__ void compress_block(
     const uint16_t* __restrict__ kv, const uint16_t* __restrict__ z,
     const int64_t* __restrict__ kv_off, const int64_t* __restrict__ ent_off,
     const int64_t* __restrict__ first_entry, int D, int m, int64_t max_new, void* __restrict__ out, int b,
     int64_t blk) {
-  constexpr int EPB = NT / (TPE * RS);  // entries per block
+  static_assert(TPE * RS <= kWave, "in-wave row-splits merge by shuffles");
+  static_assert(RSX == 1 || TPE * RS == kWave, "cross-wave splits take whole waves");
+  constexpr int EPB = NT / (TPE * RS * RSX);  // entries per block
+  constexpr int NSPLIT = RS * RSX;           // row-splits per entry
   const int t = threadIdx.x;
   const int dg = t % TPE;
-  const int rs = (t / TPE) % RS;
-  const int el = t / (TPE * RS);
+  const int rsw = (t / TPE) % RS;              // split inside the wave
+  const int rsx = (t / (TPE * RS)) % RSX;      // wave of the entry
+  const int rs = rsx * RS + rsw;               // row-split index of this lane
+  const int el = t / (TPE * RS * RSX);
 
   const int64_t row0 = kv_off[b];
   const int64_t n_rows = kv_off[b + 1] - row0;
@@ -54,15 +61,15 @@ __device__ __forceinline__ void compress_block(
     const int64_t base_row = row0 + i * (int64_t)m;
     const uint16_t* kvp = kv + base_row * D + dg * 8;
     const uint16_t* zp = HAS_Z ? (z + base_row * D + dg * 8) : nullptr;
-    // rows handled by this lane: r = rs + RS * j
-    const int my_rows = (m > rs) ? (m - rs + RS - 1) / RS : 0;
+    // rows handled by this lane: r = rs + NSPLIT * j
+    const int my_rows = (m > rs) ? (m - rs + NSPLIT - 1) / NSPLIT : 0;
     for (int j0 = 0; j0 < my_rows; j0 += ROWS) {
       u32x4 kr[ROWS], zr[ROWS];
       const int cnt = min(ROWS, my_rows - j0);
 #pragma unroll
       for (int u = 0; u < ROWS; ++u) {
         if (u < cnt) {
-          const int64_t r = rs + (int64_t)RS * (j0 + u);
+          const int64_t r = rs + (int64_t)NSPLIT * (j0 + u);
           kr[u] = *reinterpret_cast<const u32x4*>(kvp + r * D);
           if (HAS_Z) zr[u] = *reinterpret_cast<const u32x4*>(zp + r * D);
         }
@@ -124,7 +131,7 @@ __device__ __forceinline__ void compress_block(
     }
   }
 
-  // merge the RS partial states of one entry (lanes TPE*2^j apart in the same wave)
+  // merge the RS partial states of one entry inside the wave (lanes TPE*2^j apart)
 #pragma unroll
   for (int step = 1; step < RS; step <<= 1) {
     const int mask = TPE * step;
@@ -140,6 +147,36 @@ __device__ __forceinline__ void compress_block(
       s[d] = s[d] * f1 + s2 * f2;
       acc[d] = acc[d] * f1 + a2 * f2;
       mu[d] = M;
+    }
+  }
+
+  if (RSX > 1) {
+    // the RSX waves of an entry: lanes with rsw == 0 post their state, the first wave merges
+    __shared__ float xs[RSX > 1 ? EPB : 1][RSX][TPE][3][8];
+    if (rsw == 0) {
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        xs[el][rsx][dg][0][d] = mu[d];
+        xs[el][rsx][dg][1][d] = s[d];
+        xs[el][rsx][dg][2][d] = acc[d];
+      }
+    }
+    __syncthreads();
+    if (rsx == 0 && rsw == 0) {
+#pragma unroll
+      for (int w = 1; w < RSX; ++w) {
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+          const float mu2 = xs[el][w][dg][0][d], s2 = xs[el][w][dg][1][d], a2 = xs[el][w][dg][2][d];
+          const float M = fmaxf(mu[d], mu2);
+          if (M == -INFINITY) continue;
+          const float f1 = __builtin_amdgcn_exp2f(mu[d] - M);
+          const float f2 = __builtin_amdgcn_exp2f(mu2 - M);
+          s[d] = s[d] * f1 + s2 * f2;
+          acc[d] = acc[d] * f1 + a2 * f2;
+          mu[d] = M;
+        }
+      }
     }
   }
 
