@@ -441,10 +441,10 @@ AttnPlan attn_plan(int B, int T, int64_t max_keys) {
   AttnPlan p;
   const int64_t rows = (int64_t)B * T;
   const int64_t tiles = max_keys > 0 ? (max_keys + kKT - 1) / kKT : 1;
-  // aim for about one workgroup per CU, with at least two tiles per split when the list has
+  // aim for about two workgroups per CU, with at least two tiles per split when the list has
   // them: a workgroup walking several tiles prefetches them, while every extra split adds a
   // partial (o, lse) to write and merge
-  int64_t want = rows >= 256 ? 1 : (256 + rows - 1) / rows;
+  int64_t want = rows >= 512 ? 1 : (512 + rows - 1) / rows;
   if (want > (tiles + 1) / 2) want = (tiles + 1) / 2;
   if (want < 1) want = 1;
   const int64_t tps = (tiles + want - 1) / want;
