@@ -19,6 +19,8 @@ workload.
 
   python bench.py [--steps K] [--warmup W] [--copies R] [--no-cpu-baseline]
   python bench.py --copy-calibration     # plain device copy of known size (for counters)
+  python bench.py --run-workload NAME    # replay another configuration's step (for profiles;
+                                         # prints its step time, not a bench line)
 """
 from __future__ import annotations
 
@@ -35,6 +37,7 @@ if ROOT not in sys.path:
 
 METRIC = "CSA/HCA decode queries/s at 1M ctx; achieved HBM GB/s vs MI355X peak"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published peak
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published peak
 WORKLOAD = "csa_decode_1m"
 COUNTER_FILE = os.path.join(ROOT, "profiles", "indexer_csa_decode_1m_counters.txt")
 INDEXER_SOURCES = ["compressed_sparse_long_amd/csrc/indexer.hip", "compressed_sparse_long_amd/csrc/device_common.h",
@@ -52,6 +55,9 @@ def parse():
     ap.add_argument("--no-stages", action="store_true", help="skip the per-stage breakdown pass")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM counters)")
+    ap.add_argument("--run-workload", default=None,
+                    help="replay --steps steps of another synthetic configuration (for profiling) and print "
+                         "its mean step time")
     return ap.parse_args()
 
 
@@ -150,6 +156,9 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
+    if args.run_workload:
+        run_workload(args.run_workload, args.steps, args.warmup)
+        return
 
     import synth
     from compressed_sparse_long_amd import lanes
@@ -225,6 +234,11 @@ def main():
                   + B * (2 * lane.m * D * 2 + D * 2))                            # newest-chunk compress
     achieved = idx_bytes / (idx_us * 1e-6) / 1e9
     traffic = read_traffic(idx_bytes)
+    # the indexer's contraction: algorithmic flops, and the flops its MFMAs issue (the B
+    # operand holds 16 / HI query rows x HI heads, so with one query row per sequence the
+    # remaining columns are padding)
+    idx_flops = B * T * E * HI * CI * 2
+    idx_issued = B * ((T + 16 // HI - 1) // (16 // HI)) * E * 16 * CI * 2
 
     result = {
         "metric": METRIC,
@@ -245,23 +259,36 @@ def main():
         "roofline": {"kernel": "indexer_decode_kernel", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "launch_us": round(idx_us, 3), "bytes_per_launch": idx_bytes},
+        "indexer_mfma": {"flops_per_launch": idx_flops, "issued_flops_per_launch": idx_issued,
+                         "achieved": round(idx_flops / (idx_us * 1e-6) / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(idx_flops / (idx_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5)},
         "step_us_one_graph_per_step": round(single_us, 2),
         "step_hbm": {"bytes": step_bytes, "GB_s": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
                      "frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
     }
 
     if not args.no_stages:
-        # per-stage device time from graphs of single stages (top-k is timed with its indexer)
-        g_comp = [capture(lambda r=r: cl.compress_new(r)) for r in range(R)]
-        g_idx = [capture(lambda r=r: cl.index(r)) for r in range(R)]
-        g_idx_topk = [capture(lambda r=r: (cl.index(r), cl.select())) for r in range(R)]
-        g_attn = [capture(lambda r=r: cl.attend(r)) for r in range(R)]
-        t_idx = time_graphs(g_idx, 200)
+        # per-stage device time per launch: graphs of n back-to-back launches over the rotated
+        # copies (top-k is timed with its indexer, as the difference)
+        n = 25 * R
+        g_comp = capture(lambda: [cl.compress_new(i % R) for i in range(n)])
+        g_idx = capture(lambda: [cl.index(i % R) for i in range(n)])
+        g_idx_topk = capture(lambda: [(cl.index(i % R), cl.select()) for i in range(n)])
+        g_attn = capture(lambda: [cl.attend(i % R) for i in range(n)])
+        t_idx = time_graphs([g_idx], 4, per_replay=n)
         cl.select()
         torch.cuda.synchronize()
-        t_it = time_graphs(g_idx_topk, 200)
-        result["stages_us"] = {"compress_new": round(time_graphs(g_comp, 200), 2), "indexer": round(t_idx, 2),
-                               "topk": round(t_it - t_idx, 2), "attention": round(time_graphs(g_attn, 200), 2)}
+        t_it = time_graphs([g_idx_topk], 4, per_replay=n)
+        t_comp, t_attn = time_graphs([g_comp], 4, per_replay=n), time_graphs([g_attn], 4, per_replay=n)
+        result["stages_us"] = {"compress_new": round(t_comp, 2), "indexer": round(t_idx, 2),
+                               "topk": round(t_it - t_idx, 2), "attention": round(t_attn, 2)}
+        # algorithmic HBM bytes of the streaming and gather stages over their per-launch times
+        comp_bytes = B * (2 * lane.m * D * 2 + D * 2)
+        attn_bytes = B * T * (k * 4 + (k + W) * D * 2 + H * D * 2 + H * D * 4 + H * 4)  # ids, rows, q, out, lse
+        gbs = lambda nb, us: {"bytes": nb, "GB_s": round(nb / (us * 1e-6) / 1e9, 1),
+                              "frac": round(nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        result["stages_hbm"] = {"compress_new": gbs(comp_bytes, t_comp), "indexer": gbs(idx_bytes, t_idx),
+                                "attention": gbs(attn_bytes, t_attn)}
         # bulk compression of one whole 4 x 1M-token context (2 GiB read)
         g_bulk = [capture(lambda r=r: lanes.compress_kv(cl.kv, cl.z, cl.kv_off, cl.ent_off, cl.m, cl.ckv_copies[r],
                                                         max_new_entries=cl.max_entries)) for r in range(R)]
@@ -273,6 +300,34 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def run_workload(name: str, steps: int, warmup: int) -> None:
+    """Replay one configuration's whole step (every lane) as a graph; print its mean time."""
+    import torch
+    import synth
+    from compressed_sparse_long_amd import lanes
+
+    inp = synth.generate(name)
+    ls = lanes.build_lanes(inp)
+    for lane in ls:
+        lane.compress_all()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for lane in ls:
+            lane.step(0)
+    for _ in range(max(warmup, 1)):
+        g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    print(f"workload {name}: {a.elapsed_time(b) / steps * 1e3:.1f} us per step over {steps} graph replays",
+          flush=True)
 
 
 if __name__ == "__main__":
