@@ -21,6 +21,8 @@ workload.
   python bench.py --copy-calibration     # plain device copy of known size (for counters)
   python bench.py --run-workload NAME    # replay another configuration's step (for profiles;
                                          # prints its step time, not a bench line)
+  python bench.py --report-configs       # every synthetic configuration: queries/s, GB/s and
+                                         # roofline fraction beside the oracle (not a bench line)
 """
 from __future__ import annotations
 
@@ -55,6 +57,9 @@ def parse():
     ap.add_argument("--no-stages", action="store_true", help="skip the per-stage breakdown pass")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM counters)")
+    ap.add_argument("--report-configs", action="store_true",
+                    help="time every synthetic configuration's step against its roofline and the oracle; one JSON "
+                         "line per configuration")
     ap.add_argument("--run-workload", default=None,
                     help="replay --steps steps of another synthetic configuration (for profiling) and print "
                          "its mean step time")
@@ -158,6 +163,9 @@ def main():
         return
     if args.run_workload:
         run_workload(args.run_workload, args.steps, args.warmup)
+        return
+    if args.report_configs:
+        report_configs(args.copies, args.cpu_seconds)
         return
 
     import synth
@@ -328,6 +336,147 @@ def run_workload(name: str, steps: int, warmup: int) -> None:
     torch.cuda.synchronize()
     print(f"workload {name}: {a.elapsed_time(b) / steps * 1e3:.1f} us per step over {steps} graph replays",
           flush=True)
+
+
+def step_model(lane_list, D: int = 128):
+    """Algorithmic HBM bytes and MFMA flops of one step of a configuration (all lanes).
+
+    Per sequence: the step's newest compressed entries; for CSA the indexer keys once, per
+    query row the indexer query and weights, the selected ids (written and read back), the
+    gathered entries and window rows, q, the output and lse; for HCA every visible entry and
+    the window. Prefill (T > 1) counts the score matrix's round trip (the top-k reads what the
+    indexer writes) and the gathered rows once each (the rows of one sequence are shared by
+    its query rows). Flops: indexer H_I*c^I*2 per (row, visible entry); attention H*D*4 per
+    (row, key) for the logits and the value product.
+    """
+    nbytes = flops = queries = 0
+    for lane in lane_list:
+        m, W, H, T = lane.m, lane.W, lane.H, lane.T
+        for b in range(lane.B):
+            N, E, p0 = lane.lengths[b], lane.entries[b], lane.q_pos[b]
+            first = max(0, min(p0 // m, E - 1)) if E else 0
+            nbytes += (E - first) * (2 * m * D * 2 + D * 2)
+            nv = [max(0, min((p0 + t) // m, E)) for t in range(T)]
+            win = [max(0, min(p0 + t, N - 1) - max(0, min(p0 + t, N - 1) - W + 1) + 1) if N else 0 for t in range(T)]
+            queries += T
+            nbytes += T * (H * D * 2 + H * D * 4 + H * 4)
+            if lane.kind == "csa":
+                kb = (lane.CI + 4.0 / lane.scale_group) if lane.kI_fp8 else lane.CI * 2
+                sel = [min(lane.k, n) for n in nv]
+                nbytes += int(max(nv) * kb) + T * (lane.HI * lane.CI * 2 + lane.HI * 4) + T * lane.k * 4 * 2
+                if T > 1:
+                    nbytes += 2 * 4 * sum(nv) + (max(nv) + T + W - 1) * D * 2
+                else:
+                    nbytes += (sel[0] + win[0]) * D * 2
+                flops += sum(nv) * lane.HI * lane.CI * 2 + sum(s + w for s, w in zip(sel, win)) * H * D * 4
+            else:
+                nbytes += ((max(nv) + T + W - 1) if T > 1 else (nv[0] + win[0])) * D * 2
+                flops += sum(n + w for n, w in zip(nv, win)) * H * D * 4
+    return int(nbytes), int(flops), queries
+
+
+def oracle_rate(inp, seconds: float, D: int = 128):
+    """The fp64 oracle's queries/s on the host: one sampled sequence per lane, its compressed
+    cache built before the clock starts (as the GPU's is); per query the newest chunk's
+    compression, then indexer, top-k and sparse attention (CSA) or dense attention (HCA)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import csa, pipeline
+
+    scale = 1.0 / np.sqrt(D)
+    work = []
+    for li in inp.lanes:
+        lane = li.lane
+        b = max(range(lane.B), key=lambda i: lane.lengths[i])  # the longest sequence of the lane
+        r0, N, m = lane.kv_off()[b], lane.lengths[b], lane.m
+        kvb = inp.kv[r0:r0 + N].double().numpy()
+        zb = inp.z[r0:r0 + N].double().numpy() if inp.z is not None else None
+        cache = csa.to_bf16_f64(csa.compress(kvb, zb, m))
+        keys = None
+        if lane.kind == "csa":
+            e0, e1 = lane.ent_off()[b], lane.ent_off()[b + 1]
+            if lane.kI_fp8:
+                allk = pipeline.index_keys_f64(li.kI, li.k_scale, li.scale_off, lane.ent_off(), lane.scale_group)
+                keys = allk[e0:e1]
+            else:
+                keys = li.kI[e0:e1].double().numpy()
+        q = inp.q[li.q_slice][b].double().numpy()
+        work.append((li, lane, b, kvb, zb, cache, keys, q))
+    t0 = time.perf_counter()
+    n = 0
+    while n == 0 or time.perf_counter() - t0 < seconds:
+        li, lane, b, kvb, zb, cache, keys, q = work[n % len(work)]
+        t = (n // len(work)) % lane.T
+        m, N = lane.m, lane.lengths[b]
+        p = lane.q_pos[b] + t
+        e_new = min(p // m, N // m) - 1
+        if e_new >= 0:
+            csa.compress(kvb[e_new * m:(e_new + 1) * m], None if zb is None else zb[e_new * m:(e_new + 1) * m], m)
+        nv = csa.n_visible(p, m, N // m)
+        win = csa.window_rows(p, N, lane.W)
+        if lane.kind == "csa":
+            s = csa.indexer(li.qI[b, t].double().numpy(), li.w[b, t].double().numpy(), keys[:nv])
+            sel = csa.topk(s, lane.k)
+            X = np.concatenate([cache[sel[sel >= 0]], kvb[win.start:win.stop]])
+        else:
+            X = np.concatenate([cache[:nv], kvb[win.start:win.stop]])
+        csa.attend(q[t], X, scale)
+        n += 1
+    el = time.perf_counter() - t0
+    threads = 1
+    for info in threadpool_info():
+        if info.get("user_api") == "blas":
+            threads = max(threads, int(info.get("num_threads", 1)))
+    return {"value": round(n / el, 2), "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} queries ({len(work)} sampled sequence(s), fp64 numpy) in {el:.1f} s"}
+
+
+def report_configs(copies: int, cpu_seconds: float) -> None:
+    """Every synthetic configuration: whole-step time (graph of `copies` rotated steps),
+    queries/s, algorithmic GB/s and roofline fraction, and the oracle's rate beside it."""
+    import torch
+    import synth
+    from compressed_sparse_long_amd import lanes
+
+    for name in synth.CONFIG_ORDER:
+        inp = synth.generate(name)
+        ls = lanes.build_lanes(inp)
+        for lane in ls:
+            lane.rotate(copies)
+            lane.compress_all()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for r in range(copies):
+                for lane in ls:
+                    lane.step(r)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g.replay()
+        torch.cuda.synchronize()
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        reps = max(3, min(200, int(300.0 / max(a.elapsed_time(b), 1e-3))))  # about 0.3 s of replays
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        step_us = a.elapsed_time(b) / (reps * copies) * 1e3
+        nbytes, flops, queries = step_model([li.lane for li in inp.lanes])
+        bound_us = max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6
+        del ls
+        torch.cuda.empty_cache()
+        line = {"workload": name, "step_us": round(step_us, 2), "queries_per_s": round(queries / (step_us * 1e-6), 1),
+                "bytes": nbytes, "GB_s": round(nbytes / (step_us * 1e-6) / 1e9, 1),
+                "hbm_frac": round(nbytes / (step_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "flops": flops, "TFLOP_s": round(flops / (step_us * 1e-6) / 1e12, 2),
+                "bound": "hbm" if nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) else "mfma",
+                "roofline_us": round(bound_us, 2), "roofline_frac": round(bound_us / step_us, 4),
+                "cpu_baseline": oracle_rate(inp, cpu_seconds)}
+        print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

@@ -6,6 +6,7 @@ round-to-nearest-even cast) and the fp8 e4m3 encoding of indexer keys, which is 
 input-format step done with torch's own cast.
 """
 from .workloads import (  # noqa: F401
+    CONFIG_ORDER,
     WORKLOADS,
     Lane,
     Workload,
