@@ -249,15 +249,30 @@ __global__ __launch_bounds__(kFinNT) void topk_row_kernel(const float* __restric
   const uint32_t need_eq = all_in ? 0u : need;
 
   // ordered output: per (item, wave) counts of keys above the threshold and tied with it
+  // (id order is item, then wave, then lane). Each count is a ballot and a popcount; lane j
+  // of the wave collects item j's count branch-free and the wave posts them with one store
+  // per lane. Tied keys are rare (the threshold key itself), so their ballots run only in
+  // waves that hold one.
   auto above = [&](uint32_t x) {
     const uint32_t h = x >> shift;
     return x != 0u && (h > prefix || (all_in && h == prefix));
   };
   auto tied = [&](uint32_t x) { return x != 0u && !all_in && (x >> shift) == prefix; };
+  static_assert(ITEMS <= kWave, "one item count per lane");
+  const int lane = (int)lane_id();
+  bool my_tied = false;
 #pragma unroll
-  for (int j = 0; j < ITEMS; ++j) {
-    const uint64_t gm = __ballot(above(key[j])), em = __ballot(tied(key[j]));
-    if (lane_id() == 0) cnt[j * kFinWaves + wave] = (uint32_t)__popcll(gm) | ((uint32_t)__popcll(em) << 16);
+  for (int j = 0; j < ITEMS; ++j) my_tied |= tied(key[j]);
+  const bool wave_tied = __ballot(my_tied) != 0ull;  // wave-uniform
+  {
+    uint32_t mycnt = 0u;  // lane j: (above | tied << 16) count of item j in this wave
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+      uint32_t c = (uint32_t)__popcll(__ballot(above(key[j])));
+      if (wave_tied) c |= (uint32_t)__popcll(__ballot(tied(key[j]))) << 16;
+      mycnt = (lane == j) ? c : mycnt;
+    }
+    if (lane < ITEMS) cnt[lane * kFinWaves + wave] = mycnt;
   }
   __syncthreads();
   {
@@ -273,16 +288,24 @@ __global__ __launch_bounds__(kFinNT) void topk_row_kernel(const float* __restric
     if (tid < NC) cnt[tid] = before + incl - v;  // exclusive prefix of (gt | eq << 16)
     __syncthreads();
   }
+  // lane j holds item j's base for this wave; each item reads it with one lane read
+  const uint32_t mybase = (lane < ITEMS) ? cnt[lane * kFinWaves + wave] : 0u;
 #pragma unroll
   for (int j = 0; j < ITEMS; ++j) {
-    const bool g = above(key[j]), e = tied(key[j]);
-    const uint64_t gm = __ballot(g), em = __ballot(e);
-    const uint32_t base = cnt[j * kFinWaves + wave];
+    const uint32_t base = __builtin_amdgcn_readlane(mybase, j);
+    const bool g = above(key[j]);
+    const uint64_t gm = __ballot(g);
     const uint32_t gb = (base & 0xffffu) + rank_in_wave(gm);
-    const uint32_t eb = (base >> 16) + rank_in_wave(em);
     const int i = j * kFinNT + tid;
-    if (g) out[gb + min(eb, need_eq)] = i;
-    else if (e && eb < need_eq) out[gb + eb] = i;
+    if (wave_tied) {
+      const bool e = tied(key[j]);
+      const uint64_t em = __ballot(e);
+      const uint32_t eb = (base >> 16) + rank_in_wave(em);
+      if (g) out[gb + min(eb, need_eq)] = i;
+      else if (e && eb < need_eq) out[gb + eb] = i;
+    } else if (g) {
+      out[gb + min(base >> 16, need_eq)] = i;  // no tied key in this wave: every earlier tie is before
+    }
   }
   for (int p = (int)keep + tid; p < k; p += kFinNT) out[p] = -1;
 }
