@@ -15,8 +15,8 @@
 //     2^8) feeds the probabilities, each split into a bf16 high part and a bf16 residual, to
 //     O^T += V^T P^T; the V^T operand comes from the same tile through gfx950's
 //     transposing LDS reads;
-//   * workgroups that walk several tiles load the next tile's rows while the current one
-//     is multiplied;
+//   * a split of one or two tiles gathers all its rows in one round trip; a workgroup that
+//     walks more tiles loads the next tile's rows while the current one is multiplied;
 //   * with several splits per row each workgroup writes a normalised partial (o, lse) and
 //     a merge kernel combines them with log-sum-exp weights.
 #include "device_common.h"

@@ -163,8 +163,9 @@ int csl_topk_select(const float* scores, int64_t ld, const int64_t* ent_off, con
  *   out fp32 [B, T, H, D]; lse fp32 [B, T, H] (nullable)
  *   D == 128; H a multiple of 16, <= 128; k >= 0; n_win >= 0.
  *   ws: at least csl_attn_workspace_bytes(B, T, H, D, k + n_win) bytes (contents free).
- * Arithmetic: bf16 MFMA operands (probabilities rounded to bf16 for the value product),
- * fp32 accumulation, fp32 online softmax in base 2, log-sum-exp merge of split partials.
+ * Arithmetic: bf16 MFMA operands with fp32 accumulation; each probability enters the value
+ * product as two bf16 terms (hi + bf16(p - hi)), so it carries ~2^-16 relative error; fp32
+ * online softmax in base 2; log-sum-exp merge of split partials.
  */
 size_t csl_attn_workspace_bytes(int B, int T, int H, int D, int64_t max_keys);
 int csl_sparse_attn_decode(const void* q, const void* ckv, const int32_t* idx, int k,
