@@ -40,6 +40,8 @@ def _offsets(lengths, m):
     (16, 256, [999], True),
     (4, 128, [513, 64], False),
     (128, 512, [1024], True),
+    (128, 64, [20000, 300], True),    # D = 64, m = 128: rows split over 2 waves (few entries)
+    (256, 128, [10000], True),        # m = 256: rows split over 4 waves, two loads rounds
 ])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_compress_matches_oracle(csl, m, D, lengths, has_z, out_dtype):
@@ -221,6 +223,7 @@ def _attn_inputs(lengths, m, H, T, q_pos, seed):
     (16, 1, [4096], [4096], 32, 16, 1.0),         # one tile per row: the single-tile kernel
     (48, 2, [300, 50], [300, 50], 40, 24, 0.8),   # 3 head groups, at most one tile
     (80, 300, [5000], [4000], 64, 64, 1.0),       # 300 rows: one split per row, no merge
+    (32, 300, [6000], [5000], 256, 128, 0.9),     # 2 splits of 3 tiles: the prefetching tile loop + merge
 ])
 def test_sparse_attention_matches_oracle(csl, H, T, lengths, q_pos, k, n_win, fill):
     print(f"sparse attn H={H} T={T} lengths={lengths} k={k} n_win={n_win} fill={fill}", flush=True)
@@ -270,6 +273,7 @@ def test_sparse_attention_ignores_out_of_range_ids_and_empty_sets(csl):
     (64, 1, [127, 128, 129], [127, 128, 129], 128, 128),
     (32, 2, [5000], [5000], 4, 0),
     (96, 1, [2000, 700], [2000, 700], 128, 32),   # at most 47 keys: the single-tile kernel, 6 head groups
+    (16, 300, [40000], [39000], 128, 128),        # 2 splits of 4 tiles: the prefetching tile loop, dense
 ])
 def test_hca_attention_matches_oracle(csl, H, T, lengths, q_pos, m, n_win):
     print(f"hca attn H={H} T={T} lengths={lengths} m={m} n_win={n_win}", flush=True)
