@@ -132,6 +132,40 @@ def compress(kv, z, m: int, entries=None) -> np.ndarray:
     return out.reshape(len(ids), D)
 
 
+def compress_overlap(kv_a, z_a, kv_b, z_b, m: int, entries=None) -> np.ndarray:
+    """Compressed entries of one CSA sequence from two overlapping series a and b.
+
+    Entry i pools 2m rows under one softmax per dimension: rows [m*i, m*i + m) of series a
+    and rows [m*(i-1), m*i) of series b, the block before it ([P2] 'Deep Dive', CSA
+    dual-series KV compression; [P1] section 4.3, overlap compression: the b block is
+    shared with the neighbouring entry). Entry 0 has no preceding block; its softmax runs
+    over its m series-a rows alone (reading: the b range is empty there). With z_a and
+    z_b both None the weights are uniform over the rows pooled. Both series have the same
+    row count N; entries i < floor(N/m) exist, so the last b block is never pooled.
+    """
+    kv_a = np.asarray(kv_a, dtype=np.float64)
+    kv_b = np.asarray(kv_b, dtype=np.float64)
+    assert kv_a.shape == kv_b.shape
+    assert (z_a is None) == (z_b is None)
+    n_ent = kv_a.shape[0] // m
+    ids = np.arange(n_ent) if entries is None else np.asarray(entries, dtype=np.int64)
+    has_b = ids > 0                                            # [E]
+    rows_a = ids[:, None] * m + np.arange(m)[None, :]          # [E, m]
+    rows_b = np.where(has_b[:, None], rows_a - m, 0)           # [E, m]; a dummy row when absent
+    x = np.concatenate([kv_a[rows_a], kv_b[rows_b]], axis=1)   # [E, 2m, D]
+    if z_a is None:
+        logits = np.zeros(x.shape)
+    else:
+        logits = np.concatenate([np.asarray(z_a, dtype=np.float64)[rows_a],
+                                 np.asarray(z_b, dtype=np.float64)[rows_b]], axis=1)
+    # an absent b block takes no weight
+    logits[:, m:, :] = np.where(has_b[:, None, None], logits[:, m:, :], -np.inf)
+    mu = logits.max(axis=1, keepdims=True)                     # one softmax over all 2m rows
+    e = np.exp(logits - mu)
+    w = e / e.sum(axis=1, keepdims=True)
+    return (w * x).sum(axis=1).reshape(len(ids), kv_a.shape[1])
+
+
 # ----------------------------------------------------------------------------- a2 indexer
 
 def indexer(q_idx, w, keys) -> np.ndarray:

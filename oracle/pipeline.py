@@ -32,6 +32,18 @@ def compress_lane(kv, z, kv_off, m: int) -> np.ndarray:
     return np.concatenate(out, axis=0) if out else np.zeros((0, 0))
 
 
+def compress_overlap_lane(kv_a, z_a, kv_b, z_b, kv_off, m: int) -> np.ndarray:
+    """All dual-series (overlapped) compressed entries of every sequence, packed."""
+    kv_off = [int(x) for x in kv_off]
+    out = []
+    for b in range(len(kv_off) - 1):
+        lo, hi = kv_off[b], kv_off[b + 1]
+        za = None if z_a is None else f64(z_a[lo:hi])
+        zb = None if z_b is None else f64(z_b[lo:hi])
+        out.append(csa.compress_overlap(f64(kv_a[lo:hi]), za, f64(kv_b[lo:hi]), zb, m))
+    return np.concatenate(out, axis=0) if out else np.zeros((0, 0))
+
+
 def index_keys_f64(kI, k_scale=None, scale_off=None, ent_off=None, group: int = 64) -> np.ndarray:
     """Indexer keys as fp64; fp8 codes are decoded and multiplied by their group's scale."""
     if k_scale is None:

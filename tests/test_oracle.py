@@ -114,6 +114,128 @@ def test_compress_within_chunk_permutation_and_bounds():
     np.testing.assert_array_equal(sub, base[[3, 17, 0]])
 
 
+# ------------------------------------------------------------------- overlapped compression
+
+def _two_series(seed, m, E, D, tail=0, zscale=1.0):
+    r = _rng(seed)
+    N = m * E + tail
+    return (r.standard_normal((N, D)), r.standard_normal((N, D)) * zscale,
+            r.standard_normal((N, D)), r.standard_normal((N, D)) * zscale)
+
+
+def test_overlap_p3_chunk_beside_a_constant_block():
+    """[P3] section 3 toy chunk as the series-a block of entry 1, beside a series-b block of
+    four equal rows V. With z_a = ln(S/2) and z_b = ln(1/8) every column of the joint
+    weights sums to one, so the joint softmax reproduces S/2 and 1/8 exactly and the entry
+    is the midpoint of the page's result and V. Dropping either series, or normalising
+    the two blocks separately, misses it."""
+    C, S, expected = _load_p3()
+    V = np.array([2.0, 4.0, 6.0])
+    kv_a = np.concatenate([np.zeros((4, 3)), C])
+    z_a = np.concatenate([np.zeros((4, 3)), np.log(S / 2)])
+    kv_b = np.concatenate([np.tile(V, (4, 1)), np.zeros((4, 3))])
+    z_b = np.concatenate([np.full((4, 3), np.log(1 / 8)), np.zeros((4, 3))])
+    got = csa.compress_overlap(kv_a, z_a, kv_b, z_b, 4)
+    np.testing.assert_allclose(got[1], (expected + V) / 2, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(got[1], [1.35, 2.3, 3.3], rtol=0, atol=1e-14)
+
+
+def test_overlap_entry0_pools_series_a_only():
+    """Entry 0 has no earlier block: it equals single-series compression of its a rows,
+    whatever series b holds."""
+    kv_a, z_a, kv_b, z_b = _two_series(10, 4, 6, 8)
+    got = csa.compress_overlap(kv_a, z_a, kv_b, z_b, 4)
+    np.testing.assert_allclose(got[0], csa.compress(kv_a, z_a, 4)[0], rtol=1e-14, atol=1e-14)
+    got2 = csa.compress_overlap(kv_a, z_a, kv_b * 5 + 1, z_b - 3, 4)
+    np.testing.assert_array_equal(got2[0], got[0])
+
+
+def test_overlap_series_b_absent_reduces_to_single_series():
+    """Logits of -inf on series b remove it: every entry is single-series compression of a."""
+    kv_a, z_a, kv_b, _ = _two_series(11, 4, 9, 5, tail=3)
+    got = csa.compress_overlap(kv_a, z_a, kv_b, np.full(kv_b.shape, -np.inf), 4)
+    np.testing.assert_allclose(got, csa.compress(kv_a, z_a, 4), rtol=1e-14, atol=1e-14)
+
+
+def test_overlap_block_reach():
+    """Series-a block j feeds entry j only; series-b block j feeds entry j+1 only, and the
+    last b block feeds nothing ([P2] 'Deep Dive': C^b covers [m(i-1), mi-1] for entry i)."""
+    m, E, D = 4, 7, 3
+    kv_a, z_a, kv_b, z_b = _two_series(12, m, E, D)
+    base = csa.compress_overlap(kv_a, z_a, kv_b, z_b, m)
+    for j in range(E):
+        for which in ("a", "b"):
+            ka, kb = kv_a.copy(), kv_b.copy()
+            (ka if which == "a" else kb)[j * m:(j + 1) * m] += 10.0
+            got = csa.compress_overlap(ka, z_a, kb, z_b, m)
+            changed = set(np.nonzero(np.abs(got - base).max(axis=1) > 1e-9)[0].tolist())
+            want = {j} if which == "a" else ({j + 1} if j + 1 < E else set())
+            assert changed == want, (which, j, changed)
+
+
+def test_overlap_uniform_weights_give_mean():
+    """No logits (or equal logits): entry i > 0 is the mean of its 2m rows, entry 0 the
+    mean of its m series-a rows."""
+    m, E, D = 4, 6, 5
+    kv_a, _, kv_b, _ = _two_series(13, m, E, D, tail=2)
+    ref = np.empty((E, D))
+    ref[0] = kv_a[:m].mean(axis=0)
+    for i in range(1, E):
+        ref[i] = np.concatenate([kv_a[i * m:(i + 1) * m], kv_b[(i - 1) * m:i * m]]).mean(axis=0)
+    np.testing.assert_allclose(csa.compress_overlap(kv_a, None, kv_b, None, m), ref, rtol=1e-14, atol=1e-14)
+    zc = np.full(kv_a.shape, 0.37)
+    np.testing.assert_allclose(csa.compress_overlap(kv_a, zc, kv_b, zc, m), ref, rtol=1e-13, atol=1e-14)
+
+
+def test_overlap_brute_force_tiny():
+    """Pure-Python joint softmax over the 2m (or m) rows of each entry."""
+    for m in (1, 2, 3, 4, 5):
+        E, D = 5, 3
+        kv_a, z_a, kv_b, z_b = _two_series(14 + m, m, E, D, tail=m - 1, zscale=3.0)
+        got = csa.compress_overlap(kv_a, z_a, kv_b, z_b, m)
+        assert got.shape == (E, D)
+        for i in range(E):
+            for d in range(D):
+                pool = [(z_a[i * m + j, d], kv_a[i * m + j, d]) for j in range(m)]
+                if i > 0:
+                    pool += [(z_b[(i - 1) * m + j, d], kv_b[(i - 1) * m + j, d]) for j in range(m)]
+                den = sum(math.exp(zz) for zz, _ in pool)
+                ref = sum(math.exp(zz) / den * v for zz, v in pool)
+                assert abs(got[i, d] - ref) < 1e-12
+
+
+def test_overlap_is_single_series_over_spliced_chunks():
+    """Splicing each entry's b block and a block into one 2m-row chunk of a new sequence
+    turns the dual series into single-series compression with ratio 2m; the bounds of a
+    convex combination hold too."""
+    m, E, D = 4, 8, 6
+    kv_a, z_a, kv_b, z_b = _two_series(20, m, E, D)
+    got = csa.compress_overlap(kv_a, z_a, kv_b, z_b, m)
+    kv_s = np.concatenate([np.concatenate([kv_b[(i - 1) * m:i * m], kv_a[i * m:(i + 1) * m]]) for i in range(1, E)])
+    z_s = np.concatenate([np.concatenate([z_b[(i - 1) * m:i * m], z_a[i * m:(i + 1) * m]]) for i in range(1, E)])
+    np.testing.assert_allclose(got[1:], csa.compress(kv_s, z_s, 2 * m), rtol=1e-13, atol=1e-14)
+    lo = kv_s.reshape(E - 1, 2 * m, D).min(axis=1)
+    hi = kv_s.reshape(E - 1, 2 * m, D).max(axis=1)
+    assert np.all(got[1:] >= lo - 1e-12) and np.all(got[1:] <= hi + 1e-12)
+    sub = csa.compress_overlap(kv_a, z_a, kv_b, z_b, m, entries=[5, 0, 2])
+    np.testing.assert_array_equal(sub, got[[5, 0, 2]])
+
+
+def test_overlap_lane_is_per_sequence():
+    """The packed driver restarts the block count at every sequence: each sequence's entry 0
+    sees no b rows of the sequence before it."""
+    r = _rng(21)
+    lens = [9, 3, 17, 8]
+    off = np.concatenate([[0], np.cumsum(lens)])
+    N = off[-1]
+    kv_a, z_a, kv_b, z_b = (r.standard_normal((N, 4)) for _ in range(4))
+    got = pipeline.compress_overlap_lane(kv_a, z_a, kv_b, z_b, off, 4)
+    ref = np.concatenate([csa.compress_overlap(kv_a[lo:hi], z_a[lo:hi], kv_b[lo:hi], z_b[lo:hi], 4)
+                          for lo, hi in zip(off[:-1], off[1:])])
+    assert got.shape == (sum(n // 4 for n in lens), 4)
+    np.testing.assert_array_equal(got, ref)
+
+
 # ------------------------------------------------------------------------------ fp8 / bf16
 
 def test_e4m3_decode_matches_torch_for_all_codes():
