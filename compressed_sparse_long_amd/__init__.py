@@ -13,7 +13,7 @@ import os
 import torch
 
 __all__ = [
-    "compress_kv", "indexer_scores", "topk_select", "sparse_attn_decode", "hca_attn_decode", "csa_decode_step",
+    "compress_kv", "compress_kv_overlap", "indexer_scores", "topk_select", "sparse_attn_decode", "hca_attn_decode", "csa_decode_step",
     "topk_workspace_bytes", "attn_workspace_bytes", "version", "LIB_PATH", "EXPORTS",
     "CslError",
 ]
@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsl.so")
 
 BF16, F32, FP8_E4M3 = 0, 1, 2
 EXPORTS = [
-    "csl_last_error", "csl_version", "csl_compress_kv", "csl_indexer_scores",
+    "csl_last_error", "csl_version", "csl_compress_kv", "csl_compress_kv_overlap", "csl_indexer_scores",
     "csl_topk_workspace_bytes", "csl_topk_select", "csl_attn_workspace_bytes",
     "csl_sparse_attn_decode", "csl_hca_attn_decode", "csl_csa_decode_step",
 ]
@@ -53,13 +53,14 @@ class CslError(RuntimeError):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m compressed_sparse_long_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python compressed_sparse_long_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P, I, L, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     sig = {
         "csl_last_error": (ctypes.c_char_p, []),
         "csl_version": (I, []),
         "csl_compress_kv": (I, [P, P, P, P, P, I, I, I, L, P, I, P]),
+        "csl_compress_kv_overlap": (I, [P, P, P, P, P, P, P, I, I, I, L, P, I, P]),
         "csl_indexer_scores": (I, [P, P, P, I, P, P, I, P, P, I, I, I, I, I, L, P, L, P, S, I, P]),
         "csl_topk_workspace_bytes": (S, [I, I, L, I]),
         "csl_topk_select": (I, [P, L, P, P, I, I, I, I, L, P, P, S, I, P]),
@@ -126,6 +127,26 @@ def compress_kv(kv, z, kv_off, ent_off, m: int, out, first_entry=None, max_new_e
         _ptr(kv, "kv", _BF16), _ptr(z, "z", _BF16), _ptr(kv_off, "kv_off", _I64), _ptr(ent_off, "ent_off", _I64),
         _ptr(first_entry, "first_entry", _I64), B, D, int(m), int(max_new_entries), _ptr(out, "out"), dt,
         _stream(stream)))
+    return out
+
+
+def compress_kv_overlap(kv_a, z_a, kv_b, z_b, kv_off, ent_off, m: int, out, first_entry=None,
+                        max_new_entries: int | None = None, stream=None):
+    """CSA's overlapped compression: entry i pools series-a rows [m*i, m*i + m) with series-b
+    rows [m*(i-1), m*i) under one softmax per dimension, into out (fp32 or bf16 [*, D]); see csl.h."""
+    B = kv_off.numel() - 1
+    D = kv_a.shape[-1]
+    dt = {torch.float32: F32, torch.bfloat16: BF16}.get(out.dtype)
+    if dt is None:
+        raise ValueError("out must be float32 or bfloat16")
+    if kv_b.shape != kv_a.shape:
+        raise ValueError("kv_a and kv_b must have the same shape")
+    if max_new_entries is None:
+        max_new_entries = out.shape[0]
+    _check(_lib.csl_compress_kv_overlap(
+        _ptr(kv_a, "kv_a", _BF16), _ptr(z_a, "z_a", _BF16), _ptr(kv_b, "kv_b", _BF16), _ptr(z_b, "z_b", _BF16),
+        _ptr(kv_off, "kv_off", _I64), _ptr(ent_off, "ent_off", _I64), _ptr(first_entry, "first_entry", _I64),
+        B, D, int(m), int(max_new_entries), _ptr(out, "out"), dt, _stream(stream)))
     return out
 
 

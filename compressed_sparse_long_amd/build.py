@@ -1,6 +1,9 @@
 """Build libcsl.so (HIP kernels for gfx950 + the C ABI) in-tree with hipcc.
 
-    python -m compressed_sparse_long_amd.build        # or build() from Python
+    python compressed_sparse_long_amd/build.py        # or __graft_entry__.build()
+
+(Run it as a script: ``python -m compressed_sparse_long_amd.build`` would import the package,
+which loads the library this rebuilds.)
 
 Each translation unit is compiled separately (in parallel) and linked into one shared
 library next to this file. The build always recompiles; it never runs anything on a GPU.

@@ -55,17 +55,17 @@ namespace {
 // Validation halves of the entry points: CSL_OK when the arguments are good (the launch may
 // still have nothing to do), an error status (with the message set) otherwise.
 int check_compress(const void* kv, const void* z, const int64_t* kv_off, const int64_t* ent_off, int B, int D, int m,
-                   int64_t max_new_entries, const void* out, int out_dtype) {
-  if (B < 0 || max_new_entries < 0) return fail(CSL_ERR_INVALID, "compress_kv: negative B or max_new_entries");
-  if (!kv || !kv_off || !ent_off || !out) return fail(CSL_ERR_INVALID, "compress_kv: null pointer argument");
-  if (m < 1 || m > 65536) return fail(CSL_ERR_INVALID, "compress_kv: m must be in [1, 65536], got %d", m);
+                   int64_t max_new_entries, const void* out, int out_dtype, const char* who = "compress_kv") {
+  if (B < 0 || max_new_entries < 0) return fail(CSL_ERR_INVALID, "%s: negative B or max_new_entries", who);
+  if (!kv || !kv_off || !ent_off || !out) return fail(CSL_ERR_INVALID, "%s: null pointer argument", who);
+  if (m < 1 || m > 65536) return fail(CSL_ERR_INVALID, "%s: m must be in [1, 65536], got %d", who, m);
   if (D != 64 && D != 128 && D != 256 && D != 512)
-    return fail(CSL_ERR_UNSUPPORTED, "compress_kv: D must be 64, 128, 256 or 512, got %d", D);
+    return fail(CSL_ERR_UNSUPPORTED, "%s: D must be 64, 128, 256 or 512, got %d", who, D);
   if (out_dtype != CSL_DTYPE_F32 && out_dtype != CSL_DTYPE_BF16)
-    return fail(CSL_ERR_UNSUPPORTED, "compress_kv: out_dtype must be F32 or BF16");
-  if (B > kMaxGridY) return fail(CSL_ERR_UNSUPPORTED, "compress_kv: B must be <= %d", kMaxGridY);
+    return fail(CSL_ERR_UNSUPPORTED, "%s: out_dtype must be F32 or BF16", who);
+  if (B > kMaxGridY) return fail(CSL_ERR_UNSUPPORTED, "%s: B must be <= %d", who, kMaxGridY);
   if (!aligned(kv, 16) || (z && !aligned(z, 16)) || !aligned(out, 16))
-    return fail(CSL_ERR_INVALID, "compress_kv: kv, z and out must be 16-byte aligned");
+    return fail(CSL_ERR_INVALID, "%s: kv, z and out must be 16-byte aligned", who);
   return CSL_OK;
 }
 
@@ -139,6 +139,23 @@ int csl_compress_kv(const void* kv, const void* z, const int64_t* kv_off, const 
   return hip_status(csl::launch_compress(kv, z, kv_off, ent_off, first_entry, B, D, m, max_new_entries, out,
                                          out_dtype == CSL_DTYPE_BF16, as_stream(stream)),
                     "compress_kv launch");
+}
+
+int csl_compress_kv_overlap(const void* kv_a, const void* z_a, const void* kv_b, const void* z_b,
+                            const int64_t* kv_off, const int64_t* ent_off, const int64_t* first_entry, int B, int D,
+                            int m, int64_t max_new_entries, void* out, int out_dtype, void* stream) {
+  int st = check_compress(kv_a, z_a, kv_off, ent_off, B, D, m, max_new_entries, out, out_dtype, "compress_kv_overlap");
+  if (st != CSL_OK) return st;
+  if (!kv_b) return fail(CSL_ERR_INVALID, "compress_kv_overlap: null kv_b");
+  if ((z_a == nullptr) != (z_b == nullptr))
+    return fail(CSL_ERR_INVALID, "compress_kv_overlap: z_a and z_b must both be given or both be NULL");
+  if (!aligned(kv_b, 16) || (z_b && !aligned(z_b, 16)))
+    return fail(CSL_ERR_INVALID, "compress_kv_overlap: kv_b and z_b must be 16-byte aligned");
+  if (B == 0 || max_new_entries == 0) return ok();
+  return hip_status(csl::launch_compress_overlap(kv_a, z_a, kv_b, z_b, kv_off, ent_off, first_entry, B, D, m,
+                                                 max_new_entries, out, out_dtype == CSL_DTYPE_BF16,
+                                                 as_stream(stream)),
+                    "compress_kv_overlap launch");
 }
 
 int csl_indexer_scores(const void* q_idx, const float* w, const void* k_idx, int k_dtype, const float* k_scale,

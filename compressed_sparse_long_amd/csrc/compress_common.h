@@ -6,13 +6,19 @@
 // logits z[:, d] applied to kv[:, d] ([P3] section 3: per-dimension weights of the chunk
 // tokens; [P2] "Deep Dive", CSA step 2 and HCA "How it works").
 //
+// With DUAL (CSA's overlapped compression, [P2] "Deep Dive", dual-series KV compression;
+// [P1] section 4.3) entry i pools 2m rows under one softmax per dimension: rows
+// [m*i, m*i + m) of series a (kv, z) and rows [m*(i-1), m*i) of series b (kv_b, z_b), the
+// block before it. Entry 0 has no earlier block and pools its m series-a rows alone. The
+// 2m rows are one virtual chunk, series a first, split over the lanes like a plain chunk.
+//
 // Layout: a thread owns 8 consecutive dimensions (16 bytes of bf16) of one entry and a
 // strided subset of its rows; TPE = D/8 threads cover one row, RS row-splits of the same
 // entry sit TPE lanes apart inside a wave and merge their partial softmax states with
 // xor-shuffles, and for long chunks RSX waves split the rows further and merge through LDS
 // (an m = 128 entry then loads in one round trip). Loads are 16-byte, row-contiguous across
 // the TPE lanes, so a wave reads whole 256-byte rows. It reads 2*m*D*2 bytes and writes D*4
-// (fp32) or D*2 (bf16) bytes per entry.
+// (fp32) or D*2 (bf16) bytes per entry (twice the reads with DUAL).
 #pragma once
 
 #include "device_common.h"
@@ -23,12 +29,12 @@ namespace csl {
 // blk * that .. of sequence b (entries past max_new or past the sequence end are skipped).
 // Each thread loads ROWS of its rows at a time. With RSX > 1 every thread of the workgroup
 // must call this (it holds a workgroup barrier).
-template <int NT, int TPE, int RS, bool HAS_Z, bool OUT_BF16, int ROWS = 4, int RSX = 1>
+template <int NT, int TPE, int RS, bool HAS_Z, bool OUT_BF16, int ROWS = 4, int RSX = 1, bool DUAL = false>
 __device__ __forceinline__ void compress_block(
     const uint16_t* __restrict__ kv, const uint16_t* __restrict__ z,
     const int64_t* __restrict__ kv_off, const int64_t* __restrict__ ent_off,
     const int64_t* __restrict__ first_entry, int D, int m, int64_t max_new, void* __restrict__ out, int b,
-    int64_t blk) {
+    int64_t blk, const uint16_t* __restrict__ kv_b = nullptr, const uint16_t* __restrict__ z_b = nullptr) {
   static_assert(TPE * RS <= kWave, "in-wave row-splits merge by shuffles");
   static_assert(RSX == 1 || TPE * RS == kWave, "cross-wave splits take whole waves");
   constexpr int EPB = NT / (TPE * RS * RSX);  // entries per block
@@ -59,19 +65,22 @@ __device__ __forceinline__ void compress_block(
 
   if (valid) {
     const int64_t base_row = row0 + i * (int64_t)m;
-    const uint16_t* kvp = kv + base_row * D + dg * 8;
-    const uint16_t* zp = HAS_Z ? (z + base_row * D + dg * 8) : nullptr;
-    // rows handled by this lane: r = rs + NSPLIT * j
-    const int my_rows = (m > rs) ? (m - rs + NSPLIT - 1) / NSPLIT : 0;
+    // virtual chunk rows v < m are series-a rows base_row + v; with DUAL, rows m <= v < 2m
+    // are series-b rows base_row + v - 2m (absent for entry 0)
+    const int nv = (DUAL && i > 0) ? 2 * m : m;
+    // rows handled by this lane: v = rs + NSPLIT * j
+    const int my_rows = (nv > rs) ? (nv - rs + NSPLIT - 1) / NSPLIT : 0;
     for (int j0 = 0; j0 < my_rows; j0 += ROWS) {
       u32x4 kr[ROWS], zr[ROWS];
       const int cnt = min(ROWS, my_rows - j0);
 #pragma unroll
       for (int u = 0; u < ROWS; ++u) {
         if (u < cnt) {
-          const int64_t r = rs + (int64_t)NSPLIT * (j0 + u);
-          kr[u] = *reinterpret_cast<const u32x4*>(kvp + r * D);
-          if (HAS_Z) zr[u] = *reinterpret_cast<const u32x4*>(zp + r * D);
+          const int v = rs + NSPLIT * (j0 + u);
+          const bool in_b = DUAL && v >= m;
+          const int64_t e = (base_row + v - (in_b ? 2 * m : 0)) * D + dg * 8;
+          kr[u] = *reinterpret_cast<const u32x4*>((in_b ? kv_b : kv) + e);
+          if (HAS_Z) zr[u] = *reinterpret_cast<const u32x4*>((in_b ? z_b : z) + e);
         }
       }
       if (HAS_Z) {

@@ -11,6 +11,12 @@ namespace csl {
 hipError_t launch_compress(const void* kv, const void* z, const int64_t* kv_off, const int64_t* ent_off,
                            const int64_t* first_entry, int B, int D, int m, int64_t max_new_entries,
                            void* out, bool out_bf16, hipStream_t stream);
+// CSA's overlapped compression: entry i pools series-a rows [m*i, m*i + m) with series-b rows
+// [m*(i-1), m*i) under one softmax per dimension (entry 0: series a alone)
+hipError_t launch_compress_overlap(const void* kv_a, const void* z_a, const void* kv_b, const void* z_b,
+                                   const int64_t* kv_off, const int64_t* ent_off, const int64_t* first_entry,
+                                   int B, int D, int m, int64_t max_new_entries, void* out, bool out_bf16,
+                                   hipStream_t stream);
 
 // Newest-chunk compression (bf16 out, D = 128, m <= 8) that the decode indexer can run in
 // spare workgroups of its own launch.

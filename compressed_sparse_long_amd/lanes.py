@@ -15,7 +15,7 @@ import math
 
 import torch
 
-from . import (attn_workspace_bytes, compress_kv, csa_decode_step, hca_attn_decode, indexer_scores, sparse_attn_decode,
+from . import (attn_workspace_bytes, compress_kv, compress_kv_overlap, csa_decode_step, hca_attn_decode, indexer_scores, sparse_attn_decode,
                topk_select, topk_workspace_bytes)
 
 
@@ -65,8 +65,11 @@ class _Lane:
 
 
 class CsaLane(_Lane):
-    def __init__(self, lane, kv, z, q, li, device="cuda", fused: bool = True):
+    def __init__(self, lane, kv, z, q, li, device="cuda", fused: bool = True, kv_b=None, z_b=None):
         super().__init__(lane, kv, z, q, li.kv_off, li.ent_off, li.q_pos, device)
+        # overlapped compression ([P2] "Deep Dive", dual-series KV compression): series b
+        # rows kv_b / z_b, shaped like kv / z; None keeps single-series compression
+        self.kv_b, self.z_b = kv_b, z_b
         self.k = lane.k
         self.fused = fused  # the indexer leaves top-k candidate lists for the selection
         self.qI = li.qI.to(device)
@@ -82,6 +85,21 @@ class CsaLane(_Lane):
         na = attn_workspace_bytes(self.B, self.T, self.H, lane.D, self.k + self.W)
         self.attn_ws = torch.empty(max(na, 16), dtype=torch.uint8, device=device)
         self.kI_copies = [self.kI]
+
+    def compress_all(self):
+        if self.kv_b is None:
+            return super().compress_all()
+        for c in self.ckv_copies:
+            compress_kv_overlap(self.kv, self.z, self.kv_b, self.z_b, self.kv_off, self.ent_off, self.m, c,
+                                max_new_entries=self.max_entries)
+
+    def compress_new(self, r: int = 0):
+        if self.kv_b is None:
+            return super().compress_new(r)
+        if self.n_new:
+            compress_kv_overlap(self.kv, self.z, self.kv_b, self.z_b, self.kv_off, self.ent_off, self.m,
+                                self.ckv_copies[r % len(self.ckv_copies)], first_entry=self.first_new,
+                                max_new_entries=self.n_new)
 
     def rotate(self, copies: int):
         super().rotate(copies)
@@ -110,7 +128,12 @@ class CsaLane(_Lane):
             self.select()
             self.attend(r)
             return
-        csa_decode_step(self.kv, self.z, self.kv_off, self.ent_off, self.first_new, self.n_new,
+        n_new = self.n_new
+        if self.kv_b is not None:
+            # the step call compresses one series only: run the overlapped compression first
+            self.compress_new(r)
+            n_new = 0
+        csa_decode_step(self.kv, self.z, self.kv_off, self.ent_off, self.first_new, n_new,
                         self.ckv_copies[r % len(self.ckv_copies)], self.qI, self.w,
                         self.kI_copies[r % len(self.kI_copies)], self.scores,
                         self.topk_ws, self.k, self.idx, self.q, self.W, self.out, self.q_pos,
@@ -138,10 +161,15 @@ def build_lanes(inp, device="cuda"):
     """Upload a ``synth.Inputs`` and wrap each of its lanes."""
     kv = inp.kv.to(device)
     z = None if inp.z is None else inp.z.to(device)
+    # series b (if drawn) switches the CSA lanes to overlapped compression; HCA keeps one series
+    kv_b = None if getattr(inp, "kv_b", None) is None else inp.kv_b.to(device)
+    z_b = None if getattr(inp, "z_b", None) is None else inp.z_b.to(device)
     q_all = inp.q.to(device)
     lanes = []
     for li in inp.lanes:
         q = q_all[li.q_slice].contiguous()
-        cls = CsaLane if li.lane.kind == "csa" else HcaLane
-        lanes.append(cls(li.lane, kv, z, q, li, device))
+        if li.lane.kind == "csa":
+            lanes.append(CsaLane(li.lane, kv, z, q, li, device, kv_b=kv_b, z_b=z_b))
+        else:
+            lanes.append(HcaLane(li.lane, kv, z, q, li, device))
     return lanes

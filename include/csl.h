@@ -91,6 +91,30 @@ int csl_compress_kv(const void* kv, const void* z, const int64_t* kv_off, const 
                     void* out, int out_dtype, void* stream);
 
 /*
+ * compress_kv_overlap -- CSA's overlapped (dual-series) compression ([P2] "Deep Dive", CSA
+ * dual-series KV compression; [P1] section 4.3, overlap compression). Two series a and b of
+ * raw rows, each with its own logits, share the packed layout of compress_kv. Entry i pools
+ * the m series-a rows of its own block and the m series-b rows of the block before it under
+ * one softmax per dimension:
+ *
+ *   out[ent_off[b] + i, d] = sum_{r<m} wa_r[d] * kv_a[R + m*i + r, d]
+ *                          + sum_{r<m} wb_r[d] * kv_b[R + m*(i-1) + r, d]       (R = kv_off[b])
+ *   (wa, wb)[:, d] = softmax over the 2m logits z_a[R + m*i + r, d], z_b[R + m*(i-1) + r, d]
+ *
+ * Entry 0 has no block before it: its softmax runs over its m series-a rows alone. With
+ * z_a and z_b both NULL the weights are uniform over the rows pooled. Entries, first_entry,
+ * max_new_entries, D, m, out and out_dtype are as for compress_kv; series b rows
+ * [m*(E_b-1), N_b) are never read.
+ *
+ *   kv_a, kv_b   bf16 [rows, D], the same rows and offsets; 16-byte aligned
+ *   z_a, z_b     bf16 [rows, D], both given or both NULL (else CSL_ERR_INVALID)
+ * It reads twice the bytes of compress_kv for the same entries.
+ */
+int csl_compress_kv_overlap(const void* kv_a, const void* z_a, const void* kv_b, const void* z_b,
+                            const int64_t* kv_off, const int64_t* ent_off, const int64_t* first_entry, int B, int D,
+                            int m, int64_t max_new_entries, void* out, int out_dtype, void* stream);
+
+/*
  * indexer_scores -- Lightning-indexer scores ([P5], the indexer score formula;
  * [P2] "Deep Dive", CSA Lightning Indexer; [P1] section 4.2):
  *

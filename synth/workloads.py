@@ -6,7 +6,8 @@ That makes the values independent of the number of threads used to draw them, an
 lets a test regenerate one chunk (for example the rows of one compressed entry)
 without drawing the whole array.
 
-Stream ids follow a fixed order: lengths, kv, z, q, qI, kI, w.
+Stream ids follow a fixed order: lengths, kv, z, q, qI, kI, w, then kv_b and z_b (the
+second raw series and its logits of CSA's overlapped compression, drawn only on request).
 Normal draws are float32, scaled by an exact power of two where a variance of 1/64
 is asked for (std 0.125), then rounded to bf16 by torch's round-to-nearest-even cast.
 """
@@ -22,7 +23,7 @@ import torch
 
 CHUNK = 1 << 22  # values per counter-addressed chunk
 
-S_LENGTHS, S_KV, S_Z, S_Q, S_QI, S_KI, S_W = range(7)
+S_LENGTHS, S_KV, S_Z, S_Q, S_QI, S_KI, S_W, S_KV_B, S_Z_B = range(9)
 S_EXTRA = 100  # first stream id for ad-hoc test draws
 
 
@@ -245,6 +246,8 @@ class Inputs:
     z: torch.Tensor | None       # bf16 [rows, D]
     q: torch.Tensor | None       # bf16 [S, T, H, D]
     lanes: list
+    kv_b: torch.Tensor | None = None   # bf16 [rows, D], series b of overlapped compression
+    z_b: torch.Tensor | None = None    # bf16 [rows, D]
 
 
 def _encode_e4m3(x: torch.Tensor, lengths_e: list, group: int):
@@ -269,7 +272,9 @@ def _encode_e4m3(x: torch.Tensor, lengths_e: list, group: int):
 
 
 def generate(wl: Workload | str, parts=("kv", "z", "q", "qI", "kI", "w")) -> Inputs:
-    """Draw the inputs of a workload (CPU tensors). ``parts`` selects which arrays to draw."""
+    """Draw the inputs of a workload (CPU tensors). ``parts`` selects which arrays to draw;
+    "kv_b" and "z_b" (series b of overlapped compression, shaped like kv and z) are drawn
+    only when listed."""
     if isinstance(wl, str):
         wl = WORKLOADS[wl]
     D = wl.lanes[0].D
@@ -314,7 +319,9 @@ def generate(wl: Workload | str, parts=("kv", "z", "q", "qI", "kI", "w")) -> Inp
             ki_off += nk
             w_off += nw
         lanes.append(li)
-    return Inputs(wl, kv, z, q, lanes)
+    kv_b = normal_bf16(wl.seed, S_KV_B, (rows, D)) if "kv_b" in parts else None
+    z_b = normal_bf16(wl.seed, S_Z_B, (rows, D)) if ("z_b" in parts and wl.z_present) else None
+    return Inputs(wl, kv, z, q, lanes, kv_b, z_b)
 
 
 # --------------------------------------------------------------------------------------

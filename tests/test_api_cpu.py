@@ -14,7 +14,12 @@ LIB = os.path.join(ROOT, "compressed_sparse_long_amd", "libcsl.so")
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        from compressed_sparse_long_amd import build as b
+        # build.py by path: importing the package would try to load the missing library
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "_csl_build", os.path.join(ROOT, "compressed_sparse_long_amd", "build.py"))
+        b = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(b)
         b.build()
     return ctypes.CDLL(LIB)
 
@@ -62,6 +67,24 @@ def test_compress_validation(lib):
     assert "aligned" in _err(lib)
     # nothing to do is a success without touching the device
     assert f(FAKE, None, FAKE, FAKE, None, 0, 128, 4, 10, FAKE, 1, None) == 0
+    assert _err(lib) == ""
+
+
+def test_compress_overlap_validation(lib):
+    f = lib.csl_compress_kv_overlap
+    f.argtypes = [P, P, P, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64, P, ctypes.c_int, P]
+    # kv_a, z_a, kv_b, z_b, kv_off, ent_off, first, B, D, m, max_new, out, dtype, stream
+    assert f(FAKE, None, None, None, FAKE, FAKE, None, 1, 128, 4, 10, FAKE, 1, None) == 1
+    assert "kv_b" in _err(lib)
+    assert f(FAKE, FAKE, FAKE, None, FAKE, FAKE, None, 1, 128, 4, 10, FAKE, 1, None) == 1
+    assert "both" in _err(lib)
+    assert f(FAKE, None, FAKE, FAKE, FAKE, FAKE, None, 1, 128, 4, 10, FAKE, 1, None) == 1
+    assert f(FAKE, None, P((1 << 20) + 8), None, FAKE, FAKE, None, 1, 128, 4, 10, FAKE, 1, None) == 1
+    assert "aligned" in _err(lib)
+    assert f(FAKE, None, FAKE, None, FAKE, FAKE, None, 1, 96, 4, 10, FAKE, 1, None) == 2
+    assert _err(lib).startswith("compress_kv_overlap:")
+    assert f(FAKE, None, FAKE, None, FAKE, FAKE, None, 1, 128, 70000, 10, FAKE, 1, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 128, 4, 10, FAKE, 0, None) == 0
     assert _err(lib) == ""
 
 

@@ -81,6 +81,79 @@ def test_compress_newest_chunk_only(csl):
         assert np.isnan(got[int(ent_off[b]):last]).all()
 
 
+# ------------------------------------------------------------------ overlapped compression
+
+def _two_series(seed, rows, D, has_z):
+    kv_a = W.normal_bf16(seed, W.S_EXTRA + 2, (rows, D))
+    kv_b = W.normal_bf16(seed, W.S_EXTRA + 4, (rows, D))
+    if not has_z:
+        return kv_a, None, kv_b, None
+    z_a = W.normal_bf16(seed, W.S_EXTRA + 3, (rows, D), std=2.0)
+    z_b = W.normal_bf16(seed, W.S_EXTRA + 5, (rows, D), std=2.0)
+    return kv_a, z_a, kv_b, z_b
+
+
+@pytest.mark.parametrize("m,D,lengths,has_z", [
+    (4, 128, [4096, 0, 3, 4, 7, 37, 1001], True),   # N < m, N = m (entry 0 only), ragged tails
+    (4, 128, [513, 64], False),
+    (1, 64, [77, 5], True),
+    (3, 64, [1000, 2], True),
+    (16, 256, [999], True),
+    (64, 512, [4096, 100], True),
+    (128, 128, [16384, 127, 300], True),            # few entries: 256 rows over 4 waves
+    (128, 64, [20000, 300], True),
+    (4, 128, [50000, 4099], True),                  # many entries: one wave walks each entry
+])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_compress_overlap_matches_oracle(csl, m, D, lengths, has_z, out_dtype):
+    print(f"compress_overlap m={m} D={D} lengths={lengths} z={has_z} out={out_dtype}", flush=True)
+    kv_a, z_a, kv_b, z_b = _two_series(14, sum(lengths), D, has_z)
+    kv_off, ent_off = _offsets(lengths, m)
+    E = int(ent_off[-1])
+    out = torch.full((E + 1, D), float("nan"), dtype=out_dtype, device="cuda")
+    csl.compress_kv_overlap(dev(kv_a), dev(z_a), dev(kv_b), dev(z_b), dev(kv_off), dev(ent_off), m, out,
+                            max_new_entries=max(1, E))
+    torch.cuda.synchronize()
+    ref = pipeline.compress_overlap_lane(kv_a, z_a, kv_b, z_b, kv_off.tolist(), m)
+    got = f64(out)
+    if E:
+        assert_rows_close(got[:E], ref, bf16=(out_dtype == torch.bfloat16), what="compress_overlap")
+    assert np.isnan(got[E]).all(), "wrote past the last entry"
+
+
+def test_compress_overlap_newest_chunk_only(csl):
+    """first_entry = E_b - 1 recompresses the newest entry of each sequence, pooling its own
+    series-a block with the series-b block before it (a one-entry sequence: series a only)."""
+    m, D = 4, 128
+    lengths = [4096, 1023, 8, 5]
+    kv_a, z_a, kv_b, z_b = _two_series(15, sum(lengths), D, True)
+    kv_off, ent_off = _offsets(lengths, m)
+    E = [n // m for n in lengths]
+    first = torch.tensor([e - 1 for e in E], dtype=torch.int64)
+    out = torch.full((int(ent_off[-1]), D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    csl.compress_kv_overlap(dev(kv_a), dev(z_a), dev(kv_b), dev(z_b), dev(kv_off), dev(ent_off), m, out,
+                            first_entry=dev(first), max_new_entries=1)
+    torch.cuda.synchronize()
+    got = f64(out)
+    ref = pipeline.compress_overlap_lane(kv_a, z_a, kv_b, z_b, kv_off.tolist(), m)
+    for b in range(len(lengths)):
+        last = int(ent_off[b + 1]) - 1
+        assert_rows_close(got[last], ref[last], bf16=True, what=f"newest overlapped entry of seq {b}")
+        assert np.isnan(got[int(ent_off[b]):last]).all(), "wrote an older entry"
+
+
+def test_compress_overlap_argument_errors(csl):
+    """z_a and z_b must come together; kv_b is required; a bad call enqueues nothing."""
+    kv_off, ent_off = _offsets([16], 4)
+    kv = torch.zeros(16, 128, dtype=torch.bfloat16, device="cuda")
+    out = torch.full((4, 128), float("nan"), dtype=torch.float32, device="cuda")
+    with pytest.raises(csl.CslError) as e:
+        csl.compress_kv_overlap(kv, kv, kv, None, dev(kv_off), dev(ent_off), 4, out)
+    assert e.value.status == 1
+    torch.cuda.synchronize()
+    assert torch.isnan(out).all()
+
+
 # ------------------------------------------------------------------------------- indexer
 
 def _index_lane(HI, T, lengths, q_pos, fp8=False, seed=21):

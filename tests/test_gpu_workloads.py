@@ -38,32 +38,51 @@ def _oracle_entries(kv, z, row0, m, ids):
     return csa.compress(kvs, zs, m)
 
 
-def _oracle_attention(q_bt, kv, z, lane, b, p, sel, scale):
+def _oracle_overlap_entries(kv_a, z_a, kv_b, z_b, row0, m, ids):
+    """Oracle overlapped entries ``ids`` of the sequence whose raw rows start at row0: entry i
+    is entry 1 of the two-block sequence made of blocks i-1 and i of both series (entry 0:
+    entry 0 of block 0 alone)."""
+    out = np.zeros((len(ids), kv_a.shape[1]))
+    for j, i in enumerate(np.asarray(ids, dtype=np.int64).tolist()):
+        lo = row0 + m * max(i - 1, 0)
+        hi = row0 + m * (i + 1)
+        loc = [None if t is None else f64(t[lo:hi]) for t in (kv_a, z_a, kv_b, z_b)]
+        out[j] = csa.compress_overlap(*loc, m)[min(i, 1)]
+    return out
+
+
+def _oracle_attention(q_bt, kv, z, lane, b, p, sel, scale, entries_fn=None):
     """Oracle attention of one query row: its selected entries (oracle-compressed, in the bf16
-    cache format) followed by the raw window rows."""
+    cache format) followed by the raw window rows. ``entries_fn(row0, m, ids)`` gives the
+    compressed entries (default: single-series compression of kv, z)."""
     row0 = lane.kv_off()[b]
     n_b = lane.lengths[b]
-    comp = csa.to_bf16_f64(_oracle_entries(kv, z, row0, lane.m, sel))
+    if entries_fn is None:
+        entries_fn = lambda r0, m, ids: _oracle_entries(kv, z, r0, m, ids)
+    comp = csa.to_bf16_f64(entries_fn(row0, lane.m, sel))
     win = list(csa.window_rows(p, n_b, lane.W))
     wrows = f64(kv[row0 + win[0]: row0 + win[-1] + 1]) if win else np.zeros((0, kv.shape[1]))
     X = np.concatenate([comp, wrows], axis=0)
     return csa.attend(f64(q_bt), X, scale)
 
 
-def _check_compressed_sample(cl, kv, z, lane, nsample, seed):
+def _check_compressed_sample(cl, kv, z, lane, nsample, seed, entries_fn=None):
     g = np.random.default_rng(seed)
     ckv = cl.ckv
+    if entries_fn is None:
+        entries_fn = lambda r0, m, ids: _oracle_entries(kv, z, r0, m, ids)
     for b in range(lane.B):
         E = lane.entries[b]
         if E == 0:
             continue
-        ids = np.unique(np.concatenate([[0, E - 1], g.integers(0, E, size=min(nsample, E))]))
-        ref = _oracle_entries(kv, z, lane.kv_off()[b], lane.m, ids)
+        ids = np.unique(np.concatenate([[0, 1, E - 1], g.integers(0, E, size=min(nsample, E))]))
+        ids = ids[ids < E]
+        ref = entries_fn(lane.kv_off()[b], lane.m, ids)
         got = f64(ckv[lane.ent_off()[b] + torch.from_numpy(ids).to(ckv.device)])
         assert_rows_close(got, ref, bf16=True, what=f"compressed entries of seq {b}")
 
 
-def _check_csa_row(cl, inp, li, b, t, keys_f64):
+def _check_csa_row(cl, inp, li, b, t, keys_f64, entries_fn=None):
     lane = li.lane
     p = lane.q_pos[b] + t
     E = lane.entries[b]
@@ -76,7 +95,7 @@ def _check_csa_row(cl, inp, li, b, t, keys_f64):
     same = topk_band_check(got_idx, ref_s, lane.k, what=f"top-k b={b} t={t}")
     ref_sel = csa.topk(ref_s, lane.k)
     ref_sel = ref_sel[ref_sel >= 0]
-    ro, rl = _oracle_attention(inp.q[li.q_slice][b, t], inp.kv, inp.z, lane, b, p, ref_sel, cl.scale)
+    ro, rl = _oracle_attention(inp.q[li.q_slice][b, t], inp.kv, inp.z, lane, b, p, ref_sel, cl.scale, entries_fn)
     go, gl = f64(cl.out[b, t]), f64(cl.lse[b, t])
     if same:
         assert_attn_close(go, ro, f"out b={b} t={t}")
@@ -91,9 +110,10 @@ def _csa_keys(li):
     return pipeline.index_keys_f64(li.kI, li.k_scale, li.scale_off, li.ent_off, li.lane.scale_group)
 
 
-def _run(lanes_mod, name):
-    print(f"workload {name}: generating inputs", flush=True)
-    inp = synth.generate(name)
+def _run(lanes_mod, name, overlap=False):
+    print(f"workload {name}{' (overlapped compression)' if overlap else ''}: generating inputs", flush=True)
+    parts = ("kv", "z", "q", "qI", "kI", "w") + (("kv_b", "z_b") if overlap else ())
+    inp = synth.generate(name, parts=parts)
     print(f"workload {name}: running on the GPU", flush=True)
     cls = lanes_mod.build_lanes(inp)
     for cl in cls:
@@ -107,7 +127,8 @@ def _run(lanes_mod, name):
 def test_csa_decode_4k(lanes_mod):
     inp, (cl,) = _run(lanes_mod, "csa_decode_4k")
     li = inp.lanes[0]
-    ref_ckv = csa.to_bf16_f64(pipeline.compress_lane(inp.kv, inp.z, li.kv_off, 4))
+    # the cache holds one bf16 rounding of each fp32 entry: compare with the unrounded oracle
+    ref_ckv = pipeline.compress_lane(inp.kv, inp.z, li.kv_off, 4)
     assert_rows_close(f64(cl.ckv), ref_ckv, bf16=True, what="ckv")
     _check_csa_row(cl, inp, li, 0, 0, _csa_keys(li))
 
@@ -135,6 +156,31 @@ def test_csa_decode_1m(lanes_mod):
     keys = _csa_keys(li)
     for b in range(li.lane.B):
         _check_csa_row(cl, inp, li, b, 0, keys)
+
+
+def _overlap_fn(inp):
+    return lambda r0, m, ids: _oracle_overlap_entries(inp.kv, inp.z, inp.kv_b, inp.z_b, r0, m, ids)
+
+
+def test_csa_decode_4k_overlapped(lanes_mod):
+    """The small CSA workload with overlapped (dual-series) compression: every compressed
+    entry, then the step's scores, selection and attention over those entries."""
+    inp, (cl,) = _run(lanes_mod, "csa_decode_4k", overlap=True)
+    li = inp.lanes[0]
+    ref_ckv = pipeline.compress_overlap_lane(inp.kv, inp.z, inp.kv_b, inp.z_b, li.kv_off, 4)
+    assert_rows_close(f64(cl.ckv), ref_ckv, bf16=True, what="ckv (overlapped)")
+    _check_csa_row(cl, inp, li, 0, 0, _csa_keys(li), _overlap_fn(inp))
+
+
+def test_csa_decode_1m_overlapped(lanes_mod):
+    """4 x 1M-token CSA decode with overlapped compression, in the launch configuration the
+    benchmark times for it: sampled entries of the bulk pass, then every query row."""
+    inp, (cl,) = _run(lanes_mod, "csa_decode_1m", overlap=True)
+    li = inp.lanes[0]
+    _check_compressed_sample(cl, inp.kv, inp.z, li.lane, 1024, 5, _overlap_fn(inp))
+    keys = _csa_keys(li)
+    for b in range(li.lane.B):
+        _check_csa_row(cl, inp, li, b, 0, keys, _overlap_fn(inp))
 
 
 def test_csa_prefill_8k_on_128k(lanes_mod):
