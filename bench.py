@@ -324,7 +324,13 @@ def main():
         result["compress_overlap_bulk"] = {"us": round(t_ov_bulk, 1), "bytes": ov_bytes,
                                            "GB_s": round(ov_bytes / (t_ov_bulk * 1e-6) / 1e9, 1),
                                            "frac": round(ov_bytes / (t_ov_bulk * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-        del kv_b, z_b, ckv_s
+        # the whole decode step with overlapped compression (carried by the indexer launch),
+        # timed like the headline loop
+        cl.kv_b, cl.z_b = kv_b, z_b
+        g_ov_step = capture(lambda: [cl.step(r) for r in range(R)])
+        result["overlap_step_us"] = round(time_graphs([g_ov_step], max(1, 400 // R), per_replay=R), 2)
+        cl.kv_b = cl.z_b = None
+        del kv_b, z_b, ckv_s, g_ov_step
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)

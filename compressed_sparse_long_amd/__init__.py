@@ -42,6 +42,7 @@ class _CsaStep(ctypes.Structure):
         ("q", _P), ("H", _I), ("D", _I), ("n_win", _I), ("scale", _F), ("out", _P), ("lse", _P), ("attn_ws", _P),
         ("attn_ws_bytes", _S),
         ("q_pos", _P), ("m", _I), ("B", _I), ("T", _I), ("max_entries", _L),
+        ("kv_b", _P), ("z_b", _P),
     ]
 
 
@@ -244,9 +245,10 @@ def _nbytes(t) -> int:
 def csa_decode_step(kv, z, kv_off, ent_off, first_entry, max_new_entries: int, ckv, qI, w, kI, scores, topk_ws,
                     k: int, idx, q, n_win: int, out, q_pos, m: int, lse=None, scale: float | None = None,
                     k_scale=None, scale_off=None, scale_group: int = 64, max_entries: int | None = None,
-                    attn_ws=None, stream=None):
-    """One whole CSA step (compress_kv of the newest entries into ckv, indexer_scores with
-    candidate lists, topk_select, sparse_attn_decode) in one C call; see csl.h."""
+                    attn_ws=None, kv_b=None, z_b=None, stream=None):
+    """One whole CSA step (compress_kv of the newest entries into ckv, or compress_kv_overlap
+    when series b ``kv_b``/``z_b`` is given, indexer_scores with candidate lists, topk_select,
+    sparse_attn_decode) in one C call; see csl.h."""
     B, T, HI, CI = qI.shape
     H, D = q.shape[2], q.shape[3]
     if kI.dtype == torch.bfloat16:
@@ -272,6 +274,7 @@ def csa_decode_step(kv, z, kv_off, ent_off, first_entry, max_new_entries: int, c
         k=int(k), idx=_ptr(idx, "idx", (torch.int32,)),
         q=_ptr(q, "q", _BF16), H=H, D=D, n_win=int(n_win), scale=float(scale), out=_ptr(out, "out", _F32),
         lse=_ptr(lse, "lse", _F32), attn_ws=_ptr(attn_ws, "attn_ws"), attn_ws_bytes=awb,
+        kv_b=_ptr(kv_b, "kv_b", _BF16), z_b=_ptr(z_b, "z_b", _BF16),
         q_pos=_ptr(q_pos, "q_pos", _I64), m=int(m), B=B, T=T, max_entries=int(max_entries))
     _check(_lib.csl_csa_decode_step(ctypes.byref(s), _stream(stream)))
     return out

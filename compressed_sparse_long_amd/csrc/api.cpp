@@ -46,7 +46,7 @@ extern "C" {
 
 const char* csl_last_error(void) { return g_last_error.c_str(); }
 
-int csl_version(void) { return 100; }
+int csl_version(void) { return 200; }
 
 }  // extern "C"
 
@@ -66,6 +66,16 @@ int check_compress(const void* kv, const void* z, const int64_t* kv_off, const i
   if (B > kMaxGridY) return fail(CSL_ERR_UNSUPPORTED, "%s: B must be <= %d", who, kMaxGridY);
   if (!aligned(kv, 16) || (z && !aligned(z, 16)) || !aligned(out, 16))
     return fail(CSL_ERR_INVALID, "%s: kv, z and out must be 16-byte aligned", who);
+  return CSL_OK;
+}
+
+// series b of the overlapped compression: kv_b given, its logits exactly when series a has them
+int check_series_b(const void* kv_b, const void* z_a, const void* z_b, const char* who) {
+  if (!kv_b) return fail(CSL_ERR_INVALID, "%s: null kv_b", who);
+  if ((z_a == nullptr) != (z_b == nullptr))
+    return fail(CSL_ERR_INVALID, "%s: z and z_b must both be given or both be NULL", who);
+  if (!aligned(kv_b, 16) || (z_b && !aligned(z_b, 16)))
+    return fail(CSL_ERR_INVALID, "%s: kv_b and z_b must be 16-byte aligned", who);
   return CSL_OK;
 }
 
@@ -146,11 +156,8 @@ int csl_compress_kv_overlap(const void* kv_a, const void* z_a, const void* kv_b,
                             int m, int64_t max_new_entries, void* out, int out_dtype, void* stream) {
   int st = check_compress(kv_a, z_a, kv_off, ent_off, B, D, m, max_new_entries, out, out_dtype, "compress_kv_overlap");
   if (st != CSL_OK) return st;
-  if (!kv_b) return fail(CSL_ERR_INVALID, "compress_kv_overlap: null kv_b");
-  if ((z_a == nullptr) != (z_b == nullptr))
-    return fail(CSL_ERR_INVALID, "compress_kv_overlap: z_a and z_b must both be given or both be NULL");
-  if (!aligned(kv_b, 16) || (z_b && !aligned(z_b, 16)))
-    return fail(CSL_ERR_INVALID, "compress_kv_overlap: kv_b and z_b must be 16-byte aligned");
+  st = check_series_b(kv_b, z_a, z_b, "compress_kv_overlap");
+  if (st != CSL_OK) return st;
   if (B == 0 || max_new_entries == 0) return ok();
   return hip_status(csl::launch_compress_overlap(kv_a, z_a, kv_b, z_b, kv_off, ent_off, first_entry, B, D, m,
                                                  max_new_entries, out, out_dtype == CSL_DTYPE_BF16,
@@ -249,8 +256,13 @@ int csl_csa_decode_step(const csl_csa_step* s, void* stream) {
   if (!s) return fail(CSL_ERR_INVALID, "csa_decode_step: null argument");
   // every part is validated before anything is enqueued
   int st = check_compress(s->kv, s->z, s->kv_off, s->ent_off, s->B, s->D, s->m, s->max_new_entries, s->ckv,
-                          CSL_DTYPE_BF16);
+                          CSL_DTYPE_BF16, "csa_decode_step");
   if (st != CSL_OK) return st;
+  const bool overlap = s->kv_b != nullptr || s->z_b != nullptr;
+  if (overlap) {
+    st = check_series_b(s->kv_b, s->z, s->z_b, "csa_decode_step");
+    if (st != CSL_OK) return st;
+  }
   void* topk_ws = s->topk_ws;
   st = check_indexer(s->q_idx, s->w, s->k_idx, s->k_dtype, s->k_scale, s->scale_off, s->scale_group, s->ent_off,
                      s->q_pos, s->m, s->B, s->T, s->HI, s->CI, s->max_entries, s->scores, s->ld, topk_ws,
@@ -272,11 +284,15 @@ int csl_csa_decode_step(const csl_csa_step* s, void* stream) {
   hipError_t e = hipSuccess;
   if (compress && index && csl::indexer_carries_compress(topk_ws, s->B, s->T, s->max_entries, s->D, s->m)) {
     // the newest-chunk compression rides in spare workgroups of the indexer launch
-    const csl::CompressJob job{s->kv, s->z, s->kv_off, s->first_entry, s->max_new_entries, s->ckv, s->m};
+    const csl::CompressJob job{s->kv, s->z, s->kv_off, s->first_entry, s->max_new_entries, s->ckv, s->m,
+                               s->kv_b, s->z_b};
     e = csl::launch_indexer(s->q_idx, s->w, s->k_idx, fp8, s->k_scale, s->scale_off, s->scale_group, s->ent_off,
                             s->q_pos, s->m, s->B, s->T, s->HI, s->max_entries, s->scores, s->ld, topk_ws, s->k, hs, &job);
   } else {
-    if (compress)
+    if (compress && overlap)
+      e = csl::launch_compress_overlap(s->kv, s->z, s->kv_b, s->z_b, s->kv_off, s->ent_off, s->first_entry, s->B,
+                                       s->D, s->m, s->max_new_entries, s->ckv, true, hs);
+    else if (compress)
       e = csl::launch_compress(s->kv, s->z, s->kv_off, s->ent_off, s->first_entry, s->B, s->D, s->m,
                                s->max_new_entries, s->ckv, true, hs);
     if (e == hipSuccess && index)

@@ -205,7 +205,8 @@ __device__ __forceinline__ float head_sum(float v) {
 // and query row; with a top-k workspace (T == 1) every thread then holds the key of one entry
 // of the block's 512-entry slice for the candidate lists. Workgroups past the key range
 // (blockIdx.x >= key_blocks, first query tile) run a CompressJob instead: 4 row-splits x 16
-// lanes per entry, one row per thread, so the job adds no registers to the streaming path.
+// lanes per entry, one row per thread (two for the overlapped pair), so the job adds no
+// registers to the streaming path.
 constexpr int kJobRS = 4;
 constexpr int kJobEntriesPerBlock = kSlice / (16 * kJobRS);
 
@@ -230,12 +231,26 @@ __global__ __launch_bounds__(kSlice) void indexer_decode_kernel(
       const uint16_t* k16 = static_cast<const uint16_t*>(job.kv);
       const uint16_t* z16 = static_cast<const uint16_t*>(job.z);
       const int64_t blk = (int64_t)blockIdx.x - key_blocks;
-      if (z16)
+      if (job.kv_b) {
+        // overlapped pair: up to 2m <= 16 rows per entry, one row in flight per thread (the
+        // job hides under the key stream; two would raise the whole kernel's register count)
+        const uint16_t* kb16 = static_cast<const uint16_t*>(job.kv_b);
+        const uint16_t* zb16 = static_cast<const uint16_t*>(job.z_b);
+        if (z16)
+          compress_block<kSlice, 16, kJobRS, true, true, 1, 1, true>(k16, z16, job.kv_off, ent_off, job.first_entry,
+                                                                     128, job.m, job.max_new, job.out, blockIdx.z,
+                                                                     blk, kb16, zb16);
+        else
+          compress_block<kSlice, 16, kJobRS, false, true, 1, 1, true>(k16, z16, job.kv_off, ent_off, job.first_entry,
+                                                                      128, job.m, job.max_new, job.out, blockIdx.z,
+                                                                      blk, kb16, zb16);
+      } else if (z16) {
         compress_block<kSlice, 16, kJobRS, true, true, 1>(k16, z16, job.kv_off, ent_off, job.first_entry, 128, job.m,
                                                        job.max_new, job.out, blockIdx.z, blk);
-      else
+      } else {
         compress_block<kSlice, 16, kJobRS, false, true, 1>(k16, z16, job.kv_off, ent_off, job.first_entry, 128, job.m,
                                                         job.max_new, job.out, blockIdx.z, blk);
+      }
     }
     return;
   }

@@ -18,8 +18,8 @@ hipError_t launch_compress_overlap(const void* kv_a, const void* z_a, const void
                                    int B, int D, int m, int64_t max_new_entries, void* out, bool out_bf16,
                                    hipStream_t stream);
 
-// Newest-chunk compression (bf16 out, D = 128, m <= 8) that the decode indexer can run in
-// spare workgroups of its own launch.
+// Newest-chunk compression (bf16 out, D = 128, m <= 8; one series or the overlapped pair) that
+// the decode indexer can run in spare workgroups of its own launch.
 struct CompressJob {
   const void* kv;
   const void* z;
@@ -28,6 +28,8 @@ struct CompressJob {
   int64_t max_new;
   void* out;
   int m;
+  const void* kv_b = nullptr;  // series b of the overlapped compression, or nullptr (one series)
+  const void* z_b = nullptr;
 };
 
 hipError_t launch_indexer(const void* qI, const float* w, const void* kI, bool fp8, const float* k_scale,

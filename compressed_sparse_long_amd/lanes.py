@@ -128,17 +128,13 @@ class CsaLane(_Lane):
             self.select()
             self.attend(r)
             return
-        n_new = self.n_new
-        if self.kv_b is not None:
-            # the step call compresses one series only: run the overlapped compression first
-            self.compress_new(r)
-            n_new = 0
-        csa_decode_step(self.kv, self.z, self.kv_off, self.ent_off, self.first_new, n_new,
+        csa_decode_step(self.kv, self.z, self.kv_off, self.ent_off, self.first_new, self.n_new,
                         self.ckv_copies[r % len(self.ckv_copies)], self.qI, self.w,
                         self.kI_copies[r % len(self.kI_copies)], self.scores,
                         self.topk_ws, self.k, self.idx, self.q, self.W, self.out, self.q_pos,
                         self.m, lse=self.lse, scale=self.scale, k_scale=self.k_scale, scale_off=self.scale_off,
-                        scale_group=self.scale_group, max_entries=self.max_entries, attn_ws=self.attn_ws)
+                        scale_group=self.scale_group, max_entries=self.max_entries, attn_ws=self.attn_ws,
+                        kv_b=self.kv_b, z_b=self.z_b)
 
 
 class HcaLane(_Lane):

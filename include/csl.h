@@ -65,7 +65,7 @@ typedef enum {
 /* Message for the last failed call on this thread ("" if none). Never NULL. */
 const char* csl_last_error(void);
 
-/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH (0.2.0: overlapped compression). */
 int csl_version(void);
 
 /*
@@ -220,7 +220,9 @@ int csl_hca_attn_decode(const void* q, const void* ckv, const void* kv, const in
  * anything is enqueued. Where the shapes allow (D == 128, m <= 8, the decode tiling of the
  * indexer), the compression runs in spare workgroups of the indexer launch instead of a
  * launch of its own; it never reads what the indexer writes, and the attention runs after
- * both.
+ * both. With kv_b (and z_b when z is given) set, the compression is csl_compress_kv_overlap
+ * of the series pair (kv, z) and (kv_b, z_b) instead, carried the same way; kv_b and z_b
+ * both NULL keeps single-series compression.
  */
 typedef struct csl_csa_step {
   /* raw K = V cache and the compression this step adds to ckv */
@@ -264,6 +266,9 @@ typedef struct csl_csa_step {
   int B;
   int T;
   int64_t max_entries;
+  /* overlapped compression (NULL, NULL: one series) */
+  const void* kv_b;           /* bf16 [N_tot, D] series b, or NULL */
+  const void* z_b;            /* bf16 [N_tot, D] its logits: given exactly when z is */
 } csl_csa_step;
 
 int csl_csa_decode_step(const csl_csa_step* s, void* stream);

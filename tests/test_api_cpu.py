@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, s), s
     import compressed_sparse_long_amd as csl
     assert sorted(csl.EXPORTS) == declared_symbols()
-    assert csl.version() == 100
+    assert csl.version() == 200
 
 
 P = ctypes.c_void_p
@@ -178,5 +178,10 @@ def test_step_validation(lib):
     assert call(k=0) == 2
     assert call(kv=P((1 << 20) + 2)) == 1       # misaligned raw cache
     assert call(m=0) == 1
+    assert call(z_b=FAKE) == 1                  # series-b logits without series b
+    assert "kv_b" in _err(lib)
+    assert call(kv_b=FAKE, z_b=FAKE) == 1       # series-b logits without series-a logits
+    assert "z_b" in _err(lib)
+    assert call(kv_b=P((1 << 20) + 4)) == 1     # misaligned series b
     assert call(B=0) == 0                       # nothing to do: nothing enqueued
     assert _err(lib) == ""

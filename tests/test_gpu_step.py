@@ -13,18 +13,24 @@ from synth import workloads as W
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("lengths,m,has_z,k,HI,fp8,H", [
-    ((600000, 300000, 4000), 4, True, 1024, 8, False, 64),    # long rows: candidate lists, compression in the indexer launch
-    ((4096,), 4, False, 64, 4, False, 16),                    # short row: one-workgroup selection, uniform weights
-    ((200000, 70000, 0), 8, True, 512, 8, True, 32),          # m = 8, fp8 keys, an empty sequence
-    ((100000, 50001), 2, True, 256, 16, False, 64),           # m = 2, 16 indexer heads
-    ((65536,), 16, True, 128, 8, False, 16),                  # m = 16: compression in its own launch
+@pytest.mark.parametrize("lengths,m,has_z,k,HI,fp8,H,overlap", [
+    ((600000, 300000, 4000), 4, True, 1024, 8, False, 64, False),  # long rows: candidate lists, compression in the indexer launch
+    ((4096,), 4, False, 64, 4, False, 16, False),                  # short row: one-workgroup selection, uniform weights
+    ((200000, 70000, 0), 8, True, 512, 8, True, 32, False),        # m = 8, fp8 keys, an empty sequence
+    ((100000, 50001), 2, True, 256, 16, False, 64, False),         # m = 2, 16 indexer heads
+    ((65536,), 16, True, 128, 8, False, 16, False),                # m = 16: compression in its own launch
+    # overlapped compression (series a and b)
+    ((600000, 300000, 4000), 4, True, 1024, 8, False, 64, True),   # carried by the indexer launch
+    ((4, 9000, 7), 4, True, 64, 8, False, 16, True),               # a one-entry sequence: series a only
+    ((4096,), 8, False, 64, 4, False, 16, True),                   # uniform weights over 2m = 16 rows
+    ((65536,), 16, True, 128, 8, False, 16, True),                 # m = 16: its own launch
 ])
-def test_csa_decode_step_matches_separate_calls(lengths, m, has_z, k, HI, fp8, H):
+def test_csa_decode_step_matches_separate_calls(lengths, m, has_z, k, HI, fp8, H, overlap):
     from compressed_sparse_long_amd import lanes
-    print(f"step lengths={lengths} m={m} z={has_z} k={k} HI={HI} fp8={fp8} H={H}", flush=True)
+    print(f"step lengths={lengths} m={m} z={has_z} k={k} HI={HI} fp8={fp8} H={H} overlap={overlap}", flush=True)
     lane = W.Lane("csa", tuple(lengths), tuple(lengths), T=1, H=H, m=m, k=k, HI=HI, kI_fp8=fp8)
-    inp = synth.generate(W.Workload("step", 11 + m, (lane,), z_present=has_z))
+    parts = ("kv", "z", "q", "qI", "kI", "w") + (("kv_b", "z_b") if overlap else ())
+    inp = synth.generate(W.Workload("step", 11 + m, (lane,), z_present=has_z), parts=parts)
     (cl,) = lanes.build_lanes(inp)
     cl.compress_all()
     E = lane.entries
