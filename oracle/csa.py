@@ -15,14 +15,18 @@ Readings where the pages leave a step open (each is listed in the design notes):
   * compression weights: an explicit per-token, per-dimension logit array Z; the softmax
     runs over the m rows of one chunk, separately for every dimension ([P3] section 3,
     whose toy weights sum to one down each dimension). Z absent means uniform weights.
-  * the hot path uses single-series compression for both CSA and HCA.
+  * the hot path uses single-series compression for both CSA and HCA; CSA's overlapped
+    dual series is the alternative compress_overlap, whose entry 0 pools series a alone.
   * one softmax covers the selected compressed entries and the raw window rows together,
-    with no de-duplication between the two lanes and no attention sink.
+    with no de-duplication between the two lanes; the attention sink, when given, is a
+    per-head logit exp(z'_h) added to that softmax's denominator, carrying no value.
+  * partial RoPE, when asked for, rotates the query's and the output's last dims (pairs of
+    adjacent dims, angle pos * base^(-2j/R)); key rows are taken as stored.
   * a query at absolute position p sees compressed entries s < floor(p/m) (never its own
     block, [P1] section 6.1) and the window of the W newest raw rows j <= p that exist.
   * top-k keeps the k largest scores, lower entry id first on ties, and returns the ids
     in ascending order padded with -1.
-  * an empty attention set yields a zero output and lse = -inf.
+  * an empty attention set yields a zero output and lse = -inf (the sink logit, if given).
 """
 from __future__ import annotations
 
@@ -204,31 +208,70 @@ def topk(scores, k: int) -> np.ndarray:
 
 # ----------------------------------------------------------------------------- a4/a5 attention
 
-def attend(q, X, scale: float):
+def attend(q, X, scale: float, sink=None):
     """Shared-KV multi-query attention of H query heads over key=value rows X.
 
     o_h = sum_x softmax_x(scale * q_h . x) * x and lse_h = log sum_x exp(scale * q_h . x).
     [P5] (Attention(Q,K,V) = softmax(Q K^T / sqrt(d_k)) V); [P2] 'Deep Dive', CSA core
     attention: every head reads the same entries, which act as both keys and values.
+
+    ``sink`` (per-head logits z'_h, [H]) adds exp(z'_h) to head h's softmax denominator
+    ([P1] section 7, the attention sink: the weights may then sum to less than one). The
+    sink carries no value, and lse_h = log(exp(z'_h) + sum_x exp(scale * q_h . x)).
     """
     q = np.asarray(q, dtype=np.float64)
     X = np.asarray(X, dtype=np.float64).reshape(-1, q.shape[1])
     H, D = q.shape
+    zs = np.full(H, -np.inf) if sink is None else np.asarray(sink, dtype=np.float64).reshape(H)
     o = np.zeros((H, D))
-    lse = np.full(H, -np.inf)
+    lse = zs.copy()                       # no key: the denominator is the sink alone
     if X.shape[0] == 0:
         return o, lse
     for h in range(H):
         logit = (X @ q[h]) * scale
-        mu = logit.max()
+        mu = max(logit.max(), zs[h])
         e = np.exp(logit - mu)
-        ssum = e.sum()
-        o[h] = (e @ X) / ssum
-        lse[h] = mu + np.log(ssum)
+        den = e.sum() + np.exp(zs[h] - mu)
+        o[h] = (e @ X) / den
+        lse[h] = mu + np.log(den)
     return o, lse
 
 
-def sparse_attn(q, ckv_b, kv_b, idx, p: int, W: int, scale: float):
+def rope(x, pos: float, R: int, base: float) -> np.ndarray:
+    """Rotary position encoding of the last R dimensions of x (any leading shape) at
+    position ``pos``; the other dimensions pass through.
+
+    [P1] section 8 (partial RoPE: only the last 64 dimensions of queries and KV vectors are
+    rotated; the attention output is rotated at the negated query position). The rotation
+    itself is the original RoPE: inside the last R dims, pair j = (x[2j], x[2j+1]) turns by
+    the angle pos * base^(-2j/R), counter-clockwise.
+    """
+    x = np.array(x, dtype=np.float64)
+    if R == 0:
+        return x
+    D = x.shape[-1]
+    j = np.arange(R // 2)
+    ang = float(pos) * np.power(float(base), -2.0 * j / R)
+    c, s_ = np.cos(ang), np.sin(ang)
+    a = x[..., D - R::2].copy()
+    b = x[..., D - R + 1::2].copy()
+    x[..., D - R::2] = a * c - b * s_
+    x[..., D - R + 1::2] = a * s_ + b * c
+    return x
+
+
+def attend_at(q, X, scale: float, p: int, sink=None, rope_dims: int = 0, rope_base: float = 10000.0):
+    """attend() for a query at absolute position p with the per-query extras of the core
+    attention: the query's last rope_dims dims rotated at p before the scores, the output's
+    rotated back at -p ([P1] section 8, inverse RoPE on the output), and the sink. Key rows
+    enter as given (their own rotation, if any, is applied where they are written)."""
+    qr = rope(q, p, rope_dims, rope_base)
+    o, lse = attend(qr, X, scale, sink)
+    return rope(o, -p, rope_dims, rope_base), lse
+
+
+def sparse_attn(q, ckv_b, kv_b, idx, p: int, W: int, scale: float, sink=None, rope_dims: int = 0,
+                rope_base: float = 10000.0):
     """CSA core attention for one query row: the selected compressed entries (ids >= 0)
     plus the raw window rows, under one softmax ([P2] 'Putting It Together': MQA over the
     top-k entries plus 128 sliding-window entries)."""
@@ -238,10 +281,11 @@ def sparse_attn(q, ckv_b, kv_b, idx, p: int, W: int, scale: float):
     assert all(i < ckv_b.shape[0] for i in sel), "selected id beyond the sequence's entries"
     rows = [ckv_b[i] for i in sel] + [kv_b[j] for j in window_rows(p, kv_b.shape[0], W)]
     X = np.array(rows).reshape(len(rows), np.asarray(q).shape[1])
-    return attend(q, X, scale)
+    return attend_at(q, X, scale, p, sink, rope_dims, rope_base)
 
 
-def hca_attn(q, ckv_b, kv_b, p: int, m: int, W: int, scale: float):
+def hca_attn(q, ckv_b, kv_b, p: int, m: int, W: int, scale: float, sink=None, rope_dims: int = 0,
+             rope_base: float = 10000.0):
     """HCA attention for one query row: every visible compressed entry plus the raw window
     rows, under one softmax ([P1] section 5.1; [P2] 'Heavily Compressed Attention')."""
     ckv_b = np.asarray(ckv_b, dtype=np.float64)
@@ -249,4 +293,4 @@ def hca_attn(q, ckv_b, kv_b, p: int, m: int, W: int, scale: float):
     nv = n_visible(p, m, ckv_b.shape[0])
     rows = [ckv_b[s] for s in range(nv)] + [kv_b[j] for j in window_rows(p, kv_b.shape[0], W)]
     X = np.array(rows).reshape(len(rows), np.asarray(q).shape[1])
-    return attend(q, X, scale)
+    return attend_at(q, X, scale, p, sink, rope_dims, rope_base)

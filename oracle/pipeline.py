@@ -90,7 +90,8 @@ def topk_lane(scores, k: int) -> np.ndarray:
     return out
 
 
-def sparse_attn_lane(q, ckv, idx, kv, kv_off, ent_off, q_pos, W: int, scale: float):
+def sparse_attn_lane(q, ckv, idx, kv, kv_off, ent_off, q_pos, W: int, scale: float, sink=None, rope_dims: int = 0,
+                     rope_base: float = 10000.0):
     """CSA attention for every (b, t): o [B, T, H, D], lse [B, T, H]."""
     q = f64(q)
     B, T, H, D = q.shape
@@ -104,11 +105,12 @@ def sparse_attn_lane(q, ckv, idx, kv, kv_off, ent_off, q_pos, W: int, scale: flo
         kv_b = f64(kv[kv_off[b]:kv_off[b + 1]])
         for t in range(T):
             o[b, t], lse[b, t] = csa.sparse_attn(q[b, t], ckv_b, kv_b, idx[b, t],
-                                                 int(q_pos[b]) + t, W, scale)
+                                                 int(q_pos[b]) + t, W, scale, sink, rope_dims, rope_base)
     return o, lse
 
 
-def hca_attn_lane(q, ckv, kv, kv_off, ent_off, q_pos, m: int, W: int, scale: float):
+def hca_attn_lane(q, ckv, kv, kv_off, ent_off, q_pos, m: int, W: int, scale: float, sink=None, rope_dims: int = 0,
+                  rope_base: float = 10000.0):
     """HCA attention for every (b, t): o [B, T, H, D], lse [B, T, H]."""
     q = f64(q)
     B, T, H, D = q.shape
@@ -120,7 +122,8 @@ def hca_attn_lane(q, ckv, kv, kv_off, ent_off, q_pos, m: int, W: int, scale: flo
         ckv_b = f64(ckv[ent_off[b]:ent_off[b + 1]])
         kv_b = f64(kv[kv_off[b]:kv_off[b + 1]])
         for t in range(T):
-            o[b, t], lse[b, t] = csa.hca_attn(q[b, t], ckv_b, kv_b, int(q_pos[b]) + t, m, W, scale)
+            o[b, t], lse[b, t] = csa.hca_attn(q[b, t], ckv_b, kv_b, int(q_pos[b]) + t, m, W, scale, sink, rope_dims,
+                                              rope_base)
     return o, lse
 
 

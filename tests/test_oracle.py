@@ -395,6 +395,108 @@ def test_sparse_attn_window_only_and_hca_equals_full_selection():
     np.testing.assert_allclose(lh, ls, rtol=1e-14)
 
 
+# ----------------------------------------------------------------- attention sink and RoPE
+
+def test_sink_is_a_zero_value_key_in_sdpa():
+    """[P1] section 7: the sink adds exp(z'_h) to head h's denominator and carries nothing.
+    Per head, that is a library attention with separate keys and values over X plus one
+    extra key whose logit is z'_h and whose value row is zero."""
+    r = _rng(30)
+    H, D, n = 6, 16, 40
+    q, X = r.standard_normal((H, D)), r.standard_normal((n, D))
+    z = np.array([-3.0, 0.0, 1.5, 4.0, 9.0, -np.inf])
+    sc = 0.3
+    o, lse = csa.attend(q, X, sc, sink=z)
+    for h in range(H):
+        if np.isfinite(z[h]):
+            ks = q[h] * (z[h] / (sc * q[h] @ q[h]))          # sc * q_h . ks = z_h
+            K = np.vstack([X, ks])
+            V = np.vstack([X, np.zeros(D)])
+        else:
+            K, V = X, X
+        qt = torch.from_numpy(q[h])[None, None, None, :]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qt, torch.from_numpy(K)[None, None], torch.from_numpy(V)[None, None], scale=sc)[0, 0, 0].numpy()
+        np.testing.assert_allclose(o[h], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_sink_closed_form_and_limits():
+    """out_sink = out * sigmoid(lse - z), lse_sink = logaddexp(lse, z); the weights then sum
+    to 1 - exp(z - lse_sink) (read off with identity keys); no keys: out 0, lse z."""
+    r = _rng(31)
+    H, D = 5, 12
+    q, X = r.standard_normal((H, D)), r.standard_normal((30, D))
+    z = r.standard_normal(H) * 3
+    o, lse = csa.attend(q, X, 0.4)
+    os_, ls = csa.attend(q, X, 0.4, sink=z)
+    np.testing.assert_allclose(os_, o / (1 + np.exp(z - lse))[:, None], rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(ls, np.logaddexp(lse, z), rtol=1e-14)
+    oi, li = csa.attend(q, np.eye(D), 0.4, sink=z)
+    np.testing.assert_allclose(oi.sum(axis=1), 1 - np.exp(z - li), rtol=1e-13)
+    oe, le = csa.attend(q, np.zeros((0, D)), 0.4, sink=z)
+    assert np.all(oe == 0) and np.array_equal(le, z)
+    on, ln = csa.attend(q, X, 0.4, sink=np.full(H, -np.inf))
+    np.testing.assert_array_equal(on, o)
+    np.testing.assert_array_equal(ln, lse)
+
+
+def test_rope_textbook_values():
+    """The first rotated pair turns by pos radians; pair j by pos * base^(-2j/R), so at
+    pos = base^(2j/R) it turns by one radian; the dimensions before the last R pass."""
+    D, R = 16, 8
+    e = np.zeros(D)
+    e[D - R] = 1.0                                   # pair 0, first component
+    y = csa.rope(e, 0.7, R, 10000.0)
+    np.testing.assert_allclose(y[D - R:D - R + 2], [math.cos(0.7), math.sin(0.7)], rtol=1e-15, atol=1e-16)
+    e2 = np.zeros(D)
+    e2[D - R + 5] = 1.0                              # pair 2, second component
+    y2 = csa.rope(e2, 100.0, R, 10000.0)             # 10000^(-4/8) = 1/100: one radian
+    np.testing.assert_allclose(y2[D - R + 4:D - R + 6], [-math.sin(1.0), math.cos(1.0)], rtol=1e-14, atol=1e-15)
+    x = _rng(32).standard_normal((3, D))
+    np.testing.assert_array_equal(csa.rope(x, 123.0, R, 10000.0)[:, :D - R], x[:, :D - R])
+    np.testing.assert_array_equal(csa.rope(x, 123.0, 0, 10000.0), x)
+
+
+def test_rope_is_complex_rotation_and_a_group():
+    """Pairs as complex numbers are multiplied by exp(i * angle); rotations compose, p then
+    -p is the identity, norms of pairs are kept, and q.k after rotating q at p and k at j
+    depends on j - p only (the relative-position property)."""
+    r = _rng(33)
+    D, R, base = 128, 64, 10000.0
+    x = r.standard_normal((4, D))
+    y = csa.rope(x, 1048577.0, R, base)
+    zc = x[:, D - R::2] + 1j * x[:, D - R + 1::2]
+    ang = 1048577.0 * base ** (-np.arange(0, R, 2) / R)
+    w = zc * np.exp(1j * ang)
+    np.testing.assert_allclose(y[:, D - R::2], w.real, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(y[:, D - R + 1::2], w.imag, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(csa.rope(csa.rope(x, 700.0, R, base), 300.0, R, base), csa.rope(x, 1000.0, R, base),
+                               rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(csa.rope(y, -1048577.0, R, base), x, rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(np.hypot(y[:, D - R::2], y[:, D - R + 1::2]), np.abs(zc), rtol=1e-13)
+    qv, kv = r.standard_normal(D), r.standard_normal(D)
+    s1 = csa.rope(qv, 5000.0, R, base) @ csa.rope(kv, 4000.0, R, base)
+    s2 = csa.rope(qv, 905000.0, R, base) @ csa.rope(kv, 904000.0, R, base)
+    assert abs(s1 - s2) < 1e-9
+
+
+def test_attend_at_inverse_rope_makes_positions_relative():
+    """[P1] section 8: a value row stored rotated at its own position j, read by a query at p
+    whose output is rotated at -p, comes out rotated at j - p. With one key the output is
+    that key, so attend_at returns rope(v, j - p); with no rope and no sink it is attend."""
+    r = _rng(34)
+    H, D, R = 4, 32, 16
+    q, v = r.standard_normal((H, D)), r.standard_normal(D)
+    j, p = 777, 1000
+    o, _ = csa.attend_at(q, csa.rope(v, j, R, 500.0)[None], 0.2, p, rope_dims=R, rope_base=500.0)
+    np.testing.assert_allclose(o, np.tile(csa.rope(v, j - p, R, 500.0), (H, 1)), rtol=1e-11, atol=1e-12)
+    X = r.standard_normal((20, D))
+    a = csa.attend_at(q, X, 0.2, p)
+    b = csa.attend(q, X, 0.2)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+
+
 def test_m1_full_topk_no_window_reduces_to_dense_attention():
     """With m=1, k = every entry and no window, the whole CSA lane is dense
     softmax(Q K^T / sqrt(d)) V over the context (K = V)."""
