@@ -324,13 +324,26 @@ def main():
         result["compress_overlap_bulk"] = {"us": round(t_ov_bulk, 1), "bytes": ov_bytes,
                                            "GB_s": round(ov_bytes / (t_ov_bulk * 1e-6) / 1e9, 1),
                                            "frac": round(ov_bytes / (t_ov_bulk * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-        # the whole decode step with overlapped compression (carried by the indexer launch),
-        # timed like the headline loop
-        cl.kv_b, cl.z_b = kv_b, z_b
-        g_ov_step = capture(lambda: [cl.step(r) for r in range(R)])
-        result["overlap_step_us"] = round(time_graphs([g_ov_step], max(1, 400 // R), per_replay=R), 2)
-        cl.kv_b = cl.z_b = None
-        del kv_b, z_b, ckv_s, g_ov_step
+        # the whole decode step with the method's options, timed like the headline loop:
+        # overlapped compression (carried by the indexer launch), the attention sink with
+        # partial RoPE on the last 64 dims, and both
+        import synth.workloads as SW
+        sink = SW.normal_f32(inp.workload.seed, SW.S_EXTRA + 7, (H,), std=2.0).cuda()
+
+        def options_step(overlap: bool, extras: bool) -> float:
+            cl.kv_b, cl.z_b = (kv_b, z_b) if overlap else (None, None)
+            cl.sink, cl.rope_dims = (sink, 64) if extras else (None, 0)
+            g = capture(lambda: [cl.step(r) for r in range(R)])
+            t = time_graphs([g], max(1, 400 // R), per_replay=R)
+            cl.kv_b = cl.z_b = cl.sink = None
+            cl.rope_dims = 0
+            return round(t, 2)
+
+        result["options_step_us"] = {"plain": round(ms_step * 1e3, 2),
+                                     "overlap": options_step(True, False),
+                                     "sink_rope64": options_step(False, True),
+                                     "overlap_sink_rope64": options_step(True, True)}
+        del kv_b, z_b, ckv_s
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)

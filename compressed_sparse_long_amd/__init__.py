@@ -43,7 +43,13 @@ class _CsaStep(ctypes.Structure):
         ("attn_ws_bytes", _S),
         ("q_pos", _P), ("m", _I), ("B", _I), ("T", _I), ("max_entries", _L),
         ("kv_b", _P), ("z_b", _P),
+        ("sink", _P), ("rope_dims", _I), ("rope_base", _F),
     ]
+
+
+class _AttnExtras(ctypes.Structure):
+    """csl_attn_extras (include/csl.h), field for field."""
+    _fields_ = [("sink", _P), ("rope_dims", _I), ("rope_base", _F)]
 
 
 class CslError(RuntimeError):
@@ -66,8 +72,10 @@ def _load() -> ctypes.CDLL:
         "csl_topk_workspace_bytes": (S, [I, I, L, I]),
         "csl_topk_select": (I, [P, L, P, P, I, I, I, I, L, P, P, S, I, P]),
         "csl_attn_workspace_bytes": (S, [I, I, I, I, L]),
-        "csl_sparse_attn_decode": (I, [P, P, P, I, P, P, P, P, I, I, I, I, I, F, P, P, P, S, P]),
-        "csl_hca_attn_decode": (I, [P, P, P, P, P, P, I, I, I, I, I, I, F, L, P, P, P, S, P]),
+        "csl_sparse_attn_decode": (I, [P, P, P, I, P, P, P, P, I, I, I, I, I, F, P, P, P, S,
+                                       ctypes.POINTER(_AttnExtras), P]),
+        "csl_hca_attn_decode": (I, [P, P, P, P, P, P, I, I, I, I, I, I, F, L, P, P, P, S,
+                                    ctypes.POINTER(_AttnExtras), P]),
         "csl_csa_decode_step": (I, [ctypes.POINTER(_CsaStep), P]),
     }
     for name, (res, args) in sig.items():
@@ -207,9 +215,18 @@ def _attn_ws(ws, B, T, H, D, max_keys, device):
     return ws, (0 if ws is None else ws.numel() * ws.element_size())
 
 
+def _extras(sink, rope_dims: int, rope_base: float):
+    if sink is None and not rope_dims:
+        return None
+    return ctypes.byref(_AttnExtras(sink=_ptr(sink, "sink", _F32), rope_dims=int(rope_dims),
+                                    rope_base=float(rope_base)))
+
+
 def sparse_attn_decode(q, ckv, idx, kv, kv_off, ent_off, q_pos, n_win: int, out, lse=None, scale: float | None = None,
-                       ws=None, stream=None):
-    """CSA attention over the selected entries plus the raw window; see csl.h."""
+                       ws=None, sink=None, rope_dims: int = 0, rope_base: float = 10000.0, stream=None):
+    """CSA attention over the selected entries plus the raw window; ``sink`` (fp32 [H] logits)
+    and ``rope_dims``/``rope_base`` (partial RoPE of q at p, of the output at -p) are the
+    optional extras; see csl.h."""
     B, T, H, D = q.shape
     k = idx.shape[-1]
     if scale is None:
@@ -218,13 +235,16 @@ def sparse_attn_decode(q, ckv, idx, kv, kv_off, ent_off, q_pos, n_win: int, out,
     _check(_lib.csl_sparse_attn_decode(
         _ptr(q, "q", _BF16), _ptr(ckv, "ckv", _BF16), _ptr(idx, "idx", (torch.int32,)), k, _ptr(kv, "kv", _BF16),
         _ptr(kv_off, "kv_off", _I64), _ptr(ent_off, "ent_off", _I64), _ptr(q_pos, "q_pos", _I64), int(n_win), B, T, H,
-        D, float(scale), _ptr(out, "out", _F32), _ptr(lse, "lse", _F32), _ptr(ws, "ws"), wb, _stream(stream)))
+        D, float(scale), _ptr(out, "out", _F32), _ptr(lse, "lse", _F32), _ptr(ws, "ws"), wb,
+        _extras(sink, rope_dims, rope_base), _stream(stream)))
     return out
 
 
 def hca_attn_decode(q, ckv, kv, kv_off, ent_off, q_pos, m: int, n_win: int, out, lse=None, scale: float | None = None,
-                    max_entries: int | None = None, ws=None, stream=None):
-    """HCA dense attention over every visible entry plus the raw window; see csl.h."""
+                    max_entries: int | None = None, ws=None, sink=None, rope_dims: int = 0, rope_base: float = 10000.0,
+                    stream=None):
+    """HCA dense attention over every visible entry plus the raw window, with the same
+    optional extras as sparse_attn_decode; see csl.h."""
     B, T, H, D = q.shape
     if scale is None:
         scale = D ** -0.5
@@ -234,7 +254,8 @@ def hca_attn_decode(q, ckv, kv, kv_off, ent_off, q_pos, m: int, n_win: int, out,
     _check(_lib.csl_hca_attn_decode(
         _ptr(q, "q", _BF16), _ptr(ckv, "ckv", _BF16), _ptr(kv, "kv", _BF16), _ptr(kv_off, "kv_off", _I64),
         _ptr(ent_off, "ent_off", _I64), _ptr(q_pos, "q_pos", _I64), int(m), int(n_win), B, T, H, D, float(scale),
-        int(max_entries), _ptr(out, "out", _F32), _ptr(lse, "lse", _F32), _ptr(ws, "ws"), wb, _stream(stream)))
+        int(max_entries), _ptr(out, "out", _F32), _ptr(lse, "lse", _F32), _ptr(ws, "ws"), wb,
+        _extras(sink, rope_dims, rope_base), _stream(stream)))
     return out
 
 
@@ -245,7 +266,8 @@ def _nbytes(t) -> int:
 def csa_decode_step(kv, z, kv_off, ent_off, first_entry, max_new_entries: int, ckv, qI, w, kI, scores, topk_ws,
                     k: int, idx, q, n_win: int, out, q_pos, m: int, lse=None, scale: float | None = None,
                     k_scale=None, scale_off=None, scale_group: int = 64, max_entries: int | None = None,
-                    attn_ws=None, kv_b=None, z_b=None, stream=None):
+                    attn_ws=None, kv_b=None, z_b=None, sink=None, rope_dims: int = 0, rope_base: float = 10000.0,
+                    stream=None):
     """One whole CSA step (compress_kv of the newest entries into ckv, or compress_kv_overlap
     when series b ``kv_b``/``z_b`` is given, indexer_scores with candidate lists, topk_select,
     sparse_attn_decode) in one C call; see csl.h."""
@@ -275,6 +297,7 @@ def csa_decode_step(kv, z, kv_off, ent_off, first_entry, max_new_entries: int, c
         q=_ptr(q, "q", _BF16), H=H, D=D, n_win=int(n_win), scale=float(scale), out=_ptr(out, "out", _F32),
         lse=_ptr(lse, "lse", _F32), attn_ws=_ptr(attn_ws, "attn_ws"), attn_ws_bytes=awb,
         kv_b=_ptr(kv_b, "kv_b", _BF16), z_b=_ptr(z_b, "z_b", _BF16),
+        sink=_ptr(sink, "sink", _F32), rope_dims=int(rope_dims), rope_base=float(rope_base),
         q_pos=_ptr(q_pos, "q_pos", _I64), m=int(m), B=B, T=T, max_entries=int(max_entries))
     _check(_lib.csl_csa_decode_step(ctypes.byref(s), _stream(stream)))
     return out

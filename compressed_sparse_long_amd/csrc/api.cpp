@@ -46,7 +46,7 @@ extern "C" {
 
 const char* csl_last_error(void) { return g_last_error.c_str(); }
 
-int csl_version(void) { return 200; }
+int csl_version(void) { return 300; }
 
 }  // extern "C"
 
@@ -222,9 +222,29 @@ static int check_attn(const char* who, const void* q, const void* ckv, const voi
   return CSL_OK;
 }
 
+// attention extras: a valid RoPE width and base, an aligned sink; fills the launcher's form
+static int check_extras(const char* who, const float* sink, int rope_dims, float rope_base, csl::AttnExtras& ex) {
+  if (rope_dims < 0) return fail(CSL_ERR_INVALID, "%s: rope_dims must be >= 0", who);
+  if (rope_dims != 0 && rope_dims != 64)
+    return fail(CSL_ERR_UNSUPPORTED, "%s: rope_dims must be 0 or 64, got %d", who, rope_dims);
+  if (rope_dims > 0 && !(std::isfinite(rope_base) && rope_base > 1.f))
+    return fail(CSL_ERR_INVALID, "%s: rope_base must be finite and > 1", who);
+  if (sink && !aligned(sink, 4)) return fail(CSL_ERR_INVALID, "%s: sink must be 4-byte aligned", who);
+  ex.sink = sink;
+  ex.rope_dims = rope_dims;
+  ex.rope_theta1 = rope_dims > 0 ? std::pow((double)rope_base, -2.0 / rope_dims) : 1.0;
+  return CSL_OK;
+}
+
 int csl_sparse_attn_decode(const void* q, const void* ckv, const int32_t* idx, int k, const void* kv,
                            const int64_t* kv_off, const int64_t* ent_off, const int64_t* q_pos, int n_win, int B, int T,
-                           int H, int D, float scale, float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+                           int H, int D, float scale, float* out, float* lse, void* ws, size_t ws_bytes,
+                           const csl_attn_extras* extras, void* stream) {
+  csl::AttnExtras ex;
+  if (extras) {
+    const int se = check_extras("sparse_attn_decode", extras->sink, extras->rope_dims, extras->rope_base, ex);
+    if (se != CSL_OK) return se;
+  }
   if (k < 0) return fail(CSL_ERR_INVALID, "sparse_attn_decode: k must be >= 0");
   if (k > 0 && !idx) return fail(CSL_ERR_INVALID, "sparse_attn_decode: idx is NULL");
   const int64_t max_keys = (int64_t)k + n_win;
@@ -233,13 +253,19 @@ int csl_sparse_attn_decode(const void* q, const void* ckv, const int32_t* idx, i
   if (st == -1) return ok();
   if (st != CSL_OK) return st;
   return hip_status(csl::launch_attention(true, q, ckv, idx, k, kv, kv_off, ent_off, q_pos, 1, n_win, B, T, H, scale,
-                                          (int64_t)1 << 62, max_keys, out, lse, ws, as_stream(stream)),
+                                          (int64_t)1 << 62, max_keys, out, lse, ws, ex, as_stream(stream)),
                     "sparse_attn_decode launch");
 }
 
 int csl_hca_attn_decode(const void* q, const void* ckv, const void* kv, const int64_t* kv_off, const int64_t* ent_off,
                         const int64_t* q_pos, int m, int n_win, int B, int T, int H, int D, float scale,
-                        int64_t max_entries, float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+                        int64_t max_entries, float* out, float* lse, void* ws, size_t ws_bytes,
+                        const csl_attn_extras* extras, void* stream) {
+  csl::AttnExtras ex;
+  if (extras) {
+    const int se = check_extras("hca_attn_decode", extras->sink, extras->rope_dims, extras->rope_base, ex);
+    if (se != CSL_OK) return se;
+  }
   if (m < 1) return fail(CSL_ERR_INVALID, "hca_attn_decode: m must be >= 1");
   if (max_entries < 0) return fail(CSL_ERR_INVALID, "hca_attn_decode: max_entries must be >= 0");
   const int64_t max_keys = max_entries + n_win;
@@ -248,7 +274,7 @@ int csl_hca_attn_decode(const void* q, const void* ckv, const void* kv, const in
   if (st == -1) return ok();
   if (st != CSL_OK) return st;
   return hip_status(csl::launch_attention(false, q, ckv, nullptr, 0, kv, kv_off, ent_off, q_pos, m, n_win, B, T, H,
-                                          scale, max_entries, max_keys, out, lse, ws, as_stream(stream)),
+                                          scale, max_entries, max_keys, out, lse, ws, ex, as_stream(stream)),
                     "hca_attn_decode launch");
 }
 
@@ -263,6 +289,9 @@ int csl_csa_decode_step(const csl_csa_step* s, void* stream) {
     st = check_series_b(s->kv_b, s->z, s->z_b, "csa_decode_step");
     if (st != CSL_OK) return st;
   }
+  csl::AttnExtras ex;
+  st = check_extras("csa_decode_step", s->sink, s->rope_dims, s->rope_base, ex);
+  if (st != CSL_OK) return st;
   void* topk_ws = s->topk_ws;
   st = check_indexer(s->q_idx, s->w, s->k_idx, s->k_dtype, s->k_scale, s->scale_off, s->scale_group, s->ent_off,
                      s->q_pos, s->m, s->B, s->T, s->HI, s->CI, s->max_entries, s->scores, s->ld, topk_ws,
@@ -305,7 +334,7 @@ int csl_csa_decode_step(const csl_csa_step* s, void* stream) {
   if (e != hipSuccess) return hip_status(e, "csa_decode_step launch");
   return hip_status(csl::launch_attention(true, s->q, s->ckv, s->idx, s->k, s->kv, s->kv_off, s->ent_off, s->q_pos, 1,
                                           s->n_win, s->B, s->T, s->H, s->scale, (int64_t)1 << 62, max_keys, s->out,
-                                          s->lse, s->attn_ws, hs),
+                                          s->lse, s->attn_ws, ex, hs),
                     "csa_decode_step launch");
 }
 

@@ -18,7 +18,13 @@
 //   * a split of one or two tiles gathers all its rows in one round trip; a workgroup that
 //     walks more tiles loads the next tile's rows while the current one is multiplied;
 //   * with several splits per row each workgroup writes a normalised partial (o, lse) and
-//     a merge kernel combines them with log-sum-exp weights.
+//     a merge kernel combines them with log-sum-exp weights;
+//   * optional per-query extras ([P1] sections 7 and 8): the attention sink, a per-head logit
+//     whose exponential joins the final softmax denominator with no value, and partial RoPE:
+//     the query's last 64 dims are rotated at its position p before the scores (kept exact
+//     as a bf16 pair, like the probabilities) and the output's last 64 dims at -p after
+//     normalisation. Both act where the row's result is final: in the single-split
+//     epilogue or in the merge.
 #include "device_common.h"
 #include "launch.h"
 
@@ -28,6 +34,9 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kKT = 64;               // keys per tile
+constexpr int kRope = 64;             // partial RoPE: the last 64 dims ([P1] section 8)
+constexpr int kRopeOff = kD - kRope;  // first rotated dim
+constexpr int kRopeKK = kRopeOff / 32;  // first rotated 32-dim chunk of the query operand
 
 struct RowGeom {
   int64_t ent_base, n_ent, kv_base, win_lo, win_cnt, nvis;
@@ -81,6 +90,24 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* lds_base, int byte
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(p));
 }
 
+// (cos, sin) of RoPE pair j at position p: the angle p * theta1^j (theta1 = base^(-2/R)) is
+// formed in double, in revolutions, and reduced to [-1/2, 1/2] there (p reaches 2^20 and
+// more, where a float angle would be off by hundredths of a radian); the hardware sine and
+// cosine, which take revolutions, finish in float. theta1^j comes from square-and-multiply
+// over j's 6 bits.
+__device__ __forceinline__ float2 rope_cs(int64_t p, int j, double theta1) {
+  double th = 1.0, sq = theta1;
+#pragma unroll
+  for (int bit = 0; bit < 6; ++bit) {
+    if (j & (1 << bit)) th *= sq;
+    sq *= sq;
+  }
+  double rev = (double)p * th * 0.15915494309189535;  // 1 / (2 pi)
+  rev -= rint(rev);
+  const float f = (float)rev;
+  return make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
+}
+
 // A score must exceed the running maximum (base-2 logits) by more than this before the
 // accumulators are rescaled; in between, probabilities are taken relative to the stale
 // maximum and stay below 2^8, which fp32 sums and bf16 probabilities hold without loss.
@@ -90,23 +117,33 @@ constexpr float kRescaleSlack = 8.f;
 // online softmax in base 2 (vld[v] != 0: slot v holds a key), and O^T += V^T P^T with each
 // probability split into two bf16 terms. V^T comes from the same row-major tile through
 // transposing reads.
+template <bool ROPE>
 __device__ __forceinline__ void tile_compute(const uint8_t* Ks, const uint8_t* vld, const bf16x8 (&qb)[4],
-                                             float scale_log2, f32x4 (&oacc)[8], float& m_run, float& l_run,
-                                             int c, int g) {
+                                             const bf16x8 (&ql)[4], float scale_log2, f32x4 (&oacc)[8],
+                                             float& m_run, float& l_run, int c, int g) {
   // K operand: lane (c, g) takes key 16mb + c, dims 32kk + 8g.. (unit 4kk + g); every row
   // 16mb + c shares the swizzle of row c
   const int swc = ks_swz(c);
   f32x4 sacc[4];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) sacc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bf16x8 ka[4][4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     const int koff = c * 256 + 16 * ((4 * kk + g) ^ swc);
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(Ks + koff + mb * 16 * 256));
-      sacc[mb] = mfma16x16x32(ka, qb[kk], sacc[mb]);
+      ka[kk][mb] = as_bf16x8(*reinterpret_cast<const u32x4*>(Ks + koff + mb * 16 * 256));
+      sacc[mb] = mfma16x16x32(ka[kk][mb], qb[kk], sacc[mb]);
     }
+  }
+  if (ROPE) {
+    // rotated query chunks carry a bf16 residual: a second product per block keeps q.k exact
+    // to fp32 (issued after all the main products, so no product waits on its own block's)
+#pragma unroll
+    for (int kk = kRopeKK; kk < 4; ++kk)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) sacc[mb] = mfma16x16x32(ka[kk][mb], ql[kk], sacc[mb]);
   }
   // this lane's 16 keys are 16mb + 4g + i; a tile with every slot filled skips the masking
   uint32_t okw[4];
@@ -189,23 +226,44 @@ __device__ __forceinline__ void tile_compute(const uint8_t* Ks, const uint8_t* v
   }
 }
 
-// Common epilogue: normalise and write the output (one split) or the partial (o, lse).
+// Common epilogue: normalise and write the output (one split) or the partial (o, lse). The
+// single-split output is final: the sink joins its denominator and its last R dims rotate
+// at -p (rcs holds the (cos, sin) of the row's R/2 RoPE pairs).
+template <bool ROPE>
 __device__ __forceinline__ void attn_write(const f32x4 (&oacc)[8], float m_run, float l_run, int row, int nrows,
                                            int split, int H, int head, int g, float* __restrict__ out,
                                            float* __restrict__ lse_out, float* __restrict__ ws_o,
-                                           float* __restrict__ ws_lse) {
+                                           float* __restrict__ ws_lse, const float* __restrict__ sink,
+                                           const float2* rcs) {
   // reduce the lane-partial denominators across the 4 lane groups
   float l = l_run;
   l += shfl_xor_f(l, 16);
   l += shfl_xor_f(l, 32);
-  const bool empty = !(l > 0.f);
-  const float inv = empty ? 0.f : 1.f / l;
-  const float lse = empty ? -INFINITY : (m_run + __log2f(l)) * kLn2;
   const bool single = (gridDim.x == 1);
+  // sink logit in base 2 (-inf without a sink; partials never take it)
+  const float zs = (single && sink) ? sink[head] * kLog2e : -INFINITY;
+  const float M = fmaxf(l > 0.f ? m_run : -INFINITY, zs);
+  float inv = 0.f, lse = -INFINITY;
+  if (M != -INFINITY) {
+    const float a = l > 0.f ? __builtin_amdgcn_exp2f(m_run - M) : 0.f;
+    const float den = l * a + __builtin_amdgcn_exp2f(zs - M);
+    inv = a / den;
+    lse = (M + __log2f(den)) * kLn2;
+  }
   float* o_dst = single ? out + ((int64_t)row * H + head) * kD : ws_o + (((int64_t)split * nrows + row) * H + head) * kD;
 #pragma unroll
   for (int db = 0; db < 8; ++db) {
-    const f32x4 v = oacc[db] * inv;
+    f32x4 v = oacc[db] * inv;
+    if (ROPE && single && 16 * db >= kRopeOff) {
+      // dims 16db + 4g + 0..3 are two pairs; rotate each at -p
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float2 cs = rcs[(16 * db + 4 * g + 2 * i - kRopeOff) >> 1];
+        const float x0 = v[2 * i], x1 = v[2 * i + 1];
+        v[2 * i] = x0 * cs.x + x1 * cs.y;
+        v[2 * i + 1] = x1 * cs.x - x0 * cs.y;
+      }
+    }
     *reinterpret_cast<float4*>(o_dst + 16 * db + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
   }
   if (g == 0) {
@@ -225,13 +283,14 @@ __device__ __forceinline__ void attn_write(const f32x4 (&oacc)[8], float m_run, 
 // for each tile's rows in turn. MODE 0: the workgroup walks many tiles and loads the next
 // tile's rows (and the selected ids of the one after) into registers while the current tile
 // is multiplied.
-template <int NHG, bool SPARSE, int MODE>
+template <int NHG, bool SPARSE, int MODE, bool ROPE>
 __global__ __launch_bounds__(NHG * 64) void attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ ckv, const int32_t* __restrict__ idx, int k,
     const uint16_t* __restrict__ kv, const int64_t* __restrict__ kv_off, const int64_t* __restrict__ ent_off,
     const int64_t* __restrict__ q_pos, int m, int n_win, int T, float scale_log2, int64_t max_entries,
     int keys_per_split, float* __restrict__ out, float* __restrict__ lse_out, float* __restrict__ ws_o,
-    float* __restrict__ ws_lse) {
+    float* __restrict__ ws_lse, const float* __restrict__ sink, double rope_theta1,
+    float2* __restrict__ ws_rope) {
   constexpr bool MULTI = MODE == 0;
   constexpr int NTL = MULTI ? 1 : MODE;    // tiles held in LDS at once
   constexpr int NT = NHG * 64;
@@ -242,6 +301,7 @@ __global__ __launch_bounds__(NHG * 64) void attn_kernel(
   static_assert(RPT <= 32, "one mask bit per gathered row");
   __shared__ __align__(16) uint8_t Ks[NTL][kKT * kD * 2];
   __shared__ __align__(16) uint8_t vld[NTL][kKT];  // slot v of a tile holds a key
+  __shared__ float2 rcs_all[ROPE ? NHG : 1][kRope / 2];  // RoPE (cos, sin) per pair at the row's position, per wave
 
   const int split = blockIdx.x;
   const int row = blockIdx.y;
@@ -321,6 +381,50 @@ __global__ __launch_bounds__(NHG * 64) void attn_kernel(
   float l_run = 0.f;
 
   if (k_lo < k_hi) issue(k_lo, ids_cur);
+
+  // partial RoPE: the row's (cos, sin) table, then the rotated query chunks as bf16 pairs.
+  // Every wave builds its own copy, so no workgroup barrier (which would also wait for the
+  // gathered rows in flight) stands between the table and its readers; the first split
+  // also leaves the table in the workspace for the merge. The table needs only the row's
+  // position, so it is built while the rows are in flight; the rotation needs the query,
+  // whose loads may be queued behind the rows', so a single-round kernel rotates once the
+  // rows have landed (the prefetching loop has its query in registers before the rows go
+  // out).
+  float2* rcs = rcs_all[ROPE ? wave : 0];
+  bf16x8 ql[4];
+  if (ROPE) {
+    const int64_t p = q_pos[b] + t;
+    if (lane < kRope / 2) {
+      const float2 cs = rope_cs(p, lane, rope_theta1);
+      rcs[lane] = cs;
+      if (ws_rope && split == 0 && wave == 0) ws_rope[(int64_t)row * (kRope / 2) + lane] = cs;
+    }
+    // the wave's own LDS writes, ordered before its reads (in-wave: no hardware wait needed)
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  }
+  auto rotate_q = [&]() {
+#pragma unroll
+    for (int kk = kRopeKK; kk < 4; ++kk) {
+      const u32x4 w = __builtin_bit_cast(u32x4, qb[kk]);
+      const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+      uint32_t hv[4], lv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {  // dims 32kk + 8g + 2i, +1: pair (32kk + 8g + 2i - kRopeOff) / 2
+        const float2 cs = rcs[(32 * kk + 8 * g + 2 * i - kRopeOff) >> 1];
+        const float x0 = bf16lo(wv[i]), x1 = bf16hi(wv[i]);
+        const float y0 = x0 * cs.x - x1 * cs.y;
+        const float y1 = x0 * cs.y + x1 * cs.x;
+        const uint32_t h = pack_bf16x2(y0, y1);
+        hv[i] = h;
+        lv[i] = pack_bf16x2(y0 - bf16lo(h), y1 - bf16hi(h));
+      }
+      qb[kk] = as_bf16x8(u32x4{hv[0], hv[1], hv[2], hv[3]});
+      ql[kk] = as_bf16x8(u32x4{lv[0], lv[1], lv[2], lv[3]});
+    }
+  };
+  if (ROPE && MULTI) rotate_q();
+
   for (int64_t t0 = k_lo; t0 < k_hi; t0 += NV) {
     // this round's rows (in flight since the previous round) into the swizzled K tiles
 #pragma unroll
@@ -337,6 +441,7 @@ __global__ __launch_bounds__(NHG * 64) void attn_kernel(
       if (u == 0) vld[tl][vr] = ok ? 1 : 0;
     }
     __syncthreads();
+    if (ROPE && !MULTI) rotate_q();  // single round: the rows (and so the query) have landed
     // the next tile's rows and the ids two tiles ahead go out while this one computes
     if (MULTI && t0 + kKT < k_hi) {
       issue(t0 + kKT, ids_nxt);
@@ -344,25 +449,33 @@ __global__ __launch_bounds__(NHG * 64) void attn_kernel(
     }
 #pragma unroll
     for (int tl = 0; tl < NTL; ++tl)
-      if (tl == 0 || t0 + tl * kKT < k_hi) tile_compute(Ks[tl], vld[tl], qb, scale_log2, oacc, m_run, l_run, c, g);
+      if (tl == 0 || t0 + tl * kKT < k_hi)
+        tile_compute<ROPE>(Ks[tl], vld[tl], qb, ql, scale_log2, oacc, m_run, l_run, c, g);
     if (!MULTI) break;  // the launch gives single-round kernels at most NTL tiles
     __syncthreads();    // the next tile overwrites Ks / vld
   }
-  attn_write(oacc, m_run, l_run, row, nrows, split, H, head, g, out, lse_out, ws_o, ws_lse);
+  attn_write<ROPE>(oacc, m_run, l_run, row, nrows, split, H, head, g, out, lse_out, ws_o, ws_lse, sink, rcs);
 }
 
 // Log-sum-exp merge of the split partials: one thread per (query row, head, dim). Splits are
 // consumed CH at a time with all their loads issued together and an online rescale; the
 // launch picks CH >= nsplit when it can, so the merge waits on memory once.
+// The merged row is final: the sink joins the denominator and, with RoPE, each thread's dim
+// is rotated at -p together with its pair partner (the neighbouring lane), with the row's
+// (cos, sin) table that the attention kernel left in the workspace.
 template <int CH>
 __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
                                                          int nsplit, int nrows, int H, float* __restrict__ out,
-                                                         float* __restrict__ lse_out) {
+                                                         float* __restrict__ lse_out, const float* __restrict__ sink,
+                                                         bool rope, const float2* __restrict__ ws_rope) {
   const int row = blockIdx.x;
   const int e = blockIdx.y * 256 + threadIdx.x;  // (head, dim) index inside the row
   if (e >= H * kD) return;
   const int h = e / kD;
   const int d = e % kD;
+  // issued with the partials' loads: the pair's (cos, sin), read once the merge is done
+  const float2 cs = (rope && d >= kRopeOff) ? ws_rope[(int64_t)row * (kRope / 2) + ((d - kRopeOff) >> 1)]
+                                            : make_float2(1.f, 0.f);
   const float* lse_p = ws_lse + (int64_t)row * H + h;
   const float* o_p = ws_o + ((int64_t)row * H + h) * kD + d;
   const int64_t lse_stride = (int64_t)nrows * H;
@@ -395,30 +508,45 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
     }
     M = Mn;
   }
-  out[((int64_t)row * H + h) * kD + d] = (M == -INFINITY) ? 0.f : acc / wsum;
-  if (d == 0 && lse_out) lse_out[(int64_t)row * H + h] = (M == -INFINITY) ? -INFINITY : M + __logf(wsum);
+  float den = wsum;
+  if (sink) {  // the sink joins the denominator with no value
+    const float z = sink[h];
+    const float Mf = fmaxf(M, z);
+    if (Mf != -INFINITY) {
+      const float a = (M == -INFINITY) ? 0.f : __expf(M - Mf);
+      acc *= a;
+      den = wsum * a + __expf(z - Mf);
+      M = Mf;
+    }
+  }
+  float o = (M == -INFINITY) ? 0.f : acc / den;
+  if (rope) {  // uniform: every lane takes part in the exchange
+    const float partner = __shfl_xor(o, 1, kWave);
+    if (d >= kRopeOff) o = (d & 1) ? o * cs.x - partner * cs.y : o * cs.x + partner * cs.y;
+  }
+  out[((int64_t)row * H + h) * kD + d] = o;
+  if (d == 0 && lse_out) lse_out[(int64_t)row * H + h] = (M == -INFINITY) ? -INFINITY : M + __logf(den);
 }
 
-template <bool SPARSE>
+template <bool SPARSE, bool ROPE>
 hipError_t launch_nhg(int H, dim3 grid, hipStream_t st, const uint16_t* q, const uint16_t* ckv, const int32_t* idx,
                       int k, const uint16_t* kv, const int64_t* kv_off, const int64_t* ent_off, const int64_t* q_pos,
                       int m, int n_win, int T, float scale_log2, int64_t max_entries, int kps, float* out,
-                      float* lse, float* ws_o, float* ws_lse) {
+                      float* lse, float* ws_o, float* ws_lse, float2* ws_rope, const AttnExtras& ex) {
   const int tiles = kps / kKT;  // 1 or 2: gathered in one round; more: the prefetching loop
-#define CSL_ATTN_CASE(NHG)                                                                                     \
-  case NHG:                                                                                                    \
-    if (tiles == 1)                                                                                            \
-      attn_kernel<NHG, SPARSE, 1><<<grid, NHG * 64, 0, st>>>(q, ckv, idx, k, kv, kv_off, ent_off, q_pos, m, n_win, \
-                                                             T, scale_log2, max_entries, kps, out, lse, ws_o,      \
-                                                             ws_lse);                                              \
-    else if (tiles == 2)                                                                                       \
-      attn_kernel<NHG, SPARSE, 2><<<grid, NHG * 64, 0, st>>>(q, ckv, idx, k, kv, kv_off, ent_off, q_pos, m, n_win, \
-                                                             T, scale_log2, max_entries, kps, out, lse, ws_o,      \
-                                                             ws_lse);                                              \
-    else                                                                                                       \
-      attn_kernel<NHG, SPARSE, 0><<<grid, NHG * 64, 0, st>>>(q, ckv, idx, k, kv, kv_off, ent_off, q_pos, m, n_win, \
-                                                             T, scale_log2, max_entries, kps, out, lse, ws_o,      \
-                                                             ws_lse);                                              \
+#define CSL_ATTN_LAUNCH(NHG, MODE)                                                                              \
+  attn_kernel<NHG, SPARSE, MODE, ROPE><<<grid, NHG * 64, 0, st>>>(q, ckv, idx, k, kv, kv_off, ent_off, q_pos, m, \
+                                                                  n_win, T, scale_log2, max_entries, kps, out, lse, \
+                                                                  ws_o, ws_lse, ex.sink, ex.rope_theta1, \
+                                                                  ws_rope)
+#define CSL_ATTN_CASE(NHG)                 \
+  case NHG:                                \
+    if (tiles == 1)                        \
+      CSL_ATTN_LAUNCH(NHG, 1);             \
+    else if (tiles == 2)                   \
+      CSL_ATTN_LAUNCH(NHG, 2);             \
+    else                                   \
+      CSL_ATTN_LAUNCH(NHG, 0);             \
     break;
   switch (H / 16) {
     CSL_ATTN_CASE(1)
@@ -432,6 +560,7 @@ hipError_t launch_nhg(int H, dim3 grid, hipStream_t st, const uint16_t* q, const
     default: return hipErrorInvalidValue;
   }
 #undef CSL_ATTN_CASE
+#undef CSL_ATTN_LAUNCH
   return hipGetLastError();
 }
 
@@ -456,34 +585,45 @@ AttnPlan attn_plan(int B, int T, int64_t max_keys) {
 size_t attn_workspace_bytes(int B, int T, int H, int64_t max_keys) {
   const AttnPlan p = attn_plan(B, T, max_keys);
   if (p.nsplit <= 1) return 0;
-  return (size_t)p.nsplit * B * T * H * (kD + 1) * sizeof(float);
+  // partials (o, lse) of every split, then one RoPE (cos, sin) table per row
+  return (size_t)p.nsplit * B * T * H * (kD + 1) * sizeof(float) + (size_t)B * T * (kRope / 2) * sizeof(float2);
 }
 
 hipError_t launch_attention(bool sparse, const void* q, const void* ckv, const int32_t* idx, int k, const void* kv,
                             const int64_t* kv_off, const int64_t* ent_off, const int64_t* q_pos, int m, int n_win,
                             int B, int T, int H, float scale, int64_t max_entries, int64_t max_keys, float* out,
-                            float* lse, void* ws, hipStream_t st) {
+                            float* lse, void* ws, const AttnExtras& ex, hipStream_t st) {
   const AttnPlan p = attn_plan(B, T, max_keys);
   const int rows = B * T;
   float* ws_o = static_cast<float*>(ws);
   float* ws_lse = ws_o ? ws_o + (size_t)p.nsplit * rows * H * kD : nullptr;
+  // the rows' RoPE tables follow the partials (8-byte aligned: the partials are whole rows
+  // of 16 heads); only the merge reads them
+  float2* ws_rope = ws_o ? reinterpret_cast<float2*>(ws_lse + (size_t)p.nsplit * rows * H) : nullptr;
   dim3 grid((unsigned)p.nsplit, (unsigned)rows);
   const float sl2 = scale * kLog2e;
   const uint16_t* q16 = static_cast<const uint16_t*>(q);
   const uint16_t* c16 = static_cast<const uint16_t*>(ckv);
   const uint16_t* k16 = static_cast<const uint16_t*>(kv);
-  hipError_t e = sparse ? launch_nhg<true>(H, grid, st, q16, c16, idx, k, k16, kv_off, ent_off, q_pos, m, n_win, T, sl2,
-                                           max_entries, p.keys_per_split, out, lse, ws_o, ws_lse)
-                        : launch_nhg<false>(H, grid, st, q16, c16, idx, k, k16, kv_off, ent_off, q_pos, m, n_win, T,
-                                            sl2, max_entries, p.keys_per_split, out, lse, ws_o, ws_lse);
+#define CSL_ATTN_NHG(SP, RP)                                                                                    \
+  launch_nhg<SP, RP>(H, grid, st, q16, c16, idx, k, k16, kv_off, ent_off, q_pos, m, n_win, T, sl2, max_entries, \
+                     p.keys_per_split, out, lse, ws_o, ws_lse, ws_rope, ex)
+  const bool rope = ex.rope_dims > 0;
+  hipError_t e = sparse ? (rope ? CSL_ATTN_NHG(true, true) : CSL_ATTN_NHG(true, false))
+                        : (rope ? CSL_ATTN_NHG(false, true) : CSL_ATTN_NHG(false, false));
+#undef CSL_ATTN_NHG
   if (e != hipSuccess || p.nsplit <= 1) return e;
   const dim3 mgrid((unsigned)rows, (unsigned)((H * kD + 255) / 256));
+#define CSL_MERGE(CH)                                                                                         \
+  attn_merge_kernel<CH><<<mgrid, 256, 0, st>>>(ws_o, ws_lse, p.nsplit, rows, H, out, lse, ex.sink, \
+                                               ex.rope_dims > 0, ws_rope)
   if (p.nsplit <= 8)
-    attn_merge_kernel<8><<<mgrid, 256, 0, st>>>(ws_o, ws_lse, p.nsplit, rows, H, out, lse);
+    CSL_MERGE(8);
   else if (p.nsplit <= 16)
-    attn_merge_kernel<16><<<mgrid, 256, 0, st>>>(ws_o, ws_lse, p.nsplit, rows, H, out, lse);
+    CSL_MERGE(16);
   else
-    attn_merge_kernel<32><<<mgrid, 256, 0, st>>>(ws_o, ws_lse, p.nsplit, rows, H, out, lse);
+    CSL_MERGE(32);
+#undef CSL_MERGE
   return hipGetLastError();
 }
 

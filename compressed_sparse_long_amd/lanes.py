@@ -47,6 +47,11 @@ class _Lane:
         self.lse = torch.empty((self.B, self.T, self.H), dtype=torch.float32, device=device)
         self.scale = 1.0 / math.sqrt(lane.D)
         self.ckv_copies = [self.ckv]
+        # attention extras ([P1] sections 7 and 8): per-head sink logits (fp32 [H] on the
+        # device) and partial RoPE of the query / output; none by default
+        self.sink = None
+        self.rope_dims = 0
+        self.rope_base = 10000.0
 
     def compress_all(self):
         for c in self.ckv_copies:
@@ -117,7 +122,7 @@ class CsaLane(_Lane):
     def attend(self, r: int = 0):
         sparse_attn_decode(self.q, self.ckv_copies[r % len(self.ckv_copies)], self.idx, self.kv, self.kv_off,
                            self.ent_off, self.q_pos, self.W, self.out, lse=self.lse, scale=self.scale,
-                           ws=self.attn_ws)
+                           ws=self.attn_ws, sink=self.sink, rope_dims=self.rope_dims, rope_base=self.rope_base)
 
     def step(self, r: int = 0, fused: bool = True):
         """One decode step on rotated copy r: one csa_decode_step call, or (fused=False) the
@@ -134,7 +139,8 @@ class CsaLane(_Lane):
                         self.topk_ws, self.k, self.idx, self.q, self.W, self.out, self.q_pos,
                         self.m, lse=self.lse, scale=self.scale, k_scale=self.k_scale, scale_off=self.scale_off,
                         scale_group=self.scale_group, max_entries=self.max_entries, attn_ws=self.attn_ws,
-                        kv_b=self.kv_b, z_b=self.z_b)
+                        kv_b=self.kv_b, z_b=self.z_b, sink=self.sink, rope_dims=self.rope_dims,
+                        rope_base=self.rope_base)
 
 
 class HcaLane(_Lane):
@@ -146,7 +152,8 @@ class HcaLane(_Lane):
     def attend(self, r: int = 0):
         hca_attn_decode(self.q, self.ckv_copies[r % len(self.ckv_copies)], self.kv, self.kv_off, self.ent_off,
                         self.q_pos, self.m, self.W, self.out, lse=self.lse, scale=self.scale,
-                        max_entries=self.max_entries, ws=self.attn_ws)
+                        max_entries=self.max_entries, ws=self.attn_ws, sink=self.sink, rope_dims=self.rope_dims,
+                        rope_base=self.rope_base)
 
     def step(self, r: int = 0):
         self.compress_new(r)

@@ -65,7 +65,8 @@ typedef enum {
 /* Message for the last failed call on this thread ("" if none). Never NULL. */
 const char* csl_last_error(void);
 
-/* Library version as MAJOR*10000 + MINOR*100 + PATCH (0.2.0: overlapped compression). */
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH (0.3.0: overlapped compression,
+ * attention sink and partial RoPE). */
 int csl_version(void);
 
 /*
@@ -187,26 +188,50 @@ int csl_topk_select(const float* scores, int64_t ld, const int64_t* ent_off, con
  *   out fp32 [B, T, H, D]; lse fp32 [B, T, H] (nullable)
  *   D == 128; H a multiple of 16, <= 128; k >= 0; n_win >= 0.
  *   ws: at least csl_attn_workspace_bytes(B, T, H, D, k + n_win) bytes (contents free).
+ * extras (nullable; NULL means none of them) adds per-query parts of the core attention:
+ *   sink       device fp32 [H] or NULL: head h's sink logit z'_h ([P1] section 7). exp(z'_h)
+ *              joins the softmax denominator with no value, so the weights sum to less
+ *              than one: out = sum_x exp(l_x - lse) x, lse = log(exp(z'_h) + sum_x exp(l_x)).
+ *              An empty X then gives out = 0 and lse = z'_h.
+ *   rope_dims  0 or 64 ([P1] section 8, partial RoPE on the last 64 dims): the last R = 64
+ *              dims of q are rotated at the query position p before the scores, and the
+ *              same dims of out at -p after normalisation (the inverse rotation on the
+ *              output side). Pair j = (dims D - R + 2j, D - R + 2j + 1) turns by the angle
+ *              pos * rope_base^(-2j/R), counter-clockwise. Key rows (ckv, kv) are used as
+ *              stored: rotating them at their own positions is up to their writer. Other
+ *              widths return CSL_ERR_UNSUPPORTED.
+ *   rope_base  > 1 and finite when rope_dims > 0 (the original RoPE uses 10000).
  * Arithmetic: bf16 MFMA operands with fp32 accumulation; each probability enters the value
- * product as two bf16 terms (hi + bf16(p - hi)), so it carries ~2^-16 relative error; fp32
- * online softmax in base 2; log-sum-exp merge of split partials.
+ * product as two bf16 terms (hi + bf16(p - hi)), so it carries ~2^-16 relative error, and so
+ * does each rotated query dim; fp32 online softmax in base 2; log-sum-exp merge of split
+ * partials. RoPE angles are formed and reduced to one turn in double precision; their sine
+ * and cosine come from the hardware instructions (absolute error about 1e-6).
  */
+typedef struct csl_attn_extras {
+  const float* sink; /* device fp32 [H], or NULL */
+  int rope_dims;     /* 0 or 64 */
+  float rope_base;   /* > 1 when rope_dims > 0 */
+} csl_attn_extras;
+
 size_t csl_attn_workspace_bytes(int B, int T, int H, int D, int64_t max_keys);
 int csl_sparse_attn_decode(const void* q, const void* ckv, const int32_t* idx, int k,
                            const void* kv, const int64_t* kv_off, const int64_t* ent_off,
                            const int64_t* q_pos, int n_win, int B, int T, int H, int D, float scale,
-                           float* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+                           float* out, float* lse, void* ws, size_t ws_bytes,
+                           const csl_attn_extras* extras, void* stream);
 
 /*
  * hca_attn_decode -- HCA dense attention ([P1] section 5.1; [P2] "Heavily Compressed
  * Attention"): as sparse_attn_decode, with the compressed part of X being every visible
  * entry s < min(floor(p / m), E_b, max_entries) instead of a selected list.
  *   ws: at least csl_attn_workspace_bytes(B, T, H, D, max_entries + n_win) bytes.
+ *   extras: as for sparse_attn_decode.
  */
 int csl_hca_attn_decode(const void* q, const void* ckv, const void* kv, const int64_t* kv_off,
                         const int64_t* ent_off, const int64_t* q_pos, int m, int n_win, int B,
                         int T, int H, int D, float scale, int64_t max_entries, float* out,
-                        float* lse, void* ws, size_t ws_bytes, void* stream);
+                        float* lse, void* ws, size_t ws_bytes, const csl_attn_extras* extras,
+                        void* stream);
 
 /*
  * csa_decode_step -- one whole CSA step of one layer ([P2] "Putting It Together"; [P1]
@@ -269,6 +294,10 @@ typedef struct csl_csa_step {
   /* overlapped compression (NULL, NULL: one series) */
   const void* kv_b;           /* bf16 [N_tot, D] series b, or NULL */
   const void* z_b;            /* bf16 [N_tot, D] its logits: given exactly when z is */
+  /* attention extras, as csl_attn_extras (sink NULL and rope_dims 0: none) */
+  const float* sink;          /* device fp32 [H], or NULL */
+  int rope_dims;
+  float rope_base;
 } csl_csa_step;
 
 int csl_csa_decode_step(const csl_csa_step* s, void* stream);

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, s), s
     import compressed_sparse_long_amd as csl
     assert sorted(csl.EXPORTS) == declared_symbols()
-    assert csl.version() == 200
+    assert csl.version() == 300
 
 
 P = ctypes.c_void_p
@@ -137,11 +137,14 @@ def test_attention_validation_and_workspace(lib):
     ws.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64]
     assert ws(1, 8192, 64, 128, 640) == 0     # many rows: one split per row
     w3 = ws(4, 1, 64, 128, 1024 + 128)
-    assert w3 > 0 and w3 % (4 * 64 * 129 * 4) == 0
+    # whole (o, lse) partials of 4 rows x 64 heads per split, plus one RoPE table per row
+    assert w3 > 0 and (w3 - 4 * 32 * 8) % (4 * 64 * 129 * 4) == 0
     f = lib.csl_sparse_attn_decode
     I = ctypes.c_int
-    f.argtypes = [P, P, P, I, P, P, P, P, I, I, I, I, I, ctypes.c_float, P, P, P, ctypes.c_size_t, P]
-    base = [FAKE, FAKE, FAKE, 1024, FAKE, FAKE, FAKE, FAKE, 128, 4, 1, 64, 128, 0.088, FAKE, None, FAKE, w3, None]
+    import compressed_sparse_long_amd as csl
+    EX = ctypes.POINTER(csl._AttnExtras)
+    f.argtypes = [P, P, P, I, P, P, P, P, I, I, I, I, I, ctypes.c_float, P, P, P, ctypes.c_size_t, EX, P]
+    base = [FAKE, FAKE, FAKE, 1024, FAKE, FAKE, FAKE, FAKE, 128, 4, 1, 64, 128, 0.088, FAKE, None, FAKE, w3, None, None]
     bad = list(base); bad[12] = 64
     assert f(*bad) == 2                       # D
     bad = list(base); bad[11] = 24
@@ -152,10 +155,22 @@ def test_attention_validation_and_workspace(lib):
     assert f(*bad) == 1
     bad = list(base); bad[13] = float("nan")
     assert f(*bad) == 1
+    # attention extras: RoPE width and base, sink alignment
+    for ex, status in (((None, 48, 10000.0), 2), ((None, -32, 10000.0), 1), ((None, 64, 1.0), 1),
+                       ((None, 64, float("nan")), 1), ((P((1 << 20) + 2), 0, 0.0), 1), ((None, 128, 10000.0), 2),
+                       ((None, 32, 10000.0), 2)):
+        bad = list(base); bad[18] = ctypes.pointer(csl._AttnExtras(*ex))
+        assert f(*bad) == status, ex
+    assert "rope" in _err(lib) or "sink" in _err(lib)
     g = lib.csl_hca_attn_decode
     L = ctypes.c_int64
-    g.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, ctypes.c_float, L, P, P, P, ctypes.c_size_t, P]
-    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 128, 8, 1, 64, 128, 0.088, 1024, FAKE, None, FAKE, 0, None) == 1
+    g.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, ctypes.c_float, L, P, P, P, ctypes.c_size_t, EX, P]
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 128, 8, 1, 64, 128, 0.088, 1024, FAKE, None, FAKE, 0, None,
+             None) == 1
+    ex = ctypes.pointer(csl._AttnExtras(None, 64, 0.5))
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 128, 128, 8, 1, 64, 128, 0.088, 1024, FAKE, None, FAKE, 1 << 30, ex,
+             None) == 1
+    assert "rope_base" in _err(lib)
 
 
 def test_step_validation(lib):
@@ -183,5 +198,7 @@ def test_step_validation(lib):
     assert call(kv_b=FAKE, z_b=FAKE) == 1       # series-b logits without series-a logits
     assert "z_b" in _err(lib)
     assert call(kv_b=P((1 << 20) + 4)) == 1     # misaligned series b
+    assert call(rope_dims=64, rope_base=0.5) == 1   # RoPE base <= 1
+    assert call(rope_dims=40, rope_base=1e4) == 2   # RoPE width not a multiple of 32
     assert call(B=0) == 0                       # nothing to do: nothing enqueued
     assert _err(lib) == ""

@@ -363,6 +363,83 @@ def test_hca_attention_matches_oracle(csl, H, T, lengths, q_pos, m, n_win):
     assert_attn_close(f64(lse), rl, "lse")
 
 
+# ------------------------------------------------- attention extras: sink and partial RoPE
+
+@pytest.mark.parametrize("kind,H,T,lengths,q_pos,k,m,n_win,rope,base,with_sink", [
+    ("csa", 64, 1, [(1 << 20) + 3, 4000], [(1 << 20) + 3, 4000], 1024, 4, 128, 64, 10000.0, True),  # 9 splits + merge
+    ("csa", 16, 1, [4096], [4096], 32, 4, 16, 64, 10000.0, True),          # one split: the kernel's own epilogue
+    ("csa", 64, 300, [5000], [4000], 64, 4, 64, 64, 10000.0, True),        # 300 positions, one split per row
+    ("csa", 32, 300, [6000], [5000], 256, 4, 128, 64, 160000.0, True),     # prefetching loop + merge, base 160000
+    ("csa", 48, 2, [300, 50], [300, 50], 40, 4, 24, 64, 10000.0, False),   # 3 head groups, no sink
+    ("csa", 64, 1, [9000], [9000], 200, 4, 50, 0, 10000.0, True),          # sink alone
+    ("hca", 64, 1, [131072, 9000], [131072, 9000], 0, 128, 128, 64, 10000.0, True),
+    ("hca", 16, 4, [9000], [7000], 0, 4, 128, 64, 500000.0, False),
+    ("hca", 16, 300, [40000], [39000], 0, 128, 128, 64, 10000.0, True),   # 2 splits of 4 tiles + merge
+])
+def test_attention_extras_match_oracle(csl, kind, H, T, lengths, q_pos, k, m, n_win, rope, base, with_sink):
+    print(f"attn extras {kind} H={H} T={T} lengths={lengths} k={k} m={m} n_win={n_win} rope={rope} "
+          f"base={base} sink={with_sink}", flush=True)
+    kv, ckv, q, kv_off, ent_off, qp = _attn_inputs(lengths, m, H, T, q_pos, 71 + H + T)
+    B = len(lengths)
+    sink = None
+    if with_sink:
+        sink = W.normal_f32(71 + H, W.S_EXTRA + 7, (H,), std=2.0)
+        sink[0] = float("-inf")          # a head without a sink
+        sink[1] = 9.0                    # a head whose sink outweighs every key
+    out = torch.full((B, T, H, 128), float("nan"), device="cuda")
+    lse = torch.full((B, T, H), float("nan"), device="cuda")
+    sc = 128 ** -0.5
+    if kind == "csa":
+        nvis = [[csa.n_visible(q_pos[b] + t, m, lengths[b] // m) for t in range(T)] for b in range(B)]
+        idx = torch.stack([synth.random_selection(600 + b, T, nvis[b], k, fill=0.9) for b in range(B)])
+        csl.sparse_attn_decode(dev(q), dev(ckv), dev(idx), dev(kv), dev(kv_off), dev(ent_off), dev(qp), n_win, out,
+                               lse=lse, scale=sc, sink=dev(sink), rope_dims=rope, rope_base=base)
+        torch.cuda.synchronize()
+        ro, rl = pipeline.sparse_attn_lane(q, ckv, idx.numpy(), kv, kv_off, ent_off, qp, n_win, sc,
+                                           sink=None if sink is None else sink.numpy(), rope_dims=rope,
+                                           rope_base=base)
+    else:
+        max_e = max(n // m for n in lengths)
+        csl.hca_attn_decode(dev(q), dev(ckv), dev(kv), dev(kv_off), dev(ent_off), dev(qp), m, n_win, out, lse=lse,
+                            scale=sc, max_entries=max_e, sink=dev(sink), rope_dims=rope, rope_base=base)
+        torch.cuda.synchronize()
+        ro, rl = pipeline.hca_attn_lane(q, ckv, kv, kv_off, ent_off, qp, m, n_win, sc,
+                                        sink=None if sink is None else sink.numpy(), rope_dims=rope, rope_base=base)
+    assert_attn_close(f64(out), ro, "out")
+    assert_attn_close(f64(lse), rl, "lse")
+
+
+def test_attention_extras_on_empty_sets(csl):
+    """A row that sees nothing: output 0 and lse equal to each head's sink logit."""
+    H, k = 16, 64
+    lengths = [1000, 1000]
+    kv, ckv, q, kv_off, ent_off, qp = _attn_inputs(lengths, 4, H, 1, [1000, 1000], 78)
+    idx = torch.full((2, 1, k), -1, dtype=torch.int32)
+    sink = W.normal_f32(78, W.S_EXTRA + 7, (H,), std=2.0)
+    out = torch.full((2, 1, H, 128), float("nan"), device="cuda")
+    lse = torch.full((2, 1, H), float("nan"), device="cuda")
+    csl.sparse_attn_decode(dev(q), dev(ckv), dev(idx), dev(kv), dev(kv_off), dev(ent_off), dev(qp), 0, out, lse=lse,
+                           sink=dev(sink), rope_dims=64)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0)
+    # the kernel keeps logits in base 2 (a log2(e) prescale, then ln 2 back): a few ulps
+    torch.testing.assert_close(lse.cpu(), sink.view(1, 1, H).expand(2, 1, H), rtol=1e-6, atol=1e-6)
+
+
+def test_attention_extras_argument_errors(csl):
+    lengths = [256]
+    kv, ckv, q, kv_off, ent_off, qp = _attn_inputs(lengths, 4, 16, 1, [256], 79)
+    idx = torch.zeros((1, 1, 8), dtype=torch.int32, device="cuda")
+    out = torch.full((1, 1, 16, 128), float("nan"), device="cuda")
+    for kw, status in (({"rope_dims": 48}, 2), ({"rope_dims": 32}, 2), ({"rope_dims": 64, "rope_base": 1.0}, 1),
+                       ({"rope_dims": -32}, 1), ({"rope_dims": 64, "rope_base": float("inf")}, 1)):
+        with pytest.raises(csl.CslError) as e:
+            csl.sparse_attn_decode(dev(q), dev(ckv), idx, dev(kv), dev(kv_off), dev(ent_off), dev(qp), 0, out, **kw)
+        assert e.value.status == status, kw
+    torch.cuda.synchronize()
+    assert torch.isnan(out).all()
+
+
 def test_calls_are_deterministic(csl):
     lane = W.Lane("csa", (200000,), (200000,), T=1, H=64, m=4, k=1024, HI=8)
     li = synth.generate(W.Workload("det", 5, (lane,)), parts=("qI", "kI", "w")).lanes[0]

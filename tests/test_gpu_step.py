@@ -26,12 +26,30 @@ pytestmark = pytest.mark.gpu
     ((65536,), 16, True, 128, 8, False, 16, True),                 # m = 16: its own launch
 ])
 def test_csa_decode_step_matches_separate_calls(lengths, m, has_z, k, HI, fp8, H, overlap):
+    _step_vs_calls(lengths, m, has_z, k, HI, fp8, H, overlap, extras=False)
+
+
+@pytest.mark.parametrize("lengths,m,k,H,overlap", [
+    ((600000, 300000, 4000), 4, 1024, 64, False),
+    ((600000, 4), 4, 1024, 64, True),
+    ((4096,), 4, 64, 16, False),
+])
+def test_csa_decode_step_with_sink_and_rope_matches_separate_calls(lengths, m, k, H, overlap):
+    """The step forwards the attention extras (per-head sink, partial RoPE) unchanged."""
+    _step_vs_calls(lengths, m, True, k, 8, False, H, overlap, extras=True)
+
+
+def _step_vs_calls(lengths, m, has_z, k, HI, fp8, H, overlap, extras):
     from compressed_sparse_long_amd import lanes
-    print(f"step lengths={lengths} m={m} z={has_z} k={k} HI={HI} fp8={fp8} H={H} overlap={overlap}", flush=True)
+    print(f"step lengths={lengths} m={m} z={has_z} k={k} HI={HI} fp8={fp8} H={H} overlap={overlap} "
+          f"extras={extras}", flush=True)
     lane = W.Lane("csa", tuple(lengths), tuple(lengths), T=1, H=H, m=m, k=k, HI=HI, kI_fp8=fp8)
     parts = ("kv", "z", "q", "qI", "kI", "w") + (("kv_b", "z_b") if overlap else ())
     inp = synth.generate(W.Workload("step", 11 + m, (lane,), z_present=has_z), parts=parts)
     (cl,) = lanes.build_lanes(inp)
+    if extras:
+        cl.sink = W.normal_f32(11 + m, W.S_EXTRA + 7, (H,), std=2.0).cuda()
+        cl.rope_dims, cl.rope_base = 64, 10000.0
     cl.compress_all()
     E = lane.entries
     newest = [(int(cl.ent_off[b]) + int(cl.first_new[b]), int(cl.ent_off[b]) + E[b]) for b in range(lane.B)]

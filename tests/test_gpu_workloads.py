@@ -51,10 +51,11 @@ def _oracle_overlap_entries(kv_a, z_a, kv_b, z_b, row0, m, ids):
     return out
 
 
-def _oracle_attention(q_bt, kv, z, lane, b, p, sel, scale, entries_fn=None):
+def _oracle_attention(q_bt, kv, z, lane, b, p, sel, scale, entries_fn=None, extras=None):
     """Oracle attention of one query row: its selected entries (oracle-compressed, in the bf16
     cache format) followed by the raw window rows. ``entries_fn(row0, m, ids)`` gives the
-    compressed entries (default: single-series compression of kv, z)."""
+    compressed entries (default: single-series compression of kv, z); ``extras`` is
+    (sink, rope_dims, rope_base) or None."""
     row0 = lane.kv_off()[b]
     n_b = lane.lengths[b]
     if entries_fn is None:
@@ -63,7 +64,10 @@ def _oracle_attention(q_bt, kv, z, lane, b, p, sel, scale, entries_fn=None):
     win = list(csa.window_rows(p, n_b, lane.W))
     wrows = f64(kv[row0 + win[0]: row0 + win[-1] + 1]) if win else np.zeros((0, kv.shape[1]))
     X = np.concatenate([comp, wrows], axis=0)
-    return csa.attend(f64(q_bt), X, scale)
+    if extras is None:
+        return csa.attend(f64(q_bt), X, scale)
+    sink, rope_dims, rope_base = extras
+    return csa.attend_at(f64(q_bt), X, scale, p, sink, rope_dims, rope_base)
 
 
 def _check_compressed_sample(cl, kv, z, lane, nsample, seed, entries_fn=None):
@@ -82,7 +86,7 @@ def _check_compressed_sample(cl, kv, z, lane, nsample, seed, entries_fn=None):
         assert_rows_close(got, ref, bf16=True, what=f"compressed entries of seq {b}")
 
 
-def _check_csa_row(cl, inp, li, b, t, keys_f64, entries_fn=None):
+def _check_csa_row(cl, inp, li, b, t, keys_f64, entries_fn=None, extras=None):
     lane = li.lane
     p = lane.q_pos[b] + t
     E = lane.entries[b]
@@ -95,7 +99,8 @@ def _check_csa_row(cl, inp, li, b, t, keys_f64, entries_fn=None):
     same = topk_band_check(got_idx, ref_s, lane.k, what=f"top-k b={b} t={t}")
     ref_sel = csa.topk(ref_s, lane.k)
     ref_sel = ref_sel[ref_sel >= 0]
-    ro, rl = _oracle_attention(inp.q[li.q_slice][b, t], inp.kv, inp.z, lane, b, p, ref_sel, cl.scale, entries_fn)
+    ro, rl = _oracle_attention(inp.q[li.q_slice][b, t], inp.kv, inp.z, lane, b, p, ref_sel, cl.scale, entries_fn,
+                               extras)
     go, gl = f64(cl.out[b, t]), f64(cl.lse[b, t])
     if same:
         assert_attn_close(go, ro, f"out b={b} t={t}")
@@ -110,13 +115,17 @@ def _csa_keys(li):
     return pipeline.index_keys_f64(li.kI, li.k_scale, li.scale_off, li.ent_off, li.lane.scale_group)
 
 
-def _run(lanes_mod, name, overlap=False):
-    print(f"workload {name}{' (overlapped compression)' if overlap else ''}: generating inputs", flush=True)
+def _run(lanes_mod, name, overlap=False, extras=None):
+    print(f"workload {name}{' (overlapped compression)' if overlap else ''}"
+          f"{' (sink, rope)' if extras else ''}: generating inputs", flush=True)
     parts = ("kv", "z", "q", "qI", "kI", "w") + (("kv_b", "z_b") if overlap else ())
     inp = synth.generate(name, parts=parts)
     print(f"workload {name}: running on the GPU", flush=True)
     cls = lanes_mod.build_lanes(inp)
     for cl in cls:
+        if extras is not None:
+            cl.sink = extras[0].to(cl.q.device)
+            cl.rope_dims, cl.rope_base = extras[1], extras[2]
         cl.compress_all()
         cl.step()
     torch.cuda.synchronize()
@@ -162,6 +171,11 @@ def _overlap_fn(inp):
     return lambda r0, m, ids: _oracle_overlap_entries(inp.kv, inp.z, inp.kv_b, inp.z_b, r0, m, ids)
 
 
+def _sink(H, seed):
+    import synth.workloads as W
+    return W.normal_f32(seed, W.S_EXTRA + 7, (H,), std=2.0)
+
+
 def test_csa_decode_4k_overlapped(lanes_mod):
     """The small CSA workload with overlapped (dual-series) compression: every compressed
     entry, then the step's scores, selection and attention over those entries."""
@@ -172,15 +186,32 @@ def test_csa_decode_4k_overlapped(lanes_mod):
     _check_csa_row(cl, inp, li, 0, 0, _csa_keys(li), _overlap_fn(inp))
 
 
-def test_csa_decode_1m_overlapped(lanes_mod):
-    """4 x 1M-token CSA decode with overlapped compression, in the launch configuration the
-    benchmark times for it: sampled entries of the bulk pass, then every query row."""
-    inp, (cl,) = _run(lanes_mod, "csa_decode_1m", overlap=True)
+def test_csa_decode_1m_overlapped_with_sink_and_rope(lanes_mod):
+    """4 x 1M-token CSA decode with every option of the method: overlapped compression, a
+    per-head attention sink and partial RoPE on the last 64 dims (query at p, output at -p).
+    Sampled entries of the bulk pass, then every query row."""
+    inp, (cl,) = _run(lanes_mod, "csa_decode_1m", overlap=True,
+                      extras=(_sink(64, 8), 64, 10000.0))
     li = inp.lanes[0]
     _check_compressed_sample(cl, inp.kv, inp.z, li.lane, 1024, 5, _overlap_fn(inp))
     keys = _csa_keys(li)
+    ex = (_sink(64, 8).numpy(), 64, 10000.0)
     for b in range(li.lane.B):
-        _check_csa_row(cl, inp, li, b, 0, keys, _overlap_fn(inp))
+        _check_csa_row(cl, inp, li, b, 0, keys, _overlap_fn(inp), ex)
+
+
+def test_hca_decode_128k_with_sink_and_rope(lanes_mod):
+    """The HCA workload with a per-head sink and partial RoPE."""
+    inp, (cl,) = _run(lanes_mod, "hca_decode_128k", extras=(_sink(64, 9), 64, 10000.0))
+    li = inp.lanes[0]
+    lane = li.lane
+    ex = (_sink(64, 9).numpy(), 64, 10000.0)
+    for b in range(lane.B):
+        p = lane.q_pos[b]
+        nv = csa.n_visible(p, lane.m, lane.entries[b])
+        ro, rl = _oracle_attention(inp.q[b, 0], inp.kv, inp.z, lane, b, p, np.arange(nv), cl.scale, None, ex)
+        assert_attn_close(f64(cl.out[b, 0]), ro, f"out b={b}")
+        assert_attn_close(f64(cl.lse[b, 0]), rl, f"lse b={b}")
 
 
 def test_csa_prefill_8k_on_128k(lanes_mod):
