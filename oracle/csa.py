@@ -52,6 +52,42 @@ def decode_e4m3(codes) -> np.ndarray:
     return np.where((e == 15) & (f == 7), np.nan, out)
 
 
+def decode_e2m1(codes) -> np.ndarray:
+    """Value of 4-bit E2M1 codes (1 sign bit, 2 exponent bits with bias 1, 1 mantissa bit;
+    exponent 0 is subnormal: m * 0.5; no infinities or NaN), the element format of OCP MXFP4.
+
+    The pages run the indexer in FP4 ([P1] section 2, footnote 3; section 4.2: FP4 dot
+    products; [P2] 'Where It Breaks': the FP4 QK indexer); the format is the published
+    OCP microscaling definition.
+    """
+    c = np.asarray(codes, dtype=np.int64) & 0xF
+    sgn = np.where(c >> 3, -1.0, 1.0)
+    e = (c >> 1) & 0x3
+    mbit = c & 0x1
+    val = np.where(e == 0, mbit * 0.5, (1.0 + mbit / 2.0) * np.exp2(e - 1.0))
+    return sgn * val
+
+
+def decode_e8m0(codes) -> np.ndarray:
+    """Value of 8-bit E8M0 scale codes: 2^(e - 127); e = 255 is NaN (OCP microscaling
+    shared-scale format)."""
+    e = np.asarray(codes, dtype=np.int64)
+    return np.where(e == 255, np.nan, np.exp2(e - 127.0))
+
+
+def decode_mxfp4_rows(packed, scales) -> np.ndarray:
+    """MXFP4 rows to fp64: ``packed`` uint8 [E, C/2] holds element 2j in the low nibble and
+    element 2j+1 in the high nibble of byte j; ``scales`` uint8 [E, C/32] holds one E8M0 scale
+    per block of 32 consecutive elements. value = e2m1(code) * 2^(e - 127)."""
+    pk = np.asarray(packed, dtype=np.uint8)
+    E, half = pk.shape
+    codes = np.empty((E, 2 * half), dtype=np.uint8)
+    codes[:, 0::2] = pk & 0xF
+    codes[:, 1::2] = pk >> 4
+    sc = decode_e8m0(np.asarray(scales, dtype=np.uint8))          # [E, C/32]
+    return decode_e2m1(codes) * np.repeat(sc, 32, axis=1)
+
+
 def to_bf16_f64(x) -> np.ndarray:
     """Round fp64 values to the nearest bfloat16 (8 significant bits, ties to even), as fp64.
 

@@ -44,8 +44,13 @@ def compress_overlap_lane(kv_a, z_a, kv_b, z_b, kv_off, m: int) -> np.ndarray:
     return np.concatenate(out, axis=0) if out else np.zeros((0, 0))
 
 
-def index_keys_f64(kI, k_scale=None, scale_off=None, ent_off=None, group: int = 64) -> np.ndarray:
-    """Indexer keys as fp64; fp8 codes are decoded and multiplied by their group's scale."""
+def index_keys_f64(kI, k_scale=None, scale_off=None, ent_off=None, group: int = 64, fp4: bool = False) -> np.ndarray:
+    """Indexer keys as fp64; fp8 codes are decoded and multiplied by their group's scale;
+    MXFP4 keys (``fp4``: packed codes [E, 32] and E8M0 scales [E, 2]) are decoded per block."""
+    if fp4:
+        pk = kI.numpy() if hasattr(kI, "numpy") else kI
+        sc = k_scale.numpy() if hasattr(k_scale, "numpy") else k_scale
+        return csa.decode_mxfp4_rows(pk, sc)
     if k_scale is None:
         return f64(kI)
     codes = np.asarray(kI.numpy() if hasattr(kI, "numpy") else kI, dtype=np.uint8)

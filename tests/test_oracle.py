@@ -247,6 +247,46 @@ def test_e4m3_decode_matches_torch_for_all_codes():
     assert np.isnan(got[0x7F]) and np.isnan(got[0xFF]) and got[0x80] == 0.0
 
 
+def test_e2m1_decode_table_and_e4m3_reencoding():
+    """The 16 E2M1 codes give +-{0, 0.5, 1, 1.5, 2, 3, 4, 6} (OCP MXFP4 element table), and
+    each equals the E4M3 value of the same sign, exponent (rebiased 1 -> 7) and mantissa
+    bit, decoded by the torch-pinned E4M3 path."""
+    got = csa.decode_e2m1(np.arange(16))
+    np.testing.assert_array_equal(got[:8], [0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    np.testing.assert_array_equal(got[8:], -got[:8])
+    for c in range(16):
+        sgn, e, mb = c >> 3, (c >> 1) & 3, c & 1
+        if e == 0:
+            ref = (-1) ** sgn * mb * 0.5
+        else:
+            e4 = (sgn << 7) | ((e - 1 + 7) << 3) | (mb << 2)
+            ref = csa.decode_e4m3(np.array([e4], dtype=np.uint8))[0]
+        assert got[c] == ref, c
+
+
+def test_e8m0_decode_matches_torch_for_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    got = csa.decode_e8m0(codes)
+    np.testing.assert_array_equal(got[:255], ref[:255])
+    assert np.isnan(got[255]) and np.isnan(ref[255]) and got[127] == 1.0
+
+
+def test_mxfp4_rows_elementwise():
+    """Packed rows decode element by element: element i comes from nibble i % 2 of byte
+    i // 2 and is scaled by block i // 32's E8M0 scale."""
+    r = _rng(40)
+    pk = r.integers(0, 256, size=(5, 32)).astype(np.uint8)
+    sc = r.integers(100, 150, size=(5, 2)).astype(np.uint8)
+    got = csa.decode_mxfp4_rows(pk, sc)
+    table = [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+    for e in range(5):
+        for i in range(64):
+            code = (int(pk[e, i // 2]) >> (4 * (i % 2))) & 0xF
+            v = (-1 if code & 8 else 1) * table[code & 7] * 2.0 ** (int(sc[e, i // 32]) - 127)
+            assert got[e, i] == v
+
+
 def test_bf16_rounding_matches_torch_on_fp32_values():
     r = _rng(6)
     x = (r.standard_normal(20000) * np.exp2(r.integers(-30, 30, 20000))).astype(np.float32)
