@@ -339,6 +339,33 @@ def main():
             cl.rope_dims = 0
             return round(t, 2)
 
+        # MXFP4 indexer keys (E2M1 codes + an E8M0 scale per 32 dims: 34 bytes per key) for
+        # the same draws: the indexer launch and the whole step, over 16 rotated key copies
+        # (570 MB, past the last-level cache)
+        import synth as SY
+        li4 = SY.generate(SW.with_lanes(inp.workload, kI_fp4=True), parts=("kI",)).lanes[0]
+        saved = (cl.kI_copies, cl.k_scale_copies, cl.k_format)
+        n4 = 16
+        cl.kI_copies = [li4.kI.cuda()] + [None] * (n4 - 1)
+        cl.k_scale_copies = [li4.k_scale.cuda()] + [None] * (n4 - 1)
+        for i in range(1, n4):
+            cl.kI_copies[i] = cl.kI_copies[0].clone()
+            cl.k_scale_copies[i] = cl.k_scale_copies[0].clone()
+        cl.k_format = "mxfp4"
+        g4 = capture(lambda: [cl.index(i) for i in range(n4 * 4)])
+        t4 = time_graphs([g4], 4, per_replay=n4 * 4)
+        cl.select()
+        torch.cuda.synchronize()
+        g4s = capture(lambda: [cl.step(i) for i in range(n4)])
+        t4s = time_graphs([g4s], max(1, 400 // n4), per_replay=n4)
+        b4 = B * (E * (CI // 2 + CI // 32) + E * 4 + HI * CI * 2 + HI * 4)
+        result["mxfp4_keys"] = {"indexer_us": round(t4, 2), "bytes_per_launch": b4,
+                                "GB_s": round(b4 / (t4 * 1e-6) / 1e9, 1),
+                                "frac": round(b4 / (t4 * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                "step_us": round(t4s, 2), "queries_per_s": round(B / (t4s * 1e-6), 1)}
+        cl.kI_copies, cl.k_scale_copies, cl.k_format = saved
+        del g4, g4s
+
         result["options_step_us"] = {"plain": round(ms_step * 1e3, 2),
                                      "overlap": options_step(True, False),
                                      "sink_rope64": options_step(False, True),

@@ -20,7 +20,7 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsl.so")
 
-BF16, F32, FP8_E4M3 = 0, 1, 2
+BF16, F32, FP8_E4M3, MXFP4 = 0, 1, 2, 3
 EXPORTS = [
     "csl_last_error", "csl_version", "csl_compress_kv", "csl_compress_kv_overlap", "csl_indexer_scores",
     "csl_topk_workspace_bytes", "csl_topk_select", "csl_attn_workspace_bytes",
@@ -159,22 +159,32 @@ def compress_kv_overlap(kv_a, z_a, kv_b, z_b, kv_off, ent_off, m: int, out, firs
     return out
 
 
-def indexer_scores(qI, w, kI, ent_off, q_pos, m: int, scores, max_entries: int | None = None, k_scale=None,
-                   scale_off=None, scale_group: int = 64, topk_ws=None, topk_k: int = 0, stream=None):
-    """Lightning-indexer scores into scores fp32 [B, T, ld]; with ``topk_ws``/``topk_k`` it also
-    leaves top-k candidate lists for ``topk_select(..., prepared=True)``; see csl.h."""
-    B, T, HI, CI = qI.shape
+def _key_format(kI, k_format):
+    """C key dtype and the accepted k_scale dtypes for indexer keys ``kI``."""
+    if k_format == "mxfp4":
+        if kI.dtype != torch.uint8:
+            raise ValueError("MXFP4 keys are packed uint8 codes [E, CI/2]")
+        return MXFP4, (torch.uint8,)
     if kI.dtype == torch.bfloat16:
-        kd = BF16
-    elif kI.dtype in (torch.uint8, torch.float8_e4m3fn):
-        kd = FP8_E4M3
-    else:
-        raise ValueError("kI must be bfloat16 or fp8 e4m3 (uint8 codes)")
+        return BF16, _F32
+    if kI.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return FP8_E4M3, _F32
+    raise ValueError("kI must be bfloat16, fp8 e4m3 (uint8 codes) or, with k_format='mxfp4', packed MXFP4")
+
+
+def indexer_scores(qI, w, kI, ent_off, q_pos, m: int, scores, max_entries: int | None = None, k_scale=None,
+                   scale_off=None, scale_group: int = 64, topk_ws=None, topk_k: int = 0, k_format=None,
+                   stream=None):
+    """Lightning-indexer scores into scores fp32 [B, T, ld]; with ``topk_ws``/``topk_k`` it also
+    leaves top-k candidate lists for ``topk_select(..., prepared=True)``. ``k_format='mxfp4'``
+    takes packed E2M1 keys with their E8M0 scales in ``k_scale``; see csl.h."""
+    B, T, HI, CI = qI.shape
+    kd, sdt = _key_format(kI, k_format)
     ld = scores.shape[-1]
     if max_entries is None:
         max_entries = ld
     _check(_lib.csl_indexer_scores(
-        _ptr(qI, "qI", _BF16), _ptr(w, "w", _F32), _ptr(kI, "kI"), kd, _ptr(k_scale, "k_scale", _F32),
+        _ptr(qI, "qI", _BF16), _ptr(w, "w", _F32), _ptr(kI, "kI"), kd, _ptr(k_scale, "k_scale", sdt),
         _ptr(scale_off, "scale_off", _I64), int(scale_group), _ptr(ent_off, "ent_off", _I64),
         _ptr(q_pos, "q_pos", _I64), int(m), B, T, HI, CI, int(max_entries), _ptr(scores, "scores", _F32), ld,
         _ptr(topk_ws, "topk_ws"), 0 if topk_ws is None else topk_ws.numel() * topk_ws.element_size(), int(topk_k),
@@ -267,18 +277,13 @@ def csa_decode_step(kv, z, kv_off, ent_off, first_entry, max_new_entries: int, c
                     k: int, idx, q, n_win: int, out, q_pos, m: int, lse=None, scale: float | None = None,
                     k_scale=None, scale_off=None, scale_group: int = 64, max_entries: int | None = None,
                     attn_ws=None, kv_b=None, z_b=None, sink=None, rope_dims: int = 0, rope_base: float = 10000.0,
-                    stream=None):
+                    k_format=None, stream=None):
     """One whole CSA step (compress_kv of the newest entries into ckv, or compress_kv_overlap
     when series b ``kv_b``/``z_b`` is given, indexer_scores with candidate lists, topk_select,
     sparse_attn_decode) in one C call; see csl.h."""
     B, T, HI, CI = qI.shape
     H, D = q.shape[2], q.shape[3]
-    if kI.dtype == torch.bfloat16:
-        kd = BF16
-    elif kI.dtype in (torch.uint8, torch.float8_e4m3fn):
-        kd = FP8_E4M3
-    else:
-        raise ValueError("kI must be bfloat16 or fp8 e4m3 (uint8 codes)")
+    kd, sdt = _key_format(kI, k_format)
     ld = scores.shape[-1]
     if max_entries is None:
         max_entries = ld
@@ -290,7 +295,7 @@ def csa_decode_step(kv, z, kv_off, ent_off, first_entry, max_new_entries: int, c
         ent_off=_ptr(ent_off, "ent_off", _I64), first_entry=_ptr(first_entry, "first_entry", _I64),
         max_new_entries=int(max_new_entries), ckv=_ptr(ckv, "ckv", _BF16),
         q_idx=_ptr(qI, "qI", _BF16), w=_ptr(w, "w", _F32), k_idx=_ptr(kI, "kI"), k_dtype=kd,
-        k_scale=_ptr(k_scale, "k_scale", _F32), scale_off=_ptr(scale_off, "scale_off", _I64),
+        k_scale=_ptr(k_scale, "k_scale", sdt), scale_off=_ptr(scale_off, "scale_off", _I64),
         scale_group=int(scale_group), HI=HI, CI=CI, scores=_ptr(scores, "scores", _F32), ld=ld,
         topk_ws=_ptr(topk_ws, "topk_ws"), topk_ws_bytes=_nbytes(topk_ws),
         k=int(k), idx=_ptr(idx, "idx", (torch.int32,)),

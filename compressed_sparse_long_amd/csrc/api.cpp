@@ -79,8 +79,13 @@ int check_series_b(const void* kv_b, const void* z_a, const void* z_b, const cha
   return CSL_OK;
 }
 
+// the launcher's key type: 0 bf16, 1 fp8 e4m3, 2 MXFP4
+int key_type(int k_dtype) {
+  return k_dtype == CSL_DTYPE_FP8_E4M3 ? 1 : k_dtype == CSL_DTYPE_MXFP4 ? 2 : 0;
+}
+
 // topk_ws is cleared when the shapes need no candidate lists
-int check_indexer(const void* q_idx, const float* w, const void* k_idx, int k_dtype, const float* k_scale,
+int check_indexer(const void* q_idx, const float* w, const void* k_idx, int k_dtype, const void* k_scale,
                   const int64_t* scale_off, int scale_group, const int64_t* ent_off, const int64_t* q_pos, int m, int B,
                   int T, int HI, int CI, int64_t max_entries, const float* scores, int64_t ld, void*& topk_ws,
                   size_t topk_ws_bytes, int topk_k) {
@@ -88,19 +93,22 @@ int check_indexer(const void* q_idx, const float* w, const void* k_idx, int k_dt
   if (!q_idx || !w || !k_idx || !ent_off || !q_pos || !scores)
     return fail(CSL_ERR_INVALID, "indexer_scores: null pointer argument");
   if (m < 1) return fail(CSL_ERR_INVALID, "indexer_scores: m must be >= 1");
-  if (k_dtype != CSL_DTYPE_BF16 && k_dtype != CSL_DTYPE_FP8_E4M3)
-    return fail(CSL_ERR_UNSUPPORTED, "indexer_scores: k_dtype must be BF16 or FP8_E4M3");
+  if (k_dtype != CSL_DTYPE_BF16 && k_dtype != CSL_DTYPE_FP8_E4M3 && k_dtype != CSL_DTYPE_MXFP4)
+    return fail(CSL_ERR_UNSUPPORTED, "indexer_scores: k_dtype must be BF16, FP8_E4M3 or MXFP4");
   const bool fp8 = k_dtype == CSL_DTYPE_FP8_E4M3;
+  const bool fp4 = k_dtype == CSL_DTYPE_MXFP4;
   if (fp8 && (!k_scale || !scale_off || scale_group < 1))
     return fail(CSL_ERR_INVALID, "indexer_scores: fp8 keys need k_scale, scale_off and scale_group >= 1");
+  if (fp4 && !k_scale) return fail(CSL_ERR_INVALID, "indexer_scores: MXFP4 keys need their E8M0 scales in k_scale");
   if (HI != 1 && HI != 2 && HI != 4 && HI != 8 && HI != 16)
     return fail(CSL_ERR_UNSUPPORTED, "indexer_scores: HI must be 1, 2, 4, 8 or 16, got %d", HI);
   if (CI != 64) return fail(CSL_ERR_UNSUPPORTED, "indexer_scores: CI must be 64, got %d", CI);
   if (ld < max_entries) return fail(CSL_ERR_INVALID, "indexer_scores: ld (%lld) < max_entries (%lld)",
                                     (long long)ld, (long long)max_entries);
   if (B > kMaxGridY) return fail(CSL_ERR_UNSUPPORTED, "indexer_scores: B must be <= %d", kMaxGridY);
-  if (!aligned(q_idx, 16) || !aligned(k_idx, fp8 ? 8 : 16))
-    return fail(CSL_ERR_INVALID, "indexer_scores: q_idx must be 16-byte and k_idx %d-byte aligned", fp8 ? 8 : 16);
+  const int kalign = (fp8 || fp4) ? 8 : 16;
+  if (!aligned(q_idx, 16) || !aligned(k_idx, kalign))
+    return fail(CSL_ERR_INVALID, "indexer_scores: q_idx must be 16-byte and k_idx %d-byte aligned", kalign);
   if (topk_ws) {
     if (topk_k < 1 || topk_k > csl::topk_max_k())
       return fail(CSL_ERR_UNSUPPORTED, "indexer_scores: topk_k must be in [1, %d], got %d", csl::topk_max_k(), topk_k);
@@ -165,7 +173,7 @@ int csl_compress_kv_overlap(const void* kv_a, const void* z_a, const void* kv_b,
                     "compress_kv_overlap launch");
 }
 
-int csl_indexer_scores(const void* q_idx, const float* w, const void* k_idx, int k_dtype, const float* k_scale,
+int csl_indexer_scores(const void* q_idx, const float* w, const void* k_idx, int k_dtype, const void* k_scale,
                        const int64_t* scale_off, int scale_group, const int64_t* ent_off, const int64_t* q_pos, int m,
                        int B, int T, int HI, int CI, int64_t max_entries, float* scores, int64_t ld, void* topk_ws,
                        size_t topk_ws_bytes, int topk_k, void* stream) {
@@ -173,7 +181,7 @@ int csl_indexer_scores(const void* q_idx, const float* w, const void* k_idx, int
                                CI, max_entries, scores, ld, topk_ws, topk_ws_bytes, topk_k);
   if (st != CSL_OK) return st;
   if (B == 0 || T == 0 || max_entries == 0) return ok();
-  return hip_status(csl::launch_indexer(q_idx, w, k_idx, k_dtype == CSL_DTYPE_FP8_E4M3, k_scale, scale_off, scale_group,
+  return hip_status(csl::launch_indexer(q_idx, w, k_idx, key_type(k_dtype), k_scale, scale_off, scale_group,
                                         ent_off, q_pos, m, B, T, HI, max_entries, scores, ld, topk_ws, topk_k,
                                         as_stream(stream)),
                     "indexer_scores launch");
@@ -307,7 +315,7 @@ int csl_csa_decode_step(const csl_csa_step* s, void* stream) {
   if (st != CSL_OK) return st;
 
   const hipStream_t hs = as_stream(stream);
-  const bool fp8 = s->k_dtype == CSL_DTYPE_FP8_E4M3;
+  const int kt = key_type(s->k_dtype);
   const bool compress = s->max_new_entries > 0;
   const bool index = s->max_entries > 0;
   hipError_t e = hipSuccess;
@@ -315,7 +323,7 @@ int csl_csa_decode_step(const csl_csa_step* s, void* stream) {
     // the newest-chunk compression rides in spare workgroups of the indexer launch
     const csl::CompressJob job{s->kv, s->z, s->kv_off, s->first_entry, s->max_new_entries, s->ckv, s->m,
                                s->kv_b, s->z_b};
-    e = csl::launch_indexer(s->q_idx, s->w, s->k_idx, fp8, s->k_scale, s->scale_off, s->scale_group, s->ent_off,
+    e = csl::launch_indexer(s->q_idx, s->w, s->k_idx, kt, s->k_scale, s->scale_off, s->scale_group, s->ent_off,
                             s->q_pos, s->m, s->B, s->T, s->HI, s->max_entries, s->scores, s->ld, topk_ws, s->k, hs, &job);
   } else {
     if (compress && overlap)
@@ -325,7 +333,7 @@ int csl_csa_decode_step(const csl_csa_step* s, void* stream) {
       e = csl::launch_compress(s->kv, s->z, s->kv_off, s->ent_off, s->first_entry, s->B, s->D, s->m,
                                s->max_new_entries, s->ckv, true, hs);
     if (e == hipSuccess && index)
-      e = csl::launch_indexer(s->q_idx, s->w, s->k_idx, fp8, s->k_scale, s->scale_off, s->scale_group, s->ent_off,
+      e = csl::launch_indexer(s->q_idx, s->w, s->k_idx, kt, s->k_scale, s->scale_off, s->scale_group, s->ent_off,
                               s->q_pos, s->m, s->B, s->T, s->HI, s->max_entries, s->scores, s->ld, topk_ws, s->k, hs);
   }
   if (e != hipSuccess) return hip_status(e, "csa_decode_step launch");

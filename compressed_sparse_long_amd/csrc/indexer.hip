@@ -6,8 +6,15 @@
 // It runs on the gfx950 matrix cores as 16x16x32 bf16 MFMA tiles of 16/HI query rows x HI
 // heads against 16 consecutive keys of one sequence (streamed from HBM), dot products in fp32.
 // ReLU, the head weights, the optional fp8 group scale and the head sum run on the
-// accumulator registers, so each key costs 128 bytes of reads (64 for fp8) and 4 bytes
-// of score write per query row.
+// accumulator registers, so each key costs 128 bytes of reads (64 for fp8, 34 for MXFP4)
+// and 4 bytes of score write per query row.
+//
+// Key formats: bf16; fp8 e4m3 codes with an fp32 scale per group of entries (widened to
+// bf16 in registers, the scale applied to the score); MXFP4 ([P1] section 4.2 and [P2]
+// "Where It Breaks": an FP4 indexer), E2M1 codes with an E8M0 scale per 32 dims, widened
+// and scaled to bf16 exactly by gfx950's scaled fp4 conversion. For MXFP4 a lane holds 16
+// consecutive dims of a key (one scale block) and the query operand takes the same
+// k-slot order, which only has to agree between the two operands.
 //
 // Two tilings:
 //   decode  (indexer_decode_kernel): 8 waves per workgroup, each with one pass over its own
@@ -29,40 +36,68 @@ namespace csl {
 
 namespace {
 
-template <bool FP8>
-__device__ __forceinline__ void load_key_tile(const void* __restrict__ kI, int64_t row, bool ok, int g,
-                                              u32x4& k0, u32x4& k1) {
+enum { kKeyBF16 = 0, kKeyFP8 = 1, kKeyFP4 = 2 };
+
+// first dim of the 8 k-slots that lane group g supplies for MFMA kk (the key and query
+// operands share this order)
+template <int KT>
+__device__ __forceinline__ int kslot_dim(int kk, int g) {
+  return KT == kKeyFP4 ? g * 16 + kk * 8 : kk * 32 + g * 8;
+}
+
+// One lane's share of a key row for both MFMAs (raw codes; key_operand widens them).
+// MXFP4: 8 bytes = dims 16g..16g+15 (block g / 2) plus that block's E8M0 scale byte.
+template <int KT>
+__device__ __forceinline__ void load_key_tile(const void* __restrict__ kI, const uint8_t* __restrict__ k_mx,
+                                              int64_t row, bool ok, int g, u32x4& k0, u32x4& k1) {
   if (!ok) {
     k0 = u32x4{0, 0, 0, 0};
     k1 = u32x4{0, 0, 0, 0};
     return;
   }
-  if (!FP8) {
+  if (KT == kKeyBF16) {
     const uint16_t* p = static_cast<const uint16_t*>(kI) + row * 64 + g * 8;
     k0 = *reinterpret_cast<const u32x4*>(p);
     k1 = *reinterpret_cast<const u32x4*>(p + 32);
-  } else {
+  } else if (KT == kKeyFP8) {
     const uint8_t* p = static_cast<const uint8_t*>(kI) + row * 64 + g * 8;
     const u32x2 c0 = *reinterpret_cast<const u32x2*>(p);
     const u32x2 c1 = *reinterpret_cast<const u32x2*>(p + 32);
     // keep the raw codes; they are widened to bf16 just before the MFMA
     k0 = u32x4{c0.x, c0.y, 0, 0};
     k1 = u32x4{c1.x, c1.y, 0, 0};
+  } else {
+    const u32x2 c = *reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(kI) + row * 32 + g * 8);
+    const uint32_t e = k_mx[row * 2 + (g >> 1)];
+    k0 = u32x4{c.x, e, 0, 0};
+    k1 = u32x4{c.y, e, 0, 0};
   }
 }
 
-template <bool FP8>
+template <int KT>
 __device__ __forceinline__ bf16x8 key_operand(const u32x4& k) {
-  if (!FP8) return as_bf16x8(k);
-  const u32x2 lo = e4m3x4_to_bf16x4(k.x);
-  const u32x2 hi = e4m3x4_to_bf16x4(k.y);
-  return as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
+  if (KT == kKeyBF16) return as_bf16x8(k);
+  if (KT == kKeyFP8) {
+    const u32x2 lo = e4m3x4_to_bf16x4(k.x);
+    const u32x2 hi = e4m3x4_to_bf16x4(k.y);
+    return as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
+  }
+  // 8 E2M1 codes (byte j: dims 2j, 2j + 1 in its low and high nibble) times 2^(e - 127),
+  // exact in bf16; a zero exponent byte gives the float 2^-127 (subnormal)
+  const float sc = k.y ? __uint_as_float(k.y << 23) : __uint_as_float(0x00400000u);
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t r0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(k.x, sc, 0);
+  const bf16x2_t r1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(k.x, sc, 1);
+  const bf16x2_t r2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(k.x, sc, 2);
+  const bf16x2_t r3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(k.x, sc, 3);
+  return as_bf16x8(u32x4{__builtin_bit_cast(uint32_t, r0), __builtin_bit_cast(uint32_t, r1),
+                         __builtin_bit_cast(uint32_t, r2), __builtin_bit_cast(uint32_t, r3)});
 }
 
-template <int HI, int NB, int NWAVES, int WQ, int U, bool FP8>
+template <int HI, int NB, int NWAVES, int WQ, int U, int KT>
 __global__ __launch_bounds__(NWAVES * 64) void indexer_kernel(
     const uint16_t* __restrict__ qI, const float* __restrict__ w, const void* __restrict__ kI,
-    const float* __restrict__ k_scale, const int64_t* __restrict__ scale_off, int scale_group,
+    const void* __restrict__ k_scale_v, const int64_t* __restrict__ scale_off, int scale_group,
     const int64_t* __restrict__ ent_off, const int64_t* __restrict__ q_pos, int m, int T,
     int64_t max_entries, float* __restrict__ scores, int64_t ld, int epw) {
   constexpr int QPB = 16 / HI;       // query rows per A tile
@@ -80,6 +115,9 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_kernel(
 
   const int t0 = (blockIdx.y * WQ + wq) * QPW;
   if (t0 >= T) return;
+  constexpr bool FP8 = KT == kKeyFP8;
+  const float* k_scale = static_cast<const float*>(k_scale_v);          // fp8: per entry group
+  const uint8_t* k_mx = static_cast<const uint8_t*>(k_scale_v);         // MXFP4: E8M0 per block
 
   const int64_t e_base = ent_off[b];
   const int64_t n_ent = ent_off[b + 1] - e_base;
@@ -111,7 +149,7 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_kernel(
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       u32x4 v = u32x4{0, 0, 0, 0};
-      if (t < T) v = *reinterpret_cast<const u32x4*>(qI + (((int64_t)b * T + t) * HI + j) * 64 + kk * 32 + g * 8);
+      if (t < T) v = *reinterpret_cast<const u32x4*>(qI + (((int64_t)b * T + t) * HI + j) * 64 + kslot_dim<KT>(kk, g));
       a[nb][kk] = as_bf16x8(v);
     }
 #pragma unroll
@@ -136,15 +174,15 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_kernel(
     for (int u = 0; u < U; ++u) {
       const int64_t s = s0 + u * 16 + c;
       const bool ok = s < e_end;
-      load_key_tile<FP8>(kI, e_base + s, ok, g, kb[u][0], kb[u][1]);
+      load_key_tile<KT>(kI, k_mx, e_base + s, ok, g, kb[u][0], kb[u][1]);
       if (FP8) sc[u] = ok ? k_scale[scale_off[b] + s / scale_group] : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t s = s0 + u * 16 + c;
       if (s0 + u * 16 >= e_end) break;
-      const bf16x8 b0 = key_operand<FP8>(kb[u][0]);
-      const bf16x8 b1 = key_operand<FP8>(kb[u][1]);
+      const bf16x8 b0 = key_operand<KT>(kb[u][0]);
+      const bf16x8 b1 = key_operand<KT>(kb[u][1]);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -210,18 +248,18 @@ __device__ __forceinline__ float head_sum(float v) {
 constexpr int kJobRS = 4;
 constexpr int kJobEntriesPerBlock = kSlice / (16 * kJobRS);
 
-template <int HI, bool FP8, bool PREP>
+template <int HI, int KT, bool PREP>
 __global__ __launch_bounds__(kSlice) void indexer_decode_kernel(
     const uint16_t* __restrict__ qI, const float* __restrict__ w, const void* __restrict__ kI,
-    const float* __restrict__ k_scale, const int64_t* __restrict__ scale_off, int scale_group,
+    const void* __restrict__ k_scale_v, const int64_t* __restrict__ scale_off, int scale_group,
     const int64_t* __restrict__ ent_off, const int64_t* __restrict__ q_pos, int m, int T,
     int64_t max_entries, float* __restrict__ scores, int64_t ld, void* topk_ws, int topk_k, int slot_budget,
     int key_blocks, CompressJob job) {
   constexpr int NW = kSlice / kWave;
+  constexpr int QPB = 16 / HI;  // query rows per tile
   constexpr int U = 4;
   constexpr int EPW = 16 * U;   // keys per wave: one per lane on the way out
   constexpr int EPB = EPW * NW; // keys per block
-  constexpr int QPB = 16 / HI;  // query rows per tile
   static_assert(EPW == kWave && EPB == kSlice, "one key per thread, one slice per block");
   __shared__ __align__(16) float sval[QPB][EPB];
   __shared__ SliceScratch sc;
@@ -260,6 +298,9 @@ __global__ __launch_bounds__(kSlice) void indexer_decode_kernel(
   const int c = lane % 16;
   const int b = blockIdx.z;
   const int t0 = blockIdx.y * QPB;
+  constexpr bool FP8 = KT == kKeyFP8;
+  const float* k_scale = static_cast<const float*>(k_scale_v);   // fp8: per entry group
+  const uint8_t* k_mx = static_cast<const uint8_t*>(k_scale_v);  // MXFP4: E8M0 per block
 
   const int64_t e_base = ent_off[b];
   const int64_t n_ent = ent_off[b + 1] - e_base;
@@ -274,7 +315,7 @@ __global__ __launch_bounds__(kSlice) void indexer_decode_kernel(
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t s = e0 + u * 16 + c;
-    load_key_tile<FP8>(kI, e_base + s, s < e_end, g, kb[u][0], kb[u][1]);
+    load_key_tile<KT>(kI, k_mx, e_base + s, s < e_end, g, kb[u][0], kb[u][1]);
   }
   float my_scale = 1.f;  // fp8 group scale of this lane's entry on the way out
   if (FP8 && e0 + lane < e_end) my_scale = k_scale[scale_off[b] + (e0 + lane) / scale_group];
@@ -285,7 +326,7 @@ __global__ __launch_bounds__(kSlice) void indexer_decode_kernel(
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     u32x4 v = u32x4{0, 0, 0, 0};
-    if (tq < T) v = *reinterpret_cast<const u32x4*>(qI + (((int64_t)b * T + tq) * HI + c % HI) * 64 + kk * 32 + g * 8);
+    if (tq < T) v = *reinterpret_cast<const u32x4*>(qI + (((int64_t)b * T + tq) * HI + c % HI) * 64 + kslot_dim<KT>(kk, g));
     qb[kk] = as_bf16x8(v);
   }
   const float wc = (tq < T) ? w[((int64_t)b * T + tq) * HI + c % HI] : 0.f;
@@ -301,8 +342,8 @@ __global__ __launch_bounds__(kSlice) void indexer_decode_kernel(
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    acc = mfma16x16x32(key_operand<FP8>(kb[u][0]), qb[0], acc);
-    acc = mfma16x16x32(key_operand<FP8>(kb[u][1]), qb[1], acc);
+    acc = mfma16x16x32(key_operand<KT>(kb[u][0]), qb[0], acc);
+    acc = mfma16x16x32(key_operand<KT>(kb[u][1]), qb[1], acc);
     float v[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = head_sum<HI>(wc * fmaxf(acc[i], 0.f));
@@ -336,8 +377,8 @@ __global__ __launch_bounds__(kSlice) void indexer_decode_kernel(
   }
 }
 
-template <int HI, bool FP8>
-hipError_t launch_hi(const void* qI, const float* w, const void* kI, const float* k_scale,
+template <int HI, int KT>
+hipError_t launch_hi(const void* qI, const float* w, const void* kI, const void* k_scale,
                      const int64_t* scale_off, int scale_group, const int64_t* ent_off,
                      const int64_t* q_pos, int m, int B, int T, int64_t max_entries, float* scores,
                      int64_t ld, void* topk_ws, int topk_k, hipStream_t st, const CompressJob* job) {
@@ -352,7 +393,7 @@ hipError_t launch_hi(const void* qI, const float* w, const void* kI, const float
     const int64_t gx = (max_entries + epw - 1) / epw;
     const int gy = (T + QPW * WQ - 1) / (QPW * WQ);
     dim3 grid((unsigned)(gx > 0 ? gx : 1), (unsigned)gy, (unsigned)B);
-    indexer_kernel<HI, NB, NW, WQ, U, FP8><<<grid, NW * 64, 0, st>>>(q16, w, kI, k_scale, scale_off, scale_group,
+    indexer_kernel<HI, NB, NW, WQ, U, KT><<<grid, NW * 64, 0, st>>>(q16, w, kI, k_scale, scale_off, scale_group,
                                                                     ent_off, q_pos, m, T, max_entries, scores, ld, epw);
   } else {
     // decode tiling: 8 waves per block, each with one pass over 64 keys (plus the job's blocks)
@@ -364,25 +405,25 @@ hipError_t launch_hi(const void* qI, const float* w, const void* kI, const float
     const CompressJob none{};
     const CompressJob& cj = job ? *job : none;
     if (prep)
-      indexer_decode_kernel<HI, FP8, true><<<grid, kSlice, 0, st>>>(q16, w, kI, k_scale, scale_off, scale_group, ent_off,
+      indexer_decode_kernel<HI, KT, true><<<grid, kSlice, 0, st>>>(q16, w, kI, k_scale, scale_off, scale_group, ent_off,
                                                                     q_pos, m, T, max_entries, scores, ld, topk_ws, topk_k,
                                                                     topk_slot_budget(max_entries, topk_k), (int)kb, cj);
     else
-      indexer_decode_kernel<HI, FP8, false><<<grid, kSlice, 0, st>>>(q16, w, kI, k_scale, scale_off, scale_group,
+      indexer_decode_kernel<HI, KT, false><<<grid, kSlice, 0, st>>>(q16, w, kI, k_scale, scale_off, scale_group,
                                                                      ent_off, q_pos, m, T, max_entries, scores, ld,
                                                                      nullptr, 0, 0, (int)kb, cj);
   }
   return hipGetLastError();
 }
 
-template <bool FP8>
-hipError_t launch_fp8(int HI, const void* qI, const float* w, const void* kI, const float* k_scale,
+template <int KT>
+hipError_t launch_kt(int HI, const void* qI, const float* w, const void* kI, const void* k_scale,
                       const int64_t* scale_off, int scale_group, const int64_t* ent_off,
                       const int64_t* q_pos, int m, int B, int T, int64_t max_entries, float* scores,
                       int64_t ld, void* topk_ws, int topk_k, hipStream_t st, const CompressJob* job) {
 #define CSL_IDX_CASE(H)                                                                                          \
   case H:                                                                                                        \
-    return launch_hi<H, FP8>(qI, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T, max_entries, \
+    return launch_hi<H, KT>(qI, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T, max_entries, \
                              scores, ld, topk_ws, topk_k, st, job);
   switch (HI) {
     CSL_IDX_CASE(1)
@@ -409,16 +450,20 @@ bool indexer_carries_compress(const void* topk_ws, int B, int T, int64_t max_ent
   return D == 128 && m >= 1 && m <= 8 && max_entries > 0 && !uses_prefill_tiling(topk_ws, B, T, max_entries);
 }
 
-hipError_t launch_indexer(const void* qI, const float* w, const void* kI, bool fp8, const float* k_scale,
+hipError_t launch_indexer(const void* qI, const float* w, const void* kI, int key_type, const void* k_scale,
                           const int64_t* scale_off, int scale_group, const int64_t* ent_off,
                           const int64_t* q_pos, int m, int B, int T, int HI, int64_t max_entries,
                           float* scores, int64_t ld, void* topk_ws, int topk_k, hipStream_t stream,
                           const CompressJob* job) {
-  if (fp8)
-    return launch_fp8<true>(HI, qI, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T, max_entries,
-                            scores, ld, topk_ws, topk_k, stream, job);
-  return launch_fp8<false>(HI, qI, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T, max_entries,
-                           scores, ld, topk_ws, topk_k, stream, job);
+#define CSL_IDX_KT(KT)                                                                                     \
+  launch_kt<KT>(HI, qI, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T, max_entries, scores, \
+                ld, topk_ws, topk_k, stream, job)
+  switch (key_type) {
+    case kKeyFP8: return CSL_IDX_KT(kKeyFP8);
+    case kKeyFP4: return CSL_IDX_KT(kKeyFP4);
+    default: return CSL_IDX_KT(kKeyBF16);
+  }
+#undef CSL_IDX_KT
 }
 
 }  // namespace csl

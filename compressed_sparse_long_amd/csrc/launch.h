@@ -32,7 +32,9 @@ struct CompressJob {
   const void* z_b = nullptr;
 };
 
-hipError_t launch_indexer(const void* qI, const float* w, const void* kI, bool fp8, const float* k_scale,
+// key_type: 0 bf16, 1 fp8 e4m3 (k_scale fp32 per scale_group entries), 2 MXFP4 (k_scale
+// E8M0 bytes, two per key row)
+hipError_t launch_indexer(const void* qI, const float* w, const void* kI, int key_type, const void* k_scale,
                           const int64_t* scale_off, int scale_group, const int64_t* ent_off,
                           const int64_t* q_pos, int m, int B, int T, int HI, int64_t max_entries,
                           float* scores, int64_t ld, void* topk_ws, int topk_k, hipStream_t stream,

@@ -83,6 +83,7 @@ class CsaLane(_Lane):
         self.k_scale = None if li.k_scale is None else li.k_scale.to(device)
         self.scale_off = None if li.scale_off is None else li.scale_off.to(device)
         self.scale_group = lane.scale_group
+        self.k_format = "mxfp4" if getattr(lane, "kI_fp4", False) else None
         self.scores = torch.empty((self.B, self.T, max(self.max_entries, 1)), dtype=torch.float32, device=device)
         self.idx = torch.empty((self.B, self.T, self.k), dtype=torch.int32, device=device)
         nb = topk_workspace_bytes(self.B, self.T, self.max_entries, self.k)
@@ -90,6 +91,7 @@ class CsaLane(_Lane):
         na = attn_workspace_bytes(self.B, self.T, self.H, lane.D, self.k + self.W)
         self.attn_ws = torch.empty(max(na, 16), dtype=torch.uint8, device=device)
         self.kI_copies = [self.kI]
+        self.k_scale_copies = [self.k_scale]
 
     def compress_all(self):
         if self.kv_b is None:
@@ -109,11 +111,16 @@ class CsaLane(_Lane):
     def rotate(self, copies: int):
         super().rotate(copies)
         self.kI_copies = [self.kI] + [self.kI.clone() for _ in range(copies - 1)]
+        # per-row MXFP4 scales are as large a stream as the keys' own share: copy them too
+        if self.k_format == "mxfp4":
+            self.k_scale_copies = [self.k_scale] + [self.k_scale.clone() for _ in range(copies - 1)]
 
     def index(self, r: int = 0):
         indexer_scores(self.qI, self.w, self.kI_copies[r % len(self.kI_copies)], self.ent_off, self.q_pos, self.m,
-                       self.scores, max_entries=self.max_entries, k_scale=self.k_scale, scale_off=self.scale_off,
-                       scale_group=self.scale_group, topk_ws=self.topk_ws if self.fused else None, topk_k=self.k)
+                       self.scores, max_entries=self.max_entries,
+                       k_scale=self.k_scale_copies[r % len(self.k_scale_copies)], scale_off=self.scale_off,
+                       scale_group=self.scale_group, topk_ws=self.topk_ws if self.fused else None, topk_k=self.k,
+                       k_format=self.k_format)
 
     def select(self):
         topk_select(self.scores, self.ent_off, self.q_pos, self.m, self.k, self.idx, ws=self.topk_ws,
@@ -137,10 +144,11 @@ class CsaLane(_Lane):
                         self.ckv_copies[r % len(self.ckv_copies)], self.qI, self.w,
                         self.kI_copies[r % len(self.kI_copies)], self.scores,
                         self.topk_ws, self.k, self.idx, self.q, self.W, self.out, self.q_pos,
-                        self.m, lse=self.lse, scale=self.scale, k_scale=self.k_scale, scale_off=self.scale_off,
+                        self.m, lse=self.lse, scale=self.scale,
+                        k_scale=self.k_scale_copies[r % len(self.k_scale_copies)], scale_off=self.scale_off,
                         scale_group=self.scale_group, max_entries=self.max_entries, attn_ws=self.attn_ws,
                         kv_b=self.kv_b, z_b=self.z_b, sink=self.sink, rope_dims=self.rope_dims,
-                        rope_base=self.rope_base)
+                        rope_base=self.rope_base, k_format=self.k_format)
 
 
 class HcaLane(_Lane):

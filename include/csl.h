@@ -59,7 +59,8 @@ typedef enum {
 typedef enum {
   CSL_DTYPE_BF16 = 0,
   CSL_DTYPE_F32 = 1,
-  CSL_DTYPE_FP8_E4M3 = 2 /* OCP E4M3FN: bias 7, no infinities, max 448, S.1111.111 = NaN */
+  CSL_DTYPE_FP8_E4M3 = 2, /* OCP E4M3FN: bias 7, no infinities, max 448, S.1111.111 = NaN */
+  CSL_DTYPE_MXFP4 = 3     /* OCP MXFP4: E2M1 codes, two per byte, one E8M0 scale per 32 values */
 } csl_dtype;
 
 /* Message for the last failed call on this thread ("" if none). Never NULL. */
@@ -123,14 +124,20 @@ int csl_compress_kv_overlap(const void* kv_a, const void* z_a, const void* kv_b,
  *
  * for s < n(b, t) = min(floor(p / m), E_b, max_entries), E_b = ent_off[b+1] - ent_off[b].
  * key(s, c) = k_idx[ent_off[b] + s, c] for bf16 keys; for fp8 keys it is
- * decode(k_idx[ent_off[b] + s, c]) * k_scale[scale_off[b] + s / scale_group].
+ * decode(k_idx[ent_off[b] + s, c]) * k_scale[scale_off[b] + s / scale_group]; for MXFP4
+ * keys ([P1] section 4.2, FP4 indexer; [P2] "Where It Breaks", the FP4 QK indexer) it is
+ * e2m1(code c of row ent_off[b] + s) * 2^(E - 127), E the row's E8M0 byte for block c / 32.
  * No 1/sqrt(CI) factor is applied. scores[b, t, s] for s >= n(b, t) is not written.
  *
  *   q_idx   bf16 [B, T, HI, CI]     HI in {1, 2, 4, 8, 16}; CI == 64
  *   w       fp32 [B, T, HI]
- *   k_idx   [E_tot, CI] of k_dtype (CSL_DTYPE_BF16 or CSL_DTYPE_FP8_E4M3)
- *   k_scale fp32, scale_off int64 [B+1]: required for fp8 keys, ignored (may be NULL) else;
- *           scales must be positive. scale_group >= 1.
+ *   k_idx   [E_tot, CI] of k_dtype (CSL_DTYPE_BF16 or CSL_DTYPE_FP8_E4M3), or for
+ *           CSL_DTYPE_MXFP4 uint8 [E_tot, CI/2]: byte j holds code 2j in its low nibble and
+ *           code 2j+1 in its high nibble (8-byte aligned)
+ *   k_scale fp8: fp32 scales with scale_off int64 [B+1], scale_group >= 1 entries per
+ *           scale, scales positive. MXFP4: uint8 E8M0 [E_tot, CI/32], one per block of 32
+ *           dims of a row, exponent bytes in [0, 254] (255, NaN, is a precondition
+ *           violation); scale_off and scale_group are ignored. bf16: ignored (may be NULL).
  *   scores  fp32 [B, T, ld], ld >= max_entries
  *   topk_ws (nullable) with topk_ws_bytes >= csl_topk_workspace_bytes(B, T, max_entries,
  *           topk_k): when given with T == 1 and rows longer than 34816 entries, the kernel
@@ -139,10 +146,11 @@ int csl_compress_kv_overlap(const void* kv_a, const void* z_a, const void* kv_b,
  *           csl_topk_select call that follows with prepared = 1 and the same k and
  *           max_entries (rows of at most 2^20 entries); for other shapes it is not touched.
  * Arithmetic: bf16 MFMA products with fp32 accumulation; fp8 codes are widened to bf16
- * exactly before the product and the group scale multiplies the fp32 dot.
+ * exactly before the product and the group scale multiplies the fp32 dot; MXFP4 codes are
+ * widened and scaled to bf16 exactly (every such value is a bf16) before the product.
  */
 int csl_indexer_scores(const void* q_idx, const float* w, const void* k_idx, int k_dtype,
-                       const float* k_scale, const int64_t* scale_off, int scale_group,
+                       const void* k_scale, const int64_t* scale_off, int scale_group,
                        const int64_t* ent_off, const int64_t* q_pos, int m, int B, int T, int HI,
                        int CI, int64_t max_entries, float* scores, int64_t ld, void* topk_ws,
                        size_t topk_ws_bytes, int topk_k, void* stream);
@@ -263,7 +271,7 @@ typedef struct csl_csa_step {
   const float* w;             /* fp32 [B, T, HI] */
   const void* k_idx;          /* [E_tot, CI] of k_dtype */
   int k_dtype;
-  const float* k_scale;
+  const void* k_scale;        /* as for csl_indexer_scores */
   const int64_t* scale_off;
   int scale_group;
   int HI;

@@ -134,6 +134,7 @@ class Lane:
     HI: int = 0
     CI: int = 64
     kI_fp8: bool = False
+    kI_fp4: bool = False         # MXFP4 indexer keys (E2M1 codes, one E8M0 scale per 32 dims)
     scale_group: int = 64
     row_base: int = 0
     seq_base: int = 0
@@ -271,6 +272,37 @@ def _encode_e4m3(x: torch.Tensor, lengths_e: list, group: int):
     return codes, torch.tensor(np.array(scales, dtype=np.float32))
 
 
+def _encode_mxfp4(x: torch.Tensor):
+    """OCP MXFP4 encoding of key rows x fp32 [E, C]: per block of 32 consecutive dims, the
+    shared scale is 2^X with X = floor(log2(amax)) - 2 (2 = the largest E2M1 exponent),
+    clamped to [-127, 127] (an all-zero block takes X = -127); each element is x / 2^X
+    rounded to nearest-even on the E2M1 grid {0, 0.5, 1, 1.5, 2, 3, 4, 6} and saturated to
+    +-6. Returns packed codes uint8 [E, C/2] (element 2j in the low nibble of byte j) and
+    E8M0 scales uint8 [E, C/32]."""
+    v = x.numpy().astype(np.float64)
+    E, C = v.shape
+    blk = v.reshape(E, C // 32, 32)
+    amax = np.abs(blk).max(axis=2)
+    with np.errstate(divide="ignore"):
+        X = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, -127)
+    X = np.clip(X, -127, 127)
+    y = np.abs(blk) / np.exp2(X)[:, :, None]
+    # round to nearest even on the grid: steps of 0.5 below 2, 1 in [2, 4), 2 from 4 up
+    q = np.where(y < 2, np.rint(y * 2) / 2, np.where(y < 4, np.rint(y), 2 * np.rint(y / 2)))
+    q = np.minimum(q, 6.0)
+    code = _e2m1_code(q) | np.where(blk < 0, 8, 0).astype(np.uint8)
+    code = code.reshape(E, C)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
+    scales = (X + 127).astype(np.uint8)
+    return torch.from_numpy(packed), torch.from_numpy(scales)
+
+
+def _e2m1_code(q: np.ndarray) -> np.ndarray:
+    """E2M1 magnitude code of grid values q in {0, 0.5, 1, 1.5, 2, 3, 4, 6}."""
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    return np.searchsorted(grid, q).astype(np.uint8)
+
+
 def generate(wl: Workload | str, parts=("kv", "z", "q", "qI", "kI", "w")) -> Inputs:
     """Draw the inputs of a workload (CPU tensors). ``parts`` selects which arrays to draw;
     "kv_b" and "z_b" (series b of overlapped compression, shaped like kv and z) are drawn
@@ -311,6 +343,8 @@ def generate(wl: Workload | str, parts=("kv", "z", "q", "qI", "kI", "w")) -> Inp
                 if lane.kI_fp8:
                     li.kI, li.k_scale = _encode_e4m3(x, lane.entries, lane.scale_group)
                     li.scale_off = torch.tensor(lane.scale_off(), dtype=torch.int64)
+                elif lane.kI_fp4:
+                    li.kI, li.k_scale = _encode_mxfp4(x)
                 else:
                     li.kI = x.to(torch.bfloat16)
             if w_all is not None:

@@ -156,8 +156,8 @@ def test_compress_overlap_argument_errors(csl):
 
 # ------------------------------------------------------------------------------- indexer
 
-def _index_lane(HI, T, lengths, q_pos, fp8=False, seed=21):
-    lane = W.Lane("csa", tuple(lengths), tuple(q_pos), T=T, H=16, m=4, k=8, HI=HI, kI_fp8=fp8)
+def _index_lane(HI, T, lengths, q_pos, fp8=False, seed=21, fp4=False):
+    lane = W.Lane("csa", tuple(lengths), tuple(q_pos), T=T, H=16, m=4, k=8, HI=HI, kI_fp8=fp8, kI_fp4=fp4)
     return synth.generate(W.Workload("idx", seed, (lane,)), parts=("qI", "kI", "w")).lanes[0]
 
 
@@ -176,17 +176,32 @@ def test_indexer_fp8_keys_match_oracle(csl, HI, T):
     _run_indexer(csl, HI, T, [70000, 1000, 130], [70000, 900, 130], fp8=True)
 
 
-def _run_indexer(csl, HI, T, lengths, q_pos, fp8):
-    print(f"indexer HI={HI} T={T} lengths={lengths} fp8={fp8}", flush=True)
-    li = _index_lane(HI, T, lengths, q_pos, fp8)
+@pytest.mark.parametrize("HI,T,lengths,q_pos", [
+    (8, 1, [300000, 1000, 130, 0], [300000, 900, 130, 0]),      # decode tiling with top-k candidate lists
+    (4, 20, [70000, 1000, 130], [69000, 900, 60]),              # prefill tiling
+    (16, 3, [2000, 333], [1500, 100]),
+    (1, 1, [4096], [4096]),
+])
+def test_indexer_mxfp4_keys_match_oracle(csl, HI, T, lengths, q_pos):
+    _run_indexer(csl, HI, T, lengths, q_pos, fp8=False, fp4=True)
+
+
+def _run_indexer(csl, HI, T, lengths, q_pos, fp8, fp4=False):
+    print(f"indexer HI={HI} T={T} lengths={lengths} fp8={fp8} fp4={fp4}", flush=True)
+    li = _index_lane(HI, T, lengths, q_pos, fp8, fp4=fp4)
     B = len(lengths)
     E = li.lane.entries
     ld = max(max(E), 1) + 5
     scores = torch.full((B, T, ld), float("nan"), dtype=torch.float32, device="cuda")
+    topk = {}
+    if fp4 and T == 1 and max(E) > 34816:  # the candidate-list path of the decode kernel too
+        topk = dict(topk_ws=torch.empty(csl.topk_workspace_bytes(B, T, max(E), 64), dtype=torch.uint8,
+                                        device="cuda"), topk_k=64)
     csl.indexer_scores(dev(li.qI), dev(li.w), dev(li.kI), dev(li.ent_off), dev(li.q_pos), 4, scores,
-                       max_entries=max(E), k_scale=dev(li.k_scale), scale_off=dev(li.scale_off), scale_group=64)
+                       max_entries=max(E), k_scale=dev(li.k_scale), scale_off=dev(li.scale_off), scale_group=64,
+                       k_format="mxfp4" if fp4 else None, **topk)
     torch.cuda.synchronize()
-    keys = pipeline.index_keys_f64(li.kI, li.k_scale, li.scale_off, li.ent_off, 64)
+    keys = pipeline.index_keys_f64(li.kI, li.k_scale, li.scale_off, li.ent_off, 64, fp4=fp4)
     ref = pipeline.indexer_lane(li.qI, li.w, keys, li.ent_off, li.q_pos, 4)
     got = f64(scores)
     for b in range(B):

@@ -112,14 +112,19 @@ def _check_csa_row(cl, inp, li, b, t, keys_f64, entries_fn=None, extras=None):
 
 
 def _csa_keys(li):
-    return pipeline.index_keys_f64(li.kI, li.k_scale, li.scale_off, li.ent_off, li.lane.scale_group)
+    return pipeline.index_keys_f64(li.kI, li.k_scale, li.scale_off, li.ent_off, li.lane.scale_group,
+                                   fp4=getattr(li.lane, "kI_fp4", False))
 
 
-def _run(lanes_mod, name, overlap=False, extras=None):
+def _run(lanes_mod, name, overlap=False, extras=None, fp4=False):
     print(f"workload {name}{' (overlapped compression)' if overlap else ''}"
-          f"{' (sink, rope)' if extras else ''}: generating inputs", flush=True)
+          f"{' (sink, rope)' if extras else ''}{' (MXFP4 keys)' if fp4 else ''}: generating inputs", flush=True)
     parts = ("kv", "z", "q", "qI", "kI", "w") + (("kv_b", "z_b") if overlap else ())
-    inp = synth.generate(name, parts=parts)
+    wl = synth.WORKLOADS[name]
+    if fp4:
+        from synth import workloads as W
+        wl = W.with_lanes(wl, kI_fp4=True)
+    inp = synth.generate(wl, parts=parts)
     print(f"workload {name}: running on the GPU", flush=True)
     cls = lanes_mod.build_lanes(inp)
     for cl in cls:
@@ -212,6 +217,16 @@ def test_hca_decode_128k_with_sink_and_rope(lanes_mod):
         ro, rl = _oracle_attention(inp.q[b, 0], inp.kv, inp.z, lane, b, p, np.arange(nv), cl.scale, None, ex)
         assert_attn_close(f64(cl.out[b, 0]), ro, f"out b={b}")
         assert_attn_close(f64(cl.lse[b, 0]), rl, f"lse b={b}")
+
+
+def test_csa_decode_1m_mxfp4_keys(lanes_mod):
+    """4 x 1M-token CSA decode with MXFP4 indexer keys: every row's scores against the
+    oracle on the decoded keys, the selection (boundary band) and the attention."""
+    inp, (cl,) = _run(lanes_mod, "csa_decode_1m", fp4=True)
+    li = inp.lanes[0]
+    keys = _csa_keys(li)
+    for b in range(li.lane.B):
+        _check_csa_row(cl, inp, li, b, 0, keys)
 
 
 def test_csa_prefill_8k_on_128k(lanes_mod):

@@ -61,3 +61,34 @@ def test_random_stage_inputs():
         good = sel[r][sel[r] >= 0]
         assert len(good) == min(8, n, round(0.75 * min(8, n)))
         assert torch.all(good < n) and torch.all(good[1:] > good[:-1])
+
+
+def test_mxfp4_encoding_rounds_to_the_grid():
+    """Every decoded key lies on the E2M1 grid of its block's scale, within half a grid step
+    of the fp32 value (or saturated at 6 * scale), with the block maximum at 4..8 scales;
+    an all-zero block encodes as zero codes with the smallest scale."""
+    r = np.random.default_rng(5)
+    x = (r.standard_normal((300, 64)) * 0.125).astype(np.float32)
+    x[7, :32] = 0.0
+    pk, sc = W._encode_mxfp4(torch.from_numpy(x))
+    assert pk.shape == (300, 32) and sc.shape == (300, 2)
+    d = csa.decode_mxfp4_rows(pk.numpy(), sc.numpy())
+    scale = np.repeat(csa.decode_e8m0(sc.numpy()), 32, axis=1)
+    y = np.abs(x) / scale
+    step = np.where(y < 2, 0.5, np.where(y < 4, 1.0, 2.0))
+    sat = y >= 6
+    err = np.abs(d - x) / scale
+    assert np.all(err[~sat] <= step[~sat] / 2 + 1e-12)
+    assert np.all(np.abs(d[sat]) == 6 * scale[sat])
+    amax = np.abs(x.reshape(300, 2, 32)).max(axis=2)
+    s_blk = csa.decode_e8m0(sc.numpy())
+    nz = amax > 0
+    assert np.all(amax[nz] / s_blk[nz] >= 4) and np.all(amax[nz] / s_blk[nz] < 8)
+    assert np.all(pk.numpy()[7, :16] == 0) and sc.numpy()[7, 0] == 0
+
+
+def test_fp4_lane_generation():
+    lane = W.Lane("csa", (1000, 333), (1000, 333), T=1, H=16, m=4, k=8, HI=4, kI_fp4=True)
+    li = synth.generate(W.Workload("t4", 3, (lane,))).lanes[0]
+    assert li.kI.dtype == torch.uint8 and li.kI.shape == (250 + 83, 32)
+    assert li.k_scale.dtype == torch.uint8 and li.k_scale.shape == (250 + 83, 2)
