@@ -366,7 +366,26 @@ def main():
         cl.kI_copies, cl.k_scale_copies, cl.k_format = saved
         del g4, g4s
 
-        result["options_step_us"] = {"plain": round(ms_step * 1e3, 2),
+        # the same step with the cache paged (entries and keys in a pool of 32-entry blocks,
+        # raw rows in 256-row rings), the blocks in a random order (a free list after churn)
+        # or handed out round-robin over the sequences (concurrent growth); a separate lane
+        # over the same inputs
+        def paged_step(order: str) -> float:
+            (pl,) = lanes.build_lanes(inp)
+            pl.compress_all()
+            pl.paginate(ring_rows=256, order=order)
+            pl.rotate(R)
+            gpg = capture(lambda: [pl.step(r) for r in range(R)])
+            t = time_graphs([gpg], max(1, 400 // R), per_replay=R)
+            del gpg, pl
+            torch.cuda.empty_cache()
+            return round(t, 2)
+
+        paged_us = paged_step("random")
+        paged_il_us = paged_step("interleaved")
+
+        result["options_step_us"] = {"plain": round(ms_step * 1e3, 2), "paged": paged_us,
+                                     "paged_interleaved": paged_il_us,
                                      "overlap": options_step(True, False),
                                      "sink_rope64": options_step(False, True),
                                      "overlap_sink_rope64": options_step(True, True)}

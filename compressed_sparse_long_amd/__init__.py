@@ -14,8 +14,8 @@ import torch
 
 __all__ = [
     "compress_kv", "compress_kv_overlap", "indexer_scores", "topk_select", "sparse_attn_decode", "hca_attn_decode", "csa_decode_step",
-    "topk_workspace_bytes", "attn_workspace_bytes", "version", "LIB_PATH", "EXPORTS",
-    "CslError",
+    "topk_workspace_bytes", "attn_workspace_bytes", "PagedCache", "version", "LIB_PATH",
+    "EXPORTS", "CslError",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsl.so")
@@ -44,7 +44,14 @@ class _CsaStep(ctypes.Structure):
         ("q_pos", _P), ("m", _I), ("B", _I), ("T", _I), ("max_entries", _L),
         ("kv_b", _P), ("z_b", _P),
         ("sink", _P), ("rope_dims", _I), ("rope_base", _F),
+        ("paged", _P),
     ]
+
+
+class _PagedCache(ctypes.Structure):
+    """csl_paged_cache (include/csl.h), field for field."""
+    _fields_ = [("block_table", _P), ("max_blocks", _I), ("block_entries", _I), ("pool_entries", _L),
+                ("ring_rows", _I)]
 
 
 class _AttnExtras(ctypes.Structure):
@@ -66,16 +73,16 @@ def _load() -> ctypes.CDLL:
     sig = {
         "csl_last_error": (ctypes.c_char_p, []),
         "csl_version": (I, []),
-        "csl_compress_kv": (I, [P, P, P, P, P, I, I, I, L, P, I, P]),
-        "csl_compress_kv_overlap": (I, [P, P, P, P, P, P, P, I, I, I, L, P, I, P]),
-        "csl_indexer_scores": (I, [P, P, P, I, P, P, I, P, P, I, I, I, I, I, L, P, L, P, S, I, P]),
+        "csl_compress_kv": (I, [P, P, P, P, P, I, I, I, L, P, I, P, P]),
+        "csl_compress_kv_overlap": (I, [P, P, P, P, P, P, P, I, I, I, L, P, I, P, P]),
+        "csl_indexer_scores": (I, [P, P, P, I, P, P, I, P, P, I, I, I, I, I, L, P, L, P, S, I, P, P]),
         "csl_topk_workspace_bytes": (S, [I, I, L, I]),
         "csl_topk_select": (I, [P, L, P, P, I, I, I, I, L, P, P, S, I, P]),
         "csl_attn_workspace_bytes": (S, [I, I, I, I, L]),
         "csl_sparse_attn_decode": (I, [P, P, P, I, P, P, P, P, I, I, I, I, I, F, P, P, P, S,
-                                       ctypes.POINTER(_AttnExtras), P]),
+                                       ctypes.POINTER(_AttnExtras), P, P]),
         "csl_hca_attn_decode": (I, [P, P, P, P, P, P, I, I, I, I, I, I, F, L, P, P, P, S,
-                                    ctypes.POINTER(_AttnExtras), P]),
+                                    ctypes.POINTER(_AttnExtras), P, P]),
         "csl_csa_decode_step": (I, [ctypes.POINTER(_CsaStep), P]),
     }
     for name, (res, args) in sig.items():
@@ -117,13 +124,35 @@ def _stream(stream) -> int | None:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+class PagedCache:
+    """Paged heterogeneous cache ([P2] "KV Cache Management"; csl_paged_cache in csl.h):
+    ``block_table`` int32 [B, max_blocks] of pool blocks of ``block_entries`` entries each,
+    ``pool_entries`` rows in the entry pool, raw rows in per-sequence rings of ``ring_rows``
+    rows (0: packed)."""
+
+    def __init__(self, block_table, block_entries: int, pool_entries: int, ring_rows: int = 0):
+        self.block_table = block_table
+        self.block_entries = int(block_entries)
+        self.pool_entries = int(pool_entries)
+        self.ring_rows = int(ring_rows)
+
+    def _struct(self):
+        bt = _ptr(self.block_table, "block_table", (torch.int32,))
+        return _PagedCache(block_table=bt, max_blocks=int(self.block_table.shape[-1]),
+                           block_entries=self.block_entries, pool_entries=self.pool_entries, ring_rows=self.ring_rows)
+
+
+def _paged(paged):
+    return None if paged is None else ctypes.byref(paged._struct())
+
+
 _I64 = (torch.int64,)
 _BF16 = (torch.bfloat16,)
 _F32 = (torch.float32,)
 
 
 def compress_kv(kv, z, kv_off, ent_off, m: int, out, first_entry=None, max_new_entries: int | None = None,
-                stream=None):
+                paged=None, stream=None):
     """Softmax-weighted pooling of every m raw rows into out (fp32 or bf16 [*, D]); see csl.h."""
     B = kv_off.numel() - 1
     D = kv.shape[-1]
@@ -135,12 +164,12 @@ def compress_kv(kv, z, kv_off, ent_off, m: int, out, first_entry=None, max_new_e
     _check(_lib.csl_compress_kv(
         _ptr(kv, "kv", _BF16), _ptr(z, "z", _BF16), _ptr(kv_off, "kv_off", _I64), _ptr(ent_off, "ent_off", _I64),
         _ptr(first_entry, "first_entry", _I64), B, D, int(m), int(max_new_entries), _ptr(out, "out"), dt,
-        _stream(stream)))
+        _paged(paged), _stream(stream)))
     return out
 
 
 def compress_kv_overlap(kv_a, z_a, kv_b, z_b, kv_off, ent_off, m: int, out, first_entry=None,
-                        max_new_entries: int | None = None, stream=None):
+                        max_new_entries: int | None = None, paged=None, stream=None):
     """CSA's overlapped compression: entry i pools series-a rows [m*i, m*i + m) with series-b
     rows [m*(i-1), m*i) under one softmax per dimension, into out (fp32 or bf16 [*, D]); see csl.h."""
     B = kv_off.numel() - 1
@@ -155,7 +184,7 @@ def compress_kv_overlap(kv_a, z_a, kv_b, z_b, kv_off, ent_off, m: int, out, firs
     _check(_lib.csl_compress_kv_overlap(
         _ptr(kv_a, "kv_a", _BF16), _ptr(z_a, "z_a", _BF16), _ptr(kv_b, "kv_b", _BF16), _ptr(z_b, "z_b", _BF16),
         _ptr(kv_off, "kv_off", _I64), _ptr(ent_off, "ent_off", _I64), _ptr(first_entry, "first_entry", _I64),
-        B, D, int(m), int(max_new_entries), _ptr(out, "out"), dt, _stream(stream)))
+        B, D, int(m), int(max_new_entries), _ptr(out, "out"), dt, _paged(paged), _stream(stream)))
     return out
 
 
@@ -174,7 +203,7 @@ def _key_format(kI, k_format):
 
 def indexer_scores(qI, w, kI, ent_off, q_pos, m: int, scores, max_entries: int | None = None, k_scale=None,
                    scale_off=None, scale_group: int = 64, topk_ws=None, topk_k: int = 0, k_format=None,
-                   stream=None):
+                   paged=None, stream=None):
     """Lightning-indexer scores into scores fp32 [B, T, ld]; with ``topk_ws``/``topk_k`` it also
     leaves top-k candidate lists for ``topk_select(..., prepared=True)``. ``k_format='mxfp4'``
     takes packed E2M1 keys with their E8M0 scales in ``k_scale``; see csl.h."""
@@ -188,7 +217,7 @@ def indexer_scores(qI, w, kI, ent_off, q_pos, m: int, scores, max_entries: int |
         _ptr(scale_off, "scale_off", _I64), int(scale_group), _ptr(ent_off, "ent_off", _I64),
         _ptr(q_pos, "q_pos", _I64), int(m), B, T, HI, CI, int(max_entries), _ptr(scores, "scores", _F32), ld,
         _ptr(topk_ws, "topk_ws"), 0 if topk_ws is None else topk_ws.numel() * topk_ws.element_size(), int(topk_k),
-        _stream(stream)))
+        _paged(paged), _stream(stream)))
     return scores
 
 
@@ -233,7 +262,7 @@ def _extras(sink, rope_dims: int, rope_base: float):
 
 
 def sparse_attn_decode(q, ckv, idx, kv, kv_off, ent_off, q_pos, n_win: int, out, lse=None, scale: float | None = None,
-                       ws=None, sink=None, rope_dims: int = 0, rope_base: float = 10000.0, stream=None):
+                       ws=None, sink=None, rope_dims: int = 0, rope_base: float = 10000.0, paged=None, stream=None):
     """CSA attention over the selected entries plus the raw window; ``sink`` (fp32 [H] logits)
     and ``rope_dims``/``rope_base`` (partial RoPE of q at p, of the output at -p) are the
     optional extras; see csl.h."""
@@ -246,13 +275,13 @@ def sparse_attn_decode(q, ckv, idx, kv, kv_off, ent_off, q_pos, n_win: int, out,
         _ptr(q, "q", _BF16), _ptr(ckv, "ckv", _BF16), _ptr(idx, "idx", (torch.int32,)), k, _ptr(kv, "kv", _BF16),
         _ptr(kv_off, "kv_off", _I64), _ptr(ent_off, "ent_off", _I64), _ptr(q_pos, "q_pos", _I64), int(n_win), B, T, H,
         D, float(scale), _ptr(out, "out", _F32), _ptr(lse, "lse", _F32), _ptr(ws, "ws"), wb,
-        _extras(sink, rope_dims, rope_base), _stream(stream)))
+        _extras(sink, rope_dims, rope_base), _paged(paged), _stream(stream)))
     return out
 
 
 def hca_attn_decode(q, ckv, kv, kv_off, ent_off, q_pos, m: int, n_win: int, out, lse=None, scale: float | None = None,
                     max_entries: int | None = None, ws=None, sink=None, rope_dims: int = 0, rope_base: float = 10000.0,
-                    stream=None):
+                    paged=None, stream=None):
     """HCA dense attention over every visible entry plus the raw window, with the same
     optional extras as sparse_attn_decode; see csl.h."""
     B, T, H, D = q.shape
@@ -265,7 +294,7 @@ def hca_attn_decode(q, ckv, kv, kv_off, ent_off, q_pos, m: int, n_win: int, out,
         _ptr(q, "q", _BF16), _ptr(ckv, "ckv", _BF16), _ptr(kv, "kv", _BF16), _ptr(kv_off, "kv_off", _I64),
         _ptr(ent_off, "ent_off", _I64), _ptr(q_pos, "q_pos", _I64), int(m), int(n_win), B, T, H, D, float(scale),
         int(max_entries), _ptr(out, "out", _F32), _ptr(lse, "lse", _F32), _ptr(ws, "ws"), wb,
-        _extras(sink, rope_dims, rope_base), _stream(stream)))
+        _extras(sink, rope_dims, rope_base), _paged(paged), _stream(stream)))
     return out
 
 
@@ -277,7 +306,7 @@ def csa_decode_step(kv, z, kv_off, ent_off, first_entry, max_new_entries: int, c
                     k: int, idx, q, n_win: int, out, q_pos, m: int, lse=None, scale: float | None = None,
                     k_scale=None, scale_off=None, scale_group: int = 64, max_entries: int | None = None,
                     attn_ws=None, kv_b=None, z_b=None, sink=None, rope_dims: int = 0, rope_base: float = 10000.0,
-                    k_format=None, stream=None):
+                    k_format=None, paged=None, stream=None):
     """One whole CSA step (compress_kv of the newest entries into ckv, or compress_kv_overlap
     when series b ``kv_b``/``z_b`` is given, indexer_scores with candidate lists, topk_select,
     sparse_attn_decode) in one C call; see csl.h."""
@@ -290,6 +319,7 @@ def csa_decode_step(kv, z, kv_off, ent_off, first_entry, max_new_entries: int, c
     if scale is None:
         scale = D ** -0.5
     attn_ws, awb = _attn_ws(attn_ws, B, T, H, D, k + n_win, q.device)
+    pstruct = None if paged is None else paged._struct()  # kept alive across the call
     s = _CsaStep(
         kv=_ptr(kv, "kv", _BF16), z=_ptr(z, "z", _BF16), kv_off=_ptr(kv_off, "kv_off", _I64),
         ent_off=_ptr(ent_off, "ent_off", _I64), first_entry=_ptr(first_entry, "first_entry", _I64),
@@ -303,6 +333,7 @@ def csa_decode_step(kv, z, kv_off, ent_off, first_entry, max_new_entries: int, c
         lse=_ptr(lse, "lse", _F32), attn_ws=_ptr(attn_ws, "attn_ws"), attn_ws_bytes=awb,
         kv_b=_ptr(kv_b, "kv_b", _BF16), z_b=_ptr(z_b, "z_b", _BF16),
         sink=_ptr(sink, "sink", _F32), rope_dims=int(rope_dims), rope_base=float(rope_base),
+        paged=None if paged is None else ctypes.addressof(pstruct),
         q_pos=_ptr(q_pos, "q_pos", _I64), m=int(m), B=B, T=T, max_entries=int(max_entries))
     _check(_lib.csl_csa_decode_step(ctypes.byref(s), _stream(stream)))
     return out

@@ -46,7 +46,7 @@ extern "C" {
 
 const char* csl_last_error(void) { return g_last_error.c_str(); }
 
-int csl_version(void) { return 300; }
+int csl_version(void) { return 400; }
 
 }  // extern "C"
 
@@ -76,6 +76,25 @@ int check_series_b(const void* kv_b, const void* z_a, const void* z_b, const cha
     return fail(CSL_ERR_INVALID, "%s: z and z_b must both be given or both be NULL", who);
   if (!aligned(kv_b, 16) || (z_b && !aligned(z_b, 16)))
     return fail(CSL_ERR_INVALID, "%s: kv_b and z_b must be 16-byte aligned", who);
+  return CSL_OK;
+}
+
+// The paged cache descriptor: a table of pool blocks (a power-of-two number of entries each)
+// and a power-of-two ring of raw rows per sequence; fills the launchers' view.
+int check_paged(const char* who, const csl_paged_cache* pc, int B, csl::PagedView& pv) {
+  if (!pc->block_table) return fail(CSL_ERR_INVALID, "%s: paged cache without a block table", who);
+  if (pc->max_blocks < 1 || pc->block_entries < 1 || (pc->block_entries & (pc->block_entries - 1)))
+    return fail(CSL_ERR_INVALID, "%s: paged cache needs max_blocks >= 1 and a power-of-two block_entries", who);
+  if (pc->ring_rows < 0 || (pc->ring_rows & (pc->ring_rows - 1)))
+    return fail(CSL_ERR_INVALID, "%s: ring_rows must be 0 or a power of two", who);
+  if (pc->pool_entries < 0 || pc->pool_entries > 0x7fffffff)
+    return fail(CSL_ERR_INVALID, "%s: pool_entries must be in [0, 2^31)", who);
+  if ((int64_t)B * pc->max_blocks > ((int64_t)1 << 40)) return fail(CSL_ERR_INVALID, "%s: block table too large", who);
+  pv.table = pc->block_table;
+  pv.max_blocks = pc->max_blocks;
+  pv.eb_shift = __builtin_ctz((unsigned)pc->block_entries);
+  pv.ring_rows = pc->ring_rows;
+  pv.pool_rows = pc->pool_entries;
   return CSL_OK;
 }
 
@@ -150,40 +169,62 @@ extern "C" {
 
 int csl_compress_kv(const void* kv, const void* z, const int64_t* kv_off, const int64_t* ent_off,
                     const int64_t* first_entry, int B, int D, int m, int64_t max_new_entries, void* out,
-                    int out_dtype, void* stream) {
-  const int st = check_compress(kv, z, kv_off, ent_off, B, D, m, max_new_entries, out, out_dtype);
+                    int out_dtype, const csl_paged_cache* paged, void* stream) {
+  int st = check_compress(kv, z, kv_off, ent_off, B, D, m, max_new_entries, out, out_dtype);
   if (st != CSL_OK) return st;
+  csl::PagedView pv;
+  if (paged) {
+    st = check_paged("compress_kv", paged, B, pv);
+    if (st != CSL_OK) return st;
+    if (paged->ring_rows > 0 && paged->ring_rows < m)
+      return fail(CSL_ERR_INVALID, "compress_kv: ring_rows must hold a chunk (>= m)");
+  }
   if (B == 0 || max_new_entries == 0) return ok();
   return hip_status(csl::launch_compress(kv, z, kv_off, ent_off, first_entry, B, D, m, max_new_entries, out,
-                                         out_dtype == CSL_DTYPE_BF16, as_stream(stream)),
+                                         out_dtype == CSL_DTYPE_BF16, as_stream(stream), paged ? &pv : nullptr),
                     "compress_kv launch");
 }
 
 int csl_compress_kv_overlap(const void* kv_a, const void* z_a, const void* kv_b, const void* z_b,
                             const int64_t* kv_off, const int64_t* ent_off, const int64_t* first_entry, int B, int D,
-                            int m, int64_t max_new_entries, void* out, int out_dtype, void* stream) {
+                            int m, int64_t max_new_entries, void* out, int out_dtype, const csl_paged_cache* paged,
+                            void* stream) {
   int st = check_compress(kv_a, z_a, kv_off, ent_off, B, D, m, max_new_entries, out, out_dtype, "compress_kv_overlap");
   if (st != CSL_OK) return st;
   st = check_series_b(kv_b, z_a, z_b, "compress_kv_overlap");
   if (st != CSL_OK) return st;
+  csl::PagedView pv;
+  if (paged) {
+    st = check_paged("compress_kv_overlap", paged, B, pv);
+    if (st != CSL_OK) return st;
+    if (paged->ring_rows > 0 && paged->ring_rows < 2 * m)
+      return fail(CSL_ERR_INVALID, "compress_kv_overlap: ring_rows must hold two chunks (>= 2m)");
+  }
   if (B == 0 || max_new_entries == 0) return ok();
   return hip_status(csl::launch_compress_overlap(kv_a, z_a, kv_b, z_b, kv_off, ent_off, first_entry, B, D, m,
                                                  max_new_entries, out, out_dtype == CSL_DTYPE_BF16,
-                                                 as_stream(stream)),
+                                                 as_stream(stream), paged ? &pv : nullptr),
                     "compress_kv_overlap launch");
 }
 
 int csl_indexer_scores(const void* q_idx, const float* w, const void* k_idx, int k_dtype, const void* k_scale,
                        const int64_t* scale_off, int scale_group, const int64_t* ent_off, const int64_t* q_pos, int m,
                        int B, int T, int HI, int CI, int64_t max_entries, float* scores, int64_t ld, void* topk_ws,
-                       size_t topk_ws_bytes, int topk_k, void* stream) {
-  const int st = check_indexer(q_idx, w, k_idx, k_dtype, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T, HI,
-                               CI, max_entries, scores, ld, topk_ws, topk_ws_bytes, topk_k);
+                       size_t topk_ws_bytes, int topk_k, const csl_paged_cache* paged, void* stream) {
+  int st = check_indexer(q_idx, w, k_idx, k_dtype, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T, HI,
+                         CI, max_entries, scores, ld, topk_ws, topk_ws_bytes, topk_k);
   if (st != CSL_OK) return st;
+  csl::PagedView pv;
+  if (paged) {
+    st = check_paged("indexer_scores", paged, B, pv);
+    if (st != CSL_OK) return st;
+    if (k_dtype == CSL_DTYPE_FP8_E4M3)
+      return fail(CSL_ERR_UNSUPPORTED, "indexer_scores: fp8 keys (group scales) are not supported in a paged cache");
+  }
   if (B == 0 || T == 0 || max_entries == 0) return ok();
   return hip_status(csl::launch_indexer(q_idx, w, k_idx, key_type(k_dtype), k_scale, scale_off, scale_group,
                                         ent_off, q_pos, m, B, T, HI, max_entries, scores, ld, topk_ws, topk_k,
-                                        as_stream(stream)),
+                                        as_stream(stream), nullptr, paged ? &pv : nullptr),
                     "indexer_scores launch");
 }
 
@@ -247,7 +288,7 @@ static int check_extras(const char* who, const float* sink, int rope_dims, float
 int csl_sparse_attn_decode(const void* q, const void* ckv, const int32_t* idx, int k, const void* kv,
                            const int64_t* kv_off, const int64_t* ent_off, const int64_t* q_pos, int n_win, int B, int T,
                            int H, int D, float scale, float* out, float* lse, void* ws, size_t ws_bytes,
-                           const csl_attn_extras* extras, void* stream) {
+                           const csl_attn_extras* extras, const csl_paged_cache* paged, void* stream) {
   csl::AttnExtras ex;
   if (extras) {
     const int se = check_extras("sparse_attn_decode", extras->sink, extras->rope_dims, extras->rope_base, ex);
@@ -256,19 +297,27 @@ int csl_sparse_attn_decode(const void* q, const void* ckv, const int32_t* idx, i
   if (k < 0) return fail(CSL_ERR_INVALID, "sparse_attn_decode: k must be >= 0");
   if (k > 0 && !idx) return fail(CSL_ERR_INVALID, "sparse_attn_decode: idx is NULL");
   const int64_t max_keys = (int64_t)k + n_win;
-  const int st = check_attn("sparse_attn_decode", q, ckv, kv, kv_off, ent_off, q_pos, n_win, B, T, H, D, scale, out, ws,
-                            ws_bytes, max_keys);
+  int st = check_attn("sparse_attn_decode", q, ckv, kv, kv_off, ent_off, q_pos, n_win, B, T, H, D, scale, out, ws,
+                      ws_bytes, max_keys);
   if (st == -1) return ok();
   if (st != CSL_OK) return st;
+  csl::PagedView pv;
+  if (paged) {
+    st = check_paged("sparse_attn_decode", paged, B, pv);
+    if (st != CSL_OK) return st;
+    if (n_win > 0 && paged->ring_rows < n_win)
+      return fail(CSL_ERR_INVALID, "sparse_attn_decode: ring_rows must hold the window (>= n_win)");
+  }
   return hip_status(csl::launch_attention(true, q, ckv, idx, k, kv, kv_off, ent_off, q_pos, 1, n_win, B, T, H, scale,
-                                          (int64_t)1 << 62, max_keys, out, lse, ws, ex, as_stream(stream)),
+                                          (int64_t)1 << 62, max_keys, out, lse, ws, ex, as_stream(stream),
+                                          paged ? &pv : nullptr),
                     "sparse_attn_decode launch");
 }
 
 int csl_hca_attn_decode(const void* q, const void* ckv, const void* kv, const int64_t* kv_off, const int64_t* ent_off,
                         const int64_t* q_pos, int m, int n_win, int B, int T, int H, int D, float scale,
                         int64_t max_entries, float* out, float* lse, void* ws, size_t ws_bytes,
-                        const csl_attn_extras* extras, void* stream) {
+                        const csl_attn_extras* extras, const csl_paged_cache* paged, void* stream) {
   csl::AttnExtras ex;
   if (extras) {
     const int se = check_extras("hca_attn_decode", extras->sink, extras->rope_dims, extras->rope_base, ex);
@@ -277,12 +326,20 @@ int csl_hca_attn_decode(const void* q, const void* ckv, const void* kv, const in
   if (m < 1) return fail(CSL_ERR_INVALID, "hca_attn_decode: m must be >= 1");
   if (max_entries < 0) return fail(CSL_ERR_INVALID, "hca_attn_decode: max_entries must be >= 0");
   const int64_t max_keys = max_entries + n_win;
-  const int st = check_attn("hca_attn_decode", q, ckv, kv, kv_off, ent_off, q_pos, n_win, B, T, H, D, scale, out, ws,
-                            ws_bytes, max_keys);
+  int st = check_attn("hca_attn_decode", q, ckv, kv, kv_off, ent_off, q_pos, n_win, B, T, H, D, scale, out, ws,
+                      ws_bytes, max_keys);
   if (st == -1) return ok();
   if (st != CSL_OK) return st;
+  csl::PagedView pv;
+  if (paged) {
+    st = check_paged("hca_attn_decode", paged, B, pv);
+    if (st != CSL_OK) return st;
+    if (n_win > 0 && paged->ring_rows < n_win)
+      return fail(CSL_ERR_INVALID, "hca_attn_decode: ring_rows must hold the window (>= n_win)");
+  }
   return hip_status(csl::launch_attention(false, q, ckv, nullptr, 0, kv, kv_off, ent_off, q_pos, m, n_win, B, T, H,
-                                          scale, max_entries, max_keys, out, lse, ws, ex, as_stream(stream)),
+                                          scale, max_entries, max_keys, out, lse, ws, ex, as_stream(stream),
+                                          paged ? &pv : nullptr),
                     "hca_attn_decode launch");
 }
 
@@ -300,6 +357,17 @@ int csl_csa_decode_step(const csl_csa_step* s, void* stream) {
   csl::AttnExtras ex;
   st = check_extras("csa_decode_step", s->sink, s->rope_dims, s->rope_base, ex);
   if (st != CSL_OK) return st;
+  csl::PagedView pv;
+  const csl::PagedView* pvp = nullptr;
+  if (s->paged) {
+    st = check_paged("csa_decode_step", s->paged, s->B, pv);
+    if (st != CSL_OK) return st;
+    if (s->k_dtype == CSL_DTYPE_FP8_E4M3)
+      return fail(CSL_ERR_UNSUPPORTED, "csa_decode_step: fp8 keys are not supported in a paged cache");
+    if (s->paged->ring_rows < s->n_win || s->paged->ring_rows < (overlap ? 2 : 1) * s->m)
+      return fail(CSL_ERR_INVALID, "csa_decode_step: ring_rows must hold the window and the newest chunk(s)");
+    pvp = &pv;
+  }
   void* topk_ws = s->topk_ws;
   st = check_indexer(s->q_idx, s->w, s->k_idx, s->k_dtype, s->k_scale, s->scale_off, s->scale_group, s->ent_off,
                      s->q_pos, s->m, s->B, s->T, s->HI, s->CI, s->max_entries, s->scores, s->ld, topk_ws,
@@ -324,17 +392,19 @@ int csl_csa_decode_step(const csl_csa_step* s, void* stream) {
     const csl::CompressJob job{s->kv, s->z, s->kv_off, s->first_entry, s->max_new_entries, s->ckv, s->m,
                                s->kv_b, s->z_b};
     e = csl::launch_indexer(s->q_idx, s->w, s->k_idx, kt, s->k_scale, s->scale_off, s->scale_group, s->ent_off,
-                            s->q_pos, s->m, s->B, s->T, s->HI, s->max_entries, s->scores, s->ld, topk_ws, s->k, hs, &job);
+                            s->q_pos, s->m, s->B, s->T, s->HI, s->max_entries, s->scores, s->ld, topk_ws, s->k, hs, &job,
+                            pvp);
   } else {
     if (compress && overlap)
       e = csl::launch_compress_overlap(s->kv, s->z, s->kv_b, s->z_b, s->kv_off, s->ent_off, s->first_entry, s->B,
-                                       s->D, s->m, s->max_new_entries, s->ckv, true, hs);
+                                       s->D, s->m, s->max_new_entries, s->ckv, true, hs, pvp);
     else if (compress)
       e = csl::launch_compress(s->kv, s->z, s->kv_off, s->ent_off, s->first_entry, s->B, s->D, s->m,
-                               s->max_new_entries, s->ckv, true, hs);
+                               s->max_new_entries, s->ckv, true, hs, pvp);
     if (e == hipSuccess && index)
       e = csl::launch_indexer(s->q_idx, s->w, s->k_idx, kt, s->k_scale, s->scale_off, s->scale_group, s->ent_off,
-                              s->q_pos, s->m, s->B, s->T, s->HI, s->max_entries, s->scores, s->ld, topk_ws, s->k, hs);
+                              s->q_pos, s->m, s->B, s->T, s->HI, s->max_entries, s->scores, s->ld, topk_ws, s->k, hs,
+                              nullptr, pvp);
   }
   if (e != hipSuccess) return hip_status(e, "csa_decode_step launch");
   e = csl::launch_topk(s->scores, s->ld, s->ent_off, s->q_pos, s->m, s->B, s->T, s->k, s->max_entries, s->idx,
@@ -342,7 +412,7 @@ int csl_csa_decode_step(const csl_csa_step* s, void* stream) {
   if (e != hipSuccess) return hip_status(e, "csa_decode_step launch");
   return hip_status(csl::launch_attention(true, s->q, s->ckv, s->idx, s->k, s->kv, s->kv_off, s->ent_off, s->q_pos, 1,
                                           s->n_win, s->B, s->T, s->H, s->scale, (int64_t)1 << 62, max_keys, s->out,
-                                          s->lse, s->attn_ws, ex, hs),
+                                          s->lse, s->attn_ws, ex, hs, pvp),
                     "csa_decode_step launch");
 }
 

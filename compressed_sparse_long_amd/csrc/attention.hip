@@ -38,6 +38,15 @@ constexpr int kRope = 64;             // partial RoPE: the last 64 dims ([P1] se
 constexpr int kRopeOff = kD - kRope;  // first rotated dim
 constexpr int kRopeKK = kRopeOff / 32;  // first rotated 32-dim chunk of the query operand
 
+// The paged cache as the attention reads it: entry e of sequence b at pool row
+// table[b * max_blocks + (e >> eb_shift)] << eb_shift | (e & mask); raw rows in rings
+struct AttnLayout {
+  const int32_t* table = nullptr;
+  int max_blocks = 0;
+  int eb_shift = 0;
+  int ring_rows = 0;                         // 0: raw rows packed in kv; else a power-of-two ring
+};
+
 struct RowGeom {
   int64_t ent_base, n_ent, kv_base, win_lo, win_cnt, nvis;
 };
@@ -283,14 +292,14 @@ __device__ __forceinline__ void attn_write(const f32x4 (&oacc)[8], float m_run, 
 // for each tile's rows in turn. MODE 0: the workgroup walks many tiles and loads the next
 // tile's rows (and the selected ids of the one after) into registers while the current tile
 // is multiplied.
-template <int NHG, bool SPARSE, int MODE, bool ROPE>
+template <int NHG, bool SPARSE, int MODE, bool ROPE, bool PAGED>
 __global__ __launch_bounds__(NHG * 64) void attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ ckv, const int32_t* __restrict__ idx, int k,
     const uint16_t* __restrict__ kv, const int64_t* __restrict__ kv_off, const int64_t* __restrict__ ent_off,
     const int64_t* __restrict__ q_pos, int m, int n_win, int T, float scale_log2, int64_t max_entries,
     int keys_per_split, float* __restrict__ out, float* __restrict__ lse_out, float* __restrict__ ws_o,
     float* __restrict__ ws_lse, const float* __restrict__ sink, double rope_theta1,
-    float2* __restrict__ ws_rope) {
+    float2* __restrict__ ws_rope, AttnLayout lay) {
   constexpr bool MULTI = MODE == 0;
   constexpr int NTL = MULTI ? 1 : MODE;    // tiles held in LDS at once
   constexpr int NT = NHG * 64;
@@ -336,16 +345,27 @@ __global__ __launch_bounds__(NHG * 64) void attn_kernel(
   // Row addresses as integers, computed without branches. Slot t0 + v of a round (v < NV) is
   // a compressed entry while v < n_comp - t0 and holds a key while v < k_hi - t0; both limits
   // are clamped to [0, NV] so the per-slot tests are 32-bit.
+  // Entry e of the sequence is ckv row ent_off[b] + e or, in the paged layout, the pool row
+  // its block table gives (looked up here, between the id and the row loads). Window slot
+  // s (s >= n_comp) is raw row win_lo + s - n_comp of the sequence: kv row kv_off[b] + that,
+  // or ring row b * R + (that mod R) in the paged layout.
   const uint64_t ckv_a = reinterpret_cast<uint64_t>(ckv);
-  const uint64_t ent_a = ckv_a + (uint64_t)geo.ent_base * (kD * 2);
-  const uint64_t win_a = reinterpret_cast<uint64_t>(kv) + (uint64_t)(geo.kv_base + geo.win_lo - n_comp) * (kD * 2);
+  const uint64_t ent_a = ckv_a + (uint64_t)(PAGED ? 0 : geo.ent_base) * (kD * 2);
   const uint32_t n_ent32 = (uint32_t)(geo.n_ent < 0x7fffffff ? geo.n_ent : 0x7fffffff);
+  const int32_t* tbl = PAGED ? lay.table + (int64_t)b * lay.max_blocks : nullptr;
+  const uint32_t emask = PAGED ? (1u << lay.eb_shift) - 1u : 0u;
+  const bool ring = PAGED && lay.ring_rows > 0;
+  const uint64_t wmask = ring ? (uint64_t)(lay.ring_rows - 1) : ~0ull;
+  const uint64_t wrow0 = ring ? (uint64_t)b * lay.ring_rows : (uint64_t)(geo.kv_base + geo.win_lo - n_comp);
+  const uint64_t woff = ring ? (uint64_t)(geo.win_lo - n_comp) : 0ull;  // wraps for compressed slots: unused there
+  const uint64_t kv_a = reinterpret_cast<uint64_t>(kv);
+  const uint64_t win_a = kv_a + wrow0 * (kD * 2);  // packed layout: slot s at win_a + s rows
   auto clamp_round = [](int64_t x) { return (int)(x < 0 ? 0 : (x > NV ? NV : x)); };
   u32x4 r[RPT][4];
   uint32_t okm = 0;  // bit j: pair j's row holds a key
   auto issue = [&](int64_t t0, const int32_t (&ids)[RPT]) {
     const int lim_c = clamp_round(n_comp - t0), lim_h = clamp_round(k_hi - t0);
-    const uint64_t win_t = win_a + (uint64_t)t0 * (kD * 2);
+
     okm = 0;
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
@@ -355,7 +375,15 @@ __global__ __launch_bounds__(NHG * 64) void attn_kernel(
       const uint32_t e = SPARSE ? (uint32_t)ids[j] : (uint32_t)(t0 + v);  // negative ids wrap to huge
       const bool comp = v < lim_c;
       const bool ok = in && v < lim_h && (!comp || e < n_ent32);
-      const uint64_t a = comp ? ent_a + (uint64_t)e * (kD * 2) : win_t + (uint64_t)v * (kD * 2);
+      uint64_t erow = e;
+      if (PAGED) {  // the entry's pool row (a clamped table slot where it is not used)
+        uint32_t j = (comp && ok) ? (e >> lay.eb_shift) : 0u;
+        j = j < (uint32_t)lay.max_blocks ? j : (uint32_t)lay.max_blocks - 1u;
+        erow = ((uint64_t)(uint32_t)tbl[j] << lay.eb_shift) | (e & emask);
+      }
+      const uint64_t a = comp ? ent_a + erow * (kD * 2)
+                              : (PAGED ? kv_a + (wrow0 + ((woff + (uint64_t)(t0 + v)) & wmask)) * (kD * 2)
+                                       : win_a + (uint64_t)(t0 + v) * (kD * 2));
       okm |= (ok ? 1u : 0u) << j;
       const uint16_t* src = reinterpret_cast<const uint16_t*>(ok ? a : ckv_a) + 8 * (pr % 4);
 #pragma unroll
@@ -528,17 +556,18 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
   if (d == 0 && lse_out) lse_out[(int64_t)row * H + h] = (M == -INFINITY) ? -INFINITY : M + __logf(den);
 }
 
-template <bool SPARSE, bool ROPE>
+template <bool SPARSE, bool ROPE, bool PAGED>
 hipError_t launch_nhg(int H, dim3 grid, hipStream_t st, const uint16_t* q, const uint16_t* ckv, const int32_t* idx,
                       int k, const uint16_t* kv, const int64_t* kv_off, const int64_t* ent_off, const int64_t* q_pos,
                       int m, int n_win, int T, float scale_log2, int64_t max_entries, int kps, float* out,
-                      float* lse, float* ws_o, float* ws_lse, float2* ws_rope, const AttnExtras& ex) {
+                      float* lse, float* ws_o, float* ws_lse, float2* ws_rope, const AttnExtras& ex,
+                      const AttnLayout& lay) {
   const int tiles = kps / kKT;  // 1 or 2: gathered in one round; more: the prefetching loop
 #define CSL_ATTN_LAUNCH(NHG, MODE)                                                                              \
-  attn_kernel<NHG, SPARSE, MODE, ROPE><<<grid, NHG * 64, 0, st>>>(q, ckv, idx, k, kv, kv_off, ent_off, q_pos, m, \
+  attn_kernel<NHG, SPARSE, MODE, ROPE, PAGED><<<grid, NHG * 64, 0, st>>>(q, ckv, idx, k, kv, kv_off, ent_off, q_pos, m, \
                                                                   n_win, T, scale_log2, max_entries, kps, out, lse, \
                                                                   ws_o, ws_lse, ex.sink, ex.rope_theta1, \
-                                                                  ws_rope)
+                                                                  ws_rope, lay)
 #define CSL_ATTN_CASE(NHG)                 \
   case NHG:                                \
     if (tiles == 1)                        \
@@ -592,8 +621,15 @@ size_t attn_workspace_bytes(int B, int T, int H, int64_t max_keys) {
 hipError_t launch_attention(bool sparse, const void* q, const void* ckv, const int32_t* idx, int k, const void* kv,
                             const int64_t* kv_off, const int64_t* ent_off, const int64_t* q_pos, int m, int n_win,
                             int B, int T, int H, float scale, int64_t max_entries, int64_t max_keys, float* out,
-                            float* lse, void* ws, const AttnExtras& ex, hipStream_t st) {
+                            float* lse, void* ws, const AttnExtras& ex, hipStream_t st, const PagedView* paged) {
   const AttnPlan p = attn_plan(B, T, max_keys);
+  AttnLayout lay;
+  if (paged) {
+    lay.table = paged->table;
+    lay.max_blocks = paged->max_blocks;
+    lay.eb_shift = paged->eb_shift;
+    lay.ring_rows = paged->ring_rows;
+  }
   const int rows = B * T;
   float* ws_o = static_cast<float*>(ws);
   float* ws_lse = ws_o ? ws_o + (size_t)p.nsplit * rows * H * kD : nullptr;
@@ -605,12 +641,17 @@ hipError_t launch_attention(bool sparse, const void* q, const void* ckv, const i
   const uint16_t* q16 = static_cast<const uint16_t*>(q);
   const uint16_t* c16 = static_cast<const uint16_t*>(ckv);
   const uint16_t* k16 = static_cast<const uint16_t*>(kv);
-#define CSL_ATTN_NHG(SP, RP)                                                                                    \
-  launch_nhg<SP, RP>(H, grid, st, q16, c16, idx, k, k16, kv_off, ent_off, q_pos, m, n_win, T, sl2, max_entries, \
-                     p.keys_per_split, out, lse, ws_o, ws_lse, ws_rope, ex)
+#define CSL_ATTN_NHG(SP, RP, PG)                                                                                \
+  launch_nhg<SP, RP, PG>(H, grid, st, q16, c16, idx, k, k16, kv_off, ent_off, q_pos, m, n_win, T, sl2,         \
+                         max_entries, p.keys_per_split, out, lse, ws_o, ws_lse, ws_rope, ex, lay)
   const bool rope = ex.rope_dims > 0;
-  hipError_t e = sparse ? (rope ? CSL_ATTN_NHG(true, true) : CSL_ATTN_NHG(true, false))
-                        : (rope ? CSL_ATTN_NHG(false, true) : CSL_ATTN_NHG(false, false));
+  hipError_t e;
+  if (paged)
+    e = sparse ? (rope ? CSL_ATTN_NHG(true, true, true) : CSL_ATTN_NHG(true, false, true))
+               : (rope ? CSL_ATTN_NHG(false, true, true) : CSL_ATTN_NHG(false, false, true));
+  else
+    e = sparse ? (rope ? CSL_ATTN_NHG(true, true, false) : CSL_ATTN_NHG(true, false, false))
+               : (rope ? CSL_ATTN_NHG(false, true, false) : CSL_ATTN_NHG(false, false, false));
 #undef CSL_ATTN_NHG
   if (e != hipSuccess || p.nsplit <= 1) return e;
   const dim3 mgrid((unsigned)rows, (unsigned)((H * kD + 255) / 256));

@@ -14,10 +14,10 @@ template <int TPE, int RS, int RSX, bool HAS_Z, bool OUT_BF16, bool DUAL>
 __global__ __launch_bounds__(256) void compress_kernel(
     const uint16_t* __restrict__ kv, const uint16_t* __restrict__ z, const uint16_t* __restrict__ kv_b,
     const uint16_t* __restrict__ z_b, const int64_t* __restrict__ kv_off, const int64_t* __restrict__ ent_off,
-    const int64_t* __restrict__ first_entry, int D, int m, int64_t max_new, void* __restrict__ out) {
+    const int64_t* __restrict__ first_entry, int D, int m, int64_t max_new, void* __restrict__ out, PagedView pg) {
   // long chunks split over waves hold 8 rows in flight per thread
   compress_block<256, TPE, RS, HAS_Z, OUT_BF16, (RSX > 1 ? 8 : 4), RSX, DUAL>(
-      kv, z, kv_off, ent_off, first_entry, D, m, max_new, out, blockIdx.y, blockIdx.x, kv_b, z_b);
+      kv, z, kv_off, ent_off, first_entry, D, m, max_new, out, blockIdx.y, blockIdx.x, kv_b, z_b, pg);
 }
 
 struct CompressArgs {
@@ -27,6 +27,7 @@ struct CompressArgs {
   int64_t max_new;
   void* out;
   bool out_bf16;
+  PagedView pg;
 };
 
 template <int TPE, int RS, int RSX, bool DUAL>
@@ -40,7 +41,7 @@ hipError_t launch_tpe_rs(const CompressArgs& a, hipStream_t st) {
   const uint16_t* zb16 = static_cast<const uint16_t*>(a.z_b);
 #define CSL_COMPRESS_LAUNCH(HZ, OB)                                                                     \
   compress_kernel<TPE, RS, RSX, HZ, OB, DUAL><<<grid, 256, 0, st>>>(k16, z16, kb16, zb16, a.kv_off, a.ent_off, \
-                                                                  a.first, a.D, a.m, a.max_new, a.out)
+                                                                  a.first, a.D, a.m, a.max_new, a.out, a.pg)
   if (a.z) {
     if (a.out_bf16) CSL_COMPRESS_LAUNCH(true, true);
     else CSL_COMPRESS_LAUNCH(true, false);
@@ -83,16 +84,18 @@ hipError_t launch_d(const CompressArgs& a, hipStream_t st) {
 
 hipError_t launch_compress(const void* kv, const void* z, const int64_t* kv_off, const int64_t* ent_off,
                            const int64_t* first_entry, int B, int D, int m, int64_t max_new_entries,
-                           void* out, bool out_bf16, hipStream_t stream) {
-  const CompressArgs a{kv, z, nullptr, nullptr, kv_off, ent_off, first_entry, B, D, m, max_new_entries, out, out_bf16};
+                           void* out, bool out_bf16, hipStream_t stream, const PagedView* paged) {
+  const CompressArgs a{kv, z, nullptr, nullptr, kv_off, ent_off, first_entry, B, D, m, max_new_entries, out, out_bf16,
+                       paged ? *paged : PagedView{}};
   return launch_d<false>(a, stream);
 }
 
 hipError_t launch_compress_overlap(const void* kv_a, const void* z_a, const void* kv_b, const void* z_b,
                                    const int64_t* kv_off, const int64_t* ent_off, const int64_t* first_entry,
                                    int B, int D, int m, int64_t max_new_entries, void* out, bool out_bf16,
-                                   hipStream_t stream) {
-  const CompressArgs a{kv_a, z_a, kv_b, z_b, kv_off, ent_off, first_entry, B, D, m, max_new_entries, out, out_bf16};
+                                   hipStream_t stream, const PagedView* paged) {
+  const CompressArgs a{kv_a, z_a, kv_b, z_b, kv_off, ent_off, first_entry, B, D, m, max_new_entries, out, out_bf16,
+                       paged ? *paged : PagedView{}};
   return launch_d<true>(a, stream);
 }
 

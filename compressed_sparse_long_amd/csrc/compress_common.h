@@ -22,6 +22,7 @@
 #pragma once
 
 #include "device_common.h"
+#include "launch.h"
 
 namespace csl {
 
@@ -34,7 +35,8 @@ __device__ __forceinline__ void compress_block(
     const uint16_t* __restrict__ kv, const uint16_t* __restrict__ z,
     const int64_t* __restrict__ kv_off, const int64_t* __restrict__ ent_off,
     const int64_t* __restrict__ first_entry, int D, int m, int64_t max_new, void* __restrict__ out, int b,
-    int64_t blk, const uint16_t* __restrict__ kv_b = nullptr, const uint16_t* __restrict__ z_b = nullptr) {
+    int64_t blk, const uint16_t* __restrict__ kv_b = nullptr, const uint16_t* __restrict__ z_b = nullptr,
+    PagedView pg = PagedView{}) {
   static_assert(TPE * RS <= kWave, "in-wave row-splits merge by shuffles");
   static_assert(RSX == 1 || TPE * RS == kWave, "cross-wave splits take whole waves");
   constexpr int EPB = NT / (TPE * RS * RSX);  // entries per block
@@ -64,9 +66,13 @@ __device__ __forceinline__ void compress_block(
   }
 
   if (valid) {
-    const int64_t base_row = row0 + i * (int64_t)m;
-    // virtual chunk rows v < m are series-a rows base_row + v; with DUAL, rows m <= v < 2m
-    // are series-b rows base_row + v - 2m (absent for entry 0)
+    // virtual chunk rows v < m are series-a raw rows m*i + v of the sequence; with DUAL, rows
+    // m <= v < 2m are series-b raw rows m*i + v - 2m (absent for entry 0). Raw row r sits at
+    // kv_off[b] + r, or in the paged layout at ring row b * R + (r mod R).
+    const bool ring = pg.ring_rows > 0;
+    const int64_t rbase = ring ? (int64_t)b * pg.ring_rows : row0;
+    const int64_t rmask = ring ? (int64_t)pg.ring_rows - 1 : -1;
+    const int64_t base_rel = i * (int64_t)m;
     const int nv = (DUAL && i > 0) ? 2 * m : m;
     // rows handled by this lane: v = rs + NSPLIT * j
     const int my_rows = (nv > rs) ? (nv - rs + NSPLIT - 1) / NSPLIT : 0;
@@ -78,7 +84,7 @@ __device__ __forceinline__ void compress_block(
         if (u < cnt) {
           const int v = rs + NSPLIT * (j0 + u);
           const bool in_b = DUAL && v >= m;
-          const int64_t e = (base_row + v - (in_b ? 2 * m : 0)) * D + dg * 8;
+          const int64_t e = (rbase + ((base_rel + v - (in_b ? 2 * m : 0)) & rmask)) * D + dg * 8;
           kr[u] = *reinterpret_cast<const u32x4*>((in_b ? kv_b : kv) + e);
           if (HAS_Z) zr[u] = *reinterpret_cast<const u32x4*>((in_b ? z_b : z) + e);
         }
@@ -190,7 +196,13 @@ __device__ __forceinline__ void compress_block(
   }
 
   if (valid && rs == 0) {
-    const int64_t orow = ent_off[b] + i;
+    // entry i of sequence b: row ent_off[b] + i, or its pool row in the paged layout
+    int64_t orow = ent_off[b] + i;
+    if (pg.table) {
+      int64_t j = i >> pg.eb_shift;
+      j = j < pg.max_blocks ? j : pg.max_blocks - 1;
+      orow = ((int64_t)pg.table[(int64_t)b * pg.max_blocks + j] << pg.eb_shift) | (i & ((1 << pg.eb_shift) - 1));
+    }
     float o[8];
 #pragma unroll
     for (int d = 0; d < 8; ++d) o[d] = acc[d] / s[d];

@@ -38,6 +38,16 @@ namespace {
 
 enum { kKeyBF16 = 0, kKeyFP8 = 1, kKeyFP4 = 2 };
 
+// Row of entry s of sequence b in the key array: e_base + s, or in the paged layout its pool
+// row (table entries past the table are clamped: such entries are never loaded)
+template <bool PAGED>
+__device__ __forceinline__ int64_t key_row(const PagedView& pg, int b, int64_t e_base, int64_t s) {
+  if (!PAGED) return e_base + s;
+  int64_t j = s >> pg.eb_shift;
+  j = j < pg.max_blocks ? j : pg.max_blocks - 1;
+  return ((int64_t)pg.table[(int64_t)b * pg.max_blocks + j] << pg.eb_shift) | (s & ((1 << pg.eb_shift) - 1));
+}
+
 // first dim of the 8 k-slots that lane group g supplies for MFMA kk (the key and query
 // operands share this order)
 template <int KT>
@@ -94,12 +104,12 @@ __device__ __forceinline__ bf16x8 key_operand(const u32x4& k) {
                          __builtin_bit_cast(uint32_t, r2), __builtin_bit_cast(uint32_t, r3)});
 }
 
-template <int HI, int NB, int NWAVES, int WQ, int U, int KT>
+template <int HI, int NB, int NWAVES, int WQ, int U, int KT, bool PAGED>
 __global__ __launch_bounds__(NWAVES * 64) void indexer_kernel(
     const uint16_t* __restrict__ qI, const float* __restrict__ w, const void* __restrict__ kI,
     const void* __restrict__ k_scale_v, const int64_t* __restrict__ scale_off, int scale_group,
     const int64_t* __restrict__ ent_off, const int64_t* __restrict__ q_pos, int m, int T,
-    int64_t max_entries, float* __restrict__ scores, int64_t ld, int epw) {
+    int64_t max_entries, float* __restrict__ scores, int64_t ld, int epw, PagedView pg) {
   constexpr int QPB = 16 / HI;       // query rows per A tile
   constexpr int QPW = NB * QPB;      // query rows per wave
   constexpr int WE = NWAVES / WQ;    // key sub-ranges per block
@@ -174,7 +184,7 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_kernel(
     for (int u = 0; u < U; ++u) {
       const int64_t s = s0 + u * 16 + c;
       const bool ok = s < e_end;
-      load_key_tile<KT>(kI, k_mx, e_base + s, ok, g, kb[u][0], kb[u][1]);
+      load_key_tile<KT>(kI, k_mx, key_row<PAGED>(pg, b, e_base, s), ok, g, kb[u][0], kb[u][1]);
       if (FP8) sc[u] = ok ? k_scale[scale_off[b] + s / scale_group] : 0.f;
     }
 #pragma unroll
@@ -248,13 +258,13 @@ __device__ __forceinline__ float head_sum(float v) {
 constexpr int kJobRS = 4;
 constexpr int kJobEntriesPerBlock = kSlice / (16 * kJobRS);
 
-template <int HI, int KT, bool PREP>
+template <int HI, int KT, bool PREP, bool PAGED>
 __global__ __launch_bounds__(kSlice) void indexer_decode_kernel(
     const uint16_t* __restrict__ qI, const float* __restrict__ w, const void* __restrict__ kI,
     const void* __restrict__ k_scale_v, const int64_t* __restrict__ scale_off, int scale_group,
     const int64_t* __restrict__ ent_off, const int64_t* __restrict__ q_pos, int m, int T,
     int64_t max_entries, float* __restrict__ scores, int64_t ld, void* topk_ws, int topk_k, int slot_budget,
-    int key_blocks, CompressJob job) {
+    int key_blocks, CompressJob job, PagedView pg) {
   constexpr int NW = kSlice / kWave;
   constexpr int QPB = 16 / HI;  // query rows per tile
   constexpr int U = 4;
@@ -264,11 +274,18 @@ __global__ __launch_bounds__(kSlice) void indexer_decode_kernel(
   __shared__ __align__(16) float sval[QPB][EPB];
   __shared__ SliceScratch sc;
 
-  if ((int)blockIdx.x >= key_blocks) {
+  // paged: workgroups walk the sequences fastest, so consecutive workgroups take the same slice
+  // of every sequence and the key reads in flight together spread over all sequences' blocks
+  // (blocks handed out round-robin would otherwise be read at a stride of B blocks); the
+  // packed layout keeps the launch order, one sequence's contiguous range at a time
+  const uint32_t lin = blockIdx.x + gridDim.x * blockIdx.z;
+  const int bx = PAGED ? (int)(lin / gridDim.z) : (int)blockIdx.x;
+  const int bz = PAGED ? (int)(lin % gridDim.z) : (int)blockIdx.z;
+  if ((int)bx >= key_blocks) {
     if (blockIdx.y == 0) {
       const uint16_t* k16 = static_cast<const uint16_t*>(job.kv);
       const uint16_t* z16 = static_cast<const uint16_t*>(job.z);
-      const int64_t blk = (int64_t)blockIdx.x - key_blocks;
+      const int64_t blk = (int64_t)bx - key_blocks;
       if (job.kv_b) {
         // overlapped pair: up to 2m <= 16 rows per entry, one row in flight per thread (the
         // job hides under the key stream; two would raise the whole kernel's register count)
@@ -276,18 +293,18 @@ __global__ __launch_bounds__(kSlice) void indexer_decode_kernel(
         const uint16_t* zb16 = static_cast<const uint16_t*>(job.z_b);
         if (z16)
           compress_block<kSlice, 16, kJobRS, true, true, 1, 1, true>(k16, z16, job.kv_off, ent_off, job.first_entry,
-                                                                     128, job.m, job.max_new, job.out, blockIdx.z,
-                                                                     blk, kb16, zb16);
+                                                                     128, job.m, job.max_new, job.out, bz,
+                                                                     blk, kb16, zb16, pg);
         else
           compress_block<kSlice, 16, kJobRS, false, true, 1, 1, true>(k16, z16, job.kv_off, ent_off, job.first_entry,
-                                                                      128, job.m, job.max_new, job.out, blockIdx.z,
-                                                                      blk, kb16, zb16);
+                                                                      128, job.m, job.max_new, job.out, bz,
+                                                                      blk, kb16, zb16, pg);
       } else if (z16) {
         compress_block<kSlice, 16, kJobRS, true, true, 1>(k16, z16, job.kv_off, ent_off, job.first_entry, 128, job.m,
-                                                       job.max_new, job.out, blockIdx.z, blk);
+                                                       job.max_new, job.out, bz, blk, nullptr, nullptr, pg);
       } else {
         compress_block<kSlice, 16, kJobRS, false, true, 1>(k16, z16, job.kv_off, ent_off, job.first_entry, 128, job.m,
-                                                        job.max_new, job.out, blockIdx.z, blk);
+                                                        job.max_new, job.out, bz, blk, nullptr, nullptr, pg);
       }
     }
     return;
@@ -296,18 +313,43 @@ __global__ __launch_bounds__(kSlice) void indexer_decode_kernel(
   const int lane = threadIdx.x % kWave;
   const int g = lane / 16;
   const int c = lane % 16;
-  const int b = blockIdx.z;
+  const int b = bz;
   const int t0 = blockIdx.y * QPB;
   constexpr bool FP8 = KT == kKeyFP8;
   const float* k_scale = static_cast<const float*>(k_scale_v);   // fp8: per entry group
   const uint8_t* k_mx = static_cast<const uint8_t*>(k_scale_v);  // MXFP4: E8M0 per block
 
+  const int64_t wg_e0 = (int64_t)bx * EPB;
+  const int64_t e0 = wg_e0 + (int64_t)wave * EPW;
   const int64_t e_base = ent_off[b];
   const int64_t n_ent = ent_off[b + 1] - e_base;
+  // paged layout: the pool rows of this lane's keys depend only on the block's position, so
+  // their table entries load together with the entry offsets and the keys wait for one
+  // round trip, not two
+  int64_t prow[U];
+  if (PAGED) {
+    if (pg.eb_shift >= 4) {
+      // blocks of 16 or more entries: each 16-key tile lies in one block, so its table entry
+      // is the same for the whole wave; the table is read-only for the kernel's lifetime and
+      // a constant-space read issues as a scalar load, all four before any is used
+      const __attribute__((address_space(4))) int32_t* tbl =
+          (const __attribute__((address_space(4))) int32_t*)(pg.table + (int64_t)b * pg.max_blocks);
+      const uint32_t we0 = (uint32_t)wg_e0 + (uint32_t)__builtin_amdgcn_readfirstlane(threadIdx.x / kWave) * EPW;
+      const uint32_t sh = (uint32_t)pg.eb_shift, jmax = (uint32_t)pg.max_blocks - 1u;
+      uint32_t blk[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) blk[u] = (uint32_t)tbl[min((we0 + u * 16) >> sh, jmax)];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        prow[u] = ((int64_t)blk[u] << sh) | (int64_t)((we0 + u * 16 + c) & ((1u << sh) - 1u));
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) prow[u] = key_row<true>(pg, b, 0, e0 + u * 16 + c);
+    }
+  }
+
   const int64_t n_load = n_ent < max_entries ? n_ent : max_entries;
-  const int64_t wg_e0 = (int64_t)blockIdx.x * EPB;
   if (wg_e0 >= n_load) return;  // the whole slice lies past this sequence: nothing to score or list
-  const int64_t e0 = wg_e0 + (int64_t)wave * EPW;
   const int64_t e_end = min(e0 + EPW, n_load);
 
   // key tiles first: they depend on nothing but the sequence's entry range
@@ -315,7 +357,7 @@ __global__ __launch_bounds__(kSlice) void indexer_decode_kernel(
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t s = e0 + u * 16 + c;
-    load_key_tile<KT>(kI, k_mx, e_base + s, s < e_end, g, kb[u][0], kb[u][1]);
+    load_key_tile<KT>(kI, k_mx, PAGED ? prow[u] : e_base + s, s < e_end, g, kb[u][0], kb[u][1]);
   }
   float my_scale = 1.f;  // fp8 group scale of this lane's entry on the way out
   if (FP8 && e0 + lane < e_end) my_scale = k_scale[scale_off[b] + (e0 + lane) / scale_group];
@@ -371,8 +413,8 @@ __global__ __launch_bounds__(kSlice) void indexer_decode_kernel(
       const uint32_t x = (s < n) ? score_key(mine) : 0u;
       const TopkRowWs rw = topk_row_ws(topk_ws, (int64_t)b * T, max_entries, slot_budget);
       const int R = topk_row_slots(n, max_entries, slot_budget);
-      slice_candidates(x, slice_quota(n, topk_k, R), topk_wave_list(n, topk_k), R, sc, wg_e0, &rw.cuts[blockIdx.x],
-                       rw.slots + (int64_t)blockIdx.x * R);
+      slice_candidates(x, slice_quota(n, topk_k, R), topk_wave_list(n, topk_k), R, sc, wg_e0, &rw.cuts[bx],
+                       rw.slots + (int64_t)bx * R);
     }
   }
 }
@@ -381,7 +423,8 @@ template <int HI, int KT>
 hipError_t launch_hi(const void* qI, const float* w, const void* kI, const void* k_scale,
                      const int64_t* scale_off, int scale_group, const int64_t* ent_off,
                      const int64_t* q_pos, int m, int B, int T, int64_t max_entries, float* scores,
-                     int64_t ld, void* topk_ws, int topk_k, hipStream_t st, const CompressJob* job) {
+                     int64_t ld, void* topk_ws, int topk_k, hipStream_t st, const CompressJob* job,
+                     const PagedView& pg) {
   const uint16_t* q16 = static_cast<const uint16_t*>(qI);
   const int rows = B * T;
   const bool prep = indexer_prepares_topk(topk_ws, T, max_entries);
@@ -393,25 +436,34 @@ hipError_t launch_hi(const void* qI, const float* w, const void* kI, const void*
     const int64_t gx = (max_entries + epw - 1) / epw;
     const int gy = (T + QPW * WQ - 1) / (QPW * WQ);
     dim3 grid((unsigned)(gx > 0 ? gx : 1), (unsigned)gy, (unsigned)B);
-    indexer_kernel<HI, NB, NW, WQ, U, KT><<<grid, NW * 64, 0, st>>>(q16, w, kI, k_scale, scale_off, scale_group,
-                                                                    ent_off, q_pos, m, T, max_entries, scores, ld, epw);
+    if (pg.table)
+      indexer_kernel<HI, NB, NW, WQ, U, KT, true><<<grid, NW * 64, 0, st>>>(
+          q16, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, T, max_entries, scores, ld, epw, pg);
+    else
+      indexer_kernel<HI, NB, NW, WQ, U, KT, false><<<grid, NW * 64, 0, st>>>(
+          q16, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, T, max_entries, scores, ld, epw, pg);
   } else {
     // decode tiling: 8 waves per block, each with one pass over 64 keys (plus the job's blocks)
     constexpr int QPB = 16 / HI;
     const int64_t kb = (max_entries + kSlice - 1) / kSlice;
     const int64_t jb = job ? (job->max_new + kJobEntriesPerBlock - 1) / kJobEntriesPerBlock : 0;
     const int gy = (T + QPB - 1) / QPB;
+    if ((kb + jb) * B >= ((int64_t)1 << 32)) return hipErrorInvalidValue;  // the kernel's linear block id
     dim3 grid((unsigned)(kb + jb), (unsigned)gy, (unsigned)B);
     const CompressJob none{};
     const CompressJob& cj = job ? *job : none;
-    if (prep)
-      indexer_decode_kernel<HI, KT, true><<<grid, kSlice, 0, st>>>(q16, w, kI, k_scale, scale_off, scale_group, ent_off,
-                                                                    q_pos, m, T, max_entries, scores, ld, topk_ws, topk_k,
-                                                                    topk_slot_budget(max_entries, topk_k), (int)kb, cj);
-    else
-      indexer_decode_kernel<HI, KT, false><<<grid, kSlice, 0, st>>>(q16, w, kI, k_scale, scale_off, scale_group,
-                                                                     ent_off, q_pos, m, T, max_entries, scores, ld,
-                                                                     nullptr, 0, 0, (int)kb, cj);
+#define CSL_IDX_DECODE(PREP, PG)                                                                                    \
+  indexer_decode_kernel<HI, KT, PREP, PG><<<grid, kSlice, 0, st>>>(                                                 \
+      q16, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, T, max_entries, scores, ld,                  \
+      PREP ? topk_ws : nullptr, PREP ? topk_k : 0, PREP ? topk_slot_budget(max_entries, topk_k) : 0, (int)kb, cj, pg)
+    if (prep) {
+      if (pg.table) CSL_IDX_DECODE(true, true);
+      else CSL_IDX_DECODE(true, false);
+    } else {
+      if (pg.table) CSL_IDX_DECODE(false, true);
+      else CSL_IDX_DECODE(false, false);
+    }
+#undef CSL_IDX_DECODE
   }
   return hipGetLastError();
 }
@@ -420,11 +472,12 @@ template <int KT>
 hipError_t launch_kt(int HI, const void* qI, const float* w, const void* kI, const void* k_scale,
                       const int64_t* scale_off, int scale_group, const int64_t* ent_off,
                       const int64_t* q_pos, int m, int B, int T, int64_t max_entries, float* scores,
-                      int64_t ld, void* topk_ws, int topk_k, hipStream_t st, const CompressJob* job) {
+                      int64_t ld, void* topk_ws, int topk_k, hipStream_t st, const CompressJob* job,
+                      const PagedView& pg) {
 #define CSL_IDX_CASE(H)                                                                                          \
   case H:                                                                                                        \
     return launch_hi<H, KT>(qI, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T, max_entries, \
-                             scores, ld, topk_ws, topk_k, st, job);
+                             scores, ld, topk_ws, topk_k, st, job, pg);
   switch (HI) {
     CSL_IDX_CASE(1)
     CSL_IDX_CASE(2)
@@ -454,10 +507,11 @@ hipError_t launch_indexer(const void* qI, const float* w, const void* kI, int ke
                           const int64_t* scale_off, int scale_group, const int64_t* ent_off,
                           const int64_t* q_pos, int m, int B, int T, int HI, int64_t max_entries,
                           float* scores, int64_t ld, void* topk_ws, int topk_k, hipStream_t stream,
-                          const CompressJob* job) {
+                          const CompressJob* job, const PagedView* paged) {
+  const PagedView pg = paged ? *paged : PagedView{};
 #define CSL_IDX_KT(KT)                                                                                     \
   launch_kt<KT>(HI, qI, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T, max_entries, scores, \
-                ld, topk_ws, topk_k, stream, job)
+                ld, topk_ws, topk_k, stream, job, pg)
   switch (key_type) {
     case kKeyFP8: return CSL_IDX_KT(kKeyFP8);
     case kKeyFP4: return CSL_IDX_KT(kKeyFP4);

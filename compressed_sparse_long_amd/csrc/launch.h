@@ -8,15 +8,27 @@
 
 namespace csl {
 
+// Paged heterogeneous cache ([P2] "KV Cache Management"): compressed entries (and CSA
+// indexer keys) in a pool of blocks of 2^eb_shift entries, block j of sequence b at pool
+// block table[b * max_blocks + j]; raw rows in a per-sequence ring of ring_rows rows, raw
+// row r of sequence b at ring row b * ring_rows + r mod ring_rows.
+struct PagedView {
+  const int32_t* table = nullptr;
+  int max_blocks = 0;
+  int eb_shift = 0;
+  int ring_rows = 0;
+  int64_t pool_rows = 0;
+};
+
 hipError_t launch_compress(const void* kv, const void* z, const int64_t* kv_off, const int64_t* ent_off,
                            const int64_t* first_entry, int B, int D, int m, int64_t max_new_entries,
-                           void* out, bool out_bf16, hipStream_t stream);
+                           void* out, bool out_bf16, hipStream_t stream, const PagedView* paged = nullptr);
 // CSA's overlapped compression: entry i pools series-a rows [m*i, m*i + m) with series-b rows
 // [m*(i-1), m*i) under one softmax per dimension (entry 0: series a alone)
 hipError_t launch_compress_overlap(const void* kv_a, const void* z_a, const void* kv_b, const void* z_b,
                                    const int64_t* kv_off, const int64_t* ent_off, const int64_t* first_entry,
                                    int B, int D, int m, int64_t max_new_entries, void* out, bool out_bf16,
-                                   hipStream_t stream);
+                                   hipStream_t stream, const PagedView* paged = nullptr);
 
 // Newest-chunk compression (bf16 out, D = 128, m <= 8; one series or the overlapped pair) that
 // the decode indexer can run in spare workgroups of its own launch.
@@ -38,7 +50,7 @@ hipError_t launch_indexer(const void* qI, const float* w, const void* kI, int ke
                           const int64_t* scale_off, int scale_group, const int64_t* ent_off,
                           const int64_t* q_pos, int m, int B, int T, int HI, int64_t max_entries,
                           float* scores, int64_t ld, void* topk_ws, int topk_k, hipStream_t stream,
-                          const CompressJob* job = nullptr);
+                          const CompressJob* job = nullptr, const PagedView* paged = nullptr);
 // whether launch_indexer leaves top-k candidate lists in topk_ws for these shapes
 bool indexer_prepares_topk(const void* topk_ws, int T, int64_t max_entries);
 // whether launch_indexer can carry a CompressJob for these shapes (decode tiling, D = 128, m <= 8)
@@ -69,6 +81,7 @@ size_t attn_workspace_bytes(int B, int T, int H, int64_t max_keys);
 hipError_t launch_attention(bool sparse, const void* q, const void* ckv, const int32_t* idx, int k, const void* kv,
                             const int64_t* kv_off, const int64_t* ent_off, const int64_t* q_pos, int m, int n_win,
                             int B, int T, int H, float scale, int64_t max_entries, int64_t max_keys, float* out,
-                            float* lse, void* ws, const AttnExtras& ex, hipStream_t stream);
+                            float* lse, void* ws, const AttnExtras& ex, hipStream_t stream,
+                            const PagedView* paged = nullptr);
 
 }  // namespace csl

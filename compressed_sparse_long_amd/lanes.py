@@ -15,7 +15,7 @@ import math
 
 import torch
 
-from . import (attn_workspace_bytes, compress_kv, compress_kv_overlap, csa_decode_step, hca_attn_decode, indexer_scores, sparse_attn_decode,
+from . import (PagedCache, attn_workspace_bytes, compress_kv, compress_kv_overlap, csa_decode_step, hca_attn_decode, indexer_scores, sparse_attn_decode,
                topk_select, topk_workspace_bytes)
 
 
@@ -52,6 +52,7 @@ class _Lane:
         self.sink = None
         self.rope_dims = 0
         self.rope_base = 10000.0
+        self.paged = None  # PagedCache once the cache moved into the paged layout
 
     def compress_all(self):
         for c in self.ckv_copies:
@@ -60,7 +61,93 @@ class _Lane:
     def compress_new(self, r: int = 0):
         if self.n_new:
             compress_kv(self.kv, self.z, self.kv_off, self.ent_off, self.m, self.ckv_copies[r % len(self.ckv_copies)],
-                        first_entry=self.first_new, max_new_entries=self.n_new)
+                        first_entry=self.first_new, max_new_entries=self.n_new, paged=self.paged)
+
+    def paginate(self, ring_rows: int = 256, block_entries: int | None = None, spare_blocks: int = 5,
+                 seed: int = 0, order: str = "random"):
+        """Move the lane's compressed cache (and its indexer keys) into a paged pool and its
+        raw rows into per-sequence rings ([P2] "KV Cache Management": a classical cache of
+        blocks covering lcm(m, m') = 128 raw tokens, 128 / m entries each, and a state cache of
+        the newest raw rows). Pool blocks are handed out in a seeded random order (``order`` =
+        "random"), or round-robin over the sequences as concurrent growth would allocate them
+        ("interleaved"), or each sequence's blocks consecutively ("sequential"), with some spare
+        blocks left free, so every lookup goes through the block table. The compressed
+        cache must be complete (compress_all) first; afterwards every call reads the paged
+        buffers."""
+        dev = self.device
+        lane = self.lane
+        eb = block_entries or max(1, 128 // self.m)
+        E = lane.entries
+        nblk = [(e + eb - 1) // eb for e in E]
+        max_blocks = max(nblk + [1])
+        total = sum(nblk) + spare_blocks
+        table = torch.zeros((self.B, max_blocks), dtype=torch.int32)
+        if order == "random":
+            g = torch.Generator().manual_seed(seed)
+            perm = torch.randperm(total, generator=g).to(torch.int32)
+            used = 0
+            for b, n in enumerate(nblk):
+                table[b, :n] = perm[used:used + n]
+                used += n
+        elif order == "sequential":  # each sequence's blocks consecutive, in order
+            nxt = 0
+            for b, n in enumerate(nblk):
+                table[b, :n] = torch.arange(nxt, nxt + n, dtype=torch.int32)
+                nxt += n
+        else:  # block j of every sequence before block j + 1 of any
+            nxt = 0
+            for j in range(max_blocks):
+                for b, n in enumerate(nblk):
+                    if j < n:
+                        table[b, j] = nxt
+                        nxt += 1
+        # pool row of every entry, sequence by sequence (packed entry order)
+        rows = []
+        for b, e in enumerate(E):
+            i = torch.arange(e, dtype=torch.int64)
+            rows.append(table[b].to(torch.int64)[i // eb] * eb + i % eb)
+        prow = torch.cat(rows).to(dev) if rows else torch.zeros(0, dtype=torch.int64, device=dev)
+        pool_rows = total * eb
+
+        def to_pool(x):
+            out = torch.zeros((pool_rows,) + tuple(x.shape[1:]), dtype=x.dtype, device=dev)
+            if prow.numel():
+                out.index_copy_(0, prow, x[:prow.numel()])
+            return out
+
+        # ring row of the newest ring_rows raw rows of every sequence
+        src, dst = [], []
+        offs = lane.kv_off()
+        for b, n in enumerate(lane.lengths):
+            r = torch.arange(max(0, n - ring_rows), n, dtype=torch.int64)
+            src.append(offs[b] - offs[0] + r)
+            dst.append(b * ring_rows + r % ring_rows)
+        src = torch.cat(src).to(dev)
+        dst = torch.cat(dst).to(dev)
+        row0 = offs[0]
+
+        def to_ring(x):
+            if x is None:
+                return None
+            out = torch.zeros((self.B * ring_rows, x.shape[1]), dtype=x.dtype, device=dev)
+            out.index_copy_(0, dst, x[row0:].index_select(0, src))
+            return out
+
+        self.ckv_copies = [to_pool(c) for c in self.ckv_copies]
+        self.ckv = self.ckv_copies[0]
+        self.kv, self.z = to_ring(self.kv), to_ring(self.z)
+        if getattr(self, "kv_b", None) is not None:
+            self.kv_b, self.z_b = to_ring(self.kv_b), to_ring(self.z_b)
+        if hasattr(self, "kI_copies"):
+            self.kI_copies = [to_pool(c) for c in self.kI_copies]
+            self.kI = self.kI_copies[0]
+            if self.k_format == "mxfp4":
+                self.k_scale_copies = [to_pool(c) for c in self.k_scale_copies]
+                self.k_scale = self.k_scale_copies[0]
+        # row offsets now only count rows: rebase the raw-row prefix sums at 0
+        self.kv_off = self.kv_off - self.kv_off[0]
+        self.paged = PagedCache(table.to(dev), eb, pool_rows, ring_rows)
+        self.pool_rows = pool_rows
 
     def rotate(self, copies: int):
         """Keep ``copies`` independent copies of the large per-step inputs (compressed cache,
@@ -106,7 +193,7 @@ class CsaLane(_Lane):
         if self.n_new:
             compress_kv_overlap(self.kv, self.z, self.kv_b, self.z_b, self.kv_off, self.ent_off, self.m,
                                 self.ckv_copies[r % len(self.ckv_copies)], first_entry=self.first_new,
-                                max_new_entries=self.n_new)
+                                max_new_entries=self.n_new, paged=self.paged)
 
     def rotate(self, copies: int):
         super().rotate(copies)
@@ -120,7 +207,7 @@ class CsaLane(_Lane):
                        self.scores, max_entries=self.max_entries,
                        k_scale=self.k_scale_copies[r % len(self.k_scale_copies)], scale_off=self.scale_off,
                        scale_group=self.scale_group, topk_ws=self.topk_ws if self.fused else None, topk_k=self.k,
-                       k_format=self.k_format)
+                       k_format=self.k_format, paged=self.paged)
 
     def select(self):
         topk_select(self.scores, self.ent_off, self.q_pos, self.m, self.k, self.idx, ws=self.topk_ws,
@@ -129,7 +216,8 @@ class CsaLane(_Lane):
     def attend(self, r: int = 0):
         sparse_attn_decode(self.q, self.ckv_copies[r % len(self.ckv_copies)], self.idx, self.kv, self.kv_off,
                            self.ent_off, self.q_pos, self.W, self.out, lse=self.lse, scale=self.scale,
-                           ws=self.attn_ws, sink=self.sink, rope_dims=self.rope_dims, rope_base=self.rope_base)
+                           ws=self.attn_ws, sink=self.sink, rope_dims=self.rope_dims, rope_base=self.rope_base,
+                           paged=self.paged)
 
     def step(self, r: int = 0, fused: bool = True):
         """One decode step on rotated copy r: one csa_decode_step call, or (fused=False) the
@@ -148,7 +236,7 @@ class CsaLane(_Lane):
                         k_scale=self.k_scale_copies[r % len(self.k_scale_copies)], scale_off=self.scale_off,
                         scale_group=self.scale_group, max_entries=self.max_entries, attn_ws=self.attn_ws,
                         kv_b=self.kv_b, z_b=self.z_b, sink=self.sink, rope_dims=self.rope_dims,
-                        rope_base=self.rope_base, k_format=self.k_format)
+                        rope_base=self.rope_base, k_format=self.k_format, paged=self.paged)
 
 
 class HcaLane(_Lane):
@@ -161,7 +249,7 @@ class HcaLane(_Lane):
         hca_attn_decode(self.q, self.ckv_copies[r % len(self.ckv_copies)], self.kv, self.kv_off, self.ent_off,
                         self.q_pos, self.m, self.W, self.out, lse=self.lse, scale=self.scale,
                         max_entries=self.max_entries, ws=self.attn_ws, sink=self.sink, rope_dims=self.rope_dims,
-                        rope_base=self.rope_base)
+                        rope_base=self.rope_base, paged=self.paged)
 
     def step(self, r: int = 0):
         self.compress_new(r)

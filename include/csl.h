@@ -63,11 +63,36 @@ typedef enum {
   CSL_DTYPE_MXFP4 = 3     /* OCP MXFP4: E2M1 codes, two per byte, one E8M0 scale per 32 values */
 } csl_dtype;
 
+/*
+ * Paged heterogeneous cache ([P2] "KV Cache Management"): the compressed entries live in a
+ * classical cache of fixed-size blocks and the raw rows in a per-sequence state cache.
+ * Every call below takes an optional `const csl_paged_cache* paged`; NULL keeps the packed
+ * layout described above. With it:
+ *   - compressed entry e of sequence b (ckv rows, CSA indexer keys and their MXFP4 scales)
+ *     sits at pool row  block_table[b * max_blocks + e / block_entries] * block_entries
+ *     + e % block_entries; the caller allocates the blocks (block_entries = lcm(m, m') / m
+ *     covers lcm(m, m') raw tokens: 32 for CSA's m = 4 beside HCA's m' = 128, 1 for HCA);
+ *   - with ring_rows > 0, raw row r of sequence b (kv, z, and for overlapped compression
+ *     kv_b, z_b) sits at ring row b * ring_rows + r % ring_rows: the state cache keeps the
+ *     newest ring_rows rows of each sequence, which must hold every raw row a call reads
+ *     (the window, the chunks being compressed);
+ *   - kv_off and ent_off still give each sequence's raw-row and entry counts (as prefix
+ *     sums); they no longer place rows.
+ * block_table entries of the blocks a sequence uses, and the ring's rows, are preconditions.
+ */
+typedef struct csl_paged_cache {
+  const int32_t* block_table; /* device int32 [B, max_blocks] */
+  int max_blocks;             /* >= 1 */
+  int block_entries;          /* entries per block, a power of two */
+  int64_t pool_entries;       /* rows of the entry pool, < 2^31 */
+  int ring_rows;              /* 0 (raw rows packed as kv_off says) or a power of two */
+} csl_paged_cache;
+
 /* Message for the last failed call on this thread ("" if none). Never NULL. */
 const char* csl_last_error(void);
 
-/* Library version as MAJOR*10000 + MINOR*100 + PATCH (0.3.0: overlapped compression,
- * attention sink and partial RoPE). */
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH (0.4.0: overlapped compression,
+ * attention sink and partial RoPE, MXFP4 indexer keys, paged cache). */
 int csl_version(void);
 
 /*
@@ -90,7 +115,7 @@ int csl_version(void);
  */
 int csl_compress_kv(const void* kv, const void* z, const int64_t* kv_off, const int64_t* ent_off,
                     const int64_t* first_entry, int B, int D, int m, int64_t max_new_entries,
-                    void* out, int out_dtype, void* stream);
+                    void* out, int out_dtype, const csl_paged_cache* paged, void* stream);
 
 /*
  * compress_kv_overlap -- CSA's overlapped (dual-series) compression ([P2] "Deep Dive", CSA
@@ -114,7 +139,8 @@ int csl_compress_kv(const void* kv, const void* z, const int64_t* kv_off, const 
  */
 int csl_compress_kv_overlap(const void* kv_a, const void* z_a, const void* kv_b, const void* z_b,
                             const int64_t* kv_off, const int64_t* ent_off, const int64_t* first_entry, int B, int D,
-                            int m, int64_t max_new_entries, void* out, int out_dtype, void* stream);
+                            int m, int64_t max_new_entries, void* out, int out_dtype,
+                            const csl_paged_cache* paged, void* stream);
 
 /*
  * indexer_scores -- Lightning-indexer scores ([P5], the indexer score formula;
@@ -153,7 +179,7 @@ int csl_indexer_scores(const void* q_idx, const float* w, const void* k_idx, int
                        const void* k_scale, const int64_t* scale_off, int scale_group,
                        const int64_t* ent_off, const int64_t* q_pos, int m, int B, int T, int HI,
                        int CI, int64_t max_entries, float* scores, int64_t ld, void* topk_ws,
-                       size_t topk_ws_bytes, int topk_k, void* stream);
+                       size_t topk_ws_bytes, int topk_k, const csl_paged_cache* paged, void* stream);
 
 /*
  * topk_select -- top-k compressed entries per query row ([P2] "Deep Dive", CSA top-k
@@ -226,7 +252,7 @@ int csl_sparse_attn_decode(const void* q, const void* ckv, const int32_t* idx, i
                            const void* kv, const int64_t* kv_off, const int64_t* ent_off,
                            const int64_t* q_pos, int n_win, int B, int T, int H, int D, float scale,
                            float* out, float* lse, void* ws, size_t ws_bytes,
-                           const csl_attn_extras* extras, void* stream);
+                           const csl_attn_extras* extras, const csl_paged_cache* paged, void* stream);
 
 /*
  * hca_attn_decode -- HCA dense attention ([P1] section 5.1; [P2] "Heavily Compressed
@@ -239,7 +265,7 @@ int csl_hca_attn_decode(const void* q, const void* ckv, const void* kv, const in
                         const int64_t* ent_off, const int64_t* q_pos, int m, int n_win, int B,
                         int T, int H, int D, float scale, int64_t max_entries, float* out,
                         float* lse, void* ws, size_t ws_bytes, const csl_attn_extras* extras,
-                        void* stream);
+                        const csl_paged_cache* paged, void* stream);
 
 /*
  * csa_decode_step -- one whole CSA step of one layer ([P2] "Putting It Together"; [P1]
@@ -306,6 +332,8 @@ typedef struct csl_csa_step {
   const float* sink;          /* device fp32 [H], or NULL */
   int rope_dims;
   float rope_base;
+  /* paged cache (NULL: packed) */
+  const csl_paged_cache* paged;
 } csl_csa_step;
 
 int csl_csa_decode_step(const csl_csa_step* s, void* stream);

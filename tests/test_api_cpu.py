@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, s), s
     import compressed_sparse_long_amd as csl
     assert sorted(csl.EXPORTS) == declared_symbols()
-    assert csl.version() == 300
+    assert csl.version() == 400
 
 
 P = ctypes.c_void_p
@@ -56,43 +56,43 @@ def _err(lib):
 
 def test_compress_validation(lib):
     f = lib.csl_compress_kv
-    f.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64, P, ctypes.c_int, P]
-    assert f(None, None, FAKE, FAKE, None, 1, 128, 4, 10, FAKE, 1, None) == 1
+    f.argtypes = [P, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64, P, ctypes.c_int, P, P]
+    assert f(None, None, FAKE, FAKE, None, 1, 128, 4, 10, FAKE, 1, None, None) == 1
     assert "null" in _err(lib)
-    assert f(FAKE, None, FAKE, FAKE, None, 1, 96, 4, 10, FAKE, 1, None) == 2
-    assert f(FAKE, None, FAKE, FAKE, None, 1, 128, 0, 10, FAKE, 1, None) == 1
-    assert f(FAKE, None, FAKE, FAKE, None, 1, 128, 4, 10, FAKE, 2, None) == 2
-    assert f(FAKE, None, FAKE, FAKE, None, -1, 128, 4, 10, FAKE, 1, None) == 1
-    assert f(P((1 << 20) + 2), None, FAKE, FAKE, None, 1, 128, 4, 10, FAKE, 1, None) == 1
+    assert f(FAKE, None, FAKE, FAKE, None, 1, 96, 4, 10, FAKE, 1, None, None) == 2
+    assert f(FAKE, None, FAKE, FAKE, None, 1, 128, 0, 10, FAKE, 1, None, None) == 1
+    assert f(FAKE, None, FAKE, FAKE, None, 1, 128, 4, 10, FAKE, 2, None, None) == 2
+    assert f(FAKE, None, FAKE, FAKE, None, -1, 128, 4, 10, FAKE, 1, None, None) == 1
+    assert f(P((1 << 20) + 2), None, FAKE, FAKE, None, 1, 128, 4, 10, FAKE, 1, None, None) == 1
     assert "aligned" in _err(lib)
     # nothing to do is a success without touching the device
-    assert f(FAKE, None, FAKE, FAKE, None, 0, 128, 4, 10, FAKE, 1, None) == 0
+    assert f(FAKE, None, FAKE, FAKE, None, 0, 128, 4, 10, FAKE, 1, None, None) == 0
     assert _err(lib) == ""
 
 
 def test_compress_overlap_validation(lib):
     f = lib.csl_compress_kv_overlap
-    f.argtypes = [P, P, P, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64, P, ctypes.c_int, P]
+    f.argtypes = [P, P, P, P, P, P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64, P, ctypes.c_int, P, P]
     # kv_a, z_a, kv_b, z_b, kv_off, ent_off, first, B, D, m, max_new, out, dtype, stream
-    assert f(FAKE, None, None, None, FAKE, FAKE, None, 1, 128, 4, 10, FAKE, 1, None) == 1
+    assert f(FAKE, None, None, None, FAKE, FAKE, None, 1, 128, 4, 10, FAKE, 1, None, None) == 1
     assert "kv_b" in _err(lib)
-    assert f(FAKE, FAKE, FAKE, None, FAKE, FAKE, None, 1, 128, 4, 10, FAKE, 1, None) == 1
+    assert f(FAKE, FAKE, FAKE, None, FAKE, FAKE, None, 1, 128, 4, 10, FAKE, 1, None, None) == 1
     assert "both" in _err(lib)
-    assert f(FAKE, None, FAKE, FAKE, FAKE, FAKE, None, 1, 128, 4, 10, FAKE, 1, None) == 1
-    assert f(FAKE, None, P((1 << 20) + 8), None, FAKE, FAKE, None, 1, 128, 4, 10, FAKE, 1, None) == 1
+    assert f(FAKE, None, FAKE, FAKE, FAKE, FAKE, None, 1, 128, 4, 10, FAKE, 1, None, None) == 1
+    assert f(FAKE, None, P((1 << 20) + 8), None, FAKE, FAKE, None, 1, 128, 4, 10, FAKE, 1, None, None) == 1
     assert "aligned" in _err(lib)
-    assert f(FAKE, None, FAKE, None, FAKE, FAKE, None, 1, 96, 4, 10, FAKE, 1, None) == 2
+    assert f(FAKE, None, FAKE, None, FAKE, FAKE, None, 1, 96, 4, 10, FAKE, 1, None, None) == 2
     assert _err(lib).startswith("compress_kv_overlap:")
-    assert f(FAKE, None, FAKE, None, FAKE, FAKE, None, 1, 128, 70000, 10, FAKE, 1, None) == 1
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 128, 4, 10, FAKE, 0, None) == 0
+    assert f(FAKE, None, FAKE, None, FAKE, FAKE, None, 1, 128, 70000, 10, FAKE, 1, None, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 128, 4, 10, FAKE, 0, None, None) == 0
     assert _err(lib) == ""
 
 
 def test_indexer_validation(lib):
     f = lib.csl_indexer_scores
     I, L = ctypes.c_int, ctypes.c_int64
-    f.argtypes = [P, P, P, I, P, P, I, P, P, I, I, I, I, I, L, P, L, P, ctypes.c_size_t, I, P]
-    args = [FAKE, FAKE, FAKE, 0, None, None, 64, FAKE, FAKE, 4, 1, 1, 8, 64, 1000, FAKE, 1000, None, 0, 0, None]
+    f.argtypes = [P, P, P, I, P, P, I, P, P, I, I, I, I, I, L, P, L, P, ctypes.c_size_t, I, P, P]
+    args = [FAKE, FAKE, FAKE, 0, None, None, 64, FAKE, FAKE, 4, 1, 1, 8, 64, 1000, FAKE, 1000, None, 0, 0, None, None]
     bad = list(args); bad[12] = 3
     assert f(*bad) == 2                       # HI
     bad = list(args); bad[13] = 128
@@ -143,8 +143,9 @@ def test_attention_validation_and_workspace(lib):
     I = ctypes.c_int
     import compressed_sparse_long_amd as csl
     EX = ctypes.POINTER(csl._AttnExtras)
-    f.argtypes = [P, P, P, I, P, P, P, P, I, I, I, I, I, ctypes.c_float, P, P, P, ctypes.c_size_t, EX, P]
-    base = [FAKE, FAKE, FAKE, 1024, FAKE, FAKE, FAKE, FAKE, 128, 4, 1, 64, 128, 0.088, FAKE, None, FAKE, w3, None, None]
+    f.argtypes = [P, P, P, I, P, P, P, P, I, I, I, I, I, ctypes.c_float, P, P, P, ctypes.c_size_t, EX, P, P]
+    base = [FAKE, FAKE, FAKE, 1024, FAKE, FAKE, FAKE, FAKE, 128, 4, 1, 64, 128, 0.088, FAKE, None, FAKE, w3, None, None,
+            None]
     bad = list(base); bad[12] = 64
     assert f(*bad) == 2                       # D
     bad = list(base); bad[11] = 24
@@ -164,13 +165,22 @@ def test_attention_validation_and_workspace(lib):
     assert "rope" in _err(lib) or "sink" in _err(lib)
     g = lib.csl_hca_attn_decode
     L = ctypes.c_int64
-    g.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, ctypes.c_float, L, P, P, P, ctypes.c_size_t, EX, P]
+    g.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, ctypes.c_float, L, P, P, P, ctypes.c_size_t, EX, P, P]
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 128, 8, 1, 64, 128, 0.088, 1024, FAKE, None, FAKE, 0, None,
-             None) == 1
+             None, None) == 1
     ex = ctypes.pointer(csl._AttnExtras(None, 64, 0.5))
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 128, 128, 8, 1, 64, 128, 0.088, 1024, FAKE, None, FAKE, 1 << 30, ex,
-             None) == 1
+             None, None) == 1
     assert "rope_base" in _err(lib)
+    # paged cache descriptor: block size, ring size, id scratch
+    PC = csl._PagedCache
+    for pc, status in ((PC(None, 4, 32, 1 << 20, 128), 1),          # no table
+                       (PC(FAKE, 4, 24, 1 << 20, 128), 1),          # block_entries not a power of two
+                       (PC(FAKE, 4, 32, 1 << 20, 96), 1),           # ring not a power of two
+                       (PC(FAKE, 4, 32, 1 << 20, 64), 1),           # ring smaller than the window
+                       (PC(FAKE, 0, 32, 1 << 20, 128), 1)):         # no blocks
+        bad = list(base); bad[19] = P(ctypes.addressof(pc))
+        assert f(*bad) == status, _err(lib)
 
 
 def test_step_validation(lib):

@@ -229,6 +229,24 @@ def test_csa_decode_1m_mxfp4_keys(lanes_mod):
         _check_csa_row(cl, inp, li, b, 0, keys)
 
 
+def test_csa_decode_1m_paged(lanes_mod):
+    """4 x 1M-token CSA decode with the cache paged: compressed entries and indexer keys in a
+    pool of 32-entry blocks (seeded random block order) and raw rows in 256-row rings; every
+    query row against the oracle."""
+    print("workload csa_decode_1m (paged): generating inputs", flush=True)
+    inp = synth.generate("csa_decode_1m")
+    (cl,) = lanes_mod.build_lanes(inp)
+    cl.compress_all()
+    cl.paginate(ring_rows=256, seed=3)
+    cl.step()
+    torch.cuda.synchronize()
+    print("workload csa_decode_1m (paged): checking against the oracle", flush=True)
+    li = inp.lanes[0]
+    keys = _csa_keys(li)
+    for b in range(li.lane.B):
+        _check_csa_row(cl, inp, li, b, 0, keys)
+
+
 def test_csa_prefill_8k_on_128k(lanes_mod):
     inp, (cl,) = _run(lanes_mod, "csa_prefill_8k_on_128k")
     li = inp.lanes[0]
