@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--run-workload", default=None,
                     help="replay --steps steps of another synthetic configuration (for profiling) and print "
                          "its mean step time")
+    ap.add_argument("--paged", default=None, choices=("random", "interleaved"),
+                    help="with --run-workload: page every lane's cache first (blocks in this order)")
     return ap.parse_args()
 
 
@@ -162,7 +164,7 @@ def main():
         copy_calibration()
         return
     if args.run_workload:
-        run_workload(args.run_workload, args.steps, args.warmup)
+        run_workload(args.run_workload, args.steps, args.warmup, args.paged, args.copies)
         return
     if args.report_configs:
         report_configs(args.copies, args.cpu_seconds)
@@ -396,32 +398,40 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def run_workload(name: str, steps: int, warmup: int) -> None:
-    """Replay one configuration's whole step (every lane) as a graph; print its mean time."""
+def run_workload(name: str, steps: int, warmup: int, paged: str | None = None, copies: int = 4) -> None:
+    """Replay one configuration's whole step (every lane) as a graph; print its mean time.
+    Each graph holds ``copies`` steps over rotated copies of the large inputs (as in the main
+    measurement); ``paged``: move every lane's cache into a block pool first, blocks in that order."""
     import torch
     import synth
     from compressed_sparse_long_amd import lanes
 
     inp = synth.generate(name)
     ls = lanes.build_lanes(inp)
+    R = max(1, copies)
     for lane in ls:
         lane.compress_all()
+        if paged:
+            lane.paginate(ring_rows=256, order=paged)
+        lane.rotate(R)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for lane in ls:
-            lane.step(0)
-    for _ in range(max(warmup, 1)):
+        for r in range(R):
+            for lane in ls:
+                lane.step(r)
+    for _ in range(max(1, (warmup + R - 1) // R)):
         g.replay()
     torch.cuda.synchronize()
+    reps = max(1, (steps + R - 1) // R)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
-    for _ in range(steps):
+    for _ in range(reps):
         g.replay()
     b.record()
     torch.cuda.synchronize()
-    print(f"workload {name}: {a.elapsed_time(b) / steps * 1e3:.1f} us per step over {steps} graph replays",
-          flush=True)
+    print(f"workload {name}{' paged ' + paged if paged else ''}: {a.elapsed_time(b) / (reps * R) * 1e3:.1f} us per "
+          f"step over {reps * R} steps ({R} rotated input copies)", flush=True)
 
 
 def step_model(lane_list, D: int = 128):
