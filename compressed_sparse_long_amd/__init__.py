@@ -13,7 +13,8 @@ import os
 import torch
 
 __all__ = [
-    "compress_kv", "compress_kv_overlap", "indexer_scores", "topk_select", "sparse_attn_decode", "hca_attn_decode", "csa_decode_step",
+    "compress_kv", "compress_kv_overlap", "indexer_scores", "indexer_topk", "indexer_topk_max_k", "topk_select",
+    "sparse_attn_decode", "hca_attn_decode", "csa_decode_step",
     "topk_workspace_bytes", "attn_workspace_bytes", "PagedCache", "version", "LIB_PATH",
     "EXPORTS", "CslError",
 ]
@@ -23,6 +24,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsl.so")
 BF16, F32, FP8_E4M3, MXFP4 = 0, 1, 2, 3
 EXPORTS = [
     "csl_last_error", "csl_version", "csl_compress_kv", "csl_compress_kv_overlap", "csl_indexer_scores",
+    "csl_indexer_topk_max_k", "csl_indexer_topk",
     "csl_topk_workspace_bytes", "csl_topk_select", "csl_attn_workspace_bytes",
     "csl_sparse_attn_decode", "csl_hca_attn_decode", "csl_csa_decode_step",
 ]
@@ -76,6 +78,8 @@ def _load() -> ctypes.CDLL:
         "csl_compress_kv": (I, [P, P, P, P, P, I, I, I, L, P, I, P, P]),
         "csl_compress_kv_overlap": (I, [P, P, P, P, P, P, P, I, I, I, L, P, I, P, P]),
         "csl_indexer_scores": (I, [P, P, P, I, P, P, I, P, P, I, I, I, I, I, L, P, L, P, S, I, P, P]),
+        "csl_indexer_topk_max_k": (I, [I]),
+        "csl_indexer_topk": (I, [P, P, P, I, P, P, I, P, P, I, I, I, I, I, L, I, P, P, P]),
         "csl_topk_workspace_bytes": (S, [I, I, L, I]),
         "csl_topk_select": (I, [P, L, P, P, I, I, I, I, L, P, P, S, I, P]),
         "csl_attn_workspace_bytes": (S, [I, I, I, I, L]),
@@ -219,6 +223,24 @@ def indexer_scores(qI, w, kI, ent_off, q_pos, m: int, scores, max_entries: int |
         _ptr(topk_ws, "topk_ws"), 0 if topk_ws is None else topk_ws.numel() * topk_ws.element_size(), int(topk_k),
         _paged(paged), _stream(stream)))
     return scores
+
+
+def indexer_topk_max_k(HI: int) -> int:
+    return int(_lib.csl_indexer_topk_max_k(int(HI)))
+
+
+def indexer_topk(qI, w, kI, ent_off, q_pos, m: int, k: int, idx, max_entries: int, k_scale=None, scale_off=None,
+                 scale_group: int = 64, k_format=None, paged=None, stream=None):
+    """The indexer fused with top-k: ids of the k best visible entries per query row into
+    idx int32 [B, T, k] (ascending, -1 padded) without writing scores; see csl.h."""
+    B, T, HI, CI = qI.shape
+    kd, sdt = _key_format(kI, k_format)
+    _check(_lib.csl_indexer_topk(
+        _ptr(qI, "qI", _BF16), _ptr(w, "w", _F32), _ptr(kI, "kI"), kd, _ptr(k_scale, "k_scale", sdt),
+        _ptr(scale_off, "scale_off", _I64), int(scale_group), _ptr(ent_off, "ent_off", _I64),
+        _ptr(q_pos, "q_pos", _I64), int(m), B, T, HI, CI, int(max_entries), int(k),
+        _ptr(idx, "idx", (torch.int32,)), _paged(paged), _stream(stream)))
+    return idx
 
 
 def topk_workspace_bytes(B: int, T: int, max_entries: int, k: int) -> int:

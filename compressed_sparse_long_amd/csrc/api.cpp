@@ -107,35 +107,35 @@ int key_type(int k_dtype) {
 int check_indexer(const void* q_idx, const float* w, const void* k_idx, int k_dtype, const void* k_scale,
                   const int64_t* scale_off, int scale_group, const int64_t* ent_off, const int64_t* q_pos, int m, int B,
                   int T, int HI, int CI, int64_t max_entries, const float* scores, int64_t ld, void*& topk_ws,
-                  size_t topk_ws_bytes, int topk_k) {
-  if (B < 0 || T < 0 || max_entries < 0) return fail(CSL_ERR_INVALID, "indexer_scores: negative size");
+                  size_t topk_ws_bytes, int topk_k, const char* who = "indexer_scores") {
+  if (B < 0 || T < 0 || max_entries < 0) return fail(CSL_ERR_INVALID, "%s: negative size", who);
   if (!q_idx || !w || !k_idx || !ent_off || !q_pos || !scores)
-    return fail(CSL_ERR_INVALID, "indexer_scores: null pointer argument");
-  if (m < 1) return fail(CSL_ERR_INVALID, "indexer_scores: m must be >= 1");
+    return fail(CSL_ERR_INVALID, "%s: null pointer argument", who);
+  if (m < 1) return fail(CSL_ERR_INVALID, "%s: m must be >= 1", who);
   if (k_dtype != CSL_DTYPE_BF16 && k_dtype != CSL_DTYPE_FP8_E4M3 && k_dtype != CSL_DTYPE_MXFP4)
-    return fail(CSL_ERR_UNSUPPORTED, "indexer_scores: k_dtype must be BF16, FP8_E4M3 or MXFP4");
+    return fail(CSL_ERR_UNSUPPORTED, "%s: k_dtype must be BF16, FP8_E4M3 or MXFP4", who);
   const bool fp8 = k_dtype == CSL_DTYPE_FP8_E4M3;
   const bool fp4 = k_dtype == CSL_DTYPE_MXFP4;
   if (fp8 && (!k_scale || !scale_off || scale_group < 1))
-    return fail(CSL_ERR_INVALID, "indexer_scores: fp8 keys need k_scale, scale_off and scale_group >= 1");
-  if (fp4 && !k_scale) return fail(CSL_ERR_INVALID, "indexer_scores: MXFP4 keys need their E8M0 scales in k_scale");
+    return fail(CSL_ERR_INVALID, "%s: fp8 keys need k_scale, scale_off and scale_group >= 1", who);
+  if (fp4 && !k_scale) return fail(CSL_ERR_INVALID, "%s: MXFP4 keys need their E8M0 scales in k_scale", who);
   if (HI != 1 && HI != 2 && HI != 4 && HI != 8 && HI != 16)
-    return fail(CSL_ERR_UNSUPPORTED, "indexer_scores: HI must be 1, 2, 4, 8 or 16, got %d", HI);
-  if (CI != 64) return fail(CSL_ERR_UNSUPPORTED, "indexer_scores: CI must be 64, got %d", CI);
-  if (ld < max_entries) return fail(CSL_ERR_INVALID, "indexer_scores: ld (%lld) < max_entries (%lld)",
+    return fail(CSL_ERR_UNSUPPORTED, "%s: HI must be 1, 2, 4, 8 or 16, got %d", who, HI);
+  if (CI != 64) return fail(CSL_ERR_UNSUPPORTED, "%s: CI must be 64, got %d", who, CI);
+  if (ld < max_entries) return fail(CSL_ERR_INVALID, "%s: ld (%lld) < max_entries (%lld)", who,
                                     (long long)ld, (long long)max_entries);
-  if (B > kMaxGridY) return fail(CSL_ERR_UNSUPPORTED, "indexer_scores: B must be <= %d", kMaxGridY);
+  if (B > kMaxGridY) return fail(CSL_ERR_UNSUPPORTED, "%s: B must be <= %d", who, kMaxGridY);
   const int kalign = (fp8 || fp4) ? 8 : 16;
   if (!aligned(q_idx, 16) || !aligned(k_idx, kalign))
-    return fail(CSL_ERR_INVALID, "indexer_scores: q_idx must be 16-byte and k_idx %d-byte aligned", kalign);
+    return fail(CSL_ERR_INVALID, "%s: q_idx must be 16-byte and k_idx %d-byte aligned", who, kalign);
   if (topk_ws) {
     if (topk_k < 1 || topk_k > csl::topk_max_k())
-      return fail(CSL_ERR_UNSUPPORTED, "indexer_scores: topk_k must be in [1, %d], got %d", csl::topk_max_k(), topk_k);
+      return fail(CSL_ERR_UNSUPPORTED, "%s: topk_k must be in [1, %d], got %d", who, csl::topk_max_k(), topk_k);
     const size_t need = csl_topk_workspace_bytes(B, T, max_entries, topk_k);
     if (topk_ws_bytes < need)
-      return fail(CSL_ERR_WORKSPACE, "indexer_scores: top-k workspace of %zu bytes required, got %zu", need,
+      return fail(CSL_ERR_WORKSPACE, "%s: top-k workspace of %zu bytes required, got %zu", who, need,
                   topk_ws_bytes);
-    if (!aligned(topk_ws, 16)) return fail(CSL_ERR_INVALID, "indexer_scores: topk_ws must be 16-byte aligned");
+    if (!aligned(topk_ws, 16)) return fail(CSL_ERR_INVALID, "%s: topk_ws must be 16-byte aligned", who);
     if (need == 0) topk_ws = nullptr;  // short rows: the selection needs no candidate lists
   }
   return CSL_OK;
@@ -226,6 +226,40 @@ int csl_indexer_scores(const void* q_idx, const float* w, const void* k_idx, int
                                         ent_off, q_pos, m, B, T, HI, max_entries, scores, ld, topk_ws, topk_k,
                                         as_stream(stream), nullptr, paged ? &pv : nullptr),
                     "indexer_scores launch");
+}
+
+int csl_indexer_topk_max_k(int HI) {
+  return (HI == 1 || HI == 2 || HI == 4 || HI == 8 || HI == 16) ? csl::indexer_topk_max_k(HI) : 0;
+}
+
+int csl_indexer_topk(const void* q_idx, const float* w, const void* k_idx, int k_dtype, const void* k_scale,
+                     const int64_t* scale_off, int scale_group, const int64_t* ent_off, const int64_t* q_pos, int m,
+                     int B, int T, int HI, int CI, int64_t max_entries, int k, int32_t* idx,
+                     const csl_paged_cache* paged, void* stream) {
+  if (!idx) return fail(CSL_ERR_INVALID, "indexer_topk: null pointer argument");
+  void* no_ws = nullptr;
+  // the indexer's checks, with idx standing in for the score buffer it does not need
+  int st = check_indexer(q_idx, w, k_idx, k_dtype, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T, HI, CI,
+                         max_entries, reinterpret_cast<const float*>(idx), max_entries, no_ws, 0, 0,
+                         "indexer_topk");
+  if (st != CSL_OK) return st;
+  const int kmax = csl_indexer_topk_max_k(HI);
+  if (k < 1 || k > kmax) return fail(CSL_ERR_UNSUPPORTED, "indexer_topk: k must be in [1, %d], got %d", kmax, k);
+  if (!aligned(idx, 4)) return fail(CSL_ERR_INVALID, "indexer_topk: idx must be 4-byte aligned");
+  if (B > kMaxGridY) return fail(CSL_ERR_UNSUPPORTED, "indexer_topk: B must be <= %d", kMaxGridY);
+  if (max_entries > 0x7fffffff) return fail(CSL_ERR_UNSUPPORTED, "indexer_topk: max_entries must be < 2^31");
+  csl::PagedView pv;
+  if (paged) {
+    st = check_paged("indexer_topk", paged, B, pv);
+    if (st != CSL_OK) return st;
+    if (k_dtype == CSL_DTYPE_FP8_E4M3)
+      return fail(CSL_ERR_UNSUPPORTED, "indexer_topk: fp8 keys (group scales) are not supported in a paged cache");
+  }
+  if (B == 0 || T == 0) return ok();
+  return hip_status(csl::launch_indexer_topk(q_idx, w, k_idx, key_type(k_dtype), k_scale, scale_off, scale_group,
+                                             ent_off, q_pos, m, B, T, HI, max_entries, k, idx, as_stream(stream),
+                                             paged ? &pv : nullptr),
+                    "indexer_topk launch");
 }
 
 size_t csl_topk_workspace_bytes(int B, int T, int64_t max_entries, int k) {

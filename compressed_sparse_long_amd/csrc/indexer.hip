@@ -104,6 +104,48 @@ __device__ __forceinline__ bf16x8 key_operand(const u32x4& k) {
                          __builtin_bit_cast(uint32_t, r2), __builtin_bit_cast(uint32_t, r3)});
 }
 
+// Prefill tiling: queries are the MFMA A operand (16/HI query rows x HI heads per tile) and
+// keys the B operand, so lane (g, c) holds products 4g..4g+3 (query row, head) of key c. The
+// head-weighted ReLU sum of one query row gathers in part[q]; it is complete in the writer
+// lanes, and prefill_row names its row inside the A tile. The indexer and the fused
+// indexer/top-k kernel share this arithmetic, so their scores agree bit for bit.
+template <int HI>
+constexpr int prefill_rows_per_group() { return HI >= 4 ? 1 : 4 / HI; }
+
+template <int HI>
+__device__ __forceinline__ void prefill_head_sum(const f32x4& acc, const float (&wv)[4],
+                                                 float (&part)[prefill_rows_per_group<HI>()]) {
+  constexpr int RPG = prefill_rows_per_group<HI>();
+#pragma unroll
+  for (int q = 0; q < RPG; ++q) part[q] = 0.f;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int q = (HI >= 4) ? 0 : it / HI;
+    part[q] = fmaf(wv[it], fmaxf(acc[it], 0.f), part[q]);
+  }
+  // the partner row's value comes from gfx950's row swaps, not through LDS: permlane16_swap
+  // returns (even row, odd row) of each pair of 16-lane rows in every lane, permlane32_swap
+  // (lower half, upper half), so their sum is the lane's value plus its partner's
+  if (HI >= 8) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(part[0]), __float_as_uint(part[0]), false, false);
+    part[0] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  if (HI == 16) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[0]), false, false);
+    part[0] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+}
+
+template <int HI>
+__device__ __forceinline__ bool prefill_writer(int g) {
+  return (HI == 16) ? (g == 0) : (HI == 8) ? ((g & 1) == 0) : true;
+}
+
+template <int HI>
+__device__ __forceinline__ int prefill_row(int g, int q) {
+  return (HI >= 8) ? (4 * g) / HI : (4 * g) / HI + q;
+}
+
 template <int HI, int NB, int NWAVES, int WQ, int U, int KT, bool PAGED>
 __global__ __launch_bounds__(NWAVES * 64) void indexer_kernel(
     const uint16_t* __restrict__ qI, const float* __restrict__ w, const void* __restrict__ kI,
@@ -113,7 +155,7 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_kernel(
   constexpr int QPB = 16 / HI;       // query rows per A tile
   constexpr int QPW = NB * QPB;      // query rows per wave
   constexpr int WE = NWAVES / WQ;    // key sub-ranges per block
-  constexpr int ROWS_PER_GROUP = (HI >= 4) ? 1 : 4 / HI;  // query rows in one lane group's 4 C rows
+  constexpr int ROWS_PER_GROUP = prefill_rows_per_group<HI>();  // query rows in one lane group's 4 C rows
 
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
@@ -171,7 +213,7 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_kernel(
 #pragma unroll
     for (int q = 0; q < ROWS_PER_GROUP; ++q) {
       // query row written by this lane group (row index inside the A tile)
-      const int rq = (HI >= 8) ? (4 * g) / HI : (4 * g) / HI + q;
+      const int rq = prefill_row<HI>(g, q);
       const int tt = t0 + nb * QPB + rq;
       nv_row[nb][q] = (tt < T) ? n_vis(tt) : 0;
     }
@@ -199,24 +241,11 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_kernel(
         acc = mfma16x16x32(a[nb][0], b0, acc);
         acc = mfma16x16x32(a[nb][1], b1, acc);
         float part[ROWS_PER_GROUP];
-#pragma unroll
-        for (int q = 0; q < ROWS_PER_GROUP; ++q) part[q] = 0.f;
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-          const int q = (HI >= 4) ? 0 : it / HI;
-          part[q] = fmaf(wv[nb][it], fmaxf(acc[it], 0.f), part[q]);
-        }
-        if (HI == 16) {
-          part[0] += shfl_xor_f(part[0], 16);
-          part[0] += shfl_xor_f(part[0], 32);
-        } else if (HI == 8) {
-          part[0] += shfl_xor_f(part[0], 16);
-        }
-        const bool writer = (HI == 16) ? (g == 0) : (HI == 8) ? ((g & 1) == 0) : true;
-        if (writer) {
+        prefill_head_sum<HI>(acc, wv[nb], part);
+        if (prefill_writer<HI>(g)) {
 #pragma unroll
           for (int q = 0; q < ROWS_PER_GROUP; ++q) {
-            const int rq = (HI >= 8) ? (4 * g) / HI : (4 * g) / HI + q;
+            const int rq = prefill_row<HI>(g, q);
             const int tt = t0 + nb * QPB + rq;
             if (tt < T && s < nv_row[nb][q]) {
               float v = part[q];
@@ -227,6 +256,272 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_kernel(
         }
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Indexer fused with top-k: the scores never leave the chip. A workgroup takes QR query rows
+// (16; 8 at HI = 16) over the whole key range, in chunks of 256 keys: its 8 waves score the
+// chunk with the prefill tiling's MFMAs and arithmetic into one of two LDS staging buffers,
+// then each wave files the scores of its own rows into that row's candidate buffer in LDS,
+// admitting only keys above the row's bar. The keys of the next chunk are in flight while a
+// chunk is scored and filed, and with two staging buffers one barrier per chunk suffices: a
+// wave that passes the barrier of chunk j has filed chunk j - 1, whose buffer chunk j + 1
+// then reuses. The buffer holds (key << 32 | id) in ascending id order. When it could
+// overflow, the wave cuts it to exactly the k best by (score descending, id ascending) and
+// raises the bar to the k-th key: a later entry at or below the bar can never enter the top-k
+// (its key is lower, or equal with a higher id), and an entry cut is below k better ones. At
+// the end the buffer is cut to k once more and written out in id order, -1 padded.
+
+constexpr int kFusedWaves = 8;
+constexpr int kFusedU = 2;                               // key tiles of 16 per wave and chunk
+constexpr int kFusedChunk = kFusedWaves * kFusedU * 16;  // keys per chunk
+constexpr int kFusedSlots = 15360;                       // candidate slots per workgroup (120 KB)
+
+template <int HI>
+struct FusedShape {
+  static constexpr int QPB = 16 / HI;
+  static constexpr int NB = HI == 16 ? 8 : HI;  // A tiles (all waves hold all of them)
+  static constexpr int QR = NB * QPB;           // query rows per workgroup
+  static constexpr int CAP = kFusedSlots / QR;  // candidate slots per row
+  static_assert(CAP % 64 == 0, "whole waves of slots");
+};
+
+// Cut a row's candidate buffer (n > k entries, ascending ids) to exactly its k best in place,
+// keeping id order; returns the new bar (the k-th best key). One wave, wave-uniform result.
+template <int CAP>
+__device__ __forceinline__ uint32_t cut_to_k(uint64_t* row, uint32_t& n, int k) {
+  constexpr int J = CAP / kWave;
+  const int lane = (int)lane_id();
+  uint32_t xs[J];
+  uint32_t hi = 0u, lo = 0xffffffffu;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const uint32_t i = (uint32_t)(j * kWave + lane);
+    xs[j] = i < n ? (uint32_t)(row[i] >> 32) : 0u;
+    if (i < n) {
+      hi = max(hi, xs[j]);
+      lo = min(lo, xs[j]);
+    }
+  }
+  hi = wave_max_u32(hi);
+  lo = wave_min_u32(lo);
+  // the k-th largest key, bit by bit below the prefix all keys share; a prefix that already
+  // has exactly k keys at or above it ends the search (those k are the k best). The bits
+  // below the prefix come from smearing hi ^ lo rightwards: plain arithmetic, which also
+  // covers hi == lo (a select on the leading-zero count of hi ^ lo was built wrongly here:
+  // the select read a condition flag that the shift before it had overwritten)
+  uint32_t below = hi ^ lo;
+  below |= below >> 1;
+  below |= below >> 2;
+  below |= below >> 4;
+  below |= below >> 8;
+  below |= below >> 16;
+  uint32_t t = hi & ~below;
+  bool exact = false;
+  {
+    for (int bit = __popc(below) - 1; bit >= 0; --bit) {
+      const uint32_t c = t | (1u << bit);
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int j = 0; j < J; ++j) cnt += (uint32_t)__popcll(__ballot(xs[j] >= c));
+      if (cnt >= (uint32_t)k) {
+        t = c;
+        if (cnt == (uint32_t)k) {
+          exact = true;
+          break;
+        }
+      }
+    }
+  }
+  // otherwise t is the k-th key itself: keep every key above it and the lowest-id ties
+  uint32_t need = (uint32_t)k;
+  if (!exact) {
+    uint32_t gt = 0;
+#pragma unroll
+    for (int j = 0; j < J; ++j) gt += (uint32_t)__popcll(__ballot(xs[j] > t));
+    need = (uint32_t)k - gt;
+  }
+  uint32_t out = 0, ties = 0, bar = 0xffffffffu;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const uint32_t i = (uint32_t)(j * kWave + lane);
+    const bool valid = i < n;
+    const uint32_t x = xs[j];
+    const uint64_t v = valid ? row[i] : 0ull;  // slots at or after j * 64 are not yet rewritten
+    bool keep;
+    if (exact) {
+      keep = valid && x >= t;
+    } else {
+      const bool tie = valid && x == t;
+      const uint64_t tm = __ballot(tie);
+      const uint32_t tr = ties + rank_in_wave(tm);
+      ties += (uint32_t)__popcll(tm);
+      keep = valid && (x > t || (tie && tr < need));
+    }
+    const uint64_t km = __ballot(keep);
+    if (keep) {
+      row[out + rank_in_wave(km)] = v;
+      bar = min(bar, x);
+    }
+    out += (uint32_t)__popcll(km);
+  }
+  n = out;
+  return wave_min_u32(bar);
+}
+
+template <int HI, int KT, bool PAGED>
+__global__ __launch_bounds__(kFusedWaves * kWave) void indexer_topk_kernel(
+    const uint16_t* __restrict__ qI, const float* __restrict__ w, const void* __restrict__ kI,
+    const void* __restrict__ k_scale_v, const int64_t* __restrict__ scale_off, int scale_group,
+    const int64_t* __restrict__ ent_off, const int64_t* __restrict__ q_pos, int m, int T,
+    int64_t max_entries, int k, int32_t* __restrict__ idx, PagedView pg) {
+  using FS = FusedShape<HI>;
+  constexpr int QPB = FS::QPB, NB = FS::NB, QR = FS::QR, CAP = FS::CAP;
+  constexpr int U = kFusedU, CH = kFusedChunk;
+  constexpr int RPW = QR / kFusedWaves;  // rows each wave files (2, or 1 at HI = 16)
+  constexpr int RPG = prefill_rows_per_group<HI>();
+  static_assert(RPW >= 1 && QR % kFusedWaves == 0, "whole rows per wave");
+  __shared__ __align__(16) float sval[2][QR][CH];
+  __shared__ uint64_t cand[QR][CAP];
+
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int g = lane / 16;
+  const int c = lane % 16;
+  const int b = blockIdx.z;
+  const int t0 = blockIdx.x * QR;
+  constexpr bool FP8 = KT == kKeyFP8;
+  const float* k_scale = static_cast<const float*>(k_scale_v);
+  const uint8_t* k_mx = static_cast<const uint8_t*>(k_scale_v);
+
+  const int64_t e_base = ent_off[b];
+  const int64_t n_ent = ent_off[b + 1] - e_base;
+  const int64_t n_load = n_ent < max_entries ? n_ent : max_entries;
+  const int64_t p0 = q_pos[b];
+  auto n_vis = [&](int t) -> int64_t {
+    const int64_t p = p0 + t;
+    int64_t nv = (p >= 0 && p < ((int64_t)1 << 32)) ? (int64_t)((uint32_t)p / (uint32_t)m) : p / m;
+    nv = nv < n_load ? nv : n_load;
+    return nv < 0 ? 0 : nv;
+  };
+
+  // queries and head weights of all QR rows (every wave scores every row)
+  bf16x8 a[NB][2];
+  float wv[NB][4];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int t = t0 + nb * QPB + c / HI;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      u32x4 v = u32x4{0, 0, 0, 0};
+      if (t < T) v = *reinterpret_cast<const u32x4*>(qI + (((int64_t)b * T + t) * HI + c % HI) * 64 + kslot_dim<KT>(kk, g));
+      a[nb][kk] = as_bf16x8(v);
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int r = 4 * g + it;
+      const int tt = t0 + nb * QPB + r / HI;
+      wv[nb][it] = (tt < T) ? w[((int64_t)b * T + tt) * HI + (r % HI)] : 0.f;
+    }
+  }
+  // the rows this wave files: visible entries, buffer fill and bar (wave-uniform)
+  int64_t nv_mine[RPW];
+  uint32_t cnt[RPW], bar[RPW];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int t = t0 + wave * RPW + i;
+    nv_mine[i] = t < T ? n_vis(t) : 0;
+    cnt[i] = 0;
+    bar[i] = 0;  // every real key is above 0
+  }
+  const int t_last = min(t0 + QR, T) - 1;
+  const int64_t n_max = t_last >= t0 ? n_vis(t_last) : 0;  // visibility grows with t
+
+  // key tiles of one chunk for this wave: keys s0 + (wave * U + u) * 16 + c
+  u32x4 kb[U][2];
+  float sc[U];
+  auto load_chunk = [&](int64_t s0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t s = s0 + (wave * U + u) * 16 + c;
+      const bool ok = s < n_max;
+      load_key_tile<KT>(kI, k_mx, key_row<PAGED>(pg, b, e_base, s), ok, g, kb[u][0], kb[u][1]);
+      if (FP8) sc[u] = ok ? k_scale[scale_off[b] + s / scale_group] : 0.f;
+    }
+  };
+  if (n_max > 0) load_chunk(0);
+  int buf = 0;
+  for (int64_t s0 = 0; s0 < n_max; s0 += CH, buf ^= 1) {
+    bf16x8 b0[U], b1[U];
+    float scu[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      b0[u] = key_operand<KT>(kb[u][0]);
+      b1[u] = key_operand<KT>(kb[u][1]);
+      scu[u] = sc[u];
+    }
+    if (s0 + CH < n_max) load_chunk(s0 + CH);  // the next chunk's keys fly during this one
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mfma16x16x32(a[nb][0], b0[u], acc);
+        acc = mfma16x16x32(a[nb][1], b1[u], acc);
+        float part[RPG];
+        prefill_head_sum<HI>(acc, wv[nb], part);
+        if (prefill_writer<HI>(g)) {
+#pragma unroll
+          for (int q = 0; q < RPG; ++q) {
+            float v = part[q];
+            if (FP8) v *= scu[u];
+            sval[buf][nb * QPB + prefill_row<HI>(g, q)][(wave * U + u) * 16 + c] = v;
+          }
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+      const int r = wave * RPW + i;
+      if (cnt[i] + CH <= (uint32_t)CAP) {
+        // the whole chunk fits: its score reads go out together, then the ballots
+        uint32_t x[CH / kWave];
+#pragma unroll
+        for (int j = 0; j < CH / kWave; ++j) {
+          const int64_t s = s0 + j * kWave + lane;
+          x[j] = s < nv_mine[i] ? score_key(sval[buf][r][j * kWave + lane]) : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < CH / kWave; ++j) {
+          const bool admit = x[j] > bar[i];
+          const uint64_t mk = __ballot(admit);
+          if (admit) cand[r][cnt[i] + rank_in_wave(mk)] = ((uint64_t)x[j] << 32) | (uint32_t)(s0 + j * kWave + lane);
+          cnt[i] += (uint32_t)__popcll(mk);
+        }
+      } else {
+#pragma unroll 1
+        for (int j = 0; j < CH / kWave; ++j) {  // not unrolled: one copy of the cut per row
+          if (cnt[i] + kWave > (uint32_t)CAP) bar[i] = cut_to_k<CAP>(cand[r], cnt[i], k);
+          const int64_t s = s0 + j * kWave + lane;
+          const uint32_t x = s < nv_mine[i] ? score_key(sval[buf][r][j * kWave + lane]) : 0u;
+          const bool admit = x > bar[i];
+          const uint64_t mk = __ballot(admit);
+          if (admit) cand[r][cnt[i] + rank_in_wave(mk)] = ((uint64_t)x << 32) | (uint32_t)s;
+          cnt[i] += (uint32_t)__popcll(mk);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const int r = wave * RPW + i;
+    const int t = t0 + r;
+    if (t >= T) continue;
+    if (cnt[i] > (uint32_t)k) cut_to_k<CAP>(cand[r], cnt[i], k);
+    int32_t* out = idx + ((int64_t)b * T + t) * k;
+    for (int j = lane; j < k; j += kWave) out[j] = (uint32_t)j < cnt[i] ? (int32_t)(uint32_t)cand[r][j] : -1;
   }
 }
 
@@ -468,6 +763,43 @@ hipError_t launch_hi(const void* qI, const float* w, const void* kI, const void*
   return hipGetLastError();
 }
 
+template <int HI, int KT>
+hipError_t launch_topk_hi(const void* qI, const float* w, const void* kI, const void* k_scale,
+                          const int64_t* scale_off, int scale_group, const int64_t* ent_off, const int64_t* q_pos,
+                          int m, int B, int T, int64_t max_entries, int k, int32_t* idx, hipStream_t st,
+                          const PagedView& pg) {
+  constexpr int QR = FusedShape<HI>::QR;
+  dim3 grid((unsigned)((T + QR - 1) / QR), 1u, (unsigned)B);
+  const uint16_t* q16 = static_cast<const uint16_t*>(qI);
+  if (pg.table)
+    indexer_topk_kernel<HI, KT, true><<<grid, kFusedWaves * kWave, 0, st>>>(
+        q16, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, T, max_entries, k, idx, pg);
+  else
+    indexer_topk_kernel<HI, KT, false><<<grid, kFusedWaves * kWave, 0, st>>>(
+        q16, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, T, max_entries, k, idx, pg);
+  return hipGetLastError();
+}
+
+template <int KT>
+hipError_t launch_topk_kt(int HI, const void* qI, const float* w, const void* kI, const void* k_scale,
+                          const int64_t* scale_off, int scale_group, const int64_t* ent_off, const int64_t* q_pos,
+                          int m, int B, int T, int64_t max_entries, int k, int32_t* idx, hipStream_t st,
+                          const PagedView& pg) {
+#define CSL_FUSED_CASE(H)                                                                                       \
+  case H:                                                                                                       \
+    return launch_topk_hi<H, KT>(qI, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T,           \
+                                 max_entries, k, idx, st, pg);
+  switch (HI) {
+    CSL_FUSED_CASE(1)
+    CSL_FUSED_CASE(2)
+    CSL_FUSED_CASE(4)
+    CSL_FUSED_CASE(8)
+    CSL_FUSED_CASE(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef CSL_FUSED_CASE
+}
+
 template <int KT>
 hipError_t launch_kt(int HI, const void* qI, const float* w, const void* kI, const void* k_scale,
                       const int64_t* scale_off, int scale_group, const int64_t* ent_off,
@@ -490,6 +822,30 @@ hipError_t launch_kt(int HI, const void* qI, const float* w, const void* kI, con
 }
 
 }  // namespace
+
+int indexer_topk_max_k(int HI) {
+  const int cap = HI == 16 ? FusedShape<16>::CAP : FusedShape<8>::CAP;
+  return cap - kWave;  // a cut leaves k entries and a sub-step files up to 64 more
+}
+
+hipError_t launch_indexer_topk(const void* qI, const float* w, const void* kI, int key_type, const void* k_scale,
+                               const int64_t* scale_off, int scale_group, const int64_t* ent_off,
+                               const int64_t* q_pos, int m, int B, int T, int HI, int64_t max_entries, int k,
+                               int32_t* idx, hipStream_t st, const PagedView* paged) {
+  const PagedView pg = paged ? *paged : PagedView{};
+  switch (key_type) {
+    case kKeyBF16:
+      return launch_topk_kt<kKeyBF16>(HI, qI, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T,
+                                      max_entries, k, idx, st, pg);
+    case kKeyFP8:
+      return launch_topk_kt<kKeyFP8>(HI, qI, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T,
+                                     max_entries, k, idx, st, pg);
+    case kKeyFP4:
+      return launch_topk_kt<kKeyFP4>(HI, qI, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T,
+                                     max_entries, k, idx, st, pg);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 bool indexer_prepares_topk(const void* topk_ws, int T, int64_t max_entries) {
   return topk_ws != nullptr && T == 1 && !topk_uses_row_kernel(max_entries) && max_entries <= kMultiMaxEntries;

@@ -51,6 +51,13 @@ hipError_t launch_indexer(const void* qI, const float* w, const void* kI, int ke
                           const int64_t* q_pos, int m, int B, int T, int HI, int64_t max_entries,
                           float* scores, int64_t ld, void* topk_ws, int topk_k, hipStream_t stream,
                           const CompressJob* job = nullptr, const PagedView* paged = nullptr);
+// indexer fused with top-k (no scores written): ids of the k best visible entries per query
+// row into idx [B, T, k], ascending, -1 padded; k <= indexer_topk_max_k(HI)
+hipError_t launch_indexer_topk(const void* qI, const float* w, const void* kI, int key_type, const void* k_scale,
+                               const int64_t* scale_off, int scale_group, const int64_t* ent_off,
+                               const int64_t* q_pos, int m, int B, int T, int HI, int64_t max_entries, int k,
+                               int32_t* idx, hipStream_t stream, const PagedView* paged = nullptr);
+int indexer_topk_max_k(int HI);
 // whether launch_indexer leaves top-k candidate lists in topk_ws for these shapes
 bool indexer_prepares_topk(const void* topk_ws, int T, int64_t max_entries);
 // whether launch_indexer can carry a CompressJob for these shapes (decode tiling, D = 128, m <= 8)

@@ -207,6 +207,34 @@ int csl_topk_select(const float* scores, int64_t ld, const int64_t* ent_off, con
                     size_t ws_bytes, int prepared, void* stream);
 
 /*
+ * indexer_topk -- the indexer fused with the top-k selection, the scores never written
+ * ([P2] "Deep Dive", CSA Lightning Indexer and top-k selection; [P5] the indexer score
+ * formula; [P1] section 4.2).
+ *
+ *   idx[b, t, :] = topk_select(indexer_scores(...))[b, t, :]
+ *
+ * The scores come from the arithmetic of indexer_scores' prefill tiling (taken when
+ * B*T >= 64 and T >= 16, without candidate lists), so for such shapes the result equals
+ * the two calls bit for bit; for others the scores differ from indexer_scores' only in the
+ * fp32 rounding of the head sum's order. The choice is (score descending, id ascending)
+ * and the output ascending ids, -1 padded, as for topk_select. Arguments are those of
+ * indexer_scores (keys, scales, offsets, paged cache) and topk_select (k, idx), without the
+ * score buffer and workspace.
+ *
+ *   k     1 <= k <= csl_indexer_topk_max_k(HI) (896 for HI <= 8, 1856 for HI = 16)
+ *   idx   int32 [B, T, k]
+ * One workgroup scores 16 query rows (8 at HI = 16) against all of their visible entries
+ * and keeps each row's candidates in on-chip memory, so the call suits batches of many
+ * query rows (prefill); a single decode row is better served by indexer_scores with
+ * candidate lists and topk_select. No workspace; nothing but idx is written.
+ */
+int csl_indexer_topk_max_k(int HI);
+int csl_indexer_topk(const void* q_idx, const float* w, const void* k_idx, int k_dtype, const void* k_scale,
+                     const int64_t* scale_off, int scale_group, const int64_t* ent_off, const int64_t* q_pos,
+                     int m, int B, int T, int HI, int CI, int64_t max_entries, int k, int32_t* idx,
+                     const csl_paged_cache* paged, void* stream);
+
+/*
  * sparse_attn_decode -- CSA core attention ([P2] "Deep Dive", CSA core attention with
  * shared-KV MQA and the sliding-window branch; [P2] "Putting It Together"; [P5] the
  * attention formula):
