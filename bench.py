@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--run-workload", default=None,
                     help="replay --steps steps of another synthetic configuration (for profiling) and print "
                          "its mean step time")
+    ap.add_argument("--scoreless", action="store_true",
+                    help="with --run-workload: CSA steps select with the indexer fused with top-k (no scores)")
     ap.add_argument("--paged", default=None, choices=("random", "interleaved"),
                     help="with --run-workload: page every lane's cache first (blocks in this order)")
     return ap.parse_args()
@@ -164,7 +166,7 @@ def main():
         copy_calibration()
         return
     if args.run_workload:
-        run_workload(args.run_workload, args.steps, args.warmup, args.paged, args.copies)
+        run_workload(args.run_workload, args.steps, args.warmup, args.paged, args.copies, args.scoreless)
         return
     if args.report_configs:
         report_configs(args.copies, args.cpu_seconds)
@@ -398,7 +400,8 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def run_workload(name: str, steps: int, warmup: int, paged: str | None = None, copies: int = 4) -> None:
+def run_workload(name: str, steps: int, warmup: int, paged: str | None = None, copies: int = 4,
+                 scoreless: bool = False) -> None:
     """Replay one configuration's whole step (every lane) as a graph; print its mean time.
     Each graph holds ``copies`` steps over rotated copies of the large inputs (as in the main
     measurement); ``paged``: move every lane's cache into a block pool first, blocks in that order."""
@@ -407,7 +410,7 @@ def run_workload(name: str, steps: int, warmup: int, paged: str | None = None, c
     from compressed_sparse_long_amd import lanes
 
     inp = synth.generate(name)
-    ls = lanes.build_lanes(inp)
+    ls = lanes.build_lanes(inp, scoreless=scoreless)
     R = max(1, copies)
     for lane in ls:
         lane.compress_all()
@@ -430,7 +433,8 @@ def run_workload(name: str, steps: int, warmup: int, paged: str | None = None, c
         g.replay()
     b.record()
     torch.cuda.synchronize()
-    print(f"workload {name}{' paged ' + paged if paged else ''}: {a.elapsed_time(b) / (reps * R) * 1e3:.1f} us per "
+    print(f"workload {name}{' paged ' + paged if paged else ''}{' without scores' if scoreless else ''}: "
+          f"{a.elapsed_time(b) / (reps * R) * 1e3:.1f} us per "
           f"step over {reps * R} steps ({R} rotated input copies)", flush=True)
 
 
@@ -535,9 +539,8 @@ def report_configs(copies: int, cpu_seconds: float) -> None:
     import synth
     from compressed_sparse_long_amd import lanes
 
-    for name in synth.CONFIG_ORDER:
-        inp = synth.generate(name)
-        ls = lanes.build_lanes(inp)
+    def time_step(inp, scoreless: bool) -> float:
+        ls = lanes.build_lanes(inp, scoreless=scoreless)
         for lane in ls:
             lane.rotate(copies)
             lane.compress_all()
@@ -560,17 +563,27 @@ def report_configs(copies: int, cpu_seconds: float) -> None:
             g.replay()
         b.record()
         torch.cuda.synchronize()
-        step_us = a.elapsed_time(b) / (reps * copies) * 1e3
+        del g, ls
+        torch.cuda.empty_cache()
+        return a.elapsed_time(b) / (reps * copies) * 1e3
+
+    for name in synth.CONFIG_ORDER:
+        inp = synth.generate(name)
+        step_us = time_step(inp, False)
         nbytes, flops, queries = step_model([li.lane for li in inp.lanes])
         bound_us = max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6
-        del ls
-        torch.cuda.empty_cache()
+        extra = {}
+        if any(li.lane.kind == "csa" and li.lane.T >= 16 for li in inp.lanes):
+            # query batches: the same step with the indexer fused with top-k (no score matrix)
+            nos_us = time_step(inp, True)
+            extra = {"step_us_without_scores": round(nos_us, 2),
+                     "queries_per_s_without_scores": round(queries / (nos_us * 1e-6), 1)}
         line = {"workload": name, "step_us": round(step_us, 2), "queries_per_s": round(queries / (step_us * 1e-6), 1),
                 "bytes": nbytes, "GB_s": round(nbytes / (step_us * 1e-6) / 1e9, 1),
                 "hbm_frac": round(nbytes / (step_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                 "flops": flops, "TFLOP_s": round(flops / (step_us * 1e-6) / 1e12, 2),
                 "bound": "hbm" if nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) else "mfma",
-                "roofline_us": round(bound_us, 2), "roofline_frac": round(bound_us / step_us, 4),
+                "roofline_us": round(bound_us, 2), "roofline_frac": round(bound_us / step_us, 4), **extra,
                 "cpu_baseline": oracle_rate(inp, cpu_seconds)}
         print(json.dumps(line), flush=True)
 

@@ -331,12 +331,15 @@ def csa_decode_step(kv, z, kv_off, ent_off, first_entry, max_new_entries: int, c
                     k_format=None, paged=None, stream=None):
     """One whole CSA step (compress_kv of the newest entries into ckv, or compress_kv_overlap
     when series b ``kv_b``/``z_b`` is given, indexer_scores with candidate lists, topk_select,
-    sparse_attn_decode) in one C call; see csl.h."""
+    sparse_attn_decode) in one C call; with ``scores`` None the selection comes from the
+    indexer fused with top-k and no score matrix is written; see csl.h."""
     B, T, HI, CI = qI.shape
     H, D = q.shape[2], q.shape[3]
     kd, sdt = _key_format(kI, k_format)
-    ld = scores.shape[-1]
+    ld = scores.shape[-1] if scores is not None else 0  # None: the indexer fused with top-k
     if max_entries is None:
+        if scores is None:
+            raise ValueError("csa_decode_step: max_entries is required without a score buffer")
         max_entries = ld
     if scale is None:
         scale = D ** -0.5

@@ -402,14 +402,30 @@ int csl_csa_decode_step(const csl_csa_step* s, void* stream) {
       return fail(CSL_ERR_INVALID, "csa_decode_step: ring_rows must hold the window and the newest chunk(s)");
     pvp = &pv;
   }
-  void* topk_ws = s->topk_ws;
-  st = check_indexer(s->q_idx, s->w, s->k_idx, s->k_dtype, s->k_scale, s->scale_off, s->scale_group, s->ent_off,
-                     s->q_pos, s->m, s->B, s->T, s->HI, s->CI, s->max_entries, s->scores, s->ld, topk_ws,
-                     s->topk_ws_bytes, s->k);
-  if (st != CSL_OK) return st;
-  st = check_topk(s->scores, s->ld, s->ent_off, s->q_pos, s->m, s->B, s->T, s->k, s->max_entries, s->idx, s->topk_ws,
-                  s->topk_ws_bytes);
-  if (st != CSL_OK) return st;
+  // no score buffer: the indexer fused with top-k (csl_indexer_topk) makes the selection
+  const bool scoreless = s->scores == nullptr;
+  void* topk_ws = scoreless ? nullptr : s->topk_ws;
+  if (scoreless) {
+    if (!s->idx) return fail(CSL_ERR_INVALID, "csa_decode_step: null pointer argument");
+    void* no_ws = nullptr;
+    st = check_indexer(s->q_idx, s->w, s->k_idx, s->k_dtype, s->k_scale, s->scale_off, s->scale_group, s->ent_off,
+                       s->q_pos, s->m, s->B, s->T, s->HI, s->CI, s->max_entries, reinterpret_cast<const float*>(s->idx),
+                       s->max_entries, no_ws, 0, 0, "csa_decode_step");
+    if (st != CSL_OK) return st;
+    const int kmax = csl_indexer_topk_max_k(s->HI);
+    if (s->k < 1 || s->k > kmax)
+      return fail(CSL_ERR_UNSUPPORTED, "csa_decode_step: without scores k must be in [1, %d], got %d", kmax, s->k);
+    if (s->max_entries > 0x7fffffff)
+      return fail(CSL_ERR_UNSUPPORTED, "csa_decode_step: max_entries must be < 2^31");
+  } else {
+    st = check_indexer(s->q_idx, s->w, s->k_idx, s->k_dtype, s->k_scale, s->scale_off, s->scale_group, s->ent_off,
+                       s->q_pos, s->m, s->B, s->T, s->HI, s->CI, s->max_entries, s->scores, s->ld, topk_ws,
+                       s->topk_ws_bytes, s->k);
+    if (st != CSL_OK) return st;
+    st = check_topk(s->scores, s->ld, s->ent_off, s->q_pos, s->m, s->B, s->T, s->k, s->max_entries, s->idx,
+                    s->topk_ws, s->topk_ws_bytes);
+    if (st != CSL_OK) return st;
+  }
   const int64_t max_keys = (int64_t)s->k + s->n_win;
   st = check_attn("csa_decode_step", s->q, s->ckv, s->kv, s->kv_off, s->ent_off, s->q_pos, s->n_win, s->B, s->T, s->H,
                   s->D, s->scale, s->out, s->attn_ws, s->attn_ws_bytes, max_keys);
@@ -421,7 +437,17 @@ int csl_csa_decode_step(const csl_csa_step* s, void* stream) {
   const bool compress = s->max_new_entries > 0;
   const bool index = s->max_entries > 0;
   hipError_t e = hipSuccess;
-  if (compress && index && csl::indexer_carries_compress(topk_ws, s->B, s->T, s->max_entries, s->D, s->m)) {
+  if (scoreless) {
+    if (compress && overlap)
+      e = csl::launch_compress_overlap(s->kv, s->z, s->kv_b, s->z_b, s->kv_off, s->ent_off, s->first_entry, s->B,
+                                       s->D, s->m, s->max_new_entries, s->ckv, true, hs, pvp);
+    else if (compress)
+      e = csl::launch_compress(s->kv, s->z, s->kv_off, s->ent_off, s->first_entry, s->B, s->D, s->m,
+                               s->max_new_entries, s->ckv, true, hs, pvp);
+    if (e == hipSuccess)
+      e = csl::launch_indexer_topk(s->q_idx, s->w, s->k_idx, kt, s->k_scale, s->scale_off, s->scale_group, s->ent_off,
+                                   s->q_pos, s->m, s->B, s->T, s->HI, s->max_entries, s->k, s->idx, hs, pvp);
+  } else if (compress && index && csl::indexer_carries_compress(topk_ws, s->B, s->T, s->max_entries, s->D, s->m)) {
     // the newest-chunk compression rides in spare workgroups of the indexer launch
     const csl::CompressJob job{s->kv, s->z, s->kv_off, s->first_entry, s->max_new_entries, s->ckv, s->m,
                                s->kv_b, s->z_b};
@@ -441,8 +467,9 @@ int csl_csa_decode_step(const csl_csa_step* s, void* stream) {
                               nullptr, pvp);
   }
   if (e != hipSuccess) return hip_status(e, "csa_decode_step launch");
-  e = csl::launch_topk(s->scores, s->ld, s->ent_off, s->q_pos, s->m, s->B, s->T, s->k, s->max_entries, s->idx,
-                       s->topk_ws, csl::indexer_prepares_topk(topk_ws, s->T, s->max_entries), hs);
+  if (!scoreless)
+    e = csl::launch_topk(s->scores, s->ld, s->ent_off, s->q_pos, s->m, s->B, s->T, s->k, s->max_entries, s->idx,
+                         s->topk_ws, csl::indexer_prepares_topk(topk_ws, s->T, s->max_entries), hs);
   if (e != hipSuccess) return hip_status(e, "csa_decode_step launch");
   return hip_status(csl::launch_attention(true, s->q, s->ckv, s->idx, s->k, s->kv, s->kv_off, s->ent_off, s->q_pos, 1,
                                           s->n_win, s->B, s->T, s->H, s->scale, (int64_t)1 << 62, max_keys, s->out,

@@ -112,6 +112,11 @@ __device__ __forceinline__ bf16x8 key_operand(const u32x4& k) {
 template <int HI>
 constexpr int prefill_rows_per_group() { return HI >= 4 ? 1 : 4 / HI; }
 
+// max(0, x) as one integer max on the bits: a negative float (and -0) is a negative integer,
+// so it becomes +0; the same as the float maximum for every value but NaN, which products of
+// finite bf16 values do not produce
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 template <int HI>
 __device__ __forceinline__ void prefill_head_sum(const f32x4& acc, const float (&wv)[4],
                                                  float (&part)[prefill_rows_per_group<HI>()]) {
@@ -121,7 +126,7 @@ __device__ __forceinline__ void prefill_head_sum(const f32x4& acc, const float (
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int q = (HI >= 4) ? 0 : it / HI;
-    part[q] = fmaf(wv[it], fmaxf(acc[it], 0.f), part[q]);
+    part[q] = fmaf(wv[it], relu_bits(acc[it]), part[q]);
   }
   // the partner row's value comes from gfx950's row swaps, not through LDS: permlane16_swap
   // returns (even row, odd row) of each pair of 16-lane rows in every lane, permlane32_swap
@@ -287,9 +292,13 @@ struct FusedShape {
   static_assert(CAP % 64 == 0, "whole waves of slots");
 };
 
-// Cut a row's candidate buffer (n > k entries, ascending ids) to exactly its k best in place,
-// keeping id order; returns the new bar (the k-th best key). One wave, wave-uniform result.
-template <int CAP>
+// Cut a row's candidate buffer (n > k entries, ascending ids) in place, keeping id order, and
+// return the new bar. EXACT: exactly its k best remain and the bar is the k-th best key.
+// Otherwise the search may stop at a key prefix P that at least k and at most k + 32 keys
+// reach (fewer when k is close to CAP - 64), which takes fewer steps: those all remain. The bar is the smallest key kept: at
+// least k kept keys reach it, so a later key at or below it has k better ones before it.
+// One wave, wave-uniform result.
+template <int CAP, bool EXACT>
 __device__ __forceinline__ uint32_t cut_to_k(uint64_t* row, uint32_t& n, int k) {
   constexpr int J = CAP / kWave;
   const int lane = (int)lane_id();
@@ -318,15 +327,23 @@ __device__ __forceinline__ uint32_t cut_to_k(uint64_t* row, uint32_t& n, int k) 
   below |= below >> 8;
   below |= below >> 16;
   uint32_t t = hi & ~below;
-  bool exact = false;
+  bool exact = false;  // every key at or above t remains: no ties to resolve
+  uint32_t reach = n;  // keys at or above t
+  // a coarse cut keeps at most k + 32 keys, and always room for a 64-key step after it
+  const uint32_t loose = (uint32_t)k + min(32u, (uint32_t)(CAP - kWave - k));
   {
     for (int bit = __popc(below) - 1; bit >= 0; --bit) {
+      if (!EXACT && reach <= loose) {
+        exact = true;
+        break;
+      }
       const uint32_t c = t | (1u << bit);
       uint32_t cnt = 0;
 #pragma unroll
       for (int j = 0; j < J; ++j) cnt += (uint32_t)__popcll(__ballot(xs[j] >= c));
       if (cnt >= (uint32_t)k) {
         t = c;
+        reach = cnt;
         if (cnt == (uint32_t)k) {
           exact = true;
           break;
@@ -367,7 +384,7 @@ __device__ __forceinline__ uint32_t cut_to_k(uint64_t* row, uint32_t& n, int k) 
     out += (uint32_t)__popcll(km);
   }
   n = out;
-  return wave_min_u32(bar);
+  return wave_min_u32(bar);  // the smallest key kept: at least k keys reach it
 }
 
 template <int HI, int KT, bool PAGED>
@@ -384,6 +401,7 @@ __global__ __launch_bounds__(kFusedWaves * kWave) void indexer_topk_kernel(
   static_assert(RPW >= 1 && QR % kFusedWaves == 0, "whole rows per wave");
   __shared__ __align__(16) float sval[2][QR][CH];
   __shared__ uint64_t cand[QR][CAP];
+  __shared__ uint32_t cut_req;  // last chunk index by which some row asked all rows to cut
 
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
@@ -450,9 +468,11 @@ __global__ __launch_bounds__(kFusedWaves * kWave) void indexer_topk_kernel(
       if (FP8) sc[u] = ok ? k_scale[scale_off[b] + s / scale_group] : 0.f;
     }
   };
+  if (threadIdx.x == 0) cut_req = 0;  // read only after the first chunk's barrier
   if (n_max > 0) load_chunk(0);
   int buf = 0;
-  for (int64_t s0 = 0; s0 < n_max; s0 += CH, buf ^= 1) {
+  uint32_t jc = 0;  // chunk index
+  for (int64_t s0 = 0; s0 < n_max; s0 += CH, buf ^= 1, ++jc) {
     bf16x8 b0[U], b1[U];
     float scu[U];
 #pragma unroll
@@ -464,34 +484,46 @@ __global__ __launch_bounds__(kFusedWaves * kWave) void indexer_topk_kernel(
     if (s0 + CH < n_max) load_chunk(s0 + CH);  // the next chunk's keys fly during this one
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      // the NB products of a key tile are independent: issue them back to back
+      f32x4 acc[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma16x16x32(a[nb][0], b0[u], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma16x16x32(a[nb][1], b1[u], acc[nb]);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mfma16x16x32(a[nb][0], b0[u], acc);
-        acc = mfma16x16x32(a[nb][1], b1[u], acc);
         float part[RPG];
-        prefill_head_sum<HI>(acc, wv[nb], part);
-        if (prefill_writer<HI>(g)) {
+        prefill_head_sum<HI>(acc[nb], wv[nb], part);
+        // every lane writes: lanes that share a (row, key) hold the same sum bit for bit
 #pragma unroll
-          for (int q = 0; q < RPG; ++q) {
-            float v = part[q];
-            if (FP8) v *= scu[u];
-            sval[buf][nb * QPB + prefill_row<HI>(g, q)][(wave * U + u) * 16 + c] = v;
-          }
+        for (int q = 0; q < RPG; ++q) {
+          float v = part[q];
+          if (FP8) v *= scu[u];
+          sval[buf][nb * QPB + prefill_row<HI>(g, q)][(wave * U + u) * 16 + c] = v;
         }
       }
     }
     __syncthreads();
+    // Rows fill at similar rates, so cuts are taken together: a row that the next chunk might
+    // overflow asks for a cut by chunk jc + 1, and at that chunk every wave cuts its rows that
+    // hold more than k + 64 entries. Cuts taken apart would each hold up the others at the
+    // next barrier. (A wave that reads a later request cuts early: harmless.)
+    const bool cut_now = jc > 0 && *(volatile uint32_t*)&cut_req >= jc;
+    bool ask = false;
 #pragma unroll
     for (int i = 0; i < RPW; ++i) {
       const int r = wave * RPW + i;
+      if (cut_now && cnt[i] > (uint32_t)k + 64u) bar[i] = cut_to_k<CAP, false>(cand[r], cnt[i], k);
       if (cnt[i] + CH <= (uint32_t)CAP) {
         // the whole chunk fits: its score reads go out together, then the ballots
         uint32_t x[CH / kWave];
+        float v[CH / kWave];
+#pragma unroll
+        for (int j = 0; j < CH / kWave; ++j) v[j] = sval[buf][r][j * kWave + lane];  // in range: read unmasked
 #pragma unroll
         for (int j = 0; j < CH / kWave; ++j) {
           const int64_t s = s0 + j * kWave + lane;
-          x[j] = s < nv_mine[i] ? score_key(sval[buf][r][j * kWave + lane]) : 0u;
+          x[j] = s < nv_mine[i] ? score_key(v[j]) : 0u;
         }
 #pragma unroll
         for (int j = 0; j < CH / kWave; ++j) {
@@ -503,23 +535,26 @@ __global__ __launch_bounds__(kFusedWaves * kWave) void indexer_topk_kernel(
       } else {
 #pragma unroll 1
         for (int j = 0; j < CH / kWave; ++j) {  // not unrolled: one copy of the cut per row
-          if (cnt[i] + kWave > (uint32_t)CAP) bar[i] = cut_to_k<CAP>(cand[r], cnt[i], k);
+          if (cnt[i] + kWave > (uint32_t)CAP) bar[i] = cut_to_k<CAP, false>(cand[r], cnt[i], k);
           const int64_t s = s0 + j * kWave + lane;
-          const uint32_t x = s < nv_mine[i] ? score_key(sval[buf][r][j * kWave + lane]) : 0u;
+          const float v = sval[buf][r][j * kWave + lane];
+          const uint32_t x = s < nv_mine[i] ? score_key(v) : 0u;
           const bool admit = x > bar[i];
           const uint64_t mk = __ballot(admit);
           if (admit) cand[r][cnt[i] + rank_in_wave(mk)] = ((uint64_t)x << 32) | (uint32_t)s;
           cnt[i] += (uint32_t)__popcll(mk);
         }
       }
+      ask = ask || cnt[i] + CH > (uint32_t)CAP;
     }
+    if (ask && lane == 0) atomicMax(&cut_req, jc + 1);
   }
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
     const int r = wave * RPW + i;
     const int t = t0 + r;
     if (t >= T) continue;
-    if (cnt[i] > (uint32_t)k) cut_to_k<CAP>(cand[r], cnt[i], k);
+    if (cnt[i] > (uint32_t)k) cut_to_k<CAP, true>(cand[r], cnt[i], k);
     int32_t* out = idx + ((int64_t)b * T + t) * k;
     for (int j = lane; j < k; j += kWave) out[j] = (uint32_t)j < cnt[i] ? (int32_t)(uint32_t)cand[r][j] : -1;
   }

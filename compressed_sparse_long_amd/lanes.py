@@ -15,7 +15,8 @@ import math
 
 import torch
 
-from . import (PagedCache, attn_workspace_bytes, compress_kv, compress_kv_overlap, csa_decode_step, hca_attn_decode, indexer_scores, sparse_attn_decode,
+from . import (PagedCache, attn_workspace_bytes, compress_kv, compress_kv_overlap, csa_decode_step, hca_attn_decode,
+               indexer_scores, indexer_topk, sparse_attn_decode,
                topk_select, topk_workspace_bytes)
 
 
@@ -157,8 +158,11 @@ class _Lane:
 
 
 class CsaLane(_Lane):
-    def __init__(self, lane, kv, z, q, li, device="cuda", fused: bool = True, kv_b=None, z_b=None):
+    def __init__(self, lane, kv, z, q, li, device="cuda", fused: bool = True, kv_b=None, z_b=None,
+                 scoreless: bool = False):
         super().__init__(lane, kv, z, q, li.kv_off, li.ent_off, li.q_pos, device)
+        # scoreless: the step selects with the indexer fused with top-k and keeps no score matrix
+        self.scoreless = scoreless
         # overlapped compression ([P2] "Deep Dive", dual-series KV compression): series b
         # rows kv_b / z_b, shaped like kv / z; None keeps single-series compression
         self.kv_b, self.z_b = kv_b, z_b
@@ -171,7 +175,8 @@ class CsaLane(_Lane):
         self.scale_off = None if li.scale_off is None else li.scale_off.to(device)
         self.scale_group = lane.scale_group
         self.k_format = "mxfp4" if getattr(lane, "kI_fp4", False) else None
-        self.scores = torch.empty((self.B, self.T, max(self.max_entries, 1)), dtype=torch.float32, device=device)
+        self.scores = None if scoreless else torch.empty((self.B, self.T, max(self.max_entries, 1)),
+                                                          dtype=torch.float32, device=device)
         self.idx = torch.empty((self.B, self.T, self.k), dtype=torch.int32, device=device)
         nb = topk_workspace_bytes(self.B, self.T, self.max_entries, self.k)
         self.topk_ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=device)  # contents never matter on entry
@@ -203,6 +208,12 @@ class CsaLane(_Lane):
             self.k_scale_copies = [self.k_scale] + [self.k_scale.clone() for _ in range(copies - 1)]
 
     def index(self, r: int = 0):
+        if self.scoreless:  # the selection itself: no score matrix
+            indexer_topk(self.qI, self.w, self.kI_copies[r % len(self.kI_copies)], self.ent_off, self.q_pos, self.m,
+                         self.k, self.idx, max_entries=self.max_entries,
+                         k_scale=self.k_scale_copies[r % len(self.k_scale_copies)], scale_off=self.scale_off,
+                         scale_group=self.scale_group, k_format=self.k_format, paged=self.paged)
+            return
         indexer_scores(self.qI, self.w, self.kI_copies[r % len(self.kI_copies)], self.ent_off, self.q_pos, self.m,
                        self.scores, max_entries=self.max_entries,
                        k_scale=self.k_scale_copies[r % len(self.k_scale_copies)], scale_off=self.scale_off,
@@ -210,6 +221,8 @@ class CsaLane(_Lane):
                        k_format=self.k_format, paged=self.paged)
 
     def select(self):
+        if self.scoreless:  # index() already selected
+            return
         topk_select(self.scores, self.ent_off, self.q_pos, self.m, self.k, self.idx, ws=self.topk_ws,
                     max_entries=self.max_entries, prepared=self.fused)
 
@@ -256,8 +269,9 @@ class HcaLane(_Lane):
         self.attend(r)
 
 
-def build_lanes(inp, device="cuda"):
-    """Upload a ``synth.Inputs`` and wrap each of its lanes."""
+def build_lanes(inp, device="cuda", scoreless: bool = False):
+    """Upload a ``synth.Inputs`` and wrap each of its lanes (``scoreless``: CSA steps select
+    with the indexer fused with top-k, keeping no score matrix)."""
     kv = inp.kv.to(device)
     z = None if inp.z is None else inp.z.to(device)
     # series b (if drawn) switches the CSA lanes to overlapped compression; HCA keeps one series
@@ -268,7 +282,7 @@ def build_lanes(inp, device="cuda"):
     for li in inp.lanes:
         q = q_all[li.q_slice].contiguous()
         if li.lane.kind == "csa":
-            lanes.append(CsaLane(li.lane, kv, z, q, li, device, kv_b=kv_b, z_b=z_b))
+            lanes.append(CsaLane(li.lane, kv, z, q, li, device, kv_b=kv_b, z_b=z_b, scoreless=scoreless))
         else:
             lanes.append(HcaLane(li.lane, kv, z, q, li, device))
     return lanes

@@ -309,7 +309,9 @@ int csl_hca_attn_decode(const void* q, const void* ckv, const void* kv, const in
  * launch of its own; it never reads what the indexer writes, and the attention runs after
  * both. With kv_b (and z_b when z is given) set, the compression is csl_compress_kv_overlap
  * of the series pair (kv, z) and (kv_b, z_b) instead, carried the same way; kv_b and z_b
- * both NULL keeps single-series compression.
+ * both NULL keeps single-series compression. With scores NULL the indexer and top-k calls
+ * are replaced by csl_indexer_topk (no score matrix; topk_ws, topk_ws_bytes and ld are
+ * ignored; k <= csl_indexer_topk_max_k(HI)), for batches of many query rows.
  */
 typedef struct csl_csa_step {
   /* raw K = V cache and the compression this step adds to ckv */
@@ -330,7 +332,7 @@ typedef struct csl_csa_step {
   int scale_group;
   int HI;
   int CI;
-  float* scores;              /* fp32 [B, T, ld] */
+  float* scores;              /* fp32 [B, T, ld], or NULL: indexer fused with top-k */
   int64_t ld;
   void* topk_ws;              /* csl_topk_workspace_bytes(B, T, max_entries, k) bytes */
   size_t topk_ws_bytes;

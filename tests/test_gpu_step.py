@@ -95,3 +95,30 @@ def test_csa_decode_step_repeats_identically():
     assert torch.equal(outs[0][0], outs[1][0])
     assert torch.equal(outs[0][1], outs[1][1])
     assert torch.equal(outs[0][2], outs[1][2])
+
+
+@pytest.mark.parametrize("lengths,q_pos,T,k,HI,overlap,fmt", [
+    ((40000, 9000, 3001), (39000, 8000, 2001), 24, 512, 8, False, None),  # prefill rows: equal bit for bit
+    ((20000, 7000), (19500, 6900), 40, 256, 16, True, None),
+    ((30000, 5000, 800), (29000, 4000, 700), 24, 300, 8, False, "mxfp4"),
+])
+def test_csa_step_without_scores_matches_step_with_scores(lengths, q_pos, T, k, HI, overlap, fmt):
+    """With no score buffer the step selects with the indexer fused with top-k: for query
+    batches where indexer_scores takes its prefill tiling (B*T >= 64, T >= 16) the compressed
+    rows, the ids and the attention equal the scored step's exactly."""
+    from compressed_sparse_long_amd import lanes
+    print(f"scoreless step lengths={lengths} T={T} k={k} HI={HI} overlap={overlap} fmt={fmt}", flush=True)
+    lane = W.Lane("csa", tuple(lengths), tuple(q_pos), T=T, H=16, m=4, k=k, HI=HI, kI_fp4=fmt == "mxfp4")
+    parts = ("kv", "z", "q", "qI", "kI", "w") + (("kv_b", "z_b") if overlap else ())
+    inp = synth.generate(W.Workload("step_nos", 17 + T, (lane,)), parts=parts)
+    res = []
+    for scoreless in (False, True):
+        (cl,) = lanes.build_lanes(inp, scoreless=scoreless)
+        cl.compress_all()
+        assert (cl.scores is None) == scoreless
+        cl.idx.fill_(-7)
+        cl.step(0)
+        torch.cuda.synchronize()
+        res.append((cl.ckv.clone(), cl.idx.clone(), cl.out.clone(), cl.lse.clone()))
+    for a, b, what in zip(res[0], res[1], ("ckv", "idx", "out", "lse")):
+        assert torch.equal(a, b), f"{what} differs without scores"

@@ -268,6 +268,24 @@ def test_csa_prefill_8k_on_128k(lanes_mod):
         _check_csa_row(cl, inp, li, 0, t, keys)
 
 
+def test_csa_prefill_8k_on_128k_without_scores(lanes_mod):
+    """The same prefill step with the indexer fused with top-k (no 1.14 GB score matrix):
+    the ids and the attention equal the scored step's bit for bit."""
+    print("workload csa_prefill_8k_on_128k without scores: generating inputs", flush=True)
+    inp = synth.generate("csa_prefill_8k_on_128k")
+    res = []
+    for scoreless in (False, True):
+        (cl,) = lanes_mod.build_lanes(inp, scoreless=scoreless)
+        cl.compress_all()
+        cl.step()
+        torch.cuda.synchronize()
+        res.append((cl.idx.clone(), cl.out.clone(), cl.lse.clone()))
+        del cl
+        torch.cuda.empty_cache()
+    for a, b, what in zip(res[0], res[1], ("idx", "out", "lse")):
+        assert torch.equal(a, b), f"{what} differs without scores"
+
+
 def test_mixed_decode_b32(lanes_mod):
     inp, (csa_l, hca_l) = _run(lanes_mod, "mixed_decode_b32")
     li_c, li_h = inp.lanes
