@@ -268,7 +268,8 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_kernel(
 // Indexer fused with top-k: the scores never leave the chip. A workgroup takes QR query rows
 // (16; 8 at HI = 16) over the whole key range, in chunks of 256 keys: its 8 waves score the
 // chunk with the prefill tiling's MFMAs and arithmetic into one of two LDS staging buffers,
-// then each wave files the scores of its own rows into that row's candidate buffer in LDS,
+// then each wave files the scores of its own rows into that row's candidate buffer in LDS
+// (the rest of the workgroup's LDS: 960 slots per row, 2240 at HI = 16),
 // admitting only keys above the row's bar. The keys of the next chunk are in flight while a
 // chunk is scored and filed, and with two staging buffers one barrier per chunk suffices: a
 // wave that passes the barrier of chunk j has filed chunk j - 1, whose buffer chunk j + 1
@@ -281,15 +282,16 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_kernel(
 constexpr int kFusedWaves = 8;
 constexpr int kFusedU = 2;                               // key tiles of 16 per wave and chunk
 constexpr int kFusedChunk = kFusedWaves * kFusedU * 16;  // keys per chunk
-constexpr int kFusedSlots = 15360;                       // candidate slots per workgroup (120 KB)
+constexpr int kFusedLds = 160 * 1024;                    // LDS of one workgroup on gfx950
 
 template <int HI>
 struct FusedShape {
   static constexpr int QPB = 16 / HI;
   static constexpr int NB = HI == 16 ? 8 : HI;  // A tiles (all waves hold all of them)
-  static constexpr int QR = NB * QPB;           // query rows per workgroup
-  static constexpr int CAP = kFusedSlots / QR;  // candidate slots per row
-  static_assert(CAP % 64 == 0, "whole waves of slots");
+  static constexpr int QR = NB * QPB;           // query rows per workgroup: 16 (8 at HI = 16)
+  // candidate slots per row: the LDS left beside the two staging buffers, in whole waves
+  static constexpr int CAP = (kFusedLds - 2 * QR * kFusedChunk * 4 - 256) / (8 * QR) / 64 * 64;
+  static_assert(CAP % 64 == 0 && CAP >= 512, "whole waves of slots");
 };
 
 // Cut a row's candidate buffer (n > k entries, ascending ids) in place, keeping id order, and

@@ -221,7 +221,7 @@ int csl_topk_select(const float* scores, int64_t ld, const int64_t* ent_off, con
  * indexer_scores (keys, scales, offsets, paged cache) and topk_select (k, idx), without the
  * score buffer and workspace.
  *
- *   k     1 <= k <= csl_indexer_topk_max_k(HI) (896 for HI <= 8, 1856 for HI = 16)
+ *   k     1 <= k <= csl_indexer_topk_max_k(HI) (896 for HI <= 8, 2176 for HI = 16)
  *   idx   int32 [B, T, k]
  * One workgroup scores 16 query rows (8 at HI = 16) against all of their visible entries
  * and keeps each row's candidates in on-chip memory, so the call suits batches of many

@@ -73,11 +73,12 @@ def _oracle_check(li, kI_cpu, got, k, fmt, rows=None):
 @pytest.mark.parametrize("HI,T,lengths,q_pos,k,fmt", [
     (8, 40, [9000, 4100, 60, 2049], [8900, 4000, 0, 2000], 64, None),     # ragged rows, one short of k
     (8, 16, [20000, 3333, 7001, 500], [19000, 3300, 7001, 400], 512, None),
-    (8, 33, [4096, 4000], [4000, 3900], None, None),                      # k at its limit
-    (16, 24, [6000, 2500, 900], [5990, 2400, 800], None, None),           # HI = 16, 8 rows per workgroup; k limit
+    (8, 33, [12000, 10000], [11900, 9900], None, None),                   # k at its limit
+    (16, 24, [16000, 2500, 900], [15990, 2400, 800], None, None),         # HI = 16; k at its limit
     (4, 20, [5000, 1300, 2222, 17], [4900, 1250, 2100, 0], 100, None),
     (2, 17, [3000, 2000, 1000, 4000], [2999, 1999, 999, 3999], 37, None),
     (1, 64, [2500], [2400], 8, None),
+    (1, 64, [9000], [8800], None, None),                                  # HI = 1; k at its limit
     (8, 18, [8000, 3000, 600, 5000], [7900, 2900, 500, 4900], 256, "fp8"),
     (8, 16, [10000, 2000, 700, 3000], [9900, 1900, 600, 2900], 512, "mxfp4"),
 ])
@@ -164,7 +165,8 @@ def test_fused_argument_errors(csl):
     idx = torch.empty((1, 16, 8), dtype=torch.int32, device="cuda")
     base = (dev(li.qI), dev(li.w), dev(li.kI), dev(li.ent_off), dev(li.q_pos), 4)
     kmax = csl.indexer_topk_max_k(8)
-    assert kmax == 896 and csl.indexer_topk_max_k(16) == 1856 and csl.indexer_topk_max_k(3) == 0
+    assert kmax == 896 and csl.indexer_topk_max_k(16) == 2176 and csl.indexer_topk_max_k(1) == 896
+    assert csl.indexer_topk_max_k(3) == 0
     with pytest.raises(csl.CslError, match="k must be in"):
         csl.indexer_topk(*base, kmax + 1, torch.empty((1, 16, kmax + 1), dtype=torch.int32, device="cuda"),
                          max_entries=250)
