@@ -212,3 +212,35 @@ def test_step_validation(lib):
     assert call(rope_dims=40, rope_base=1e4) == 2   # RoPE width not a multiple of 32
     assert call(B=0) == 0                       # nothing to do: nothing enqueued
     assert _err(lib) == ""
+    # without a score buffer: the fused indexer/top-k's limit on k applies instead
+    assert call(scores=None, k=897) == 2
+    assert "without scores" in _err(lib)
+    assert call(scores=None, idx=None) == 1
+    assert call(scores=None, ld=0, B=0) == 0    # ld is ignored without scores
+    assert _err(lib) == ""
+
+
+def test_indexer_topk_validation(lib):
+    f = lib.csl_indexer_topk
+    I, L = ctypes.c_int, ctypes.c_int64
+    f.argtypes = [P, P, P, I, P, P, I, P, P, I, I, I, I, I, L, I, P, P, P]
+    mk = lib.csl_indexer_topk_max_k
+    mk.argtypes = [I]
+    assert mk(8) == 896 and mk(4) == 896 and mk(1) == 896 and mk(16) == 2176 and mk(3) == 0
+
+    def call(idx=FAKE, k=64, HI=8, CI=64, B=1, T=16, me=1000, kd=0, ks=None, m=4):
+        # q_idx, w, k_idx, k_dtype, k_scale, scale_off, group, ent_off, q_pos, m, B, T, HI, CI, max_entries, k, idx
+        return f(FAKE, FAKE, FAKE, kd, ks, None, 64, FAKE, FAKE, m, B, T, HI, CI, me, k, idx, None, None)
+
+    assert call(idx=None) == 1 and "null" in _err(lib)
+    assert call(k=0) == 2 and "k must be in" in _err(lib)
+    assert call(k=897) == 2 and "k must be in" in _err(lib)
+    assert call(HI=3) == 2 and "HI" in _err(lib)
+    assert call(CI=32) == 2 and "CI" in _err(lib)
+    assert call(m=0) == 1
+    assert call(B=-1) == 1
+    assert call(kd=3) == 1 and "MXFP4" in _err(lib)          # MXFP4 keys need their scales
+    assert call(me=1 << 31) == 2 and "max_entries" in _err(lib)
+    assert call(idx=P((1 << 20) + 2)) == 1 and "aligned" in _err(lib)
+    # nothing to do is a success without touching the device
+    assert call(T=0) == 0 and _err(lib) == ""
