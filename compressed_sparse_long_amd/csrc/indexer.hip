@@ -266,10 +266,10 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_kernel(
 
 // ---------------------------------------------------------------------------------------------
 // Indexer fused with top-k: the scores never leave the chip. A workgroup takes QR query rows
-// (16; 8 at HI = 16) over the whole key range, in chunks of 256 keys: its 8 waves score the
+// (8; 16 at HI = 1) over the whole key range, in chunks of 256 keys: its 8 waves score the
 // chunk with the prefill tiling's MFMAs and arithmetic into one of two LDS staging buffers,
 // then each wave files the scores of its own rows into that row's candidate buffer in LDS
-// (the rest of the workgroup's LDS: 960 slots per row, 2240 at HI = 16),
+// (the LDS left to the workgroup: 960 slots per row, 2240 at HI = 16),
 // admitting only keys above the row's bar. The keys of the next chunk are in flight while a
 // chunk is scored and filed, and with two staging buffers one barrier per chunk suffices: a
 // wave that passes the barrier of chunk j has filed chunk j - 1, whose buffer chunk j + 1
@@ -282,15 +282,20 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_kernel(
 constexpr int kFusedWaves = 8;
 constexpr int kFusedU = 2;                               // key tiles of 16 per wave and chunk
 constexpr int kFusedChunk = kFusedWaves * kFusedU * 16;  // keys per chunk
-constexpr int kFusedLds = 160 * 1024;                    // LDS of one workgroup on gfx950
+constexpr int kFusedCuLds = 160 * 1024;                  // LDS of one gfx950 compute unit
 
 template <int HI>
 struct FusedShape {
   static constexpr int QPB = 16 / HI;
-  static constexpr int NB = HI == 16 ? 8 : HI;  // A tiles (all waves hold all of them)
-  static constexpr int QR = NB * QPB;           // query rows per workgroup: 16 (8 at HI = 16)
-  // candidate slots per row: the LDS left beside the two staging buffers, in whole waves
-  static constexpr int CAP = (kFusedLds - 2 * QR * kFusedChunk * 4 - 256) / (8 * QR) / 64 * 64;
+  static constexpr int QR = QPB > 8 ? QPB : 8;  // query rows per workgroup: 8 (16 at HI = 1)
+  static constexpr int NB = QR / QPB;           // A tiles (all waves hold all of them)
+  // two workgroups per compute unit, so each wave has three others on its SIMD to hide
+  // latency behind (one at HI = 1, whose A tile alone spans 16 rows, and at HI = 16, whose
+  // 8 A tiles need more registers than 4 waves per SIMD leave)
+  static constexpr int WG_PER_CU = (QR == 8 && NB <= 4) ? 2 : 1;
+  static constexpr int WAVES_PER_SIMD = WG_PER_CU * kFusedWaves / 4;
+  // candidate slots per row: the workgroup's LDS share left beside the two staging buffers
+  static constexpr int CAP = (kFusedCuLds / WG_PER_CU - 2 * QR * kFusedChunk * 4 - 256) / (8 * QR) / 64 * 64;
   static_assert(CAP % 64 == 0 && CAP >= 512, "whole waves of slots");
 };
 
@@ -390,7 +395,7 @@ __device__ __forceinline__ uint32_t cut_to_k(uint64_t* row, uint32_t& n, int k) 
 }
 
 template <int HI, int KT, bool PAGED>
-__global__ __launch_bounds__(kFusedWaves * kWave) void indexer_topk_kernel(
+__global__ __launch_bounds__(kFusedWaves * kWave, FusedShape<HI>::WAVES_PER_SIMD) void indexer_topk_kernel(
     const uint16_t* __restrict__ qI, const float* __restrict__ w, const void* __restrict__ kI,
     const void* __restrict__ k_scale_v, const int64_t* __restrict__ scale_off, int scale_group,
     const int64_t* __restrict__ ent_off, const int64_t* __restrict__ q_pos, int m, int T,
@@ -398,7 +403,7 @@ __global__ __launch_bounds__(kFusedWaves * kWave) void indexer_topk_kernel(
   using FS = FusedShape<HI>;
   constexpr int QPB = FS::QPB, NB = FS::NB, QR = FS::QR, CAP = FS::CAP;
   constexpr int U = kFusedU, CH = kFusedChunk;
-  constexpr int RPW = QR / kFusedWaves;  // rows each wave files (2, or 1 at HI = 16)
+  constexpr int RPW = QR / kFusedWaves;  // rows each wave files (1, or 2 at HI = 1)
   constexpr int RPG = prefill_rows_per_group<HI>();
   static_assert(RPW >= 1 && QR % kFusedWaves == 0, "whole rows per wave");
   __shared__ __align__(16) float sval[2][QR][CH];
@@ -516,8 +521,11 @@ __global__ __launch_bounds__(kFusedWaves * kWave) void indexer_topk_kernel(
     for (int i = 0; i < RPW; ++i) {
       const int r = wave * RPW + i;
       if (cut_now && cnt[i] > (uint32_t)k + 64u) bar[i] = cut_to_k<CAP, false>(cand[r], cnt[i], k);
-      if (cnt[i] + CH <= (uint32_t)CAP) {
-        // the whole chunk fits: its score reads go out together, then the ballots
+      // a coarse cut leaves at most k + 32 entries; when a whole chunk fits after that, one
+      // check per chunk suffices, against the keys the chunk actually admits
+      const bool chunk_check = (uint32_t)k + 32u + CH <= (uint32_t)CAP;
+      if (chunk_check || cnt[i] + CH <= (uint32_t)CAP) {
+        // the chunk's score reads go out together, then the ballots
         uint32_t x[CH / kWave];
         float v[CH / kWave];
 #pragma unroll
@@ -527,13 +535,27 @@ __global__ __launch_bounds__(kFusedWaves * kWave) void indexer_topk_kernel(
           const int64_t s = s0 + j * kWave + lane;
           x[j] = s < nv_mine[i] ? score_key(v[j]) : 0u;
         }
+        uint64_t mk[CH / kWave];
+        uint32_t adm = 0;
 #pragma unroll
         for (int j = 0; j < CH / kWave; ++j) {
-          const bool admit = x[j] > bar[i];
-          const uint64_t mk = __ballot(admit);
-          if (admit) cand[r][cnt[i] + rank_in_wave(mk)] = ((uint64_t)x[j] << 32) | (uint32_t)(s0 + j * kWave + lane);
-          cnt[i] += (uint32_t)__popcll(mk);
+          mk[j] = __ballot(x[j] > bar[i]);
+          adm += (uint32_t)__popcll(mk[j]);
         }
+        if (cnt[i] + adm > (uint32_t)CAP) {  // only with chunk_check: cut, then admit above the new bar
+          bar[i] = cut_to_k<CAP, false>(cand[r], cnt[i], k);
+#pragma unroll
+          for (int j = 0; j < CH / kWave; ++j) mk[j] = __ballot(x[j] > bar[i]);
+          adm = 0;
+        }
+#pragma unroll
+        for (int j = 0; j < CH / kWave; ++j) {
+          if ((mk[j] >> lane) & 1ull)
+            cand[r][cnt[i] + rank_in_wave(mk[j])] = ((uint64_t)x[j] << 32) | (uint32_t)(s0 + j * kWave + lane);
+          cnt[i] += (uint32_t)__popcll(mk[j]);
+        }
+        // ask for a shared cut when the next chunks are likely to overflow this row
+        ask = ask || cnt[i] + (chunk_check ? 2u * max(adm, 32u) : (uint32_t)CH) > (uint32_t)CAP;
       } else {
 #pragma unroll 1
         for (int j = 0; j < CH / kWave; ++j) {  // not unrolled: one copy of the cut per row
@@ -546,8 +568,8 @@ __global__ __launch_bounds__(kFusedWaves * kWave) void indexer_topk_kernel(
           if (admit) cand[r][cnt[i] + rank_in_wave(mk)] = ((uint64_t)x << 32) | (uint32_t)s;
           cnt[i] += (uint32_t)__popcll(mk);
         }
+        ask = ask || cnt[i] + CH > (uint32_t)CAP;
       }
-      ask = ask || cnt[i] + CH > (uint32_t)CAP;
     }
     if (ask && lane == 0) atomicMax(&cut_req, jc + 1);
   }
@@ -861,7 +883,7 @@ hipError_t launch_kt(int HI, const void* qI, const float* w, const void* kI, con
 }  // namespace
 
 int indexer_topk_max_k(int HI) {
-  const int cap = HI == 16 ? FusedShape<16>::CAP : FusedShape<8>::CAP;
+  const int cap = HI == 1 ? FusedShape<1>::CAP : HI == 16 ? FusedShape<16>::CAP : FusedShape<8>::CAP;
   return cap - kWave;  // a cut leaves k entries and a sub-step files up to 64 more
 }
 

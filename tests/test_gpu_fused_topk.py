@@ -166,6 +166,7 @@ def test_fused_argument_errors(csl):
     base = (dev(li.qI), dev(li.w), dev(li.kI), dev(li.ent_off), dev(li.q_pos), 4)
     kmax = csl.indexer_topk_max_k(8)
     assert kmax == 896 and csl.indexer_topk_max_k(16) == 2176 and csl.indexer_topk_max_k(1) == 896
+    assert csl.indexer_topk_max_k(4) == 896 and csl.indexer_topk_max_k(2) == 896
     assert csl.indexer_topk_max_k(3) == 0
     with pytest.raises(csl.CslError, match="k must be in"):
         csl.indexer_topk(*base, kmax + 1, torch.empty((1, 16, kmax + 1), dtype=torch.int32, device="cuda"),
