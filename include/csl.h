@@ -223,7 +223,7 @@ int csl_topk_select(const float* scores, int64_t ld, const int64_t* ent_off, con
  *
  *   k     1 <= k <= csl_indexer_topk_max_k(HI) (896 for HI <= 8, 2176 for HI = 16)
  *   idx   int32 [B, T, k]
- * One workgroup scores 16 query rows (8 at HI = 16) against all of their visible entries
+ * One workgroup scores 8 query rows (16 at HI = 1) against all of their visible entries
  * and keeps each row's candidates in on-chip memory, so the call suits batches of many
  * query rows (prefill); a single decode row is better served by indexer_scores with
  * candidate lists and topk_select. No workspace; nothing but idx is written.
