@@ -271,7 +271,7 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_kernel(
 // then each wave files the scores of its own rows into that row's candidate buffer in LDS
 // (the LDS left to the workgroup: 960 slots per row, 2240 at HI = 16),
 // admitting only keys above the row's bar. The keys of the next chunk are in flight while a
-// chunk is scored and filed, and with two staging buffers one barrier per chunk suffices: a
+// chunk is filed, and with two staging buffers one barrier per chunk suffices: a
 // wave that passes the barrier of chunk j has filed chunk j - 1, whose buffer chunk j + 1
 // then reuses. The buffer holds (key << 32 | id) in ascending id order. When it could
 // overflow, the wave cuts it to exactly the k best by (score descending, id ascending) and
@@ -488,7 +488,6 @@ __global__ __launch_bounds__(kFusedWaves * kWave, FusedShape<HI>::WAVES_PER_SIMD
       b1[u] = key_operand<KT>(kb[u][1]);
       scu[u] = sc[u];
     }
-    if (s0 + CH < n_max) load_chunk(s0 + CH);  // the next chunk's keys fly during this one
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       // the NB products of a key tile are independent: issue them back to back
@@ -510,6 +509,9 @@ __global__ __launch_bounds__(kFusedWaves * kWave, FusedShape<HI>::WAVES_PER_SIMD
         }
       }
     }
+    // the next chunk's keys fly during the barrier and the filing (issued after the MFMAs, so
+    // they do not hold registers beside this chunk's operands)
+    if (s0 + CH < n_max) load_chunk(s0 + CH);
     __syncthreads();
     // Rows fill at similar rates, so cuts are taken together: a row that the next chunk might
     // overflow asks for a cut by chunk jc + 1, and at that chunk every wave cuts its rows that
