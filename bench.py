@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="wall budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stages", action="store_true", help="skip the per-stage breakdown pass")
+    ap.add_argument("--no-configs", action="store_true", help="skip the every-configuration pass")
+    ap.add_argument("--config-cpu-seconds", type=float, default=3.0,
+                    help="oracle sample per configuration in the every-configuration pass")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM counters)")
     ap.add_argument("--report-configs", action="store_true",
@@ -110,10 +113,30 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "copies": 5}))
 
 
+def host_machine():
+    """The host the oracle runs on: cores this process may use, the CPU model and the BLAS
+    thread count (the oracle's only parallelism)."""
+    from threadpoolctl import threadpool_info
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = 1
+    for info in threadpool_info():
+        if info.get("user_api") == "blas":
+            blas = max(blas, int(info.get("num_threads", 1)))
+    return {"affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": model, "blas_threads": blas,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
 def cpu_baseline(inp, seconds: float):
     """The fp64 oracle on whole decode queries of the same workload, on the host cores."""
     import numpy as np
-    from threadpoolctl import threadpool_info
 
     from oracle import csa
 
@@ -145,13 +168,11 @@ def cpu_baseline(inp, seconds: float):
         csa.attend(q[b, 0].double().numpy(), X, scale)
         n += 1
     el = time.perf_counter() - t0
-    threads = 1
-    for info in threadpool_info():
-        if info.get("user_api") == "blas":
-            threads = max(threads, int(info.get("num_threads", 1)))
-    return {"value": n / el, "unit": "queries/s", "cores": threads, "kind": "oracle",
+    mach = host_machine()
+    return {"value": n / el, "unit": "queries/s", "cores": mach["blas_threads"], "kind": "oracle",
             "sample": f"{n} whole decode queries of {WORKLOAD} (fp64 numpy: newest-chunk compression, "
-                      f"indexer over 262144 keys, top-1024, attention over 1152 rows) in {el:.1f} s"}
+                      f"indexer over 262144 keys, top-1024, attention over 1152 rows) in {el:.1f} s",
+            "machine": mach}
 
 
 def main():
@@ -172,6 +193,21 @@ def main():
         report_configs(args.copies, args.cpu_seconds)
         return
 
+    result = measure_headline(args)
+    if not args.no_configs:
+        # every synthetic configuration's whole step beside its roofline and the oracle (the
+        # headline pass's buffers and graphs are released first)
+        import gc
+        gc.collect()
+        torch.cuda.empty_cache()
+        result["configs"] = {ln.pop("workload"): ln for ln in
+                             report_configs(args.copies, args.config_cpu_seconds, emit=False)}
+    print(json.dumps(result), flush=True)
+
+
+def measure_headline(args) -> dict:
+    """The bench line's headline figures on the 1M-context CSA decode workload."""
+    import torch
     import synth
     from compressed_sparse_long_amd import lanes
 
@@ -397,7 +433,7 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
-    print(json.dumps(result), flush=True)
+    return result
 
 
 def run_workload(name: str, steps: int, warmup: int, paged: str | None = None, copies: int = 4,
@@ -480,7 +516,6 @@ def oracle_rate(inp, seconds: float, D: int = 128):
     cache built before the clock starts (as the GPU's is); per query the newest chunk's
     compression, then indexer, top-k and sparse attention (CSA) or dense attention (HCA)."""
     import numpy as np
-    from threadpoolctl import threadpool_info
 
     from oracle import csa, pipeline
 
@@ -524,17 +559,15 @@ def oracle_rate(inp, seconds: float, D: int = 128):
         csa.attend(q[t], X, scale)
         n += 1
     el = time.perf_counter() - t0
-    threads = 1
-    for info in threadpool_info():
-        if info.get("user_api") == "blas":
-            threads = max(threads, int(info.get("num_threads", 1)))
-    return {"value": round(n / el, 2), "unit": "queries/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} queries ({len(work)} sampled sequence(s), fp64 numpy) in {el:.1f} s"}
+    mach = host_machine()
+    return {"value": round(n / el, 2), "unit": "queries/s", "cores": mach["blas_threads"], "kind": "oracle",
+            "sample": f"{n} queries ({len(work)} sampled sequence(s), fp64 numpy) in {el:.1f} s", "machine": mach}
 
 
-def report_configs(copies: int, cpu_seconds: float) -> None:
+def report_configs(copies: int, cpu_seconds: float, emit: bool = True) -> list:
     """Every synthetic configuration: whole-step time (graph of `copies` rotated steps),
-    queries/s, algorithmic GB/s and roofline fraction, and the oracle's rate beside it."""
+    queries/s, algorithmic GB/s and roofline fraction, and the oracle's rate beside it.
+    Returns one dict per configuration (and prints each as a JSON line when ``emit``)."""
     import torch
     import synth
     from compressed_sparse_long_amd import lanes
@@ -567,7 +600,9 @@ def report_configs(copies: int, cpu_seconds: float) -> None:
         torch.cuda.empty_cache()
         return a.elapsed_time(b) / (reps * copies) * 1e3
 
+    lines = []
     for name in synth.CONFIG_ORDER:
+        print(f"# configuration {name}: generating inputs", file=sys.stderr, flush=True)
         inp = synth.generate(name)
         step_us = time_step(inp, False)
         nbytes, flops, queries = step_model([li.lane for li in inp.lanes])
@@ -585,7 +620,13 @@ def report_configs(copies: int, cpu_seconds: float) -> None:
                 "bound": "hbm" if nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) else "mfma",
                 "roofline_us": round(bound_us, 2), "roofline_frac": round(bound_us / step_us, 4), **extra,
                 "cpu_baseline": oracle_rate(inp, cpu_seconds)}
-        print(json.dumps(line), flush=True)
+        del inp
+        lines.append(line)
+        if emit:
+            print(json.dumps(line), flush=True)
+        else:
+            print(f"# configuration {name}: {line['step_us']} us per step", file=sys.stderr, flush=True)
+    return lines
 
 
 if __name__ == "__main__":

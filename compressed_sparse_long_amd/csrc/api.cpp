@@ -98,6 +98,29 @@ int check_paged(const char* who, const csl_paged_cache* pc, int B, csl::PagedVie
   return CSL_OK;
 }
 
+// The per-sequence ring of raw rows must hold every raw row a call reads at once: the window
+// of each of the T query rows (rows p - n_win + 1 .. p for p = q_pos + t, the newest rows of a
+// context whose queries sit at its end: n_win + T - 1 rows) and the chunks being compressed
+// (entries first_entry .. first_entry + max_new - 1, the newest ones: max_new chunks of m rows,
+// one more for overlapped compression's series b, and up to m - 1 rows of uncompressed tail).
+// Both are suffixes of the sequence, so the larger one covers their union. Nothing to check
+// without a ring (raw rows packed as kv_off says).
+int check_ring(const char* who, const csl_paged_cache* pc, int n_win, int T, int m, int64_t max_new, bool overlap) {
+  if (!pc || pc->ring_rows == 0) return CSL_OK;
+  int64_t need = 0;
+  if (n_win > 0 && T > 0) need = (int64_t)n_win + T - 1;
+  if (max_new > 0) {
+    const int64_t comp = (max_new + (overlap ? 2 : 1)) * (int64_t)m - 1;
+    need = comp > need ? comp : need;
+  }
+  if ((int64_t)pc->ring_rows < need)
+    return fail(CSL_ERR_INVALID,
+                "%s: ring_rows (%d) must hold every raw row the call reads: %lld (window n_win + T - 1, "
+                "compressed chunks (max_new_entries + %d) * m - 1)",
+                who, pc->ring_rows, (long long)need, overlap ? 2 : 1);
+  return CSL_OK;
+}
+
 // the launcher's key type: 0 bf16, 1 fp8 e4m3, 2 MXFP4
 int key_type(int k_dtype) {
   return k_dtype == CSL_DTYPE_FP8_E4M3 ? 1 : k_dtype == CSL_DTYPE_MXFP4 ? 2 : 0;
@@ -176,8 +199,8 @@ int csl_compress_kv(const void* kv, const void* z, const int64_t* kv_off, const 
   if (paged) {
     st = check_paged("compress_kv", paged, B, pv);
     if (st != CSL_OK) return st;
-    if (paged->ring_rows > 0 && paged->ring_rows < m)
-      return fail(CSL_ERR_INVALID, "compress_kv: ring_rows must hold a chunk (>= m)");
+    st = check_ring("compress_kv", paged, 0, 0, m, max_new_entries, false);
+    if (st != CSL_OK) return st;
   }
   if (B == 0 || max_new_entries == 0) return ok();
   return hip_status(csl::launch_compress(kv, z, kv_off, ent_off, first_entry, B, D, m, max_new_entries, out,
@@ -197,8 +220,8 @@ int csl_compress_kv_overlap(const void* kv_a, const void* z_a, const void* kv_b,
   if (paged) {
     st = check_paged("compress_kv_overlap", paged, B, pv);
     if (st != CSL_OK) return st;
-    if (paged->ring_rows > 0 && paged->ring_rows < 2 * m)
-      return fail(CSL_ERR_INVALID, "compress_kv_overlap: ring_rows must hold two chunks (>= 2m)");
+    st = check_ring("compress_kv_overlap", paged, 0, 0, m, max_new_entries, true);
+    if (st != CSL_OK) return st;
   }
   if (B == 0 || max_new_entries == 0) return ok();
   return hip_status(csl::launch_compress_overlap(kv_a, z_a, kv_b, z_b, kv_off, ent_off, first_entry, B, D, m,
@@ -293,7 +316,7 @@ static int check_attn(const char* who, const void* q, const void* ckv, const voi
   if (D != 128) return fail(CSL_ERR_UNSUPPORTED, "%s: D must be 128, got %d", who, D);
   if (H < 16 || H > 128 || H % 16 != 0)
     return fail(CSL_ERR_UNSUPPORTED, "%s: H must be a multiple of 16 in [16, 128], got %d", who, H);
-  if (!std::isfinite(scale)) return fail(CSL_ERR_INVALID, "%s: scale must be finite", who);
+  if (!(std::isfinite(scale) && scale > 0.f)) return fail(CSL_ERR_INVALID, "%s: scale must be finite and > 0", who);
   if ((int64_t)B * T > kMaxGridY) return fail(CSL_ERR_UNSUPPORTED, "%s: B*T must be <= %d", who, kMaxGridY);
   if (!aligned(q, 16) || !aligned(ckv, 16) || !aligned(kv, 16) || !aligned(out, 16))
     return fail(CSL_ERR_INVALID, "%s: q, ckv, kv and out must be 16-byte aligned", who);
@@ -339,8 +362,8 @@ int csl_sparse_attn_decode(const void* q, const void* ckv, const int32_t* idx, i
   if (paged) {
     st = check_paged("sparse_attn_decode", paged, B, pv);
     if (st != CSL_OK) return st;
-    if (n_win > 0 && paged->ring_rows < n_win)
-      return fail(CSL_ERR_INVALID, "sparse_attn_decode: ring_rows must hold the window (>= n_win)");
+    st = check_ring("sparse_attn_decode", paged, n_win, T, 1, 0, false);
+    if (st != CSL_OK) return st;
   }
   return hip_status(csl::launch_attention(true, q, ckv, idx, k, kv, kv_off, ent_off, q_pos, 1, n_win, B, T, H, scale,
                                           (int64_t)1 << 62, max_keys, out, lse, ws, ex, as_stream(stream),
@@ -368,8 +391,8 @@ int csl_hca_attn_decode(const void* q, const void* ckv, const void* kv, const in
   if (paged) {
     st = check_paged("hca_attn_decode", paged, B, pv);
     if (st != CSL_OK) return st;
-    if (n_win > 0 && paged->ring_rows < n_win)
-      return fail(CSL_ERR_INVALID, "hca_attn_decode: ring_rows must hold the window (>= n_win)");
+    st = check_ring("hca_attn_decode", paged, n_win, T, m, 0, false);
+    if (st != CSL_OK) return st;
   }
   return hip_status(csl::launch_attention(false, q, ckv, nullptr, 0, kv, kv_off, ent_off, q_pos, m, n_win, B, T, H,
                                           scale, max_entries, max_keys, out, lse, ws, ex, as_stream(stream),
@@ -398,8 +421,8 @@ int csl_csa_decode_step(const csl_csa_step* s, void* stream) {
     if (st != CSL_OK) return st;
     if (s->k_dtype == CSL_DTYPE_FP8_E4M3)
       return fail(CSL_ERR_UNSUPPORTED, "csa_decode_step: fp8 keys are not supported in a paged cache");
-    if (s->paged->ring_rows < s->n_win || s->paged->ring_rows < (overlap ? 2 : 1) * s->m)
-      return fail(CSL_ERR_INVALID, "csa_decode_step: ring_rows must hold the window and the newest chunk(s)");
+    st = check_ring("csa_decode_step", s->paged, s->n_win, s->T, s->m, s->max_new_entries, overlap);
+    if (st != CSL_OK) return st;
     pvp = &pv;
   }
   // no score buffer: the indexer fused with top-k (csl_indexer_topk) makes the selection

@@ -399,8 +399,8 @@ __global__ __launch_bounds__(NHG * 64) void attn_kernel(
     qb[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(q + ((int64_t)row * H + head) * kD + kk * 32 + g * 8));
   // with prefetching, the query and id loads complete before the first row loads: inside the
   // tile loop the compiler then knows the query operands have arrived and the products do not
-  // wait for the prefetch (vmcnt(0); expcnt and lgkmcnt left at their maximum, gfx9 encoding)
-  if (MULTI) __builtin_amdgcn_s_waitcnt(0x0f70);
+  // wait for the prefetch
+  if (MULTI) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
   f32x4 oacc[8];
 #pragma unroll

@@ -60,6 +60,12 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
 
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, kWave); }
 
+// Immediate of s_waitcnt in the gfx9 family's encoding (gfx950 included): vmcnt in bits 3:0
+// and 15:14, expcnt in bits 6:4, lgkmcnt in bits 11:8; a field at its maximum does not wait.
+// waitcnt_vm(n): wait until at most n vector memory operations of this wave are outstanding.
+constexpr int waitcnt_vm(int n) { return (n & 0xf) | (((n >> 4) & 0x3) << 14) | (0x7 << 4) | (0xf << 8); }
+static_assert(waitcnt_vm(0) == 0x0f70 && waitcnt_vm(63) == 0xcf7f, "gfx9 s_waitcnt field layout");
+
 // Order-preserving map of an fp32 score to an unsigned key (larger score -> larger key);
 // -0.0 is folded onto +0.0 first so that the two compare equal.
 __device__ __forceinline__ uint32_t score_key(float f) {

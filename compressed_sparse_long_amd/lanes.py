@@ -116,15 +116,15 @@ class _Lane:
                 out.index_copy_(0, prow, x[:prow.numel()])
             return out
 
-        # ring row of the newest ring_rows raw rows of every sequence
+        # ring row of the newest ring_rows raw rows of every sequence (none for ring_rows = 0)
         src, dst = [], []
         offs = lane.kv_off()
-        for b, n in enumerate(lane.lengths):
+        for b, n in enumerate(lane.lengths if ring_rows > 0 else ()):
             r = torch.arange(max(0, n - ring_rows), n, dtype=torch.int64)
             src.append(offs[b] - offs[0] + r)
             dst.append(b * ring_rows + r % ring_rows)
-        src = torch.cat(src).to(dev)
-        dst = torch.cat(dst).to(dev)
+        src = torch.cat(src).to(dev) if src else None
+        dst = torch.cat(dst).to(dev) if dst else None
         row0 = offs[0]
 
         def to_ring(x):
@@ -136,9 +136,10 @@ class _Lane:
 
         self.ckv_copies = [to_pool(c) for c in self.ckv_copies]
         self.ckv = self.ckv_copies[0]
-        self.kv, self.z = to_ring(self.kv), to_ring(self.z)
-        if getattr(self, "kv_b", None) is not None:
-            self.kv_b, self.z_b = to_ring(self.kv_b), to_ring(self.z_b)
+        if ring_rows > 0:  # ring_rows = 0 keeps the raw rows packed as kv_off says
+            self.kv, self.z = to_ring(self.kv), to_ring(self.z)
+            if getattr(self, "kv_b", None) is not None:
+                self.kv_b, self.z_b = to_ring(self.kv_b), to_ring(self.z_b)
         if hasattr(self, "kI_copies"):
             self.kI_copies = [to_pool(c) for c in self.kI_copies]
             self.kI = self.kI_copies[0]
@@ -146,7 +147,8 @@ class _Lane:
                 self.k_scale_copies = [to_pool(c) for c in self.k_scale_copies]
                 self.k_scale = self.k_scale_copies[0]
         # row offsets now only count rows: rebase the raw-row prefix sums at 0
-        self.kv_off = self.kv_off - self.kv_off[0]
+        if ring_rows > 0:
+            self.kv_off = self.kv_off - self.kv_off[0]
         self.paged = PagedCache(table.to(dev), eb, pool_rows, ring_rows)
         self.pool_rows = pool_rows
 

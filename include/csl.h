@@ -74,8 +74,15 @@ typedef enum {
  *     covers lcm(m, m') raw tokens: 32 for CSA's m = 4 beside HCA's m' = 128, 1 for HCA);
  *   - with ring_rows > 0, raw row r of sequence b (kv, z, and for overlapped compression
  *     kv_b, z_b) sits at ring row b * ring_rows + r % ring_rows: the state cache keeps the
- *     newest ring_rows rows of each sequence, which must hold every raw row a call reads
- *     (the window, the chunks being compressed);
+ *     newest ring_rows rows of each sequence, which must hold every raw row a call reads.
+ *     The host checks ring_rows >= max(n_win + T - 1, (max_new_entries + 1) * m - 1), with
+ *     (max_new_entries + 2) * m - 1 for overlapped compression (each term only where the
+ *     call has a window or compresses), and returns CSL_ERR_INVALID otherwise. That covers
+ *     the windows of T query rows at the end of the context and the newest entries'
+ *     chunks; queries elsewhere in the context, or compressing from entry 0 (first_entry
+ *     NULL), need a ring that holds those rows too (a precondition);
+ *   - with ring_rows = 0 the raw rows stay packed as kv_off says (only the compressed
+ *     entries are paged);
  *   - kv_off and ent_off still give each sequence's raw-row and entry counts (as prefix
  *     sums); they no longer place rows.
  * block_table entries of the blocks a sequence uses, and the ring's rows, are preconditions.
@@ -248,7 +255,8 @@ int csl_indexer_topk(const void* q_idx, const float* w, const void* k_idx, int k
  *
  *   q bf16 [B, T, H, D]; ckv bf16 [E_tot, D]; idx int32 [B, T, k]; kv bf16 [N_tot, D]
  *   out fp32 [B, T, H, D]; lse fp32 [B, T, H] (nullable)
- *   D == 128; H a multiple of 16, <= 128; k >= 0; n_win >= 0.
+ *   D == 128; H a multiple of 16, <= 128; k >= 0; n_win >= 0; scale finite and > 0
+ *   (CSL_ERR_INVALID otherwise).
  *   ws: at least csl_attn_workspace_bytes(B, T, H, D, k + n_win) bytes (contents free).
  * extras (nullable; NULL means none of them) adds per-query parts of the core attention:
  *   sink       device fp32 [H] or NULL: head h's sink logit z'_h ([P1] section 7). exp(z'_h)

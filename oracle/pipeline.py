@@ -144,14 +144,3 @@ def csa_step(kv, z, q, qI, w, keys_f64, kv_off, q_pos, m: int, k: int, W: int, s
     idx = topk_lane(scores, k)
     o, lse = sparse_attn_lane(q, ckv, idx, kv, kv_off, ent, q_pos, W, scale)
     return ckv, scores, idx, o, lse
-
-
-def hca_step(kv, z, q, kv_off, q_pos, m: int, W: int, scale: float):
-    """Whole HCA lane: compress (bf16 cache format) then dense attention."""
-    ckv = csa.to_bf16_f64(compress_lane(kv, z, kv_off, m))
-    ent = [0]
-    kv_off_l = [int(x) for x in kv_off]
-    for b in range(len(kv_off_l) - 1):
-        ent.append(ent[-1] + (kv_off_l[b + 1] - kv_off_l[b]) // m)
-    o, lse = hca_attn_lane(q, ckv, kv, kv_off, ent, q_pos, m, W, scale)
-    return ckv, o, lse

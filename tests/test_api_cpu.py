@@ -181,6 +181,25 @@ def test_attention_validation_and_workspace(lib):
                        (PC(FAKE, 0, 32, 1 << 20, 128), 1)):         # no blocks
         bad = list(base); bad[19] = P(ctypes.addressof(pc))
         assert f(*bad) == status, _err(lib)
+    # the ring must hold the windows of all T query rows: n_win + T - 1 rows
+    for T, ring, ok in ((1, 128, True), (2, 128, False), (129, 256, True), (130, 256, False)):
+        pc = PC(FAKE, 4, 32, 1 << 20, ring)
+        args = list(base); args[10] = T; args[17] = 1 << 30; args[19] = P(ctypes.addressof(pc))
+        st = f(*args)
+        if ok:
+            assert st != 1, _err(lib)       # validation passes (without a GPU the launch itself fails)
+        else:
+            assert st == 1 and "ring_rows" in _err(lib), (T, ring, _err(lib))
+    # ring_rows = 0: the raw rows stay packed, so no ring size applies
+    pc = PC(FAKE, 4, 32, 1 << 20, 0)
+    args = list(base); args[19] = P(ctypes.addressof(pc))
+    assert f(*args) != 1 and "ring" not in _err(lib)
+    # scale must be positive: the softmax takes the running maximum of scaled logits
+    for sc in (0.0, -0.088, float("inf")):
+        bad = list(base); bad[13] = sc
+        assert f(*bad) == 1 and "scale" in _err(lib)
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 128, 128, 8, 1, 64, 128, 0.0, 1024, FAKE, None, FAKE, 1 << 30, None,
+             None, None) == 1 and "scale" in _err(lib)
 
 
 def test_step_validation(lib):
@@ -218,6 +237,24 @@ def test_step_validation(lib):
     assert call(scores=None, idx=None) == 1
     assert call(scores=None, ld=0, B=0) == 0    # ld is ignored without scores
     assert _err(lib) == ""
+    # a paged cache: the ring holds the union of the window and the newest compressed chunks
+    PC = csl._PagedCache
+    def paged_call(ring, **over):
+        pc = PC(FAKE, 8, 32, 1 << 20, ring)
+        return call(paged=P(ctypes.addressof(pc)), B=0, **over)
+    assert paged_call(128) == 0                          # window 128 >= (1 + 1) * 4 - 1 = 7
+    assert paged_call(0) == 0                            # raw rows packed: no ring to size
+    assert paged_call(64) == 1 and "ring_rows" in _err(lib)        # the window does not fit
+    assert paged_call(128, max_new_entries=31) == 0      # (31 + 1) * 4 - 1 = 127 <= 128
+    assert paged_call(128, max_new_entries=32) == 1      # (32 + 1) * 4 - 1 = 131 > 128
+    assert paged_call(256, max_new_entries=32) == 0
+    assert paged_call(128, n_win=0, m=128) == 1          # one HCA chunk plus its tail: 2 * 128 - 1 = 255
+    assert paged_call(256, n_win=0, m=128) == 0
+    assert paged_call(256, T=129) == 0                   # windows of 129 rows: 128 + 129 - 1 = 256
+    assert paged_call(256, T=130) == 1                   # 130 rows: 257 > 256
+    # overlapped compression also reads the series-b block before each entry: one more chunk
+    assert paged_call(128, kv_b=FAKE, max_new_entries=30) == 0     # (30 + 2) * 4 - 1 = 127
+    assert paged_call(128, kv_b=FAKE, max_new_entries=31) == 1     # (31 + 2) * 4 - 1 = 131
 
 
 def test_indexer_topk_validation(lib):

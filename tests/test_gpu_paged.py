@@ -96,6 +96,23 @@ def test_paged_csa_step_equals_packed(lengths, m, k, H, HI, fused, overlap, fp4)
     assert_rows_close(f64(go["scores"][0, 0, :E0]), ref_s, what="paged scores vs oracle")
 
 
+@pytest.mark.parametrize("kind", ["csa", "hca"])
+def test_paged_entries_with_packed_raw_rows_equal_packed(kind):
+    """ring_rows = 0: only the compressed entries (and indexer keys) move into the block pool,
+    the raw rows stay packed as kv_off says; the step equals the packed one bit for bit."""
+    if kind == "csa":
+        lane = W.Lane("csa", (300000, 70000, 5), (300000, 70000, 5), T=1, H=64, m=4, k=1024, HI=8)
+    else:
+        lane = W.Lane("hca", (131072, 9000, 100), (131072, 9000, 100), T=1, H=64, m=128)
+    print(f"paged entries, packed raw rows: {kind}", flush=True)
+    _, ((pk, po, pn), (gk, go, gn)) = _run_both(lane, 43, True, ring_rows=0)
+    assert gk.paged.ring_rows == 0
+    assert torch.equal(pn, gn), "newest compressed entries differ"
+    if kind == "csa":
+        assert torch.equal(po["idx"], go["idx"]), "selected ids differ"
+    assert torch.equal(po["out"], go["out"]) and torch.equal(po["lse"], go["lse"]), "attention differs"
+
+
 def test_paged_csa_step_with_sink_and_rope_equals_packed():
     lane = W.Lane("csa", (40000, 3000), (40000, 3000), T=1, H=64, m=4, k=256, HI=8)
     _, ((pk, po, pn), (gk, go, gn)) = _run_both(lane, 77, True, extras=True)

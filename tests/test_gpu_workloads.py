@@ -97,18 +97,15 @@ def _check_csa_row(cl, inp, li, b, t, keys_f64, entries_fn=None, extras=None):
     assert_rows_close(got_s, ref_s, what=f"scores b={b} t={t}")
     got_idx = cl.idx[b, t].cpu().numpy()
     same = topk_band_check(got_idx, ref_s, lane.k, what=f"top-k b={b} t={t}")
-    ref_sel = csa.topk(ref_s, lane.k)
-    ref_sel = ref_sel[ref_sel >= 0]
-    ro, rl = _oracle_attention(inp.q[li.q_slice][b, t], inp.kv, inp.z, lane, b, p, ref_sel, cl.scale, entries_fn,
+    # the band check has shown the GPU's selection to be a valid top-k of the oracle's
+    # scores; the attention is then held to the oracle's attention over that same selection
+    sel = got_idx[got_idx >= 0]
+    ro, rl = _oracle_attention(inp.q[li.q_slice][b, t], inp.kv, inp.z, lane, b, p, sel, cl.scale, entries_fn,
                                extras)
+    tag = "" if same else " (band swap: oracle over the GPU's selection)"
     go, gl = f64(cl.out[b, t]), f64(cl.lse[b, t])
-    if same:
-        assert_attn_close(go, ro, f"out b={b} t={t}")
-        assert_attn_close(gl, rl, f"lse b={b} t={t}")
-    else:
-        # a swap inside the top-k boundary band moves at most a few 1/(k+W) weights
-        swapped = len(set(got_idx[got_idx >= 0].tolist()) ^ set(ref_sel.tolist())) // 2
-        assert_attn_close(go, ro, f"out b={b} t={t} (band swap)", atol=2e-3 + swapped * 8.0 / (len(ref_sel) + 1))
+    assert_attn_close(go, ro, f"out b={b} t={t}{tag}")
+    assert_attn_close(gl, rl, f"lse b={b} t={t}{tag}")
 
 
 def _csa_keys(li):
@@ -257,13 +254,18 @@ def test_csa_prefill_8k_on_128k(lanes_mod):
     nv = np.array([csa.n_visible(lane.q_pos[0] + t, lane.m, lane.entries[0]) for t in range(lane.T)])
     assert np.all(idx >= 0) and np.all(idx < nv[:, None])
     assert np.all(np.diff(idx, axis=1) > 0)
+    # every row: finite, non-negative visible scores (w >= 0) and finite outputs
     sc = cl.scores[0]
-    for t in (0, lane.T - 1):
-        assert bool(torch.isfinite(sc[t, :nv[t]]).all()) and bool((sc[t, :nv[t]] >= 0).all())
-    assert bool(torch.isfinite(cl.out).all())
+    col = torch.arange(sc.shape[1], device=sc.device)[None, :]
+    vis = col < torch.from_numpy(nv).to(sc.device)[:, None]
+    assert bool(torch.isfinite(sc[vis]).all()) and bool((sc[vis] >= 0).all())
+    assert bool(torch.isfinite(cl.out).all()) and bool(torch.isfinite(cl.lse).all())
     keys = _csa_keys(li)
-    g = np.random.default_rng(3)
-    rows = sorted(set([0, 1, 2, 3, 4095, lane.T - 2, lane.T - 1] + g.integers(0, lane.T, 25).tolist()))
+    # 512 rows spread evenly over the chunk (first and last included) plus the rows around
+    # the 4-row compression blocks at the start, against the oracle one by one
+    even = np.linspace(0, lane.T - 1, 512).round().astype(int).tolist()
+    rows = sorted(set(even + [0, 1, 2, 3, 4, 5, lane.T - 2, lane.T - 1]))
+    assert len(rows) >= 512 and rows[0] == 0 and rows[-1] == lane.T - 1
     for t in rows:
         _check_csa_row(cl, inp, li, 0, t, keys)
 
