@@ -14,7 +14,7 @@ import torch
 
 __all__ = [
     "compress_kv", "compress_kv_overlap", "indexer_scores", "indexer_topk", "indexer_topk_max_k", "topk_select",
-    "sparse_attn_decode", "hca_attn_decode", "csa_decode_step",
+    "sparse_attn_decode", "hca_attn_decode", "csa_decode_step", "csa_decode_step_static",
     "topk_workspace_bytes", "attn_workspace_bytes", "PagedCache", "version", "LIB_PATH",
     "EXPORTS", "CslError",
 ]
@@ -26,7 +26,7 @@ EXPORTS = [
     "csl_last_error", "csl_version", "csl_compress_kv", "csl_compress_kv_overlap", "csl_indexer_scores",
     "csl_indexer_topk_max_k", "csl_indexer_topk",
     "csl_topk_workspace_bytes", "csl_topk_select", "csl_attn_workspace_bytes",
-    "csl_sparse_attn_decode", "csl_hca_attn_decode", "csl_csa_decode_step",
+    "csl_sparse_attn_decode", "csl_hca_attn_decode", "csl_csa_decode_step", "csl_csa_decode_step_static",
 ]
 
 _P, _I, _L, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -88,6 +88,7 @@ def _load() -> ctypes.CDLL:
         "csl_hca_attn_decode": (I, [P, P, P, P, P, P, I, I, I, I, I, I, F, L, P, P, P, S,
                                     ctypes.POINTER(_AttnExtras), P, P]),
         "csl_csa_decode_step": (I, [ctypes.POINTER(_CsaStep), P]),
+        "csl_csa_decode_step_static": (I, [ctypes.POINTER(_CsaStep), P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -328,7 +329,7 @@ def csa_decode_step(kv, z, kv_off, ent_off, first_entry, max_new_entries: int, c
                     k: int, idx, q, n_win: int, out, q_pos, m: int, lse=None, scale: float | None = None,
                     k_scale=None, scale_off=None, scale_group: int = 64, max_entries: int | None = None,
                     attn_ws=None, kv_b=None, z_b=None, sink=None, rope_dims: int = 0, rope_base: float = 10000.0,
-                    k_format=None, paged=None, stream=None):
+                    k_format=None, paged=None, stream=None, static_scratch: bool = False):
     """One whole CSA step (compress_kv of the newest entries into ckv, or compress_kv_overlap
     when series b ``kv_b``/``z_b`` is given, indexer_scores with candidate lists, topk_select,
     sparse_attn_decode) in one C call; with ``scores`` None the selection comes from the
@@ -343,7 +344,10 @@ def csa_decode_step(kv, z, kv_off, ent_off, first_entry, max_new_entries: int, c
         max_entries = ld
     if scale is None:
         scale = D ** -0.5
-    attn_ws, awb = _attn_ws(attn_ws, B, T, H, D, k + n_win, q.device)
+    if static_scratch:  # the library's own scratch array replaces both workspaces
+        attn_ws, awb, topk_ws = None, 0, None
+    else:
+        attn_ws, awb = _attn_ws(attn_ws, B, T, H, D, k + n_win, q.device)
     pstruct = None if paged is None else paged._struct()  # kept alive across the call
     s = _CsaStep(
         kv=_ptr(kv, "kv", _BF16), z=_ptr(z, "z", _BF16), kv_off=_ptr(kv_off, "kv_off", _I64),
@@ -360,5 +364,17 @@ def csa_decode_step(kv, z, kv_off, ent_off, first_entry, max_new_entries: int, c
         sink=_ptr(sink, "sink", _F32), rope_dims=int(rope_dims), rope_base=float(rope_base),
         paged=None if paged is None else ctypes.addressof(pstruct),
         q_pos=_ptr(q_pos, "q_pos", _I64), m=int(m), B=B, T=T, max_entries=int(max_entries))
-    _check(_lib.csl_csa_decode_step(ctypes.byref(s), _stream(stream)))
+    fn = _lib.csl_csa_decode_step_static if static_scratch else _lib.csl_csa_decode_step
+    _check(fn(ctypes.byref(s), _stream(stream)))
     return out
+
+
+def csa_decode_step_static(kv, z, kv_off, ent_off, first_entry, max_new_entries: int, ckv, qI, w, kI, scores,
+                           k: int, idx, q, n_win: int, out, q_pos, m: int, **kw):
+    """csa_decode_step without caller workspaces: csl_csa_decode_step_static takes them from
+    the library's per-device scratch array (no device allocation anywhere in the call; calls
+    overlapping on one device race); see csl.h."""
+    kw.pop("topk_ws", None)
+    kw.pop("attn_ws", None)
+    return csa_decode_step(kv, z, kv_off, ent_off, first_entry, max_new_entries, ckv, qI, w, kI, scores, None, k,
+                           idx, q, n_win, out, q_pos, m, static_scratch=True, **kw)

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/csl.h"
@@ -501,3 +502,65 @@ int csl_csa_decode_step(const csl_csa_step* s, void* stream) {
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------------------------
+// The step without allocation: its two workspaces (the top-k candidate lists and the attention
+// split partials) come from one file-scope device array instead of the caller's buffers. Every
+// GPU holds its own copy of the array; its address on each device is looked up once (with that
+// device current) and kept. Calls on one device share the array, so calls that overlap in time
+// on one device race.
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[CSL_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// the scratch array's device address on the current device (looked up on first use)
+int current_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "csa_decode_step_static: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(CSL_ERR_UNSUPPORTED, "csa_decode_step_static: device %d beyond the %d supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "csa_decode_step_static: hipGetSymbolAddress(scratch)");
+    if (!p) return fail(CSL_ERR_HIP, "csa_decode_step_static: no device address for the scratch array");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CSL_OK;
+}
+
+}  // namespace
+
+extern "C" int csl_csa_decode_step_static(const csl_csa_step* s, void* stream) {
+  if (!s) return fail(CSL_ERR_INVALID, "csa_decode_step_static: null argument");
+  // the workspaces this step needs, as csl_csa_decode_step sizes them: candidate lists only
+  // with a score buffer, split partials for the attention
+  const bool scored = s->scores != nullptr;
+  const size_t need_topk =
+      (scored && s->B > 0 && s->T > 0) ? csl_topk_workspace_bytes(s->B, s->T, s->max_entries, s->k) : 0;
+  const size_t need_attn =
+      (s->B > 0 && s->T > 0 && s->k >= 0 && s->n_win >= 0)
+          ? csl_attn_workspace_bytes(s->B, s->T, s->H, s->D, (int64_t)s->k + s->n_win)
+          : 0;
+  const size_t off_attn = (need_topk + 255) & ~(size_t)255;
+  if (off_attn + need_attn > (size_t)CSL_STATIC_SCRATCH_BYTES)
+    return fail(CSL_ERR_WORKSPACE,
+                "csa_decode_step_static: the step needs %zu bytes of workspace, beyond the %zu-byte static scratch",
+                off_attn + need_attn, (size_t)CSL_STATIC_SCRATCH_BYTES);
+  void* base = nullptr;
+  const int st = current_scratch(&base);
+  if (st != CSL_OK) return st;
+  csl_csa_step t = *s;
+  t.topk_ws = need_topk ? base : nullptr;
+  t.topk_ws_bytes = need_topk;
+  t.attn_ws = need_attn ? static_cast<unsigned char*>(base) + off_attn : nullptr;
+  t.attn_ws_bytes = need_attn;
+  return csl_csa_decode_step(&t, stream);
+}

@@ -35,8 +35,9 @@
  *     except that selected ids outside [0, E_b) are treated as padding.
  *   - Every call returns a csl_status. csl_last_error() returns a thread-local message
  *     describing the last failure on the calling thread.
- *   - The library holds no global state; calls on different streams may run concurrently
- *     as long as they do not share output or workspace buffers.
+ *   - The library holds no global state (except the per-device scratch array of
+ *     csl_csa_decode_step_static); calls on different streams may run concurrently as long
+ *     as they do not share output or workspace buffers.
  */
 #ifndef CSL_H
 #define CSL_H
@@ -375,6 +376,25 @@ typedef struct csl_csa_step {
 } csl_csa_step;
 
 int csl_csa_decode_step(const csl_csa_step* s, void* stream);
+
+/*
+ * csa_decode_step_static -- csl_csa_decode_step for callers that cannot allocate device
+ * memory (code under stream or graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same step, outputs and argument rules, but s->topk_ws, s->topk_ws_bytes,
+ * s->attn_ws and s->attn_ws_bytes are ignored. Both workspaces are taken instead from a
+ * device array of CSL_STATIC_SCRATCH_BYTES inside the library, one copy per GPU, held until
+ * the process ends; its address on a device is looked up on the first call made with that
+ * device current. The call allocates and frees nothing.
+ *   - A step whose workspaces (csl_topk_workspace_bytes with a score buffer, 256-byte
+ *     aligned, plus csl_attn_workspace_bytes for k + n_win keys) exceed
+ *     CSL_STATIC_SCRATCH_BYTES returns CSL_ERR_WORKSPACE and enqueues nothing.
+ *   - Every call on one device uses that device's one array: calls whose work overlaps in
+ *     time on one device (other streams, other threads) race and give undefined results.
+ *     Serialise them, or use csl_csa_decode_step with buffers of your own.
+ *   - The array keeps what the last call left in it; no call relies on its contents.
+ */
+#define CSL_STATIC_SCRATCH_BYTES (16u << 20)
+int csl_csa_decode_step_static(const csl_csa_step* s, void* stream);
 
 #ifdef __cplusplus
 }

@@ -257,6 +257,27 @@ def test_step_validation(lib):
     assert paged_call(128, kv_b=FAKE, max_new_entries=31) == 1     # (31 + 2) * 4 - 1 = 131
 
 
+def test_static_step_rejects_workspaces_beyond_its_scratch(lib):
+    """csl_csa_decode_step_static sizes the step's workspaces on the host and refuses, before
+    touching a device, a step that needs more than its static scratch array."""
+    import compressed_sparse_long_amd as csl
+    f = lib.csl_csa_decode_step_static
+    f.argtypes = [ctypes.POINTER(csl._CsaStep), P]
+    f.restype = ctypes.c_int
+    assert f(None, None) == 1
+    m = re.search(r"#define CSL_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    limit = int(m.group(1)) << int(m.group(2))
+    base = dict(kv=FAKE, kv_off=FAKE, ent_off=FAKE, max_new_entries=1, ckv=FAKE, q_idx=FAKE, w=FAKE, k_idx=FAKE,
+                k_dtype=0, scale_group=64, HI=8, CI=64, scores=FAKE, ld=262144, k=1024, idx=FAKE, q=FAKE, H=64,
+                D=128, n_win=128, scale=0.088, out=FAKE, q_pos=FAKE, m=4, B=300, T=1, max_entries=262144)
+    # 300 rows of 262144 entries: 300 candidate-list workspaces of ~66 KiB, more than the array
+    need = lib.csl_topk_workspace_bytes
+    need.restype, need.argtypes = ctypes.c_size_t, [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int]
+    assert need(300, 1, 262144, 1024) > limit
+    s = csl._CsaStep(**base)
+    assert f(ctypes.byref(s), None) == 3 and "static scratch" in _err(lib)
+
+
 def test_indexer_topk_validation(lib):
     f = lib.csl_indexer_topk
     I, L = ctypes.c_int, ctypes.c_int64
