@@ -257,7 +257,7 @@ def topk_select(scores, ent_off, q_pos, m: int, k: int, idx, ws=None, max_entrie
         max_entries = ld
     need = topk_workspace_bytes(B, T, max_entries, k)
     if ws is None and need > 0:
-        ws = torch.empty(need, dtype=torch.uint8, device=scores.device)
+        ws = torch.zeros(need, dtype=torch.uint8, device=scores.device)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(_lib.csl_topk_select(
         _ptr(scores, "scores", _F32), ld, _ptr(ent_off, "ent_off", _I64), _ptr(q_pos, "q_pos", _I64), int(m), B, T,
@@ -273,7 +273,7 @@ def attn_workspace_bytes(B: int, T: int, H: int, D: int, max_keys: int) -> int:
 def _attn_ws(ws, B, T, H, D, max_keys, device):
     need = attn_workspace_bytes(B, T, H, D, max_keys)
     if ws is None and need > 0:
-        ws = torch.empty(need, dtype=torch.uint8, device=device)
+        ws = torch.zeros(need, dtype=torch.uint8, device=device)
     return ws, (0 if ws is None else ws.numel() * ws.element_size())
 
 

@@ -284,6 +284,21 @@ __device__ __forceinline__ void attn_write(const f32x4 (&oacc)[8], float m_run, 
   }
 }
 
+// Merge of one wave's online-softmax state (o, m, l; base-2 logits) into another's: the two
+// states cover disjoint key sets of the same 16 heads.
+__device__ __forceinline__ void merge_state(f32x4 (&o)[8], float& m, float& l, const float (&o2)[32], float m2,
+                                            float l2) {
+  const float M = fmaxf(m, m2);
+  if (M == -INFINITY) return;  // neither side saw a key
+  const float f1 = __builtin_amdgcn_exp2f(m - M), f2 = __builtin_amdgcn_exp2f(m2 - M);
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[db][i] = o[db][i] * f1 + o2[4 * db + i] * f2;
+  l = l * f1 + l2 * f2;
+  m = M;
+}
+
 // Attention over one query row's key range. Each thread gathers whole 64-byte pieces of rows:
 // pair p = j * NT + tid takes row p / 4, units 4q + p % 4 (q = 0..3), so 4 lanes read 64
 // contiguous bytes per load and a thread resolves one row address per row it gathers.
@@ -292,8 +307,11 @@ __device__ __forceinline__ void attn_write(const f32x4 (&oacc)[8], float m_run, 
 // for each tile's rows in turn. MODE 0: the workgroup walks many tiles and loads the next
 // tile's rows (and the selected ids of the one after) into registers while the current tile
 // is multiplied.
-template <int NHG, bool SPARSE, int MODE, bool ROPE, bool PAGED>
-__global__ __launch_bounds__(NHG * 64) void attn_kernel(
+// NSUB > 1 (with MODE 1): the workgroup holds NSUB tiles at once and its waves are NSUB groups
+// of NHG, group s multiplying tile s, so the tiles' latencies overlap; the groups' states are
+// then merged through LDS into group 0, which writes the result.
+template <int NHG, int NSUB, bool SPARSE, int MODE, bool ROPE, bool PAGED>
+__global__ __launch_bounds__(NHG * NSUB * 64) void attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ ckv, const int32_t* __restrict__ idx, int k,
     const uint16_t* __restrict__ kv, const int64_t* __restrict__ kv_off, const int64_t* __restrict__ ent_off,
     const int64_t* __restrict__ q_pos, int m, int n_win, int T, float scale_log2, int64_t max_entries,
@@ -301,16 +319,24 @@ __global__ __launch_bounds__(NHG * 64) void attn_kernel(
     float* __restrict__ ws_lse, const float* __restrict__ sink, double rope_theta1,
     float2* __restrict__ ws_rope, AttnLayout lay) {
   constexpr bool MULTI = MODE == 0;
-  constexpr int NTL = MULTI ? 1 : MODE;    // tiles held in LDS at once
-  constexpr int NT = NHG * 64;
+  static_assert(NSUB == 1 || MODE == 1, "parallel tiles take single-round splits of one tile each");
+  constexpr int NTL = MULTI ? 1 : (NSUB > 1 ? NSUB : MODE);  // tiles held in LDS at once
+  constexpr int NT = NHG * NSUB * 64;
   constexpr int H = NHG * 16;
   constexpr int NV = kKT * NTL;            // rows gathered per round
   constexpr int NP = 4 * NV;               // gather pairs per round
   constexpr int RPT = (NP + NT - 1) / NT;  // pairs (rows) per thread
   static_assert(RPT <= 32, "one mask bit per gathered row");
-  __shared__ __align__(16) uint8_t Ks[NTL][kKT * kD * 2];
+  constexpr size_t kTileBytes = (size_t)kKT * kD * 2;
+  constexpr size_t kTilesBytes = NTL * kTileBytes;
+  // the tiles' LDS, shared at the end with the states of wave groups 1..NSUB-1 for the merge:
+  // per wave 32 output values, m and l, for each of 64 lanes
+  constexpr size_t kMergeBytes = (size_t)(NSUB - 1) * NHG * 34 * kWave * 4;
+  constexpr size_t kKsBytes = kTilesBytes > kMergeBytes ? kTilesBytes : kMergeBytes;
+  __shared__ __align__(16) uint8_t Ks_raw[kKsBytes];
+  uint8_t (*Ks)[kTileBytes] = reinterpret_cast<uint8_t (*)[kTileBytes]>(Ks_raw);
   __shared__ __align__(16) uint8_t vld[NTL][kKT];  // slot v of a tile holds a key
-  __shared__ float2 rcs_all[ROPE ? NHG : 1][kRope / 2];  // RoPE (cos, sin) per pair at the row's position, per wave
+  __shared__ float2 rcs_all[ROPE ? NHG * NSUB : 1][kRope / 2];  // RoPE (cos, sin) per pair at the row's position, per wave
 
   const int split = blockIdx.x;
   const int row = blockIdx.y;
@@ -321,6 +347,8 @@ __global__ __launch_bounds__(NHG * 64) void attn_kernel(
   const int lane = tid % kWave;
   const int g = lane / 16;
   const int c = lane % 16;
+  const int hg = wave % NHG;   // head group: heads 16 hg .. 16 hg + 15
+  const int sub = wave / NHG;  // tile of the round this wave multiplies (NSUB > 1)
 
   const int64_t k_lo = (int64_t)split * keys_per_split;
   // selected ids do not depend on the row geometry: the first ones load right away, from
@@ -392,7 +420,7 @@ __global__ __launch_bounds__(NHG * 64) void attn_kernel(
   };
 
   // queries of this wave's 16 heads as MFMA B operands (d-slots 8g..8g+7 of each 32-chunk)
-  const int head = wave * 16 + c;
+  const int head = hg * 16 + c;
   bf16x8 qb[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
@@ -475,12 +503,42 @@ __global__ __launch_bounds__(NHG * 64) void attn_kernel(
       issue(t0 + kKT, ids_nxt);
       if (SPARSE && t0 + 2 * kKT < k_hi) load_ids(t0 + 2 * kKT, ids_nxt);
     }
+    if (NSUB > 1) {
+      if (sub == 0 || t0 + sub * kKT < k_hi)
+        tile_compute<ROPE>(Ks[sub], vld[sub], qb, ql, scale_log2, oacc, m_run, l_run, c, g);
+    } else {
 #pragma unroll
-    for (int tl = 0; tl < NTL; ++tl)
-      if (tl == 0 || t0 + tl * kKT < k_hi)
-        tile_compute<ROPE>(Ks[tl], vld[tl], qb, ql, scale_log2, oacc, m_run, l_run, c, g);
+      for (int tl = 0; tl < NTL; ++tl)
+        if (tl == 0 || t0 + tl * kKT < k_hi)
+          tile_compute<ROPE>(Ks[tl], vld[tl], qb, ql, scale_log2, oacc, m_run, l_run, c, g);
+    }
     if (!MULTI) break;  // the launch gives single-round kernels at most NTL tiles
     __syncthreads();    // the next tile overwrites Ks / vld
+  }
+  if (NSUB > 1) {
+    // groups 1..NSUB-1 post their states (lane-major, so each LDS access is one contiguous row
+    // of 64 words) over the tiles, which every wave has finished reading; group 0 merges them
+    float* ms = reinterpret_cast<float*>(Ks_raw);
+    __syncthreads();
+    if (sub > 0) {
+      float* dst = ms + (size_t)((sub - 1) * NHG + hg) * 34 * kWave + lane;
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(4 * db + i) * kWave] = oacc[db][i];
+      dst[32 * kWave] = m_run;
+      dst[33 * kWave] = l_run;
+    }
+    __syncthreads();
+    if (sub > 0) return;
+#pragma unroll
+    for (int s2 = 1; s2 < NSUB; ++s2) {
+      const float* src = ms + (size_t)((s2 - 1) * NHG + hg) * 34 * kWave + lane;
+      float o2[32];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) o2[i] = src[i * kWave];
+      merge_state(oacc, m_run, l_run, o2, src[32 * kWave], src[33 * kWave]);
+    }
   }
   attn_write<ROPE>(oacc, m_run, l_run, row, nrows, split, H, head, g, out, lse_out, ws_o, ws_lse, sink, rcs);
 }
@@ -559,23 +617,39 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
 template <bool SPARSE, bool ROPE, bool PAGED>
 hipError_t launch_nhg(int H, dim3 grid, hipStream_t st, const uint16_t* q, const uint16_t* ckv, const int32_t* idx,
                       int k, const uint16_t* kv, const int64_t* kv_off, const int64_t* ent_off, const int64_t* q_pos,
-                      int m, int n_win, int T, float scale_log2, int64_t max_entries, int kps, float* out,
+                      int m, int n_win, int T, float scale_log2, int64_t max_entries, const AttnPlan& p, float* out,
                       float* lse, float* ws_o, float* ws_lse, float2* ws_rope, const AttnExtras& ex,
                       const AttnLayout& lay) {
+  const int kps = p.keys_per_split;
   const int tiles = kps / kKT;  // 1 or 2: gathered in one round; more: the prefetching loop
-#define CSL_ATTN_LAUNCH(NHG, MODE)                                                                              \
-  attn_kernel<NHG, SPARSE, MODE, ROPE, PAGED><<<grid, NHG * 64, 0, st>>>(q, ckv, idx, k, kv, kv_off, ent_off, q_pos, m, \
-                                                                  n_win, T, scale_log2, max_entries, kps, out, lse, \
-                                                                  ws_o, ws_lse, ex.sink, ex.rope_theta1, \
-                                                                  ws_rope, lay)
+#define CSL_ATTN_LAUNCH(NHG, NSUB, MODE)                                                                       \
+  attn_kernel<NHG, NSUB, SPARSE, MODE, ROPE, PAGED><<<grid, NHG * NSUB * 64, 0, st>>>(                        \
+      q, ckv, idx, k, kv, kv_off, ent_off, q_pos, m, n_win, T, scale_log2, max_entries, kps, out, lse, ws_o,  \
+      ws_lse, ex.sink, ex.rope_theta1, ws_rope, lay)
+  if (p.nsub > 1) {  // a row's whole key list in one workgroup, its tiles multiplied at once
+#define CSL_ATTN_PAR(NHG, NSUB)                     \
+  case NHG:                                        \
+    if (p.nsub != NSUB) return hipErrorInvalidValue; \
+    CSL_ATTN_LAUNCH(NHG, NSUB, 1);                 \
+    break;
+    switch (H / 16) {
+      CSL_ATTN_PAR(1, 4)
+      CSL_ATTN_PAR(2, 4)
+      CSL_ATTN_PAR(4, 4)
+      CSL_ATTN_PAR(8, 2)
+      default: return hipErrorInvalidValue;
+    }
+#undef CSL_ATTN_PAR
+    return hipGetLastError();
+  }
 #define CSL_ATTN_CASE(NHG)                 \
   case NHG:                                \
     if (tiles == 1)                        \
-      CSL_ATTN_LAUNCH(NHG, 1);             \
+      CSL_ATTN_LAUNCH(NHG, 1, 1);          \
     else if (tiles == 2)                   \
-      CSL_ATTN_LAUNCH(NHG, 2);             \
+      CSL_ATTN_LAUNCH(NHG, 1, 2);          \
     else                                   \
-      CSL_ATTN_LAUNCH(NHG, 0);             \
+      CSL_ATTN_LAUNCH(NHG, 1, 0);          \
     break;
   switch (H / 16) {
     CSL_ATTN_CASE(1)
@@ -595,10 +669,31 @@ hipError_t launch_nhg(int H, dim3 grid, hipStream_t st, const uint16_t* q, const
 
 }  // namespace
 
-AttnPlan attn_plan(int B, int T, int64_t max_keys) {
+// tiles multiplied at once by a decode workgroup of H heads: 4 (2 at 128 heads, whose workgroup
+// already has 8 waves per tile) for head counts of 16, 32, 64 or 128, else 1
+static int attn_nsub(int H) {
+  switch (H) {
+    case 16: case 32: case 64: return 4;
+    case 128: return 2;
+    default: return 1;
+  }
+}
+
+AttnPlan attn_plan(int B, int T, int H, int64_t max_keys) {
   AttnPlan p;
   const int64_t rows = (int64_t)B * T;
   const int64_t tiles = max_keys > 0 ? (max_keys + kKT - 1) / kKT : 1;
+  // a short key list (at most nsub tiles) in one workgroup that multiplies its tiles at once:
+  // no partials and no merge. Longer lists use several workgroups: each matrix core then
+  // multiplies fewer tiles than it would for a wave group of its own per tile
+  p.nsub = 1;
+  const int nsub = attn_nsub(H);
+  if (rows < 512 && nsub > 1 && tiles > 1 && tiles <= nsub) {
+    p.nsub = nsub;
+    p.keys_per_split = nsub * kKT;
+    p.nsplit = 1;
+    return p;
+  }
   // aim for about two workgroups per CU, with at least two tiles per split when the list has
   // them: a workgroup walking several tiles prefetches them, while every extra split adds a
   // partial (o, lse) to write and merge
@@ -612,7 +707,7 @@ AttnPlan attn_plan(int B, int T, int64_t max_keys) {
 }
 
 size_t attn_workspace_bytes(int B, int T, int H, int64_t max_keys) {
-  const AttnPlan p = attn_plan(B, T, max_keys);
+  const AttnPlan p = attn_plan(B, T, H, max_keys);
   if (p.nsplit <= 1) return 0;
   // partials (o, lse) of every split, then one RoPE (cos, sin) table per row
   return (size_t)p.nsplit * B * T * H * (kD + 1) * sizeof(float) + (size_t)B * T * (kRope / 2) * sizeof(float2);
@@ -622,7 +717,7 @@ hipError_t launch_attention(bool sparse, const void* q, const void* ckv, const i
                             const int64_t* kv_off, const int64_t* ent_off, const int64_t* q_pos, int m, int n_win,
                             int B, int T, int H, float scale, int64_t max_entries, int64_t max_keys, float* out,
                             float* lse, void* ws, const AttnExtras& ex, hipStream_t st, const PagedView* paged) {
-  const AttnPlan p = attn_plan(B, T, max_keys);
+  const AttnPlan p = attn_plan(B, T, H, max_keys);
   AttnLayout lay;
   if (paged) {
     lay.table = paged->table;
@@ -631,7 +726,9 @@ hipError_t launch_attention(bool sparse, const void* q, const void* ckv, const i
     lay.ring_rows = paged->ring_rows;
   }
   const int rows = B * T;
-  float* ws_o = static_cast<float*>(ws);
+  // the workspace exists only with several splits (attn_workspace_bytes is 0 otherwise): one
+  // split writes its output directly and never touches it
+  float* ws_o = p.nsplit > 1 ? static_cast<float*>(ws) : nullptr;
   float* ws_lse = ws_o ? ws_o + (size_t)p.nsplit * rows * H * kD : nullptr;
   // the rows' RoPE tables follow the partials (8-byte aligned: the partials are whole rows
   // of 16 heads); only the merge reads them
@@ -643,7 +740,7 @@ hipError_t launch_attention(bool sparse, const void* q, const void* ckv, const i
   const uint16_t* k16 = static_cast<const uint16_t*>(kv);
 #define CSL_ATTN_NHG(SP, RP, PG)                                                                                \
   launch_nhg<SP, RP, PG>(H, grid, st, q16, c16, idx, k, k16, kv_off, ent_off, q_pos, m, n_win, T, sl2,         \
-                         max_entries, p.keys_per_split, out, lse, ws_o, ws_lse, ws_rope, ex, lay)
+                         max_entries, p, out, lse, ws_o, ws_lse, ws_rope, ex, lay)
   const bool rope = ex.rope_dims > 0;
   hipError_t e;
   if (paged)

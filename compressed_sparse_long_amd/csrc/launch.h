@@ -74,6 +74,7 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int64_t* ent_off, 
 struct AttnPlan {
   int nsplit;
   int keys_per_split;
+  int nsub;  // tiles one workgroup multiplies at once (its waves in nsub groups)
 };
 // Per-query extras of the core attention: the attention sink (per-head logits added to the
 // softmax denominator) and partial RoPE (the query's last rope_dims dims rotated at its
@@ -83,7 +84,7 @@ struct AttnExtras {
   int rope_dims = 0;            // 0 or a multiple of 32 up to 128
   double rope_theta1 = 1.0;     // base^(-2/rope_dims): pair j turns by p * rope_theta1^j
 };
-AttnPlan attn_plan(int B, int T, int64_t max_keys);
+AttnPlan attn_plan(int B, int T, int H, int64_t max_keys);
 size_t attn_workspace_bytes(int B, int T, int H, int64_t max_keys);
 hipError_t launch_attention(bool sparse, const void* q, const void* ckv, const int32_t* idx, int k, const void* kv,
                             const int64_t* kv_off, const int64_t* ent_off, const int64_t* q_pos, int m, int n_win,

@@ -22,6 +22,7 @@
 #include "device_common.h"
 #include "launch.h"
 #include "topk_common.h"
+#include "topk_finish.h"
 
 namespace csl {
 
@@ -60,45 +61,6 @@ __global__ __launch_bounds__(kSlice) void topk_prepare_kernel(const float* __res
 
 constexpr int kFinNT = 1024;
 constexpr int kFinWaves = kFinNT / kWave;
-
-// One radix step of the finish: over BINS bins (hist in LDS), find the bin holding the
-// need-th largest key counting from the top bin down. res = {bin, count above it, count in
-// it, total}. Contains two workgroup barriers; the caller reads res after it returns.
-template <int BINS>
-__device__ __forceinline__ void fin_threshold(const uint32_t* hist, uint32_t need, uint32_t* wsum, uint32_t* res) {
-  constexpr int PER = BINS / kFinNT;
-  static_assert(PER * kFinNT == BINS, "bins per thread");
-  const int tid = threadIdx.x;
-  uint32_t v[PER];
-  uint32_t local = 0;
-#pragma unroll
-  for (int q = 0; q < PER; ++q) {
-    v[q] = hist[BINS - 1 - (tid * PER + q)];
-    local += v[q];
-  }
-  const uint32_t incl = wave_incl_scan(local);
-  if (lane_id() == kWave - 1) wsum[tid / kWave] = incl;
-  __syncthreads();
-  uint32_t before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < kFinWaves; ++w) {
-    const uint32_t x = wsum[w];
-    before += (w < tid / kWave) ? x : 0u;
-    all += x;
-  }
-  uint32_t excl = before + incl - local;
-#pragma unroll
-  for (int q = 0; q < PER; ++q) {
-    if (excl < need && need <= excl + v[q]) {
-      res[0] = (uint32_t)(BINS - 1 - (tid * PER + q));
-      res[1] = excl;
-      res[2] = v[q];
-    }
-    excl += v[q];
-  }
-  if (tid == 0) res[3] = all;
-  __syncthreads();
-}
 
 // ---------------------------------------------------------------------------------------
 // Short rows: one workgroup per row, keys in registers (element i = j * kFinNT + tid).
@@ -229,7 +191,7 @@ __global__ __launch_bounds__(kFinNT) void topk_row_kernel(const float* __restric
     for (int j = 0; j < ITEMS; ++j)
       if (key[j] && (key[j] >> shift) == prefix) atomicAdd(&hist_b[(key[j] >> sb) & ((1u << wb) - 1u)], 1u);
     __syncthreads();
-    fin_threshold<2048>(hist_b, need, wsum, res);
+    fin_threshold<kFinNT, 2048>(hist_b, need, wsum, res);
     prefix = (prefix << wb) | res[0];
     shift = sb;
     need -= res[1];
@@ -239,7 +201,7 @@ __global__ __launch_bounds__(kFinNT) void topk_row_kernel(const float* __restric
       for (int j = 0; j < ITEMS; ++j)
         if (key[j] && (key[j] >> shift) == prefix) atomicAdd(&hist_c[key[j] & ((1u << shift) - 1u)], 1u);
       __syncthreads();
-      fin_threshold<1024>(hist_c, need, wsum, res);
+      fin_threshold<kFinNT, 1024>(hist_c, need, wsum, res);
       prefix = (prefix << shift) | res[0];
       shift = 0;
       need -= res[1];
@@ -310,351 +272,20 @@ __global__ __launch_bounds__(kFinNT) void topk_row_kernel(const float* __restric
   for (int p = (int)keep + tid; p < k; p += kFinNT) out[p] = -1;
 }
 
-// Exact selection over the whole row from its scores, for rows whose candidate lists cannot
-// prove the selection and rows too dense for them. Passes over the row (from L2):
-//   1. block min and max of the keys;
-//   2. radix select of the keep-th largest key: 11 bits just below the keys' common prefix,
-//      then the rest (usually one more pass);
-//   3. ordered compaction in chunks of 8 * kFinNT ids with one packed block scan of the
-//      (above, tied) counts per chunk, lower ids first among keys tied at the threshold.
-// hist_a / hist_b: LDS [2048]; wsum: LDS [2 * kFinWaves]; res: LDS [4].
-__device__ void finish_full_row(const float* __restrict__ srow, int64_t n, uint32_t keep, int32_t* __restrict__ out,
-                                uint32_t* hist_a, uint32_t* hist_b, uint32_t* wsum, uint32_t* res) {
-  const int tid = threadIdx.x;
-  const int wave = tid / kWave;
-  // visit every key of the row: 16 coalesced loads in flight per thread
-  constexpr int U = 16;
-  auto for_keys = [&](auto&& fn) {
-    for (int64_t c0 = 0; c0 < n; c0 += (int64_t)U * kFinNT) {
-      float v[U];
-#pragma unroll
-      for (int j = 0; j < U; ++j) {
-        const int64_t i = c0 + (int64_t)j * kFinNT + tid;
-        v[j] = srow[i < n ? i : n - 1];  // clamped: no branch per load
-      }
-#pragma unroll
-      for (int j = 0; j < U; ++j)
-        if (c0 + (int64_t)j * kFinNT + tid < n) fn(score_key(v[j]));
-    }
-  };
-  for (int q = tid; q < 2048; q += kFinNT) {
-    hist_a[q] = 0;
-    hist_b[q] = 0;
-  }
-  uint32_t kmin = 0xffffffffu, kmax = 0u;
-  for_keys([&](uint32_t x) {
-    kmin = min(kmin, x);
-    kmax = max(kmax, x);
-  });
-  kmin = wave_min_u32(kmin);
-  kmax = wave_max_u32(kmax);
-  if (lane_id() == 0) {
-    wsum[wave] = kmin;
-    wsum[kFinWaves + wave] = kmax;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int w = 0; w < kFinWaves; ++w) {
-    kmin = min(kmin, wsum[w]);
-    kmax = max(kmax, wsum[kFinWaves + w]);
-  }
-  // keys share their top `common` bits: bin the 11 below them first
-  const int common = __clz(kmin ^ kmax);
-  int shift = common >= 21 ? 0 : 21 - common;
-  uint32_t need = keep;
-  for_keys([&](uint32_t x) { atomicAdd(&hist_a[(x >> shift) & 2047u], 1u); });
-  __syncthreads();
-  fin_threshold<2048>(hist_a, need, wsum, res);
-  uint32_t prefix = ((shift < 21 ? (kmin >> shift) : 0u) & ~2047u) | res[0];
-  need -= res[1];
-  bool all_in = res[2] == need;
-  uint32_t* hist = hist_b;
-  while (!all_in && shift > 0) {
-    const int wb = shift < 11 ? shift : 11;
-    const int sb = shift - wb;
-    for_keys([&](uint32_t x) {
-      if ((x >> shift) == prefix) atomicAdd(&hist[(x >> sb) & ((1u << wb) - 1u)], 1u);
-    });
-    __syncthreads();
-    fin_threshold<2048>(hist, need, wsum, res);
-    prefix = (prefix << wb) | res[0];
-    shift = sb;
-    need -= res[1];
-    all_in = res[2] == need;
-    // the other histogram is free again (its last reads ended before fin_threshold's barriers)
-    uint32_t* other = (hist == hist_b) ? hist_a : hist_b;
-    for (int q = tid; q < 2048; q += kFinNT) other[q] = 0;
-    hist = other;
-    __syncthreads();
-  }
-  const uint32_t need_eq = all_in ? 0u : need;
-
-  constexpr int J = 16;
-  uint32_t gbase = 0, ebase = 0;
-  for (int64_t c0 = 0; c0 < n; c0 += (int64_t)J * kFinNT) {
-    const int64_t i0 = c0 + (int64_t)J * tid;
-    uint32_t gm = 0, em = 0;
-    float v[J];
-#pragma unroll
-    for (int j = 0; j < J; ++j) v[j] = srow[i0 + j < n ? i0 + j : n - 1];  // clamped: no branch per load
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      if (i0 + j < n) {
-        const uint32_t h = score_key(v[j]) >> shift;
-        if (h > prefix || (all_in && h == prefix)) gm |= 1u << j;
-        else if (h == prefix) em |= 1u << j;
-      }
-    }
-    const uint32_t mine = (uint32_t)__popc(gm) | ((uint32_t)__popc(em) << 16);
-    const uint32_t incl = wave_incl_scan(mine);
-    if (lane_id() == kWave - 1) wsum[wave] = incl;
-    __syncthreads();
-    uint32_t before = 0, total = 0;
-#pragma unroll
-    for (int w = 0; w < kFinWaves; ++w) {
-      const uint32_t x = wsum[w];
-      before += (w < wave) ? x : 0u;
-      total += x;
-    }
-    __syncthreads();  // wsum is rewritten by the next chunk
-    const uint32_t ex = before + incl - mine;
-    uint32_t gpos = gbase + (ex & 0xffffu), epos = ebase + (ex >> 16);
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const bool g = (gm >> j) & 1u, e = (em >> j) & 1u;
-      if (g) {
-        out[gpos + min(epos, need_eq)] = (int32_t)(i0 + j);
-        ++gpos;
-      } else if (e) {
-        if (epos < need_eq) out[gpos + epos] = (int32_t)(i0 + j);
-        ++epos;
-      }
-    }
-    gbase += total & 0xffffu;
-    ebase += total >> 16;
-    if (gbase + min(ebase, need_eq) >= keep) break;  // every winner placed
-  }
-}
-
-// One workgroup per row. Thread i owns CH consecutive chunks of 8 slots (a slice of the row's
-// layout spans R / 8 chunks), so thread order is slot order is id order.
+// One workgroup of kFinNT threads per row finishes the selection from the row's candidate
+// lists (topk_finish.h); thread i owns CH consecutive chunks of 8 slots.
 template <int CH>
 __global__ __launch_bounds__(kFinNT) void topk_finish_kernel(const float* __restrict__ scores, int64_t ld,
                                                              const int64_t* __restrict__ ent_off,
                                                              const int64_t* __restrict__ q_pos, int m, int T, int k,
                                                              int64_t max_entries, int32_t* __restrict__ idx, void* ws,
                                                              int budget) {
-  constexpr int PER = 8;  // slots per chunk
-  static_assert(kMinSliceSlots % PER == 0, "a slice spans whole chunks");
-  __shared__ uint32_t hist_a[2048];
-  __shared__ uint32_t hist_b[2048];
-  __shared__ uint32_t hist_c[1024];
-  __shared__ uint32_t wsum[3 * kFinWaves];
-  __shared__ uint32_t res[4];
-
+  __shared__ FinishLds<kFinNT> lds;
   const int row = blockIdx.x;
   const int b = row / T, t = row % T;
-  const int tid = threadIdx.x;
   const TopkRowWs rw = topk_row_ws(ws, row, max_entries, budget);
-  const int n_chunks = (int)(topk_num_slices(max_entries) * budget / PER);
-  // every slot load is issued up front, raw (unpacked only once all of them are out)
-  // (a chunk past the row's slots reads the row's first chunk instead, so the loads carry no
-  // branches; such a chunk also lies past the row's last slice and is masked below)
-  u32x4 raw[CH][PER / 2];
-#pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const int j = tid * CH + c;
-    const u32x4* src = reinterpret_cast<const u32x4*>(rw.slots + (j < n_chunks ? (int64_t)j * PER : 0));
-#pragma unroll
-    for (int q = 0; q < PER / 2; ++q) raw[c][q] = src[q];
-  }
-  // the cut of each chunk's slice for each possible layout (2, 4 or 8 chunks per slice; the
-  // row's own layout is known only with n), also issued now and needed only at the end
-  const int ns_max = (int)topk_num_slices(max_entries);
-  uint32_t cut3[CH][3];
-#pragma unroll
-  for (int c = 0; c < CH; ++c)
-#pragma unroll
-    for (int l = 0; l < 3; ++l) cut3[c][l] = rw.cuts[min((tid * CH + c) >> (l + 1), ns_max - 1)];
-  const int64_t n = row_count(ent_off, q_pos, b, t, m, max_entries);
-  const uint32_t keep = (uint32_t)(n < k ? n : k);
-  int32_t* out = idx + (int64_t)row * k;
-  for (int q = tid; q < 2048; q += kFinNT) {
-    hist_a[q] = 0;
-    hist_b[q] = 0;
-  }
-  hist_c[tid] = 0;
-
-  if ((int64_t)keep == n) {
-    for (int p = tid; p < k; p += kFinNT) out[p] = p < n ? p : -1;
-    return;
-  }
-  if (topk_row_dense(n, k)) {
-    // winners too dense for candidate lists (more than 5 expected per wave of 64 entries):
-    // the lists were not written, search the row directly
-    finish_full_row(scores + (int64_t)row * ld, n, keep, out, hist_a, hist_b, wsum, res);
-    for (int p = (int)keep + tid; p < k; p += kFinNT) out[p] = -1;
-    return;
-  }
-  const int ns = (int)topk_num_slices(n);
-  // chunks per slice in this row's layout: 2, 4 or 8
-  const int cps_log2 = __ffs(topk_row_slots(n, max_entries, budget) / PER) - 1;
-  uint64_t sl[CH][PER];
-#pragma unroll
-  for (int c = 0; c < CH; ++c)
-#pragma unroll
-    for (int q = 0; q < PER / 2; ++q) {
-      sl[c][2 * q] = ((uint64_t)raw[c][q].y << 32) | raw[c][q].x;
-      sl[c][2 * q + 1] = ((uint64_t)raw[c][q].w << 32) | raw[c][q].z;
-    }
-  uint32_t key[CH][PER];
-  uint32_t kmin = 0xffffffffu, kmax = 0u;
-#pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const bool in = ((tid * CH + c) >> cps_log2) < ns;
-#pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      const uint32_t x = in ? (uint32_t)(sl[c][q] >> 32) : 0u;
-      key[c][q] = x;
-      if (x) {
-        kmin = min(kmin, x);
-        kmax = max(kmax, x);
-      }
-    }
-  }
-  uint32_t cut[CH];
-#pragma unroll
-  for (int c = 0; c < CH; ++c)
-    cut[c] = cps_log2 == 1 ? cut3[c][0] : (cps_log2 == 2 ? cut3[c][1] : cut3[c][2]);
-  const int wave = tid / kWave;
-  kmin = wave_min_u32(kmin);
-  kmax = wave_max_u32(kmax);
-  if (lane_id() == 0) {
-    wsum[wave] = kmin;
-    wsum[kFinWaves + wave] = kmax;
-  }
-  __syncthreads();  // histograms cleared, wave extremes posted
-#pragma unroll
-  for (int w = 0; w < kFinWaves; ++w) {
-    kmin = min(kmin, wsum[w]);
-    kmax = max(kmax, wsum[kFinWaves + w]);
-  }
-
-  // radix select of the keep-th largest listed key. The listed keys share their top
-  // L = clz(kmin ^ kmax) bits, so the first pass bins the 11 bits below those (spreading the
-  // keys over the bins instead of piling them into a few), the later passes the rest.
-  bool ok = true;
-  bool all_in = false;
-  uint32_t need = keep;
-  const int common = __clz(kmin ^ kmax);  // 32 when all keys are equal
-  int shift = common >= 21 ? 0 : 21 - common;
-  uint32_t prefix;  // value of key >> shift shared by the keys still in play
-#pragma unroll
-  for (int c = 0; c < CH; ++c)
-#pragma unroll
-    for (int q = 0; q < PER; ++q)
-      if (key[c][q]) atomicAdd(&hist_a[(key[c][q] >> shift) & 2047u], 1u);
-  __syncthreads();
-  fin_threshold<2048>(hist_a, need, wsum, res);
-  if (res[3] < keep) {
-    ok = false;  // fewer listed entries than winners
-  } else {
-    prefix = ((shift < 21 ? (kmin >> shift) : 0u) & ~2047u) | res[0];
-    need -= res[1];
-    all_in = res[2] == need;
-    if (!all_in && shift > 0) {
-      const int wb = shift < 11 ? shift : 11;
-      const int sb = shift - wb;
-#pragma unroll
-      for (int c = 0; c < CH; ++c)
-#pragma unroll
-        for (int q = 0; q < PER; ++q)
-          if (key[c][q] && (key[c][q] >> shift) == prefix)
-            atomicAdd(&hist_b[(key[c][q] >> sb) & ((1u << wb) - 1u)], 1u);
-      __syncthreads();
-      fin_threshold<2048>(hist_b, need, wsum, res);
-      prefix = (prefix << wb) | res[0];
-      shift = sb;
-      need -= res[1];
-      all_in = res[2] == need;
-      if (!all_in && shift > 0) {  // shift <= 10 here
-#pragma unroll
-        for (int c = 0; c < CH; ++c)
-#pragma unroll
-          for (int q = 0; q < PER; ++q)
-            if (key[c][q] && (key[c][q] >> shift) == prefix)
-              atomicAdd(&hist_c[key[c][q] & ((1u << shift) - 1u)], 1u);
-        __syncthreads();
-        fin_threshold<1024>(hist_c, need, wsum, res);
-        prefix = (prefix << shift) | res[0];
-        shift = 0;
-        need -= res[1];
-        all_in = res[2] == need;
-      }
-    }
-  }
-
-  if (ok) {
-    // winners: keys above the selected bin, plus (unless the whole bin is taken) the first
-    // `need` keys equal to the exact key value, in id order
-    const uint32_t lo = prefix << shift;  // lowest key a winner can have
-    uint32_t gmask = 0, emask = 0, viol = 0;
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      if (((tid * CH + c) >> cps_log2) < ns && cut[c] > lo) viol = 1;
-#pragma unroll
-      for (int q = 0; q < PER; ++q) {
-        const uint32_t x = key[c][q];
-        const uint32_t h = x >> shift;
-        const bool g = x != 0u && (h > prefix || (all_in && h == prefix));
-        const bool e = x != 0u && !all_in && h == prefix;
-        gmask |= (uint32_t)g << (c * PER + q);
-        emask |= (uint32_t)e << (c * PER + q);
-      }
-    }
-    // one block scan of (gt count | eq count << 16): a row lists at most 32768 keys
-    const uint32_t mine = (uint32_t)__popc(gmask) | ((uint32_t)__popc(emask) << 16);
-    const uint32_t incl = wave_incl_scan(mine);
-    const bool wviol = __ballot(viol != 0u) != 0ull;
-    if (lane_id() == kWave - 1) {
-      wsum[wave] = incl;
-      wsum[kFinWaves + wave] = wviol ? 1u : 0u;
-    }
-    __syncthreads();
-    uint32_t before = 0, tv = 0;
-#pragma unroll
-    for (int w = 0; w < kFinWaves; ++w) {
-      before += (w < wave) ? wsum[w] : 0u;
-      tv |= wsum[kFinWaves + w];
-    }
-    if (tv != 0u) {
-      ok = false;  // a slice may hide a winner below its cut
-      __syncthreads();
-    } else {
-      const uint32_t ex = before + incl - mine;
-      uint32_t gpos = ex & 0xffffu, epos = ex >> 16;
-      const uint32_t need_eq = all_in ? 0u : need;
-      const uint32_t wins = gmask | emask;
-#pragma unroll
-      for (int c = 0; c < CH; ++c)
-#pragma unroll
-        for (int q = 0; q < PER; ++q) {
-          const int bit = c * PER + q;
-          if ((wins >> bit) & 1u) {
-            const bool g = (gmask >> bit) & 1u;
-            const uint32_t e_before = min(epos, need_eq);
-            if (g || epos < need_eq) out[gpos + e_before] = (int32_t)(uint32_t)sl[c][q];
-            gpos += g ? 1u : 0u;
-            epos += g ? 0u : 1u;
-          }
-        }
-    }
-  }
-  if (!ok) {
-    __syncthreads();  // every thread is done with the histograms and wsum
-    finish_full_row(scores + (int64_t)row * ld, n, keep, out, hist_a, hist_b, wsum, res);
-  }
-  for (int p = (int)keep + tid; p < k; p += kFinNT) out[p] = -1;
+  finish_row<kFinNT, CH>(scores + (int64_t)row * ld, rw, [&] { return row_count(ent_off, q_pos, b, t, m, max_entries); },
+                         max_entries, budget, k, idx + (int64_t)row * k, lds);
 }
 
 template <int ITEMS>

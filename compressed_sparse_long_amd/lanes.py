@@ -181,9 +181,11 @@ class CsaLane(_Lane):
                                                           dtype=torch.float32, device=device)
         self.idx = torch.empty((self.B, self.T, self.k), dtype=torch.int32, device=device)
         nb = topk_workspace_bytes(self.B, self.T, self.max_entries, self.k)
-        self.topk_ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=device)  # contents never matter on entry
+        # workspaces start zeroed (their leading counters must be zero on first use; each call
+        # leaves them zero)
+        self.topk_ws = torch.zeros(max(nb, 16), dtype=torch.uint8, device=device)
         na = attn_workspace_bytes(self.B, self.T, self.H, lane.D, self.k + self.W)
-        self.attn_ws = torch.empty(max(na, 16), dtype=torch.uint8, device=device)
+        self.attn_ws = torch.zeros(max(na, 16), dtype=torch.uint8, device=device)
         self.kI_copies = [self.kI]
         self.k_scale_copies = [self.k_scale]
 
@@ -258,7 +260,7 @@ class HcaLane(_Lane):
     def __init__(self, lane, kv, z, q, li, device="cuda"):
         super().__init__(lane, kv, z, q, li.kv_off, li.ent_off, li.q_pos, device)
         na = attn_workspace_bytes(self.B, self.T, self.H, lane.D, self.max_entries + self.W)
-        self.attn_ws = torch.empty(max(na, 16), dtype=torch.uint8, device=device)
+        self.attn_ws = torch.zeros(max(na, 16), dtype=torch.uint8, device=device)
 
     def attend(self, r: int = 0):
         hca_attn_decode(self.q, self.ckv_copies[r % len(self.ckv_copies)], self.kv, self.kv_off, self.ent_off,

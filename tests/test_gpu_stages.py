@@ -195,7 +195,7 @@ def _run_indexer(csl, HI, T, lengths, q_pos, fp8, fp4=False):
     scores = torch.full((B, T, ld), float("nan"), dtype=torch.float32, device="cuda")
     topk = {}
     if fp4 and T == 1 and max(E) > 34816:  # the candidate-list path of the decode kernel too
-        topk = dict(topk_ws=torch.empty(csl.topk_workspace_bytes(B, T, max(E), 64), dtype=torch.uint8,
+        topk = dict(topk_ws=torch.zeros(csl.topk_workspace_bytes(B, T, max(E), 64), dtype=torch.uint8,
                                         device="cuda"), topk_k=64)
     csl.indexer_scores(dev(li.qI), dev(li.w), dev(li.kI), dev(li.ent_off), dev(li.q_pos), 4, scores,
                        max_entries=max(E), k_scale=dev(li.k_scale), scale_off=dev(li.scale_off), scale_group=64,

@@ -4,6 +4,7 @@ sentinel first, so both paths must write them. The indexer scores and the select
 from the same kernels and must match exactly; the newest compressed rows and the attention
 output may differ only by the accumulation order of the two compression layouts.
 """
+import numpy as np
 import pytest
 import torch
 
@@ -24,6 +25,11 @@ pytestmark = pytest.mark.gpu
     ((4, 9000, 7), 4, True, 64, 8, False, 16, True),               # a one-entry sequence: series a only
     ((4096,), 8, False, 64, 4, False, 16, True),                   # uniform weights over 2m = 16 rows
     ((65536,), 16, True, 128, 8, False, 16, True),                 # m = 16: its own launch
+    # rows of 2^18 entries beside a row too dense for candidate lists, a row with fewer entries
+    # than k and an empty row; fp8 keys; overlapped compression
+    ((1 << 20, 40000, 4000, 3), 4, True, 1024, 8, False, 64, False),
+    ((1 << 20, 600001), 4, True, 1024, 8, True, 64, False),
+    ((1 << 20, 5), 4, True, 1024, 8, False, 64, True),
 ])
 def test_csa_decode_step_matches_separate_calls(lengths, m, has_z, k, HI, fp8, H, overlap):
     _step_vs_calls(lengths, m, has_z, k, HI, fp8, H, overlap, extras=False)
@@ -37,6 +43,74 @@ def test_csa_decode_step_matches_separate_calls(lengths, m, has_z, k, HI, fp8, H
 def test_csa_decode_step_with_sink_and_rope_matches_separate_calls(lengths, m, k, H, overlap):
     """The step forwards the attention extras (per-head sink, partial RoPE) unchanged."""
     _step_vs_calls(lengths, m, True, k, 8, False, H, overlap, extras=True)
+
+
+def test_csa_decode_step_finishes_crowded_rows_exactly():
+    """The best keys of one row crowd into four 512-entry slices: their candidate lists cannot
+    prove the selection, and the finishing step must search the whole row. The step then equals
+    the separate calls and is a valid top-k of the oracle's scores."""
+    from compressed_sparse_long_amd import lanes
+    from oracle import csa, pipeline
+    from tests._parity import f64, topk_band_check
+    lane = W.Lane("csa", (1 << 20, 300000), (1 << 20, 300000), T=1, H=64, m=4, k=1024, HI=8)
+    inp = synth.generate(W.Workload("crowd", 23, (lane,)))
+    li = inp.lanes[0]
+    lead = li.qI[0, 0].float().sum(0)
+    li.kI[1000:3048] = (lead * 4 + 0.05 * li.kI[1000:3048].float()).to(torch.bfloat16)
+    (cl,) = lanes.build_lanes(inp)
+    cl.compress_all()
+    res = []
+    for fused in (False, True):
+        cl.idx.fill_(-7)
+        cl.step(0, fused=fused)
+        torch.cuda.synchronize()
+        res.append((cl.idx.clone(), cl.out.clone()))
+    assert torch.equal(res[0][0], res[1][0]), "selected ids differ"
+    torch.testing.assert_close(res[1][1], res[0][1], rtol=0, atol=2e-3)
+    got = res[1][0].cpu().numpy()
+    assert np.sum((got[0, 0] >= 1000) & (got[0, 0] < 3048)) > 512, "the crowded slices hold most winners"
+    keys = pipeline.index_keys_f64(li.kI)
+    for b in range(lane.B):
+        e0, e1 = lane.ent_off()[b], lane.ent_off()[b + 1]
+        ref_s = csa.indexer(f64(li.qI[b, 0]), f64(li.w[b, 0]), keys[e0:e1])
+        topk_band_check(got[b, 0], ref_s, lane.k, what=f"b={b}")
+
+
+def test_csa_decode_step_repeats_on_1m_rows():
+    """Calls in a row on 2^18-entry rows (the headline shape): every call selects the same
+    entries as the separate calls."""
+    from compressed_sparse_long_amd import lanes
+    lane = W.Lane("csa", (1 << 20, 1 << 20, 70000), (1 << 20, 1 << 20, 70000), T=1, H=64, m=4, k=1024, HI=8)
+    inp = synth.generate(W.Workload("fin_reset", 29, (lane,)))
+    (cl,) = lanes.build_lanes(inp)
+    cl.compress_all()
+    cl.step(0, fused=False)
+    torch.cuda.synchronize()
+    ref = cl.idx.clone()
+    for rep in range(4):
+        cl.idx.fill_(-7)
+        cl.step(0)
+        torch.cuda.synchronize()
+        assert torch.equal(cl.idx, ref), f"call {rep}: selected ids differ"
+
+
+def test_single_split_attention_writes_no_workspace():
+    """A step whose attention runs in one split per row needs no workspace: with RoPE and a
+    sink it must leave the bytes around the (16-byte) buffer it was given untouched (the RoPE
+    table for the merge was once written there regardless)."""
+    from compressed_sparse_long_amd import attn_workspace_bytes, lanes
+    inp = synth.generate("csa_decode_4k")
+    (cl,) = lanes.build_lanes(inp)
+    assert attn_workspace_bytes(cl.B, cl.T, cl.H, 128, cl.k + cl.W) == 0
+    cl.rope_dims = 64
+    cl.sink = W.normal_f32(3, W.S_EXTRA + 7, (cl.H,), std=2.0).cuda()
+    guard = torch.full((1 << 16,), 0x5A, dtype=torch.uint8, device="cuda")
+    cl.attn_ws = guard[4096:4096 + 16]
+    cl.compress_all()
+    cl.step()
+    torch.cuda.synchronize()
+    assert torch.all(guard == 0x5A), "bytes around the workspace were written"
+    assert bool(torch.isfinite(cl.out).all())
 
 
 def _step_vs_calls(lengths, m, has_z, k, HI, fp8, H, overlap, extras):
