@@ -99,6 +99,20 @@ int check_paged(const char* who, const csl_paged_cache* pc, int B, csl::PagedVie
   return CSL_OK;
 }
 
+// fp8 indexer keys in the paged pool keep their group scales per block: the scale of pool row r
+// is k_scale[r >> scale_shift], one scale per group of a block (groups smaller than a block) or
+// one per block (a group spanning blocks, its scale repeated in each). Groups are powers of two,
+// so a group never straddles a block boundary without covering the whole block.
+int check_paged_scales(const char* who, int k_dtype, int scale_group, csl::PagedView& pv) {
+  if (k_dtype != CSL_DTYPE_FP8_E4M3) return CSL_OK;
+  if (scale_group < 1 || (scale_group & (scale_group - 1)))
+    return fail(CSL_ERR_INVALID, "%s: fp8 keys in a paged cache need a power-of-two scale_group, got %d", who,
+                scale_group);
+  const int lg = __builtin_ctz((unsigned)scale_group);
+  pv.scale_shift = lg < pv.eb_shift ? lg : pv.eb_shift;
+  return CSL_OK;
+}
+
 // The per-sequence ring of raw rows must hold every raw row a call reads at once: the window
 // of each of the T query rows (rows p - n_win + 1 .. p for p = q_pos + t, the newest rows of a
 // context whose queries sit at its end: n_win + T - 1 rows) and the chunks being compressed
@@ -131,7 +145,7 @@ int key_type(int k_dtype) {
 int check_indexer(const void* q_idx, const float* w, const void* k_idx, int k_dtype, const void* k_scale,
                   const int64_t* scale_off, int scale_group, const int64_t* ent_off, const int64_t* q_pos, int m, int B,
                   int T, int HI, int CI, int64_t max_entries, const float* scores, int64_t ld, void*& topk_ws,
-                  size_t topk_ws_bytes, int topk_k, const char* who = "indexer_scores") {
+                  size_t topk_ws_bytes, int topk_k, const char* who = "indexer_scores", bool paged = false) {
   if (B < 0 || T < 0 || max_entries < 0) return fail(CSL_ERR_INVALID, "%s: negative size", who);
   if (!q_idx || !w || !k_idx || !ent_off || !q_pos || !scores)
     return fail(CSL_ERR_INVALID, "%s: null pointer argument", who);
@@ -140,7 +154,8 @@ int check_indexer(const void* q_idx, const float* w, const void* k_idx, int k_dt
     return fail(CSL_ERR_UNSUPPORTED, "%s: k_dtype must be BF16, FP8_E4M3 or MXFP4", who);
   const bool fp8 = k_dtype == CSL_DTYPE_FP8_E4M3;
   const bool fp4 = k_dtype == CSL_DTYPE_MXFP4;
-  if (fp8 && (!k_scale || !scale_off || scale_group < 1))
+  // (in a paged cache the scales follow the pool rows and scale_off is not used)
+  if (fp8 && (!k_scale || (!scale_off && !paged) || scale_group < 1))
     return fail(CSL_ERR_INVALID, "%s: fp8 keys need k_scale, scale_off and scale_group >= 1", who);
   if (fp4 && !k_scale) return fail(CSL_ERR_INVALID, "%s: MXFP4 keys need their E8M0 scales in k_scale", who);
   if (HI != 1 && HI != 2 && HI != 4 && HI != 8 && HI != 16)
@@ -236,14 +251,15 @@ int csl_indexer_scores(const void* q_idx, const float* w, const void* k_idx, int
                        int B, int T, int HI, int CI, int64_t max_entries, float* scores, int64_t ld, void* topk_ws,
                        size_t topk_ws_bytes, int topk_k, const csl_paged_cache* paged, void* stream) {
   int st = check_indexer(q_idx, w, k_idx, k_dtype, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T, HI,
-                         CI, max_entries, scores, ld, topk_ws, topk_ws_bytes, topk_k);
+                         CI, max_entries, scores, ld, topk_ws, topk_ws_bytes, topk_k, "indexer_scores",
+                         paged != nullptr);
   if (st != CSL_OK) return st;
   csl::PagedView pv;
   if (paged) {
     st = check_paged("indexer_scores", paged, B, pv);
     if (st != CSL_OK) return st;
-    if (k_dtype == CSL_DTYPE_FP8_E4M3)
-      return fail(CSL_ERR_UNSUPPORTED, "indexer_scores: fp8 keys (group scales) are not supported in a paged cache");
+    st = check_paged_scales("indexer_scores", k_dtype, scale_group, pv);
+    if (st != CSL_OK) return st;
   }
   if (B == 0 || T == 0 || max_entries == 0) return ok();
   return hip_status(csl::launch_indexer(q_idx, w, k_idx, key_type(k_dtype), k_scale, scale_off, scale_group,
@@ -265,7 +281,7 @@ int csl_indexer_topk(const void* q_idx, const float* w, const void* k_idx, int k
   // the indexer's checks, with idx standing in for the score buffer it does not need
   int st = check_indexer(q_idx, w, k_idx, k_dtype, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T, HI, CI,
                          max_entries, reinterpret_cast<const float*>(idx), max_entries, no_ws, 0, 0,
-                         "indexer_topk");
+                         "indexer_topk", paged != nullptr);
   if (st != CSL_OK) return st;
   const int kmax = csl_indexer_topk_max_k(HI);
   if (k < 1 || k > kmax) return fail(CSL_ERR_UNSUPPORTED, "indexer_topk: k must be in [1, %d], got %d", kmax, k);
@@ -276,8 +292,8 @@ int csl_indexer_topk(const void* q_idx, const float* w, const void* k_idx, int k
   if (paged) {
     st = check_paged("indexer_topk", paged, B, pv);
     if (st != CSL_OK) return st;
-    if (k_dtype == CSL_DTYPE_FP8_E4M3)
-      return fail(CSL_ERR_UNSUPPORTED, "indexer_topk: fp8 keys (group scales) are not supported in a paged cache");
+    st = check_paged_scales("indexer_topk", k_dtype, scale_group, pv);
+    if (st != CSL_OK) return st;
   }
   if (B == 0 || T == 0) return ok();
   return hip_status(csl::launch_indexer_topk(q_idx, w, k_idx, key_type(k_dtype), k_scale, scale_off, scale_group,
@@ -420,8 +436,8 @@ int csl_csa_decode_step(const csl_csa_step* s, void* stream) {
   if (s->paged) {
     st = check_paged("csa_decode_step", s->paged, s->B, pv);
     if (st != CSL_OK) return st;
-    if (s->k_dtype == CSL_DTYPE_FP8_E4M3)
-      return fail(CSL_ERR_UNSUPPORTED, "csa_decode_step: fp8 keys are not supported in a paged cache");
+    st = check_paged_scales("csa_decode_step", s->k_dtype, s->scale_group, pv);
+    if (st != CSL_OK) return st;
     st = check_ring("csa_decode_step", s->paged, s->n_win, s->T, s->m, s->max_new_entries, overlap);
     if (st != CSL_OK) return st;
     pvp = &pv;
@@ -434,7 +450,7 @@ int csl_csa_decode_step(const csl_csa_step* s, void* stream) {
     void* no_ws = nullptr;
     st = check_indexer(s->q_idx, s->w, s->k_idx, s->k_dtype, s->k_scale, s->scale_off, s->scale_group, s->ent_off,
                        s->q_pos, s->m, s->B, s->T, s->HI, s->CI, s->max_entries, reinterpret_cast<const float*>(s->idx),
-                       s->max_entries, no_ws, 0, 0, "csa_decode_step");
+                       s->max_entries, no_ws, 0, 0, "csa_decode_step", s->paged != nullptr);
     if (st != CSL_OK) return st;
     const int kmax = csl_indexer_topk_max_k(s->HI);
     if (s->k < 1 || s->k > kmax)
@@ -444,7 +460,7 @@ int csl_csa_decode_step(const csl_csa_step* s, void* stream) {
   } else {
     st = check_indexer(s->q_idx, s->w, s->k_idx, s->k_dtype, s->k_scale, s->scale_off, s->scale_group, s->ent_off,
                        s->q_pos, s->m, s->B, s->T, s->HI, s->CI, s->max_entries, s->scores, s->ld, topk_ws,
-                       s->topk_ws_bytes, s->k);
+                       s->topk_ws_bytes, s->k, "csa_decode_step", s->paged != nullptr);
     if (st != CSL_OK) return st;
     st = check_topk(s->scores, s->ld, s->ent_off, s->q_pos, s->m, s->B, s->T, s->k, s->max_entries, s->idx,
                     s->topk_ws, s->topk_ws_bytes);

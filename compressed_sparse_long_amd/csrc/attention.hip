@@ -37,6 +37,18 @@ constexpr int kKT = 64;               // keys per tile
 constexpr int kRope = 64;             // partial RoPE: the last 64 dims ([P1] section 8)
 constexpr int kRopeOff = kD - kRope;  // first rotated dim
 constexpr int kRopeKK = kRopeOff / 32;  // first rotated 32-dim chunk of the query operand
+#ifndef CSL_HS_WAVES
+#define CSL_HS_WAVES 8
+#endif
+#ifndef CSL_HS_TILES
+#define CSL_HS_TILES 24
+#endif
+#ifndef CSL_HS_MAX_WG
+#define CSL_HS_MAX_WG 0
+#endif
+constexpr int kHsWaves = CSL_HS_WAVES;   // head-split workgroups: waves (tiles per round)
+constexpr int kHsTiles = CSL_HS_TILES;   // head-split workgroups: most tiles per split
+constexpr int kHsMaxWg = CSL_HS_MAX_WG;  // head split while rows x head groups stays within this
 
 // The paged cache as the attention reads it: entry e of sequence b at pool row
 // table[b * max_blocks + (e >> eb_shift)] << eb_shift | (e & mask); raw rows in rings
@@ -314,15 +326,14 @@ template <int NHG, int NSUB, bool SPARSE, int MODE, bool ROPE, bool PAGED>
 __global__ __launch_bounds__(NHG * NSUB * 64) void attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ ckv, const int32_t* __restrict__ idx, int k,
     const uint16_t* __restrict__ kv, const int64_t* __restrict__ kv_off, const int64_t* __restrict__ ent_off,
-    const int64_t* __restrict__ q_pos, int m, int n_win, int T, float scale_log2, int64_t max_entries,
+    const int64_t* __restrict__ q_pos, int m, int n_win, int T, int H, float scale_log2, int64_t max_entries,
     int keys_per_split, float* __restrict__ out, float* __restrict__ lse_out, float* __restrict__ ws_o,
     float* __restrict__ ws_lse, const float* __restrict__ sink, double rope_theta1,
     float2* __restrict__ ws_rope, AttnLayout lay) {
   constexpr bool MULTI = MODE == 0;
-  static_assert(NSUB == 1 || MODE == 1, "parallel tiles take single-round splits of one tile each");
-  constexpr int NTL = MULTI ? 1 : (NSUB > 1 ? NSUB : MODE);  // tiles held in LDS at once
+  static_assert(NSUB == 1 || MODE <= 1, "parallel tiles take rounds of one tile per wave group");
+  constexpr int NTL = NSUB > 1 ? NSUB : (MULTI ? 1 : MODE);  // tiles held in LDS at once
   constexpr int NT = NHG * NSUB * 64;
-  constexpr int H = NHG * 16;
   constexpr int NV = kKT * NTL;            // rows gathered per round
   constexpr int NP = 4 * NV;               // gather pairs per round
   constexpr int RPT = (NP + NT - 1) / NT;  // pairs (rows) per thread
@@ -341,6 +352,7 @@ __global__ __launch_bounds__(NHG * NSUB * 64) void attn_kernel(
   const int split = blockIdx.x;
   const int row = blockIdx.y;
   const int nrows = gridDim.y;
+  const int hz = blockIdx.z;  // this workgroup's NHG * 16 heads: hz * NHG * 16 ..
   const int b = row / T, t = row % T;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -364,7 +376,7 @@ __global__ __launch_bounds__(NHG * NSUB * 64) void attn_kernel(
   };
   int32_t ids_cur[RPT], ids_nxt[RPT];
   load_ids(k_lo, ids_cur);
-  if (MULTI) load_ids(k_lo + kKT, ids_nxt);
+  if (MULTI) load_ids(k_lo + NV, ids_nxt);
   const RowGeom geo = row_geom(kv_off, ent_off, q_pos, b, t, m, n_win, max_entries);
   const int64_t n_comp = SPARSE ? (int64_t)k : geo.nvis;  // compressed slots in the list
   const int64_t L = n_comp + geo.win_cnt;
@@ -420,7 +432,7 @@ __global__ __launch_bounds__(NHG * NSUB * 64) void attn_kernel(
   };
 
   // queries of this wave's 16 heads as MFMA B operands (d-slots 8g..8g+7 of each 32-chunk)
-  const int head = hg * 16 + c;
+  const int head = (hz * NHG + hg) * 16 + c;
   bf16x8 qb[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
@@ -453,7 +465,7 @@ __global__ __launch_bounds__(NHG * NSUB * 64) void attn_kernel(
     if (lane < kRope / 2) {
       const float2 cs = rope_cs(p, lane, rope_theta1);
       rcs[lane] = cs;
-      if (ws_rope && split == 0 && wave == 0) ws_rope[(int64_t)row * (kRope / 2) + lane] = cs;
+      if (ws_rope && split == 0 && hz == 0 && wave == 0) ws_rope[(int64_t)row * (kRope / 2) + lane] = cs;
     }
     // the wave's own LDS writes, ordered before its reads (in-wave: no hardware wait needed)
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
@@ -498,10 +510,10 @@ __global__ __launch_bounds__(NHG * NSUB * 64) void attn_kernel(
     }
     __syncthreads();
     if (ROPE && !MULTI) rotate_q();  // single round: the rows (and so the query) have landed
-    // the next tile's rows and the ids two tiles ahead go out while this one computes
-    if (MULTI && t0 + kKT < k_hi) {
-      issue(t0 + kKT, ids_nxt);
-      if (SPARSE && t0 + 2 * kKT < k_hi) load_ids(t0 + 2 * kKT, ids_nxt);
+    // the next round's rows and the ids two rounds ahead go out while this one computes
+    if (MULTI && t0 + NV < k_hi) {
+      issue(t0 + NV, ids_nxt);
+      if (SPARSE && t0 + 2 * NV < k_hi) load_ids(t0 + 2 * NV, ids_nxt);
     }
     if (NSUB > 1) {
       if (sub == 0 || t0 + sub * kKT < k_hi)
@@ -624,8 +636,16 @@ hipError_t launch_nhg(int H, dim3 grid, hipStream_t st, const uint16_t* q, const
   const int tiles = kps / kKT;  // 1 or 2: gathered in one round; more: the prefetching loop
 #define CSL_ATTN_LAUNCH(NHG, NSUB, MODE)                                                                       \
   attn_kernel<NHG, NSUB, SPARSE, MODE, ROPE, PAGED><<<grid, NHG * NSUB * 64, 0, st>>>(                        \
-      q, ckv, idx, k, kv, kv_off, ent_off, q_pos, m, n_win, T, scale_log2, max_entries, kps, out, lse, ws_o,  \
+      q, ckv, idx, k, kv, kv_off, ent_off, q_pos, m, n_win, T, H, scale_log2, max_entries, kps, out, lse, ws_o, \
       ws_lse, ex.sink, ex.rope_theta1, ws_rope, lay)
+  if (p.head_split) {  // 16 heads per workgroup, kHsWaves tiles per round
+    if (H != 16 * p.hsplit || p.nsub != kHsWaves) return hipErrorInvalidValue;
+    if (tiles <= kHsWaves)
+      CSL_ATTN_LAUNCH(1, kHsWaves, 1);
+    else
+      CSL_ATTN_LAUNCH(1, kHsWaves, 0);
+    return hipGetLastError();
+  }
   if (p.nsub > 1) {  // a row's whole key list in one workgroup, its tiles multiplied at once
 #define CSL_ATTN_PAR(NHG, NSUB)                     \
   case NHG:                                        \
@@ -687,11 +707,23 @@ AttnPlan attn_plan(int B, int T, int H, int64_t max_keys) {
   // no partials and no merge. Longer lists use several workgroups: each matrix core then
   // multiplies fewer tiles than it would for a wave group of its own per tile
   p.nsub = 1;
+  p.hsplit = 1;
+  p.head_split = false;
   const int nsub = attn_nsub(H);
   if (rows < 512 && nsub > 1 && tiles > 1 && tiles <= nsub) {
     p.nsub = nsub;
     p.keys_per_split = nsub * kKT;
     p.nsplit = 1;
+    return p;
+  }
+  if (kHsMaxWg > 0 && H % 16 == 0 && rows * (H / 16) <= kHsMaxWg && tiles > nsub) {
+    p.head_split = true;
+    p.hsplit = H / 16;
+    p.nsub = kHsWaves;
+    p.nsplit = (int)((tiles + kHsTiles - 1) / kHsTiles);
+    const int64_t tps = (tiles + p.nsplit - 1) / p.nsplit;
+    p.keys_per_split = (int)(tps * kKT);
+    p.nsplit = (int)((tiles + tps - 1) / tps);
     return p;
   }
   // aim for about two workgroups per CU, with at least two tiles per split when the list has
@@ -733,7 +765,7 @@ hipError_t launch_attention(bool sparse, const void* q, const void* ckv, const i
   // the rows' RoPE tables follow the partials (8-byte aligned: the partials are whole rows
   // of 16 heads); only the merge reads them
   float2* ws_rope = ws_o ? reinterpret_cast<float2*>(ws_lse + (size_t)p.nsplit * rows * H) : nullptr;
-  dim3 grid((unsigned)p.nsplit, (unsigned)rows);
+  dim3 grid((unsigned)p.nsplit, (unsigned)rows, (unsigned)p.hsplit);
   const float sl2 = scale * kLog2e;
   const uint16_t* q16 = static_cast<const uint16_t*>(q);
   const uint16_t* c16 = static_cast<const uint16_t*>(ckv);

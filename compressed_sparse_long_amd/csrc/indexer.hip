@@ -48,6 +48,17 @@ __device__ __forceinline__ int64_t key_row(const PagedView& pg, int b, int64_t e
   return ((int64_t)pg.table[(int64_t)b * pg.max_blocks + j] << pg.eb_shift) | (s & ((1 << pg.eb_shift) - 1));
 }
 
+// Slot of the fp8 group scale of entry s of sequence b: scale_off[b] + s / scale_group, or in the
+// paged layout the pool scale of its key row kr, kr >> scale_shift (the pool keeps its scales
+// per block: one per power-of-two group inside a block, or one per block when a group spans
+// several blocks)
+template <bool PAGED>
+__device__ __forceinline__ int64_t fp8_scale_index(const PagedView& pg, int64_t kr, const int64_t* scale_off, int b,
+                                                   int64_t s, int scale_group) {
+  if (PAGED) return kr >> pg.scale_shift;
+  return scale_off[b] + s / scale_group;
+}
+
 // first dim of the 8 k-slots that lane group g supplies for MFMA kk (the key and query
 // operands share this order)
 template <int KT>
@@ -231,8 +242,9 @@ __global__ __launch_bounds__(NWAVES * 64) void indexer_kernel(
     for (int u = 0; u < U; ++u) {
       const int64_t s = s0 + u * 16 + c;
       const bool ok = s < e_end;
-      load_key_tile<KT>(kI, k_mx, key_row<PAGED>(pg, b, e_base, s), ok, g, kb[u][0], kb[u][1]);
-      if (FP8) sc[u] = ok ? k_scale[scale_off[b] + s / scale_group] : 0.f;
+      const int64_t kr = key_row<PAGED>(pg, b, e_base, s);
+      load_key_tile<KT>(kI, k_mx, kr, ok, g, kb[u][0], kb[u][1]);
+      if (FP8) sc[u] = ok ? k_scale[fp8_scale_index<PAGED>(pg, kr, scale_off, b, s, scale_group)] : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -471,8 +483,9 @@ __global__ __launch_bounds__(kFusedWaves * kWave, FusedShape<HI>::WAVES_PER_SIMD
     for (int u = 0; u < U; ++u) {
       const int64_t s = s0 + (wave * U + u) * 16 + c;
       const bool ok = s < n_max;
-      load_key_tile<KT>(kI, k_mx, key_row<PAGED>(pg, b, e_base, s), ok, g, kb[u][0], kb[u][1]);
-      if (FP8) sc[u] = ok ? k_scale[scale_off[b] + s / scale_group] : 0.f;
+      const int64_t kr = key_row<PAGED>(pg, b, e_base, s);
+      load_key_tile<KT>(kI, k_mx, kr, ok, g, kb[u][0], kb[u][1]);
+      if (FP8) sc[u] = ok ? k_scale[fp8_scale_index<PAGED>(pg, kr, scale_off, b, s, scale_group)] : 0.f;
     }
   };
   if (threadIdx.x == 0) cut_req = 0;  // read only after the first chunk's barrier
@@ -716,7 +729,16 @@ __global__ __launch_bounds__(kSlice) void indexer_decode_kernel(
     load_key_tile<KT>(kI, k_mx, PAGED ? prow[u] : e_base + s, s < e_end, g, kb[u][0], kb[u][1]);
   }
   float my_scale = 1.f;  // fp8 group scale of this lane's entry on the way out
-  if (FP8 && e0 + lane < e_end) my_scale = k_scale[scale_off[b] + (e0 + lane) / scale_group];
+  if (FP8 && e0 + lane < e_end) {
+    int64_t kr = e0 + lane;
+    if (PAGED) {  // entry e0 + lane is key u = lane / 16 of this lane's column c: pool row prow[u]
+      kr = prow[0];
+#pragma unroll
+      for (int u = 1; u < U; ++u)
+        if (lane / 16 == u) kr = prow[u];
+    }
+    my_scale = k_scale[fp8_scale_index<PAGED>(pg, kr, scale_off, b, e0 + lane, scale_group)];
+  }
 
   // B operand: column c is head c % HI of query row t0 + c / HI
   const int tq = t0 + c / HI;

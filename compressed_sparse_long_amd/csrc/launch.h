@@ -18,6 +18,7 @@ struct PagedView {
   int eb_shift = 0;
   int ring_rows = 0;
   int64_t pool_rows = 0;
+  int scale_shift = 0;  // fp8 indexer keys: the group scale of pool row r at k_scale[r >> scale_shift]
 };
 
 hipError_t launch_compress(const void* kv, const void* z, const int64_t* kv_off, const int64_t* ent_off,
@@ -74,7 +75,9 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int64_t* ent_off, 
 struct AttnPlan {
   int nsplit;
   int keys_per_split;
-  int nsub;  // tiles one workgroup multiplies at once (its waves in nsub groups)
+  int nsub;    // tiles one workgroup multiplies at once (its waves in nsub groups)
+  int hsplit;  // workgroups per (row, split), each taking H / hsplit heads
+  bool head_split;  // 16 heads per workgroup, whose waves each multiply one tile of a round
 };
 // Per-query extras of the core attention: the attention sink (per-head logits added to the
 // softmax denominator) and partial RoPE (the query's last rope_dims dims rotated at its

@@ -146,6 +146,21 @@ class _Lane:
             if self.k_format == "mxfp4":
                 self.k_scale_copies = [to_pool(c) for c in self.k_scale_copies]
                 self.k_scale = self.k_scale_copies[0]
+            elif self.k_scale is not None:
+                # fp8 group scales move with the blocks: the scale of pool row r sits at
+                # r >> min(log2(group), log2(block)), one per group inside a block or one per
+                # block (repeated) when a group spans several blocks
+                g = int(self.scale_group)
+                assert g > 0 and g & (g - 1) == 0 and eb & (eb - 1) == 0, "power-of-two groups and blocks"
+                sh = min(g.bit_length(), eb.bit_length()) - 1
+                soff = self.scale_off.cpu()
+                sidx = torch.cat([soff[b] + torch.arange(e, dtype=torch.int64) // g for b, e in enumerate(E)]
+                                 + [torch.zeros(0, dtype=torch.int64)]).to(dev)
+                pool_sc = torch.zeros(max(pool_rows >> sh, 1), dtype=self.k_scale.dtype, device=dev)
+                if prow.numel():
+                    pool_sc[prow >> sh] = self.k_scale[sidx]
+                self.k_scale = pool_sc
+                self.k_scale_copies = [pool_sc]
         # row offsets now only count rows: rebase the raw-row prefix sums at 0
         if ring_rows > 0:
             self.kv_off = self.kv_off - self.kv_off[0]
@@ -181,8 +196,7 @@ class CsaLane(_Lane):
                                                           dtype=torch.float32, device=device)
         self.idx = torch.empty((self.B, self.T, self.k), dtype=torch.int32, device=device)
         nb = topk_workspace_bytes(self.B, self.T, self.max_entries, self.k)
-        # workspaces start zeroed (their leading counters must be zero on first use; each call
-        # leaves them zero)
+        # workspaces (their contents on entry do not matter; zeroed once at allocation)
         self.topk_ws = torch.zeros(max(nb, 16), dtype=torch.uint8, device=device)
         na = attn_workspace_bytes(self.B, self.T, self.H, lane.D, self.k + self.W)
         self.attn_ws = torch.zeros(max(na, 16), dtype=torch.uint8, device=device)

@@ -73,6 +73,11 @@ typedef enum {
  *     sits at pool row  block_table[b * max_blocks + e / block_entries] * block_entries
  *     + e % block_entries; the caller allocates the blocks (block_entries = lcm(m, m') / m
  *     covers lcm(m, m') raw tokens: 32 for CSA's m = 4 beside HCA's m' = 128, 1 for HCA);
+ *   - fp8 indexer keys keep their group scales with the blocks: scale_group must be a power
+ *     of two, scale_off is ignored (may be NULL), and the scale of the key at pool row r is
+ *     k_scale[r >> min(log2(scale_group), log2(block_entries))] -- one scale per group of a
+ *     block, or, when a group spans several blocks, one per block (the group's scale
+ *     repeated in each of its blocks); k_scale holds pool_entries >> that shift scales;
  *   - with ring_rows > 0, raw row r of sequence b (kv, z, and for overlapped compression
  *     kv_b, z_b) sits at ring row b * ring_rows + r % ring_rows: the state cache keeps the
  *     newest ring_rows rows of each sequence, which must hold every raw row a call reads.
@@ -169,7 +174,7 @@ int csl_compress_kv_overlap(const void* kv_a, const void* z_a, const void* kv_b,
  *           CSL_DTYPE_MXFP4 uint8 [E_tot, CI/2]: byte j holds code 2j in its low nibble and
  *           code 2j+1 in its high nibble (8-byte aligned)
  *   k_scale fp8: fp32 scales with scale_off int64 [B+1], scale_group >= 1 entries per
- *           scale, scales positive. MXFP4: uint8 E8M0 [E_tot, CI/32], one per block of 32
+ *           scale, scales positive (in a paged cache: per pool block, see csl_paged_cache). MXFP4: uint8 E8M0 [E_tot, CI/32], one per block of 32
  *           dims of a row, exponent bytes in [0, 254] (255, NaN, is a precondition
  *           violation); scale_off and scale_group are ignored. bf16: ignored (may be NULL).
  *   scores  fp32 [B, T, ld], ld >= max_entries

@@ -110,6 +110,15 @@ def test_indexer_validation(lib):
     assert f(*bad) == 3                       # top-k workspace too small
     bad = list(long_rows); bad[17] = FAKE; bad[18] = 1 << 30; bad[19] = 0
     assert f(*bad) == 2                       # topk_k out of range
+    # fp8 keys in a paged cache: scales per pool block (scale_off unused), power-of-two groups
+    import compressed_sparse_long_amd as csl
+    pc = csl._PagedCache(FAKE, 8, 32, 1 << 20, 0)
+    fp8 = list(args); fp8[3] = 2; fp8[4] = FAKE; fp8[11] = 0; fp8[20] = P(ctypes.addressof(pc))
+    assert f(*fp8) == 0, _err(lib)            # scale_off NULL accepted (T = 0: nothing enqueued)
+    bad = list(fp8); bad[6] = 48
+    assert f(*bad) == 1 and "power-of-two scale_group" in _err(lib)
+    bad = list(fp8); bad[20] = None
+    assert f(*bad) == 1 and "scale_off" in _err(lib)   # packed: scale_off is needed
 
 
 def test_topk_validation_and_workspace(lib):
@@ -255,6 +264,11 @@ def test_step_validation(lib):
     # overlapped compression also reads the series-b block before each entry: one more chunk
     assert paged_call(128, kv_b=FAKE, max_new_entries=30) == 0     # (30 + 2) * 4 - 1 = 127
     assert paged_call(128, kv_b=FAKE, max_new_entries=31) == 1     # (31 + 2) * 4 - 1 = 131
+    # fp8 indexer keys in the pool: group scales per block, so the group must be a power of two
+    assert paged_call(128, k_dtype=2, k_scale=FAKE, scale_group=64) == 0
+    assert paged_call(128, k_dtype=2, k_scale=FAKE, scale_group=16, scores=None, ld=0) == 0
+    assert paged_call(128, k_dtype=2, k_scale=FAKE, scale_group=96) == 1 and "power-of-two" in _err(lib)
+    assert call(k_dtype=2, k_scale=FAKE, B=0) == 1 and "scale_off" in _err(lib)  # packed: scale_off needed
 
 
 def test_static_step_rejects_workspaces_beyond_its_scratch(lib):

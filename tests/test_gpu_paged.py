@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _outputs(cl):
-    return {"scores": cl.scores.clone() if hasattr(cl, "scores") else None,
+    return {"scores": cl.scores.clone() if getattr(cl, "scores", None) is not None else None,
             "idx": cl.idx.clone() if hasattr(cl, "idx") else None,
             "out": cl.out.clone(), "lse": cl.lse.clone()}
 
@@ -37,13 +37,13 @@ def _newest_entries(cl):
     return cl.ckv[torch.tensor(rows, dtype=torch.int64, device=cl.ckv.device)].clone()
 
 
-def _run_both(lane, seed, fused, overlap=False, extras=False, ring_rows=256, order="random"):
+def _run_both(lane, seed, fused, overlap=False, extras=False, ring_rows=256, order="random", scoreless=False):
     from compressed_sparse_long_amd import lanes
     parts = ("kv", "z", "q", "qI", "kI", "w") + (("kv_b", "z_b") if overlap else ())
     inp = synth.generate(W.Workload("paged", seed, (lane,)), parts=parts)
     res = []
     for paged in (False, True):
-        (cl,) = lanes.build_lanes(inp)
+        (cl,) = lanes.build_lanes(inp, scoreless=scoreless)
         if extras:
             cl.sink = W.normal_f32(seed, W.S_EXTRA + 7, (lane.H,), std=2.0).cuda()
             cl.rope_dims = 64
@@ -94,6 +94,37 @@ def test_paged_csa_step_equals_packed(lengths, m, k, H, HI, fused, overlap, fp4)
     e0, E0 = 0, lane.entries[0]
     ref_s = csa.indexer(f64(li.qI[0, 0]), f64(li.w[0, 0]), keys[e0:e0 + E0])
     assert_rows_close(f64(go["scores"][0, 0, :E0]), ref_s, what="paged scores vs oracle")
+
+
+@pytest.mark.parametrize("lengths,T,k,group,scoreless", [
+    ((300000, 70000, 4000), 1, 1024, 64, False),   # groups of 64 over blocks of 32: one scale per block
+    ((300000, 70000, 4000), 1, 1024, 16, False),   # groups of 16: two scales per block
+    ((200000, 9000), 1, 512, 32, True),            # group = block; the indexer fused with top-k
+    ((40000, 30000, 9000, 5000), 32, 256, 64, True),  # 32 query rows: the prefill tiling, fused
+])
+def test_paged_fp8_keys_equal_packed(lengths, T, k, group, scoreless):
+    """fp8 e4m3 indexer keys in the block pool, their group scales kept per pool block: the
+    step equals the packed one (keys, scales through scale_off) bit for bit."""
+    print(f"paged fp8 keys lengths={lengths} T={T} k={k} group={group} scoreless={scoreless}", flush=True)
+    qp = tuple(n - T + 1 for n in lengths)
+    lane = W.Lane("csa", tuple(lengths), qp, T=T, H=64, m=4, k=k, HI=8, kI_fp8=True, scale_group=group)
+    inp, ((pk, po, pn), (gk, go, gn)) = _run_both(lane, 53 + group, True, scoreless=scoreless)
+    eb = gk.paged.block_entries
+    assert gk.k_scale.numel() == gk.pool_rows // min(group, eb)
+    assert torch.equal(pn, gn), "newest compressed entries differ"
+    if not scoreless:
+        for b in range(lane.B):
+            n = lane.entries[b]
+            assert torch.equal(po["scores"][b, :, :n], go["scores"][b, :, :n]), f"scores differ, b={b}"
+    assert torch.equal(po["idx"], go["idx"]), "selected ids differ"
+    assert torch.equal(po["out"], go["out"]) and torch.equal(po["lse"], go["lse"]), "attention differs"
+    if not scoreless:
+        # the packed scores of row 0 against the oracle's fp8 key decode
+        li = inp.lanes[0]
+        keys = pipeline.index_keys_f64(li.kI, li.k_scale, li.scale_off, li.ent_off, group)
+        n0 = csa.n_visible(lane.q_pos[0], 4, lane.entries[0])
+        ref_s = csa.indexer(f64(li.qI[0, 0]), f64(li.w[0, 0]), keys[:n0])
+        assert_rows_close(f64(go["scores"][0, 0, :n0]), ref_s, what="paged fp8 scores vs oracle")
 
 
 @pytest.mark.parametrize("kind", ["csa", "hca"])

@@ -70,6 +70,15 @@ def _oracle_attention(q_bt, kv, z, lane, b, p, sel, scale, entries_fn=None, extr
     return csa.attend_at(f64(q_bt), X, scale, p, sink, rope_dims, rope_base)
 
 
+def _entry_rows(cl, lane, b, ids):
+    """Cache rows of entries ``ids`` of sequence b: packed, or their pool rows when paged."""
+    ids = torch.from_numpy(np.asarray(ids, dtype=np.int64))
+    if cl.paged is None:
+        return lane.ent_off()[b] + ids
+    eb = cl.paged.block_entries
+    return cl.paged.block_table[b].cpu().to(torch.int64)[ids // eb] * eb + ids % eb
+
+
 def _check_compressed_sample(cl, kv, z, lane, nsample, seed, entries_fn=None):
     g = np.random.default_rng(seed)
     ckv = cl.ckv
@@ -82,7 +91,7 @@ def _check_compressed_sample(cl, kv, z, lane, nsample, seed, entries_fn=None):
         ids = np.unique(np.concatenate([[0, 1, E - 1], g.integers(0, E, size=min(nsample, E))]))
         ids = ids[ids < E]
         ref = entries_fn(lane.kv_off()[b], lane.m, ids)
-        got = f64(ckv[lane.ent_off()[b] + torch.from_numpy(ids).to(ckv.device)])
+        got = f64(ckv[_entry_rows(cl, lane, b, ids).to(ckv.device)])
         assert_rows_close(got, ref, bf16=True, what=f"compressed entries of seq {b}")
 
 
@@ -113,9 +122,10 @@ def _csa_keys(li):
                                    fp4=getattr(li.lane, "kI_fp4", False))
 
 
-def _run(lanes_mod, name, overlap=False, extras=None, fp4=False):
+def _run(lanes_mod, name, overlap=False, extras=None, fp4=False, paged=None):
     print(f"workload {name}{' (overlapped compression)' if overlap else ''}"
-          f"{' (sink, rope)' if extras else ''}{' (MXFP4 keys)' if fp4 else ''}: generating inputs", flush=True)
+          f"{' (sink, rope)' if extras else ''}{' (MXFP4 keys)' if fp4 else ''}"
+          f"{f' (paged, {paged} blocks)' if paged else ''}: generating inputs", flush=True)
     parts = ("kv", "z", "q", "qI", "kI", "w") + (("kv_b", "z_b") if overlap else ())
     wl = synth.WORKLOADS[name]
     if fp4:
@@ -129,6 +139,9 @@ def _run(lanes_mod, name, overlap=False, extras=None, fp4=False):
             cl.sink = extras[0].to(cl.q.device)
             cl.rope_dims, cl.rope_base = extras[1], extras[2]
         cl.compress_all()
+        if paged:
+            # entries, indexer keys (and fp8 scales) into the block pool, raw rows into rings
+            cl.paginate(ring_rows=256, seed=5, order=paged)
         cl.step()
     torch.cuda.synchronize()
     print(f"workload {name}: checking against the oracle", flush=True)
@@ -288,8 +301,14 @@ def test_csa_prefill_8k_on_128k_without_scores(lanes_mod):
         assert torch.equal(a, b), f"{what} differs without scores"
 
 
-def test_mixed_decode_b32(lanes_mod):
-    inp, (csa_l, hca_l) = _run(lanes_mod, "mixed_decode_b32")
+@pytest.mark.parametrize("paged", [None, "random"])
+def test_mixed_decode_b32(lanes_mod, paged):
+    """Config 5; paged: the same step with both lanes' caches in block pools (the CSA lane's
+    fp8 indexer keys with their group scales kept per pool block) and raw rows in rings."""
+    inp, (csa_l, hca_l) = _run(lanes_mod, "mixed_decode_b32", paged=paged)
+    if paged:
+        assert csa_l.paged is not None and hca_l.paged is not None
+        assert csa_l.k_scale.numel() == csa_l.pool_rows >> 5  # groups of 64 over blocks of 32: one per block
     li_c, li_h = inp.lanes
     keys = _csa_keys(li_c)
     for b in range(li_c.lane.B):
