@@ -14,7 +14,7 @@ import torch
 
 __all__ = [
     "compress_kv", "compress_kv_overlap", "indexer_scores", "indexer_topk", "indexer_topk_max_k", "topk_select",
-    "sparse_attn_decode", "hca_attn_decode", "csa_decode_step", "csa_decode_step_static",
+    "sparse_attn_decode", "hca_attn_decode", "csa_decode_step", "csa_decode_step_static", "hca_decode_step",
     "topk_workspace_bytes", "attn_workspace_bytes", "PagedCache", "version", "LIB_PATH",
     "EXPORTS", "CslError",
 ]
@@ -27,6 +27,7 @@ EXPORTS = [
     "csl_indexer_topk_max_k", "csl_indexer_topk",
     "csl_topk_workspace_bytes", "csl_topk_select", "csl_attn_workspace_bytes",
     "csl_sparse_attn_decode", "csl_hca_attn_decode", "csl_csa_decode_step", "csl_csa_decode_step_static",
+    "csl_hca_decode_step",
 ]
 
 _P, _I, _L, _F, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -45,6 +46,19 @@ class _CsaStep(ctypes.Structure):
         ("attn_ws_bytes", _S),
         ("q_pos", _P), ("m", _I), ("B", _I), ("T", _I), ("max_entries", _L),
         ("kv_b", _P), ("z_b", _P),
+        ("sink", _P), ("rope_dims", _I), ("rope_base", _F),
+        ("paged", _P),
+    ]
+
+
+class _HcaStep(ctypes.Structure):
+    """csl_hca_step (include/csl.h), field for field."""
+    _fields_ = [
+        ("kv", _P), ("z", _P), ("kv_off", _P), ("ent_off", _P), ("first_entry", _P), ("max_new_entries", _L),
+        ("ckv", _P),
+        ("q", _P), ("H", _I), ("n_win", _I), ("scale", _F), ("out", _P), ("lse", _P), ("attn_ws", _P),
+        ("attn_ws_bytes", _S),
+        ("q_pos", _P), ("m", _I), ("B", _I), ("T", _I), ("max_entries", _L),
         ("sink", _P), ("rope_dims", _I), ("rope_base", _F),
         ("paged", _P),
     ]
@@ -89,6 +103,7 @@ def _load() -> ctypes.CDLL:
                                     ctypes.POINTER(_AttnExtras), P, P]),
         "csl_csa_decode_step": (I, [ctypes.POINTER(_CsaStep), P]),
         "csl_csa_decode_step_static": (I, [ctypes.POINTER(_CsaStep), P]),
+        "csl_hca_decode_step": (I, [ctypes.POINTER(_HcaStep), P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -366,6 +381,32 @@ def csa_decode_step(kv, z, kv_off, ent_off, first_entry, max_new_entries: int, c
         q_pos=_ptr(q_pos, "q_pos", _I64), m=int(m), B=B, T=T, max_entries=int(max_entries))
     fn = _lib.csl_csa_decode_step_static if static_scratch else _lib.csl_csa_decode_step
     _check(fn(ctypes.byref(s), _stream(stream)))
+    return out
+
+
+def hca_decode_step(kv, z, kv_off, ent_off, first_entry, max_new_entries: int, ckv, q, n_win: int, out, q_pos,
+                    m: int, max_entries: int, lse=None, scale: float | None = None, attn_ws=None, sink=None,
+                    rope_dims: int = 0, rope_base: float = 10000.0, paged=None, stream=None):
+    """One whole HCA step (compress_kv of the newest entries into ckv, then hca_attn_decode) in
+    one C call, the compression riding in the attention launch where the head count allows;
+    see csl.h."""
+    B, T, H, D = q.shape
+    if scale is None:
+        scale = D ** -0.5
+    attn_ws, awb = _attn_ws(attn_ws, B, T, H, D, max_entries + n_win, q.device)
+    pstruct = None if paged is None else paged._struct()  # kept alive across the call
+    s = _HcaStep(
+        kv=_ptr(kv, "kv", _BF16), z=_ptr(z, "z", _BF16), kv_off=_ptr(kv_off, "kv_off", _I64),
+        ent_off=_ptr(ent_off, "ent_off", _I64), first_entry=_ptr(first_entry, "first_entry", _I64),
+        max_new_entries=int(max_new_entries), ckv=_ptr(ckv, "ckv", _BF16),
+        q=_ptr(q, "q", _BF16), H=H, n_win=int(n_win), scale=float(scale), out=_ptr(out, "out", _F32),
+        lse=_ptr(lse, "lse", _F32), attn_ws=_ptr(attn_ws, "attn_ws"), attn_ws_bytes=awb,
+        q_pos=_ptr(q_pos, "q_pos", _I64), m=int(m), B=B, T=T, max_entries=int(max_entries),
+        sink=_ptr(sink, "sink", _F32), rope_dims=int(rope_dims), rope_base=float(rope_base),
+        paged=None if paged is None else ctypes.addressof(pstruct))
+    if D != 128:
+        raise ValueError("hca_decode_step: head dim must be 128")
+    _check(_lib.csl_hca_decode_step(ctypes.byref(s), _stream(stream)))
     return out
 
 

@@ -20,7 +20,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libcsl.so")
-SOURCES = ["api.cpp", "compress.hip", "indexer.hip", "topk.hip", "attention.hip"]
+SOURCES = ["api.cpp", "compress.hip", "indexer.hip", "topk.hip", "attention.hip", "attention_fused.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -31,7 +31,7 @@ HIPCC_FLAGS = [
 ]
 # per-file extras: the attention kernels keep their MFMA accumulators in ordinary VGPRs, which
 # saves the per-tile copies between accumulation and arithmetic registers
-FILE_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+FILE_FLAGS = {src: ["-mllvm", "-amdgpu-mfma-vgpr-form=1"] for src in ("attention.hip", "attention_fused.hip")}
 
 
 def hipcc() -> str:

@@ -417,6 +417,61 @@ int csl_hca_attn_decode(const void* q, const void* ckv, const void* kv, const in
                     "hca_attn_decode launch");
 }
 
+int csl_hca_decode_step(const csl_hca_step* s, void* stream) {
+  if (!s) return fail(CSL_ERR_INVALID, "hca_decode_step: null step");
+  int st = check_compress(s->kv, s->z, s->kv_off, s->ent_off, s->B, 128, s->m, s->max_new_entries, s->ckv,
+                          CSL_DTYPE_BF16, "hca_decode_step");
+  if (st != CSL_OK) return st;
+  csl::AttnExtras ex;
+  st = check_extras("hca_decode_step", s->sink, s->rope_dims, s->rope_base, ex);
+  if (st != CSL_OK) return st;
+  if (s->max_entries < 0) return fail(CSL_ERR_INVALID, "hca_decode_step: max_entries must be >= 0");
+  const int64_t max_keys = s->max_entries + s->n_win;
+  st = check_attn("hca_decode_step", s->q, s->ckv, s->kv, s->kv_off, s->ent_off, s->q_pos, s->n_win, s->B, s->T, s->H,
+                  128, s->scale, s->out, s->attn_ws, s->attn_ws_bytes, max_keys);
+  if (st != CSL_OK && st != -1) return st;
+  csl::PagedView pv;
+  const csl::PagedView* pvp = nullptr;
+  if (s->paged) {
+    st = check_paged("hca_decode_step", s->paged, s->B, pv);
+    if (st != CSL_OK) return st;
+    st = check_ring("hca_decode_step", s->paged, s->n_win, s->T, s->m, s->max_new_entries, false);
+    if (st != CSL_OK) return st;
+    pvp = &pv;
+  }
+  const hipStream_t hs = as_stream(stream);
+  const bool compress = s->B > 0 && s->max_new_entries > 0;
+  const bool attend = s->B > 0 && s->T > 0;
+  if (!attend) {  // no query rows: the compression alone
+    if (!compress) return ok();
+    return hip_status(csl::launch_compress(s->kv, s->z, s->kv_off, s->ent_off, s->first_entry, s->B, 128, s->m,
+                                           s->max_new_entries, s->ckv, true, hs, pvp),
+                      "hca_decode_step launch");
+  }
+  if (compress && csl::attention_carries_job(s->B, s->T, s->H, max_keys, s->max_new_entries)) {
+    // the compression rides in spare workgroups of the attention launch
+    csl::HcaJob job;
+    job.kv = static_cast<const uint16_t*>(s->kv);
+    job.z = static_cast<const uint16_t*>(s->z);
+    job.first_entry = s->first_entry;
+    job.max_new = s->max_new_entries;
+    job.ckv = static_cast<uint16_t*>(s->ckv);
+    return hip_status(csl::launch_attention(false, s->q, s->ckv, nullptr, 0, s->kv, s->kv_off, s->ent_off, s->q_pos,
+                                            s->m, s->n_win, s->B, s->T, s->H, s->scale, s->max_entries, max_keys,
+                                            s->out, s->lse, s->attn_ws, ex, hs, pvp, &job),
+                      "hca_decode_step launch");
+  }
+  hipError_t e = hipSuccess;
+  if (compress)
+    e = csl::launch_compress(s->kv, s->z, s->kv_off, s->ent_off, s->first_entry, s->B, 128, s->m, s->max_new_entries,
+                             s->ckv, true, hs, pvp);
+  if (e != hipSuccess) return hip_status(e, "hca_decode_step launch");
+  return hip_status(csl::launch_attention(false, s->q, s->ckv, nullptr, 0, s->kv, s->kv_off, s->ent_off, s->q_pos,
+                                          s->m, s->n_win, s->B, s->T, s->H, s->scale, s->max_entries, max_keys, s->out,
+                                          s->lse, s->attn_ws, ex, hs, pvp),
+                    "hca_decode_step launch");
+}
+
 int csl_csa_decode_step(const csl_csa_step* s, void* stream) {
   if (!s) return fail(CSL_ERR_INVALID, "csa_decode_step: null argument");
   // every part is validated before anything is enqueued

@@ -26,17 +26,38 @@
 
 namespace csl {
 
+// Where a finished entry goes: row orow of out (bf16 or fp32), 8 dims per thread.
+template <bool OUT_BF16>
+struct StoreEntry {
+  void* out;
+  int D;
+  __device__ __forceinline__ void operator()(int64_t /*i*/, int64_t orow, int dg, const float (&o)[8]) const {
+    if (OUT_BF16) {
+      u32x4 v;
+      v.x = pack_bf16x2(o[0], o[1]);
+      v.y = pack_bf16x2(o[2], o[3]);
+      v.z = pack_bf16x2(o[4], o[5]);
+      v.w = pack_bf16x2(o[6], o[7]);
+      *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + orow * D + dg * 8) = v;
+    } else {
+      float* op = reinterpret_cast<float*>(out) + orow * D + dg * 8;
+      *reinterpret_cast<float4*>(op) = make_float4(o[0], o[1], o[2], o[3]);
+      *reinterpret_cast<float4*>(op + 4) = make_float4(o[4], o[5], o[6], o[7]);
+    }
+  }
+};
+
 // One workgroup of NT threads compresses the NT / (TPE * RS * RSX) entries first_entry[b] +
-// blk * that .. of sequence b (entries past max_new or past the sequence end are skipped).
-// Each thread loads ROWS of its rows at a time. With RSX > 1 every thread of the workgroup
-// must call this (it holds a workgroup barrier).
-template <int NT, int TPE, int RS, bool HAS_Z, bool OUT_BF16, int ROWS = 4, int RSX = 1, bool DUAL = false>
-__device__ __forceinline__ void compress_block(
+// blk * that .. of sequence b (entries past max_new or past the sequence end are skipped) and
+// hands each finished entry i (8 dims per thread dg, its cache row orow) to store. Each thread
+// loads ROWS of its rows at a time. With RSX > 1 every thread of the workgroup must call this
+// (it holds a workgroup barrier).
+template <int NT, int TPE, int RS, bool HAS_Z, int ROWS, int RSX, bool DUAL, class Store>
+__device__ __forceinline__ void compress_block_to(
     const uint16_t* __restrict__ kv, const uint16_t* __restrict__ z,
     const int64_t* __restrict__ kv_off, const int64_t* __restrict__ ent_off,
-    const int64_t* __restrict__ first_entry, int D, int m, int64_t max_new, void* __restrict__ out, int b,
-    int64_t blk, const uint16_t* __restrict__ kv_b = nullptr, const uint16_t* __restrict__ z_b = nullptr,
-    PagedView pg = PagedView{}) {
+    const int64_t* __restrict__ first_entry, int D, int m, int64_t max_new, const Store& store, int b,
+    int64_t blk, const uint16_t* __restrict__ kv_b, const uint16_t* __restrict__ z_b, PagedView pg) {
   static_assert(TPE * RS <= kWave, "in-wave row-splits merge by shuffles");
   static_assert(RSX == 1 || TPE * RS == kWave, "cross-wave splits take whole waves");
   constexpr int EPB = NT / (TPE * RS * RSX);  // entries per block
@@ -56,6 +77,15 @@ __device__ __forceinline__ void compress_block(
   const int64_t rel = blk * EPB + el;
   const int64_t i = first + rel;
   const bool valid = (rel < max_new) && (i < n_ent);
+  // the entry's cache row, ent_off[b] + i or its pool row in the paged layout, loaded with the
+  // row offsets so that the store does not wait for another round trip
+  int64_t orow = ent_off[b] + i;
+  if (pg.table) {
+    int64_t j = i >> pg.eb_shift;
+    j = j < pg.max_blocks ? j : pg.max_blocks - 1;
+    j = j > 0 ? j : 0;
+    orow = ((int64_t)pg.table[(int64_t)b * pg.max_blocks + j] << pg.eb_shift) | (i & ((1 << pg.eb_shift) - 1));
+  }
 
   float mu[8], s[8], acc[8];
 #pragma unroll
@@ -196,29 +226,23 @@ __device__ __forceinline__ void compress_block(
   }
 
   if (valid && rs == 0) {
-    // entry i of sequence b: row ent_off[b] + i, or its pool row in the paged layout
-    int64_t orow = ent_off[b] + i;
-    if (pg.table) {
-      int64_t j = i >> pg.eb_shift;
-      j = j < pg.max_blocks ? j : pg.max_blocks - 1;
-      orow = ((int64_t)pg.table[(int64_t)b * pg.max_blocks + j] << pg.eb_shift) | (i & ((1 << pg.eb_shift) - 1));
-    }
     float o[8];
 #pragma unroll
     for (int d = 0; d < 8; ++d) o[d] = acc[d] / s[d];
-    if (OUT_BF16) {
-      u32x4 v;
-      v.x = pack_bf16x2(o[0], o[1]);
-      v.y = pack_bf16x2(o[2], o[3]);
-      v.z = pack_bf16x2(o[4], o[5]);
-      v.w = pack_bf16x2(o[6], o[7]);
-      *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + orow * D + dg * 8) = v;
-    } else {
-      float* op = reinterpret_cast<float*>(out) + orow * D + dg * 8;
-      *reinterpret_cast<float4*>(op) = make_float4(o[0], o[1], o[2], o[3]);
-      *reinterpret_cast<float4*>(op + 4) = make_float4(o[4], o[5], o[6], o[7]);
-    }
+    store(i, orow, dg, o);
   }
+}
+
+// compress_block_to with the entries written to their rows of out (bf16 or fp32)
+template <int NT, int TPE, int RS, bool HAS_Z, bool OUT_BF16, int ROWS = 4, int RSX = 1, bool DUAL = false>
+__device__ __forceinline__ void compress_block(
+    const uint16_t* __restrict__ kv, const uint16_t* __restrict__ z,
+    const int64_t* __restrict__ kv_off, const int64_t* __restrict__ ent_off,
+    const int64_t* __restrict__ first_entry, int D, int m, int64_t max_new, void* __restrict__ out, int b,
+    int64_t blk, const uint16_t* __restrict__ kv_b = nullptr, const uint16_t* __restrict__ z_b = nullptr,
+    PagedView pg = PagedView{}) {
+  compress_block_to<NT, TPE, RS, HAS_Z, ROWS, RSX, DUAL>(kv, z, kv_off, ent_off, first_entry, D, m, max_new,
+                                                         StoreEntry<OUT_BF16>{out, D}, b, blk, kv_b, z_b, pg);
 }
 
 }  // namespace csl

@@ -75,9 +75,7 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int64_t* ent_off, 
 struct AttnPlan {
   int nsplit;
   int keys_per_split;
-  int nsub;    // tiles one workgroup multiplies at once (its waves in nsub groups)
-  int hsplit;  // workgroups per (row, split), each taking H / hsplit heads
-  bool head_split;  // 16 heads per workgroup, whose waves each multiply one tile of a round
+  int nsub;  // tiles one workgroup multiplies at once (its waves in nsub groups)
 };
 // Per-query extras of the core attention: the attention sink (per-head logits added to the
 // softmax denominator) and partial RoPE (the query's last rope_dims dims rotated at its
@@ -87,12 +85,25 @@ struct AttnExtras {
   int rope_dims = 0;            // 0 or a multiple of 32 up to 128
   double rope_theta1 = 1.0;     // base^(-2/rope_dims): pair j turns by p * rope_theta1^j
 };
+// The newest-chunk compression of an HCA step (bf16 entries, D = 128), run by spare
+// workgroups of the step's attention launch: entries first_entry[b] .. + max_new of each
+// sequence, pooled from kv / z (z nullable) into the cache. Attention workgroups whose key
+// range holds such an entry pool it themselves instead of reading the cache.
+struct HcaJob {
+  const uint16_t* kv = nullptr;
+  const uint16_t* z = nullptr;
+  const int64_t* first_entry = nullptr;
+  int64_t max_new = 0;
+  uint16_t* ckv = nullptr;
+};
 AttnPlan attn_plan(int B, int T, int H, int64_t max_keys);
 size_t attn_workspace_bytes(int B, int T, int H, int64_t max_keys);
 hipError_t launch_attention(bool sparse, const void* q, const void* ckv, const int32_t* idx, int k, const void* kv,
                             const int64_t* kv_off, const int64_t* ent_off, const int64_t* q_pos, int m, int n_win,
                             int B, int T, int H, float scale, int64_t max_entries, int64_t max_keys, float* out,
                             float* lse, void* ws, const AttnExtras& ex, hipStream_t stream,
-                            const PagedView* paged = nullptr);
+                            const PagedView* paged = nullptr, const HcaJob* job = nullptr);
+// whether launch_attention can carry an HcaJob for these shapes
+bool attention_carries_job(int B, int T, int H, int64_t max_keys, int64_t max_new);
 
 }  // namespace csl

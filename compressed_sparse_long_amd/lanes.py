@@ -15,7 +15,7 @@ import math
 
 import torch
 
-from . import (PagedCache, attn_workspace_bytes, compress_kv, compress_kv_overlap, csa_decode_step, hca_attn_decode,
+from . import (PagedCache, attn_workspace_bytes, compress_kv, compress_kv_overlap, csa_decode_step, hca_attn_decode, hca_decode_step,
                indexer_scores, indexer_topk, sparse_attn_decode,
                topk_select, topk_workspace_bytes)
 
@@ -282,9 +282,18 @@ class HcaLane(_Lane):
                         max_entries=self.max_entries, ws=self.attn_ws, sink=self.sink, rope_dims=self.rope_dims,
                         rope_base=self.rope_base, paged=self.paged)
 
-    def step(self, r: int = 0):
-        self.compress_new(r)
-        self.attend(r)
+    def step(self, r: int = 0, fused: bool = True):
+        """One decode step on rotated copy r: one hca_decode_step call (the newest-entry
+        compression inside the attention launch), or (fused=False) compress_kv then
+        hca_attn_decode."""
+        if not fused:
+            self.compress_new(r)
+            self.attend(r)
+            return
+        hca_decode_step(self.kv, self.z, self.kv_off, self.ent_off, self.first_new, self.n_new,
+                        self.ckv_copies[r % len(self.ckv_copies)], self.q, self.W, self.out, self.q_pos, self.m,
+                        self.max_entries, lse=self.lse, scale=self.scale, attn_ws=self.attn_ws, sink=self.sink,
+                        rope_dims=self.rope_dims, rope_base=self.rope_base, paged=self.paged)
 
 
 def build_lanes(inp, device="cuda", scoreless: bool = False):

@@ -316,9 +316,10 @@ int csl_hca_attn_decode(const void* q, const void* ckv, const void* kv, const in
  *     csl_indexer_scores(q_idx, w, k_idx, ..., scores, ld, topk_ws, topk_ws_bytes, k)
  *     csl_topk_select(scores, ..., k, idx, topk_ws, topk_ws_bytes, prepared = 1)
  *     csl_sparse_attn_decode(q, ckv, idx, k, kv, ..., n_win, ..., out, lse, attn_ws)
- * in that order on one stream, with the same outputs (ckv rows, scores, idx, out, lse). The
- * calls' own argument rules apply to the fields below, and everything is validated before
- * anything is enqueued. Where the shapes allow (D == 128, m <= 8, the decode tiling of the
+ * in that order on one stream, with the same outputs (ckv rows, scores, idx, out, lse) up to
+ * the rounding order of the pooled sums where the compression runs inside the indexer launch
+ * (one bf16 unit in a compressed entry). The calls' own argument rules apply to the fields
+ * below, and everything is validated before anything is enqueued. Where the shapes allow (D == 128, m <= 8, the decode tiling of the
  * indexer), the compression runs in spare workgroups of the indexer launch instead of a
  * launch of its own; it never reads what the indexer writes, and the attention runs after
  * both. With kv_b (and z_b when z is given) set, the compression is csl_compress_kv_overlap
@@ -381,6 +382,51 @@ typedef struct csl_csa_step {
 } csl_csa_step;
 
 int csl_csa_decode_step(const csl_csa_step* s, void* stream);
+
+/*
+ * hca_decode_step -- one whole HCA step of one layer ([P1] section 5.1; [P2] "Heavily
+ * Compressed Attention", HCA "How it works"): exactly
+ *     csl_compress_kv(kv, z, kv_off, ent_off, first_entry, B, 128, m, max_new_entries, ckv, BF16)
+ *     csl_hca_attn_decode(q, ckv, kv, kv_off, ent_off, q_pos, m, n_win, B, T, H, 128, ...)
+ * in that order on one stream, with the same outputs up to the rounding order of the pooled
+ * sums (one bf16 unit in a compressed entry, and what follows from it in out and lse). For H
+ * in {16, 32, 64, 128} (and B * (T + max_new_entries) <= 65535) both run in one launch: spare
+ * workgroups pool the new entries into the cache while the others attend, and an attention
+ * workgroup whose key range holds an entry being rewritten pools that entry itself from the
+ * raw rows instead of reading the cache. In a decode step no query sees the entry its own
+ * token completes (a query sees only entries before its own block), so the compression then
+ * costs the attention nothing. Other head counts run the two calls one after the other. All
+ * fields follow the two calls' argument rules (D = 128, bf16 cache) and are validated before
+ * anything is enqueued.
+ */
+typedef struct csl_hca_step {
+  const void* kv;             /* bf16 [N_tot, 128] raw K = V rows */
+  const void* z;              /* bf16 [N_tot, 128] compression logits, or NULL (uniform) */
+  const int64_t* kv_off;      /* device [B+1] */
+  const int64_t* ent_off;     /* device [B+1] */
+  const int64_t* first_entry; /* device [B] or NULL (0): first entry compressed */
+  int64_t max_new_entries;    /* entries compressed per sequence, >= 0 */
+  void* ckv;                  /* bf16 [E_tot, 128] compressed cache: written, then attended */
+  const void* q;              /* bf16 [B, T, H, 128] */
+  int H;
+  int n_win;
+  float scale;
+  float* out;                 /* fp32 [B, T, H, 128] */
+  float* lse;                 /* fp32 [B, T, H] or NULL */
+  void* attn_ws;              /* csl_attn_workspace_bytes(B, T, H, 128, max_entries + n_win) bytes */
+  size_t attn_ws_bytes;
+  const int64_t* q_pos;       /* device [B] */
+  int m;
+  int B;
+  int T;
+  int64_t max_entries;
+  const float* sink;          /* attention extras as csl_attn_extras: sink NULL, rope_dims 0: none */
+  int rope_dims;
+  float rope_base;
+  const csl_paged_cache* paged; /* NULL: packed */
+} csl_hca_step;
+
+int csl_hca_decode_step(const csl_hca_step* s, void* stream);
 
 /*
  * csa_decode_step_static -- csl_csa_decode_step for callers that cannot allocate device

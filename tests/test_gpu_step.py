@@ -196,3 +196,84 @@ def test_csa_step_without_scores_matches_step_with_scores(lengths, q_pos, T, k, 
         res.append((cl.ckv.clone(), cl.idx.clone(), cl.out.clone(), cl.lse.clone()))
     for a, b, what in zip(res[0], res[1], ("ckv", "idx", "out", "lse")):
         assert torch.equal(a, b), f"{what} differs without scores"
+
+
+# ------------------------------------------------------------------ the HCA step
+
+def _hca_step_vs_calls(lengths, q_pos, m, H, T, first, max_new, has_z=True, extras=False):
+    """csl_hca_decode_step against compress_kv then hca_attn_decode on the same inputs and the
+    same starting cache, whose entries [first_b, first_b + max_new) are set to a sentinel first:
+    both paths must write them, and no attention may read the sentinel (an attention workgroup
+    whose keys include an entry being rewritten pools it itself)."""
+    import compressed_sparse_long_amd as csl
+    from oracle import csa, pipeline
+    from tests._parity import assert_attn_close, assert_rows_close, f64
+    print(f"hca step lengths={lengths} q_pos={q_pos} m={m} H={H} T={T} first={first} max_new={max_new} "
+          f"z={has_z} extras={extras}", flush=True)
+    seed = 91 + m + H + T
+    B = len(lengths)
+    kv_off = torch.tensor([0] + list(np.cumsum(lengths)), dtype=torch.int64)
+    E = [n // m for n in lengths]
+    ent_off = torch.tensor([0] + list(np.cumsum(E)), dtype=torch.int64)
+    kv = W.normal_bf16(seed, W.S_EXTRA + 1, (max(int(kv_off[-1]), 1), 128))
+    z = W.normal_bf16(seed, W.S_EXTRA + 2, (max(int(kv_off[-1]), 1), 128)) if has_z else None
+    q = W.normal_bf16(seed, W.S_EXTRA + 3, (B, T, H, 128))
+    sink = W.normal_f32(seed, W.S_EXTRA + 4, (H,), std=2.0).cuda() if extras else None
+    rope = 64 if extras else 0
+    d_kv, d_z, d_q = kv.cuda(), (z.cuda() if has_z else None), q.cuda()
+    d_kvo, d_eo = kv_off.cuda(), ent_off.cuda()
+    qp = torch.tensor(q_pos, dtype=torch.int64).cuda()
+    fe = torch.tensor(first, dtype=torch.int64).cuda()
+    max_e = max(E + [1])
+    ckv0 = torch.empty((max(int(ent_off[-1]), 1), 128), dtype=torch.bfloat16, device="cuda")
+    csl.compress_kv(d_kv, d_z, d_kvo, d_eo, m, ckv0, max_new_entries=max_e)
+    newest = [(int(ent_off[b]) + first[b], int(ent_off[b]) + min(E[b], first[b] + max_new)) for b in range(B)]
+    for lo, hi in newest:
+        ckv0[lo:hi] = 7.0
+    res = []
+    for fused in (False, True):
+        ckv = ckv0.clone()
+        out = torch.full((B, T, H, 128), float("nan"), device="cuda")
+        lse = torch.full((B, T, H), float("nan"), device="cuda")
+        if fused:
+            csl.hca_decode_step(d_kv, d_z, d_kvo, d_eo, fe, max_new, ckv, d_q, 128, out, qp, m, max_e, lse=lse,
+                                sink=sink, rope_dims=rope)
+        else:
+            csl.compress_kv(d_kv, d_z, d_kvo, d_eo, m, ckv, first_entry=fe, max_new_entries=max_new)
+            csl.hca_attn_decode(d_q, ckv, d_kv, d_kvo, d_eo, qp, m, 128, out, lse=lse, max_entries=max_e, sink=sink,
+                                rope_dims=rope)
+        torch.cuda.synchronize()
+        res.append((ckv, out, lse))
+    (rc, ro, rl), (gc, go, gl) = res
+    for lo, hi in newest:
+        assert not torch.any(gc[lo:hi] == 7.0), "the step left new entries uncompressed"
+    # the two compression layouts may round the pooled sums in another order: one bf16 unit
+    torch.testing.assert_close(gc.float(), rc.float(), rtol=8e-3, atol=1e-3)
+    torch.testing.assert_close(go, ro, rtol=0, atol=2e-3)
+    torch.testing.assert_close(gl, rl, rtol=0, atol=2e-3)
+    # and the fused step against the oracle: its entries against the oracle's pooling, its
+    # attention against the oracle's over those entries
+    ref_c = pipeline.compress_lane(kv, z, kv_off, m)
+    for b in range(B):
+        lo, hi = int(ent_off[b]), int(ent_off[b + 1])
+        if hi > lo:
+            assert_rows_close(f64(gc[lo:hi]), ref_c[lo:hi], bf16=True, what=f"entries of seq {b}")
+    oo, ol = pipeline.hca_attn_lane(q, gc.cpu(), kv, kv_off, ent_off, torch.tensor(q_pos), m, 128, 128 ** -0.5,
+                                    sink=None if sink is None else sink.cpu().numpy(), rope_dims=rope)
+    assert_attn_close(f64(go), oo, "out")
+    assert_attn_close(f64(gl), ol, "lse")
+
+
+@pytest.mark.parametrize("lengths,q_pos,m,H,T,first,max_new,has_z,extras", [
+    # decode: each sequence's newest complete entry, which its query sees only where the length
+    # is not a multiple of m (the 200-row and 70000-row sequences)
+    ((131072, 131072, 9000, 200), (131071, 131071, 8999, 199), 128, 64, 1, (1023, 1023, 69, 0), 1, True, False),
+    ((131072, 70000), (131071, 69999), 128, 16, 1, (1023, 545), 1, False, True),
+    ((40000, 9000), (39999, 8999), 4, 32, 1, (9999, 2249), 1, True, False),
+    # entries the queries do see: the attention workgroups pool them themselves
+    ((131072, 9000), (131072, 9000), 128, 64, 1, (1021, 67), 3, True, True),
+    ((20000, 3000), (20000, 3000), 4, 128, 1, (4900, 700), 60, True, False),
+    ((20000,), (19000,), 4, 16, 40, (4700,), 70, True, False),      # 40 positions, the prefetching tile loop
+])
+def test_hca_decode_step_matches_separate_calls(lengths, q_pos, m, H, T, first, max_new, has_z, extras):
+    _hca_step_vs_calls(lengths, q_pos, m, H, T, first, max_new, has_z, extras)
