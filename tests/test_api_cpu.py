@@ -271,6 +271,35 @@ def test_step_validation(lib):
     assert call(k_dtype=2, k_scale=FAKE, B=0) == 1 and "scale_off" in _err(lib)  # packed: scale_off needed
 
 
+def test_hca_step_validation(lib):
+    import compressed_sparse_long_amd as csl
+    f = lib.csl_hca_decode_step
+    f.argtypes = [ctypes.POINTER(csl._HcaStep), P]
+    f.restype = ctypes.c_int
+    assert f(None, None) == 1
+    base = dict(kv=FAKE, kv_off=FAKE, ent_off=FAKE, max_new_entries=1, ckv=FAKE, q=FAKE, H=64, n_win=128,
+                scale=0.088, out=FAKE, attn_ws=FAKE, attn_ws_bytes=1 << 30, q_pos=FAKE, m=128, B=8, T=1,
+                max_entries=1024)
+
+    def call(**over):
+        s = csl._HcaStep(**{**base, **over})
+        return f(ctypes.byref(s), None)
+    assert call(m=0) == 1                          # compression ratio
+    assert call(H=24) == 2                         # heads not a multiple of 16
+    assert call(ckv=None) == 1
+    assert call(kv=P((1 << 20) + 2)) == 1          # misaligned raw rows
+    assert call(scale=0.0) == 1 and "scale" in _err(lib)
+    assert call(max_entries=-1) == 1
+    assert call(rope_dims=64, rope_base=0.5) == 1
+    assert call(attn_ws=None, attn_ws_bytes=0) == 3  # 9 splits need a workspace
+    assert call(B=0) == 0 and _err(lib) == ""      # nothing to do
+    # a paged cache: the ring holds the window and the chunk being compressed (2m - 1 rows)
+    pc = csl._PagedCache(FAKE, 8, 1, 1 << 20, 128)
+    assert call(paged=P(ctypes.addressof(pc)), B=0) == 1 and "ring_rows" in _err(lib)
+    pc = csl._PagedCache(FAKE, 8, 1, 1 << 20, 256)
+    assert call(paged=P(ctypes.addressof(pc)), B=0) == 0
+
+
 def test_static_step_rejects_workspaces_beyond_its_scratch(lib):
     """csl_csa_decode_step_static sizes the step's workspaces on the host and refuses, before
     touching a device, a step that needs more than its static scratch array."""
