@@ -296,15 +296,16 @@ constexpr int kFusedU = 2;                               // key tiles of 16 per 
 constexpr int kFusedChunk = kFusedWaves * kFusedU * 16;  // keys per chunk
 constexpr int kFusedCuLds = 160 * 1024;                  // LDS of one gfx950 compute unit
 
-template <int HI>
+template <int HI, bool WIDE = false>
 struct FusedShape {
   static constexpr int QPB = 16 / HI;
   static constexpr int QR = QPB > 8 ? QPB : 8;  // query rows per workgroup: 8 (16 at HI = 1)
   static constexpr int NB = QR / QPB;           // A tiles (all waves hold all of them)
   // two workgroups per compute unit, so each wave has three others on its SIMD to hide
   // latency behind (one at HI = 1, whose A tile alone spans 16 rows, and at HI = 16, whose
-  // 8 A tiles need more registers than 4 waves per SIMD leave)
-  static constexpr int WG_PER_CU = (QR == 8 && NB <= 4) ? 2 : 1;
+  // 8 A tiles need more registers than 4 waves per SIMD leave). WIDE: one workgroup per CU
+  // and so twice the candidate slots, for k beyond what two workgroups' buffers hold
+  static constexpr int WG_PER_CU = (!WIDE && QR == 8 && NB <= 4) ? 2 : 1;
   static constexpr int WAVES_PER_SIMD = WG_PER_CU * kFusedWaves / 4;
   // candidate slots per row: the workgroup's LDS share left beside the two staging buffers
   static constexpr int CAP = (kFusedCuLds / WG_PER_CU - 2 * QR * kFusedChunk * 4 - 256) / (8 * QR) / 64 * 64;
@@ -406,13 +407,13 @@ __device__ __forceinline__ uint32_t cut_to_k(uint64_t* row, uint32_t& n, int k) 
   return wave_min_u32(bar);  // the smallest key kept: at least k keys reach it
 }
 
-template <int HI, int KT, bool PAGED>
-__global__ __launch_bounds__(kFusedWaves * kWave, FusedShape<HI>::WAVES_PER_SIMD) void indexer_topk_kernel(
+template <int HI, int KT, bool PAGED, bool WIDE>
+__global__ __launch_bounds__(kFusedWaves * kWave, (FusedShape<HI, WIDE>::WAVES_PER_SIMD)) void indexer_topk_kernel(
     const uint16_t* __restrict__ qI, const float* __restrict__ w, const void* __restrict__ kI,
     const void* __restrict__ k_scale_v, const int64_t* __restrict__ scale_off, int scale_group,
     const int64_t* __restrict__ ent_off, const int64_t* __restrict__ q_pos, int m, int T,
     int64_t max_entries, int k, int32_t* __restrict__ idx, PagedView pg) {
-  using FS = FusedShape<HI>;
+  using FS = FusedShape<HI, WIDE>;
   constexpr int QPB = FS::QPB, NB = FS::NB, QR = FS::QR, CAP = FS::CAP;
   constexpr int U = kFusedU, CH = kFusedChunk;
   constexpr int RPW = QR / kFusedWaves;  // rows each wave files (1, or 2 at HI = 1)
@@ -475,119 +476,160 @@ __global__ __launch_bounds__(kFusedWaves * kWave, FusedShape<HI>::WAVES_PER_SIMD
   const int t_last = min(t0 + QR, T) - 1;
   const int64_t n_max = t_last >= t0 ? n_vis(t_last) : 0;  // visibility grows with t
 
-  // key tiles of one chunk for this wave: keys s0 + (wave * U + u) * 16 + c
-  u32x4 kb[U][2];
-  float sc[U];
-  auto load_chunk = [&](int64_t s0) {
+  // key tiles of one chunk for this wave: keys s0 + (wave * U + u) * 16 + c. The narrow shape
+  // holds one chunk ahead; the wide one, with registers to spare, two (KD key buffers in turn).
+  // Past the row's end the loads take key 0 of the sequence and the values are masked, so the
+  // loads never branch and the wait before each chunk's products counts exactly the newer
+  // chunk's loads.
+  constexpr int KD = WIDE ? 2 : 1;
+  struct Keys {
+    u32x4 k[U][2];
+    float sc[U];
+  };
+  Keys kbuf[KD];
+  auto load_chunk = [&](int64_t s0, Keys& kk) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t s = s0 + (wave * U + u) * 16 + c;
       const bool ok = s < n_max;
-      const int64_t kr = key_row<PAGED>(pg, b, e_base, s);
-      load_key_tile<KT>(kI, k_mx, kr, ok, g, kb[u][0], kb[u][1]);
-      if (FP8) sc[u] = ok ? k_scale[fp8_scale_index<PAGED>(pg, kr, scale_off, b, s, scale_group)] : 0.f;
+      const int64_t kr = key_row<PAGED>(pg, b, e_base, (WIDE && !ok) ? 0 : s);
+      if (WIDE) {
+        load_key_tile<KT>(kI, k_mx, kr, true, g, kk.k[u][0], kk.k[u][1]);
+        if (FP8) kk.sc[u] = k_scale[fp8_scale_index<PAGED>(pg, kr, scale_off, b, ok ? s : 0, scale_group)];
+      } else {
+        load_key_tile<KT>(kI, k_mx, kr, ok, g, kk.k[u][0], kk.k[u][1]);
+        if (FP8) kk.sc[u] = ok ? k_scale[fp8_scale_index<PAGED>(pg, kr, scale_off, b, s, scale_group)] : 0.f;
+      }
     }
   };
   if (threadIdx.x == 0) cut_req = 0;  // read only after the first chunk's barrier
-  if (n_max > 0) load_chunk(0);
+  if (n_max > 0) {
+    load_chunk(0, kbuf[0]);
+    if (KD > 1) load_chunk(CH, kbuf[KD - 1]);
+  }
   int buf = 0;
   uint32_t jc = 0;  // chunk index
-  for (int64_t s0 = 0; s0 < n_max; s0 += CH, buf ^= 1, ++jc) {
-    bf16x8 b0[U], b1[U];
-    float scu[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      b0[u] = key_operand<KT>(kb[u][0]);
-      b1[u] = key_operand<KT>(kb[u][1]);
-      scu[u] = sc[u];
+  // one chunk (keys s0 .., its key buffer kk, which then takes the keys KD chunks ahead): the
+  // narrow shape walks it in a plain loop, the wide one twice per trip so that each copy names
+  // its key buffer at compile time (written out, not as a lambda: a lambda capturing the
+  // kernel's arrays costs the narrow shape registers)
+#define CSL_FUSED_CHUNK(S0_, kk)                                                                                   \
+  do {                                                                                                            \
+    const int64_t s0 = (S0_);                                                                                     \
+    bf16x8 b0[U], b1[U];                                                                                          \
+    float scu[U];                                                                                                 \
+_Pragma("unroll")                                                                                                 \
+    for (int u = 0; u < U; ++u) {                                                                                 \
+      b0[u] = key_operand<KT>(kk.k[u][0]);                                                                        \
+      b1[u] = key_operand<KT>(kk.k[u][1]);                                                                        \
+      scu[u] = kk.sc[u];                                                                                          \
+    }                                                                                                             \
+_Pragma("unroll")                                                                                                 \
+    for (int u = 0; u < U; ++u) {                                                                                 \
+      /* the NB products of a key tile are independent: issue them back to back */                                \
+      f32x4 acc[NB];                                                                                              \
+_Pragma("unroll")                                                                                                 \
+      for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma16x16x32(a[nb][0], b0[u], f32x4{0.f, 0.f, 0.f, 0.f});         \
+_Pragma("unroll")                                                                                                 \
+      for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma16x16x32(a[nb][1], b1[u], acc[nb]);                           \
+_Pragma("unroll")                                                                                                 \
+      for (int nb = 0; nb < NB; ++nb) {                                                                           \
+        float part[RPG];                                                                                          \
+        prefill_head_sum<HI>(acc[nb], wv[nb], part);                                                              \
+        /* every lane writes: lanes that share a (row, key) hold the same sum bit for bit */                      \
+_Pragma("unroll")                                                                                                 \
+        for (int q = 0; q < RPG; ++q) {                                                                           \
+          float v = part[q];                                                                                      \
+          if (FP8) v *= scu[u];                                                                                   \
+          sval[buf][nb * QPB + prefill_row<HI>(g, q)][(wave * U + u) * 16 + c] = v;                               \
+        }                                                                                                         \
+      }                                                                                                           \
+    }                                                                                                             \
+    /* the next chunk's keys fly during the barrier and the filing (issued after the MFMAs, so */                 \
+    /* they do not hold registers beside this chunk's operands); with two buffers, the chunk */                   \
+    /* after it goes into this chunk's buffer */                                                                  \
+    if (KD == 1) {                                                                                                \
+      if (s0 + CH < n_max) load_chunk(s0 + CH, kk);                                                               \
+    } else {                                                                                                      \
+      load_chunk(s0 + KD * CH, kk);                                                                               \
+    }                                                                                                             \
+    __syncthreads();                                                                                              \
+    /* Rows fill at similar rates, so cuts are taken together: a row that the next chunk might */                 \
+    /* overflow asks for a cut by chunk jc + 1, and at that chunk every wave cuts its rows that */                \
+    /* hold more than k + 64 entries. Cuts taken apart would each hold up the others at the */                    \
+    /* next barrier. (A wave that reads a later request cuts early: harmless.) */                                 \
+    const bool cut_now = jc > 0 && *(volatile uint32_t*)&cut_req >= jc;                                           \
+    bool ask = false;                                                                                             \
+_Pragma("unroll")                                                                                                 \
+    for (int i = 0; i < RPW; ++i) {                                                                               \
+      const int r = wave * RPW + i;                                                                               \
+      if (cut_now && cnt[i] > (uint32_t)k + 64u) bar[i] = cut_to_k<CAP, false>(cand[r], cnt[i], k);               \
+      /* a coarse cut leaves at most k + 32 entries; when a whole chunk fits after that, one */                   \
+      /* check per chunk suffices, against the keys the chunk actually admits */                                  \
+      const bool chunk_check = (uint32_t)k + 32u + CH <= (uint32_t)CAP;                                           \
+      if (chunk_check || cnt[i] + CH <= (uint32_t)CAP) {                                                          \
+        /* the chunk's score reads go out together, then the ballots */                                           \
+        uint32_t x[CH / kWave];                                                                                   \
+        float v[CH / kWave];                                                                                      \
+_Pragma("unroll")                                                                                                 \
+        for (int j = 0; j < CH / kWave; ++j) v[j] = sval[buf][r][j * kWave + lane]; /* in range: read unmasked */ \
+_Pragma("unroll")                                                                                                 \
+        for (int j = 0; j < CH / kWave; ++j) {                                                                    \
+          const int64_t s = s0 + j * kWave + lane;                                                                \
+          x[j] = s < nv_mine[i] ? score_key(v[j]) : 0u;                                                           \
+        }                                                                                                         \
+        uint64_t mk[CH / kWave];                                                                                  \
+        uint32_t adm = 0;                                                                                         \
+_Pragma("unroll")                                                                                                 \
+        for (int j = 0; j < CH / kWave; ++j) {                                                                    \
+          mk[j] = __ballot(x[j] > bar[i]);                                                                        \
+          adm += (uint32_t)__popcll(mk[j]);                                                                       \
+        }                                                                                                         \
+        if (cnt[i] + adm > (uint32_t)CAP) { /* only with chunk_check: cut, then admit above the new bar */        \
+          bar[i] = cut_to_k<CAP, false>(cand[r], cnt[i], k);                                                      \
+_Pragma("unroll")                                                                                                 \
+          for (int j = 0; j < CH / kWave; ++j) mk[j] = __ballot(x[j] > bar[i]);                                   \
+          adm = 0;                                                                                                \
+        }                                                                                                         \
+_Pragma("unroll")                                                                                                 \
+        for (int j = 0; j < CH / kWave; ++j) {                                                                    \
+          if ((mk[j] >> lane) & 1ull)                                                                             \
+            cand[r][cnt[i] + rank_in_wave(mk[j])] = ((uint64_t)x[j] << 32) | (uint32_t)(s0 + j * kWave + lane);   \
+          cnt[i] += (uint32_t)__popcll(mk[j]);                                                                    \
+        }                                                                                                         \
+        /* ask for a shared cut when the next chunks are likely to overflow this row */                           \
+        ask = ask || cnt[i] + (chunk_check ? 2u * max(adm, 32u) : (uint32_t)CH) > (uint32_t)CAP;                  \
+      } else {                                                                                                    \
+_Pragma("unroll 1")                                                                                               \
+        for (int j = 0; j < CH / kWave; ++j) { /* not unrolled: one copy of the cut per row */                    \
+          if (cnt[i] + kWave > (uint32_t)CAP) bar[i] = cut_to_k<CAP, false>(cand[r], cnt[i], k);                  \
+          const int64_t s = s0 + j * kWave + lane;                                                                \
+          const float v = sval[buf][r][j * kWave + lane];                                                         \
+          const uint32_t x = s < nv_mine[i] ? score_key(v) : 0u;                                                  \
+          const bool admit = x > bar[i];                                                                          \
+          const uint64_t mk = __ballot(admit);                                                                    \
+          if (admit) cand[r][cnt[i] + rank_in_wave(mk)] = ((uint64_t)x << 32) | (uint32_t)s;                      \
+          cnt[i] += (uint32_t)__popcll(mk);                                                                       \
+        }                                                                                                         \
+        ask = ask || cnt[i] + CH > (uint32_t)CAP;                                                                 \
+      }                                                                                                           \
+    }                                                                                                             \
+    if (ask && lane == 0) atomicMax(&cut_req, jc + 1);                                                            \
+  } while (0)
+  if constexpr (KD == 1) {
+    for (int64_t c0 = 0; c0 < n_max; c0 += CH, buf ^= 1, ++jc) CSL_FUSED_CHUNK(c0, kbuf[0]);
+  } else {
+    for (int64_t c0 = 0; c0 < n_max; c0 += 2 * CH) {
+      CSL_FUSED_CHUNK(c0, kbuf[0]);
+      buf ^= 1;
+      ++jc;
+      if (c0 + CH >= n_max) break;
+      CSL_FUSED_CHUNK(c0 + CH, kbuf[KD - 1]);
+      buf ^= 1;
+      ++jc;
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      // the NB products of a key tile are independent: issue them back to back
-      f32x4 acc[NB];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma16x16x32(a[nb][0], b0[u], f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma16x16x32(a[nb][1], b1[u], acc[nb]);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        float part[RPG];
-        prefill_head_sum<HI>(acc[nb], wv[nb], part);
-        // every lane writes: lanes that share a (row, key) hold the same sum bit for bit
-#pragma unroll
-        for (int q = 0; q < RPG; ++q) {
-          float v = part[q];
-          if (FP8) v *= scu[u];
-          sval[buf][nb * QPB + prefill_row<HI>(g, q)][(wave * U + u) * 16 + c] = v;
-        }
-      }
-    }
-    // the next chunk's keys fly during the barrier and the filing (issued after the MFMAs, so
-    // they do not hold registers beside this chunk's operands)
-    if (s0 + CH < n_max) load_chunk(s0 + CH);
-    __syncthreads();
-    // Rows fill at similar rates, so cuts are taken together: a row that the next chunk might
-    // overflow asks for a cut by chunk jc + 1, and at that chunk every wave cuts its rows that
-    // hold more than k + 64 entries. Cuts taken apart would each hold up the others at the
-    // next barrier. (A wave that reads a later request cuts early: harmless.)
-    const bool cut_now = jc > 0 && *(volatile uint32_t*)&cut_req >= jc;
-    bool ask = false;
-#pragma unroll
-    for (int i = 0; i < RPW; ++i) {
-      const int r = wave * RPW + i;
-      if (cut_now && cnt[i] > (uint32_t)k + 64u) bar[i] = cut_to_k<CAP, false>(cand[r], cnt[i], k);
-      // a coarse cut leaves at most k + 32 entries; when a whole chunk fits after that, one
-      // check per chunk suffices, against the keys the chunk actually admits
-      const bool chunk_check = (uint32_t)k + 32u + CH <= (uint32_t)CAP;
-      if (chunk_check || cnt[i] + CH <= (uint32_t)CAP) {
-        // the chunk's score reads go out together, then the ballots
-        uint32_t x[CH / kWave];
-        float v[CH / kWave];
-#pragma unroll
-        for (int j = 0; j < CH / kWave; ++j) v[j] = sval[buf][r][j * kWave + lane];  // in range: read unmasked
-#pragma unroll
-        for (int j = 0; j < CH / kWave; ++j) {
-          const int64_t s = s0 + j * kWave + lane;
-          x[j] = s < nv_mine[i] ? score_key(v[j]) : 0u;
-        }
-        uint64_t mk[CH / kWave];
-        uint32_t adm = 0;
-#pragma unroll
-        for (int j = 0; j < CH / kWave; ++j) {
-          mk[j] = __ballot(x[j] > bar[i]);
-          adm += (uint32_t)__popcll(mk[j]);
-        }
-        if (cnt[i] + adm > (uint32_t)CAP) {  // only with chunk_check: cut, then admit above the new bar
-          bar[i] = cut_to_k<CAP, false>(cand[r], cnt[i], k);
-#pragma unroll
-          for (int j = 0; j < CH / kWave; ++j) mk[j] = __ballot(x[j] > bar[i]);
-          adm = 0;
-        }
-#pragma unroll
-        for (int j = 0; j < CH / kWave; ++j) {
-          if ((mk[j] >> lane) & 1ull)
-            cand[r][cnt[i] + rank_in_wave(mk[j])] = ((uint64_t)x[j] << 32) | (uint32_t)(s0 + j * kWave + lane);
-          cnt[i] += (uint32_t)__popcll(mk[j]);
-        }
-        // ask for a shared cut when the next chunks are likely to overflow this row
-        ask = ask || cnt[i] + (chunk_check ? 2u * max(adm, 32u) : (uint32_t)CH) > (uint32_t)CAP;
-      } else {
-#pragma unroll 1
-        for (int j = 0; j < CH / kWave; ++j) {  // not unrolled: one copy of the cut per row
-          if (cnt[i] + kWave > (uint32_t)CAP) bar[i] = cut_to_k<CAP, false>(cand[r], cnt[i], k);
-          const int64_t s = s0 + j * kWave + lane;
-          const float v = sval[buf][r][j * kWave + lane];
-          const uint32_t x = s < nv_mine[i] ? score_key(v) : 0u;
-          const bool admit = x > bar[i];
-          const uint64_t mk = __ballot(admit);
-          if (admit) cand[r][cnt[i] + rank_in_wave(mk)] = ((uint64_t)x << 32) | (uint32_t)s;
-          cnt[i] += (uint32_t)__popcll(mk);
-        }
-        ask = ask || cnt[i] + CH > (uint32_t)CAP;
-      }
-    }
-    if (ask && lane == 0) atomicMax(&cut_req, jc + 1);
   }
+#undef CSL_FUSED_CHUNK
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
     const int r = wave * RPW + i;
@@ -854,12 +896,23 @@ hipError_t launch_topk_hi(const void* qI, const float* w, const void* kI, const 
   constexpr int QR = FusedShape<HI>::QR;
   dim3 grid((unsigned)((T + QR - 1) / QR), 1u, (unsigned)B);
   const uint16_t* q16 = static_cast<const uint16_t*>(qI);
-  if (pg.table)
-    indexer_topk_kernel<HI, KT, true><<<grid, kFusedWaves * kWave, 0, st>>>(
-        q16, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, T, max_entries, k, idx, pg);
-  else
-    indexer_topk_kernel<HI, KT, false><<<grid, kFusedWaves * kWave, 0, st>>>(
-        q16, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, T, max_entries, k, idx, pg);
+  // the wide shape (one workgroup per CU, twice the candidate slots) once k leaves the narrow
+  // buffer less than a chunk of room after a cut: a buffer that tight is cut almost every chunk
+  constexpr bool kHasWide = FusedShape<HI, true>::CAP > FusedShape<HI, false>::CAP;
+  const bool wide = kHasWide && k + kFusedChunk + 32 > FusedShape<HI, false>::CAP;
+#define CSL_TOPK_LAUNCH(PG, WD)                                                                   \
+  indexer_topk_kernel<HI, KT, PG, WD><<<grid, kFusedWaves * kWave, 0, st>>>(                    \
+      q16, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, T, max_entries, k, idx, pg)
+  if (wide) {
+    if constexpr (kHasWide) {
+      if (pg.table) CSL_TOPK_LAUNCH(true, true);
+      else CSL_TOPK_LAUNCH(false, true);
+    }
+  } else {
+    if (pg.table) CSL_TOPK_LAUNCH(true, false);
+    else CSL_TOPK_LAUNCH(false, false);
+  }
+#undef CSL_TOPK_LAUNCH
   return hipGetLastError();
 }
 
@@ -907,8 +960,11 @@ hipError_t launch_kt(int HI, const void* qI, const float* w, const void* kI, con
 }  // namespace
 
 int indexer_topk_max_k(int HI) {
-  const int cap = HI == 1 ? FusedShape<1>::CAP : HI == 16 ? FusedShape<16>::CAP : FusedShape<8>::CAP;
-  return cap - kWave;  // a cut leaves k entries and a sub-step files up to 64 more
+  // the larger of the two shapes' buffers (HI = 2, 4 and 8 share theirs), less a chunk and the
+  // 32 a coarse cut may keep: a cut always leaves room for a whole chunk (a buffer cut more
+  // often than that spends most of its time cutting)
+  const int cap = HI == 1 ? FusedShape<1, true>::CAP : HI == 16 ? FusedShape<16, true>::CAP : FusedShape<8, true>::CAP;
+  return cap - kFusedChunk - 32;
 }
 
 hipError_t launch_indexer_topk(const void* qI, const float* w, const void* kI, int key_type, const void* k_scale,

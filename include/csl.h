@@ -234,12 +234,13 @@ int csl_topk_select(const float* scores, int64_t ld, const int64_t* ent_off, con
  * indexer_scores (keys, scales, offsets, paged cache) and topk_select (k, idx), without the
  * score buffer and workspace.
  *
- *   k     1 <= k <= csl_indexer_topk_max_k(HI) (896 for HI <= 8, 2176 for HI = 16)
+ *   k     1 <= k <= csl_indexer_topk_max_k(HI) (1952 for HI = 2 .. 16, 672 for HI = 1)
  *   idx   int32 [B, T, k]
  * One workgroup scores 8 query rows (16 at HI = 1) against all of their visible entries
- * and keeps each row's candidates in on-chip memory, so the call suits batches of many
- * query rows (prefill); a single decode row is better served by indexer_scores with
- * candidate lists and topk_select. No workspace; nothing but idx is written.
+ * and keeps each row's candidates in on-chip memory (two workgroups per compute unit up to
+ * k = 672, one beyond), so the call suits batches of many query rows (prefill); a single
+ * decode row is better served by indexer_scores with candidate lists and topk_select. No
+ * workspace; nothing but idx is written.
  */
 int csl_indexer_topk_max_k(int HI);
 int csl_indexer_topk(const void* q_idx, const float* w, const void* k_idx, int k_dtype, const void* k_scale,

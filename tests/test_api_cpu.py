@@ -241,7 +241,7 @@ def test_step_validation(lib):
     assert call(B=0) == 0                       # nothing to do: nothing enqueued
     assert _err(lib) == ""
     # without a score buffer: the fused indexer/top-k's limit on k applies instead
-    assert call(scores=None, k=897) == 2
+    assert call(scores=None, k=1953) == 2
     assert "without scores" in _err(lib)
     assert call(scores=None, idx=None) == 1
     assert call(scores=None, ld=0, B=0) == 0    # ld is ignored without scores
@@ -327,7 +327,9 @@ def test_indexer_topk_validation(lib):
     f.argtypes = [P, P, P, I, P, P, I, P, P, I, I, I, I, I, L, I, P, P, P]
     mk = lib.csl_indexer_topk_max_k
     mk.argtypes = [I]
-    assert mk(8) == 896 and mk(4) == 896 and mk(1) == 896 and mk(16) == 2176 and mk(3) == 0
+    # a cut must leave room for a 256-key chunk: 2240 - 288 slots with one workgroup per CU (HI = 2,
+    # 4, 8 beyond k = 672, and HI = 16); HI = 1 keeps its 960-slot buffer: 672
+    assert mk(8) == 1952 and mk(4) == 1952 and mk(2) == 1952 and mk(1) == 672 and mk(16) == 1952 and mk(3) == 0
 
     def call(idx=FAKE, k=64, HI=8, CI=64, B=1, T=16, me=1000, kd=0, ks=None, m=4):
         # q_idx, w, k_idx, k_dtype, k_scale, scale_off, group, ent_off, q_pos, m, B, T, HI, CI, max_entries, k, idx
@@ -335,7 +337,8 @@ def test_indexer_topk_validation(lib):
 
     assert call(idx=None) == 1 and "null" in _err(lib)
     assert call(k=0) == 2 and "k must be in" in _err(lib)
-    assert call(k=897) == 2 and "k must be in" in _err(lib)
+    assert call(k=1953) == 2 and "k must be in" in _err(lib)
+    assert call(k=673, HI=1) == 2 and "k must be in" in _err(lib)
     assert call(HI=3) == 2 and "HI" in _err(lib)
     assert call(CI=32) == 2 and "CI" in _err(lib)
     assert call(m=0) == 1

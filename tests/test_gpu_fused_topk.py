@@ -73,7 +73,11 @@ def _oracle_check(li, kI_cpu, got, k, fmt, rows=None):
 @pytest.mark.parametrize("HI,T,lengths,q_pos,k,fmt", [
     (8, 40, [9000, 4100, 60, 2049], [8900, 4000, 0, 2000], 64, None),     # ragged rows, one short of k
     (8, 16, [20000, 3333, 7001, 500], [19000, 3300, 7001, 400], 512, None),
-    (8, 33, [12000, 10000], [11900, 9900], None, None),                   # k at its limit
+    (8, 33, [12000, 10000], [11900, 9900], None, None),                   # k at its limit (one workgroup per CU)
+    (8, 16, [40000, 9000, 600, 5000], [39000, 8900, 500, 4900], 1024, None),  # the Pro top-k: past two workgroups' buffers
+    (8, 16, [20000, 7000], [19000, 6900], 673, None),                     # the first k of the wide shape
+    (8, 16, [20000, 7000], [19000, 6900], 672, None),                     # the last k of the narrow one
+    (4, 20, [30000, 5000], [29000, 4900], 1500, "fp8"),
     (16, 24, [16000, 2500, 900], [15990, 2400, 800], None, None),         # HI = 16; k at its limit
     (4, 20, [5000, 1300, 2222, 17], [4900, 1250, 2100, 0], 100, None),
     (2, 17, [3000, 2000, 1000, 4000], [2999, 1999, 999, 3999], 37, None),
@@ -146,12 +150,14 @@ def test_fused_short_decode_rows_match_oracle(csl):
     _oracle_check(li, li.kI, got.cpu().numpy(), 512, None)
 
 
-def test_fused_prefill_workload_equals_scores_then_select(csl):
-    """The 8K-query prefill on a 128K context at full size (8,192 rows x ~34K entries, k = 512)."""
-    print("fused top-k prefill 8k on 128k", flush=True)
+@pytest.mark.parametrize("k", [None, 1024])
+def test_fused_prefill_workload_equals_scores_then_select(csl, k):
+    """The 8K-query prefill on a 128K context at full size (8,192 rows x ~34K entries), at its
+    k = 512 and at the Pro top-k of 1024."""
+    print(f"fused top-k prefill 8k on 128k k={k}", flush=True)
     inp = synth.generate("csa_prefill_8k_on_128k", parts=("qI", "kI", "w"))
     li = inp.lanes[0]
-    k = li.lane.k
+    k = k or li.lane.k
     kI = dev(li.kI)
     got = _fused(csl, li, kI, k, None)
     ref = _unfused(csl, li, kI, k, None)
@@ -165,8 +171,8 @@ def test_fused_argument_errors(csl):
     idx = torch.empty((1, 16, 8), dtype=torch.int32, device="cuda")
     base = (dev(li.qI), dev(li.w), dev(li.kI), dev(li.ent_off), dev(li.q_pos), 4)
     kmax = csl.indexer_topk_max_k(8)
-    assert kmax == 896 and csl.indexer_topk_max_k(16) == 2176 and csl.indexer_topk_max_k(1) == 896
-    assert csl.indexer_topk_max_k(4) == 896 and csl.indexer_topk_max_k(2) == 896
+    assert kmax == 1952 and csl.indexer_topk_max_k(16) == 1952 and csl.indexer_topk_max_k(1) == 672
+    assert csl.indexer_topk_max_k(4) == 1952 and csl.indexer_topk_max_k(2) == 1952
     assert csl.indexer_topk_max_k(3) == 0
     with pytest.raises(csl.CslError, match="k must be in"):
         csl.indexer_topk(*base, kmax + 1, torch.empty((1, 16, kmax + 1), dtype=torch.int32, device="cuda"),
