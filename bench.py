@@ -10,9 +10,10 @@ timed region. The compressed cache and the indexer keys are kept in several inde
 copies that consecutive steps rotate through, so every step streams from HBM rather than
 from the last-level cache.
 
-The timed region replays a HIP graph that holds R consecutive steps (one per rotated copy)
-until K steps have run; every step is the whole hot path, the graph only saves host-side
-launches. The latency of a step captured and launched on its own is reported beside it. Prints one JSON line: queries/s, ms per step, the
+The timed region replays a HIP graph that holds 8 rounds of R consecutive steps (one per
+rotated copy) until K steps have run; every step is the whole hot path, the graph only saves
+host-side launches. The latency of a step captured and launched on its own is reported beside
+it. Prints one JSON line: queries/s, ms per step, the
 indexer kernel's achieved HBM bandwidth against the 8 TB/s peak (HIP events around 100
 back-to-back launches), and the fp64 CPU oracle's rate on a bounded sample of the same
 workload.
@@ -41,6 +42,11 @@ METRIC = "CSA/HCA decode queries/s at 1M ctx; achieved HBM GB/s vs MI355X peak"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published peak
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published peak
 WORKLOAD = "csa_decode_1m"
+# A timed graph replays GRAPH_ROUNDS rounds of the rotated-copy steps back to back (32 steps
+# with 4 copies), as one replay of a model holds all of its layers' steps: the replay's own
+# launch cost is then a small share of each step. The one-step-per-replay latency is reported
+# beside it (step_us_one_graph_per_step).
+GRAPH_ROUNDS = 8
 COUNTER_FILE = os.path.join(ROOT, "profiles", "indexer_csa_decode_1m_counters.txt")
 INDEXER_SOURCES = ["compressed_sparse_long_amd/csrc/indexer.hip", "compressed_sparse_long_amd/csrc/device_common.h",
                    "compressed_sparse_long_amd/csrc/topk_common.h", "compressed_sparse_long_amd/csrc/compress_common.h"]
@@ -242,15 +248,17 @@ def measure_headline(args) -> dict:
         torch.cuda.synchronize()
         return a.elapsed_time(b) / (reps * per_replay) * 1e3  # microseconds
 
-    # the timed loop replays one graph holding R consecutive decode steps, one per rotated
-    # input copy (each step is the whole hot path; the graph only saves host launches)
-    multi = capture(lambda: [cl.step(r) for r in range(R)])
-    for i in range((args.warmup + R - 1) // R):
+    # the timed loop replays one graph holding GRAPH_ROUNDS x R consecutive decode steps, the
+    # rotated input copies in turn (each step is the whole hot path; the graph only saves host
+    # launches)
+    S = GRAPH_ROUNDS * R
+    multi = capture(lambda: [cl.step(r) for _ in range(GRAPH_ROUNDS) for r in range(R)])
+    for i in range((args.warmup + S - 1) // S):
         multi.replay()
     torch.cuda.synchronize()
 
-    reps = (args.steps + R - 1) // R
-    K = reps * R
+    reps = (args.steps + S - 1) // S
+    K = reps * S
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
@@ -454,15 +462,17 @@ def run_workload(name: str, steps: int, warmup: int, paged: str | None = None, c
             lane.paginate(ring_rows=256, order=paged)
         lane.rotate(R)
     torch.cuda.synchronize()
+    S = GRAPH_ROUNDS * R
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for r in range(R):
-            for lane in ls:
-                lane.step(r)
-    for _ in range(max(1, (warmup + R - 1) // R)):
+        for _ in range(GRAPH_ROUNDS):
+            for r in range(R):
+                for lane in ls:
+                    lane.step(r)
+    for _ in range(max(1, (warmup + S - 1) // S)):
         g.replay()
     torch.cuda.synchronize()
-    reps = max(1, (steps + R - 1) // R)
+    reps = max(1, (steps + S - 1) // S)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(reps):
@@ -470,8 +480,8 @@ def run_workload(name: str, steps: int, warmup: int, paged: str | None = None, c
     b.record()
     torch.cuda.synchronize()
     print(f"workload {name}{' paged ' + paged if paged else ''}{' without scores' if scoreless else ''}: "
-          f"{a.elapsed_time(b) / (reps * R) * 1e3:.1f} us per "
-          f"step over {reps * R} steps ({R} rotated input copies)", flush=True)
+          f"{a.elapsed_time(b) / (reps * S) * 1e3:.1f} us per "
+          f"step over {reps * S} steps ({R} rotated input copies)", flush=True)
 
 
 def step_model(lane_list, D: int = 128):
@@ -565,7 +575,7 @@ def oracle_rate(inp, seconds: float, D: int = 128):
 
 
 def report_configs(copies: int, cpu_seconds: float, emit: bool = True) -> list:
-    """Every synthetic configuration: whole-step time (graph of `copies` rotated steps),
+    """Every synthetic configuration: whole-step time (graph of GRAPH_ROUNDS x `copies` steps),
     queries/s, algorithmic GB/s and roofline fraction, and the oracle's rate beside it.
     Returns one dict per configuration (and prints each as a JSON line when ``emit``)."""
     import torch
@@ -580,9 +590,10 @@ def report_configs(copies: int, cpu_seconds: float, emit: bool = True) -> list:
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for r in range(copies):
-                for lane in ls:
-                    lane.step(r)
+            for _ in range(GRAPH_ROUNDS):
+                for r in range(copies):
+                    for lane in ls:
+                        lane.step(r)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         g.replay()
         torch.cuda.synchronize()
@@ -598,7 +609,7 @@ def report_configs(copies: int, cpu_seconds: float, emit: bool = True) -> list:
         torch.cuda.synchronize()
         del g, ls
         torch.cuda.empty_cache()
-        return a.elapsed_time(b) / (reps * copies) * 1e3
+        return a.elapsed_time(b) / (reps * copies * GRAPH_ROUNDS) * 1e3
 
     lines = []
     for name in synth.CONFIG_ORDER:

@@ -49,8 +49,11 @@ size_t attn_workspace_bytes(int B, int T, int H, int64_t max_keys) {
 }
 
 bool attention_carries_job(int B, int T, int H, int64_t max_keys, int64_t max_new) {
+  // the job rides in single-round splits (one or two tiles, no parallel-tile groups): the
+  // workgroups then pool any entry being rewritten before their own state is live
+  const AttnPlan p = attn_plan(B, T, H, max_keys);
   return (H == 16 || H == 32 || H == 64 || H == 128) && max_new >= 1 &&
-         (int64_t)B * T + (int64_t)B * max_new <= 65535 && attn_plan(B, T, H, max_keys).nsub == 1;
+         (int64_t)B * T + (int64_t)B * max_new <= 65535 && p.nsub == 1 && p.keys_per_split <= 2 * kKT;
 }
 
 hipError_t launch_attention(bool sparse, const void* q, const void* ckv, const int32_t* idx, int k, const void* kv,
@@ -75,7 +78,7 @@ hipError_t launch_attention(bool sparse, const void* q, const void* ckv, const i
   // the rows' RoPE tables follow the partials (8-byte aligned: the partials are whole rows
   // of 16 heads); only the merge reads them
   float2* ws_rope = ws_o ? reinterpret_cast<float2*>(ws_lse + (size_t)p.nsplit * rows * H) : nullptr;
-  // with a job, rows nrows .. of the grid are its workgroups (B * max_new of them)
+  // with a job, the grid's first B * max_new rows are its workgroups
   const HcaJob none{};
   const HcaJob& hj = job ? *job : none;
   const int64_t grid_rows = rows + (job ? (int64_t)B * job->max_new : 0);

@@ -27,7 +27,7 @@
 //     as a bf16 pair, like the probabilities) and the output's last 64 dims at -p after
 //     normalisation. Both act where the row's result is final: in the single-split
 //     epilogue or in the merge;
-//   * FUSED (an HCA step): rows of the grid past the query rows are workgroups that pool the
+//   * FUSED (an HCA step): rows of the grid before the query rows are workgroups that pool the
 //     step's new entries into the cache, and a workgroup whose keys include an entry being
 //     rewritten pools it from the raw rows into its tile instead of reading the cache.
 #pragma once
@@ -329,6 +329,7 @@ __global__ __launch_bounds__(NHG * NSUB * 64) void attn_kernel(
     float2* __restrict__ ws_rope, AttnLayout lay, int nrows, HcaJob job) {
   constexpr bool MULTI = MODE == 0;
   static_assert(NSUB == 1 || MODE == 1, "parallel tiles take single-round splits of one tile each");
+  static_assert(!FUSED || (!MULTI && NSUB == 1 && !SPARSE), "a fused launch is dense and single-round");
   constexpr int NTL = MULTI ? 1 : (NSUB > 1 ? NSUB : MODE);  // tiles held in LDS at once
   constexpr int NT = NHG * NSUB * 64;
   constexpr int NV = kKT * NTL;            // rows gathered per round
@@ -347,13 +348,16 @@ __global__ __launch_bounds__(NHG * NSUB * 64) void attn_kernel(
   __shared__ float2 rcs_all[ROPE ? NHG * NSUB : 1][kRope / 2];  // RoPE (cos, sin) per pair at the row's position, per wave
 
   const int split = blockIdx.x;
-  const int row = blockIdx.y;
+  // FUSED: the grid's first rows are the step's compression (dispatched first, so that it
+  // starts with the attention rather than after it), then the query rows
+  const int njob = FUSED ? (int)gridDim.y - nrows : 0;
+  const int row = (int)blockIdx.y - njob;
   const PagedView jpg{lay.table, lay.max_blocks, lay.eb_shift, lay.ring_rows};
-  if (FUSED && row >= nrows) {
-    // the step's compression: workgroup (0, nrows + j) takes new entry j % max_new of sequence
-    // j / max_new, written to its cache row
+  if (FUSED && row < 0) {
+    // workgroup (0, j) takes new entry j % max_new of sequence j / max_new, written to its
+    // cache row
     if (split == 0) {
-      const int jb = row - nrows;
+      const int jb = (int)blockIdx.y;
       const int bj = (int)(jb / job.max_new);
       const int64_t blk = jb % job.max_new;
       if (job.z)
@@ -451,6 +455,37 @@ __global__ __launch_bounds__(NHG * NSUB * 64) void attn_kernel(
     }
   };
 
+  // FUSED: entries of this split that the launch's compression rewrites are not read from the
+  // cache. The workgroup pools them itself first (with the same arithmetic, before its own
+  // state is live) into their tile slots, which the gathered rows then leave alone.
+  int64_t hz_lo = 0, hz_hi = 0;
+  if (FUSED) {
+    hz_lo = k_lo > f_new ? k_lo : f_new;
+    hz_hi = f_new + job.max_new;
+    hz_hi = hz_hi < n_comp ? hz_hi : n_comp;
+    hz_hi = hz_hi < k_hi ? hz_hi : k_hi;
+    for (int64_t e = hz_lo; e < hz_hi; ++e) {  // uniform
+      auto to_tile = [&](int64_t i, int64_t, int dg, const float (&o)[8]) {
+        const int v = (int)(i - k_lo);
+        const int tl = v / kKT, vr = v % kKT;
+        u32x4 w;
+        w.x = pack_bf16x2(o[0], o[1]);
+        w.y = pack_bf16x2(o[2], o[3]);
+        w.z = pack_bf16x2(o[4], o[5]);
+        w.w = pack_bf16x2(o[6], o[7]);
+        *reinterpret_cast<u32x4*>(Ks[tl] + vr * 256 + 16 * (dg ^ ks_swz(vr))) = w;
+      };
+      if (job.z)
+        compress_block_to<NT, 16, 4, true, 8, NT / 64, false>(job.kv, job.z, kv_off, ent_off, job.first_entry, kD, m,
+                                                             job.max_new, to_tile, b, e - f_new, nullptr, nullptr,
+                                                             jpg);
+      else
+        compress_block_to<NT, 16, 4, false, 8, NT / 64, false>(job.kv, job.z, kv_off, ent_off, job.first_entry, kD,
+                                                              m, job.max_new, to_tile, b, e - f_new, nullptr, nullptr,
+                                                              jpg);
+    }
+  }
+
   // queries of this wave's 16 heads as MFMA B operands (d-slots 8g..8g+7 of each 32-chunk)
   const int head = hg * 16 + c;
   bf16x8 qb[4];
@@ -523,42 +558,14 @@ __global__ __launch_bounds__(NHG * NSUB * 64) void attn_kernel(
       const int tl = v / kKT, vr = v % kKT;
       const bool ok = (okm >> j) & 1u;
       const int sw = ks_swz(vr);
+      // (FUSED: a slot the workgroup pooled itself keeps its row)
+      const bool own = FUSED && t0 + v >= hz_lo && t0 + v < hz_hi;
+      if (!own) {
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq)
-        *reinterpret_cast<u32x4*>(Ks[tl] + vr * 256 + 16 * ((4 * qq + u) ^ sw)) = ok ? r[j][qq] : u32x4{0, 0, 0, 0};
-      if (u == 0) vld[tl][vr] = ok ? 1 : 0;
-    }
-    if (FUSED) {
-      // entries this launch's compression rewrites are not read from the cache: the workgroup
-      // pools them itself, with the same arithmetic, into their slots of the tile
-      int64_t lo = t0 > f_new ? t0 : f_new;
-      int64_t hi = t0 + NV;
-      hi = hi < f_new + job.max_new ? hi : f_new + job.max_new;
-      hi = hi < n_comp ? hi : n_comp;
-      hi = hi < k_hi ? hi : k_hi;
-      if (lo < hi) {  // uniform
-        __syncthreads();
-        for (int64_t e = lo; e < hi; ++e) {
-          auto to_tile = [&](int64_t i, int64_t, int dg, const float (&o)[8]) {
-            const int v = (int)(i - t0);
-            const int tl = v / kKT, vr = v % kKT;
-            u32x4 w;
-            w.x = pack_bf16x2(o[0], o[1]);
-            w.y = pack_bf16x2(o[2], o[3]);
-            w.z = pack_bf16x2(o[4], o[5]);
-            w.w = pack_bf16x2(o[6], o[7]);
-            *reinterpret_cast<u32x4*>(Ks[tl] + vr * 256 + 16 * (dg ^ ks_swz(vr))) = w;
-          };
-          if (job.z)
-            compress_block_to<NT, 16, 4, true, 8, NT / 64, false>(job.kv, job.z, kv_off, ent_off, job.first_entry,
-                                                                 kD, m, job.max_new, to_tile, b, e - f_new, nullptr,
-                                                                 nullptr, jpg);
-          else
-            compress_block_to<NT, 16, 4, false, 8, NT / 64, false>(job.kv, job.z, kv_off, ent_off, job.first_entry,
-                                                                  kD, m, job.max_new, to_tile, b, e - f_new, nullptr,
-                                                                  nullptr, jpg);
-        }
+        for (int qq = 0; qq < 4; ++qq)
+          *reinterpret_cast<u32x4*>(Ks[tl] + vr * 256 + 16 * ((4 * qq + u) ^ sw)) = ok ? r[j][qq] : u32x4{0, 0, 0, 0};
       }
+      if (u == 0) vld[tl][vr] = ok ? 1 : 0;
     }
     __syncthreads();
     if (ROPE && !MULTI) rotate_q();  // single round: the rows (and so the query) have landed
@@ -722,13 +729,24 @@ hipError_t launch_nhg(int H, dim3 grid, hipStream_t st, const uint16_t* q, const
       CSL_ATTN_LAUNCH(NHG, 1, 0);          \
     break;
   if constexpr (FUSED) {
+    // single-round splits only (one or two tiles)
+#define CSL_ATTN_FUSED_CASE(NHG)           \
+  case NHG:                                \
+    if (tiles == 1)                        \
+      CSL_ATTN_LAUNCH(NHG, 1, 1);          \
+    else if (tiles == 2)                   \
+      CSL_ATTN_LAUNCH(NHG, 1, 2);          \
+    else                                   \
+      return hipErrorInvalidValue;         \
+    break;
     switch (H / 16) {
-      CSL_ATTN_CASE(1)
-      CSL_ATTN_CASE(2)
-      CSL_ATTN_CASE(4)
-      CSL_ATTN_CASE(8)
+      CSL_ATTN_FUSED_CASE(1)
+      CSL_ATTN_FUSED_CASE(2)
+      CSL_ATTN_FUSED_CASE(4)
+      CSL_ATTN_FUSED_CASE(8)
       default: return hipErrorInvalidValue;
     }
+#undef CSL_ATTN_FUSED_CASE
   } else {
     switch (H / 16) {
       CSL_ATTN_CASE(1)
