@@ -49,11 +49,12 @@ size_t attn_workspace_bytes(int B, int T, int H, int64_t max_keys) {
 }
 
 bool attention_carries_job(int B, int T, int H, int64_t max_keys, int64_t max_new) {
-  // the job rides in single-round splits (one or two tiles, no parallel-tile groups): the
-  // workgroups then pool any entry being rewritten before their own state is live
+  // the job rides in plans of one tile per wave group (no parallel-tile groups), with at most
+  // kHzMax new entries per sequence: a split pools those it finds rewritten into a side buffer
+  // of that many rows before its own state is live
   const AttnPlan p = attn_plan(B, T, H, max_keys);
-  return (H == 16 || H == 32 || H == 64 || H == 128) && max_new >= 1 &&
-         (int64_t)B * T + (int64_t)B * max_new <= 65535 && p.nsub == 1 && p.keys_per_split <= 2 * kKT;
+  return (H == 16 || H == 32 || H == 64 || H == 128) && max_new >= 1 && max_new <= kHzMax &&
+         (int64_t)B * T + (int64_t)B * max_new <= 65535 && p.nsub == 1;
 }
 
 hipError_t launch_attention(bool sparse, const void* q, const void* ckv, const int32_t* idx, int k, const void* kv,

@@ -55,6 +55,7 @@ constexpr int kKT = 64;               // keys per tile
 constexpr int kRope = 64;             // partial RoPE: the last 64 dims ([P1] section 8)
 constexpr int kRopeOff = kD - kRope;  // first rotated dim
 constexpr int kRopeKK = kRopeOff / 32;  // first rotated 32-dim chunk of the query operand
+constexpr int kHzMax = 4;  // FUSED: most entries a split can find rewritten (max_new <= this)
 
 struct RowGeom {
   int64_t ent_base, n_ent, kv_base, win_lo, win_cnt, nvis;
@@ -329,7 +330,7 @@ __global__ __launch_bounds__(NHG * NSUB * 64) void attn_kernel(
     float2* __restrict__ ws_rope, AttnLayout lay, int nrows, HcaJob job) {
   constexpr bool MULTI = MODE == 0;
   static_assert(NSUB == 1 || MODE == 1, "parallel tiles take single-round splits of one tile each");
-  static_assert(!FUSED || (!MULTI && NSUB == 1 && !SPARSE), "a fused launch is dense and single-round");
+  static_assert(!FUSED || (NSUB == 1 && !SPARSE), "a fused launch is dense, one tile per wave group");
   constexpr int NTL = MULTI ? 1 : (NSUB > 1 ? NSUB : MODE);  // tiles held in LDS at once
   constexpr int NT = NHG * NSUB * 64;
   constexpr int NV = kKT * NTL;            // rows gathered per round
@@ -345,6 +346,7 @@ __global__ __launch_bounds__(NHG * NSUB * 64) void attn_kernel(
   __shared__ __align__(16) uint8_t Ks_raw[kKsBytes];
   uint8_t (*Ks)[kTileBytes] = reinterpret_cast<uint8_t (*)[kTileBytes]>(Ks_raw);
   __shared__ __align__(16) uint8_t vld[NTL][kKT];  // slot v of a tile holds a key
+  __shared__ __align__(16) uint8_t hz_rows[FUSED ? kHzMax : 1][kD * 2];  // FUSED: entries pooled here
   __shared__ float2 rcs_all[ROPE ? NHG * NSUB : 1][kRope / 2];  // RoPE (cos, sin) per pair at the row's position, per wave
 
   const int split = blockIdx.x;
@@ -455,9 +457,10 @@ __global__ __launch_bounds__(NHG * NSUB * 64) void attn_kernel(
     }
   };
 
-  // FUSED: entries of this split that the launch's compression rewrites are not read from the
-  // cache. The workgroup pools them itself first (with the same arithmetic, before its own
-  // state is live) into their tile slots, which the gathered rows then leave alone.
+  // FUSED: entries of this split that the launch's compression rewrites (at most max_new <=
+  // kHzMax) are not read from the cache. The workgroup pools them itself first, with the same
+  // arithmetic and before its own state is live, into a side buffer that the gather copies
+  // into their tile slots in whichever round holds them.
   int64_t hz_lo = 0, hz_hi = 0;
   if (FUSED) {
     hz_lo = k_lo > f_new ? k_lo : f_new;
@@ -466,14 +469,12 @@ __global__ __launch_bounds__(NHG * NSUB * 64) void attn_kernel(
     hz_hi = hz_hi < k_hi ? hz_hi : k_hi;
     for (int64_t e = hz_lo; e < hz_hi; ++e) {  // uniform
       auto to_tile = [&](int64_t i, int64_t, int dg, const float (&o)[8]) {
-        const int v = (int)(i - k_lo);
-        const int tl = v / kKT, vr = v % kKT;
         u32x4 w;
         w.x = pack_bf16x2(o[0], o[1]);
         w.y = pack_bf16x2(o[2], o[3]);
         w.z = pack_bf16x2(o[4], o[5]);
         w.w = pack_bf16x2(o[6], o[7]);
-        *reinterpret_cast<u32x4*>(Ks[tl] + vr * 256 + 16 * (dg ^ ks_swz(vr))) = w;
+        *reinterpret_cast<u32x4*>(hz_rows[i - hz_lo] + 16 * dg) = w;
       };
       if (job.z)
         compress_block_to<NT, 16, 4, true, 8, NT / 64, false>(job.kv, job.z, kv_off, ent_off, job.first_entry, kD, m,
@@ -484,6 +485,7 @@ __global__ __launch_bounds__(NHG * NSUB * 64) void attn_kernel(
                                                               m, job.max_new, to_tile, b, e - f_new, nullptr, nullptr,
                                                               jpg);
     }
+    if (hz_lo < hz_hi) __syncthreads();  // the side rows are read by other threads of the gather
   }
 
   // queries of this wave's 16 heads as MFMA B operands (d-slots 8g..8g+7 of each 32-chunk)
@@ -558,9 +560,15 @@ __global__ __launch_bounds__(NHG * NSUB * 64) void attn_kernel(
       const int tl = v / kKT, vr = v % kKT;
       const bool ok = (okm >> j) & 1u;
       const int sw = ks_swz(vr);
-      // (FUSED: a slot the workgroup pooled itself keeps its row)
+      // (FUSED: a slot the workgroup pooled itself takes its row from the side buffer)
       const bool own = FUSED && t0 + v >= hz_lo && t0 + v < hz_hi;
-      if (!own) {
+      if (own) {
+        const uint8_t* src = hz_rows[FUSED ? t0 + v - hz_lo : 0];
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          *reinterpret_cast<u32x4*>(Ks[tl] + vr * 256 + 16 * ((4 * qq + u) ^ sw)) =
+              *reinterpret_cast<const u32x4*>(src + 16 * (4 * qq + u));
+      } else {
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq)
           *reinterpret_cast<u32x4*>(Ks[tl] + vr * 256 + 16 * ((4 * qq + u) ^ sw)) = ok ? r[j][qq] : u32x4{0, 0, 0, 0};
@@ -729,24 +737,13 @@ hipError_t launch_nhg(int H, dim3 grid, hipStream_t st, const uint16_t* q, const
       CSL_ATTN_LAUNCH(NHG, 1, 0);          \
     break;
   if constexpr (FUSED) {
-    // single-round splits only (one or two tiles)
-#define CSL_ATTN_FUSED_CASE(NHG)           \
-  case NHG:                                \
-    if (tiles == 1)                        \
-      CSL_ATTN_LAUNCH(NHG, 1, 1);          \
-    else if (tiles == 2)                   \
-      CSL_ATTN_LAUNCH(NHG, 1, 2);          \
-    else                                   \
-      return hipErrorInvalidValue;         \
-    break;
     switch (H / 16) {
-      CSL_ATTN_FUSED_CASE(1)
-      CSL_ATTN_FUSED_CASE(2)
-      CSL_ATTN_FUSED_CASE(4)
-      CSL_ATTN_FUSED_CASE(8)
+      CSL_ATTN_CASE(1)
+      CSL_ATTN_CASE(2)
+      CSL_ATTN_CASE(4)
+      CSL_ATTN_CASE(8)
       default: return hipErrorInvalidValue;
     }
-#undef CSL_ATTN_FUSED_CASE
   } else {
     switch (H / 16) {
       CSL_ATTN_CASE(1)

@@ -391,11 +391,12 @@ int csl_csa_decode_step(const csl_csa_step* s, void* stream);
  *     csl_hca_attn_decode(q, ckv, kv, kv_off, ent_off, q_pos, m, n_win, B, T, H, 128, ...)
  * in that order on one stream, with the same outputs up to the rounding order of the pooled
  * sums (one bf16 unit in a compressed entry, and what follows from it in out and lse). For H
- * in {16, 32, 64, 128}, B * (T + max_new_entries) <= 65535 and attention splits of at most
- * 128 keys (the split plan of decode batches, csl_attn_workspace_bytes' plan) both run in
- * one launch: spare workgroups pool the new entries into the cache while the others attend,
- * and an attention workgroup whose key range holds an entry being rewritten pools that entry
- * itself from the raw rows instead of reading the cache. In a decode step no query sees the entry its own
+ * in {16, 32, 64, 128}, 1 <= max_new_entries <= 4 and B * (T + max_new_entries) <= 65535
+ * (and rows of more than 64 keys at fewer than 512 query rows, whose attention plan does not
+ * multiply a row's few tiles at once) both run in one launch: spare workgroups pool the new
+ * entries into the cache while the others attend, and an attention workgroup whose key range
+ * holds an entry being rewritten pools that entry itself from the raw rows instead of
+ * reading the cache. In a decode step no query sees the entry its own
  * token completes (a query sees only entries before its own block), so the compression then
  * costs the attention nothing. Other head counts run the two calls one after the other. All
  * fields follow the two calls' argument rules (D = 128, bf16 cache) and are validated before

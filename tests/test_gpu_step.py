@@ -274,6 +274,10 @@ def _hca_step_vs_calls(lengths, q_pos, m, H, T, first, max_new, has_z=True, extr
     ((131072, 9000), (131072, 9000), 128, 64, 1, (1021, 67), 3, True, True),
     ((20000, 3000), (20000, 3000), 4, 128, 1, (4900, 700), 60, True, False),
     ((20000,), (19000,), 4, 16, 40, (4700,), 70, True, False),      # 40 positions, the prefetching tile loop
+    # splits of 3 tiles walked by the prefetching loop, the compression in the same launch, the
+    # two rewritten entries seen by every row: pooled into the side rows, copied in the last round
+    ((600007,), (599992,), 128, 16, 16, (4685,), 2, True, False),
+    ((600007,), (599992,), 128, 64, 16, (4685,), 2, True, True),
 ])
 def test_hca_decode_step_matches_separate_calls(lengths, q_pos, m, H, T, first, max_new, has_z, extras):
     _hca_step_vs_calls(lengths, q_pos, m, H, T, first, max_new, has_z, extras)
