@@ -185,8 +185,8 @@ __device__ __forceinline__ void tile_compute(const uint8_t* Ks, const uint8_t* v
         mx = fmaxf(mx, sacc[mb][i]);
       }
   }
-  mx = fmaxf(mx, shfl_xor_f(mx, 16));
-  mx = fmaxf(mx, shfl_xor_f(mx, 32));
+  mx = xor_max<16>(mx);
+  mx = xor_max<32>(mx);
   mx *= scale_log2;  // scale > 0, so the maximum commutes with the scaling
   if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleSlack) != 0) {
     const float m_new = fmaxf(m_run, mx);
@@ -256,8 +256,8 @@ __device__ __forceinline__ void attn_write(const f32x4 (&oacc)[8], float m_run, 
                                            const float2* rcs) {
   // reduce the lane-partial denominators across the 4 lane groups
   float l = l_run;
-  l += shfl_xor_f(l, 16);
-  l += shfl_xor_f(l, 32);
+  l = xor_sum<16>(l);
+  l = xor_sum<32>(l);
   const bool single = (gridDim.x == 1);
   // sink logit in base 2 (-inf without a sink; partials never take it)
   const float zs = (single && sink) ? sink[head] * kLog2e : -INFINITY;

@@ -14,8 +14,8 @@
 //
 // Layout: a thread owns 8 consecutive dimensions (16 bytes of bf16) of one entry and a
 // strided subset of its rows; TPE = D/8 threads cover one row, RS row-splits of the same
-// entry sit TPE lanes apart inside a wave and merge their partial softmax states with
-// xor-shuffles, and for long chunks RSX waves split the rows further and merge through LDS
+// entry sit TPE lanes apart inside a wave and merge their partial softmax states through
+// lane swaps, and for long chunks RSX waves split the rows further and merge through LDS
 // (an m = 128 entry then loads in one round trip). Loads are 16-byte, row-contiguous across
 // the TPE lanes, so a wave reads whole 256-byte rows. It reads 2*m*D*2 bytes and writes D*4
 // (fp32) or D*2 (bf16) bytes per entry (twice the reads with DUAL).
@@ -46,6 +46,17 @@ struct StoreEntry {
     }
   }
 };
+
+// Maximum (MAX) or sum of v over the RS in-wave row-splits of an entry, which sit TPE, 2 TPE,
+// 4 TPE lanes apart; every lane of the entry gets the same bits.
+template <int TPE, int RS>
+__device__ __forceinline__ float splits_reduce(float v, bool MAX) {
+  static_assert(RS == 1 || RS == 2 || RS == 4 || RS == 8, "power-of-two in-wave splits");
+  if constexpr (RS >= 2) v = MAX ? xor_max<TPE>(v) : xor_sum<TPE>(v);
+  if constexpr (RS >= 4) v = MAX ? xor_max<2 * TPE>(v) : xor_sum<2 * TPE>(v);
+  if constexpr (RS >= 8) v = MAX ? xor_max<4 * TPE>(v) : xor_sum<4 * TPE>(v);
+  return v;
+}
 
 // One workgroup of NT threads compresses the NT / (TPE * RS * RSX) entries first_entry[b] +
 // blk * that .. of sequence b (entries past max_new or past the sequence end are skipped) and
@@ -120,15 +131,17 @@ __device__ __forceinline__ void compress_block_to(
         }
       }
       if (HAS_Z) {
+        // the running maximum stays in logit units; 2^(z log2 e - mu log2 e) is one fma per row
         float zl[ROWS][8];
 #pragma unroll
         for (int u = 0; u < ROWS; ++u) {
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
-            zl[u][2 * w] = bf16lo(zr[u][w]) * kLog2e;
-            zl[u][2 * w + 1] = bf16hi(zr[u][w]) * kLog2e;
+            zl[u][2 * w] = bf16lo(zr[u][w]);
+            zl[u][2 * w + 1] = bf16hi(zr[u][w]);
           }
         }
+        float nb[8];
 #pragma unroll
         for (int d = 0; d < 8; ++d) {
           float cmax = zl[0][d];
@@ -136,18 +149,19 @@ __device__ __forceinline__ void compress_block_to(
           for (int u = 1; u < ROWS; ++u)
             if (u < cnt) cmax = fmaxf(cmax, zl[u][d]);
           const float nmu = fmaxf(mu[d], cmax);
-          const float alpha = __builtin_amdgcn_exp2f(mu[d] - nmu);  // 0 on the first step
+          const float alpha = __builtin_amdgcn_exp2f((mu[d] - nmu) * kLog2e);  // 0 on the first step
           s[d] *= alpha;
           acc[d] *= alpha;
           mu[d] = nmu;
+          nb[d] = -nmu * kLog2e;
         }
 #pragma unroll
         for (int u = 0; u < ROWS; ++u) {
           if (u < cnt) {
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-              const float e0 = __builtin_amdgcn_exp2f(zl[u][2 * w] - mu[2 * w]);
-              const float e1 = __builtin_amdgcn_exp2f(zl[u][2 * w + 1] - mu[2 * w + 1]);
+              const float e0 = __builtin_amdgcn_exp2f(fmaf(zl[u][2 * w], kLog2e, nb[2 * w]));
+              const float e1 = __builtin_amdgcn_exp2f(fmaf(zl[u][2 * w + 1], kLog2e, nb[2 * w + 1]));
               s[2 * w] += e0;
               s[2 * w + 1] += e1;
               acc[2 * w] = fmaf(e0, bf16lo(kr[u][w]), acc[2 * w]);
@@ -176,34 +190,49 @@ __device__ __forceinline__ void compress_block_to(
     }
   }
 
-  // merge the RS partial states of one entry inside the wave (lanes TPE*2^j apart)
+  // Merge the NSPLIT partial states (mu, s, acc) of each dimension in two passes: the maximum
+  // logit over all splits, then each split's sums rescaled to it once and added up. Inside a
+  // wave the splits sit TPE * 2^j lanes apart and combine through lane swaps; the RSX waves of
+  // an entry meet in LDS.
+  float M[8];
 #pragma unroll
-  for (int step = 1; step < RS; step <<= 1) {
-    const int mask = TPE * step;
+  for (int d = 0; d < 8; ++d) M[d] = mu[d];
 #pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      const float mu2 = shfl_xor_f(mu[d], mask);
-      const float s2 = shfl_xor_f(s[d], mask);
-      const float a2 = shfl_xor_f(acc[d], mask);
-      const float M = fmaxf(mu[d], mu2);
-      if (M == -INFINITY) continue;  // neither side saw a row
-      const float f1 = __builtin_amdgcn_exp2f(mu[d] - M);
-      const float f2 = __builtin_amdgcn_exp2f(mu2 - M);
-      s[d] = s[d] * f1 + s2 * f2;
-      acc[d] = acc[d] * f1 + a2 * f2;
-      mu[d] = M;
-    }
-  }
-
-  if (RSX > 1) {
-    // the RSX waves of an entry: lanes with rsw == 0 post their state, the first wave merges
-    __shared__ float xs[RSX > 1 ? EPB : 1][RSX][TPE][3][8];
+  for (int d = 0; d < 8; ++d) M[d] = splits_reduce<TPE, RS>(M[d], true);
+  if constexpr (RSX > 1) {
+    __shared__ __align__(16) float xm[EPB][RSX][TPE][8];
     if (rsw == 0) {
 #pragma unroll
+      for (int d = 0; d < 8; ++d) xm[el][rsx][dg][d] = M[d];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int d = 0; d < 8; ++d) M[d] = xm[el][0][dg][d];
+#pragma unroll
+    for (int w = 1; w < RSX; ++w) {
+#pragma unroll
+      for (int d = 0; d < 8; ++d) M[d] = fmaxf(M[d], xm[el][w][dg][d]);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    // a split that saw no row (mu = -inf) adds nothing
+    const float f = mu[d] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mu[d] - M[d]) * kLog2e);
+    s[d] *= f;
+    acc[d] *= f;
+  }
+#pragma unroll
+  for (int d = 0; d < 8; ++d) {
+    s[d] = splits_reduce<TPE, RS>(s[d], false);
+    acc[d] = splits_reduce<TPE, RS>(acc[d], false);
+  }
+  if constexpr (RSX > 1) {
+    __shared__ __align__(16) float xs[EPB][RSX][TPE][2][8];
+    if (rsw == 0 && rsx > 0) {
+#pragma unroll
       for (int d = 0; d < 8; ++d) {
-        xs[el][rsx][dg][0][d] = mu[d];
-        xs[el][rsx][dg][1][d] = s[d];
-        xs[el][rsx][dg][2][d] = acc[d];
+        xs[el][rsx][dg][0][d] = s[d];
+        xs[el][rsx][dg][1][d] = acc[d];
       }
     }
     __syncthreads();
@@ -212,14 +241,8 @@ __device__ __forceinline__ void compress_block_to(
       for (int w = 1; w < RSX; ++w) {
 #pragma unroll
         for (int d = 0; d < 8; ++d) {
-          const float mu2 = xs[el][w][dg][0][d], s2 = xs[el][w][dg][1][d], a2 = xs[el][w][dg][2][d];
-          const float M = fmaxf(mu[d], mu2);
-          if (M == -INFINITY) continue;
-          const float f1 = __builtin_amdgcn_exp2f(mu[d] - M);
-          const float f2 = __builtin_amdgcn_exp2f(mu2 - M);
-          s[d] = s[d] * f1 + s2 * f2;
-          acc[d] = acc[d] * f1 + a2 * f2;
-          mu[d] = M;
+          s[d] += xs[el][w][dg][0][d];
+          acc[d] += xs[el][w][dg][1][d];
         }
       }
     }

@@ -60,6 +60,34 @@ __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
 
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, kWave); }
 
+// The pair (v, value of lane ^ MASK) in some order, MASK = 8, 16 or 32, without a trip through
+// LDS: row_ror:8 (DPP) is xor 8 inside a 16-lane row; gfx950's permlane16_swap returns the
+// (even row, odd row) pair of each two 16-lane rows and permlane32_swap the (lower, upper)
+// half pair. Combined by a commutative operation, the two lanes of a pair get equal bits.
+template <int MASK>
+__device__ __forceinline__ float2 xor_pair(float v) {
+  static_assert(MASK == 8 || MASK == 16 || MASK == 32, "lane distances served by DPP and row swaps");
+  if constexpr (MASK == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  } else if constexpr (MASK == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  } else {
+    return make_float2(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf, false)));
+  }
+}
+template <int MASK>
+__device__ __forceinline__ float xor_sum(float v) {
+  const float2 p = xor_pair<MASK>(v);
+  return p.x + p.y;
+}
+template <int MASK>
+__device__ __forceinline__ float xor_max(float v) {
+  const float2 p = xor_pair<MASK>(v);
+  return fmaxf(p.x, p.y);
+}
+
 // Immediate of s_waitcnt in the gfx9 family's encoding (gfx950 included): vmcnt in bits 3:0
 // and 15:14, expcnt in bits 6:4, lgkmcnt in bits 11:8; a field at its maximum does not wait.
 // waitcnt_vm(n): wait until at most n vector memory operations of this wave are outstanding.
