@@ -14,11 +14,11 @@
 //
 // Layout: a thread owns 8 consecutive dimensions (16 bytes of bf16) of one entry and a
 // strided subset of its rows; TPE = D/8 threads cover one row, RS row-splits of the same
-// entry sit TPE lanes apart inside a wave and merge their partial softmax states through
-// lane swaps, and for long chunks RSX waves split the rows further and merge through LDS
-// (an m = 128 entry then loads in one round trip). Loads are 16-byte, row-contiguous across
-// the TPE lanes, so a wave reads whole 256-byte rows. It reads 2*m*D*2 bytes and writes D*4
-// (fp32) or D*2 (bf16) bytes per entry (twice the reads with DUAL).
+// entry sit TPE lanes apart inside a wave and merge their partial softmax states with
+// xor-shuffles; for long chunks RSX waves split the rows further (an m = 128 entry then
+// loads in one round trip) and merge in two passes, through lane swaps and LDS. Loads are
+// 16-byte, row-contiguous across the TPE lanes, so a wave reads whole 256-byte rows. It reads
+// 2*m*D*2 bytes and writes D*4 (fp32) or D*2 (bf16) bytes per entry (twice the reads with DUAL).
 #pragma once
 
 #include "device_common.h"
@@ -131,17 +131,15 @@ __device__ __forceinline__ void compress_block_to(
         }
       }
       if (HAS_Z) {
-        // the running maximum stays in logit units; 2^(z log2 e - mu log2 e) is one fma per row
         float zl[ROWS][8];
 #pragma unroll
         for (int u = 0; u < ROWS; ++u) {
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
-            zl[u][2 * w] = bf16lo(zr[u][w]);
-            zl[u][2 * w + 1] = bf16hi(zr[u][w]);
+            zl[u][2 * w] = bf16lo(zr[u][w]) * kLog2e;
+            zl[u][2 * w + 1] = bf16hi(zr[u][w]) * kLog2e;
           }
         }
-        float nb[8];
 #pragma unroll
         for (int d = 0; d < 8; ++d) {
           float cmax = zl[0][d];
@@ -149,19 +147,18 @@ __device__ __forceinline__ void compress_block_to(
           for (int u = 1; u < ROWS; ++u)
             if (u < cnt) cmax = fmaxf(cmax, zl[u][d]);
           const float nmu = fmaxf(mu[d], cmax);
-          const float alpha = __builtin_amdgcn_exp2f((mu[d] - nmu) * kLog2e);  // 0 on the first step
+          const float alpha = __builtin_amdgcn_exp2f(mu[d] - nmu);  // 0 on the first step
           s[d] *= alpha;
           acc[d] *= alpha;
           mu[d] = nmu;
-          nb[d] = -nmu * kLog2e;
         }
 #pragma unroll
         for (int u = 0; u < ROWS; ++u) {
           if (u < cnt) {
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-              const float e0 = __builtin_amdgcn_exp2f(fmaf(zl[u][2 * w], kLog2e, nb[2 * w]));
-              const float e1 = __builtin_amdgcn_exp2f(fmaf(zl[u][2 * w + 1], kLog2e, nb[2 * w + 1]));
+              const float e0 = __builtin_amdgcn_exp2f(zl[u][2 * w] - mu[2 * w]);
+              const float e1 = __builtin_amdgcn_exp2f(zl[u][2 * w + 1] - mu[2 * w + 1]);
               s[2 * w] += e0;
               s[2 * w + 1] += e1;
               acc[2 * w] = fmaf(e0, bf16lo(kr[u][w]), acc[2 * w]);
@@ -190,16 +187,34 @@ __device__ __forceinline__ void compress_block_to(
     }
   }
 
-  // Merge the NSPLIT partial states (mu, s, acc) of each dimension in two passes: the maximum
-  // logit over all splits, then each split's sums rescaled to it once and added up. Inside a
-  // wave the splits sit TPE * 2^j lanes apart and combine through lane swaps; the RSX waves of
-  // an entry meet in LDS.
-  float M[8];
+  if constexpr (RSX == 1) {
+    // one wave per entry: merge the RS partial states pairwise inside the wave (lanes TPE*2^j
+    // apart), each pair with its own rescale
 #pragma unroll
-  for (int d = 0; d < 8; ++d) M[d] = mu[d];
+    for (int step = 1; step < RS; step <<= 1) {
+      const int mask = TPE * step;
 #pragma unroll
-  for (int d = 0; d < 8; ++d) M[d] = splits_reduce<TPE, RS>(M[d], true);
-  if constexpr (RSX > 1) {
+      for (int d = 0; d < 8; ++d) {
+        const float mu2 = shfl_xor_f(mu[d], mask);
+        const float s2 = shfl_xor_f(s[d], mask);
+        const float a2 = shfl_xor_f(acc[d], mask);
+        const float M = fmaxf(mu[d], mu2);
+        if (M == -INFINITY) continue;  // neither side saw a row
+        const float f1 = __builtin_amdgcn_exp2f(mu[d] - M);
+        const float f2 = __builtin_amdgcn_exp2f(mu2 - M);
+        s[d] = s[d] * f1 + s2 * f2;
+        acc[d] = acc[d] * f1 + a2 * f2;
+        mu[d] = M;
+      }
+    }
+  } else {
+    // an entry split over RSX waves (the few-entry layout of a decode step): merge its NSPLIT
+    // partial states in two passes, the maximum logit of each dimension over all splits and
+    // then each split's sums rescaled to it once and added up. Inside a wave the splits combine
+    // through lane swaps, the waves meet in LDS.
+    float M[8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) M[d] = splits_reduce<TPE, RS>(mu[d], true);
     __shared__ __align__(16) float xm[EPB][RSX][TPE][8];
     if (rsw == 0) {
 #pragma unroll
@@ -213,20 +228,13 @@ __device__ __forceinline__ void compress_block_to(
 #pragma unroll
       for (int d = 0; d < 8; ++d) M[d] = fmaxf(M[d], xm[el][w][dg][d]);
     }
-  }
 #pragma unroll
-  for (int d = 0; d < 8; ++d) {
-    // a split that saw no row (mu = -inf) adds nothing
-    const float f = mu[d] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mu[d] - M[d]) * kLog2e);
-    s[d] *= f;
-    acc[d] *= f;
-  }
-#pragma unroll
-  for (int d = 0; d < 8; ++d) {
-    s[d] = splits_reduce<TPE, RS>(s[d], false);
-    acc[d] = splits_reduce<TPE, RS>(acc[d], false);
-  }
-  if constexpr (RSX > 1) {
+    for (int d = 0; d < 8; ++d) {
+      // a split that saw no row (mu = -inf) adds nothing
+      const float f = mu[d] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mu[d] - M[d]);
+      s[d] = splits_reduce<TPE, RS>(s[d] * f, false);
+      acc[d] = splits_reduce<TPE, RS>(acc[d] * f, false);
+    }
     __shared__ __align__(16) float xs[EPB][RSX][TPE][2][8];
     if (rsw == 0 && rsx > 0) {
 #pragma unroll
