@@ -1,7 +1,6 @@
 // The finishing step of the long-row top-k selection ([P2] "Deep Dive", CSA top-k selection),
-// as workgroup-level device functions of NT threads: the standalone finishing kernel runs them
-// with 1024 threads, and the decode attention runs them in each of a row's workgroups before it
-// gathers the selected entries.
+// as workgroup-level device functions of NT threads, which the finishing kernel runs with 1024
+// threads, one workgroup per query row.
 //
 // From the row's slice candidate lists (topk_common.h) it radix-selects the k best listed
 // entries on their 32-bit keys (lower id first within the last tied key), checks that the k-th
