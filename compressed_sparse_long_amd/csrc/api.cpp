@@ -531,6 +531,11 @@ int csl_csa_decode_step(const csl_csa_step* s, void* stream) {
   const int kt = key_type(s->k_dtype);
   const bool compress = s->max_new_entries > 0;
   const bool index = s->max_entries > 0;
+  // rows whose whole key list one attention workgroup holds: that workgroup makes the row's
+  // top-k selection itself (the same ids, also written to idx) instead of a top-k launch
+  const bool select_in_attn = !scoreless && !pvp && index &&
+                              csl::attention_selects_topk(s->B, s->T, s->H, s->k, max_keys, s->max_entries);
+  const csl::TopkIn tk{s->scores, s->ld, s->m, s->max_entries, s->idx};
   hipError_t e = hipSuccess;
   if (scoreless) {
     if (compress && overlap)
@@ -562,13 +567,13 @@ int csl_csa_decode_step(const csl_csa_step* s, void* stream) {
                               nullptr, pvp);
   }
   if (e != hipSuccess) return hip_status(e, "csa_decode_step launch");
-  if (!scoreless)
+  if (!scoreless && !select_in_attn)
     e = csl::launch_topk(s->scores, s->ld, s->ent_off, s->q_pos, s->m, s->B, s->T, s->k, s->max_entries, s->idx,
                          s->topk_ws, csl::indexer_prepares_topk(topk_ws, s->T, s->max_entries), hs);
   if (e != hipSuccess) return hip_status(e, "csa_decode_step launch");
   return hip_status(csl::launch_attention(true, s->q, s->ckv, s->idx, s->k, s->kv, s->kv_off, s->ent_off, s->q_pos, 1,
                                           s->n_win, s->B, s->T, s->H, s->scale, (int64_t)1 << 62, max_keys, s->out,
-                                          s->lse, s->attn_ws, ex, hs, pvp),
+                                          s->lse, s->attn_ws, ex, hs, pvp, nullptr, select_in_attn ? &tk : nullptr),
                     "csa_decode_step launch");
 }
 

@@ -57,12 +57,24 @@ bool attention_carries_job(int B, int T, int H, int64_t max_keys, int64_t max_ne
          (int64_t)B * T + (int64_t)B * max_new <= 65535 && p.nsub == 1;
 }
 
+bool attention_selects_topk(int B, int T, int H, int k, int64_t max_keys, int64_t max_entries) {
+  // one workgroup per query row holding the whole key list (the parallel-tile plan), whose
+  // threads hold the row's scores (kSelItems each) and whose LDS holds its k selected slots
+  const AttnPlan p = attn_plan(B, T, H, max_keys);
+  if (p.nsub <= 1 || k < 1 || k > kSelMax) return false;
+  const int64_t threads = (int64_t)(H / 16) * p.nsub * kWave;
+  return max_entries >= 1 && max_entries <= kSelItems * threads;
+}
+
 hipError_t launch_attention(bool sparse, const void* q, const void* ckv, const int32_t* idx, int k, const void* kv,
                             const int64_t* kv_off, const int64_t* ent_off, const int64_t* q_pos, int m, int n_win,
                             int B, int T, int H, float scale, int64_t max_entries, int64_t max_keys, float* out,
                             float* lse, void* ws, const AttnExtras& ex, hipStream_t st, const PagedView* paged,
-                            const HcaJob* job) {
+                            const HcaJob* job, const TopkIn* topk) {
   if (job && (sparse || !attention_carries_job(B, T, H, max_keys, job->max_new))) return hipErrorInvalidValue;
+  if (topk && (!sparse || job || paged || !topk->scores || !topk->idx || topk->m < 1 ||
+               !attention_selects_topk(B, T, H, k, max_keys, topk->max_entries)))
+    return hipErrorInvalidValue;
   const AttnPlan p = attn_plan(B, T, H, max_keys);
   AttnLayout lay;
   if (paged) {
@@ -90,7 +102,7 @@ hipError_t launch_attention(bool sparse, const void* q, const void* ckv, const i
   const uint16_t* k16 = static_cast<const uint16_t*>(kv);
 #define CSL_ATTN_NHG(SP, RP, PG, FU)                                                                            \
   launch_nhg<SP, RP, PG, FU>(H, grid, st, q16, c16, idx, k, k16, kv_off, ent_off, q_pos, m, n_win, T, sl2,     \
-                             max_entries, p, out, lse, ws_o, ws_lse, ws_rope, ex, lay, rows, hj)
+                             max_entries, p, out, lse, ws_o, ws_lse, ws_rope, ex, lay, rows, hj, topk)
   const bool rope = ex.rope_dims > 0;
   hipError_t e;
   if (job)

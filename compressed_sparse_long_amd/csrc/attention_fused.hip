@@ -12,7 +12,8 @@ hipError_t launch_attention_fused(bool rope, bool paged, int H, dim3 grid, hipSt
                                   const AttnLayout& lay, int rows, const HcaJob& job) {
 #define CSL_FUSED(RP, PG)                                                                                       \
   launch_nhg<false, RP, PG, true>(H, grid, st, q, ckv, nullptr, 0, kv, kv_off, ent_off, q_pos, m, n_win, T,    \
-                                  scale_log2, max_entries, p, out, lse, ws_o, ws_lse, ws_rope, ex, lay, rows, job)
+                                  scale_log2, max_entries, p, out, lse, ws_o, ws_lse, ws_rope, ex, lay, rows, job,   \
+                                  nullptr)
   if (paged) return rope ? CSL_FUSED(true, true) : CSL_FUSED(false, true);
   return rope ? CSL_FUSED(true, false) : CSL_FUSED(false, false);
 #undef CSL_FUSED

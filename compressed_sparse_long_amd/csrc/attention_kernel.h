@@ -29,12 +29,18 @@
 //     epilogue or in the merge;
 //   * FUSED (an HCA step): rows of the grid before the query rows are workgroups that pool the
 //     step's new entries into the cache, and a workgroup whose keys include an entry being
-//     rewritten pools it from the raw rows into its tile instead of reading the cache.
+//     rewritten pools it from the raw rows into its tile instead of reading the cache;
+//   * TOPK (a CSA step whose rows each fit one workgroup): the workgroup selects its row's
+//     top-k from the indexer's scores itself (topk_short.h), into LDS and the id buffer, and
+//     gathers from that selection.
 #pragma once
+
+#include <type_traits>
 
 #include "compress_common.h"
 #include "device_common.h"
 #include "launch.h"
+#include "topk_short.h"
 
 namespace csl {
 
@@ -56,6 +62,8 @@ constexpr int kRope = 64;             // partial RoPE: the last 64 dims ([P1] se
 constexpr int kRopeOff = kD - kRope;  // first rotated dim
 constexpr int kRopeKK = kRopeOff / 32;  // first rotated 32-dim chunk of the query operand
 constexpr int kHzMax = 4;  // FUSED: most entries a split can find rewritten (max_new <= this)
+constexpr int kSelItems = 4;   // TOPK: scores per thread, so rows of up to 4 * threads entries
+constexpr int kSelMax = 256;   // TOPK: most selected slots (a one-workgroup plan holds 4 tiles)
 
 struct RowGeom {
   int64_t ent_base, n_ent, kv_base, win_lo, win_cnt, nvis;
@@ -320,17 +328,18 @@ __device__ __forceinline__ void merge_state(f32x4 (&o)[8], float& m, float& l, c
 // NSUB > 1 (with MODE 1): the workgroup holds NSUB tiles at once and its waves are NSUB groups
 // of NHG, group s multiplying tile s, so the tiles' latencies overlap; the groups' states are
 // then merged through LDS into group 0, which writes the result.
-template <int NHG, int NSUB, bool SPARSE, int MODE, bool ROPE, bool PAGED, bool FUSED = false>
+template <int NHG, int NSUB, bool SPARSE, int MODE, bool ROPE, bool PAGED, bool FUSED = false, bool TOPK = false>
 __global__ __launch_bounds__(NHG * NSUB * 64) void attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ ckv, const int32_t* __restrict__ idx, int k,
     const uint16_t* __restrict__ kv, const int64_t* __restrict__ kv_off, const int64_t* __restrict__ ent_off,
     const int64_t* __restrict__ q_pos, int m, int n_win, int T, int H, float scale_log2, int64_t max_entries,
     int keys_per_split, float* __restrict__ out, float* __restrict__ lse_out, float* __restrict__ ws_o,
     float* __restrict__ ws_lse, const float* __restrict__ sink, double rope_theta1,
-    float2* __restrict__ ws_rope, AttnLayout lay, int nrows, HcaJob job) {
+    float2* __restrict__ ws_rope, AttnLayout lay, int nrows, HcaJob job, TopkIn tk) {
   constexpr bool MULTI = MODE == 0;
   static_assert(NSUB == 1 || MODE == 1, "parallel tiles take single-round splits of one tile each");
   static_assert(!FUSED || (NSUB == 1 && !SPARSE), "a fused launch is dense, one tile per wave group");
+  static_assert(!TOPK || (SPARSE && !FUSED && !MULTI), "the selection feeds a one-round sparse gather");
   constexpr int NTL = MULTI ? 1 : (NSUB > 1 ? NSUB : MODE);  // tiles held in LDS at once
   constexpr int NT = NHG * NSUB * 64;
   constexpr int NV = kKT * NTL;            // rows gathered per round
@@ -383,6 +392,14 @@ __global__ __launch_bounds__(NHG * NSUB * 64) void attn_kernel(
   const int sub = wave / NHG;  // tile of the round this wave multiplies (NSUB > 1)
 
   const int64_t k_lo = (int64_t)split * keys_per_split;
+  // TOPK: the row's selection first, into LDS (and the id buffer, for the caller)
+  __shared__ int32_t sel[TOPK ? kSelMax : 1];
+  __shared__ std::conditional_t<TOPK, ShortTopkLds<NT, kSelItems>, char> sel_lds;
+  if constexpr (TOPK) {
+    const int64_t n = short_row_count(ent_off, q_pos, b, t, tk.m, tk.max_entries);
+    short_row_topk<NT, kSelItems>(tk.scores + (int64_t)row * tk.ld, n, k, sel, tk.idx + (int64_t)row * k, sel_lds);
+    __syncthreads();
+  }
   // selected ids do not depend on the row geometry: the first ones load right away, from
   // clamped slots (or from q when there is no list), so the loads carry no branch
   const bool has_ids = SPARSE && k > 0;
@@ -391,7 +408,8 @@ __global__ __launch_bounds__(NHG * NSUB * 64) void attn_kernel(
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
       const int64_t slot = t0 + (j * NT + tid) / 4;
-      ids[j] = idx_row[has_ids ? (slot < k ? slot : k - 1) : 0];
+      const int64_t cs = has_ids ? (slot < k ? slot : k - 1) : 0;
+      ids[j] = TOPK ? sel[cs] : idx_row[cs];
     }
   };
   int32_t ids_cur[RPT], ids_nxt[RPT];
@@ -698,23 +716,34 @@ hipError_t launch_nhg(int H, dim3 grid, hipStream_t st, const uint16_t* q, const
                       int k, const uint16_t* kv, const int64_t* kv_off, const int64_t* ent_off, const int64_t* q_pos,
                       int m, int n_win, int T, float scale_log2, int64_t max_entries, const AttnPlan& p, float* out,
                       float* lse, float* ws_o, float* ws_lse, float2* ws_rope, const AttnExtras& ex,
-                      const AttnLayout& lay, int rows, const HcaJob& job) {
+                      const AttnLayout& lay, int rows, const HcaJob& job, const TopkIn* topk) {
   const int kps = p.keys_per_split;
   const int tiles = kps / kKT;  // 1 or 2: gathered in one round; more: the prefetching loop
   // a fused launch carries the step's compression only for head counts of 16, 32, 64 or 128
   if (FUSED && H != 16 && H != 32 && H != 64 && H != 128) return hipErrorInvalidValue;
-#define CSL_ATTN_LAUNCH(NHG, NSUB, MODE)                                                                       \
-  attn_kernel<NHG, NSUB, SPARSE, MODE, ROPE, PAGED, FUSED><<<grid, NHG * NSUB * 64, 0, st>>>(                 \
+  // the rows' own top-k selection rides only in one-workgroup plans of the packed sparse gather
+  if (topk && (p.nsub <= 1 || !SPARSE || PAGED || FUSED)) return hipErrorInvalidValue;
+  const TopkIn tki = topk ? *topk : TopkIn{};
+#define CSL_ATTN_LAUNCH_T(NHG, NSUB, MODE, TK)                                                                  \
+  attn_kernel<NHG, NSUB, SPARSE, MODE, ROPE, PAGED, FUSED, TK><<<grid, NHG * NSUB * 64, 0, st>>>(             \
       q, ckv, idx, k, kv, kv_off, ent_off, q_pos, m, n_win, T, H, scale_log2, max_entries, kps, out, lse, ws_o, \
-      ws_lse, ex.sink, ex.rope_theta1, ws_rope, lay, rows, job)
+      ws_lse, ex.sink, ex.rope_theta1, ws_rope, lay, rows, job, tki)
+#define CSL_ATTN_LAUNCH(NHG, NSUB, MODE) CSL_ATTN_LAUNCH_T(NHG, NSUB, MODE, false)
   if (p.nsub > 1) {  // a row's whole key list in one workgroup, its tiles multiplied at once
     if constexpr (FUSED) {
       return hipErrorInvalidValue;  // (its LDS holds no room for the job)
     } else {
-#define CSL_ATTN_PAR(NHG, NSUB)                     \
-  case NHG:                                        \
-    if (p.nsub != NSUB) return hipErrorInvalidValue; \
-    CSL_ATTN_LAUNCH(NHG, NSUB, 1);                 \
+#define CSL_ATTN_PAR(NHG, NSUB)                           \
+  case NHG:                                              \
+    if (p.nsub != NSUB) return hipErrorInvalidValue;       \
+    if constexpr (SPARSE && !PAGED) {                    \
+      if (topk)                                          \
+        CSL_ATTN_LAUNCH_T(NHG, NSUB, 1, true);           \
+      else                                               \
+        CSL_ATTN_LAUNCH(NHG, NSUB, 1);                   \
+    } else {                                             \
+      CSL_ATTN_LAUNCH(NHG, NSUB, 1);                     \
+    }                                                    \
     break;
       switch (H / 16) {
         CSL_ATTN_PAR(1, 4)
@@ -759,6 +788,7 @@ hipError_t launch_nhg(int H, dim3 grid, hipStream_t st, const uint16_t* q, const
   }
 #undef CSL_ATTN_CASE
 #undef CSL_ATTN_LAUNCH
+#undef CSL_ATTN_LAUNCH_T
   return hipGetLastError();
 }
 

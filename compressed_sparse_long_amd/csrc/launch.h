@@ -96,14 +96,27 @@ struct HcaJob {
   int64_t max_new = 0;
   uint16_t* ckv = nullptr;
 };
+// A CSA row's top-k selection made inside the sparse attention launch, where one workgroup
+// per query row covers the row's whole key list: the indexer's scores [B*T, ld] and the
+// selection's parameters; the selected ids are also written to the attention's idx buffer.
+struct TopkIn {
+  const float* scores = nullptr;
+  int64_t ld = 0;
+  int m = 1;                 // the indexer's compression ratio (visible entries floor(p / m))
+  int64_t max_entries = 0;
+  int32_t* idx = nullptr;    // [B*T, k]: the selection, also written here
+};
 AttnPlan attn_plan(int B, int T, int H, int64_t max_keys);
 size_t attn_workspace_bytes(int B, int T, int H, int64_t max_keys);
 hipError_t launch_attention(bool sparse, const void* q, const void* ckv, const int32_t* idx, int k, const void* kv,
                             const int64_t* kv_off, const int64_t* ent_off, const int64_t* q_pos, int m, int n_win,
                             int B, int T, int H, float scale, int64_t max_entries, int64_t max_keys, float* out,
                             float* lse, void* ws, const AttnExtras& ex, hipStream_t stream,
-                            const PagedView* paged = nullptr, const HcaJob* job = nullptr);
+                            const PagedView* paged = nullptr, const HcaJob* job = nullptr,
+                            const TopkIn* topk = nullptr);
 // whether launch_attention can carry an HcaJob for these shapes
 bool attention_carries_job(int B, int T, int H, int64_t max_keys, int64_t max_new);
+// whether the sparse attention launch can make the rows' top-k selection itself (a TopkIn)
+bool attention_selects_topk(int B, int T, int H, int k, int64_t max_keys, int64_t max_entries);
 
 }  // namespace csl

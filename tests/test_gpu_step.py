@@ -30,6 +30,10 @@ pytestmark = pytest.mark.gpu
     ((1 << 20, 40000, 4000, 3), 4, True, 1024, 8, False, 64, False),
     ((1 << 20, 600001), 4, True, 1024, 8, True, 64, False),
     ((1 << 20, 5), 4, True, 1024, 8, False, 64, True),
+    # short rows, one attention workgroup each, which then selects the row's top-k itself: rows
+    # with fewer entries than k, an empty row; 64 and 32 heads; fp8 keys
+    ((16000, 3000, 100, 0, 8192), 4, True, 128, 8, False, 64, False),
+    ((6000, 300, 8), 4, True, 100, 4, True, 32, False),
 ])
 def test_csa_decode_step_matches_separate_calls(lengths, m, has_z, k, HI, fp8, H, overlap):
     _step_vs_calls(lengths, m, has_z, k, HI, fp8, H, overlap, extras=False)
@@ -74,6 +78,36 @@ def test_csa_decode_step_finishes_crowded_rows_exactly():
         e0, e1 = lane.ent_off()[b], lane.ent_off()[b + 1]
         ref_s = csa.indexer(f64(li.qI[b, 0]), f64(li.w[b, 0]), keys[e0:e1])
         topk_band_check(got[b, 0], ref_s, lane.k, what=f"b={b}")
+
+
+def test_csa_decode_step_selects_ties_by_lowest_id():
+    """Short rows (one attention workgroup each, which makes the row's selection) whose indexer
+    keys take three values, so their scores tie in large blocks: the step's ids equal
+    topk_select's and a brute-force order of the step's own scores (score descending, lower id
+    first)."""
+    from compressed_sparse_long_amd import lanes
+    lane = W.Lane("csa", (4096, 2000, 300), (4096, 2000, 300), T=1, H=16, m=4, k=64, HI=4)
+    inp = synth.generate(W.Workload("ties", 31, (lane,)))
+    li = inp.lanes[0]
+    base = li.kI[:3].clone()
+    li.kI[:] = base[torch.arange(li.kI.shape[0]) % 3]
+    (cl,) = lanes.build_lanes(inp)
+    cl.compress_all()
+    res = []
+    for fused in (False, True):
+        cl.idx.fill_(-7)
+        cl.step(0, fused=fused)
+        torch.cuda.synchronize()
+        res.append((cl.idx.clone(), cl.scores.clone(), cl.out.clone()))
+    assert torch.equal(res[0][0], res[1][0]), "selected ids differ"
+    torch.testing.assert_close(res[1][2], res[0][2], rtol=0, atol=2e-3)
+    for b in range(lane.B):
+        n = lane.entries[b]
+        s = res[1][1][b, 0, :n].cpu().numpy()
+        best = sorted(range(n), key=lambda i: (-float(s[i]), i))[:min(n, lane.k)]
+        want = sorted(best) + [-1] * (lane.k - len(best))
+        assert res[1][0][b, 0].tolist() == want, f"b={b}: not the k best with lower ids first"
+        assert len(set(s.tolist())) <= 4, "the keys were meant to tie"
 
 
 def test_csa_decode_step_repeats_on_1m_rows():
