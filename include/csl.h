@@ -320,10 +320,16 @@ int csl_hca_attn_decode(const void* q, const void* ckv, const void* kv, const in
  * in that order on one stream, with the same outputs (ckv rows, scores, idx, out, lse) up to
  * the rounding order of the pooled sums where the compression runs inside the indexer launch
  * (one bf16 unit in a compressed entry). The calls' own argument rules apply to the fields
- * below, and everything is validated before anything is enqueued. Where the shapes allow (D == 128, m <= 8, the decode tiling of the
- * indexer), the compression runs in spare workgroups of the indexer launch instead of a
- * launch of its own; it never reads what the indexer writes, and the attention runs after
- * both. With kv_b (and z_b when z is given) set, the compression is csl_compress_kv_overlap
+ * below, and everything is validated before anything is enqueued. Where the shapes allow
+ * (D == 128, m <= 8, the decode tiling of the indexer), the compression runs in spare
+ * workgroups of the indexer launch instead of a launch of its own; it never reads what the
+ * indexer writes, and the attention runs after both. Where one attention workgroup per query
+ * row holds the row's whole key list (k + n_win spanning 2 to 4 tiles of 64 keys at H = 16,
+ * 32 or 64, 2 tiles at H = 128, fewer than 512 query rows, k <= 256, max_entries <=
+ * 1024 * H / 16 and <= 4096, unpaged), that workgroup selects the row's top-k from the scores
+ * itself, with csl_topk_select's rule, and writes the same ids to idx: the top-k launch is
+ * then left out.
+ * With kv_b (and z_b when z is given) set, the compression is csl_compress_kv_overlap
  * of the series pair (kv, z) and (kv_b, z_b) instead, carried the same way; kv_b and z_b
  * both NULL keeps single-series compression. With scores NULL the indexer and top-k calls
  * are replaced by csl_indexer_topk (no score matrix; topk_ws, topk_ws_bytes and ld are
