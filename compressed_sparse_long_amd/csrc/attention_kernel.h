@@ -392,14 +392,10 @@ __global__ __launch_bounds__(NHG * NSUB * 64) void attn_kernel(
   const int sub = wave / NHG;  // tile of the round this wave multiplies (NSUB > 1)
 
   const int64_t k_lo = (int64_t)split * keys_per_split;
-  // TOPK: the row's selection first, into LDS (and the id buffer, for the caller)
+  // TOPK: the row's selection, made below while the window rows are in flight, into LDS (and
+  // the id buffer, for the caller)
   __shared__ int32_t sel[TOPK ? kSelMax : 1];
   __shared__ std::conditional_t<TOPK, ShortTopkLds<NT, kSelItems>, char> sel_lds;
-  if constexpr (TOPK) {
-    const int64_t n = short_row_count(ent_off, q_pos, b, t, tk.m, tk.max_entries);
-    short_row_topk<NT, kSelItems>(tk.scores + (int64_t)row * tk.ld, n, k, sel, tk.idx + (int64_t)row * k, sel_lds);
-    __syncthreads();
-  }
   // selected ids do not depend on the row geometry: the first ones load right away, from
   // clamped slots (or from q when there is no list), so the loads carry no branch
   const bool has_ids = SPARSE && k > 0;
@@ -413,7 +409,12 @@ __global__ __launch_bounds__(NHG * NSUB * 64) void attn_kernel(
     }
   };
   int32_t ids_cur[RPT], ids_nxt[RPT];
-  load_ids(k_lo, ids_cur);
+  if (TOPK) {
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) ids_cur[j] = 0;  // (the window rows issued first read no id)
+  } else {
+    load_ids(k_lo, ids_cur);
+  }
   if (MULTI) load_ids(k_lo + NV, ids_nxt);
   const RowGeom geo = row_geom(kv_off, ent_off, q_pos, b, t, m, n_win, max_entries);
   const int64_t n_comp = SPARSE ? (int64_t)k : geo.nvis;  // compressed slots in the list
@@ -447,10 +448,11 @@ __global__ __launch_bounds__(NHG * NSUB * 64) void attn_kernel(
   auto clamp_round = [](int64_t x) { return (int)(x < 0 ? 0 : (x > NV ? NV : x)); };
   u32x4 r[RPT][4];
   uint32_t okm = 0;  // bit j: pair j's row holds a key
-  auto issue = [&](int64_t t0, const int32_t (&ids)[RPT]) {
+  // part 0: every row of the round; 1: its window rows only; 2: its compressed entries only
+  auto issue = [&](int64_t t0, const int32_t (&ids)[RPT], int part) {
     const int lim_c = clamp_round(n_comp - t0), lim_h = clamp_round(k_hi - t0);
 
-    okm = 0;
+    if (part != 2) okm = 0;
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
       const int pr = j * NT + tid;
@@ -458,6 +460,7 @@ __global__ __launch_bounds__(NHG * NSUB * 64) void attn_kernel(
       const int v = pr / 4;
       const uint32_t e = SPARSE ? (uint32_t)ids[j] : (uint32_t)(t0 + v);  // negative ids wrap to huge
       const bool comp = v < lim_c;
+      if (part != 0 && comp != (part == 2)) continue;
       const bool ok = in && v < lim_h && (!comp || e < n_ent32);
       uint64_t erow = e;
       if (PAGED) {  // the entry's pool row (a clamped table slot where it is not used)
@@ -523,7 +526,19 @@ __global__ __launch_bounds__(NHG * NSUB * 64) void attn_kernel(
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  if (k_lo < k_hi) issue(k_lo, ids_cur);
+  if constexpr (TOPK) {
+    // the window rows depend on no selection: they are in flight while the workgroup selects
+    // the row's entries (a barrier waits for no load), then the selected entries follow
+    if (k_lo < k_hi) issue(k_lo, ids_cur, 1);
+    const int64_t n = short_row_count(ent_off, q_pos, b, t, tk.m, tk.max_entries);
+    short_row_topk<NT, kSelItems>(tk.scores + (int64_t)row * tk.ld, tk.max_entries, n, k, sel,
+                                  tk.idx + (int64_t)row * k, sel_lds);
+    __syncthreads();
+    load_ids(k_lo, ids_cur);
+    if (k_lo < k_hi) issue(k_lo, ids_cur, 2);
+  } else {
+    if (k_lo < k_hi) issue(k_lo, ids_cur, 0);
+  }
 
   // partial RoPE: the row's (cos, sin) table, then the rotated query chunks as bf16 pairs.
   // Every wave builds its own copy, so no workgroup barrier (which would also wait for the
@@ -597,7 +612,7 @@ __global__ __launch_bounds__(NHG * NSUB * 64) void attn_kernel(
     if (ROPE && !MULTI) rotate_q();  // single round: the rows (and so the query) have landed
     // the next round's rows and the ids two rounds ahead go out while this one computes
     if (MULTI && t0 + NV < k_hi) {
-      issue(t0 + NV, ids_nxt);
+      issue(t0 + NV, ids_nxt, 0);
       if (SPARSE && t0 + 2 * NV < k_hi) load_ids(t0 + 2 * NV, ids_nxt);
     }
     if (NSUB > 1) {

@@ -34,11 +34,12 @@ __device__ __forceinline__ int64_t short_row_count(const int64_t* __restrict__ e
   return n < 0 ? 0 : n;
 }
 
-// Writes the selection to sel[0, k) (LDS) and out[0, k) (global). Every thread of the
-// workgroup calls it; it holds workgroup barriers, and the caller puts one more between it and
-// the first read of sel.
+// Writes the selection to sel[0, k) (LDS) and out[0, k) (global). srow holds at least cap >= n
+// readable scores (the row's stride allows max_entries), so the score loads need not wait for
+// n, whose own loads may still be in flight. Every thread of the workgroup calls it; it holds
+// workgroup barriers, and the caller puts one more between it and the first read of sel.
 template <int NT, int ITEMS>
-__device__ __forceinline__ void short_row_topk(const float* __restrict__ srow, int64_t n, int k,
+__device__ __forceinline__ void short_row_topk(const float* __restrict__ srow, int64_t cap, int64_t n, int k,
                                                int32_t* __restrict__ sel, int32_t* __restrict__ out,
                                                ShortTopkLds<NT, ITEMS>& L) {
   constexpr int NW = NT / kWave;
@@ -47,6 +48,16 @@ __device__ __forceinline__ void short_row_topk(const float* __restrict__ srow, i
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid % kWave;
+  // the scores first, from ids clamped to cap (no branch per load); the ids past the row are
+  // then marked invalid
+  float sv[ITEMS];
+  if (cap > 0) {
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+      const int64_t i = j * NT + tid;
+      sv[j] = srow[i < cap ? i : cap - 1];
+    }
+  }
   const uint32_t keep = (uint32_t)(n < k ? n : (int64_t)k);
   if ((int64_t)keep == n) {  // everything visible is selected
     for (int p = tid; p < k; p += NT) {
@@ -56,15 +67,13 @@ __device__ __forceinline__ void short_row_topk(const float* __restrict__ srow, i
     }
     return;
   }
-  // n > k >= 1 here: the loads read clamped ids (no branch per load), the ids past the row
-  // are then marked invalid
   uint32_t key[ITEMS];
   bool valid[ITEMS];
 #pragma unroll
   for (int j = 0; j < ITEMS; ++j) {
     const int i = j * NT + tid;
     valid[j] = i < n;
-    key[j] = score_key(srow[i < n ? i : n - 1]);
+    key[j] = valid[j] ? score_key(sv[j]) : 0u;
   }
   uint32_t prefix = 0u, need = keep;
   bool all_in = false;
@@ -75,7 +84,8 @@ __device__ __forceinline__ void short_row_topk(const float* __restrict__ srow, i
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j)
-      if (valid[j] && (pass == 0 || (key[j] >> (shift + 8)) == prefix)) atomicAdd(&L.hist[(key[j] >> shift) & 255u], 1u);
+      if (valid[j] && (pass == 0 || (key[j] >> (shift + 8)) == prefix))
+        atomicAdd(&L.hist[(key[j] >> shift) & 255u], 1u);
     __syncthreads();
     if (wave == 0) {
       // bins from the top down, 4 per lane: lane l holds bins 255 - 4l .. 252 - 4l
