@@ -23,19 +23,11 @@
 #include "launch.h"
 #include "topk_common.h"
 #include "topk_finish.h"
+#include "topk_short.h"
 
 namespace csl {
 
 namespace {
-
-__device__ __forceinline__ int64_t row_count(const int64_t* ent_off, const int64_t* q_pos, int b, int t, int m,
-                                             int64_t max_entries) {
-  const int64_t n_ent = ent_off[b + 1] - ent_off[b];
-  int64_t n = (q_pos[b] + t) / m;
-  n = n < n_ent ? n : n_ent;
-  n = n < max_entries ? n : max_entries;
-  return n < 0 ? 0 : n;
-}
 
 // ---------------------------------------------------------------------------------------
 // Long rows: slice candidates, then one finishing workgroup per row.
@@ -47,7 +39,7 @@ __global__ __launch_bounds__(kSlice) void topk_prepare_kernel(const float* __res
   __shared__ SliceScratch sc;
   const int row = blockIdx.y;
   const int b = row / T, t = row % T;
-  const int64_t n = row_count(ent_off, q_pos, b, t, m, max_entries);
+  const int64_t n = visible_entries(ent_off, q_pos, b, t, m, max_entries);
   if (n <= k || topk_row_dense(n, k)) return;  // the finishing kernel selects everything / searches the row
   const int64_t lo = (int64_t)blockIdx.x * kSlice;
   if (lo >= n) return;
@@ -130,7 +122,7 @@ __global__ __launch_bounds__(kFinNT) void topk_row_kernel(const float* __restric
   const int b = row / T, t = row % T;
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
-  const int64_t n = row_count(ent_off, q_pos, b, t, m, max_entries);
+  const int64_t n = visible_entries(ent_off, q_pos, b, t, m, max_entries);
   const uint32_t keep = (uint32_t)(n < k ? n : k);
   int32_t* out = idx + (int64_t)row * k;
   const float* srow = scores + (int64_t)row * ld;
@@ -284,7 +276,8 @@ __global__ __launch_bounds__(kFinNT) void topk_finish_kernel(const float* __rest
   const int row = blockIdx.x;
   const int b = row / T, t = row % T;
   const TopkRowWs rw = topk_row_ws(ws, row, max_entries, budget);
-  finish_row<kFinNT, CH>(scores + (int64_t)row * ld, rw, [&] { return row_count(ent_off, q_pos, b, t, m, max_entries); },
+  finish_row<kFinNT, CH>(scores + (int64_t)row * ld, rw,
+                         [&] { return visible_entries(ent_off, q_pos, b, t, m, max_entries); },
                          max_entries, budget, k, idx + (int64_t)row * k, lds);
 }
 

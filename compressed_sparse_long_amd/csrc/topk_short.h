@@ -23,10 +23,10 @@ struct ShortTopkLds {
 };
 
 // The visible entries of query row (b, t): floor(p / m) at position p = q_pos[b] + t, capped at
-// the sequence's entries and at max_entries.
-__device__ __forceinline__ int64_t short_row_count(const int64_t* __restrict__ ent_off,
-                                                   const int64_t* __restrict__ q_pos, int b, int t, int m,
-                                                   int64_t max_entries) {
+// the sequence's entries and at max_entries (every top-k kernel counts a row's entries so).
+__device__ __forceinline__ int64_t visible_entries(const int64_t* __restrict__ ent_off,
+                                                  const int64_t* __restrict__ q_pos, int b, int t, int m,
+                                                  int64_t max_entries) {
   const int64_t n_ent = ent_off[b + 1] - ent_off[b];
   int64_t n = (q_pos[b] + t) / m;
   n = n < n_ent ? n : n_ent;
