@@ -80,13 +80,18 @@ def test_csa_decode_step_finishes_crowded_rows_exactly():
         topk_band_check(got[b, 0], ref_s, lane.k, what=f"b={b}")
 
 
-def test_csa_decode_step_selects_ties_by_lowest_id():
+@pytest.mark.parametrize("lengths,H,win", [
+    ((4096, 2000, 300), 16, 128),   # 4 waves, 3 tiles (one wave group per tile)
+    ((12000, 4000, 100), 128, 64),  # 16 waves in two groups of 8, 2 tiles, 3,000 entries
+])
+def test_csa_decode_step_selects_ties_by_lowest_id(lengths, H, win):
     """Short rows (one attention workgroup each, which makes the row's selection) whose indexer
     keys take three values, so their scores tie in large blocks: the step's ids equal
     topk_select's and a brute-force order of the step's own scores (score descending, lower id
     first)."""
     from compressed_sparse_long_amd import lanes
-    lane = W.Lane("csa", (4096, 2000, 300), (4096, 2000, 300), T=1, H=16, m=4, k=64, HI=4)
+    print(f"ties lengths={lengths} H={H} W={win}", flush=True)
+    lane = W.Lane("csa", lengths, lengths, T=1, H=H, m=4, W=win, k=64, HI=4)
     inp = synth.generate(W.Workload("ties", 31, (lane,)))
     li = inp.lanes[0]
     base = li.kI[:3].clone()
