@@ -528,7 +528,8 @@ __global__ __launch_bounds__(NHG * NSUB * 64) void attn_kernel(
 
   if constexpr (TOPK) {
     // the window rows depend on no selection: they are in flight while the workgroup selects
-    // the row's entries (a barrier waits for no load), then the selected entries follow
+    // the row's entries (no store precedes the selection's barriers, so they wait for no
+    // load), then the selected entries follow
     if (k_lo < k_hi) issue(k_lo, ids_cur, 1);
     const int64_t n = visible_entries(ent_off, q_pos, b, t, tk.m, tk.max_entries);
     short_row_topk<NT, kSelItems>(tk.scores + (int64_t)row * tk.ld, tk.max_entries, n, k, sel,
