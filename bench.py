@@ -10,15 +10,20 @@ timed region. The compressed cache and the indexer keys are kept in several inde
 copies that consecutive steps rotate through, so every step streams from HBM rather than
 from the last-level cache.
 
-The timed region replays a HIP graph that holds 8 rounds of R consecutive steps (one per
-rotated copy) until K steps have run; every step is the whole hot path, the graph only saves
-host-side launches. The latency of a step captured and launched on its own is reported beside
-it. Prints one JSON line: queries/s, ms per step, the
+The timed region replays a HIP graph that keeps M independent micro-batches in flight
+(default 4), as a serving engine overlaps independent batches: each micro-batch is a chain
+of consecutive whole steps on its own graph branch, with its own outputs and workspaces and
+its own rotated input copies, so the latency-bound tail of one micro-batch's step (top-k
+finish, attention, merge on a few compute units) runs beside another's HBM-bound indexer.
+Every step is the whole hot path; the graph only saves host-side launches. The time per step
+of one micro-batch at a time (a chain of 32 dependent steps) and the latency of a step
+captured and launched on its own are reported beside it. Prints one JSON line: queries/s,
+ms per step, the
 indexer kernel's achieved HBM bandwidth against the 8 TB/s peak (HIP events around 100
 back-to-back launches), and the fp64 CPU oracle's rate on a bounded sample of the same
 workload.
 
-  python bench.py [--steps K] [--warmup W] [--copies R] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--copies R] [--inflight M] [--no-cpu-baseline]
   python bench.py --copy-calibration     # plain device copy of known size (for counters)
   python bench.py --run-workload NAME    # replay another configuration's step (for profiles;
                                          # prints its step time, not a bench line)
@@ -57,7 +62,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--copies", type=int, default=4, help="rotated input copies (>= 4 defeats the 256 MB MALL)")
+    ap.add_argument("--copies", type=int, default=4,
+                    help="rotated input copies (>= 4 defeats the 256 MB MALL; at least 2 per micro-batch in flight)")
+    ap.add_argument("--inflight", type=int, default=4,
+                    help="independent micro-batches whose step chains the timed graph runs concurrently")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="wall budget of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stages", action="store_true", help="skip the per-stage breakdown pass")
@@ -196,7 +204,7 @@ def main():
         run_workload(args.run_workload, args.steps, args.warmup, args.paged, args.copies, args.scoreless)
         return
     if args.report_configs:
-        report_configs(args.copies, args.cpu_seconds)
+        report_configs(args.copies, args.cpu_seconds, inflight=args.inflight)
         return
 
     result = measure_headline(args)
@@ -207,7 +215,8 @@ def main():
         gc.collect()
         torch.cuda.empty_cache()
         result["configs"] = {ln.pop("workload"): ln for ln in
-                             report_configs(args.copies, args.config_cpu_seconds, emit=False)}
+                             report_configs(args.copies, args.config_cpu_seconds, emit=False,
+                                            inflight=args.inflight)}
     print(json.dumps(result), flush=True)
 
 
@@ -220,7 +229,8 @@ def measure_headline(args) -> dict:
     t_gen = time.perf_counter()
     inp = synth.generate(WORKLOAD)
     (cl,) = lanes.build_lanes(inp)
-    cl.rotate(args.copies)
+    M = max(1, args.inflight)
+    cl.rotate(max(args.copies, 2 * M))
     cl.compress_all()
     torch.cuda.synchronize()
     print(f"# inputs ready in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
@@ -248,11 +258,17 @@ def measure_headline(args) -> dict:
         torch.cuda.synchronize()
         return a.elapsed_time(b) / (reps * per_replay) * 1e3  # microseconds
 
-    # the timed loop replays one graph holding GRAPH_ROUNDS x R consecutive decode steps, the
-    # rotated input copies in turn (each step is the whole hot path; the graph only saves host
-    # launches)
-    S = GRAPH_ROUNDS * R
-    multi = capture(lambda: [cl.step(r) for _ in range(GRAPH_ROUNDS) for r in range(R)])
+    # the timed loop replays one graph holding M independent micro-batches in flight: M chains
+    # of consecutive decode steps on parallel graph branches, S steps in all per replay. Each
+    # micro-batch owns its outputs and workspaces and steps through its own rotated copies
+    # (copy c belongs to micro-batch c mod M), so no two concurrent steps touch the same
+    # memory; every step is the whole hot path, the graph only saves host launches.
+    mbs = [cl] + [cl.micro_batch() for _ in range(M - 1)]
+    own = [[c for c in range(R) if c % M == i] for i in range(M)]
+    per_chain = max(1, GRAPH_ROUNDS * 4 // M)
+    S = per_chain * M
+    multi = lanes.in_flight_graph([[lambda mb=mbs[i], r=own[i][j % len(own[i])]: mb.step(r) for j in range(per_chain)]
+                                   for i in range(M)])
     for i in range((args.warmup + S - 1) // S):
         multi.replay()
     torch.cuda.synchronize()
@@ -271,7 +287,12 @@ def measure_headline(args) -> dict:
     queries = B * T * K
     value = queries / (total_ms / 1e3)
 
-    # latency of a step launched on its own (one graph per step, replayed back to back)
+    # one micro-batch at a time: a graph of GRAPH_ROUNDS x 4 consecutive steps over 4 rotated
+    # copies (each step waits for the one before), and a step launched on its own (one graph
+    # per step, replayed back to back)
+    serial = capture(lambda: [cl.step(r) for _ in range(GRAPH_ROUNDS) for r in range(4)])
+    serial_us = time_graphs([serial], max(2, args.steps // (GRAPH_ROUNDS * 4)), per_replay=GRAPH_ROUNDS * 4)
+    del serial
     singles = [capture(lambda r=r: cl.step(r)) for r in range(R)]
     single_us = time_graphs(singles, 200)
 
@@ -311,13 +332,14 @@ def measure_headline(args) -> dict:
         "data": "synthetic",
         "config": {"workload": WORKLOAD, "batch": B, "context_tokens": lane.lengths[0], "entries": E,
                    "heads": H, "head_dim": D, "m": lane.m, "top_k": k, "window": W, "indexer_heads": HI,
-                   "indexer_dim": CI, "rotated_copies": args.copies},
+                   "indexer_dim": CI, "rotated_copies": R, "micro_batches_in_flight": M},
         "roofline": {"kernel": "indexer_decode_kernel", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "launch_us": round(idx_us, 3), "bytes_per_launch": idx_bytes},
         "indexer_mfma": {"flops_per_launch": idx_flops, "issued_flops_per_launch": idx_issued,
                          "achieved": round(idx_flops / (idx_us * 1e-6) / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(idx_flops / (idx_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5)},
+        "step_us_serial": round(serial_us, 2),
         "step_us_one_graph_per_step": round(single_us, 2),
         "step_hbm": {"bytes": step_bytes, "GB_s": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
                      "frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
@@ -432,7 +454,7 @@ def measure_headline(args) -> dict:
         paged_us = paged_step("random")
         paged_il_us = paged_step("interleaved")
 
-        result["options_step_us"] = {"plain": round(ms_step * 1e3, 2), "paged": paged_us,
+        result["options_step_us"] = {"plain": round(serial_us, 2), "paged": paged_us,
                                      "paged_interleaved": paged_il_us,
                                      "overlap": options_step(True, False),
                                      "sink_rope64": options_step(False, True),
@@ -574,26 +596,39 @@ def oracle_rate(inp, seconds: float, D: int = 128):
             "sample": f"{n} queries ({len(work)} sampled sequence(s), fp64 numpy) in {el:.1f} s", "machine": mach}
 
 
-def report_configs(copies: int, cpu_seconds: float, emit: bool = True) -> list:
-    """Every synthetic configuration: whole-step time (graph of GRAPH_ROUNDS x `copies` steps),
-    queries/s, algorithmic GB/s and roofline fraction, and the oracle's rate beside it.
-    Returns one dict per configuration (and prints each as a JSON line when ``emit``)."""
+def report_configs(copies: int, cpu_seconds: float, emit: bool = True, inflight: int = 4) -> list:
+    """Every synthetic configuration: whole-step time with ``inflight`` independent
+    micro-batches in flight (each a chain of steps on its own graph branch, every lane of a
+    micro-batch a chain of its own) and one micro-batch at a time (a graph of GRAPH_ROUNDS x
+    `copies` consecutive steps), queries/s, algorithmic GB/s and roofline fraction, and the
+    oracle's rate beside it. Returns one dict per configuration (and prints each as a JSON
+    line when ``emit``)."""
     import torch
     import synth
     from compressed_sparse_long_amd import lanes
 
-    def time_step(inp, scoreless: bool) -> float:
+    def time_step(inp, scoreless: bool, M: int) -> float:
         ls = lanes.build_lanes(inp, scoreless=scoreless)
+        R = max(copies, 2 * M) if M > 1 else copies
         for lane in ls:
-            lane.rotate(copies)
+            lane.rotate(R)
             lane.compress_all()
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for _ in range(GRAPH_ROUNDS):
-                for r in range(copies):
-                    for lane in ls:
-                        lane.step(r)
+        if M > 1:
+            mbs = [[lane] + [lane.micro_batch() for _ in range(M - 1)] for lane in ls]
+            own = [[c for c in range(R) if c % M == i] for i in range(M)]
+            per_chain = max(1, GRAPH_ROUNDS * 4 // M)
+            steps = per_chain * M
+            g = lanes.in_flight_graph([[lambda mb=mbs[j][i], r=own[i][t % len(own[i])]: mb.step(r)
+                                        for t in range(per_chain)] for j in range(len(ls)) for i in range(M)])
+        else:
+            steps = GRAPH_ROUNDS * R
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(GRAPH_ROUNDS):
+                    for r in range(R):
+                        for lane in ls:
+                            lane.step(r)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         g.replay()
         torch.cuda.synchronize()
@@ -609,22 +644,25 @@ def report_configs(copies: int, cpu_seconds: float, emit: bool = True) -> list:
         torch.cuda.synchronize()
         del g, ls
         torch.cuda.empty_cache()
-        return a.elapsed_time(b) / (reps * copies * GRAPH_ROUNDS) * 1e3
+        return a.elapsed_time(b) / (reps * steps) * 1e3
 
     lines = []
     for name in synth.CONFIG_ORDER:
         print(f"# configuration {name}: generating inputs", file=sys.stderr, flush=True)
         inp = synth.generate(name)
-        step_us = time_step(inp, False)
+        step_us = time_step(inp, False, max(1, inflight))
+        serial_us = time_step(inp, False, 1)
         nbytes, flops, queries = step_model([li.lane for li in inp.lanes])
         bound_us = max(nbytes / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e6
         extra = {}
         if any(li.lane.kind == "csa" and li.lane.T >= 16 for li in inp.lanes):
             # query batches: the same step with the indexer fused with top-k (no score matrix)
-            nos_us = time_step(inp, True)
+            nos_us = time_step(inp, True, max(1, inflight))
             extra = {"step_us_without_scores": round(nos_us, 2),
                      "queries_per_s_without_scores": round(queries / (nos_us * 1e-6), 1)}
-        line = {"workload": name, "step_us": round(step_us, 2), "queries_per_s": round(queries / (step_us * 1e-6), 1),
+        line = {"workload": name, "micro_batches_in_flight": max(1, inflight), "step_us": round(step_us, 2),
+                "queries_per_s": round(queries / (step_us * 1e-6), 1), "step_us_serial": round(serial_us, 2),
+                "queries_per_s_serial": round(queries / (serial_us * 1e-6), 1),
                 "bytes": nbytes, "GB_s": round(nbytes / (step_us * 1e-6) / 1e9, 1),
                 "hbm_frac": round(nbytes / (step_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                 "flops": flops, "TFLOP_s": round(flops / (step_us * 1e-6) / 1e12, 2),

@@ -11,6 +11,7 @@ entries plus the raw window. HCA step: compress the newest chunk(s), attend dens
 """
 from __future__ import annotations
 
+import copy
 import math
 
 import torch
@@ -173,6 +174,21 @@ class _Lane:
         exceed the last-level cache and each step reads from HBM."""
         self.ckv_copies = [self.ckv] + [self.ckv.clone() for _ in range(copies - 1)]
 
+    # per-step outputs and scratch: everything a step writes apart from the cache's newest entries
+    _STEP_BUFFERS = ("scores", "idx", "out", "lse", "topk_ws", "attn_ws")
+
+    def micro_batch(self):
+        """A lane over the same inputs and cache copies with its own outputs and workspaces,
+        so that its steps can run concurrently with this lane's (independent micro-batches in
+        flight on parallel streams or graph branches). Concurrent steps must use different
+        cache copies: every step rewrites its copy's newest entries."""
+        twin = copy.copy(self)
+        for name in self._STEP_BUFFERS:
+            buf = getattr(self, name, None)
+            if buf is not None:
+                setattr(twin, name, torch.zeros_like(buf))
+        return twin
+
 
 class CsaLane(_Lane):
     def __init__(self, lane, kv, z, q, li, device="cuda", fused: bool = True, kv_b=None, z_b=None,
@@ -294,6 +310,27 @@ class HcaLane(_Lane):
                         self.ckv_copies[r % len(self.ckv_copies)], self.q, self.W, self.out, self.q_pos, self.m,
                         self.max_entries, lse=self.lse, scale=self.scale, attn_ws=self.attn_ws, sink=self.sink,
                         rope_dims=self.rope_dims, rope_base=self.rope_base, paged=self.paged)
+
+
+def in_flight_graph(chains):
+    """Capture one HIP graph whose branches are independent chains of calls (each a list of
+    callables that enqueue work on the current stream), for example the steps of several
+    micro-batches. Each chain is recorded on its own side stream, forked from the capture
+    stream at the start and joined to it at the end, so a replay runs the chains
+    concurrently and returns on the stream it was replayed on once all of them are done.
+    Chains must not write what another chain reads or writes."""
+    side = [torch.cuda.Stream() for _ in chains]  # default priority, like every stream here
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cap = torch.cuda.current_stream()
+        for st, chain in zip(side, chains):
+            st.wait_stream(cap)
+            with torch.cuda.stream(st):
+                for fn in chain:
+                    fn()
+        for st in side:
+            cap.wait_stream(st)
+    return g
 
 
 def build_lanes(inp, device="cuda", scoreless: bool = False):
