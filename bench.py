@@ -80,6 +80,8 @@ def parse():
     ap.add_argument("--run-workload", default=None,
                     help="replay --steps steps of another synthetic configuration (for profiling) and print "
                          "its mean step time")
+    ap.add_argument("--inflight-workload", action="store_true",
+                    help="with --run-workload: keep --inflight micro-batches in flight (default: one at a time)")
     ap.add_argument("--scoreless", action="store_true",
                     help="with --run-workload: CSA steps select with the indexer fused with top-k (no scores)")
     ap.add_argument("--paged", default=None, choices=("random", "interleaved"),
@@ -201,7 +203,8 @@ def main():
         copy_calibration()
         return
     if args.run_workload:
-        run_workload(args.run_workload, args.steps, args.warmup, args.paged, args.copies, args.scoreless)
+        run_workload(args.run_workload, args.steps, args.warmup, args.paged, args.copies, args.scoreless,
+                     args.inflight if args.inflight_workload else 1)
         return
     if args.report_configs:
         report_configs(args.copies, args.cpu_seconds, inflight=args.inflight)
@@ -467,30 +470,43 @@ def measure_headline(args) -> dict:
 
 
 def run_workload(name: str, steps: int, warmup: int, paged: str | None = None, copies: int = 4,
-                 scoreless: bool = False) -> None:
+                 scoreless: bool = False, inflight: int = 1) -> None:
     """Replay one configuration's whole step (every lane) as a graph; print its mean time.
     Each graph holds ``copies`` steps over rotated copies of the large inputs (as in the main
-    measurement); ``paged``: move every lane's cache into a block pool first, blocks in that order."""
+    measurement); ``paged``: move every lane's cache into a block pool first, blocks in that
+    order; ``inflight`` > 1: that many independent micro-batches in flight, each lane of each a
+    chain of steps on its own graph branch over its own rotated copies (as the bench line)."""
     import torch
     import synth
     from compressed_sparse_long_amd import lanes
 
     inp = synth.generate(name)
     ls = lanes.build_lanes(inp, scoreless=scoreless)
-    R = max(1, copies)
+    M = max(1, inflight)
+    R = max(1, copies, 2 * M if M > 1 else 1)
     for lane in ls:
         lane.compress_all()
         if paged:
             lane.paginate(ring_rows=256, order=paged)
         lane.rotate(R)
     torch.cuda.synchronize()
-    S = GRAPH_ROUNDS * R
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for _ in range(GRAPH_ROUNDS):
-            for r in range(R):
-                for lane in ls:
-                    lane.step(r)
+    if M > 1:
+        if paged:
+            raise SystemExit("--paged with --inflight > 1 is not supported (the micro-batches share one pool)")
+        mbs = [[lane] + [lane.micro_batch() for _ in range(M - 1)] for lane in ls]
+        own = [[c for c in range(R) if c % M == i] for i in range(M)]
+        per_chain = max(1, GRAPH_ROUNDS * 4 // M)
+        S = per_chain * M
+        g = lanes.in_flight_graph([[lambda mb=mbs[j][i], r=own[i][t % len(own[i])]: mb.step(r)
+                                    for t in range(per_chain)] for j in range(len(ls)) for i in range(M)])
+    else:
+        S = GRAPH_ROUNDS * R
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(GRAPH_ROUNDS):
+                for r in range(R):
+                    for lane in ls:
+                        lane.step(r)
     for _ in range(max(1, (warmup + S - 1) // S)):
         g.replay()
     torch.cuda.synchronize()
@@ -501,8 +517,8 @@ def run_workload(name: str, steps: int, warmup: int, paged: str | None = None, c
         g.replay()
     b.record()
     torch.cuda.synchronize()
-    print(f"workload {name}{' paged ' + paged if paged else ''}{' without scores' if scoreless else ''}: "
-          f"{a.elapsed_time(b) / (reps * S) * 1e3:.1f} us per "
+    print(f"workload {name}{' paged ' + paged if paged else ''}{' without scores' if scoreless else ''}"
+          f"{f' with {M} micro-batches in flight' if M > 1 else ''}: {a.elapsed_time(b) / (reps * S) * 1e3:.1f} us per "
           f"step over {reps * S} steps ({R} rotated input copies)", flush=True)
 
 
