@@ -52,6 +52,10 @@ WORKLOAD = "csa_decode_1m"
 # launch cost is then a small share of each step. The one-step-per-replay latency is reported
 # beside it (step_us_one_graph_per_step).
 GRAPH_ROUNDS = 8
+# With micro-batches in flight, one replay holds this many steps in all (a chain of
+# IN_FLIGHT_STEPS / M steps per micro-batch): the replay's start and end, where the chains
+# fill and drain, are then a small share of each step.
+IN_FLIGHT_STEPS = 64
 COUNTER_FILE = os.path.join(ROOT, "profiles", "indexer_csa_decode_1m_counters.txt")
 INDEXER_SOURCES = ["compressed_sparse_long_amd/csrc/indexer.hip", "compressed_sparse_long_amd/csrc/device_common.h",
                    "compressed_sparse_long_amd/csrc/topk_common.h", "compressed_sparse_long_amd/csrc/compress_common.h"]
@@ -262,13 +266,13 @@ def measure_headline(args) -> dict:
         return a.elapsed_time(b) / (reps * per_replay) * 1e3  # microseconds
 
     # the timed loop replays one graph holding M independent micro-batches in flight: M chains
-    # of consecutive decode steps on parallel graph branches, S steps in all per replay. Each
+    # of consecutive decode steps on parallel graph branches, S = IN_FLIGHT_STEPS in all per replay. Each
     # micro-batch owns its outputs and workspaces and steps through its own rotated copies
     # (copy c belongs to micro-batch c mod M), so no two concurrent steps touch the same
     # memory; every step is the whole hot path, the graph only saves host launches.
     mbs = [cl] + [cl.micro_batch() for _ in range(M - 1)]
     own = [[c for c in range(R) if c % M == i] for i in range(M)]
-    per_chain = max(1, GRAPH_ROUNDS * 4 // M)
+    per_chain = max(1, IN_FLIGHT_STEPS // M)
     S = per_chain * M
     multi = lanes.in_flight_graph([[lambda mb=mbs[i], r=own[i][j % len(own[i])]: mb.step(r) for j in range(per_chain)]
                                    for i in range(M)])
@@ -495,7 +499,7 @@ def run_workload(name: str, steps: int, warmup: int, paged: str | None = None, c
             raise SystemExit("--paged with --inflight > 1 is not supported (the micro-batches share one pool)")
         mbs = [[lane] + [lane.micro_batch() for _ in range(M - 1)] for lane in ls]
         own = [[c for c in range(R) if c % M == i] for i in range(M)]
-        per_chain = max(1, GRAPH_ROUNDS * 4 // M)
+        per_chain = max(1, IN_FLIGHT_STEPS // M)
         S = per_chain * M
         g = lanes.in_flight_graph([[lambda mb=mbs[j][i], r=own[i][t % len(own[i])]: mb.step(r)
                                     for t in range(per_chain)] for j in range(len(ls)) for i in range(M)])
@@ -633,7 +637,7 @@ def report_configs(copies: int, cpu_seconds: float, emit: bool = True, inflight:
         if M > 1:
             mbs = [[lane] + [lane.micro_batch() for _ in range(M - 1)] for lane in ls]
             own = [[c for c in range(R) if c % M == i] for i in range(M)]
-            per_chain = max(1, GRAPH_ROUNDS * 4 // M)
+            per_chain = max(1, IN_FLIGHT_STEPS // M)
             steps = per_chain * M
             g = lanes.in_flight_graph([[lambda mb=mbs[j][i], r=own[i][t % len(own[i])]: mb.step(r)
                                         for t in range(per_chain)] for j in range(len(ls)) for i in range(M)])
