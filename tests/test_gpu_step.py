@@ -320,3 +320,40 @@ def _hca_step_vs_calls(lengths, q_pos, m, H, T, first, max_new, has_z=True, extr
 ])
 def test_hca_decode_step_matches_separate_calls(lengths, q_pos, m, H, T, first, max_new, has_z, extras):
     _hca_step_vs_calls(lengths, q_pos, m, H, T, first, max_new, has_z, extras)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_ragged_batch_indexer_matches_each_sequence_alone(fp8):
+    """A ragged batch with a 2^18-entry row beside short and empty rows (one workgroup per
+    sequence and slice of the longest row, most of them past their sequence's end): every
+    sequence's scores equal, bit for bit, those of a call on that sequence alone, its selected
+    ids equal, and the step equals the separate calls."""
+    from compressed_sparse_long_amd import indexer_scores, lanes, topk_select, topk_workspace_bytes
+    lengths = (1 << 20, 3001, 0, 70000, 9, 400000)
+    lane = W.Lane("csa", lengths, lengths, T=1, H=64, m=4, k=1024, HI=8, kI_fp8=fp8)
+    print(f"ragged batch indexer, fp8={fp8}", flush=True)
+    inp = synth.generate(W.Workload("compact", 31, (lane,)))
+    (cl,) = lanes.build_lanes(inp)
+    cl.compress_all()
+    cl.scores.fill_(-5.0)
+    cl.step(0, fused=False)
+    torch.cuda.synchronize()
+    ref_idx, ref_out, scores = cl.idx.clone(), cl.out.clone(), cl.scores.clone()
+    cl.idx.fill_(-7)
+    cl.step(0)
+    torch.cuda.synchronize()
+    assert torch.equal(cl.idx, ref_idx), "the step's ids differ from the separate calls"
+    torch.testing.assert_close(cl.out, ref_out, rtol=0, atol=2e-3)
+    E = lane.entries
+    for b in range(lane.B):
+        eo = cl.ent_off[b:b + 2]
+        s1 = torch.full((1, 1, max(E[b], 1)), -5.0, dtype=torch.float32, device="cuda")
+        ws = torch.zeros(max(topk_workspace_bytes(1, 1, max(E[b], 1), lane.k), 16), dtype=torch.uint8, device="cuda")
+        indexer_scores(cl.qI[b:b + 1], cl.w[b:b + 1], cl.kI, eo, cl.q_pos[b:b + 1], lane.m, s1,
+                       max_entries=max(E[b], 1), k_scale=cl.k_scale, scale_off=None if cl.scale_off is None
+                       else cl.scale_off[b:b + 2], scale_group=cl.scale_group, topk_ws=ws, topk_k=lane.k)
+        i1 = torch.full((1, 1, lane.k), -7, dtype=torch.int32, device="cuda")
+        topk_select(s1, eo, cl.q_pos[b:b + 1], lane.m, lane.k, i1, ws=ws, max_entries=max(E[b], 1), prepared=True)
+        torch.cuda.synchronize()
+        assert torch.equal(scores[b, 0, :E[b]], s1[0, 0, :E[b]]), f"scores of sequence {b} differ"
+        assert torch.equal(ref_idx[b], i1[0]), f"ids of sequence {b} differ"
