@@ -64,8 +64,8 @@ INDEXER_SOURCES = ["compressed_sparse_long_amd/csrc/indexer.hip", "compressed_sp
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=2048)
+    ap.add_argument("--warmup", type=int, default=256)
     ap.add_argument("--copies", type=int, default=4,
                     help="rotated input copies (>= 4 defeats the 256 MB MALL; at least 2 per micro-batch in flight)")
     ap.add_argument("--inflight", type=int, default=4,
