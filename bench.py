@@ -61,6 +61,23 @@ INDEXER_SOURCES = ["compressed_sparse_long_amd/csrc/indexer.hip", "compressed_sp
                    "compressed_sparse_long_amd/csrc/topk_common.h", "compressed_sparse_long_amd/csrc/compress_common.h"]
 
 
+def in_flight_steps(lane_list, M: int, R: int):
+    """The graph of M independent micro-batches in flight over ``lane_list`` (the lanes of one
+    step, with R >= M rotated copies each): every lane of every micro-batch is a chain of
+    IN_FLIGHT_STEPS / M consecutive steps on its own graph branch. Micro-batch i owns its
+    outputs and workspaces (the first is the lane itself) and steps through the copies c with
+    c mod M == i, so no two concurrent steps touch the same memory. Returns the graph, the
+    steps per replay (a step being one pass of every lane over one micro-batch) and, per lane,
+    its M micro-batches."""
+    from compressed_sparse_long_amd import lanes
+    mbs = [[lane] + [lane.micro_batch() for _ in range(M - 1)] for lane in lane_list]
+    own = [[c for c in range(R) if c % M == i] for i in range(M)]
+    per_chain = max(1, IN_FLIGHT_STEPS // M)
+    g = lanes.in_flight_graph([[lambda mb=mbs[j][i], r=own[i][t % len(own[i])]: mb.step(r) for t in range(per_chain)]
+                               for j in range(len(lane_list)) for i in range(M)])
+    return g, per_chain * M, mbs
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -266,16 +283,10 @@ def measure_headline(args) -> dict:
         return a.elapsed_time(b) / (reps * per_replay) * 1e3  # microseconds
 
     # the timed loop replays one graph holding M independent micro-batches in flight: M chains
-    # of consecutive decode steps on parallel graph branches, S = IN_FLIGHT_STEPS in all per replay. Each
-    # micro-batch owns its outputs and workspaces and steps through its own rotated copies
-    # (copy c belongs to micro-batch c mod M), so no two concurrent steps touch the same
-    # memory; every step is the whole hot path, the graph only saves host launches.
-    mbs = [cl] + [cl.micro_batch() for _ in range(M - 1)]
-    own = [[c for c in range(R) if c % M == i] for i in range(M)]
-    per_chain = max(1, IN_FLIGHT_STEPS // M)
-    S = per_chain * M
-    multi = lanes.in_flight_graph([[lambda mb=mbs[i], r=own[i][j % len(own[i])]: mb.step(r) for j in range(per_chain)]
-                                   for i in range(M)])
+    # of consecutive decode steps on parallel graph branches, S = IN_FLIGHT_STEPS in all per
+    # replay (in_flight_steps); every step is the whole hot path, the graph only saves host
+    # launches
+    multi, S, (mbs,) = in_flight_steps([cl], M, R)
     for i in range((args.warmup + S - 1) // S):
         multi.replay()
     torch.cuda.synchronize()
@@ -512,12 +523,7 @@ def run_workload(name: str, steps: int, warmup: int, paged: str | None = None, c
     if M > 1:
         if paged:
             raise SystemExit("--paged with --inflight > 1 is not supported (the micro-batches share one pool)")
-        mbs = [[lane] + [lane.micro_batch() for _ in range(M - 1)] for lane in ls]
-        own = [[c for c in range(R) if c % M == i] for i in range(M)]
-        per_chain = max(1, IN_FLIGHT_STEPS // M)
-        S = per_chain * M
-        g = lanes.in_flight_graph([[lambda mb=mbs[j][i], r=own[i][t % len(own[i])]: mb.step(r)
-                                    for t in range(per_chain)] for j in range(len(ls)) for i in range(M)])
+        g, S, _ = in_flight_steps(ls, M, R)
     else:
         S = GRAPH_ROUNDS * R
         g = torch.cuda.CUDAGraph()
@@ -650,12 +656,7 @@ def report_configs(copies: int, cpu_seconds: float, emit: bool = True, inflight:
             lane.compress_all()
         torch.cuda.synchronize()
         if M > 1:
-            mbs = [[lane] + [lane.micro_batch() for _ in range(M - 1)] for lane in ls]
-            own = [[c for c in range(R) if c % M == i] for i in range(M)]
-            per_chain = max(1, IN_FLIGHT_STEPS // M)
-            steps = per_chain * M
-            g = lanes.in_flight_graph([[lambda mb=mbs[j][i], r=own[i][t % len(own[i])]: mb.step(r)
-                                        for t in range(per_chain)] for j in range(len(ls)) for i in range(M)])
+            g, steps, _ = in_flight_steps(ls, M, R)
         else:
             steps = GRAPH_ROUNDS * R
             g = torch.cuda.CUDAGraph()
