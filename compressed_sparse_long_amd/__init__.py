@@ -47,7 +47,7 @@ class _CsaStep(ctypes.Structure):
         ("q_pos", _P), ("m", _I), ("B", _I), ("T", _I), ("max_entries", _L),
         ("kv_b", _P), ("z_b", _P),
         ("sink", _P), ("rope_dims", _I), ("rope_base", _F),
-        ("paged", _P),
+        ("paged", _P), ("scores_on_demand", _I),
     ]
 
 
@@ -344,11 +344,13 @@ def csa_decode_step(kv, z, kv_off, ent_off, first_entry, max_new_entries: int, c
                     k: int, idx, q, n_win: int, out, q_pos, m: int, lse=None, scale: float | None = None,
                     k_scale=None, scale_off=None, scale_group: int = 64, max_entries: int | None = None,
                     attn_ws=None, kv_b=None, z_b=None, sink=None, rope_dims: int = 0, rope_base: float = 10000.0,
-                    k_format=None, paged=None, stream=None, static_scratch: bool = False):
+                    k_format=None, paged=None, stream=None, static_scratch: bool = False,
+                    scores_on_demand: bool = False):
     """One whole CSA step (compress_kv of the newest entries into ckv, or compress_kv_overlap
     when series b ``kv_b``/``z_b`` is given, indexer_scores with candidate lists, topk_select,
     sparse_attn_decode) in one C call; with ``scores`` None the selection comes from the
-    indexer fused with top-k and no score matrix is written; see csl.h."""
+    indexer fused with top-k and no score matrix is written; ``scores_on_demand``: rows
+    selected from candidate lists keep no scores (see csl.h)."""
     B, T, HI, CI = qI.shape
     H, D = q.shape[2], q.shape[3]
     kd, sdt = _key_format(kI, k_format)
@@ -378,7 +380,8 @@ def csa_decode_step(kv, z, kv_off, ent_off, first_entry, max_new_entries: int, c
         kv_b=_ptr(kv_b, "kv_b", _BF16), z_b=_ptr(z_b, "z_b", _BF16),
         sink=_ptr(sink, "sink", _F32), rope_dims=int(rope_dims), rope_base=float(rope_base),
         paged=None if paged is None else ctypes.addressof(pstruct),
-        q_pos=_ptr(q_pos, "q_pos", _I64), m=int(m), B=B, T=T, max_entries=int(max_entries))
+        q_pos=_ptr(q_pos, "q_pos", _I64), m=int(m), B=B, T=T, max_entries=int(max_entries),
+        scores_on_demand=int(bool(scores_on_demand)))
     fn = _lib.csl_csa_decode_step_static if static_scratch else _lib.csl_csa_decode_step
     _check(fn(ctypes.byref(s), _stream(stream)))
     return out

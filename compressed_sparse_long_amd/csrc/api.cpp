@@ -536,6 +536,12 @@ int csl_csa_decode_step(const csl_csa_step* s, void* stream) {
   const bool select_in_attn = !scoreless && !pvp && index &&
                               csl::attention_selects_topk(s->B, s->T, s->H, s->k, max_keys, s->max_entries);
   const csl::TopkIn tk{s->scores, s->ld, s->m, s->max_entries, s->idx};
+  // scores on demand: rows selected from candidate lists keep no scores; the finishing step
+  // recomputes a row's scores where its lists cannot prove the selection
+  const bool on_demand = s->scores_on_demand != 0 && !scoreless && !select_in_attn && !pvp && index &&
+                         csl::indexer_prepares_topk(topk_ws, s->T, s->max_entries) &&
+                         csl::topk_finish_can_rescore(s->max_entries, s->k);
+  const csl::RescoreIn rescore{s->q_idx, s->w, s->k_idx, kt, s->k_scale, s->scale_off, s->scale_group, s->HI};
   hipError_t e = hipSuccess;
   if (scoreless) {
     if (compress && overlap)
@@ -553,7 +559,7 @@ int csl_csa_decode_step(const csl_csa_step* s, void* stream) {
                                s->kv_b, s->z_b};
     e = csl::launch_indexer(s->q_idx, s->w, s->k_idx, kt, s->k_scale, s->scale_off, s->scale_group, s->ent_off,
                             s->q_pos, s->m, s->B, s->T, s->HI, s->max_entries, s->scores, s->ld, topk_ws, s->k, hs, &job,
-                            pvp);
+                            pvp, on_demand);
   } else {
     if (compress && overlap)
       e = csl::launch_compress_overlap(s->kv, s->z, s->kv_b, s->z_b, s->kv_off, s->ent_off, s->first_entry, s->B,
@@ -564,12 +570,13 @@ int csl_csa_decode_step(const csl_csa_step* s, void* stream) {
     if (e == hipSuccess && index)
       e = csl::launch_indexer(s->q_idx, s->w, s->k_idx, kt, s->k_scale, s->scale_off, s->scale_group, s->ent_off,
                               s->q_pos, s->m, s->B, s->T, s->HI, s->max_entries, s->scores, s->ld, topk_ws, s->k, hs,
-                              nullptr, pvp);
+                              nullptr, pvp, on_demand);
   }
   if (e != hipSuccess) return hip_status(e, "csa_decode_step launch");
   if (!scoreless && !select_in_attn)
     e = csl::launch_topk(s->scores, s->ld, s->ent_off, s->q_pos, s->m, s->B, s->T, s->k, s->max_entries, s->idx,
-                         s->topk_ws, csl::indexer_prepares_topk(topk_ws, s->T, s->max_entries), hs);
+                         s->topk_ws, csl::indexer_prepares_topk(topk_ws, s->T, s->max_entries), hs,
+                         on_demand ? &rescore : nullptr);
   if (e != hipSuccess) return hip_status(e, "csa_decode_step launch");
   return hip_status(csl::launch_attention(true, s->q, s->ckv, s->idx, s->k, s->kv, s->kv_off, s->ent_off, s->q_pos, 1,
                                           s->n_win, s->B, s->T, s->H, s->scale, (int64_t)1 << 62, max_keys, s->out,

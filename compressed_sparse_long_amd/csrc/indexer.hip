@@ -31,89 +31,11 @@
 #include "device_common.h"
 #include "launch.h"
 #include "topk_common.h"
+#include "indexer_common.h"
 
 namespace csl {
 
 namespace {
-
-enum { kKeyBF16 = 0, kKeyFP8 = 1, kKeyFP4 = 2 };
-
-// Row of entry s of sequence b in the key array: e_base + s, or in the paged layout its pool
-// row (table entries past the table are clamped: such entries are never loaded)
-template <bool PAGED>
-__device__ __forceinline__ int64_t key_row(const PagedView& pg, int b, int64_t e_base, int64_t s) {
-  if (!PAGED) return e_base + s;
-  int64_t j = s >> pg.eb_shift;
-  j = j < pg.max_blocks ? j : pg.max_blocks - 1;
-  return ((int64_t)pg.table[(int64_t)b * pg.max_blocks + j] << pg.eb_shift) | (s & ((1 << pg.eb_shift) - 1));
-}
-
-// Slot of the fp8 group scale of entry s of sequence b: scale_off[b] + s / scale_group, or in the
-// paged layout the pool scale of its key row kr, kr >> scale_shift (the pool keeps its scales
-// per block: one per power-of-two group inside a block, or one per block when a group spans
-// several blocks)
-template <bool PAGED>
-__device__ __forceinline__ int64_t fp8_scale_index(const PagedView& pg, int64_t kr, const int64_t* scale_off, int b,
-                                                   int64_t s, int scale_group) {
-  if (PAGED) return kr >> pg.scale_shift;
-  return scale_off[b] + s / scale_group;
-}
-
-// first dim of the 8 k-slots that lane group g supplies for MFMA kk (the key and query
-// operands share this order)
-template <int KT>
-__device__ __forceinline__ int kslot_dim(int kk, int g) {
-  return KT == kKeyFP4 ? g * 16 + kk * 8 : kk * 32 + g * 8;
-}
-
-// One lane's share of a key row for both MFMAs (raw codes; key_operand widens them).
-// MXFP4: 8 bytes = dims 16g..16g+15 (block g / 2) plus that block's E8M0 scale byte.
-template <int KT>
-__device__ __forceinline__ void load_key_tile(const void* __restrict__ kI, const uint8_t* __restrict__ k_mx,
-                                              int64_t row, bool ok, int g, u32x4& k0, u32x4& k1) {
-  if (!ok) {
-    k0 = u32x4{0, 0, 0, 0};
-    k1 = u32x4{0, 0, 0, 0};
-    return;
-  }
-  if (KT == kKeyBF16) {
-    const uint16_t* p = static_cast<const uint16_t*>(kI) + row * 64 + g * 8;
-    k0 = *reinterpret_cast<const u32x4*>(p);
-    k1 = *reinterpret_cast<const u32x4*>(p + 32);
-  } else if (KT == kKeyFP8) {
-    const uint8_t* p = static_cast<const uint8_t*>(kI) + row * 64 + g * 8;
-    const u32x2 c0 = *reinterpret_cast<const u32x2*>(p);
-    const u32x2 c1 = *reinterpret_cast<const u32x2*>(p + 32);
-    // keep the raw codes; they are widened to bf16 just before the MFMA
-    k0 = u32x4{c0.x, c0.y, 0, 0};
-    k1 = u32x4{c1.x, c1.y, 0, 0};
-  } else {
-    const u32x2 c = *reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(kI) + row * 32 + g * 8);
-    const uint32_t e = k_mx[row * 2 + (g >> 1)];
-    k0 = u32x4{c.x, e, 0, 0};
-    k1 = u32x4{c.y, e, 0, 0};
-  }
-}
-
-template <int KT>
-__device__ __forceinline__ bf16x8 key_operand(const u32x4& k) {
-  if (KT == kKeyBF16) return as_bf16x8(k);
-  if (KT == kKeyFP8) {
-    const u32x2 lo = e4m3x4_to_bf16x4(k.x);
-    const u32x2 hi = e4m3x4_to_bf16x4(k.y);
-    return as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
-  }
-  // 8 E2M1 codes (byte j: dims 2j, 2j + 1 in its low and high nibble) times 2^(e - 127),
-  // exact in bf16; a zero exponent byte gives the float 2^-127 (subnormal)
-  const float sc = k.y ? __uint_as_float(k.y << 23) : __uint_as_float(0x00400000u);
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  const bf16x2_t r0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(k.x, sc, 0);
-  const bf16x2_t r1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(k.x, sc, 1);
-  const bf16x2_t r2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(k.x, sc, 2);
-  const bf16x2_t r3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(k.x, sc, 3);
-  return as_bf16x8(u32x4{__builtin_bit_cast(uint32_t, r0), __builtin_bit_cast(uint32_t, r1),
-                         __builtin_bit_cast(uint32_t, r2), __builtin_bit_cast(uint32_t, r3)});
-}
 
 // Prefill tiling: queries are the MFMA A operand (16/HI query rows x HI heads per tile) and
 // keys the B operand, so lane (g, c) holds products 4g..4g+3 (query row, head) of key c. The
@@ -641,22 +563,6 @@ _Pragma("unroll 1")                                                             
   }
 }
 
-// Sum over the HI consecutive lanes that hold one query row's heads (HI a power of two up to
-// 16, groups aligned inside a row of 16 lanes): xor-1 and xor-2 quad permutes, then the
-// half-row and row mirrors, all DPP, so every lane of the group ends with the group sum.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
-}
-template <int HI>
-__device__ __forceinline__ float head_sum(float v) {
-  if (HI >= 2) v += dpp_f<0xb1>(v);   // quad_perm [1,0,3,2]
-  if (HI >= 4) v += dpp_f<0x4e>(v);   // quad_perm [2,3,0,1]
-  if (HI >= 8) v += dpp_f<0x141>(v);  // row_half_mirror
-  if (HI >= 16) v += dpp_f<0x140>(v); // row_mirror
-  return v;
-}
-
 // Decode tiling: 8 waves, each with one pass over its own 64 consecutive keys (4 tiles of 16).
 // The keys are the MFMA A operand and the 16/HI query rows x HI heads the B operand, so the
 // accumulator holds 4 keys x 1 (row, head) per lane and the head sum stays inside a row of 16
@@ -675,7 +581,7 @@ __global__ __launch_bounds__(kSlice) void indexer_decode_kernel(
     const void* __restrict__ k_scale_v, const int64_t* __restrict__ scale_off, int scale_group,
     const int64_t* __restrict__ ent_off, const int64_t* __restrict__ q_pos, int m, int T,
     int64_t max_entries, float* __restrict__ scores, int64_t ld, void* topk_ws, int topk_k, int slot_budget,
-    int key_blocks, CompressJob job, PagedView pg) {
+    int key_blocks, CompressJob job, PagedView pg, int on_demand) {
   constexpr int NW = kSlice / kWave;
   constexpr int QPB = 16 / HI;  // query rows per tile
   constexpr int U = 4;
@@ -803,12 +709,8 @@ __global__ __launch_bounds__(kSlice) void indexer_decode_kernel(
   const bool writer = (c % HI) == 0 && tq < T;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    acc = mfma16x16x32(key_operand<KT>(kb[u][0]), qb[0], acc);
-    acc = mfma16x16x32(key_operand<KT>(kb[u][1]), qb[1], acc);
     float v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = head_sum<HI>(wc * fmaxf(acc[i], 0.f));
+    decode_score_tile<HI, KT>(kb[u][0], kb[u][1], qb, wc, v);
     if (writer)
       *reinterpret_cast<float4*>(&sval[c / HI][wave * EPW + u * 16 + 4 * g]) = make_float4(v[0], v[1], v[2], v[3]);
   }
@@ -819,13 +721,17 @@ __global__ __launch_bounds__(kSlice) void indexer_decode_kernel(
 
   const int64_t s = e0 + lane;
   float mine = 0.f;
+  // scores on demand: a row whose selection runs on candidate lists keeps no scores (the
+  // finishing step recomputes a row's scores if its lists cannot prove the selection); rows
+  // too dense for lists are selected from their scores
+  const bool keep_scores = !(PREP && on_demand) || topk_row_dense(n_vis(0), topk_k);
 #pragma unroll
   for (int q = 0; q < QPB; ++q) {
     const int tt = t0 + q;
     if (tt >= T) break;
     const float val = sval[q][wave * EPW + lane] * my_scale;
     if (q == 0) mine = val;
-    if (s < n_vis(tt)) scores[((int64_t)b * T + tt) * ld + s] = val;
+    if (keep_scores && s < n_vis(tt)) scores[((int64_t)b * T + tt) * ld + s] = val;
   }
   if (PREP) {
     const int64_t n = n_vis(0);
@@ -844,7 +750,7 @@ hipError_t launch_hi(const void* qI, const float* w, const void* kI, const void*
                      const int64_t* scale_off, int scale_group, const int64_t* ent_off,
                      const int64_t* q_pos, int m, int B, int T, int64_t max_entries, float* scores,
                      int64_t ld, void* topk_ws, int topk_k, hipStream_t st, const CompressJob* job,
-                     const PagedView& pg) {
+                     const PagedView& pg, bool on_demand) {
   const uint16_t* q16 = static_cast<const uint16_t*>(qI);
   const int rows = B * T;
   const bool prep = indexer_prepares_topk(topk_ws, T, max_entries);
@@ -875,7 +781,8 @@ hipError_t launch_hi(const void* qI, const float* w, const void* kI, const void*
 #define CSL_IDX_DECODE(PREP, PG)                                                                                    \
   indexer_decode_kernel<HI, KT, PREP, PG><<<grid, kSlice, 0, st>>>(                                                 \
       q16, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, T, max_entries, scores, ld,                  \
-      PREP ? topk_ws : nullptr, PREP ? topk_k : 0, PREP ? topk_slot_budget(max_entries, topk_k) : 0, (int)kb, cj, pg)
+      PREP ? topk_ws : nullptr, PREP ? topk_k : 0, PREP ? topk_slot_budget(max_entries, topk_k) : 0, (int)kb, cj, pg, \
+      (PREP && on_demand) ? 1 : 0)
     if (prep) {
       if (pg.table) CSL_IDX_DECODE(true, true);
       else CSL_IDX_DECODE(true, false);
@@ -941,11 +848,11 @@ hipError_t launch_kt(int HI, const void* qI, const float* w, const void* kI, con
                       const int64_t* scale_off, int scale_group, const int64_t* ent_off,
                       const int64_t* q_pos, int m, int B, int T, int64_t max_entries, float* scores,
                       int64_t ld, void* topk_ws, int topk_k, hipStream_t st, const CompressJob* job,
-                      const PagedView& pg) {
+                      const PagedView& pg, bool on_demand) {
 #define CSL_IDX_CASE(H)                                                                                          \
   case H:                                                                                                        \
     return launch_hi<H, KT>(qI, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T, max_entries, \
-                             scores, ld, topk_ws, topk_k, st, job, pg);
+                             scores, ld, topk_ws, topk_k, st, job, pg, on_demand);
   switch (HI) {
     CSL_IDX_CASE(1)
     CSL_IDX_CASE(2)
@@ -1002,11 +909,13 @@ hipError_t launch_indexer(const void* qI, const float* w, const void* kI, int ke
                           const int64_t* scale_off, int scale_group, const int64_t* ent_off,
                           const int64_t* q_pos, int m, int B, int T, int HI, int64_t max_entries,
                           float* scores, int64_t ld, void* topk_ws, int topk_k, hipStream_t stream,
-                          const CompressJob* job, const PagedView* paged) {
+                          const CompressJob* job, const PagedView* paged, bool scores_on_demand) {
   const PagedView pg = paged ? *paged : PagedView{};
+  // scores on demand only where the finishing step can recompute a row: packed layout
+  const bool on_demand = scores_on_demand && !paged;
 #define CSL_IDX_KT(KT)                                                                                     \
   launch_kt<KT>(HI, qI, w, kI, k_scale, scale_off, scale_group, ent_off, q_pos, m, B, T, max_entries, scores, \
-                ld, topk_ws, topk_k, stream, job, pg)
+                ld, topk_ws, topk_k, stream, job, pg, on_demand)
   switch (key_type) {
     case kKeyFP8: return CSL_IDX_KT(kKeyFP8);
     case kKeyFP4: return CSL_IDX_KT(kKeyFP4);

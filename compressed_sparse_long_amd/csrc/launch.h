@@ -51,7 +51,8 @@ hipError_t launch_indexer(const void* qI, const float* w, const void* kI, int ke
                           const int64_t* scale_off, int scale_group, const int64_t* ent_off,
                           const int64_t* q_pos, int m, int B, int T, int HI, int64_t max_entries,
                           float* scores, int64_t ld, void* topk_ws, int topk_k, hipStream_t stream,
-                          const CompressJob* job = nullptr, const PagedView* paged = nullptr);
+                          const CompressJob* job = nullptr, const PagedView* paged = nullptr,
+                          bool scores_on_demand = false);
 // indexer fused with top-k (no scores written): ids of the k best visible entries per query
 // row into idx [B, T, k], ascending, -1 padded; k <= indexer_topk_max_k(HI)
 hipError_t launch_indexer_topk(const void* qI, const float* w, const void* kI, int key_type, const void* k_scale,
@@ -68,9 +69,25 @@ bool topk_uses_row_kernel(int64_t max_entries);
 int64_t topk_max_entries();
 size_t topk_workspace_bytes(int B, int T, int64_t max_entries, int k);
 int topk_max_k();
+// The indexer inputs of a step whose indexer wrote no scores for rows with candidate lists
+// (scores on demand): a row whose lists cannot prove its selection gets its scores recomputed,
+// with the indexer's arithmetic, into its row of scores before the exact row pass. Packed
+// layout, one query row per sequence.
+struct RescoreIn {
+  const void* qI;
+  const float* w;
+  const void* kI;
+  int key_type;
+  const void* k_scale;
+  const int64_t* scale_off;
+  int scale_group;
+  int HI;
+};
+// whether the finishing kernel can recompute rows for these shapes (one chunk of 8 slots per thread)
+bool topk_finish_can_rescore(int64_t max_entries, int k);
 hipError_t launch_topk(const float* scores, int64_t ld, const int64_t* ent_off, const int64_t* q_pos, int m,
                        int B, int T, int k, int64_t max_entries, int32_t* idx, void* ws, bool prepared,
-                       hipStream_t stream);
+                       hipStream_t stream, const RescoreIn* rescore = nullptr);
 
 struct AttnPlan {
   int nsplit;

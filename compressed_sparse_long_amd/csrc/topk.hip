@@ -20,6 +20,7 @@
 //     writes the winners in ascending id order straight from the slot order with one
 //     block-wide scan. If the check fails it runs an exact pass over the whole row instead.
 #include "device_common.h"
+#include "indexer_common.h"
 #include "launch.h"
 #include "topk_common.h"
 #include "topk_finish.h"
@@ -264,21 +265,101 @@ __global__ __launch_bounds__(kFinNT) void topk_row_kernel(const float* __restric
   for (int p = (int)keep + tid; p < k; p += kFinNT) out[p] = -1;
 }
 
+// Scores on demand: the scores of entries [0, n) of sequence b's one query row, recomputed by
+// the workgroup's waves, 64 keys per wave and pass, with the decode indexer's loads, tile
+// arithmetic (decode_score_tile) and LDS staging, so each score has the indexer's bits. The
+// query operand holds row 0 only: the lists exist only for one query row per sequence.
+template <int NT, int HI, int KT>
+__device__ __forceinline__ void rescore_row_hk(const RescoreIn& rs, const int64_t* __restrict__ ent_off, int b,
+                                               int64_t n, float* __restrict__ srow, float* stage) {
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int g = lane / 16, c = lane % 16;
+  const int64_t e_base = ent_off[b];
+  const float* k_scale = static_cast<const float*>(rs.k_scale);
+  const uint8_t* k_mx = static_cast<const uint8_t*>(rs.k_scale);
+  const uint16_t* q16 = static_cast<const uint16_t*>(rs.qI);
+  // B operand: column c is head c % HI of query row c / HI, and only row 0 exists
+  const bool row0 = c / HI == 0;
+  bf16x8 qb[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    u32x4 v = u32x4{0, 0, 0, 0};
+    if (row0) v = *reinterpret_cast<const u32x4*>(q16 + ((int64_t)b * HI + c % HI) * 64 + kslot_dim<KT>(kk, g));
+    qb[kk] = as_bf16x8(v);
+  }
+  const float wc = row0 ? rs.w[(int64_t)b * HI + c % HI] : 0.f;
+  const bool writer = (c % HI) == 0 && row0;
+  for (int64_t e0 = (int64_t)wave * kWave; e0 < n; e0 += NT) {
+    const int64_t e_end = e0 + kWave < n ? e0 + kWave : n;
+    u32x4 kb[4][2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t s = e0 + u * 16 + c;
+      load_key_tile<KT>(rs.kI, k_mx, e_base + s, s < e_end, g, kb[u][0], kb[u][1]);
+    }
+    float my_scale = 1.f;
+    if (KT == kKeyFP8 && e0 + lane < e_end)
+      my_scale = k_scale[fp8_scale_index<false>(PagedView{}, 0, rs.scale_off, b, e0 + lane, rs.scale_group)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float v[4];
+      decode_score_tile<HI, KT>(kb[u][0], kb[u][1], qb, wc, v);
+      if (writer) *reinterpret_cast<float4*>(&stage[wave * kWave + u * 16 + 4 * g]) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+    // each wave reads back only what it wrote: LDS operations of one wave complete in order
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const float val = stage[wave * kWave + lane] * my_scale;
+    if (e0 + lane < n) srow[e0 + lane] = val;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
+template <int NT>
+__device__ void rescore_row(const RescoreIn& rs, const int64_t* __restrict__ ent_off, int b, int64_t n,
+                            float* __restrict__ srow, float* stage) {
+#define CSL_RESCORE(H, KT) \
+  case (KT) * 32 + (H): rescore_row_hk<NT, H, KT>(rs, ent_off, b, n, srow, stage); break;
+  switch (rs.key_type * 32 + rs.HI) {
+    CSL_RESCORE(1, kKeyBF16) CSL_RESCORE(2, kKeyBF16) CSL_RESCORE(4, kKeyBF16) CSL_RESCORE(8, kKeyBF16) CSL_RESCORE(16, kKeyBF16)
+    CSL_RESCORE(1, kKeyFP8) CSL_RESCORE(2, kKeyFP8) CSL_RESCORE(4, kKeyFP8) CSL_RESCORE(8, kKeyFP8) CSL_RESCORE(16, kKeyFP8)
+    CSL_RESCORE(1, kKeyFP4) CSL_RESCORE(2, kKeyFP4) CSL_RESCORE(4, kKeyFP4) CSL_RESCORE(8, kKeyFP4) CSL_RESCORE(16, kKeyFP4)
+    default: break;
+  }
+#undef CSL_RESCORE
+  // the row pass that follows reads these scores back through global memory
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  __syncthreads();
+}
+
 // One workgroup of kFinNT threads per row finishes the selection from the row's candidate
-// lists (topk_finish.h); thread i owns CH consecutive chunks of 8 slots.
-template <int CH>
-__global__ __launch_bounds__(kFinNT) void topk_finish_kernel(const float* __restrict__ scores, int64_t ld,
+// lists (topk_finish.h); thread i owns CH consecutive chunks of 8 slots. RESCORE: the indexer
+// kept no scores for list rows (scores on demand), and a row whose lists cannot prove its
+// selection has them recomputed first.
+template <int CH, bool RESCORE>
+__global__ __launch_bounds__(kFinNT) void topk_finish_kernel(float* __restrict__ scores, int64_t ld,
                                                              const int64_t* __restrict__ ent_off,
                                                              const int64_t* __restrict__ q_pos, int m, int T, int k,
                                                              int64_t max_entries, int32_t* __restrict__ idx, void* ws,
-                                                             int budget) {
+                                                             int budget, RescoreIn rs) {
   __shared__ FinishLds<kFinNT> lds;
+  __shared__ __align__(16) float stage[RESCORE ? kFinNT : 1];
   const int row = blockIdx.x;
   const int b = row / T, t = row % T;
   const TopkRowWs rw = topk_row_ws(ws, row, max_entries, budget);
-  finish_row<kFinNT, CH>(scores + (int64_t)row * ld, rw,
-                         [&] { return visible_entries(ent_off, q_pos, b, t, m, max_entries); },
-                         max_entries, budget, k, idx + (int64_t)row * k, lds);
+  float* srow = scores + (int64_t)row * ld;
+  if constexpr (RESCORE) {
+    finish_row<kFinNT, CH>(srow, rw, [&] { return visible_entries(ent_off, q_pos, b, t, m, max_entries); },
+                           max_entries, budget, k, idx + (int64_t)row * k, lds,
+                           [&](int64_t n) { rescore_row<kFinNT>(rs, ent_off, b, n, srow, stage); });
+  } else {
+    finish_row<kFinNT, CH>(srow, rw, [&] { return visible_entries(ent_off, q_pos, b, t, m, max_entries); },
+                           max_entries, budget, k, idx + (int64_t)row * k, lds);
+  }
 }
 
 template <int ITEMS>
@@ -301,8 +382,14 @@ size_t topk_workspace_bytes(int B, int T, int64_t max_entries, int k) {
 
 int topk_max_k() { return kTopkMaxK; }
 
+bool topk_finish_can_rescore(int64_t max_entries, int k) {
+  if (topk_uses_row_kernel(max_entries) || max_entries <= k || max_entries > kMultiMaxEntries) return false;
+  return topk_num_slices(max_entries) * topk_slot_budget(max_entries, k) / 8 <= kFinNT;
+}
+
 hipError_t launch_topk(const float* scores, int64_t ld, const int64_t* ent_off, const int64_t* q_pos, int m, int B,
-                       int T, int k, int64_t max_entries, int32_t* idx, void* ws, bool prepared, hipStream_t st) {
+                       int T, int k, int64_t max_entries, int32_t* idx, void* ws, bool prepared, hipStream_t st,
+                       const RescoreIn* rescore) {
   if (topk_uses_row_kernel(max_entries)) {
     if (max_entries <= 1024) return launch_row<1>(scores, ld, ent_off, q_pos, m, B, T, k, max_entries, idx, st);
     if (max_entries <= 4096) return launch_row<4>(scores, ld, ent_off, q_pos, m, B, T, k, max_entries, idx, st);
@@ -320,12 +407,22 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int64_t* ent_off, 
   // chunks of 8 slots, CH per thread
   const int64_t chunks = topk_num_slices(max_entries) * budget / 8;
   const dim3 fg((unsigned)rows);
-  if (chunks <= kFinNT)
-    topk_finish_kernel<1><<<fg, kFinNT, 0, st>>>(scores, ld, ent_off, q_pos, m, T, k, max_entries, idx, ws, budget);
-  else if (chunks <= 2 * kFinNT)
-    topk_finish_kernel<2><<<fg, kFinNT, 0, st>>>(scores, ld, ent_off, q_pos, m, T, k, max_entries, idx, ws, budget);
-  else  // at most kMaxRowSlots / 8 = 4 * kFinNT chunks
-    topk_finish_kernel<4><<<fg, kFinNT, 0, st>>>(scores, ld, ent_off, q_pos, m, T, k, max_entries, idx, ws, budget);
+  float* sc = const_cast<float*>(scores);  // written only by the recomputing instance
+  const RescoreIn none{};
+  if (rescore) {
+    if (!prepared || T != 1 || chunks > kFinNT) return hipErrorInvalidValue;
+    topk_finish_kernel<1, true><<<fg, kFinNT, 0, st>>>(sc, ld, ent_off, q_pos, m, T, k, max_entries, idx, ws, budget,
+                                                       *rescore);
+  } else if (chunks <= kFinNT) {
+    topk_finish_kernel<1, false><<<fg, kFinNT, 0, st>>>(sc, ld, ent_off, q_pos, m, T, k, max_entries, idx, ws, budget,
+                                                        none);
+  } else if (chunks <= 2 * kFinNT) {
+    topk_finish_kernel<2, false><<<fg, kFinNT, 0, st>>>(sc, ld, ent_off, q_pos, m, T, k, max_entries, idx, ws, budget,
+                                                        none);
+  } else {  // at most kMaxRowSlots / 8 = 4 * kFinNT chunks
+    topk_finish_kernel<4, false><<<fg, kFinNT, 0, st>>>(sc, ld, ent_off, q_pos, m, T, k, max_entries, idx, ws, budget,
+                                                        none);
+  }
   return hipGetLastError();
 }
 

@@ -200,10 +200,16 @@ __device__ __forceinline__ void finish_full_row(const float* __restrict__ srow, 
 // when the check fails). Thread i owns CH consecutive chunks of 8 slots of the row's layout
 // (a slice spans R / 8 chunks), so thread order is slot order is id order; the row's layout
 // must fit: topk_num_slices(max_entries) * budget <= 8 * CH * NT.
-template <int NT, int CH, typename RowN>
+// What finish_row does before the exact row pass when the lists cannot prove a row's
+// selection: nothing (the row's scores are in place), or recompute them (scores on demand).
+struct NoRepair {
+  __device__ void operator()(int64_t) const {}
+};
+
+template <int NT, int CH, typename RowN, typename Repair = NoRepair>
 __device__ __forceinline__ void finish_row(const float* __restrict__ srow, TopkRowWs rw, RowN row_n,
                                            int64_t max_entries, int budget, int k, int32_t* __restrict__ out,
-                                           FinishLds<NT>& L) {
+                                           FinishLds<NT>& L, const Repair& repair = Repair{}) {
   constexpr int PER = 8;  // slots per chunk
   constexpr int NW = NT / kWave;
   static_assert(kMinSliceSlots % PER == 0, "a slice spans whole chunks");
@@ -408,6 +414,7 @@ __device__ __forceinline__ void finish_row(const float* __restrict__ srow, TopkR
   }
   if (!ok) {
     __syncthreads();  // every thread is done with the histograms and wsum
+    repair(n);        // the row's scores, where the indexer left none
     finish_full_row<NT>(srow, n, keep, out, L);
   }
   for (int p = (int)keep + tid; p < k; p += NT) out[p] = -1;

@@ -218,6 +218,8 @@ class CsaLane(_Lane):
         self.attn_ws = torch.zeros(max(na, 16), dtype=torch.uint8, device=device)
         self.kI_copies = [self.kI]
         self.k_scale_copies = [self.k_scale]
+        # steps keep no scores for rows selected from candidate lists (csl.h, scores_on_demand)
+        self.scores_on_demand = False
 
     def compress_all(self):
         if self.kv_b is None:
@@ -283,7 +285,8 @@ class CsaLane(_Lane):
                         k_scale=self.k_scale_copies[r % len(self.k_scale_copies)], scale_off=self.scale_off,
                         scale_group=self.scale_group, max_entries=self.max_entries, attn_ws=self.attn_ws,
                         kv_b=self.kv_b, z_b=self.z_b, sink=self.sink, rope_dims=self.rope_dims,
-                        rope_base=self.rope_base, k_format=self.k_format, paged=self.paged)
+                        rope_base=self.rope_base, k_format=self.k_format, paged=self.paged,
+                        scores_on_demand=self.scores_on_demand)
 
 
 class HcaLane(_Lane):

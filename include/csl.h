@@ -386,6 +386,16 @@ typedef struct csl_csa_step {
   float rope_base;
   /* paged cache (NULL: packed) */
   const csl_paged_cache* paged;
+  /* 0: scores are written for every visible entry, as csl_indexer_scores does. Nonzero
+   * (scores on demand): rows whose selection runs on candidate lists keep no scores (their
+   * rows of `scores` are not written), which saves the score stores' share of the indexer's
+   * HBM traffic; the selected ids, out and lse are the same. A row whose lists cannot prove
+   * its selection (its winners crowd into a few 512-entry slices) gets its scores recomputed,
+   * with the indexer's arithmetic and bits, into its row of `scores` inside the top-k launch,
+   * at the cost of streaming that row's keys through one workgroup. Takes effect for single
+   * query rows (T == 1) on candidate lists (max_entries > 34,816 and the finishing workgroup's
+   * slots at most 8,192), packed layout; otherwise ignored. scores must still be given. */
+  int scores_on_demand;
 } csl_csa_step;
 
 int csl_csa_decode_step(const csl_csa_step* s, void* stream);

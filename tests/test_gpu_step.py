@@ -357,3 +357,55 @@ def test_ragged_batch_indexer_matches_each_sequence_alone(fp8):
         torch.cuda.synchronize()
         assert torch.equal(scores[b, 0, :E[b]], s1[0, 0, :E[b]]), f"scores of sequence {b} differ"
         assert torch.equal(ref_idx[b], i1[0]), f"ids of sequence {b} differ"
+
+
+@pytest.mark.parametrize("lengths,k,HI,fp8,H,crowd", [
+    ((1 << 20, 40000, 4000, 3), 1024, 8, False, 64, False),  # list rows, a row too dense for lists, short rows
+    ((1 << 20, 300001), 1024, 8, True, 64, False),           # fp8 keys
+    ((600000, 300000), 512, 16, False, 32, False),           # 16 indexer heads
+    ((400000, 200000), 256, 4, False, 16, False),            # 4 indexer heads
+    ((1 << 20, 300000), 1024, 8, False, 64, True),           # row 0's winners crowd into 4 slices
+    ((1 << 20, 300000), 1024, 8, True, 64, True),            # the same with fp8 keys
+])
+def test_scores_on_demand_matches_step_with_scores(lengths, k, HI, fp8, H, crowd):
+    """Scores on demand: the step keeps no scores for rows selected from candidate lists, and
+    selects the same ids with the same outputs, bit for bit. Rows too dense for lists keep
+    their scores; a row whose winners crowd into a few slices (its lists cannot prove the
+    selection) gets its scores recomputed, equal bit for bit to the indexer's."""
+    from compressed_sparse_long_amd import lanes
+    lane = W.Lane("csa", lengths, lengths, T=1, H=H, m=4, k=k, HI=HI, kI_fp8=fp8)
+    print(f"scores on demand: {lengths} k={k} HI={HI} fp8={fp8} crowd={crowd}", flush=True)
+    inp = synth.generate(W.Workload("on_demand", 37, (lane,)))
+    li = inp.lanes[0]
+    if crowd:  # the best keys of row 0 in entries 1024 .. 3071 (four slices)
+        if fp8:
+            li.k_scale[16:48] *= 100.0
+        else:
+            lead = li.qI[0, 0].float().sum(0)
+            li.kI[1024:3072] = (lead * 4 + 0.05 * li.kI[1024:3072].float()).to(torch.bfloat16)
+    (cl,) = lanes.build_lanes(inp)
+    cl.compress_all()
+    cl.step(0)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (cl.idx, cl.out, cl.lse, cl.scores, cl.ckv)]
+    if crowd:
+        got0 = ref[0][0, 0].cpu().numpy()
+        assert np.sum((got0 >= 1024) & (got0 < 3072)) > k // 2, "the crowded slices hold most winners"
+    cl.scores_on_demand = True
+    cl.scores.fill_(-5.0)
+    cl.idx.fill_(-7)
+    cl.step(0)
+    torch.cuda.synchronize()
+    assert torch.equal(cl.idx, ref[0]), "selected ids differ"
+    assert torch.equal(cl.out, ref[1]), "out differs"
+    assert torch.equal(cl.lse, ref[2]), "lse differs"
+    assert torch.equal(cl.ckv, ref[4]), "compressed cache differs"
+    E = lane.entries
+    for b in range(lane.B):
+        n = min(E[b], lane.q_pos[b] // lane.m)
+        row = cl.scores[b, 0, :n]
+        dense = 64 * k > 5 * n
+        if dense or (crowd and b == 0):
+            assert torch.equal(row, ref[3][b, 0, :n]), f"scores of row {b} differ"
+        else:
+            assert bool((row == -5.0).all()), f"row {b} selected from lists kept scores"
