@@ -15,7 +15,10 @@ The timed region replays a HIP graph that keeps M independent micro-batches in f
 of consecutive whole steps on its own graph branch, with its own outputs and workspaces and
 its own rotated input copies, so the latency-bound tail of one micro-batch's step (top-k
 finish, attention, merge on a few compute units) runs beside another's HBM-bound indexer.
-Every step is the whole hot path; the graph only saves host-side launches. The time per step
+Every step is the whole hot path; the graph only saves host-side launches. Steps keep no
+scores for rows whose top-k runs on candidate lists (csl.h, scores_on_demand: the ids and
+outputs are the same; the in-flight time of steps that write every score is reported beside
+it, and --with-scores times those instead). The time per step
 of one micro-batch at a time (a chain of 32 dependent steps) and the latency of a step
 captured and launched on its own are reported beside it. Prints one JSON line: queries/s,
 ms per step, the
@@ -57,7 +60,8 @@ GRAPH_ROUNDS = 8
 # fill and drain, are then a small share of each step.
 IN_FLIGHT_STEPS = 64
 COUNTER_FILE = os.path.join(ROOT, "profiles", "indexer_csa_decode_1m_counters.txt")
-INDEXER_SOURCES = ["compressed_sparse_long_amd/csrc/indexer.hip", "compressed_sparse_long_amd/csrc/device_common.h",
+INDEXER_SOURCES = ["compressed_sparse_long_amd/csrc/indexer.hip", "compressed_sparse_long_amd/csrc/indexer_common.h",
+                   "compressed_sparse_long_amd/csrc/device_common.h",
                    "compressed_sparse_long_amd/csrc/topk_common.h", "compressed_sparse_long_amd/csrc/compress_common.h"]
 
 
@@ -85,6 +89,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=256)
     ap.add_argument("--copies", type=int, default=4,
                     help="rotated input copies (>= 4 defeats the 256 MB MALL; at least 2 per micro-batch in flight)")
+    ap.add_argument("--with-scores", action="store_true",
+                    help="the timed steps write every score (default: scores on demand, see csl.h)")
     ap.add_argument("--inflight", type=int, default=4,
                     help="independent micro-batches whose step chains the timed graph runs concurrently")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="wall budget of the oracle sample")
@@ -225,10 +231,10 @@ def main():
         return
     if args.run_workload:
         run_workload(args.run_workload, args.steps, args.warmup, args.paged, args.copies, args.scoreless,
-                     args.inflight if args.inflight_workload else 1)
+                     args.inflight if args.inflight_workload else 1, args.with_scores)
         return
     if args.report_configs:
-        report_configs(args.copies, args.cpu_seconds, inflight=args.inflight)
+        report_configs(args.copies, args.cpu_seconds, inflight=args.inflight, on_demand=not args.with_scores)
         return
 
     result = measure_headline(args)
@@ -240,7 +246,7 @@ def main():
         torch.cuda.empty_cache()
         result["configs"] = {ln.pop("workload"): ln for ln in
                              report_configs(args.copies, args.config_cpu_seconds, emit=False,
-                                            inflight=args.inflight)}
+                                            inflight=args.inflight, on_demand=not args.with_scores)}
     print(json.dumps(result), flush=True)
 
 
@@ -253,6 +259,9 @@ def measure_headline(args) -> dict:
     t_gen = time.perf_counter()
     inp = synth.generate(WORKLOAD)
     (cl,) = lanes.build_lanes(inp)
+    # the step keeps no scores for rows selected from candidate lists (csl.h, scores_on_demand):
+    # the ids and outputs are those of the step with scores, which is timed beside it
+    cl.scores_on_demand = not args.with_scores
     M = max(1, args.inflight)
     cl.rotate(max(args.copies, 2 * M))
     cl.compress_all()
@@ -293,6 +302,22 @@ def measure_headline(args) -> dict:
 
     reps = (args.steps + S - 1) // S
     K = reps * S
+    # the same timed loop with every step writing its scores
+    for mb in mbs:
+        mb.scores_on_demand = False
+    with_scores = in_flight_steps([cl], M, R)[0]
+    with_scores.replay()
+    torch.cuda.synchronize()
+    ws_a, ws_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ws_a.record()
+    for i in range(reps):
+        with_scores.replay()
+    ws_b.record()
+    torch.cuda.synchronize()
+    with_scores_us = ws_a.elapsed_time(ws_b) / K * 1e3
+    del with_scores
+    for mb in mbs:
+        mb.scores_on_demand = not args.with_scores
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
@@ -362,7 +387,8 @@ def measure_headline(args) -> dict:
         "data": "synthetic",
         "config": {"workload": WORKLOAD, "batch": B, "context_tokens": lane.lengths[0], "entries": E,
                    "heads": H, "head_dim": D, "m": lane.m, "top_k": k, "window": W, "indexer_heads": HI,
-                   "indexer_dim": CI, "rotated_copies": R, "micro_batches_in_flight": M},
+                   "indexer_dim": CI, "rotated_copies": R, "micro_batches_in_flight": M,
+                   "scores_on_demand": not args.with_scores},
         "roofline": {"kernel": "indexer_decode_kernel", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "launch_us": round(idx_us, 3), "bytes_per_launch": idx_bytes,
@@ -372,6 +398,7 @@ def measure_headline(args) -> dict:
         "indexer_mfma": {"flops_per_launch": idx_flops, "issued_flops_per_launch": idx_issued,
                          "achieved": round(idx_flops / (idx_us * 1e-6) / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(idx_flops / (idx_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5)},
+        "step_us_with_scores": round(with_scores_us, 2),
         "step_us_serial": round(serial_us, 2),
         "step_us_one_graph_per_step": round(single_us, 2),
         "step_hbm": {"bytes": step_bytes, "GB_s": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
@@ -500,7 +527,7 @@ def measure_headline(args) -> dict:
 
 
 def run_workload(name: str, steps: int, warmup: int, paged: str | None = None, copies: int = 4,
-                 scoreless: bool = False, inflight: int = 1) -> None:
+                 scoreless: bool = False, inflight: int = 1, with_scores: bool = False) -> None:
     """Replay one configuration's whole step (every lane) as a graph; print its mean time.
     Each graph holds ``copies`` steps over rotated copies of the large inputs (as in the main
     measurement); ``paged``: move every lane's cache into a block pool first, blocks in that
@@ -512,6 +539,9 @@ def run_workload(name: str, steps: int, warmup: int, paged: str | None = None, c
 
     inp = synth.generate(name)
     ls = lanes.build_lanes(inp, scoreless=scoreless)
+    for lane in ls:  # as the bench line: CSA steps keep no scores for rows on candidate lists
+        if hasattr(lane, "scores_on_demand"):
+            lane.scores_on_demand = not with_scores
     M = max(1, inflight)
     R = max(1, copies, 2 * M if M > 1 else 1)
     for lane in ls:
@@ -637,7 +667,8 @@ def oracle_rate(inp, seconds: float, D: int = 128):
             "sample": f"{n} queries ({len(work)} sampled sequence(s), fp64 numpy) in {el:.1f} s", "machine": mach}
 
 
-def report_configs(copies: int, cpu_seconds: float, emit: bool = True, inflight: int = 4) -> list:
+def report_configs(copies: int, cpu_seconds: float, emit: bool = True, inflight: int = 4,
+                   on_demand: bool = True) -> list:
     """Every synthetic configuration: whole-step time with ``inflight`` independent
     micro-batches in flight (each a chain of steps on its own graph branch, every lane of a
     micro-batch a chain of its own) and one micro-batch at a time (a graph of GRAPH_ROUNDS x
@@ -650,6 +681,9 @@ def report_configs(copies: int, cpu_seconds: float, emit: bool = True, inflight:
 
     def time_step(inp, scoreless: bool, M: int) -> float:
         ls = lanes.build_lanes(inp, scoreless=scoreless)
+        for lane in ls:  # CSA steps keep no scores for rows on candidate lists (csl.h)
+            if hasattr(lane, "scores_on_demand"):
+                lane.scores_on_demand = on_demand
         R = max(copies, 2 * M) if M > 1 else copies
         for lane in ls:
             lane.rotate(R)
@@ -696,7 +730,8 @@ def report_configs(copies: int, cpu_seconds: float, emit: bool = True, inflight:
             nos_us = time_step(inp, True, max(1, inflight))
             extra = {"step_us_without_scores": round(nos_us, 2),
                      "queries_per_s_without_scores": round(queries / (nos_us * 1e-6), 1)}
-        line = {"workload": name, "micro_batches_in_flight": max(1, inflight), "step_us": round(step_us, 2),
+        line = {"workload": name, "micro_batches_in_flight": max(1, inflight), "scores_on_demand": on_demand,
+                "step_us": round(step_us, 2),
                 "queries_per_s": round(queries / (step_us * 1e-6), 1), "step_us_serial": round(serial_us, 2),
                 "queries_per_s_serial": round(queries / (serial_us * 1e-6), 1),
                 "bytes": nbytes, "GB_s": round(nbytes / (step_us * 1e-6) / 1e9, 1),
