@@ -265,15 +265,14 @@ __global__ __launch_bounds__(kFinNT) void topk_row_kernel(const float* __restric
   for (int p = (int)keep + tid; p < k; p += kFinNT) out[p] = -1;
 }
 
-// Scores on demand: the scores of entries [0, n) of sequence b's one query row, recomputed by
-// the workgroup's waves, 64 keys per wave and pass, with the decode indexer's loads, tile
-// arithmetic (decode_score_tile) and LDS staging, so each score has the indexer's bits. The
+// Scores on demand: the scores of entries [e0, min(e0 + 64, n)) of sequence b's one query row,
+// recomputed by one wave with the decode indexer's loads, tile arithmetic (decode_score_tile)
+// and LDS staging (64 floats of the wave's own), so each score has the indexer's bits. The
 // query operand holds row 0 only: the lists exist only for one query row per sequence.
-template <int NT, int HI, int KT>
-__device__ __forceinline__ void rescore_row_hk(const RescoreIn& rs, const int64_t* __restrict__ ent_off, int b,
-                                               int64_t n, float* __restrict__ srow, float* stage) {
-  const int tid = threadIdx.x;
-  const int wave = tid / kWave, lane = tid % kWave;
+template <int HI, int KT>
+__device__ __forceinline__ void rescore_wave_hk(const RescoreIn& rs, const int64_t* __restrict__ ent_off, int b,
+                                                int64_t e0, int64_t n, float* __restrict__ srow, float* stage) {
+  const int lane = threadIdx.x % kWave;
   const int g = lane / 16, c = lane % 16;
   const int64_t e_base = ent_off[b];
   const float* k_scale = static_cast<const float*>(rs.k_scale);
@@ -290,51 +289,55 @@ __device__ __forceinline__ void rescore_row_hk(const RescoreIn& rs, const int64_
   }
   const float wc = row0 ? rs.w[(int64_t)b * HI + c % HI] : 0.f;
   const bool writer = (c % HI) == 0 && row0;
-  for (int64_t e0 = (int64_t)wave * kWave; e0 < n; e0 += NT) {
-    const int64_t e_end = e0 + kWave < n ? e0 + kWave : n;
-    u32x4 kb[4][2];
+  const int64_t e_end = e0 + kWave < n ? e0 + kWave : n;
+  u32x4 kb[4][2];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t s = e0 + u * 16 + c;
-      load_key_tile<KT>(rs.kI, k_mx, e_base + s, s < e_end, g, kb[u][0], kb[u][1]);
-    }
-    float my_scale = 1.f;
-    if (KT == kKeyFP8 && e0 + lane < e_end)
-      my_scale = k_scale[fp8_scale_index<false>(PagedView{}, 0, rs.scale_off, b, e0 + lane, rs.scale_group)];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      float v[4];
-      decode_score_tile<HI, KT>(kb[u][0], kb[u][1], qb, wc, v);
-      if (writer) *reinterpret_cast<float4*>(&stage[wave * kWave + u * 16 + 4 * g]) = make_float4(v[0], v[1], v[2], v[3]);
-    }
-    // each wave reads back only what it wrote: LDS operations of one wave complete in order
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const float val = stage[wave * kWave + lane] * my_scale;
-    if (e0 + lane < n) srow[e0 + lane] = val;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  for (int u = 0; u < 4; ++u) {
+    const int64_t s = e0 + u * 16 + c;
+    load_key_tile<KT>(rs.kI, k_mx, e_base + s, s < e_end, g, kb[u][0], kb[u][1]);
   }
+  float my_scale = 1.f;
+  if (KT == kKeyFP8 && e0 + lane < e_end)
+    my_scale = k_scale[fp8_scale_index<false>(PagedView{}, 0, rs.scale_off, b, e0 + lane, rs.scale_group)];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    float v[4];
+    decode_score_tile<HI, KT>(kb[u][0], kb[u][1], qb, wc, v);
+    if (writer) *reinterpret_cast<float4*>(&stage[u * 16 + 4 * g]) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+  // each wave reads back only what it wrote: LDS operations of one wave complete in order
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const float val = stage[lane] * my_scale;
+  if (e0 + lane < n) srow[e0 + lane] = val;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int NT>
-__device__ void rescore_row(const RescoreIn& rs, const int64_t* __restrict__ ent_off, int b, int64_t n,
-                            float* __restrict__ srow, float* stage) {
+// finish_row's Repair for scores on demand: each wave recomputes with its own 64 floats of LDS
+struct RescoreRepair {
+  static constexpr bool kActive = true;
+  RescoreIn rs;
+  const int64_t* ent_off;
+  int b;
+  float* srow;
+  float* stage;  // 64 floats per wave
+  __device__ __forceinline__ void wave(int64_t e0, int64_t n) const {
+    float* st = stage + (threadIdx.x / kWave) * kWave;
 #define CSL_RESCORE(H, KT) \
-  case (KT) * 32 + (H): rescore_row_hk<NT, H, KT>(rs, ent_off, b, n, srow, stage); break;
-  switch (rs.key_type * 32 + rs.HI) {
-    CSL_RESCORE(1, kKeyBF16) CSL_RESCORE(2, kKeyBF16) CSL_RESCORE(4, kKeyBF16) CSL_RESCORE(8, kKeyBF16) CSL_RESCORE(16, kKeyBF16)
-    CSL_RESCORE(1, kKeyFP8) CSL_RESCORE(2, kKeyFP8) CSL_RESCORE(4, kKeyFP8) CSL_RESCORE(8, kKeyFP8) CSL_RESCORE(16, kKeyFP8)
-    CSL_RESCORE(1, kKeyFP4) CSL_RESCORE(2, kKeyFP4) CSL_RESCORE(4, kKeyFP4) CSL_RESCORE(8, kKeyFP4) CSL_RESCORE(16, kKeyFP4)
-    default: break;
-  }
+  case (KT) * 32 + (H): rescore_wave_hk<H, KT>(rs, ent_off, b, e0, n, srow, st); break;
+    switch (rs.key_type * 32 + rs.HI) {
+      CSL_RESCORE(1, kKeyBF16) CSL_RESCORE(2, kKeyBF16) CSL_RESCORE(4, kKeyBF16) CSL_RESCORE(8, kKeyBF16)
+      CSL_RESCORE(16, kKeyBF16) CSL_RESCORE(1, kKeyFP8) CSL_RESCORE(2, kKeyFP8) CSL_RESCORE(4, kKeyFP8)
+      CSL_RESCORE(8, kKeyFP8) CSL_RESCORE(16, kKeyFP8) CSL_RESCORE(1, kKeyFP4) CSL_RESCORE(2, kKeyFP4)
+      CSL_RESCORE(4, kKeyFP4) CSL_RESCORE(8, kKeyFP4) CSL_RESCORE(16, kKeyFP4)
+      default: break;
+    }
 #undef CSL_RESCORE
-  // the row pass that follows reads these scores back through global memory
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-  __syncthreads();
-}
+  }
+};
 
 // One workgroup of kFinNT threads per row finishes the selection from the row's candidate
 // lists (topk_finish.h); thread i owns CH consecutive chunks of 8 slots. RESCORE: the indexer
@@ -355,7 +358,7 @@ __global__ __launch_bounds__(kFinNT) void topk_finish_kernel(float* __restrict__
   if constexpr (RESCORE) {
     finish_row<kFinNT, CH>(srow, rw, [&] { return visible_entries(ent_off, q_pos, b, t, m, max_entries); },
                            max_entries, budget, k, idx + (int64_t)row * k, lds,
-                           [&](int64_t n) { rescore_row<kFinNT>(rs, ent_off, b, n, srow, stage); });
+                           RescoreRepair{rs, ent_off, b, srow, stage});
   } else {
     finish_row<kFinNT, CH>(srow, rw, [&] { return visible_entries(ent_off, q_pos, b, t, m, max_entries); },
                            max_entries, budget, k, idx + (int64_t)row * k, lds);

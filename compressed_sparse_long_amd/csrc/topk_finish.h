@@ -92,7 +92,10 @@ __device__ __forceinline__ void finish_full_row(const float* __restrict__ srow, 
       }
 #pragma unroll
       for (int j = 0; j < U; ++j)
-        if (c0 + (int64_t)j * NT + tid < n) fn(score_key(v[j]));
+        if (c0 + (int64_t)j * NT + tid < n) {
+          const uint32_t x = score_key(v[j]);
+          if (x) fn(x);  // key 0 marks no entry (kNoScoreBits below)
+        }
     }
   };
   for (int q = tid; q < 2048; q += NT) {
@@ -157,8 +160,9 @@ __device__ __forceinline__ void finish_full_row(const float* __restrict__ srow, 
     for (int j = 0; j < J; ++j) v[j] = srow[i0 + j < n ? i0 + j : n - 1];  // clamped: no branch per load
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      if (i0 + j < n) {
-        const uint32_t h = score_key(v[j]) >> shift;
+      const uint32_t x = score_key(v[j]);
+      if (i0 + j < n && x) {
+        const uint32_t h = x >> shift;
         if (h > prefix || (all_in && h == prefix)) gm |= 1u << j;
         else if (h == prefix) em |= 1u << j;
       }
@@ -201,15 +205,27 @@ __device__ __forceinline__ void finish_full_row(const float* __restrict__ srow, 
 // (a slice spans R / 8 chunks), so thread order is slot order is id order; the row's layout
 // must fit: topk_num_slices(max_entries) * budget <= 8 * CH * NT.
 // What finish_row does before the exact row pass when the lists cannot prove a row's
-// selection: nothing (the row's scores are in place), or recompute them (scores on demand).
+// selection: nothing (the row's scores are in place), or, when the indexer left no scores
+// for the row (scores on demand), build them: a Repair with kActive recomputes the scores of
+// entries [e0, min(e0 + 64, n)) with one wave (wave(e0, n)).
 struct NoRepair {
-  __device__ void operator()(int64_t) const {}
+  static constexpr bool kActive = false;
+  __device__ void wave(int64_t, int64_t) const {}
 };
+
+// A value in a score row that the exact row pass skips: the one float whose key is 0 (a NaN
+// with every bit set, which no score is)
+constexpr uint32_t kNoScoreBits = 0xffffffffu;
+
+// The float whose score_key is x (score_key is one-to-one on floats other than -0)
+__device__ __forceinline__ float key_score(uint32_t x) {
+  return __uint_as_float((x & 0x80000000u) ? (x & 0x7fffffffu) : ~x);
+}
 
 template <int NT, int CH, typename RowN, typename Repair = NoRepair>
 __device__ __forceinline__ void finish_row(const float* __restrict__ srow, TopkRowWs rw, RowN row_n,
                                            int64_t max_entries, int budget, int k, int32_t* __restrict__ out,
-                                           FinishLds<NT>& L, const Repair& repair = Repair{}) {
+                                           FinishLds<NT>& L, Repair repair = Repair{}) {
   constexpr int PER = 8;  // slots per chunk
   constexpr int NW = NT / kWave;
   static_assert(kMinSliceSlots % PER == 0, "a slice spans whole chunks");
@@ -357,10 +373,12 @@ __device__ __forceinline__ void finish_row(const float* __restrict__ srow, TopkR
     }
   }
 
+  const bool listed_enough = ok;  // the lists hold at least `keep` keys
+  uint32_t lo = 0;                 // lowest key a listed winner can have
   if (ok) {
     // winners: keys above the selected bin, plus (unless the whole bin is taken) the first
     // `need` keys equal to the exact key value, in id order
-    const uint32_t lo = prefix << shift;  // lowest key a winner can have
+    lo = prefix << shift;
     uint32_t gmask = 0, emask = 0, viol = 0;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
@@ -414,7 +432,42 @@ __device__ __forceinline__ void finish_row(const float* __restrict__ srow, TopkR
   }
   if (!ok) {
     __syncthreads();  // every thread is done with the histograms and wsum
-    repair(n);        // the row's scores, where the indexer left none
+    if constexpr (Repair::kActive) {
+      // no scores from the indexer: build the row the exact pass reads. With fewer listed keys
+      // than winners, recompute every entry. Otherwise the true threshold is at or above the
+      // k-th listed key lo, so a slice whose cut is at or below lo lists every entry that can
+      // win: its listed entries take their listed keys and the rest kNoScoreBits, which the
+      // exact pass skips;
+      // the slices whose cut is above lo are recomputed whole.
+      float* row = const_cast<float*>(srow);
+      const int wave = tid / kWave;
+      if (!listed_enough) {
+        for (int64_t e0 = (int64_t)wave * kWave; e0 < n; e0 += NT) repair.wave(e0, n);
+      } else {
+        uint32_t* redo = hist_a;  // per slice: recompute it (ns <= 2048)
+        for (int64_t i = tid; i < n; i += NT) row[i] = __uint_as_float(kNoScoreBits);
+        for (int q = tid; q < ns; q += NT) redo[q] = 0u;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __syncthreads();
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+          const int slice = (tid * CH + c) >> cps_log2;
+          if (slice >= ns) continue;
+          if (cut[c] > lo) redo[slice] = 1u;
+#pragma unroll
+          for (int q = 0; q < PER; ++q)
+            if (key[c][q]) row[(uint32_t)sl[c][q]] = key_score(key[c][q]);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __syncthreads();
+        constexpr int WPS = kSlice / kWave;  // wave-sized parts of a slice
+        for (int t = wave; t < ns * WPS; t += NW)
+          if (redo[t / WPS]) repair.wave((int64_t)t * kWave, n);
+      }
+      // the exact pass reads the row back through global memory
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+      __syncthreads();
+    }
     finish_full_row<NT>(srow, n, keep, out, L);
   }
   for (int p = (int)keep + tid; p < k; p += NT) out[p] = -1;

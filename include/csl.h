@@ -390,11 +390,13 @@ typedef struct csl_csa_step {
    * (scores on demand): rows whose selection runs on candidate lists keep no scores (their
    * rows of `scores` are not written), which saves the score stores' share of the indexer's
    * HBM traffic; the selected ids, out and lse are the same. A row whose lists cannot prove
-   * its selection (its winners crowd into a few 512-entry slices) gets its scores recomputed,
-   * with the indexer's arithmetic and bits, into its row of `scores` inside the top-k launch,
-   * at the cost of streaming that row's keys through one workgroup. Takes effect for single
+   * its selection (its winners crowd into a few 512-entry slices) has its row of `scores`
+   * rebuilt inside the top-k launch before the exact row pass: the slices that could hide a
+   * winner recomputed whole with the indexer's arithmetic and bits, the listed entries of the
+   * others at their scores, elsewhere the NaN with every bit set (a row with fewer listed
+   * entries than k is recomputed whole, streaming its keys through one workgroup). For single
    * query rows (T == 1) on candidate lists (max_entries > 34,816 and the finishing workgroup's
-   * slots at most 8,192), packed layout; otherwise ignored. scores must still be given. */
+   * slots at most 8,192), packed layout; ignored otherwise. scores must still be given. */
   int scores_on_demand;
 } csl_csa_step;
 
