@@ -717,7 +717,9 @@ def report_configs(copies: int, cpu_seconds: float, emit: bool = True, inflight:
         return a.elapsed_time(b) / (reps * steps) * 1e3
 
     lines = []
-    for name in synth.CONFIG_ORDER:
+    # the prefill configuration last: its long MFMA-heavy replays would otherwise heat the chip
+    # right before the next configuration's timing
+    for name in sorted(synth.CONFIG_ORDER, key=lambda n: "prefill" in n):
         print(f"# configuration {name}: generating inputs", file=sys.stderr, flush=True)
         inp = synth.generate(name)
         step_us = time_step(inp, False, max(1, inflight))
