@@ -417,3 +417,27 @@ def test_scores_on_demand_matches_step_with_scores(lengths, k, HI, fp8, H, crowd
             assert bool(have[1024:3072].all()), "the crowded slices were not recomputed"
         else:
             assert bool((row == -5.0).all()), f"row {b} selected from lists kept scores"
+
+
+def test_scores_on_demand_is_ignored_for_a_paged_cache():
+    """With the cache paged the step writes every score whatever scores_on_demand says (the
+    finishing step recomputes rows from the packed layout only): the same ids, outputs and
+    scores as the paged step with scores."""
+    from compressed_sparse_long_amd import lanes
+    lane = W.Lane("csa", (1 << 20, 300001), (1 << 20, 300001), T=1, H=64, m=4, k=1024, HI=8)
+    print("scores on demand, paged", flush=True)
+    inp = synth.generate(W.Workload("on_demand_paged", 43, (lane,)))
+    (cl,) = lanes.build_lanes(inp)
+    cl.compress_all()
+    cl.paginate(ring_rows=256)
+    cl.step(0)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (cl.idx, cl.out, cl.lse, cl.scores)]
+    cl.scores_on_demand = True
+    cl.scores.fill_(-5.0)
+    cl.idx.fill_(-7)
+    cl.step(0)
+    torch.cuda.synchronize()
+    assert torch.equal(cl.idx, ref[0]) and torch.equal(cl.out, ref[1]) and torch.equal(cl.lse, ref[2])
+    for b, e in enumerate(lane.entries):
+        assert torch.equal(cl.scores[b, 0, :e], ref[3][b, 0, :e]), f"scores of row {b} not written"
