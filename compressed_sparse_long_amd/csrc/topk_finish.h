@@ -447,7 +447,7 @@ __device__ __forceinline__ void finish_row(const float* __restrict__ srow, TopkR
         uint32_t* redo = hist_a;  // per slice: recompute it (ns <= 2048)
         for (int64_t i = tid; i < n; i += NT) row[i] = __uint_as_float(kNoScoreBits);
         for (int q = tid; q < ns; q += NT) redo[q] = 0u;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __threadfence();  // stores of every wave done before the next writes to the same row
         __syncthreads();
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
@@ -458,14 +458,15 @@ __device__ __forceinline__ void finish_row(const float* __restrict__ srow, TopkR
           for (int q = 0; q < PER; ++q)
             if (key[c][q]) row[(uint32_t)sl[c][q]] = key_score(key[c][q]);
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __threadfence();  // stores of every wave done before the next writes to the same row
         __syncthreads();
         constexpr int WPS = kSlice / kWave;  // wave-sized parts of a slice
         for (int t = wave; t < ns * WPS; t += NW)
           if (redo[t / WPS]) repair.wave((int64_t)t * kWave, n);
       }
-      // the exact pass reads the row back through global memory
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+      // the exact pass reads the row back through global memory (a rare path: the fences are
+      // device-wide, so no wave's store can land after another wave's read or write)
+      __threadfence();
       __syncthreads();
     }
     finish_full_row<NT>(srow, n, keep, out, L);
