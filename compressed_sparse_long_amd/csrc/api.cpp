@@ -47,7 +47,7 @@ extern "C" {
 
 const char* csl_last_error(void) { return g_last_error.c_str(); }
 
-int csl_version(void) { return 400; }
+int csl_version(void) { return 500; }
 
 }  // extern "C"
 

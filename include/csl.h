@@ -104,8 +104,9 @@ typedef struct csl_paged_cache {
 /* Message for the last failed call on this thread ("" if none). Never NULL. */
 const char* csl_last_error(void);
 
-/* Library version as MAJOR*10000 + MINOR*100 + PATCH (0.4.0: overlapped compression,
- * attention sink and partial RoPE, MXFP4 indexer keys, paged cache). */
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH (0.5.0: csl_csa_step gains
+ * scores_on_demand at its end; 0.4.0: overlapped compression, attention sink and partial
+ * RoPE, MXFP4 indexer keys, paged cache). */
 int csl_version(void);
 
 /*

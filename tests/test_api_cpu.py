@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, s), s
     import compressed_sparse_long_amd as csl
     assert sorted(csl.EXPORTS) == declared_symbols()
-    assert csl.version() == 400
+    assert csl.version() == 500
 
 
 P = ctypes.c_void_p
