@@ -339,28 +339,28 @@ struct RescoreRepair {
   }
 };
 
-// One workgroup of kFinNT threads per row finishes the selection from the row's candidate
-// lists (topk_finish.h); thread i owns CH consecutive chunks of 8 slots. RESCORE: the indexer
+// One workgroup of NT threads per row finishes the selection from the row's candidate lists
+// (topk_finish.h); thread i owns CH consecutive chunks of 8 slots. RESCORE: the indexer
 // kept no scores for list rows (scores on demand), and a row whose lists cannot prove its
 // selection has them recomputed first.
-template <int CH, bool RESCORE>
-__global__ __launch_bounds__(kFinNT) void topk_finish_kernel(float* __restrict__ scores, int64_t ld,
+template <int NT, int CH, bool RESCORE>
+__global__ __launch_bounds__(NT) void topk_finish_kernel(float* __restrict__ scores, int64_t ld,
                                                              const int64_t* __restrict__ ent_off,
                                                              const int64_t* __restrict__ q_pos, int m, int T, int k,
                                                              int64_t max_entries, int32_t* __restrict__ idx, void* ws,
                                                              int budget, RescoreIn rs) {
-  __shared__ FinishLds<kFinNT> lds;
-  __shared__ __align__(16) float stage[RESCORE ? kFinNT : 1];
+  __shared__ FinishLds<NT> lds;
+  __shared__ __align__(16) float stage[RESCORE ? NT : 1];
   const int row = blockIdx.x;
   const int b = row / T, t = row % T;
   const TopkRowWs rw = topk_row_ws(ws, row, max_entries, budget);
   float* srow = scores + (int64_t)row * ld;
   if constexpr (RESCORE) {
-    finish_row<kFinNT, CH>(srow, rw, [&] { return visible_entries(ent_off, q_pos, b, t, m, max_entries); },
+    finish_row<NT, CH>(srow, rw, [&] { return visible_entries(ent_off, q_pos, b, t, m, max_entries); },
                            max_entries, budget, k, idx + (int64_t)row * k, lds,
                            RescoreRepair{rs, ent_off, b, srow, stage});
   } else {
-    finish_row<kFinNT, CH>(srow, rw, [&] { return visible_entries(ent_off, q_pos, b, t, m, max_entries); },
+    finish_row<NT, CH>(srow, rw, [&] { return visible_entries(ent_off, q_pos, b, t, m, max_entries); },
                            max_entries, budget, k, idx + (int64_t)row * k, lds);
   }
 }
@@ -412,19 +412,25 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int64_t* ent_off, 
   const dim3 fg((unsigned)rows);
   float* sc = const_cast<float*>(scores);  // written only by the recomputing instance
   const RescoreIn none{};
+  // rows of at most 2 * 512 chunks (8,192 slots): 512 threads with two chunks each. A
+  // 1,024-thread workgroup needs most of a compute unit's wave slots and registers at once, so
+  // beside other kernels' workgroups (decode steps of several micro-batches in flight) it waited
+  // for a whole compute unit to drain; the 512-thread one starts sooner there (in-flight steps
+  // 27.6 -> 26.9 us at 1M context) at ~1 us more on its own (256 threads: slower both ways)
+  constexpr int NS = 512;
   if (rescore) {
-    if (!prepared || T != 1 || chunks > kFinNT) return hipErrorInvalidValue;
-    topk_finish_kernel<1, true><<<fg, kFinNT, 0, st>>>(sc, ld, ent_off, q_pos, m, T, k, max_entries, idx, ws, budget,
+    if (!prepared || T != 1 || chunks > 2 * NS) return hipErrorInvalidValue;
+    topk_finish_kernel<NS, 2, true><<<fg, NS, 0, st>>>(sc, ld, ent_off, q_pos, m, T, k, max_entries, idx, ws, budget,
                                                        *rescore);
-  } else if (chunks <= kFinNT) {
-    topk_finish_kernel<1, false><<<fg, kFinNT, 0, st>>>(sc, ld, ent_off, q_pos, m, T, k, max_entries, idx, ws, budget,
+  } else if (chunks <= 2 * NS) {
+    topk_finish_kernel<NS, 2, false><<<fg, NS, 0, st>>>(sc, ld, ent_off, q_pos, m, T, k, max_entries, idx, ws, budget,
                                                         none);
   } else if (chunks <= 2 * kFinNT) {
-    topk_finish_kernel<2, false><<<fg, kFinNT, 0, st>>>(sc, ld, ent_off, q_pos, m, T, k, max_entries, idx, ws, budget,
-                                                        none);
+    topk_finish_kernel<kFinNT, 2, false><<<fg, kFinNT, 0, st>>>(sc, ld, ent_off, q_pos, m, T, k, max_entries, idx, ws,
+                                                                budget, none);
   } else {  // at most kMaxRowSlots / 8 = 4 * kFinNT chunks
-    topk_finish_kernel<4, false><<<fg, kFinNT, 0, st>>>(sc, ld, ent_off, q_pos, m, T, k, max_entries, idx, ws, budget,
-                                                        none);
+    topk_finish_kernel<kFinNT, 4, false><<<fg, kFinNT, 0, st>>>(sc, ld, ent_off, q_pos, m, T, k, max_entries, idx, ws,
+                                                                budget, none);
   }
   return hipGetLastError();
 }
