@@ -240,6 +240,11 @@ def test_step_validation(lib):
     assert call(rope_dims=40, rope_base=1e4) == 2   # RoPE width not a multiple of 32
     assert call(B=0) == 0                       # nothing to do: nothing enqueued
     assert _err(lib) == ""
+    # scores on demand is a mode of the same call: validated alike, still needing a score buffer
+    assert call(scores_on_demand=1, B=0) == 0
+    assert call(scores_on_demand=1, idx=None) == 1
+    assert call(scores_on_demand=1, HI=3) == 2
+    assert ctypes.sizeof(csl._CsaStep) == csl._CsaStep.scores_on_demand.offset + 8  # the last field, padded
     # without a score buffer: the fused indexer/top-k's limit on k applies instead
     assert call(scores=None, k=1953) == 2
     assert "without scores" in _err(lib)
